@@ -1,0 +1,200 @@
+"""Seeded synthetic inputs for the routed MoE layer (Python side of csrc/synth.c).
+
+Everything here is input generation: random draws and their encoding into the
+formats the layer reads.  None of the layer's arithmetic lives here; where an
+input recipe needs routing decisions (the top-k margin filter, the Zipf bias
+calibration) the caller passes in the function that makes them.
+
+Recipe (seed 0 unless stated):
+- x: N(0, 1) per element, rounded to bf16; a row may be redrawn (attempt a+1)
+  by a caller-supplied filter.
+- router weight: N(0, 0.02) fp32 [E][d].
+- experts 0..E-1 routed and expert E = the shared expert: gate/up N(0, 1/sqrt(d)),
+  down N(0, 1/sqrt(I)), fp32 then MXFP4 (E2M1 + per-32 E8M0).
+- hash routing: tid2eid [vocab][k] with k distinct ids per token id, token ids
+  uniform over the vocabulary.
+- Zipf load: per-row selection probability q_e = min(1, c * rank_e^-1.2) with
+  sum q = k; ranks map to a seeded permutation of the experts.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .configs import CFG_TAG, ROUTER_STD, SET_TAG, MoEShape, expert_std
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoe_synth.so")
+_lib = None
+
+MAT_GATE, MAT_UP, MAT_DOWN = 1, 2, 3
+
+
+def usable_cpus() -> int:
+    """CPUs this process may run on: affinity mask, capped by a cgroup v2 quota."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            n = max(1, min(n, int(int(quota) // int(period))))
+    except (OSError, ValueError):
+        pass
+    return max(1, n)
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(_LIB_PATH)
+        u64, i64, i32, dbl, vp = ctypes.c_uint64, ctypes.c_long, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+        lib.synth_x_bf16.argtypes = [u64, u64, i64, i64, vp, vp, i32]
+        lib.synth_router_f32.argtypes = [u64, u64, i64, i64, dbl, vp, i32]
+        lib.synth_mxfp4.argtypes = [u64, u64, u64, i64, i64, i64, i64, dbl, vp, vp, i32]
+        lib.synth_mxfp4.restype = i32
+        lib.synth_encode_mxfp4.argtypes = [vp, i64, i64, vp, vp]
+        lib.synth_tid2eid.argtypes = [u64, u64, i64, i32, i32, vp, i32]
+        lib.synth_tid2eid.restype = i32
+        lib.synth_token_ids.argtypes = [u64, u64, i64, i64, vp]
+        lib.synth_permutation.argtypes = [u64, u64, i64, vp]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def gen_x(shape: MoEShape, seed: int = 0, attempts=None, threads=None) -> np.ndarray:
+    """x [N][d] as bf16 bit patterns (uint16)."""
+    out = np.empty((shape.n_rows, shape.d_model), dtype=np.uint16)
+    att = None
+    if attempts is not None:
+        att = np.ascontiguousarray(attempts, dtype=np.int32)
+        assert att.shape == (shape.n_rows,)
+    _load().synth_x_bf16(seed, CFG_TAG[shape.name], shape.n_rows, shape.d_model,
+                         _ptr(att) if att is not None else None, _ptr(out), threads or usable_cpus())
+    return out
+
+
+def gen_router(shape: MoEShape, seed: int = 0, threads=None) -> np.ndarray:
+    out = np.empty((shape.n_experts, shape.d_model), dtype=np.float32)
+    _load().synth_router_f32(seed, SET_TAG[shape.weight_set], shape.n_experts, shape.d_model,
+                             ROUTER_STD, _ptr(out), threads or usable_cpus())
+    return out
+
+
+def gen_mxfp4(set_tag: int, mat_tag: int, first: int, count: int, rows: int, K: int, std: float,
+              seed: int = 0, threads=None):
+    q = np.empty((count, rows, K // 2), dtype=np.uint8)
+    s = np.empty((count, rows, K // 32), dtype=np.uint8)
+    rc = _load().synth_mxfp4(seed, set_tag, mat_tag, first, count, rows, K, std, _ptr(q), _ptr(s),
+                             threads or usable_cpus())
+    if rc != 0:
+        raise ValueError("synth_mxfp4: bad shape")
+    return q, s
+
+
+_EXPERT_CACHE = {}
+
+
+def gen_experts(shape: MoEShape, seed: int = 0, threads=None) -> dict:
+    """Routed experts 0..E-1 and the shared expert (index E) in natural layout.
+
+    Returns gate_q/up_q [E+1][I][d/2], gate_s/up_s [E+1][I][d/32],
+    down_q [E+1][d][I/2], down_s [E+1][d][I/32] (uint8).  Cached per process.
+    """
+    key = (shape.weight_set, shape.n_experts, shape.d_model, shape.d_ff, seed)
+    if key in _EXPERT_CACHE:
+        return _EXPERT_CACHE[key]
+    st = SET_TAG[shape.weight_set]
+    E, d, I = shape.n_experts, shape.d_model, shape.d_ff
+    w = {}
+    w["gate_q"], w["gate_s"] = gen_mxfp4(st, MAT_GATE, 0, E + 1, I, d, expert_std(d), seed, threads)
+    w["up_q"], w["up_s"] = gen_mxfp4(st, MAT_UP, 0, E + 1, I, d, expert_std(d), seed, threads)
+    w["down_q"], w["down_s"] = gen_mxfp4(st, MAT_DOWN, 0, E + 1, d, I, expert_std(I), seed, threads)
+    _EXPERT_CACHE[key] = w
+    return w
+
+
+def encode_mxfp4(v: np.ndarray):
+    """Encode fp32 rows [R][K] to MXFP4 (q [R][K/2], s [R][K/32])."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    R, K = v.shape
+    assert K % 32 == 0
+    q = np.empty((R, K // 2), dtype=np.uint8)
+    s = np.empty((R, K // 32), dtype=np.uint8)
+    _load().synth_encode_mxfp4(_ptr(v), R, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def gen_tid2eid(shape: MoEShape, seed: int = 0, threads=None) -> np.ndarray:
+    out = np.empty((shape.vocab, shape.top_k), dtype=np.int32)
+    rc = _load().synth_tid2eid(seed, SET_TAG[shape.weight_set], shape.vocab, shape.n_experts, shape.top_k,
+                               _ptr(out), threads or usable_cpus())
+    if rc != 0:
+        raise ValueError("synth_tid2eid: bad shape")
+    return out
+
+
+def gen_token_ids(shape: MoEShape, seed: int = 0) -> np.ndarray:
+    out = np.empty(shape.n_rows, dtype=np.int32)
+    _load().synth_token_ids(seed, CFG_TAG[shape.name], shape.n_rows, shape.vocab, _ptr(out))
+    return out
+
+
+def gen_permutation(n: int, tag: int, seed: int = 0) -> np.ndarray:
+    out = np.empty(n, dtype=np.int32)
+    _load().synth_permutation(seed, tag, n, _ptr(out))
+    return out
+
+
+def zipf_targets(shape: MoEShape, s: float = 1.2, seed: int = 0) -> np.ndarray:
+    """Per-row selection probability per expert, q_e = min(1, c*rank_e^-s), sum q = k.
+
+    A row picks k distinct experts, so no expert can hold more than 1/k of the
+    assignments; capping q at 1 and filling the rest by rank is the closest
+    Zipf-shaped load that k-of-E selection can reach.
+    """
+    E, k = shape.n_experts, shape.top_k
+    ranks = np.arange(1, E + 1, dtype=np.float64)
+    base = ranks ** (-s)
+    lo, hi = 0.0, 1.0
+    while np.minimum(1.0, hi * base).sum() < k:
+        hi *= 2.0
+    for _ in range(200):
+        mid = 0.5 * (lo + hi)
+        if np.minimum(1.0, mid * base).sum() < k:
+            lo = mid
+        else:
+            hi = mid
+    q_rank = np.minimum(1.0, hi * base)
+    order = gen_permutation(E, 0x7A00 + CFG_TAG[shape.name], seed)  # rank i -> expert order[i]
+    q = np.empty(E, dtype=np.float64)
+    q[order] = q_rank
+    return q
+
+
+def resample_rows(shape: MoEShape, accept_rows, seed: int = 0, max_tries: int = 1000, threads=None):
+    """Draw x and redraw every row that the filter rejects.
+
+    `accept_rows(x_rows) -> bool[len(x_rows)]` is called on the rows drawn in
+    each round (all rows first, then only the redrawn ones).  A rejected row r
+    moves to its next attempt (a fresh stream of the same seed), so the
+    accepted x is a function of the seed and the filter only.
+    Returns (x, attempts).
+    """
+    attempts = np.zeros(shape.n_rows, dtype=np.int32)
+    x = gen_x(shape, seed, attempts, threads)
+    todo = np.arange(shape.n_rows)
+    for _ in range(max_tries):
+        ok = np.asarray(accept_rows(x[todo]), dtype=bool)
+        todo = todo[~ok]
+        if todo.size == 0:
+            return x, attempts
+        attempts[todo] += 1
+        x = gen_x(shape, seed, attempts, threads)
+    raise RuntimeError(f"{shape.name}: rows still rejected after {max_tries} redraws")

@@ -1,0 +1,367 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: the OCP MX format definition,
+library routines (numpy), closed forms, brute force on tiny inputs, invariants
+of the layer, and the byte counts the pages print (tests/golden/).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from mxfp4_routed_expert_sqrt_amd import synth
+from mxfp4_routed_expert_sqrt_amd.configs import SHAPES, MoEShape
+from tests.inputs import workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- formats
+
+def test_e2m1_matches_ocp_value_set():
+    # OCP MX v1.0, E2M1: values {0, 0.5, 1, 1.5, 2, 3, 4, 6} with a sign bit;
+    # max normal 6.0, min normal 1.0, only subnormal 0.5.
+    vals = [oracle.e2m1(c) for c in range(16)]
+    assert sorted(vals[:8]) == vals[:8]  # codes 0..7 increase
+    assert set(vals[:8]) == {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}
+    assert vals[8:] == [-v for v in vals[:8]]
+    assert math.copysign(1.0, vals[8]) == -1.0  # code 8 is -0
+    assert max(vals) == 6.0 and min(v for v in vals if v > 0) == 0.5
+
+
+def test_e8m0_is_power_of_two():
+    for e in range(255):
+        assert oracle.e8m0(e) == 2.0 ** (e - 127)
+    assert math.isnan(oracle.e8m0(255))
+
+
+def test_bf16_decode_matches_numpy():
+    bits = np.arange(0, 65536, 7, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        ref = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    got = np.array([oracle.bf16(int(b)) for b in bits])
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+def test_nibble_order_and_scale():
+    # element 2i is the low nibble of byte i; one scale per 32 elements
+    q = np.zeros((1, 32), dtype=np.uint8)  # K = 64
+    q[0, 0] = 0x21        # elem0 = code 1 (0.5), elem1 = code 2 (1.0)
+    q[0, 16] = 0xF7       # elem32 = code 7 (6.0), elem33 = code 15 (-6.0)
+    s = np.array([[127 + 3, 127 - 2]], dtype=np.uint8)
+    w = oracle.decode_mxfp4(q, s)[0]
+    assert w[0] == 0.5 * 8 and w[1] == 1.0 * 8
+    assert w[32] == 6.0 / 4 and w[33] == -6.0 / 4
+    assert np.count_nonzero(w) == 4
+
+
+def test_generator_encoding_roundtrips_through_decode():
+    # values already on the MXFP4 grid come back exactly (independent encoder)
+    rng = np.random.default_rng(1)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
+    v = grid[rng.integers(0, 8, (8, 64))] * rng.choice([-1, 1], (8, 64))
+    v[:, 0] = 6.0  # pin each block's max so the shared exponent is 0 ... then scale it
+    v[:, 32] = -6.0
+    scale = 2.0 ** rng.integers(-20, 20, (8, 1))
+    vv = (v * scale).astype(np.float32)
+    q, s = synth.encode_mxfp4(vv)
+    assert np.array_equal(oracle.decode_mxfp4(q, s), vv.astype(np.float64))
+
+
+def test_decoded_weight_statistics_follow_recipe():
+    sh = SHAPES["tiny"]
+    ex = synth.gen_experts(sh)
+    w = oracle.decode_mxfp4(ex["gate_q"][3], ex["gate_s"][3])
+    assert abs(w.std() * math.sqrt(sh.d_model) - 1.0) < 0.05
+    dn = oracle.decode_mxfp4(ex["down_q"][3], ex["down_s"][3])
+    assert abs(dn.std() * math.sqrt(sh.d_ff) - 1.0) < 0.05
+
+
+# ------------------------------------------------------------------ router
+
+def test_softplus_identities_and_asymptotes():
+    for z in np.linspace(-30, 30, 121):
+        assert abs(oracle.softplus(z) - oracle.softplus(-z) - z) < 1e-13
+    assert oracle.score(0.0) == pytest.approx(0.8325546111576977, abs=1e-16)  # sqrt(ln 2)
+    assert oracle.softplus(-40.0) / math.exp(-40.0) == pytest.approx(1.0, abs=1e-15)
+    assert oracle.softplus(40.0) == 40.0
+    zs = np.linspace(-20, 20, 401)
+    sp = np.array([oracle.softplus(z) for z in zs])
+    assert np.all(np.diff(sp) > 0)
+    assert np.allclose(sp, np.logaddexp(0.0, zs), rtol=1e-15, atol=0)  # numpy's log(e^0 + e^z)
+
+
+def test_router_logits_match_numpy_matmul():
+    wl = workload("tiny")
+    x = (wl["x"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = x @ wl["router_w"].astype(np.float64).T
+    z = oracle.router_logits(wl["x"], wl["router_w"])
+    assert np.allclose(z, ref, rtol=1e-12, atol=1e-14)
+    b = np.linspace(-1, 1, wl["shape"].n_experts).astype(np.float32)
+    zb = oracle.router_logits(wl["x"], wl["router_w"], b)
+    assert np.allclose(zb - z, b.astype(np.float64)[None, :], atol=1e-12)
+
+
+def test_topk_brute_force_and_argsort():
+    rng = np.random.default_rng(5)
+    for E, k in [(16, 2), (256, 6), (8, 8), (33, 1)]:
+        for _ in range(20):
+            s = rng.random(E)
+            idx, gap = oracle.topk(s, k)
+            brute = sorted(sorted(range(E), key=lambda e: -s[e])[:k])
+            assert list(idx) == brute
+            assert list(idx) == sorted(np.argsort(-s, kind="stable")[:k].tolist())
+            chosen = s[idx]
+            rest = np.delete(s, idx)
+            assert chosen.min() >= (rest.max() if rest.size else -np.inf)
+            assert len(set(idx.tolist())) == k
+            if k < E:
+                assert gap == pytest.approx(chosen.min() - rest.max(), abs=0)
+
+
+def test_topk_tie_goes_to_lower_id():
+    s = np.array([1.0, 3.0, 2.0, 3.0, 2.0, 2.0])
+    idx, gap = oracle.topk(s, 3)
+    assert list(idx) == [1, 2, 3] and gap == 0.0
+
+
+def test_gates_are_normalised_selected_scores():
+    wl = workload("tiny")
+    sh = wl["shape"]
+    z = oracle.router_logits(wl["x"], wl["router_w"])
+    idx, gates, margin = oracle.route(z, sh.top_k)
+    s = np.sqrt(np.logaddexp(0.0, z))
+    assert np.allclose(gates.sum(1), 1.0, atol=1e-15)
+    assert np.all(gates > 0)
+    sel = np.take_along_axis(s, idx.astype(np.int64), 1)
+    assert np.allclose(gates, sel / sel.sum(1, keepdims=True), rtol=1e-14)
+    assert np.all(np.diff(idx, axis=1) > 0)  # ascending expert id
+
+
+def test_hash_routing_takes_table_rows():
+    sh = MoEShape("t", 6, 64, 8, 3, 32, "hash", "tiny", vocab=5)
+    table = np.array([[7, 1, 4], [0, 2, 5], [3, 6, 1], [5, 4, 3], [2, 7, 0]], dtype=np.int32)
+    tok = np.array([4, 0, 0, 2, 3, 1], dtype=np.int32)
+    z = np.random.default_rng(0).standard_normal((6, 8))
+    idx, gates, margin = oracle.route(z, 3, "hash", tok, table)
+    for r in range(6):
+        assert list(idx[r]) == sorted(table[tok[r]].tolist())
+    s = np.sqrt(np.logaddexp(0.0, z))
+    sel = np.take_along_axis(s, idx.astype(np.int64), 1)
+    assert np.allclose(gates, sel / sel.sum(1, keepdims=True), rtol=1e-14)
+    assert np.all(np.isinf(margin))
+    bad = table.copy()
+    bad[4, 1] = 2  # duplicate id
+    with pytest.raises(ValueError):
+        oracle.route(z, 3, "hash", tok, bad)
+
+
+# -------------------------------------------------------------- bookkeeping
+
+def test_bookkeeping_brute_force():
+    rng = np.random.default_rng(2)
+    for N, k, E in [(32, 2, 16), (100, 6, 256), (7, 3, 4), (1, 1, 1)]:
+        idx = np.stack([np.sort(rng.choice(E, k, replace=False)) for _ in range(N)]).astype(np.int32)
+        counts, offsets, perm, inv = oracle.bookkeeping(idx, E)
+        # brute force: list pairs expert by expert, rows ascending
+        order = [r * k + j for e in range(E) for r in range(N) for j in range(k) if idx[r, j] == e]
+        assert perm.tolist() == order
+        assert counts.tolist() == [int((idx == e).sum()) for e in range(E)]
+        assert offsets.tolist() == [0] + np.cumsum(counts).tolist()
+        assert sorted(perm.tolist()) == list(range(N * k))
+        assert np.array_equal(inv[perm], np.arange(N * k))
+        for e in range(E):
+            seg = perm[offsets[e]:offsets[e + 1]]
+            assert np.all(idx.ravel()[seg] == e)
+            assert np.all(np.diff(seg // k) > 0)
+
+
+# ---------------------------------------------------------------- the layer
+
+def _numpy_decode(q, s):
+    """Independent vectorised MXFP4 decode (closed form of E2M1, power-of-two scales)."""
+    codes = np.stack([q & 15, q >> 4], axis=-1).reshape(*q.shape[:-1], q.shape[-1] * 2).astype(np.int64)
+    sign = np.where(codes & 8, -1.0, 1.0)
+    E = (codes >> 1) & 3
+    M = codes & 1
+    mag = np.where(E == 0, 0.5 * M, np.ldexp(1.0 + 0.5 * M, E - 1))
+    scale = np.ldexp(1.0, s.astype(np.int64) - 127)
+    return sign * mag * np.repeat(scale, 32, axis=-1)
+
+
+def _numpy_layer(shape, x_bits, w, ex, bias=None, route_scale=1.0, limit=10.0):
+    """Dense formulation: every expert on every row, masked by the routing."""
+    x = (x_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    z = x @ w.astype(np.float64).T
+    if bias is not None:
+        z = z + bias.astype(np.float64)
+    s = np.sqrt(np.logaddexp(0.0, z))
+    E, k = shape.n_experts, shape.top_k
+    top = np.sort(np.argsort(-s, axis=1, kind="stable")[:, :k], axis=1)
+    sel = np.take_along_axis(s, top, 1)
+    g = sel / sel.sum(1, keepdims=True)
+    mask = np.zeros((shape.n_rows, E))
+    np.put_along_axis(mask, top, g, 1)
+    out = np.zeros((shape.n_rows, shape.d_model))
+    for e in range(E + 1):
+        Wg = _numpy_decode(ex["gate_q"][e], ex["gate_s"][e])
+        Wu = _numpy_decode(ex["up_q"][e], ex["up_s"][e])
+        Wd = _numpy_decode(ex["down_q"][e], ex["down_s"][e])
+        a, b = x @ Wg.T, x @ Wu.T
+        if limit > 0:
+            a, b = np.minimum(a, limit), np.clip(b, -limit, limit)
+        y = (a / (1 + np.exp(-a)) * b) @ Wd.T
+        out += y if e == E else route_scale * mask[:, e:e + 1] * y
+    return out, top, g
+
+
+def test_layer_matches_dense_numpy_formulation():
+    wl = workload("tiny")
+    r = oracle.forward(wl["shape"], wl["x"], wl["router_w"], wl["experts"])
+    ref, top, g = _numpy_layer(wl["shape"], wl["x"], wl["router_w"], wl["experts"])
+    assert np.array_equal(r["idx"], top)
+    assert np.allclose(r["gates"], g, rtol=1e-13)
+    assert np.allclose(r["out"], ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
+def test_layer_matches_dense_numpy_with_bias_and_scale():
+    wl = workload("tiny")
+    sh = wl["shape"]
+    bias = np.linspace(-0.5, 0.5, sh.n_experts).astype(np.float32)[::-1].copy()
+    r = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], router_bias=bias, route_scale=1.5)
+    ref, top, _ = _numpy_layer(sh, wl["x"], wl["router_w"], wl["experts"], bias=bias, route_scale=1.5)
+    assert np.array_equal(r["idx"], top)
+    assert np.allclose(r["out"], ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
+def _single_entry_experts(sh, entries):
+    """Weights that are zero except listed (matrix, expert, row, col) = 1.0 entries."""
+    E, d, I = sh.n_experts, sh.d_model, sh.d_ff
+    ex = {}
+    for name, R, K in [("gate", I, d), ("up", I, d), ("down", d, I)]:
+        ex[name + "_q"] = np.zeros((E + 1, R, K // 2), dtype=np.uint8)
+        ex[name + "_s"] = np.full((E + 1, R, K // 32), 127, dtype=np.uint8)
+    for name, e, row, col in entries:
+        code = 2  # E2M1 code 2 is exactly 1.0; scale byte 127 is 2^0
+        ex[name + "_q"][e, row, col // 2] |= code << (4 * (col % 2))
+    return ex
+
+
+def _bf16_bits(v):
+    return (np.asarray(v, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_closed_form_single_weight_ffn():
+    # one routed expert (k=1 of 2) and the shared expert, each with one 1.0 entry per matrix:
+    # h_n = silu(x_i) * x_j and y_m = h_n, all other outputs exactly 0
+    sh = MoEShape("t", 4, 64, 2, 1, 32, "topk", "tiny", swiglu_limit=0.0)
+    ex = _single_entry_experts(sh, [("gate", 1, 5, 3), ("up", 1, 5, 10), ("down", 1, 7, 5),
+                                    ("gate", 2, 0, 1), ("up", 2, 0, 2), ("down", 2, 60, 0)])
+    x = np.zeros((4, 64), dtype=np.float32)
+    x[:, 3] = [0.5, -1.25, 2.0, 3.0]
+    x[:, 10] = [1.5, 2.0, -0.75, 0.25]
+    x[:, 1] = [1.0, -2.0, 0.375, 4.0]
+    x[:, 2] = [0.5, 0.5, -1.0, 2.0]
+    w = np.zeros((2, 64), dtype=np.float32)
+    w[1, 20] = 1.0
+    x[:, 20] = 1.0  # expert 1 wins every row: logits (0, 1)
+    r = oracle.forward(sh, _bf16_bits(x), w, ex)
+    assert np.all(r["idx"][:, 0] == 1) and np.all(r["gates"] == 1.0)
+    silu = lambda v: v / (1.0 + math.exp(-v))
+    for row in range(4):
+        exp = np.zeros(64)
+        exp[7] = silu(float(x[row, 3])) * float(x[row, 10])
+        exp[60] = silu(float(x[row, 1])) * float(x[row, 2])
+        assert np.array_equal(r["out"][row], exp)
+
+
+def test_swiglu_limit_clamps_gate_above_and_up_both_sides():
+    sh = MoEShape("t", 2, 64, 2, 1, 32, "topk", "tiny", swiglu_limit=10.0)
+    ex = _single_entry_experts(sh, [("gate", 1, 0, 3), ("up", 1, 0, 4), ("down", 1, 0, 0)])
+    x = np.zeros((2, 64), dtype=np.float32)
+    x[:, 3] = [12.0, -12.0]   # gate: 12 -> 10 ; -12 stays (no lower clamp)
+    x[:, 4] = [-15.0, 16.0]   # up: -15 -> -10 ; 16 -> 10
+    x[:, 20] = 1.0
+    w = np.zeros((2, 64), dtype=np.float32)
+    w[1, 20] = 1.0
+    r = oracle.forward(sh, _bf16_bits(x), w, ex, with_shared=False)
+    silu = lambda v: v / (1.0 + math.exp(-v))
+    assert r["out"][0, 0] == silu(10.0) * -10.0
+    assert r["out"][1, 0] == silu(-12.0) * 10.0
+    r0 = oracle.forward(sh, _bf16_bits(x), w, ex, with_shared=False, swiglu_limit=0.0)
+    assert r0["out"][0, 0] == silu(12.0) * -15.0
+
+
+def test_identical_experts_reduce_to_scaled_shared():
+    # if every routed expert equals the shared one, out = (1 + rs) * FFN(x) since sum g = 1
+    wl = workload("tiny")
+    sh = wl["shape"]
+    ex = {k: np.repeat(v[-1:], sh.n_experts + 1, axis=0) for k, v in wl["experts"].items()}
+    full = oracle.forward(sh, wl["x"], wl["router_w"], ex, route_scale=1.5)["out"]
+    shared_only = oracle.forward(sh, wl["x"], wl["router_w"], ex, route_scale=0.0)["out"]
+    assert np.allclose(full, 2.5 * shared_only, rtol=1e-13, atol=1e-15)
+
+
+def test_zero_row_gives_zero_output_and_rows_are_independent():
+    wl = workload("tiny")
+    sh = wl["shape"]
+    x = wl["x"].copy()
+    x[5] = 0
+    r = oracle.forward(sh, x, wl["router_w"], wl["experts"])
+    assert np.all(r["out"][5] == 0.0)
+    perm = np.random.default_rng(3).permutation(sh.n_rows)
+    rp = oracle.forward(sh, x[perm].copy(), wl["router_w"], wl["experts"])
+    assert np.array_equal(rp["out"], r["out"][perm])  # bit-exact row-permutation invariance
+    assert np.array_equal(rp["idx"], r["idx"][perm])
+
+
+def test_row_subset_and_thread_count_do_not_change_bits():
+    wl = workload("tiny")
+    sh = wl["shape"]
+    a = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], threads=1)
+    b = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], threads=7)
+    rows = [31, 0, 17, 17, 4]
+    c = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], rows=rows, threads=3)
+    assert np.array_equal(a["out"], b["out"])
+    assert np.array_equal(c["out"], a["out"][rows])
+    for key in ("idx", "perm", "offsets", "inv"):
+        assert np.array_equal(a[key], c[key])
+
+
+def test_constant_hash_table_routes_every_row_alike():
+    sh = MoEShape("h", 32, 256, 16, 2, 128, "hash", "tiny", vocab=50)
+    wl = workload("tiny")
+    table = np.tile(np.array([[9, 3]], dtype=np.int32), (50, 1))
+    tok = np.random.default_rng(4).integers(0, 50, 32).astype(np.int32)
+    r = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], token_ids=tok, tid2eid=table)
+    assert np.all(r["idx"] == [3, 9])
+    assert r["counts"][3] == 32 and r["counts"][9] == 32 and r["counts"].sum() == 64
+
+
+def test_tiny_workload_margins():
+    wl = workload("tiny")
+    z = oracle.router_logits(wl["x"], wl["router_w"])
+    _, _, margin = oracle.route(z, wl["shape"].top_k)
+    assert margin.min() >= 1e-3
+
+
+# -------------------------------------------------------------- byte model
+
+def test_byte_model_matches_pages():
+    with open(os.path.join(GOLDEN, "byte_model.json")) as f:
+        g = json.load(f)
+    sh = SHAPES["verify512"]
+    d, I = sh.d_model, sh.d_ff
+    per_matrix = d * I // 2 + d * I // 32  # nibbles + one E8M0 byte per 32
+    per_expert = 3 * per_matrix
+    assert per_expert == g["expert_payload_bytes"]["value"]
+    assert abs(per_expert / 1e6 - g["expert_payload_mb_printed"]["value"]) < 0.05
+    assert abs(sh.top_k * per_expert / 1e6 - g["routed_mb_per_token_printed"]["value"]) < 1.0
+    total_gib = g["layers"]["value"] * sh.n_experts * per_expert / 2 ** 30
+    assert abs(total_gib - g["routed_expert_gib_printed"]["value"]) < 0.5
+    assert abs(sh.n_experts * 3 * d * I / 1e9 - g["params_per_layer_billion_printed"]["value"]) < 0.01
