@@ -1,0 +1,163 @@
+/*
+ * moe_mxfp4.h - C ABI of the routed MoE layer on MXFP4 expert weights (gfx950).
+ *
+ * What the layer computes (one call = N token rows):
+ *   z[r][e]  = sum_i x[r][i] * W_r[e][i] (+ bias[e])          router logits
+ *   s[r][e]  = sqrt(softplus(z[r][e]))                          router scores
+ *   sel(r)   = the k experts with the largest s (top-k mode), or
+ *              tid2eid[token_ids[r]][0..k) (hash mode); listed in ascending id
+ *   g[r][j]  = s[r][sel_j] / sum_j' s[r][sel_j']                gates, sum 1
+ *   FFN_e(v) = W_down[e] (silu(min(W_gate[e] v, L)) * clamp(W_up[e] v, -L, L))
+ *   out[r]   = FFN_shared(x[r]) + route_scale * sum_j g[r][j] FFN_{sel_j}(x[r])
+ * Sources (pages on DeepSeek V4 Flash):
+ *   - top-6 of 256 routed experts plus one shared expert, sqrt-softplus routing
+ *     with hash layers: TensorSharp "DeepSeek V4 Flash (deepseek4)", intro and
+ *     "How TensorSharp runs it";
+ *   - top-k = 6, hash routing, route_scale, swiglu_limit = 10: aimarketly model
+ *     card "Deepseek-V4-Flash-Dspark-FST", "Model Architecture and Objective";
+ *   - router weight/bias and per-expert w1/w2/w3 tensors plus shared experts:
+ *     ds4 issue "DeepSeek-V4-Flash-DSpark", "Loader spec";
+ *   - MXFP4 experts as 32-value blocks with one e8m0 scale: model card
+ *     "Preprocessing"; FaStar README "Expert virtual memory"; TensorSharp
+ *     "Getting a drafter" (per-32 E8M0 scales);
+ *   - the weighted-sum epilogue over the selected experts: TensorSharp
+ *     "Fitting the model" (moe_scatter_add); shared and routed FFN paths: pypto
+ *     "DeepSeek V4-Flash, DSpark point", "MoE and output stages".
+ * The pages do not fix gate normalisation, the placement of the swiglu clamp
+ * or the bias semantics; this library normalises the selected scores to sum
+ * 1, clamps the gate from above and the up projection on both sides at L, and
+ * adds the bias to the logit before the score.
+ *
+ * Conventions for every entry point:
+ *   - Return 0 (MOE_OK) or a negative MOE_ERR_* code.  Argument validation is
+ *     done on the host before anything is enqueued: on error nothing runs.
+ *   - Device pointers are caller-owned and must stay valid until the stream
+ *     has executed the work; the library keeps no pointer after returning.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  No allocation, no host<->device copy, no host synchronisation.
+ *   - Results are bitwise reproducible for identical inputs and sizes.
+ *   - Concurrent calls are safe when their workspaces and outputs differ.
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MXFP4_VERSION 1
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = -1,     /* null/misaligned pointer, bad enum, aliasing output */
+  MOE_ERR_UNSUPPORTED = -2, /* shape outside the supported range */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or too small */
+  MOE_ERR_HIP = -4          /* a HIP launch failed */
+};
+
+enum { MOE_ROUTING_TOPK = 0, MOE_ROUTING_HASH = 1 };
+
+/* Supported shapes: d_model and d_ff multiples of 128 (>= 128, <= 65536),
+ * 1 <= n_experts <= 1024, 1 <= top_k <= min(8, n_experts),
+ * 0 <= n_rows <= MOE_MAX_ROWS. */
+#define MOE_MAX_ROWS (1 << 20)
+
+typedef struct moe_config {
+  int32_t d_model;      /* d: hidden size */
+  int32_t d_ff;         /* I: expert intermediate size */
+  int32_t n_experts;    /* E: routed experts */
+  int32_t top_k;        /* k: experts per row */
+  int32_t routing;      /* MOE_ROUTING_TOPK or MOE_ROUTING_HASH */
+  int32_t has_shared;   /* 1: one shared expert on every row; 0: none */
+  float route_scale;    /* multiplies the routed sum only (1.0 = plain sum) */
+  float swiglu_limit;   /* L; <= 0 disables the clamp */
+} moe_config_t;
+
+/*
+ * MXFP4 matrices in the library's packed layout (see moe_pack_mxfp4).  A
+ * matrix [rows][K] of E2M1 values with one E8M0 scale per 32 consecutive
+ * values along K.  Each group of n_mat matrices is stored back to back.
+ *   gate, up : routed, n_mat = E, each [I][d]   (w1 and w3 of each expert)
+ *   down     : routed, n_mat = E, each [d][I]   (w2)
+ *   sh_*     : the shared expert, n_mat = 1 (ignored when has_shared == 0)
+ * q pointers 16-byte aligned, s pointers 4-byte aligned.
+ */
+typedef struct moe_weights {
+  const void *gate_q, *gate_s;
+  const void *up_q, *up_s;
+  const void *down_q, *down_s;
+  const void *sh_gate_q, *sh_gate_s;
+  const void *sh_up_q, *sh_up_s;
+  const void *sh_down_q, *sh_down_s;
+} moe_weights_t;
+
+typedef struct moe_args {
+  int32_t n_rows;             /* N >= 0; N == 0 returns MOE_OK and enqueues nothing */
+  const void* x;              /* bf16 [N][d], row-major, 16-byte aligned */
+  const float* router_w;      /* fp32 [E][d], row-major, 16-byte aligned */
+  const float* router_bias;   /* fp32 [E] added to the logits, or NULL */
+  const int32_t* token_ids;   /* hash mode: int32 [N], each in [0, vocab) */
+  const int32_t* tid2eid;     /* hash mode: int32 [vocab][k], k distinct ids in [0, E) per row;
+                                 out-of-range or repeated ids are undefined behaviour */
+  int64_t vocab;              /* hash mode: rows of tid2eid */
+  moe_weights_t w;            /* packed expert weights */
+  void* out;                  /* bf16 [N][d], 16-byte aligned; must not overlap x */
+  /* Optional outputs (NULL to skip), for inspection of the routing:
+   *   topk_idx [N][k] int32 ascending expert ids;  topk_w [N][k] fp32 gates;
+   *   counts [E] rows per expert; offsets [E+1] exclusive prefix sum of counts;
+   *   perm [N*k]: pair index r*k+j at each expert-major position (rows ascending
+   *   within an expert); inv [N*k]: position of pair r*k+j. */
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv;
+  void* workspace;            /* device scratch, 256-byte aligned, >= moe_workspace_size() */
+  size_t workspace_bytes;
+} moe_args_t;
+
+/* Library version (MOE_MXFP4_VERSION). */
+int moe_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* moe_status_string(int status);
+
+/*
+ * Bytes of one packed MXFP4 matrix [rows][K]: rows % 16 == 0, K % 128 == 0.
+ * q_bytes = rows*K/2; s_bytes = (rows/16) * ceil(K/512) * 256.
+ */
+int moe_packed_mxfp4_bytes(int32_t rows, int32_t K, size_t* q_bytes, size_t* s_bytes);
+
+/*
+ * Re-lay n_mat MXFP4 matrices from the natural layout to the packed layout
+ * (same values, one-time weight preparation, e.g. at checkpoint load).
+ * Natural layout (device pointers): q [n_mat][rows][K/2] with element 2t in the
+ * low nibble of byte t, s [n_mat][rows][K/32], one E8M0 byte per 32 values.
+ * Packed layout, per matrix, with nks = K/128 and n_sg = ceil(nks/4):
+ *   q_out: fragment (rt, ks) for rt < rows/16, ks < nks, at byte
+ *          (rt*nks + ks)*1024; its lane l (0..63) holds 16 bytes = the 32
+ *          values of row 16*rt + l%16 in the 32-block 4*ks + l/16.
+ *   s_out: group (rt, sg) at byte (rt*n_sg + sg)*256; lane l holds 4 bytes,
+ *          byte j = the scale of row 16*rt + l%16, 32-block 4*(4*sg + j) + l/16
+ *          (127 where 4*sg + j >= nks).
+ * q/q_out 16-byte aligned, s/s_out 4-byte aligned; outputs must not overlap
+ * inputs.  Asynchronous on `stream`.
+ */
+int moe_pack_mxfp4(const void* q, const void* s, int32_t n_mat, int32_t rows, int32_t K, void* q_out,
+                   void* s_out, void* stream);
+
+/* Device workspace bytes that moe_layer_forward needs for n_rows rows. */
+int moe_workspace_size(const moe_config_t* cfg, int32_t n_rows, size_t* bytes);
+
+/* The whole layer (router, routing bookkeeping, expert FFNs, combine) on `stream`. */
+int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

@@ -1,0 +1,103 @@
+"""ctypes binding of include/moe_mxfp4.h (argument marshalling only).
+
+Every entry point has the same name and arguments as in the C header; device
+pointers are passed as integers (e.g. torch's `data_ptr()`), the stream as a
+hipStream_t integer (e.g. `torch.cuda.current_stream().cuda_stream`).  Loading
+fails loudly if the HIP library has not been built: there is no fallback.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mxfp4.so")
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ROUTING_TOPK, MOE_ROUTING_HASH = 0, 1
+MOE_MAX_ROWS = 1 << 20
+
+c_i32, c_i64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("d_model", c_i32), ("d_ff", c_i32), ("n_experts", c_i32), ("top_k", c_i32), ("routing", c_i32),
+                ("has_shared", c_i32), ("route_scale", c_f32), ("swiglu_limit", c_f32)]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [(n, c_vp) for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s", "sh_gate_q", "sh_gate_s",
+                                    "sh_up_q", "sh_up_s", "sh_down_q", "sh_down_s")]
+
+
+class MoeArgs(ctypes.Structure):
+    _fields_ = [("n_rows", c_i32), ("x", c_vp), ("router_w", c_vp), ("router_bias", c_vp), ("token_ids", c_vp),
+                ("tid2eid", c_vp), ("vocab", c_i64), ("w", MoeWeights), ("out", c_vp), ("topk_idx", c_vp),
+                ("topk_w", c_vp), ("counts", c_vp), ("offsets", c_vp), ("perm", c_vp), ("inv", c_vp),
+                ("workspace", c_vp), ("workspace_bytes", c_size)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library {LIB_PATH} is not built (run __graft_entry__.build()); "
+                               "there is no CPU fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_version.argtypes, L.moe_version.restype = [], ctypes.c_int
+        L.moe_status_string.argtypes, L.moe_status_string.restype = [ctypes.c_int], ctypes.c_char_p
+        L.moe_packed_mxfp4_bytes.argtypes = [c_i32, c_i32, ctypes.POINTER(c_size), ctypes.POINTER(c_size)]
+        L.moe_packed_mxfp4_bytes.restype = ctypes.c_int
+        L.moe_pack_mxfp4.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
+        L.moe_pack_mxfp4.restype = ctypes.c_int
+        L.moe_workspace_size.argtypes = [ctypes.POINTER(MoeConfig), c_i32, ctypes.POINTER(c_size)]
+        L.moe_workspace_size.restype = ctypes.c_int
+        L.moe_layer_forward.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeArgs), c_vp]
+        L.moe_layer_forward.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+EXPORTED = ("moe_version", "moe_status_string", "moe_packed_mxfp4_bytes", "moe_pack_mxfp4", "moe_workspace_size",
+            "moe_layer_forward")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(f"moe status {status}: {moe_status_string(status)}")
+
+
+def _check(status):
+    if status != MOE_OK:
+        raise MoeError(status)
+    return status
+
+
+def moe_version() -> int:
+    return lib().moe_version()
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def moe_packed_mxfp4_bytes(rows: int, K: int):
+    q, s = c_size(), c_size()
+    _check(lib().moe_packed_mxfp4_bytes(rows, K, ctypes.byref(q), ctypes.byref(s)))
+    return q.value, s.value
+
+
+def moe_pack_mxfp4(q, s, n_mat, rows, K, q_out, s_out, stream) -> int:
+    return lib().moe_pack_mxfp4(q, s, n_mat, rows, K, q_out, s_out, stream)
+
+
+def moe_workspace_size(cfg: MoeConfig, n_rows: int) -> int:
+    b = c_size()
+    _check(lib().moe_workspace_size(ctypes.byref(cfg), n_rows, ctypes.byref(b)))
+    return b.value
+
+
+def moe_layer_forward(cfg: MoeConfig, args: MoeArgs, stream) -> int:
+    return lib().moe_layer_forward(ctypes.byref(cfg), ctypes.byref(args), stream)

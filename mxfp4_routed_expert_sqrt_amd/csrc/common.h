@@ -1,0 +1,81 @@
+// Device helpers shared by the gfx950 kernels of the routed MoE layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kGroupRows = 32;   // token rows of one grouped-GEMM work unit
+constexpr int kFeatPerWave = 32; // output features of one wave in the expert GEMMs
+constexpr int kWavesPerWG = 4;
+constexpr int kFeatPerWG = kFeatPerWave * kWavesPerWG;
+constexpr int kXcds = 8;         // gfx950: workgroups are dealt round-robin to 8 XCDs
+
+// One work unit of the grouped GEMMs: rows [p0, p0 + cnt) of expert e.
+struct Group {
+  int32_t e, p0, cnt, pad;
+};
+
+// Maps this workgroup to a work unit so that each XCD receives a contiguous
+// range of units (units of one group share activations in that XCD's L2).
+// Returns false for workgroups beyond the device-side unit count.
+__device__ __forceinline__ bool xcd_unit(int n_units, int* unit) {
+  const int bid = blockIdx.x;
+  const int xcd = bid % kXcds, slot = bid / kXcds;
+  const int per = (n_units + kXcds - 1) / kXcds;
+  if (slot >= per) return false;
+  const int u = xcd * per + slot;
+  if (u >= n_units) return false;
+  *unit = u;
+  return true;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Shared exponent for a two-term FP8 (E4M3) split of a block whose largest
+// magnitude is amax: amax / 2^e lands in [128, 256), inside E4M3's normal range
+// (max 448), so no element saturates.  Clamped to the E8M0 range.
+__device__ __forceinline__ int split_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int ex;
+  frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1)
+  int e = ex - 1 - 7;
+  e = e < -127 ? -127 : e;
+  e = e > 127 ? 127 : e;
+  return e;
+}
+
+// 4 floats -> 4 E4M3 bytes (round to nearest even), packed little-endian.
+__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
+__device__ __forceinline__ float fp8_byte_to_f32(uint32_t word, int byte) {
+  switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)word, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)word, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)word, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)word, 3);
+  }
+}
+
+template <int kOff>
+__device__ __forceinline__ float shfl_xor_max(float v) {
+  return fmaxf(v, __shfl_xor(v, kOff, kWave));
+}
+
+}  // namespace moe

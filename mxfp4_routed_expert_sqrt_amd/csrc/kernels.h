@@ -1,0 +1,69 @@
+// Launch wrappers of the gfx950 kernels (host side).  All launches are
+// asynchronous on `stream`; shapes are validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace moe {
+
+// Packed-layout sizes of one MXFP4 matrix [rows][K] (rows % 16 == 0, K % 128 == 0).
+__host__ __device__ inline size_t packed_q_bytes(int rows, int K) { return (size_t)rows * (size_t)(K / 2); }
+__host__ __device__ inline size_t packed_s_bytes(int rows, int K) {
+  const int nks = K / 128, n_sg = (nks + 3) / 4;
+  return (size_t)(rows / 16) * (size_t)n_sg * 256;
+}
+// Two-term FP8 split of activation rows of length K.
+__host__ __device__ inline size_t split_q_row_bytes(int K) { return (size_t)K * 2; }
+__host__ __device__ inline size_t split_s_row_bytes(int K) {
+  const int nks = K / 128, n_sg = (nks + 3) / 4;
+  return (size_t)2 * n_sg * 16;
+}
+
+hipError_t launch_pack_mxfp4(const uint8_t* q, const uint8_t* s, int n_mat, int rows, int K, uint8_t* q_out,
+                             uint8_t* s_out, hipStream_t stream);
+
+hipError_t launch_split_bf16(const uint16_t* x, int n_rows, int K, uint8_t* xq, uint8_t* xs, hipStream_t stream);
+
+hipError_t launch_router_logits(const uint16_t* x, const float* w, const float* bias, int n_rows, int d, int E,
+                                float* z, hipStream_t stream);
+
+hipError_t launch_select(const float* z, int n_rows, int E, int k, int routing, const int32_t* token_ids,
+                         const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, hipStream_t stream);
+
+hipError_t launch_route(const int32_t* idx, int n_rows, int k, int E, int has_shared, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* inv, Group* groups, int32_t* n_groups,
+                        hipStream_t stream);
+
+struct ExpertArgs {
+  // weights of the routed experts (E matrices) and of the shared expert
+  const uint8_t *q0, *s0, *q1, *s1;      // gate/up: q0/s0 gate, q1/s1 up; down: q0/s0
+  const uint8_t *sq0, *ss0, *sq1, *ss1;  // shared expert, same roles
+  const uint8_t* aq;                     // activation split bytes (x for gate/up, h for down)
+  const uint8_t* as;                     // activation split scales
+  const int32_t* perm;                   // expert-major pair -> r*k + j
+  const Group* groups;
+  const int32_t* n_groups;
+  int K, R;                              // contraction length, rows of each weight matrix
+  int E, k, P;                           // experts, top-k, routed pairs (N*k)
+  float limit;                           // swiglu limit (<= 0: none)
+  uint8_t* hq;                           // gate/up output: split h bytes
+  uint8_t* hs;                           // gate/up output: split h scales
+  float* y;                              // down output [pairs][R]
+};
+
+hipError_t launch_gateup(const ExpertArgs& a, int max_groups, hipStream_t stream);
+hipError_t launch_down(const ExpertArgs& a, int max_groups, hipStream_t stream);
+
+hipError_t launch_combine(const float* y, const int32_t* inv, const float* gates, int n_rows, int d, int k,
+                          int P, int has_shared, float route_scale, uint16_t* out, hipStream_t stream);
+
+// Worst-case number of work groups for n_rows rows: sum_e ceil(c_e/32) <= ceil(P/32) + E, plus the shared rows.
+inline int max_work_groups(int n_rows, int k, int E, int has_shared) {
+  const long P = (long)n_rows * k;
+  return (int)((P + kGroupRows - 1) / kGroupRows + E + (has_shared ? (n_rows + kGroupRows - 1) / kGroupRows : 0));
+}
+
+}  // namespace moe

@@ -1,0 +1,232 @@
+// C-ABI entry points of the routed MoE layer: validation, workspace layout and
+// the launch sequence on the caller's stream.
+#include <string.h>
+
+#include "kernels.h"
+#include "moe_mxfp4.h"
+
+using namespace moe;
+
+namespace {
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, xq, xs, hq, hs, y, total;
+  int max_groups;
+};
+
+// Workspace carve-up; every region starts on a 256-byte boundary.
+Layout make_layout(const moe_config_t& c, int n) {
+  Layout L;
+  const size_t N = (size_t)n, E = (size_t)c.n_experts, k = (size_t)c.top_k;
+  const size_t P = N * k, Ptot = P + (c.has_shared ? N : 0);
+  L.max_groups = max_work_groups(n, c.top_k, c.n_experts, c.has_shared);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L.z = take(N * E * 4);
+  L.idx = take(P * 4);
+  L.gates = take(P * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm = take(P * 4);
+  L.inv = take(P * 4);
+  L.groups = take((size_t)L.max_groups * sizeof(Group));
+  L.n_groups = take(4);
+  L.xq = take(N * split_q_row_bytes(c.d_model));
+  L.xs = take(N * split_s_row_bytes(c.d_model));
+  L.hq = take(Ptot * split_q_row_bytes(c.d_ff));
+  L.hs = take(Ptot * split_s_row_bytes(c.d_ff));
+  L.y = take(Ptot * (size_t)c.d_model * 4);
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int check_config(const moe_config_t* c) {
+  if (!c) return MOE_ERR_INVALID;
+  if (c->routing != MOE_ROUTING_TOPK && c->routing != MOE_ROUTING_HASH) return MOE_ERR_INVALID;
+  if (c->has_shared != 0 && c->has_shared != 1) return MOE_ERR_INVALID;
+  if (c->d_model < 128 || c->d_model > 65536 || c->d_model % 128) return MOE_ERR_UNSUPPORTED;
+  if (c->d_ff < 128 || c->d_ff > 65536 || c->d_ff % 128) return MOE_ERR_UNSUPPORTED;
+  if (c->n_experts < 1 || c->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
+  if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts) return MOE_ERR_UNSUPPORTED;
+  if (!(c->route_scale == c->route_scale) || !(c->swiglu_limit == c->swiglu_limit)) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+int check_mat(const void* q, const void* s) {
+  if (!q || !s) return MOE_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(s, 4)) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return MOE_MXFP4_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_packed_mxfp4_bytes(int32_t rows, int32_t K, size_t* q_bytes, size_t* s_bytes) {
+  if (!q_bytes || !s_bytes) return MOE_ERR_INVALID;
+  if (rows < 16 || rows % 16 || K < 128 || K % 128) return MOE_ERR_UNSUPPORTED;
+  *q_bytes = packed_q_bytes(rows, K);
+  *s_bytes = packed_s_bytes(rows, K);
+  return MOE_OK;
+}
+
+int moe_pack_mxfp4(const void* q, const void* s, int32_t n_mat, int32_t rows, int32_t K, void* q_out, void* s_out,
+                   void* stream) {
+  if (n_mat < 0) return MOE_ERR_INVALID;
+  if (rows < 16 || rows % 16 || K < 128 || K % 128 || rows > 65536 || K > 65536) return MOE_ERR_UNSUPPORTED;
+  if (n_mat == 0) return MOE_OK;
+  if (!q || !s || !q_out || !s_out) return MOE_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(q_out, 16) || !aligned(s_out, 4)) return MOE_ERR_INVALID;
+  const size_t nq = (size_t)n_mat * packed_q_bytes(rows, K);
+  const size_t ns_in = (size_t)n_mat * rows * (K / 32), ns_out = (size_t)n_mat * packed_s_bytes(rows, K);
+  if (overlap(q, nq, q_out, nq) || overlap(s, ns_in, s_out, ns_out) || overlap(q, nq, s_out, ns_out) ||
+      overlap(s, ns_in, q_out, nq))
+    return MOE_ERR_INVALID;
+  hipError_t err = launch_pack_mxfp4((const uint8_t*)q, (const uint8_t*)s, n_mat, rows, K, (uint8_t*)q_out,
+                                     (uint8_t*)s_out, (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_workspace_size(const moe_config_t* cfg, int32_t n_rows, size_t* bytes) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!bytes || n_rows < 0) return MOE_ERR_INVALID;
+  if (n_rows > MOE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
+  *bytes = n_rows == 0 ? 0 : make_layout(*cfg, n_rows).total;
+  return MOE_OK;
+}
+
+int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* stream_) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!args) return MOE_ERR_INVALID;
+  const moe_config_t& c = *cfg;
+  const moe_args_t& a = *args;
+  const int N = a.n_rows;
+  if (N < 0) return MOE_ERR_INVALID;
+  if (N > MOE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
+  if (N == 0) return MOE_OK;
+  const int d = c.d_model, I = c.d_ff, E = c.n_experts, k = c.top_k;
+  if (!a.x || !a.router_w || !a.out) return MOE_ERR_INVALID;
+  if (!aligned(a.x, 16) || !aligned(a.router_w, 16) || !aligned(a.out, 16)) return MOE_ERR_INVALID;
+  if (a.router_bias && !aligned(a.router_bias, 4)) return MOE_ERR_INVALID;
+  if ((rc = check_mat(a.w.gate_q, a.w.gate_s)) || (rc = check_mat(a.w.up_q, a.w.up_s)) ||
+      (rc = check_mat(a.w.down_q, a.w.down_s)))
+    return rc;
+  if (c.has_shared && ((rc = check_mat(a.w.sh_gate_q, a.w.sh_gate_s)) || (rc = check_mat(a.w.sh_up_q, a.w.sh_up_s)) ||
+                       (rc = check_mat(a.w.sh_down_q, a.w.sh_down_s))))
+    return rc;
+  if (c.routing == MOE_ROUTING_HASH) {
+    if (!a.token_ids || !a.tid2eid || a.vocab < 1 || !aligned(a.token_ids, 4) || !aligned(a.tid2eid, 4))
+      return MOE_ERR_INVALID;
+  }
+  const void* opt[] = {a.topk_idx, a.topk_w, a.counts, a.offsets, a.perm, a.inv};
+  for (const void* p : opt)
+    if (p && !aligned(p, 4)) return MOE_ERR_INVALID;
+  const size_t out_bytes = (size_t)N * d * 2;
+  if (overlap(a.out, out_bytes, a.x, out_bytes)) return MOE_ERR_INVALID;
+  const Layout L = make_layout(c, N);
+  if (!a.workspace || a.workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(a.workspace, 256)) return MOE_ERR_INVALID;
+  if (overlap(a.out, out_bytes, a.workspace, L.total)) return MOE_ERR_INVALID;
+
+  hipStream_t stream = (hipStream_t)stream_;
+  uint8_t* ws = (uint8_t*)a.workspace;
+  float* z = (float*)(ws + L.z);
+  int32_t* idx = a.topk_idx ? a.topk_idx : (int32_t*)(ws + L.idx);
+  float* gates = a.topk_w ? a.topk_w : (float*)(ws + L.gates);
+  int32_t* counts = a.counts ? a.counts : (int32_t*)(ws + L.counts);
+  int32_t* offsets = a.offsets ? a.offsets : (int32_t*)(ws + L.offsets);
+  int32_t* perm = a.perm ? a.perm : (int32_t*)(ws + L.perm);
+  int32_t* inv = a.inv ? a.inv : (int32_t*)(ws + L.inv);
+  Group* groups = (Group*)(ws + L.groups);
+  int32_t* n_groups = (int32_t*)(ws + L.n_groups);
+  uint8_t *xq = ws + L.xq, *xs = ws + L.xs, *hq = ws + L.hq, *hs = ws + L.hs;
+  float* y = (float*)(ws + L.y);
+  const int P = N * k;
+
+  hipError_t err;
+  if ((err = launch_split_bf16((const uint16_t*)a.x, N, d, xq, xs, stream)) != hipSuccess) return MOE_ERR_HIP;
+  if ((err = launch_router_logits((const uint16_t*)a.x, a.router_w, a.router_bias, N, d, E, z, stream)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  if ((err = launch_select(z, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, stream)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  if ((err = launch_route(idx, N, k, E, c.has_shared, counts, offsets, perm, inv, groups, n_groups, stream)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+
+  ExpertArgs ga;
+  memset(&ga, 0, sizeof(ga));
+  ga.q0 = (const uint8_t*)a.w.gate_q;
+  ga.s0 = (const uint8_t*)a.w.gate_s;
+  ga.q1 = (const uint8_t*)a.w.up_q;
+  ga.s1 = (const uint8_t*)a.w.up_s;
+  ga.sq0 = (const uint8_t*)a.w.sh_gate_q;
+  ga.ss0 = (const uint8_t*)a.w.sh_gate_s;
+  ga.sq1 = (const uint8_t*)a.w.sh_up_q;
+  ga.ss1 = (const uint8_t*)a.w.sh_up_s;
+  ga.aq = xq;
+  ga.as = xs;
+  ga.perm = perm;
+  ga.groups = groups;
+  ga.n_groups = n_groups;
+  ga.K = d;
+  ga.R = I;
+  ga.E = E;
+  ga.k = k;
+  ga.P = P;
+  ga.limit = c.swiglu_limit;
+  ga.hq = hq;
+  ga.hs = hs;
+  if ((err = launch_gateup(ga, L.max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
+
+  ExpertArgs da = ga;
+  da.q0 = (const uint8_t*)a.w.down_q;
+  da.s0 = (const uint8_t*)a.w.down_s;
+  da.q1 = da.s1 = nullptr;
+  da.sq0 = (const uint8_t*)a.w.sh_down_q;
+  da.ss0 = (const uint8_t*)a.w.sh_down_s;
+  da.sq1 = da.ss1 = nullptr;
+  da.aq = hq;
+  da.as = hs;
+  da.K = I;
+  da.R = d;
+  da.hq = da.hs = nullptr;
+  da.y = y;
+  if ((err = launch_down(da, L.max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
+
+  if ((err = launch_combine(y, inv, gates, N, d, k, P, c.has_shared, c.route_scale, (uint16_t*)a.out, stream)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

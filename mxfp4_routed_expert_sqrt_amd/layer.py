@@ -1,0 +1,114 @@
+"""Thin torch-side wrapper of the C ABI: torch supplies device memory and the
+stream, every step of the layer runs in the HIP library.
+"""
+import numpy as np
+import torch
+
+from . import capi
+from .configs import MoEShape
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def make_config(shape: MoEShape, has_shared: bool = True, route_scale=None, swiglu_limit=None) -> capi.MoeConfig:
+    return capi.MoeConfig(shape.d_model, shape.d_ff, shape.n_experts, shape.top_k,
+                          capi.MOE_ROUTING_TOPK if shape.routing == "topk" else capi.MOE_ROUTING_HASH,
+                          1 if has_shared else 0,
+                          float(shape.route_scale if route_scale is None else route_scale),
+                          float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit))
+
+
+def pack_mxfp4(q: torch.Tensor, s: torch.Tensor, rows: int, K: int, stream=None):
+    """Natural-layout device tensors q [n][rows][K/2], s [n][rows][K/32] -> packed (q, s) device tensors."""
+    n = q.shape[0]
+    qb, sb = capi.moe_packed_mxfp4_bytes(rows, K)
+    q_out = torch.empty(n * qb, dtype=torch.uint8, device=q.device)
+    s_out = torch.empty(n * sb, dtype=torch.uint8, device=q.device)
+    st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    rc = capi.moe_pack_mxfp4(q.data_ptr(), s.data_ptr(), n, rows, K, q_out.data_ptr(), s_out.data_ptr(), st)
+    if rc != capi.MOE_OK:
+        raise capi.MoeError(rc)
+    return q_out, s_out
+
+
+class PackedExperts:
+    """Routed experts 0..E-1 and the shared expert (index E), packed on the device."""
+
+    def __init__(self, experts: dict, shape: MoEShape, device, has_shared: bool = True):
+        E, d, I = shape.n_experts, shape.d_model, shape.d_ff
+        self.t = {}
+        for name, rows, K in (("gate", I, d), ("up", I, d), ("down", d, I)):
+            q = torch.from_numpy(np.ascontiguousarray(experts[name + "_q"])).to(device)
+            s = torch.from_numpy(np.ascontiguousarray(experts[name + "_s"])).to(device)
+            self.t[name] = pack_mxfp4(q[:E], s[:E], rows, K)
+            if has_shared:
+                self.t["sh_" + name] = pack_mxfp4(q[E:E + 1], s[E:E + 1], rows, K)
+            del q, s
+        torch.cuda.synchronize(device)
+        self.has_shared = has_shared
+
+    def weights(self, with_shared: bool = True) -> capi.MoeWeights:
+        t = self.t
+        sh = (lambda n, i: _ptr(t["sh_" + n][i])) if (self.has_shared and with_shared) else (lambda n, i: None)
+        return capi.MoeWeights(_ptr(t["gate"][0]), _ptr(t["gate"][1]), _ptr(t["up"][0]), _ptr(t["up"][1]),
+                               _ptr(t["down"][0]), _ptr(t["down"][1]), sh("gate", 0), sh("gate", 1), sh("up", 0),
+                               sh("up", 1), sh("down", 0), sh("down", 1))
+
+
+class MoELayer:
+    def __init__(self, shape: MoEShape, router_w, experts, device="cuda", router_bias=None,
+                 has_shared: bool = True, route_scale=None, swiglu_limit=None):
+        """experts: natural-layout arrays (dict, packed here) or an already packed PackedExperts."""
+        self.shape = shape
+        self.device = torch.device(device)
+        self.cfg = make_config(shape, has_shared, route_scale, swiglu_limit)
+        self.router_w = torch.as_tensor(np.ascontiguousarray(router_w, dtype=np.float32)).to(self.device)
+        self.router_bias = None if router_bias is None else \
+            torch.as_tensor(np.ascontiguousarray(router_bias, dtype=np.float32)).to(self.device)
+        if isinstance(experts, PackedExperts):
+            if has_shared and not experts.has_shared:
+                raise ValueError("packed experts carry no shared expert")
+            self.experts = experts
+        else:
+            self.experts = PackedExperts(experts, shape, self.device, has_shared)
+        self.has_shared = has_shared
+
+    def workspace_bytes(self, n_rows: int) -> int:
+        return capi.moe_workspace_size(self.cfg, n_rows)
+
+    def new_workspace(self, n_rows: int) -> torch.Tensor:
+        return torch.empty(max(self.workspace_bytes(n_rows), 256), dtype=torch.uint8, device=self.device)
+
+    def args(self, x, out, workspace, token_ids=None, tid2eid=None, routing=None) -> capi.MoeArgs:
+        N = x.shape[0]
+        r = routing or {}
+        return capi.MoeArgs(N, _ptr(x), _ptr(self.router_w), _ptr(self.router_bias), _ptr(token_ids), _ptr(tid2eid),
+                            0 if tid2eid is None else tid2eid.shape[0], self.experts.weights(self.has_shared), _ptr(out),
+                            _ptr(r.get("topk_idx")), _ptr(r.get("topk_w")), _ptr(r.get("counts")),
+                            _ptr(r.get("offsets")), _ptr(r.get("perm")), _ptr(r.get("inv")), _ptr(workspace),
+                            0 if workspace is None else workspace.numel())
+
+    def forward(self, x: torch.Tensor, token_ids=None, tid2eid=None, out=None, workspace=None, with_routing=False,
+                stream=None):
+        """x: bf16 [N][d] on the device.  Returns out (bf16 [N][d]) or (out, routing dict)."""
+        N, k, E = x.shape[0], self.shape.top_k, self.shape.n_experts
+        if out is None:
+            out = torch.empty_like(x)
+        if workspace is None:
+            workspace = self.new_workspace(N)
+        routing = None
+        if with_routing:
+            dev = self.device
+            routing = dict(topk_idx=torch.empty((N, k), dtype=torch.int32, device=dev),
+                           topk_w=torch.empty((N, k), dtype=torch.float32, device=dev),
+                           counts=torch.empty(E, dtype=torch.int32, device=dev),
+                           offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                           perm=torch.empty(N * k, dtype=torch.int32, device=dev),
+                           inv=torch.empty(N * k, dtype=torch.int32, device=dev))
+        st = torch.cuda.current_stream(self.device).cuda_stream if stream is None else stream
+        rc = capi.moe_layer_forward(self.cfg, self.args(x, out, workspace, token_ids, tid2eid, routing), st)
+        if rc != capi.MOE_OK:
+            raise capi.MoeError(rc)
+        return (out, routing) if with_routing else out

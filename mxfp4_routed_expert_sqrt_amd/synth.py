@@ -18,6 +18,7 @@ Recipe (seed 0 unless stated):
 """
 import ctypes
 import os
+import zlib
 
 import numpy as np
 
@@ -28,6 +29,14 @@ _LIB_PATH = os.path.join(_HERE, "libmoe_synth.so")
 _lib = None
 
 MAT_GATE, MAT_UP, MAT_DOWN = 1, 2, 3
+
+
+def _cfg_tag(shape: MoEShape) -> int:
+    return CFG_TAG[shape.name] if shape.name in CFG_TAG else 1000 + zlib.crc32(shape.name.encode())
+
+
+def _set_tag(shape: MoEShape) -> int:
+    return SET_TAG[shape.weight_set] if shape.weight_set in SET_TAG else 2000 + zlib.crc32(shape.weight_set.encode())
 
 
 def usable_cpus() -> int:
@@ -75,14 +84,14 @@ def gen_x(shape: MoEShape, seed: int = 0, attempts=None, threads=None) -> np.nda
     if attempts is not None:
         att = np.ascontiguousarray(attempts, dtype=np.int32)
         assert att.shape == (shape.n_rows,)
-    _load().synth_x_bf16(seed, CFG_TAG[shape.name], shape.n_rows, shape.d_model,
+    _load().synth_x_bf16(seed, _cfg_tag(shape), shape.n_rows, shape.d_model,
                          _ptr(att) if att is not None else None, _ptr(out), threads or usable_cpus())
     return out
 
 
 def gen_router(shape: MoEShape, seed: int = 0, threads=None) -> np.ndarray:
     out = np.empty((shape.n_experts, shape.d_model), dtype=np.float32)
-    _load().synth_router_f32(seed, SET_TAG[shape.weight_set], shape.n_experts, shape.d_model,
+    _load().synth_router_f32(seed, _set_tag(shape), shape.n_experts, shape.d_model,
                              ROUTER_STD, _ptr(out), threads or usable_cpus())
     return out
 
@@ -110,7 +119,7 @@ def gen_experts(shape: MoEShape, seed: int = 0, threads=None) -> dict:
     key = (shape.weight_set, shape.n_experts, shape.d_model, shape.d_ff, seed)
     if key in _EXPERT_CACHE:
         return _EXPERT_CACHE[key]
-    st = SET_TAG[shape.weight_set]
+    st = _set_tag(shape)
     E, d, I = shape.n_experts, shape.d_model, shape.d_ff
     w = {}
     w["gate_q"], w["gate_s"] = gen_mxfp4(st, MAT_GATE, 0, E + 1, I, d, expert_std(d), seed, threads)
@@ -133,7 +142,7 @@ def encode_mxfp4(v: np.ndarray):
 
 def gen_tid2eid(shape: MoEShape, seed: int = 0, threads=None) -> np.ndarray:
     out = np.empty((shape.vocab, shape.top_k), dtype=np.int32)
-    rc = _load().synth_tid2eid(seed, SET_TAG[shape.weight_set], shape.vocab, shape.n_experts, shape.top_k,
+    rc = _load().synth_tid2eid(seed, _set_tag(shape), shape.vocab, shape.n_experts, shape.top_k,
                                _ptr(out), threads or usable_cpus())
     if rc != 0:
         raise ValueError("synth_tid2eid: bad shape")
@@ -142,7 +151,7 @@ def gen_tid2eid(shape: MoEShape, seed: int = 0, threads=None) -> np.ndarray:
 
 def gen_token_ids(shape: MoEShape, seed: int = 0) -> np.ndarray:
     out = np.empty(shape.n_rows, dtype=np.int32)
-    _load().synth_token_ids(seed, CFG_TAG[shape.name], shape.n_rows, shape.vocab, _ptr(out))
+    _load().synth_token_ids(seed, _cfg_tag(shape), shape.n_rows, shape.vocab, _ptr(out))
     return out
 
 
@@ -172,7 +181,7 @@ def zipf_targets(shape: MoEShape, s: float = 1.2, seed: int = 0) -> np.ndarray:
         else:
             hi = mid
     q_rank = np.minimum(1.0, hi * base)
-    order = gen_permutation(E, 0x7A00 + CFG_TAG[shape.name], seed)  # rank i -> expert order[i]
+    order = gen_permutation(E, 0x7A00 + _cfg_tag(shape), seed)  # rank i -> expert order[i]
     q = np.empty(E, dtype=np.float64)
     q[order] = q_rank
     return q

@@ -1,0 +1,58 @@
+// Single-wave probes of the gfx950 instructions the expert kernels rely on:
+// the scaled FP4 x FP8 MFMA (operand lane layout, scale byte selection, result
+// layout) and the FP8 (E4M3) conversions.  Test-only; every access is within
+// the 64-lane buffers the host passes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../mxfp4_routed_expert_sqrt_amd/csrc/common.h"
+
+using namespace moe;
+
+template <int JA, int JB, int FA, int FB>
+__global__ void probe_mfma_kernel(const u32x4* a, const u32x4* b, const uint32_t* sa, const uint32_t* sb, v4f* d) {
+  const int l = threadIdx.x;
+  const u32x4 a0 = a[2 * l], a1 = a[2 * l + 1];
+  const u32x4 b0 = b[2 * l], b1 = b[2 * l + 1];
+  const v8i av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const v8i bv = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  v4f c = {0.f, 0.f, 0.f, 0.f};
+  d[l] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, FA, FB, JA, (int)sa[l], JB, (int)sb[l]);
+}
+
+__global__ void probe_fp8_kernel(const float* in, uint32_t* packed, float* back, int n4) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const uint32_t w = pack4_fp8(in[4 * i], in[4 * i + 1], in[4 * i + 2], in[4 * i + 3]);
+  packed[i] = w;
+  for (int b = 0; b < 4; ++b) back[4 * i + b] = fp8_byte_to_f32(w, b);
+}
+
+// a, b: 64 lanes x 32 bytes; sa, sb: 64 dwords; d: 64 x 4 floats.
+// variant 0: A E2M1, B E4M3, scale bytes 0/0; 1: same with scale bytes 2 (A) / 1 (B);
+// variant 2: A E2M1, B E2M1, scale bytes 0/0.
+extern "C" int probe_mfma(const void* a, const void* b, const void* sa, const void* sb, void* d, int variant) {
+  const u32x4* A = (const u32x4*)a;
+  const u32x4* B = (const u32x4*)b;
+  const uint32_t* SA = (const uint32_t*)sa;
+  const uint32_t* SB = (const uint32_t*)sb;
+  v4f* D = (v4f*)d;
+  if (variant == 0)
+    hipLaunchKernelGGL((probe_mfma_kernel<0, 0, 4, 0>), dim3(1), dim3(64), 0, 0, A, B, SA, SB, D);
+  else if (variant == 1)
+    hipLaunchKernelGGL((probe_mfma_kernel<2, 1, 4, 0>), dim3(1), dim3(64), 0, 0, A, B, SA, SB, D);
+  else if (variant == 2)
+    hipLaunchKernelGGL((probe_mfma_kernel<0, 0, 4, 4>), dim3(1), dim3(64), 0, 0, A, B, SA, SB, D);
+  else
+    return -1;
+  if (hipGetLastError() != hipSuccess) return -4;
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -4;
+}
+
+extern "C" int probe_fp8(const void* in, void* packed, void* back, int n4) {
+  if (n4 <= 0) return 0;
+  hipLaunchKernelGGL(probe_fp8_kernel, dim3((n4 + 255) / 256), dim3(256), 0, 0, (const float*)in, (uint32_t*)packed,
+                     (float*)back, n4);
+  if (hipGetLastError() != hipSuccess) return -4;
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -4;
+}

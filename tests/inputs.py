@@ -9,6 +9,7 @@ making the routing decisions:
   b_e += ln q_e - ln max(q_hat_e, 1/(2N)) on the workload's x, then frozen.
 """
 import functools
+import time
 
 import numpy as np
 
@@ -32,11 +33,17 @@ def calibrate_zipf_bias(shape, x, w, steps=30, seed=0):
 
 
 @functools.lru_cache(maxsize=None)
-def workload(name: str, seed: int = 0):
-    """dict(shape, x, router_w, bias, token_ids, tid2eid, experts, attempts)."""
-    shape = SHAPES[name]
+def workload(name, seed: int = 0, x_scale: float = 1.0):
+    """dict(shape, x, router_w, bias, token_ids, tid2eid, experts, attempts).
+
+    name: a workload name or a MoEShape.  x_scale (a power of two) multiplies
+    the drawn x exactly before the margin filter (used to make the swiglu clamp bind).
+    """
+    shape = SHAPES[name] if isinstance(name, str) else name
+    t0 = time.time()
     w = synth.gen_router(shape, seed)
     experts = synth.gen_experts(shape, seed)
+    print(f"[inputs] {shape.name}: weights ready in {time.time() - t0:.1f}s", flush=True)
     bias = token_ids = tid2eid = None
     if shape.routing == "hash":
         x = synth.gen_x(shape, seed)
@@ -52,9 +59,24 @@ def workload(name: str, seed: int = 0):
             _, _, margin = oracle.route(z, shape.top_k)
             return margin >= MIN_MARGIN
 
-        x, attempts = synth.resample_rows(shape, accept, seed)
+        if x_scale != 1.0:
+            def accept_scaled(rows, _acc=accept):
+                return _acc(_scale_bf16(rows, x_scale))
+            x, attempts = synth.resample_rows(shape, accept_scaled, seed)
+        else:
+            x, attempts = synth.resample_rows(shape, accept, seed)
+    if x_scale != 1.0:
+        x = _scale_bf16(x, x_scale)
+    print(f"[inputs] {shape.name}: x ready ({int((attempts > 0).sum())} rows redrawn) after "
+          f"{time.time() - t0:.1f}s", flush=True)
     return dict(shape=shape, x=x, router_w=w, bias=bias, token_ids=token_ids, tid2eid=tid2eid,
                 experts=experts, attempts=attempts)
+
+
+def _scale_bf16(x_bits, factor):
+    """Multiply bf16 bit patterns by a power of two (exact while in range)."""
+    f = (x_bits.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
 
 
 def oracle_forward(wl, rows=None, **kw):

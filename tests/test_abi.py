@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+that include/*.h declares, and rejects invalid arguments on the host before
+any HIP call (nothing is enqueued, so no device is needed)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from mxfp4_routed_expert_sqrt_amd import capi
+from mxfp4_routed_expert_sqrt_amd.configs import SHAPES
+from mxfp4_routed_expert_sqrt_amd.layer import make_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    lib = capi.lib()
+    names = declared_functions()
+    assert "moe_layer_forward" in names and "moe_workspace_size" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(capi.EXPORTED)
+
+
+def test_version_and_status_strings():
+    assert capi.moe_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert capi.moe_status_string(st) != "unknown status"
+    assert capi.moe_status_string(7) == "unknown status"
+
+
+def test_packed_sizes():
+    # q keeps the natural byte count; scales are padded to whole 4-k-step groups
+    assert capi.moe_packed_mxfp4_bytes(2048, 4096) == (2048 * 2048, 128 * 8 * 256)
+    assert capi.moe_packed_mxfp4_bytes(4096, 2048) == (4096 * 1024, 256 * 4 * 256)
+    assert capi.moe_packed_mxfp4_bytes(128, 256) == (128 * 128, 8 * 1 * 256)
+    with pytest.raises(capi.MoeError):
+        capi.moe_packed_mxfp4_bytes(24, 256)
+    with pytest.raises(capi.MoeError):
+        capi.moe_packed_mxfp4_bytes(32, 96)
+
+
+def test_workspace_size_arithmetic():
+    sh = SHAPES["verify512"]
+    cfg = make_config(sh)
+    b = capi.moe_workspace_size(cfg, 512)
+    N, k, E, d, I = 512, 6, 256, 4096, 2048
+    Ptot = N * k + N
+    # the big regions: fp32 y, split h, split x, router logits
+    assert b >= Ptot * d * 4 + Ptot * I * 2 + N * d * 2 + N * E * 4
+    assert b < (Ptot * d * 4 + Ptot * I * 2 + N * d * 2 + N * E * 4) * 1.05
+    assert capi.moe_workspace_size(cfg, 0) == 0
+    assert capi.moe_workspace_size(cfg, 1024) > b
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d_model", 96, capi.MOE_ERR_UNSUPPORTED), ("d_ff", 200, capi.MOE_ERR_UNSUPPORTED),
+    ("n_experts", 0, capi.MOE_ERR_UNSUPPORTED), ("n_experts", 1025, capi.MOE_ERR_UNSUPPORTED),
+    ("top_k", 0, capi.MOE_ERR_UNSUPPORTED), ("top_k", 9, capi.MOE_ERR_UNSUPPORTED),
+    ("routing", 2, capi.MOE_ERR_INVALID), ("has_shared", 3, capi.MOE_ERR_INVALID),
+])
+def test_bad_config_rejected(field, value, status):
+    cfg = make_config(SHAPES["tiny"])
+    setattr(cfg, field, value)
+    b = ctypes.c_size_t()
+    assert capi.lib().moe_workspace_size(ctypes.byref(cfg), 32, ctypes.byref(b)) == status
+    args = capi.MoeArgs()
+    args.n_rows = 32
+    assert capi.moe_layer_forward(cfg, args, None) == status
+
+
+def _valid_args(cfg, N):
+    """Arguments with plausible (never dereferenced) aligned addresses."""
+    a = capi.MoeArgs()
+    a.n_rows = N
+    a.x, a.router_w, a.out = 0x10000000, 0x20000000, 0x30000000
+    w = capi.MoeWeights()
+    for i, name in enumerate(n for n, _ in capi.MoeWeights._fields_):
+        setattr(w, name, 0x40000000 + i * 0x1000000)
+    a.w = w
+    a.workspace = 0x80000000
+    a.workspace_bytes = capi.moe_workspace_size(cfg, N) if N else 0
+    return a
+
+
+def test_invalid_arguments_return_before_any_hip_call():
+    cfg = make_config(SHAPES["tiny"])
+    N = 32
+    cases = []
+    a = _valid_args(cfg, N); a.x = None; cases.append((a, capi.MOE_ERR_INVALID))
+    a = _valid_args(cfg, N); a.out = 0x30000008; cases.append((a, capi.MOE_ERR_INVALID))     # misaligned
+    a = _valid_args(cfg, N); a.out = a.x + 64; cases.append((a, capi.MOE_ERR_INVALID))       # overlaps x
+    a = _valid_args(cfg, N); a.w.down_s = None; cases.append((a, capi.MOE_ERR_INVALID))
+    a = _valid_args(cfg, N); a.w.sh_up_q = 0x50000004; cases.append((a, capi.MOE_ERR_INVALID))
+    a = _valid_args(cfg, N); a.workspace_bytes -= 1; cases.append((a, capi.MOE_ERR_WORKSPACE))
+    a = _valid_args(cfg, N); a.workspace = None; cases.append((a, capi.MOE_ERR_WORKSPACE))
+    a = _valid_args(cfg, N); a.workspace = 0x80000080; cases.append((a, capi.MOE_ERR_INVALID))
+    a = _valid_args(cfg, N); a.perm = 0x90000002; cases.append((a, capi.MOE_ERR_INVALID))
+    a = _valid_args(cfg, N); a.n_rows = -1; cases.append((a, capi.MOE_ERR_INVALID))
+    a = _valid_args(cfg, N); a.n_rows = capi.MOE_MAX_ROWS + 1; cases.append((a, capi.MOE_ERR_UNSUPPORTED))
+    for a, st in cases:
+        assert capi.moe_layer_forward(cfg, a, None) == st
+    hcfg = make_config(SHAPES["hash2048"])
+    a = _valid_args(hcfg, 8)
+    assert capi.moe_layer_forward(hcfg, a, None) == capi.MOE_ERR_INVALID  # hash mode without a table
+    nosh = make_config(SHAPES["tiny"], has_shared=False)
+    a = _valid_args(nosh, N); a.w.sh_gate_q = None
+    a.workspace_bytes = 0
+    assert capi.moe_layer_forward(nosh, a, None) == capi.MOE_ERR_WORKSPACE  # shared pointers not needed
+
+
+def test_zero_rows_is_a_no_op():
+    cfg = make_config(SHAPES["tiny"])
+    a = capi.MoeArgs()
+    a.n_rows = 0
+    assert capi.moe_layer_forward(cfg, a, None) == capi.MOE_OK
+
+
+def test_pack_rejects_bad_arguments():
+    L = capi.lib()
+    assert capi.moe_pack_mxfp4(None, None, 0, 16, 128, None, None, None) == capi.MOE_OK
+    assert capi.moe_pack_mxfp4(None, 0x1000, 1, 16, 128, 0x2000, 0x3000, None) == capi.MOE_ERR_INVALID
+    assert capi.moe_pack_mxfp4(0x1000, 0x2000, 1, 20, 128, 0x3000, 0x4000, None) == capi.MOE_ERR_UNSUPPORTED
+    assert capi.moe_pack_mxfp4(0x1008, 0x2000, 1, 16, 128, 0x3000, 0x4000, None) == capi.MOE_ERR_INVALID
+    assert capi.moe_pack_mxfp4(0x1000, 0x2000, 1, 16, 128, 0x1200, 0x4000, None) == capi.MOE_ERR_INVALID  # overlap
+    assert L is not None

@@ -1,0 +1,184 @@
+"""Parity of the HIP path with the fp64 oracle, through the C ABI.
+
+Bar: routing (expert ids, counts, offsets, perm, inv) bit-exact; gates within
+1e-5 relative; bf16 output with max|err| <= 2e-2 * rms(out) and
+sum|err| / sum|out| <= 5e-3.  Small workloads are compared on every output;
+the full-size ones on every routing entry and on sampled output rows (the
+oracle computes those rows one by one in fp64).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from mxfp4_routed_expert_sqrt_amd.configs import SHAPES, MoEShape  # noqa: E402
+from mxfp4_routed_expert_sqrt_amd.layer import MoELayer, PackedExperts  # noqa: E402
+from tests.inputs import oracle_forward, workload  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+MAX_ERR = 2e-2
+MEAN_REL = 5e-3
+GATE_RTOL = 1e-5
+
+_PACKED = {}
+
+
+def bf16_to_f64(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_out(got_bits, ref, label=""):
+    got = bf16_to_f64(got_bits)
+    assert np.all(np.isfinite(got)), f"{label}: non-finite outputs"
+    err = np.abs(got - ref)
+    rms = np.sqrt(np.mean(ref ** 2))
+    max_rel = err.max() / rms
+    mean_rel = err.sum() / np.abs(ref).sum()
+    print(f"{label}: max|err|/rms = {max_rel:.3e}, mean-rel = {mean_rel:.3e}, rms = {rms:.4f}", flush=True)
+    assert max_rel <= MAX_ERR, f"{label}: max|err|/rms {max_rel}"
+    assert mean_rel <= MEAN_REL, f"{label}: mean-rel {mean_rel}"
+    return max_rel, mean_rel
+
+
+def packed_for(wl, has_shared=True):
+    sh = wl["shape"]
+    key = (sh.weight_set, sh.n_experts, sh.d_model, sh.d_ff, has_shared)
+    if key not in _PACKED:
+        _PACKED[key] = PackedExperts(wl["experts"], sh, torch.device("cuda"), has_shared)
+    return _PACKED[key]
+
+
+def run_gpu(wl, has_shared=True, **cfg_kw):
+    sh = wl["shape"]
+    dev = torch.device("cuda")
+    layer = MoELayer(sh, wl["router_w"], packed_for(wl, has_shared), dev, router_bias=wl["bias"],
+                     has_shared=has_shared, **cfg_kw)
+    x = torch.from_numpy(wl["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    tok = tab = None
+    if sh.routing == "hash":
+        tok = torch.from_numpy(wl["token_ids"]).to(dev)
+        tab = torch.from_numpy(wl["tid2eid"]).to(dev)
+    print(f"gpu forward {sh.name} N={sh.n_rows} shared={has_shared} {cfg_kw}", flush=True)
+    out, routing = layer.forward(x, tok, tab, with_routing=True)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy() for k, v in routing.items()}
+    res["out"] = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    return res, layer, x, tok, tab
+
+
+def check_routing(gpu, ref, label=""):
+    assert np.array_equal(gpu["topk_idx"], ref["idx"]), f"{label}: expert ids differ"
+    assert np.array_equal(gpu["counts"], ref["counts"]), f"{label}: counts differ"
+    assert np.array_equal(gpu["offsets"], ref["offsets"]), f"{label}: offsets differ"
+    assert np.array_equal(gpu["perm"], ref["perm"]), f"{label}: perm differs"
+    assert np.array_equal(gpu["inv"], ref["inv"]), f"{label}: inv differs"
+    np.testing.assert_allclose(gpu["topk_w"], ref["gates"], rtol=GATE_RTOL, atol=0)
+
+
+def sample_rows(n, count, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(n, size=min(count, n), replace=False))
+    return np.unique(np.concatenate([[0, n - 1], rows])).astype(np.int32)
+
+
+# --------------------------------------------------------------------- small
+
+def test_tiny_full_parity():
+    wl = workload("tiny")
+    gpu, *_ = run_gpu(wl)
+    ref = oracle_forward(wl)
+    check_routing(gpu, ref, "tiny")
+    check_out(gpu["out"], ref["out"], "tiny")
+
+
+def test_tiny_bitwise_deterministic_across_runs_and_streams():
+    wl = workload("tiny")
+    gpu, layer, x, tok, tab = run_gpu(wl)
+    outs = []
+    for i in range(3):
+        s = torch.cuda.Stream() if i == 2 else None
+        ctx = torch.cuda.stream(s) if s is not None else torch.cuda.stream(torch.cuda.current_stream())
+        with ctx:
+            o = layer.forward(x, tok, tab)
+        torch.cuda.synchronize()
+        outs.append(o.view(torch.int16).cpu().numpy())
+    for o in outs:
+        assert np.array_equal(o.view(np.uint16), gpu["out"])
+
+
+def test_decode8_full_parity():
+    wl = workload("decode8")
+    gpu, *_ = run_gpu(wl)
+    ref = oracle_forward(wl)
+    check_routing(gpu, ref, "decode8")
+    check_out(gpu["out"], ref["out"], "decode8")
+
+
+# ---------------------------------------------------------------- full size
+
+@pytest.mark.parametrize("name,n_sample", [("verify512", 48), ("prefill8192", 24), ("zipf2048", 24),
+                                           ("hash2048", 24)])
+def test_full_size_parity(name, n_sample):
+    wl = workload(name)
+    gpu, *_ = run_gpu(wl)
+    rows = sample_rows(wl["shape"].n_rows, n_sample)
+    ref = oracle_forward(wl, rows=rows)
+    check_routing(gpu, ref, name)
+    assert np.all(np.isfinite(bf16_to_f64(gpu["out"])))
+    check_out(gpu["out"][rows], ref["out"], name)
+    if name == "zipf2048":
+        load = gpu["counts"] / wl["shape"].n_rows
+        print(f"zipf2048 hottest expert load {load.max():.3f} of rows, {load.max() / wl['shape'].top_k:.3f} of "
+              f"assignments", flush=True)
+
+
+# ---------------------------------------------------------------- edge cases
+
+EDGE = {
+    "one_row": MoEShape("edge_one_row", 1, 256, 16, 2, 128, "topk", "tiny"),
+    "ragged37": MoEShape("edge_ragged37", 37, 256, 16, 2, 128, "topk", "tiny"),
+    "k1": MoEShape("edge_k1", 40, 256, 16, 1, 128, "topk", "tiny"),
+    "e20_k8": MoEShape("edge_e20_k8", 70, 384, 20, 8, 256, "topk", "edge20"),
+    "hash_small": MoEShape("edge_hash", 50, 256, 16, 2, 128, "hash", "tiny", vocab=97),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_edge_shapes(case):
+    wl = workload(EDGE[case])
+    gpu, *_ = run_gpu(wl)
+    ref = oracle_forward(wl)
+    check_routing(gpu, ref, case)
+    check_out(gpu["out"], ref["out"], case)
+
+
+def test_no_shared_expert_bias_and_route_scale():
+    sh = SHAPES["tiny"]
+    wl = dict(workload("tiny"))
+    wl["bias"] = np.linspace(-0.3, 0.3, sh.n_experts).astype(np.float32)
+    gpu, *_ = run_gpu(wl, has_shared=False, route_scale=1.5)
+    ref = oracle_forward(wl, with_shared=False, route_scale=1.5)
+    check_routing(gpu, ref, "no-shared+bias+rs1.5")
+    check_out(gpu["out"], ref["out"], "no-shared+bias+rs1.5")
+
+
+def test_swiglu_limit_binds():
+    # x scaled by 16 puts gate/up pre-activations around +-16, so the clamp at 10 binds often
+    wl = workload(SHAPES["tiny"], 0, 16.0)
+    gpu, *_ = run_gpu(wl)
+    ref = oracle_forward(wl)
+    ref_unclamped = oracle_forward(wl, swiglu_limit=0.0)
+    assert np.abs(ref["out"] - ref_unclamped["out"]).max() > 0.1 * np.sqrt(np.mean(ref["out"] ** 2))
+    check_routing(gpu, ref, "clamp")
+    check_out(gpu["out"], ref["out"], "clamp")
+
+
+def test_zero_rows_enqueue_nothing():
+    wl = workload("tiny")
+    sh = wl["shape"]
+    layer = MoELayer(sh, wl["router_w"], packed_for(wl), torch.device("cuda"))
+    x = torch.empty((0, sh.d_model), dtype=torch.bfloat16, device="cuda")
+    out = layer.forward(x, workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert out.shape == (0, sh.d_model)
