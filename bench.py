@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MoE layer (sqrt-softplus top-6 of 256 + 1 shared
+expert, MXFP4 SwiGLU experts) on one MI355X, through the C ABI.
+
+One step = one moe_layer_forward over one batch of token rows with every input
+already resident in HBM: activation split, router logits, top-k selection,
+routing bookkeeping, gate/up GEMM, down GEMM, combine.  Default workload: the
+512-row DSpark verify step (64 requests x 8 rows), d=4096, I=2048.
+
+Prints one JSON line (rank 0).  Besides the contract fields it carries
+- roofline: the gate/up GEMM (the dominant kernel) against HBM bandwidth, its
+  duration measured with HIP events recorded on the launch stream around that
+  kernel in every timed step;
+- cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
+  workload on this host (routing of all rows, outputs of the first rows).
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+EXPERT_BYTES_NOTE = "gate+up MXFP4 bytes of every touched expert (incl. shared) + x and h at 2 B/value"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_verify512_traffic.md")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="verify512")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample-rows", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls the benchmark needs for events."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for name in ("k_expert.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "mxfp4_routed_expert_sqrt_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter summary, if it still matches the kernel."""
+    if workload != "verify512" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(shape, x, router_w, experts, rows, bias=None, token_ids=None, tid2eid=None):
+    import oracle
+    from mxfp4_routed_expert_sqrt_amd.synth import usable_cpus
+    threads = usable_cpus()
+    sample = list(range(min(rows, shape.n_rows)))
+    t0 = time.perf_counter()
+    oracle.forward(shape, x, router_w, experts, router_bias=bias, token_ids=token_ids, tid2eid=tid2eid, rows=sample,
+                   threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": len(sample) / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle on rows 0..{len(sample) - 1} of the {shape.n_rows}-row {shape.name} batch "
+                      f"(routing of all {shape.n_rows} rows, every touched expert decoded once), same inputs; "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (expert parallelism is a design "
+              "note only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mxfp4_routed_expert_sqrt_amd import capi, synth
+    from mxfp4_routed_expert_sqrt_amd.configs import SHAPES
+    from mxfp4_routed_expert_sqrt_amd.layer import MoELayer
+
+    shape = SHAPES[args.workload]
+    if shape.bias != "none":
+        raise SystemExit(f"{shape.name} needs a calibrated router bias; benchmark a top-k or hash workload")
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    x_np = synth.gen_x(shape, args.seed)
+    w_np = synth.gen_router(shape, args.seed)
+    experts = synth.gen_experts(shape, args.seed)
+    tok_np = tab_np = None
+    if shape.routing == "hash":
+        tok_np, tab_np = synth.gen_token_ids(shape, args.seed), synth.gen_tid2eid(shape, args.seed)
+    print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    layer = MoELayer(shape, w_np, experts, dev)
+    x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    tok = None if tok_np is None else torch.from_numpy(tok_np).to(dev)
+    tab = None if tab_np is None else torch.from_numpy(tab_np).to(dev)
+    out = torch.empty_like(x)
+    ws = layer.new_workspace(shape.n_rows)
+
+    # routing of this batch (untimed): touched experts for the byte count
+    _, routing = layer.forward(x, tok, tab, with_routing=True)
+    torch.cuda.synchronize()
+    counts = routing["counts"].cpu().numpy()
+    touched = int((counts > 0).sum()) + 1  # + shared expert
+    N, d, I, E = shape.n_rows, shape.d_model, shape.d_ff, shape.n_experts
+    per_expert = 3 * (I * d // 2 + I * d // 32)
+    layer_bytes = touched * per_expert + E * d * 4 + 2 * N * d * 2
+    gateup_bytes = touched * 2 * (I * d // 2 + I * d // 32) + N * d * 2 + (N * shape.top_k + N) * I * 2
+
+    hip = Hip()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    K, W = args.steps, args.warmup
+    events = [[hip.event() for _ in range(capi.MOE_N_STAGE_EVENTS)] for _ in range(K)]
+    ev_arrays = [(ctypes.c_void_p * capi.MOE_N_STAGE_EVENTS)(*evs) for evs in events]
+    call = layer.args(x, out, ws, tok, tab)
+
+    def step(ev=None):
+        call.stage_events = ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None
+        rc = capi.moe_layer_forward(layer.cfg, call, stream)
+        if rc != capi.MOE_OK:
+            raise capi.MoeError(rc)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(ev_arrays[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = np.array([[hip.elapsed_ms(events[i][s], events[i][s + 1]) for s in range(capi.MOE_N_STAGES)]
+                         for i in range(K)])
+    gpu_ms = np.array([hip.elapsed_ms(events[i][0], events[i][-1]) for i in range(K)])
+    for evs in events:
+        for e in evs:
+            hip.destroy(e)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ms_per_step = elapsed * 1e3 / K
+    stages_us = {n: round(float(np.mean(stage_ms[:, s])) * 1e3, 2) for s, n in enumerate(capi.STAGE_NAMES)}
+    t_gateup = float(np.mean(stage_ms[:, 4])) * 1e-3
+    achieved = gateup_bytes / t_gateup / 1e9
+    traffic = recorded_traffic(shape.name)
+    result = {
+        "metric": "MoE-layer token rows/s at 512-row verify" if shape.name == "verify512"
+        else f"MoE-layer token rows/s ({shape.name})",
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4xfp8",
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name}: {N} token rows, d={d}, {E} routed experts top-{shape.top_k} + 1 "
+                               f"shared, I={I}, MXFP4 experts ({shape.routing} routing)",
+                   "global_batch": N, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gateup_kernel", "algorithmic_bytes": gateup_bytes,
+                     "bytes_definition": EXPERT_BYTES_NOTE, "kernel_us": t_gateup * 1e6},
+        "layer": {"gpu_us_per_step": float(np.mean(gpu_ms)) * 1e3, "algorithmic_bytes": layer_bytes,
+                  "hbm_frac": layer_bytes / (float(np.mean(gpu_ms)) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "touched_experts": touched, "stages_us": stages_us},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(shape, x_np, w_np, experts, args.cpu_sample_rows,
+                                              token_ids=tok_np, tid2eid=tab_np)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -100,8 +100,9 @@ typedef struct moe_args {
   const float* router_w;      /* fp32 [E][d], row-major, 16-byte aligned */
   const float* router_bias;   /* fp32 [E] added to the logits, or NULL */
   const int32_t* token_ids;   /* hash mode: int32 [N], each in [0, vocab) */
-  const int32_t* tid2eid;     /* hash mode: int32 [vocab][k], k distinct ids in [0, E) per row;
-                                 out-of-range or repeated ids are undefined behaviour */
+  const int32_t* tid2eid;     /* hash mode: int32 [vocab][k], k distinct ids in [0, E) per row.
+                                 Invalid entries give an unspecified routing but never an
+                                 out-of-bounds access (token and expert ids are clamped) */
   int64_t vocab;              /* hash mode: rows of tid2eid */
   moe_weights_t w;            /* packed expert weights */
   void* out;                  /* bf16 [N][d], 16-byte aligned; must not overlap x */
@@ -118,7 +119,16 @@ typedef struct moe_args {
   int32_t* inv;
   void* workspace;            /* device scratch, 256-byte aligned, >= moe_workspace_size() */
   size_t workspace_bytes;
+  /* Optional stage timing (NULL to skip): MOE_N_STAGE_EVENTS hipEvent_t handles
+   * created by the caller.  Event i is recorded on `stream` just before stage i
+   * and the last one after the final stage; the stages are
+   * 0 activation split, 1 router logits, 2 top-k/hash selection, 3 routing
+   * bookkeeping, 4 gate/up GEMM, 5 down GEMM, 6 combine. */
+  void* const* stage_events;
 } moe_args_t;
+
+#define MOE_N_STAGES 7
+#define MOE_N_STAGE_EVENTS (MOE_N_STAGES + 1)
 
 /* Library version (MOE_MXFP4_VERSION). */
 int moe_version(void);

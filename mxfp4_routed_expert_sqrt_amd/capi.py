@@ -32,7 +32,12 @@ class MoeArgs(ctypes.Structure):
     _fields_ = [("n_rows", c_i32), ("x", c_vp), ("router_w", c_vp), ("router_bias", c_vp), ("token_ids", c_vp),
                 ("tid2eid", c_vp), ("vocab", c_i64), ("w", MoeWeights), ("out", c_vp), ("topk_idx", c_vp),
                 ("topk_w", c_vp), ("counts", c_vp), ("offsets", c_vp), ("perm", c_vp), ("inv", c_vp),
-                ("workspace", c_vp), ("workspace_bytes", c_size)]
+                ("workspace", c_vp), ("workspace_bytes", c_size), ("stage_events", c_vp)]
+
+
+MOE_N_STAGES = 7
+MOE_N_STAGE_EVENTS = MOE_N_STAGES + 1
+STAGE_NAMES = ("split", "router_logits", "select", "route", "gateup", "down", "combine")
 
 
 _lib = None

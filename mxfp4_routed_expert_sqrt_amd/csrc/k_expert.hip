@@ -5,12 +5,12 @@
 // activations as two FP8 (E4M3) terms with per-32 E8M0 scales (x ~= q1*2^e1 +
 // q2*2^e2), so every product is weight * (q1 + q2) accumulated in fp32.
 //
-// One workgroup = one work unit = (group of <= 32 rows of one expert, 128
-// output features).  Its 4 waves take 32 features each (two 16-row weight
-// tiles per matrix); the rows form one or two 16-column token tiles.  Weight
-// fragments are read straight from HBM into registers: the packed layout makes
-// each wave's 16-byte-per-lane load one contiguous kilobyte, and every weight
-// byte is used by exactly one wave, so no LDS staging is needed.
+// One workgroup = one work unit = (group of <= 16 rows of one expert = one
+// MFMA column tile, 128 output features).  gate/up: 4 waves x 32 features (two
+// 16-row weight tiles per matrix); down: 2 waves x 64 features (four tiles).
+// Weight fragments are read straight from HBM into registers: the packed
+// layout makes each wave's 16-byte-per-lane load one contiguous kilobyte, and
+// every weight byte is used by exactly one wave, so no LDS staging is needed.
 //
 // Lane layout of the 16x16x128 scaled MFMA (measured on gfx950; the probe test
 // pins it): lane l supplies row/column l%16; a 4-bit operand holds K values
@@ -34,50 +34,99 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const u32x4& a, const v8i& b, const 
                                                           (int)sb);
 }
 
-// One 128-wide k-step; J selects the scale byte (k-step index within its group of 4).
-template <int J, int NA, int NT>
-__device__ __forceinline__ void kstep(const uint8_t* const (&aq)[NA], const uint8_t* const (&bq)[NT], int ks,
-                                      const uint32_t (&sa)[NA], const uint32_t (&sb)[NT][2], v4f (&acc)[NA][NT]) {
+// Operand fragments of one 128-wide k-step: NA weight tiles, NT token tiles x 2 terms.
+template <int NA, int NT>
+struct Frag {
   u32x4 A[NA];
-#pragma unroll
-  for (int a = 0; a < NA; ++a) A[a] = *(const u32x4*)(aq[a] + (size_t)ks * 1024);
   v8i B[NT][2];
+};
+
+template <int NA, int NT>
+__device__ __forceinline__ void load_frag(Frag<NA, NT>& f, const uint8_t* const (&aq)[NA],
+                                          const uint8_t* const (&bq)[NT], int ks) {
+#pragma unroll
+  for (int a = 0; a < NA; ++a) f.A[a] = *(const u32x4*)(aq[a] + (size_t)ks * 1024);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
 #pragma unroll
     for (int term = 0; term < 2; ++term) {
       const u32x4 lo = *(const u32x4*)(bq[t] + (size_t)ks * 256 + term * 32);
       const u32x4 hi = *(const u32x4*)(bq[t] + (size_t)ks * 256 + term * 32 + 16);
-      B[t][term] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      f.B[t][term] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     }
   }
+}
+
+// J = k-step index within its group of 4 = the scale byte to use.
+template <int J, int NA, int NT>
+__device__ __forceinline__ void mma_frag(const Frag<NA, NT>& f, const uint32_t (&sa)[NA], const uint32_t (&sb)[NT][2],
+                                         v4f (&acc)[NA][NT]) {
 #pragma unroll
   for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int term = 0; term < 2; ++term) acc[a][t] = mfma_fp4_fp8<J>(A[a], B[t][term], acc[a][t], sa[a], sb[t][term]);
+      for (int term = 0; term < 2; ++term) acc[a][t] = mfma_fp4_fp8<J>(f.A[a], f.B[t][term], acc[a][t], sa[a], sb[t][term]);
 }
 
+template <int NA, int NT>
+__device__ __forceinline__ void load_scales(uint32_t (&sa)[NA], uint32_t (&sb)[NT][2], const uint8_t* const (&as)[NA],
+                                            const uint8_t* const (&bs)[NT], int sg, int n_sg) {
+#pragma unroll
+  for (int a = 0; a < NA; ++a) sa[a] = *(const uint32_t*)(as[a] + (size_t)sg * 256);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    sb[t][0] = *(const uint32_t*)(bs[t] + (size_t)sg * 16);
+    sb[t][1] = *(const uint32_t*)(bs[t] + (size_t)(n_sg + sg) * 16);
+  }
+}
+
+// K loop with a 4-deep register ring: while k-step ks is multiplied, the
+// fragments of ks+1..ks+3 are in flight, and the scales of the next group of
+// 4 k-steps are fetched one group ahead, so each wave keeps ~3 k-steps of
+// weight bytes outstanding.  Every load is unconditional (indices past the
+// end are clamped to the last k-step, a cache hit) so that the compiler's
+// in-order load counter waits only for the fragment about to be used; only
+// the MFMAs of a partial last group are skipped.
 template <int NA, int NT>
 __device__ __forceinline__ void mainloop(const uint8_t* const (&aq)[NA], const uint8_t* const (&as)[NA],
                                          const uint8_t* const (&bq)[NT], const uint8_t* const (&bs)[NT], int nks,
                                          v4f (&acc)[NA][NT]) {
-  const int n_sg = (nks + 3) / 4;
+  const int n_sg = (nks + 3) / 4, last = nks - 1;
+  Frag<NA, NT> f0, f1, f2, f3;
+  uint32_t sa[NA], sb[NT][2], sa_n[NA], sb_n[NT][2];
+  load_scales(sa, sb, as, bs, 0, n_sg);
+  load_frag(f0, aq, bq, 0);
+  load_frag(f1, aq, bq, min(1, last));
+  load_frag(f2, aq, bq, min(2, last));
+  // sched_barrier(0) keeps the compiler from moving loads across these
+  // points, so the issue order (and hence each wait) is exactly as written.
   for (int sg = 0; sg < n_sg; ++sg) {
-    uint32_t sa[NA], sb[NT][2];
+    const int k0 = 4 * sg;
+    load_scales(sa_n, sb_n, as, bs, min(sg + 1, n_sg - 1), n_sg);
+    load_frag(f3, aq, bq, min(k0 + 3, last));
+    __builtin_amdgcn_sched_barrier(0);
+    mma_frag<0>(f0, sa, sb, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frag(f0, aq, bq, min(k0 + 4, last));
+    __builtin_amdgcn_sched_barrier(0);
+    if (k0 + 1 < nks) mma_frag<1>(f1, sa, sb, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frag(f1, aq, bq, min(k0 + 5, last));
+    __builtin_amdgcn_sched_barrier(0);
+    if (k0 + 2 < nks) mma_frag<2>(f2, sa, sb, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frag(f2, aq, bq, min(k0 + 6, last));
+    __builtin_amdgcn_sched_barrier(0);
+    if (k0 + 3 < nks) mma_frag<3>(f3, sa, sb, acc);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int a = 0; a < NA; ++a) sa[a] = *(const uint32_t*)(as[a] + (size_t)sg * 256);
+    for (int a = 0; a < NA; ++a) sa[a] = sa_n[a];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      sb[t][0] = *(const uint32_t*)(bs[t] + (size_t)sg * 16);
-      sb[t][1] = *(const uint32_t*)(bs[t] + (size_t)(n_sg + sg) * 16);
+      sb[t][0] = sb_n[t][0];
+      sb[t][1] = sb_n[t][1];
     }
-    const int k0 = sg * 4;
-    kstep<0>(aq, bq, k0, sa, sb, acc);
-    if (k0 + 1 < nks) kstep<1>(aq, bq, k0 + 1, sa, sb, acc);
-    if (k0 + 2 < nks) kstep<2>(aq, bq, k0 + 2, sa, sb, acc);
-    if (k0 + 3 < nks) kstep<3>(aq, bq, k0 + 3, sa, sb, acc);
   }
 }
 
@@ -190,10 +239,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(ExpertArgs a) {
   if (!xcd_unit(*a.n_groups * n_fb, &unit)) return;
   const Group g = a.groups[unit / n_fb];
   const int fb = unit % n_fb;
-  if (g.cnt > 16)
-    gateup_unit<2>(a, g, fb);
-  else
-    gateup_unit<1>(a, g, fb);
+  gateup_unit<1>(a, g, fb);
 }
 
 // ---------------------------------------------------------------------------
@@ -205,14 +251,19 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int K = a.K, R = a.R, nks = K / 128, n_sg = (nks + 3) / 4;
-  const int f0 = fb * kFeatPerWG + wave * kFeatPerWave, rt0 = f0 / 16;
+  const int f0 = fb * kFeatPerWG + wave * kDownFeatPerWave, rt0 = f0 / 16;
   const bool shared = g.e == a.E;
   const size_t mq = packed_q_bytes(R, K), ms = packed_s_bytes(R, K);
   const uint8_t* dq = shared ? a.sq0 : a.q0 + (size_t)g.e * mq;
   const uint8_t* ds = shared ? a.ss0 : a.s0 + (size_t)g.e * ms;
   const size_t tq = (size_t)nks * 1024, ts = (size_t)n_sg * 256;
-  const uint8_t* aq[2] = {dq + rt0 * tq + lane * 16, dq + (rt0 + 1) * tq + lane * 16};
-  const uint8_t* as[2] = {ds + rt0 * ts + lane * 4, ds + (rt0 + 1) * ts + lane * 4};
+  const uint8_t* aq[4];
+  const uint8_t* as[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    aq[i] = dq + (rt0 + i) * tq + lane * 16;
+    as[i] = ds + (rt0 + i) * ts + lane * 4;
+  }
   const uint8_t* bq[NT];
   const uint8_t* bs[NT];
 #pragma unroll
@@ -222,33 +273,30 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
     bq[t] = a.aq + p * split_q_row_bytes(K) + grp * 64;
     bs[t] = a.as + p * split_s_row_bytes(K) + grp * 4;
   }
-  v4f acc[2][NT];
+  v4f acc[4][NT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  mainloop<2, NT>(aq, as, bq, bs, nks, acc);
+  mainloop<4, NT>(aq, as, bq, bs, nks, acc);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int i = t * 16 + col;
     if (i < g.cnt) {
       float* dst = a.y + ((size_t)g.p0 + i) * R + f0 + 4 * grp;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) *(v4f*)(dst + 16 * tt) = acc[tt][t];
+      for (int tt = 0; tt < 4; ++tt) *(v4f*)(dst + 16 * tt) = acc[tt][t];
     }
   }
 }
 
-__global__ void __launch_bounds__(256) down_kernel(ExpertArgs a) {
+__global__ void __launch_bounds__(kDownThreads) down_kernel(ExpertArgs a) {
   const int n_fb = a.R / kFeatPerWG;
   int unit;
   if (!xcd_unit(*a.n_groups * n_fb, &unit)) return;
   const Group g = a.groups[unit / n_fb];
   const int fb = unit % n_fb;
-  if (g.cnt > 16)
-    down_unit<2>(a, g, fb);
-  else
-    down_unit<1>(a, g, fb);
+  down_unit<1>(a, g, fb);
 }
 
 static unsigned unit_grid(int max_groups, int n_fb) {
@@ -262,7 +310,7 @@ hipError_t launch_gateup(const ExpertArgs& a, int max_groups, hipStream_t stream
 }
 
 hipError_t launch_down(const ExpertArgs& a, int max_groups, hipStream_t stream) {
-  hipLaunchKernelGGL(down_kernel, dim3(unit_grid(max_groups, a.R / kFeatPerWG)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(down_kernel, dim3(unit_grid(max_groups, a.R / kFeatPerWG)), dim3(kDownThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -172,13 +172,20 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   const int P = N * k;
 
   hipError_t err;
+  auto mark = [&](int i) -> bool {
+    return !a.stage_events || hipEventRecord((hipEvent_t)a.stage_events[i], stream) == hipSuccess;
+  };
+  if (!mark(0)) return MOE_ERR_HIP;
   if ((err = launch_split_bf16((const uint16_t*)a.x, N, d, xq, xs, stream)) != hipSuccess) return MOE_ERR_HIP;
+  if (!mark(1)) return MOE_ERR_HIP;
   if ((err = launch_router_logits((const uint16_t*)a.x, a.router_w, a.router_bias, N, d, E, z, stream)) !=
       hipSuccess)
     return MOE_ERR_HIP;
+  if (!mark(2)) return MOE_ERR_HIP;
   if ((err = launch_select(z, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, stream)) !=
       hipSuccess)
     return MOE_ERR_HIP;
+  if (!mark(3)) return MOE_ERR_HIP;
   if ((err = launch_route(idx, N, k, E, c.has_shared, counts, offsets, perm, inv, groups, n_groups, stream)) !=
       hipSuccess)
     return MOE_ERR_HIP;
@@ -206,6 +213,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   ga.limit = c.swiglu_limit;
   ga.hq = hq;
   ga.hs = hs;
+  if (!mark(4)) return MOE_ERR_HIP;
   if ((err = launch_gateup(ga, L.max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
 
   ExpertArgs da = ga;
@@ -221,11 +229,14 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   da.R = d;
   da.hq = da.hs = nullptr;
   da.y = y;
+  if (!mark(5)) return MOE_ERR_HIP;
   if ((err = launch_down(da, L.max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
+  if (!mark(6)) return MOE_ERR_HIP;
 
   if ((err = launch_combine(y, inv, gates, N, d, k, P, c.has_shared, c.route_scale, (uint16_t*)a.out, stream)) !=
       hipSuccess)
     return MOE_ERR_HIP;
+  if (!mark(7)) return MOE_ERR_HIP;
   return MOE_OK;
 }
 
