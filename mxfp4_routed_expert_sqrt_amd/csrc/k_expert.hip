@@ -8,9 +8,12 @@
 // One workgroup = one work unit = (group of <= 16 rows of one expert = one
 // MFMA column tile, 128 output features).  gate/up: 4 waves x 32 features (two
 // 16-row weight tiles per matrix); down: 2 waves x 64 features (four tiles).
-// Weight fragments are read straight from HBM into registers: the packed
-// layout makes each wave's 16-byte-per-lane load one contiguous kilobyte, and
-// every weight byte is used by exactly one wave, so no LDS staging is needed.
+// Weight fragments go straight from HBM into a 4-deep register ring per wave:
+// the packed layout makes each wave's 16-byte-per-lane load one contiguous
+// kilobyte, and every weight byte is used by exactly one wave.  The
+// activations, which all waves of the workgroup share, are staged once per
+// workgroup through LDS in chunks of 4 k-steps (double-buffered), so the
+// waves' vector-memory queues carry weight bytes only.
 //
 // Lane layout of the 16x16x128 scaled MFMA (measured on gfx950; the probe test
 // pins it): lane l supplies row/column l%16; a 4-bit operand holds K values
@@ -34,99 +37,128 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const u32x4& a, const v8i& b, const 
                                                           (int)sb);
 }
 
-// Operand fragments of one 128-wide k-step: NA weight tiles, NT token tiles x 2 terms.
-template <int NA, int NT>
-struct Frag {
-  u32x4 A[NA];
-  v8i B[NT][2];
+// ---------------------------------------------------------------------------
+// Activation chunk in LDS: 4 k-steps of the 16 token rows of a unit, laid out
+// for conflict-free MFMA reads as [step j][term t][half h][group g][col][16 B]
+// (16 KB), followed by the B scales [term][group][col] as dwords (512 B).  The
+// half h holds the operand bytes 16h..16h+15 of lane (col, g).
+constexpr int kChunkData = 16384;
+constexpr int kChunkBytes = kChunkData + 512;
+
+// This thread's share of one chunk (global -> registers -> LDS).  Piece
+// p = tid + THREADS*m (16 bytes) of the chunk is (j, t, h, g, col) =
+// (p>>8, p>>7 & 1, p>>6 & 1, p>>4 & 3, p & 15); col = tid % 16 for every m,
+// so each thread reads one token row.
+template <int THREADS>
+struct ChunkStage {
+  static constexpr int kPieces = 1024 / THREADS;
+  u32x4 q[kPieces];
+  uint32_t s;
+
+  __device__ __forceinline__ void load(const uint8_t* brow_q, const uint8_t* brow_s, int sg, int nks, int n_sg) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < kPieces; ++m) {
+      const int p = tid + THREADS * m;
+      const int j = p >> 8, t = (p >> 7) & 1, h = (p >> 6) & 1, g = (p >> 4) & 3;
+      const int ks = min(4 * sg + j, nks - 1);  // past the end: any valid step (never multiplied)
+      q[m] = *(const u32x4*)(brow_q + (size_t)ks * 256 + g * 64 + t * 32 + h * 16);
+    }
+    const int t = (tid >> 6) & 1, g = (tid >> 4) & 3;
+    s = *(const uint32_t*)(brow_s + (size_t)(t * n_sg + sg) * 16 + g * 4);
+  }
+
+  __device__ __forceinline__ void store(uint8_t* chunk) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < kPieces; ++m) *(u32x4*)(chunk + (tid + THREADS * m) * 16) = q[m];
+    if (tid < 128) *(uint32_t*)(chunk + kChunkData + tid * 4) = s;
+  }
 };
 
-template <int NA, int NT>
-__device__ __forceinline__ void load_frag(Frag<NA, NT>& f, const uint8_t* const (&aq)[NA],
-                                          const uint8_t* const (&bq)[NT], int ks) {
+template <int NA>
+struct WFrag {
+  u32x4 A[NA];
+};
+
+template <int NA>
+__device__ __forceinline__ void load_w(WFrag<NA>& f, const uint8_t* const (&aq)[NA], int ks) {
 #pragma unroll
   for (int a = 0; a < NA; ++a) f.A[a] = *(const u32x4*)(aq[a] + (size_t)ks * 1024);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-#pragma unroll
-    for (int term = 0; term < 2; ++term) {
-      const u32x4 lo = *(const u32x4*)(bq[t] + (size_t)ks * 256 + term * 32);
-      const u32x4 hi = *(const u32x4*)(bq[t] + (size_t)ks * 256 + term * 32 + 16);
-      f.B[t][term] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    }
-  }
 }
 
-// J = k-step index within its group of 4 = the scale byte to use.
-template <int J, int NA, int NT>
-__device__ __forceinline__ void mma_frag(const Frag<NA, NT>& f, const uint32_t (&sa)[NA], const uint32_t (&sb)[NT][2],
-                                         v4f (&acc)[NA][NT]) {
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int term = 0; term < 2; ++term) acc[a][t] = mfma_fp4_fp8<J>(f.A[a], f.B[t][term], acc[a][t], sa[a], sb[t][term]);
-}
-
-template <int NA, int NT>
-__device__ __forceinline__ void load_scales(uint32_t (&sa)[NA], uint32_t (&sb)[NT][2], const uint8_t* const (&as)[NA],
-                                            const uint8_t* const (&bs)[NT], int sg, int n_sg) {
+template <int NA>
+__device__ __forceinline__ void load_wscales(uint32_t (&sa)[NA], const uint8_t* const (&as)[NA], int sg) {
 #pragma unroll
   for (int a = 0; a < NA; ++a) sa[a] = *(const uint32_t*)(as[a] + (size_t)sg * 256);
+}
+
+// k-step J of the current chunk: B from LDS, weights from a ring slot.
+template <int J, int NA>
+__device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chunk, const uint32_t (&sa)[NA],
+                                         const uint32_t (&sb)[2], v4f (&acc)[NA]) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    sb[t][0] = *(const uint32_t*)(bs[t] + (size_t)sg * 16);
-    sb[t][1] = *(const uint32_t*)(bs[t] + (size_t)(n_sg + sg) * 16);
+  for (int t = 0; t < 2; ++t) {
+    const u32x4 lo = *(const u32x4*)(chunk + ((J * 2 + t) * 2 + 0) * 1024 + lane * 16);
+    const u32x4 hi = *(const u32x4*)(chunk + ((J * 2 + t) * 2 + 1) * 1024 + lane * 16);
+    const v8i b = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+    for (int a = 0; a < NA; ++a) acc[a] = mfma_fp4_fp8<J>(f.A[a], b, acc[a], sa[a], sb[t]);
   }
 }
 
-// K loop with a 4-deep register ring: while k-step ks is multiplied, the
-// fragments of ks+1..ks+3 are in flight, and the scales of the next group of
-// 4 k-steps are fetched one group ahead, so each wave keeps ~3 k-steps of
-// weight bytes outstanding.  Every load is unconditional (indices past the
-// end are clamped to the last k-step, a cache hit) so that the compiler's
-// in-order load counter waits only for the fragment about to be used; only
-// the MFMAs of a partial last group are skipped.
-template <int NA, int NT>
+// K loop.  Weights: a 4-deep register ring (fragments of ks+1..ks+3 in flight
+// while ks is multiplied; weight scales one group of 4 k-steps ahead).
+// Activations: chunk sg+1 is fetched into registers at the start of group sg
+// and written to the other LDS buffer at its end, then one workgroup barrier
+// per group (it waits on LDS traffic only, not on the weight loads in flight).
+// Loads are unconditional (clamped indices) and the sched_barrier(0) points
+// keep their issue order, so each wait on the in-order vector-memory counter
+// covers only what is about to be used.
+template <int NA, int THREADS>
 __device__ __forceinline__ void mainloop(const uint8_t* const (&aq)[NA], const uint8_t* const (&as)[NA],
-                                         const uint8_t* const (&bq)[NT], const uint8_t* const (&bs)[NT], int nks,
-                                         v4f (&acc)[NA][NT]) {
+                                         const uint8_t* brow_q, const uint8_t* brow_s, int nks, v4f (&acc)[NA],
+                                         uint8_t* lds) {
+  const int lane = threadIdx.x & 63;
   const int n_sg = (nks + 3) / 4, last = nks - 1;
-  Frag<NA, NT> f0, f1, f2, f3;
-  uint32_t sa[NA], sb[NT][2], sa_n[NA], sb_n[NT][2];
-  load_scales(sa, sb, as, bs, 0, n_sg);
-  load_frag(f0, aq, bq, 0);
-  load_frag(f1, aq, bq, min(1, last));
-  load_frag(f2, aq, bq, min(2, last));
-  // sched_barrier(0) keeps the compiler from moving loads across these
-  // points, so the issue order (and hence each wait) is exactly as written.
+  ChunkStage<THREADS> stage;
+  WFrag<NA> f0, f1, f2, f3;
+  uint32_t sa[NA], sa_n[NA], sb[2];
+  stage.load(brow_q, brow_s, 0, nks, n_sg);
+  load_wscales(sa, as, 0);
+  load_w(f0, aq, 0);
+  load_w(f1, aq, min(1, last));
+  load_w(f2, aq, min(2, last));
+  stage.store(lds);
+  __syncthreads();
   for (int sg = 0; sg < n_sg; ++sg) {
     const int k0 = 4 * sg;
-    load_scales(sa_n, sb_n, as, bs, min(sg + 1, n_sg - 1), n_sg);
-    load_frag(f3, aq, bq, min(k0 + 3, last));
+    const uint8_t* chunk = lds + (sg & 1) * kChunkBytes;
+    sb[0] = *(const uint32_t*)(chunk + kChunkData + lane * 4);
+    sb[1] = *(const uint32_t*)(chunk + kChunkData + 256 + lane * 4);
+    stage.load(brow_q, brow_s, min(sg + 1, n_sg - 1), nks, n_sg);
+    load_wscales(sa_n, as, min(sg + 1, n_sg - 1));
+    load_w(f3, aq, min(k0 + 3, last));
     __builtin_amdgcn_sched_barrier(0);
-    mma_frag<0>(f0, sa, sb, acc);
+    mma_step<0>(f0, chunk, sa, sb, acc);
     __builtin_amdgcn_sched_barrier(0);
-    load_frag(f0, aq, bq, min(k0 + 4, last));
+    load_w(f0, aq, min(k0 + 4, last));
     __builtin_amdgcn_sched_barrier(0);
-    if (k0 + 1 < nks) mma_frag<1>(f1, sa, sb, acc);
+    if (k0 + 1 < nks) mma_step<1>(f1, chunk, sa, sb, acc);
     __builtin_amdgcn_sched_barrier(0);
-    load_frag(f1, aq, bq, min(k0 + 5, last));
+    load_w(f1, aq, min(k0 + 5, last));
     __builtin_amdgcn_sched_barrier(0);
-    if (k0 + 2 < nks) mma_frag<2>(f2, sa, sb, acc);
+    if (k0 + 2 < nks) mma_step<2>(f2, chunk, sa, sb, acc);
     __builtin_amdgcn_sched_barrier(0);
-    load_frag(f2, aq, bq, min(k0 + 6, last));
+    load_w(f2, aq, min(k0 + 6, last));
     __builtin_amdgcn_sched_barrier(0);
-    if (k0 + 3 < nks) mma_frag<3>(f3, sa, sb, acc);
+    if (k0 + 3 < nks) mma_step<3>(f3, chunk, sa, sb, acc);
     __builtin_amdgcn_sched_barrier(0);
+    stage.store(lds + ((sg + 1) & 1) * kChunkBytes);
+    __syncthreads();
 #pragma unroll
     for (int a = 0; a < NA; ++a) sa[a] = sa_n[a];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      sb[t][0] = sb_n[t][0];
-      sb[t][1] = sb_n[t][1];
-    }
   }
 }
 
@@ -134,9 +166,14 @@ __device__ __forceinline__ void mainloop(const uint8_t* const (&aq)[NA], const u
 // gate/up: h = silu(min(gate, L)) * clamp(up, -L, L), written as the two-term
 // FP8 split that the down GEMM consumes (same layout as the x split, K = I).
 
-template <int NT>
-__device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, int fb) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ void __launch_bounds__(256) gateup_kernel(ExpertArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunkBytes];
+  const int n_fb = a.R / kFeatPerWG;
+  int unit;
+  if (!xcd_unit(*a.n_groups * n_fb, &unit)) return;
+  const Group g = a.groups[unit / n_fb];
+  const int fb = unit % n_fb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int K = a.K, R = a.R, nks = K / 128, n_sg = (nks + 3) / 4;
   const int f0 = fb * kFeatPerWG + wave * kFeatPerWave, rt0 = f0 / 16;
@@ -151,104 +188,90 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
                           uq + (rt0 + 1) * tq + lane * 16};
   const uint8_t* as[4] = {gs + rt0 * ts + lane * 4, gs + (rt0 + 1) * ts + lane * 4, us + rt0 * ts + lane * 4,
                           us + (rt0 + 1) * ts + lane * 4};
-  const uint8_t* bq[NT];
-  const uint8_t* bs[NT];
+  // the token row this thread stages (column tid % 16); padding columns reuse the group's first row
+  const int tcol = tid & 15;
+  const int p_ld = g.p0 + (tcol < g.cnt ? tcol : 0);
+  const int row = shared ? p_ld - a.P : a.perm[p_ld] / a.k;
+  const uint8_t* brow_q = a.aq + (size_t)row * split_q_row_bytes(K);
+  const uint8_t* brow_s = a.as + (size_t)row * split_s_row_bytes(K);
+  v4f acc[4];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int i = t * 16 + col;
-    const int p = g.p0 + (i < g.cnt ? i : 0);  // padding columns reuse the group's first row
-    const int row = shared ? p - a.P : a.perm[p] / a.k;
-    bq[t] = a.aq + (size_t)row * split_q_row_bytes(K) + grp * 64;
-    bs[t] = a.as + (size_t)row * split_s_row_bytes(K) + grp * 4;
-  }
-  v4f acc[4][NT];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  mainloop<4, NT>(aq, as, bq, bs, nks, acc);
+  for (int i = 0; i < 4; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  mainloop<4, 256>(aq, as, brow_q, brow_s, nks, acc, lds);
 
   const int n_sg_h = (R / 128 + 3) / 4;
   const int blk_h = f0 / 32;
   const float L = a.limit;
+  float h[8];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    float h[8];
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        float gv = acc[tt][t][ii], uv = acc[2 + tt][t][ii];
-        if (L > 0.f) {
-          gv = fminf(gv, L);
-          uv = fminf(fmaxf(uv, -L), L);
-        }
-        h[tt * 4 + ii] = gv / (1.f + __expf(-gv)) * uv;
+    for (int ii = 0; ii < 4; ++ii) {
+      float gv = acc[tt][ii], uv = acc[2 + tt][ii];
+      if (L > 0.f) {
+        gv = fminf(gv, L);
+        uv = fminf(fmaxf(uv, -L), L);
       }
-    // 32-feature block of one token = 4 lanes (grp 0..3) x 8 values
-    float amax = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[j]));
-    amax = shfl_xor_max<16>(amax);
-    amax = shfl_xor_max<32>(amax);
-    const int e1 = split_exponent(amax);
-    const float inv1 = ldexpf(1.f, -e1), sc1 = ldexpf(1.f, e1);
-    uint32_t w1[2], w2[2];
-    float res[8];
-    float amax2 = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      w1[tt] = pack4_fp8(h[4 * tt] * inv1, h[4 * tt + 1] * inv1, h[4 * tt + 2] * inv1, h[4 * tt + 3] * inv1);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        res[4 * tt + ii] = h[4 * tt + ii] - fp8_byte_to_f32(w1[tt], ii) * sc1;
-        amax2 = fmaxf(amax2, fabsf(res[4 * tt + ii]));
-      }
+      h[tt * 4 + ii] = gv / (1.f + __expf(-gv)) * uv;
     }
-    amax2 = shfl_xor_max<16>(amax2);
-    amax2 = shfl_xor_max<32>(amax2);
-    const int e2 = split_exponent(amax2);
-    const float inv2 = ldexpf(1.f, -e2);
+  // 32-feature block of one token = 4 lanes (grp 0..3) x 8 values
+  float amax = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-      w2[tt] = pack4_fp8(res[4 * tt] * inv2, res[4 * tt + 1] * inv2, res[4 * tt + 2] * inv2, res[4 * tt + 3] * inv2);
-    const int i = t * 16 + col;
-    if (i < g.cnt) {
-      const size_t p = (size_t)g.p0 + i;
-      // feature 16tt + 4grp + ii of block blk_h = 4ks + bb: group 2*(bb%2) + tt, byte 16*(bb/2) + 4grp + ii
-      const int bb = blk_h & 3;
-      uint8_t* dst = a.hq + p * split_q_row_bytes(R) + (size_t)(blk_h >> 2) * 256 + 16 * (bb >> 1) + 4 * grp;
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[j]));
+  amax = shfl_xor_max<16>(amax);
+  amax = shfl_xor_max<32>(amax);
+  const int e1 = split_exponent(amax);
+  const float inv1 = ldexpf(1.f, -e1), sc1 = ldexpf(1.f, e1);
+  uint32_t w1[2], w2[2];
+  float res[8];
+  float amax2 = 0.f;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        uint8_t* gdst = dst + (2 * (bb & 1) + tt) * 64;
-        *(uint32_t*)(gdst) = w1[tt];
-        *(uint32_t*)(gdst + 32) = w2[tt];
-      }
-      if (grp == 0) {
-        uint8_t* srow = a.hs + p * split_s_row_bytes(R);
-        srow[split_scale_offset_h(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
-        srow[split_scale_offset_h(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
-      }
+  for (int tt = 0; tt < 2; ++tt) {
+    w1[tt] = pack4_fp8(h[4 * tt] * inv1, h[4 * tt + 1] * inv1, h[4 * tt + 2] * inv1, h[4 * tt + 3] * inv1);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      res[4 * tt + ii] = h[4 * tt + ii] - fp8_byte_to_f32(w1[tt], ii) * sc1;
+      amax2 = fmaxf(amax2, fabsf(res[4 * tt + ii]));
     }
   }
-}
-
-__global__ void __launch_bounds__(256) gateup_kernel(ExpertArgs a) {
-  const int n_fb = a.R / kFeatPerWG;
-  int unit;
-  if (!xcd_unit(*a.n_groups * n_fb, &unit)) return;
-  const Group g = a.groups[unit / n_fb];
-  const int fb = unit % n_fb;
-  gateup_unit<1>(a, g, fb);
+  amax2 = shfl_xor_max<16>(amax2);
+  amax2 = shfl_xor_max<32>(amax2);
+  const int e2 = split_exponent(amax2);
+  const float inv2 = ldexpf(1.f, -e2);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+    w2[tt] = pack4_fp8(res[4 * tt] * inv2, res[4 * tt + 1] * inv2, res[4 * tt + 2] * inv2, res[4 * tt + 3] * inv2);
+  if (col < g.cnt) {
+    const size_t p = (size_t)g.p0 + col;
+    // feature 16tt + 4grp + ii of block blk_h = 4ks + bb: group 2*(bb%2) + tt, byte 16*(bb/2) + 4grp + ii
+    const int bb = blk_h & 3;
+    uint8_t* dst = a.hq + p * split_q_row_bytes(R) + (size_t)(blk_h >> 2) * 256 + 16 * (bb >> 1) + 4 * grp;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      uint8_t* gdst = dst + (2 * (bb & 1) + tt) * 64;
+      *(uint32_t*)(gdst) = w1[tt];
+      *(uint32_t*)(gdst + 32) = w2[tt];
+    }
+    if (grp == 0) {
+      uint8_t* srow = a.hs + p * split_s_row_bytes(R);
+      srow[split_scale_offset_h(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
+      srow[split_scale_offset_h(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 // down: y[p][f] = sum_n W_down[e][f][n] h[p][n], fp32 rows in expert-major
 // pair order (routed) followed by the shared expert's rows.
 
-template <int NT>
-__device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, int fb) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ void __launch_bounds__(kDownThreads) down_kernel(ExpertArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunkBytes];
+  const int n_fb = a.R / kFeatPerWG;
+  int unit;
+  if (!xcd_unit(*a.n_groups * n_fb, &unit)) return;
+  const Group g = a.groups[unit / n_fb];
+  const int fb = unit % n_fb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int K = a.K, R = a.R, nks = K / 128, n_sg = (nks + 3) / 4;
   const int f0 = fb * kFeatPerWG + wave * kDownFeatPerWave, rt0 = f0 / 16;
@@ -264,39 +287,19 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
     aq[i] = dq + (rt0 + i) * tq + lane * 16;
     as[i] = ds + (rt0 + i) * ts + lane * 4;
   }
-  const uint8_t* bq[NT];
-  const uint8_t* bs[NT];
+  const int tcol = tid & 15;
+  const size_t p_ld = (size_t)g.p0 + (tcol < g.cnt ? tcol : 0);
+  const uint8_t* brow_q = a.aq + p_ld * split_q_row_bytes(K);
+  const uint8_t* brow_s = a.as + p_ld * split_s_row_bytes(K);
+  v4f acc[4];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int i = t * 16 + col;
-    const size_t p = (size_t)g.p0 + (i < g.cnt ? i : 0);
-    bq[t] = a.aq + p * split_q_row_bytes(K) + grp * 64;
-    bs[t] = a.as + p * split_s_row_bytes(K) + grp * 4;
+  for (int i = 0; i < 4; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  mainloop<4, kDownThreads>(aq, as, brow_q, brow_s, nks, acc, lds);
+  if (col < g.cnt) {
+    float* dst = a.y + ((size_t)g.p0 + col) * R + f0 + 4 * grp;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) *(v4f*)(dst + 16 * tt) = acc[tt];
   }
-  v4f acc[4][NT];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  mainloop<4, NT>(aq, as, bq, bs, nks, acc);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int i = t * 16 + col;
-    if (i < g.cnt) {
-      float* dst = a.y + ((size_t)g.p0 + i) * R + f0 + 4 * grp;
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) *(v4f*)(dst + 16 * tt) = acc[tt][t];
-    }
-  }
-}
-
-__global__ void __launch_bounds__(kDownThreads) down_kernel(ExpertArgs a) {
-  const int n_fb = a.R / kFeatPerWG;
-  int unit;
-  if (!xcd_unit(*a.n_groups * n_fb, &unit)) return;
-  const Group g = a.groups[unit / n_fb];
-  const int fb = unit % n_fb;
-  down_unit<1>(a, g, fb);
 }
 
 static unsigned unit_grid(int max_groups, int n_fb) {
