@@ -8,7 +8,10 @@ namespace moe {
 // z[r][e] = sum_i x[r][i] * W[e][i] + bias[e], fp32 accumulation on
 // v_mfma_f32_16x16x4_f32 (bf16 x is exact in fp32).  A workgroup computes one
 // 16-row x 16-expert tile; its 4 waves take one quarter of K each and the
-// partial tiles are added in wave order through LDS.
+// partial tiles are added in wave order through LDS.  Each lane loads 8
+// consecutive K values of its row and of its expert per 32-wide k-chunk (lane
+// group g supplies k = k0 + 8g + i to MFMA i, for A and B alike), and 4 chunks
+// are loaded before any is multiplied.
 __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __restrict__ x,
                                                              const float* __restrict__ w,
                                                              const float* __restrict__ bias, int n_rows, int d,
@@ -19,18 +22,43 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __re
   const int r0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
   const int ra = min(r0 + col, n_rows - 1);  // A operand row of this lane (clamped; result discarded)
   const int eb = min(e0 + col, E - 1);       // B operand expert of this lane
-  const int kq = d / 4, kbeg = wave * kq;
-  const uint16_t* xp = x + (size_t)ra * d + kbeg + 4 * grp;
-  const float* wp = w + (size_t)eb * d + kbeg + 4 * grp;
+  const int kq = d / 4, kbeg = wave * kq;    // kq is a multiple of 32
+  const uint16_t* xp = x + (size_t)ra * d + kbeg + 8 * grp;
+  const float* wp = w + (size_t)eb * d + kbeg + 8 * grp;
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  // k-step of 16: lane group g supplies k = kk + 4g + i to MFMA i, for A and B alike
-  for (int kk = 0; kk < kq; kk += 16) {
-    const uint2 xa = *(const uint2*)(xp + kk);
-    const float4 wb = *(const float4*)(wp + kk);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(xa.x << 16), wb.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(xa.x & 0xffff0000u), wb.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(xa.y << 16), wb.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(xa.y & 0xffff0000u), wb.w, acc, 0, 0, 0);
+  constexpr int kUnroll = 4;
+  int kk = 0;
+  for (; kk + 32 * kUnroll <= kq; kk += 32 * kUnroll) {
+    u32x4 xa[kUnroll];
+    float4 wa[kUnroll], wb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      xa[u] = *(const u32x4*)(xp + kk + 32 * u);
+      wa[u] = *(const float4*)(wp + kk + 32 * u);
+      wb[u] = *(const float4*)(wp + kk + 32 * u + 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all 4 chunks in flight before the first multiply
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float wv[8] = {wa[u].x, wa[u].y, wa[u].z, wa[u].w, wb[u].x, wb[u].y, wb[u].z, wb[u].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t pair = xa[u][i >> 1];
+        const float xv = __uint_as_float((i & 1) ? (pair & 0xffff0000u) : (pair << 16));
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, wv[i], acc, 0, 0, 0);
+      }
+    }
+  }
+  for (; kk < kq; kk += 32) {
+    const u32x4 xa = *(const u32x4*)(xp + kk);
+    const float4 wa = *(const float4*)(wp + kk), wb = *(const float4*)(wp + kk + 4);
+    const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t pair = xa[i >> 1];
+      const float xv = __uint_as_float((i & 1) ? (pair & 0xffff0000u) : (pair << 16));
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, wv[i], acc, 0, 0, 0);
+    }
   }
   // lane holds D[row 4*grp + i][expert col]
 #pragma unroll
@@ -68,6 +96,47 @@ __device__ __forceinline__ float router_score(float zv) {
 
 constexpr int kMaxExpertsPerLane = 16;  // E <= 1024
 constexpr int kMaxTopK = 8;
+constexpr int kNoExpert = 0x7fffffff;
+
+// (value, id) order used by the selection: larger value first, then lower id;
+// an empty candidate (id kNoExpert) loses to any real one.
+__device__ __forceinline__ bool better(float v, int e, float bv, int be) {
+  return e != kNoExpert && (be == kNoExpert || v > bv || (v == bv && e < be));
+}
+
+// One DPP step of the (value, id) max-reduction inside each row of 16 lanes.
+template <int kCtrl>
+__device__ __forceinline__ void dpp_best(float& bv, int& be) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), kCtrl, 0xF, 0xF, false));
+  const int oe = __builtin_amdgcn_update_dpp(kNoExpert, be, kCtrl, 0xF, 0xF, false);
+  if (better(ov, oe, bv, be)) {
+    bv = ov;
+    be = oe;
+  }
+}
+
+// Best (value, id) over the wave, returned uniform in every lane: DPP
+// exchanges within rows of 16 lanes (xor 1, xor 2, rotate 4, rotate 8), then
+// the four row results are read out and compared in scalar registers.
+__device__ __forceinline__ void wave_best(float& bv, int& be) {
+  dpp_best<0xB1>(bv, be);   // quad_perm [1,0,3,2]
+  dpp_best<0x4E>(bv, be);   // quad_perm [2,3,0,1]
+  dpp_best<0x124>(bv, be);  // row_ror:4
+  dpp_best<0x128>(bv, be);  // row_ror:8
+  float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+  int re = __builtin_amdgcn_readlane(be, 0);
+#pragma unroll
+  for (int row = 1; row < 4; ++row) {
+    const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * row));
+    const int oe = __builtin_amdgcn_readlane(be, 16 * row);
+    if (better(ov, oe, rv, re)) {
+      rv = ov;
+      re = oe;
+    }
+  }
+  bv = rv;
+  be = re;
+}
 
 __global__ void __launch_bounds__(256) select_kernel(const float* __restrict__ z, int n_rows, int E, int k,
                                                       int routing, const int32_t* __restrict__ token_ids,
@@ -87,32 +156,27 @@ __global__ void __launch_bounds__(256) select_kernel(const float* __restrict__ z
       s[c] = (e < E) ? router_score(zr[e]) : -INFINITY;
     }
     uint32_t taken = 0;  // bit c: expert c*64 + lane already selected
-    for (int j = 0; j < k; ++j) {
-      // lane-local best among untaken experts (ties: lower id).  The first
-      // candidate is always accepted, so some untaken id wins even if scores
-      // are NaN: the selection stays a set of k distinct valid ids.
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
 #pragma unroll
-      for (int c = 0; c < kMaxExpertsPerLane; ++c) {
-        const int e = c * 64 + lane;
-        if (e < E && !((taken >> c) & 1u) && (be == 0x7fffffff || s[c] > bv || (s[c] == bv && e < be))) {
-          bv = s[c];
-          be = e;
-        }
-      }
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        // lane-local best among untaken experts; the first candidate is always
+        // accepted, so some untaken id wins even if scores are NaN and the
+        // selection stays a set of k distinct valid ids
+        float bv = -INFINITY;
+        int be = kNoExpert;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oe = __shfl_xor(be, off, 64);
-        if (oe != 0x7fffffff && (be == 0x7fffffff || ov > bv || (ov == bv && oe < be))) {
-          bv = ov;
-          be = oe;
+        for (int c = 0; c < kMaxExpertsPerLane; ++c) {
+          const int e = c * 64 + lane;
+          if (e < E && !((taken >> c) & 1u) && better(s[c], e, bv, be)) {
+            bv = s[c];
+            be = e;
+          }
         }
+        wave_best(bv, be);
+        sel[j] = be;
+        sv[j] = bv;
+        if ((be & 63) == lane) taken |= 1u << (be >> 6);
       }
-      sel[j] = be;
-      sv[j] = bv;
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
     }
   } else {
     // Hash mode.  Table entries must be valid (distinct ids in [0, E)); an
@@ -120,25 +184,34 @@ __global__ void __launch_bounds__(256) select_kernel(const float* __restrict__ z
     // gives an unspecified routing but never an out-of-bounds access.
     const int64_t t = min(max((int64_t)token_ids[r], (int64_t)0), vocab - 1);
     const int32_t* row = tid2eid + t * k;
-    for (int j = 0; j < k; ++j) {
-      sel[j] = min(max(row[j], 0), E - 1);
-      sv[j] = router_score(zr[sel[j]]);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        sel[j] = min(max(row[j], 0), E - 1);
+        sv[j] = router_score(zr[sel[j]]);
+      }
     }
   }
-  // ascending expert id (k <= 8: insertion sort, identical in every lane)
-  for (int a = 1; a < k; ++a)
-    for (int b = a; b > 0 && sel[b - 1] > sel[b]; --b) {
-      const int te = sel[b];
-      sel[b] = sel[b - 1];
-      sel[b - 1] = te;
-      const float tv = sv[b];
-      sv[b] = sv[b - 1];
-      sv[b - 1] = tv;
-    }
+  // ascending expert id (k <= 8: compare-exchange passes on wave-uniform values)
+#pragma unroll
+  for (int pass = 0; pass < kMaxTopK; ++pass)
+#pragma unroll
+    for (int b = 1; b < kMaxTopK; ++b)
+      if (b < k && sel[b - 1] > sel[b]) {
+        const int te = sel[b];
+        sel[b] = sel[b - 1];
+        sel[b - 1] = te;
+        const float tv = sv[b];
+        sv[b] = sv[b - 1];
+        sv[b - 1] = tv;
+      }
   float sum = 0.f;
-  for (int j = 0; j < k; ++j) sum += sv[j];
-  for (int j = 0; j < k; ++j)
-    if (lane == j) {
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k) sum += sv[j];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k && lane == j) {
       idx[(size_t)r * k + j] = sel[j];
       gates[(size_t)r * k + j] = sv[j] / sum;
     }
