@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="verify512")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-rows", type=int, default=64)
+    ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")

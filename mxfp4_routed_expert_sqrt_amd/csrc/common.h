@@ -11,11 +11,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kGroupRows = 16;   // token rows of one grouped-GEMM work unit (one MFMA column tile)
-constexpr int kFeatPerWave = 32; // gate/up: features of one wave (2 gate + 2 up weight tiles)
-constexpr int kWavesPerWG = 4;
-constexpr int kFeatPerWG = kFeatPerWave * kWavesPerWG;  // output features of one work unit (both GEMMs)
-constexpr int kDownFeatPerWave = 64;                     // down: 4 weight tiles per wave
-constexpr int kDownThreads = 64 * kFeatPerWG / kDownFeatPerWave;
 constexpr int kXcds = 8;         // gfx950: workgroups are dealt round-robin to 8 XCDs
 
 // One work unit of the grouped GEMMs: rows [p0, p0 + cnt) of expert e.

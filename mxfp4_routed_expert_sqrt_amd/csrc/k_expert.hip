@@ -6,8 +6,9 @@
 // q2*2^e2), so every product is weight * (q1 + q2) accumulated in fp32.
 //
 // One workgroup = one work unit = (group of <= 16 rows of one expert = one
-// MFMA column tile, 128 output features).  gate/up: 4 waves x 32 features (two
-// 16-row weight tiles per matrix); down: 2 waves x 64 features (four tiles).
+// MFMA column tile, a block of output features).  4 waves per workgroup, each
+// with several 16-row weight tiles; the block is the widest of 512/256/128
+// features that divides the output width.
 // Weight fragments go straight from HBM into a 4-deep register ring per wave:
 // the packed layout makes each wave's 16-byte-per-lane load one contiguous
 // kilobyte, and every weight byte is used by exactly one wave.  The
@@ -43,6 +44,8 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const u32x4& a, const v8i& b, const 
 // (16 KB), followed by the B scales [term][group][col] as dwords (512 B).  The
 // half h holds the operand bytes 16h..16h+15 of lane (col, g).
 constexpr int kChunkData = 16384;
+constexpr int kRing = 4;           // weight ring slots per wave (4 or 8)
+constexpr int kDownUnitMax = 512;  // widest down work unit (features)
 constexpr int kChunkBytes = kChunkData + 512;
 
 // This thread's share of one chunk (global -> registers -> LDS).  Piece
@@ -81,16 +84,29 @@ struct WFrag {
   u32x4 A[NA];
 };
 
-template <int NA>
-__device__ __forceinline__ void load_w(WFrag<NA>& f, const uint8_t* const (&aq)[NA], int ks) {
-#pragma unroll
-  for (int a = 0; a < NA; ++a) f.A[a] = *(const u32x4*)(aq[a] + (size_t)ks * 1024);
+// Wave-uniform pointer into global memory: kept in scalar registers, so each
+// weight load is "scalar base + one shared per-lane offset".
+typedef const __attribute__((address_space(1))) uint8_t* gptr;
+
+__device__ __forceinline__ gptr uniform_gptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (gptr)(((uint64_t)hi << 32) | lo);
 }
 
 template <int NA>
-__device__ __forceinline__ void load_wscales(uint32_t (&sa)[NA], const uint8_t* const (&as)[NA], int sg) {
+__device__ __forceinline__ void load_w(WFrag<NA>& f, const gptr (&wq)[NA], int ks) {
+  const uint32_t off = (threadIdx.x & 63) * 16 + (uint32_t)ks * 1024;
 #pragma unroll
-  for (int a = 0; a < NA; ++a) sa[a] = *(const uint32_t*)(as[a] + (size_t)sg * 256);
+  for (int a = 0; a < NA; ++a) f.A[a] = *(const __attribute__((address_space(1))) u32x4*)(wq[a] + off);
+}
+
+template <int NA>
+__device__ __forceinline__ void load_wscales(uint32_t (&sa)[NA], const gptr (&ws)[NA], int sg) {
+  const uint32_t off = (threadIdx.x & 63) * 4 + (uint32_t)sg * 256;
+#pragma unroll
+  for (int a = 0; a < NA; ++a) sa[a] = *(const __attribute__((address_space(1))) uint32_t*)(ws[a] + off);
 }
 
 // k-step J of the current chunk: B from LDS, weights from a ring slot.
@@ -108,75 +124,95 @@ __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chun
   }
 }
 
-// K loop.  Weights: a 4-deep register ring (fragments of ks+1..ks+3 in flight
-// while ks is multiplied; weight scales one group of 4 k-steps ahead).
-// Activations: chunk sg+1 is fetched into registers at the start of group sg
-// and written to the other LDS buffer at its end, then one workgroup barrier
-// per group (it waits on LDS traffic only, not on the weight loads in flight).
-// Loads are unconditional (clamped indices) and the sched_barrier(0) points
-// keep their issue order, so each wait on the in-order vector-memory counter
-// covers only what is about to be used.
-template <int NA, int THREADS>
-__device__ __forceinline__ void mainloop(const uint8_t* const (&aq)[NA], const uint8_t* const (&as)[NA],
-                                         const uint8_t* brow_q, const uint8_t* brow_s, int nks, v4f (&acc)[NA],
-                                         uint8_t* lds) {
-  const int lane = threadIdx.x & 63;
+// One group of 4 k-steps (chunk sg of the activations is in LDS buffer sg & 1).
+// Weights: ring slot of step ks is ks % RING; while step ks is multiplied the
+// fragments of ks+1 .. ks+RING-1 are in flight.  GI = position of this group
+// inside a ring cycle (RING/4 groups per cycle), so every slot index and scale
+// byte is a compile-time constant.
+template <int GI, int RING, int NA, int THREADS>
+__device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS>& stage, uint32_t (&sa)[NA],
+                                        uint32_t (&sa_n)[NA], const gptr (&aq)[NA], const gptr (&as)[NA],
+                                        const uint8_t* brow_q,
+                                        const uint8_t* brow_s, int sg, int nks, int n_sg, v4f (&acc)[NA],
+                                        uint8_t* lds) {
+  const int lane = threadIdx.x & 63, last = nks - 1, k0 = 4 * sg;
+  const uint8_t* chunk = lds + (sg & 1) * kChunkBytes;
+  uint32_t sb[2];
+  sb[0] = *(const uint32_t*)(chunk + kChunkData + lane * 4);
+  sb[1] = *(const uint32_t*)(chunk + kChunkData + 256 + lane * 4);
+  stage.load(brow_q, brow_s, min(sg + 1, n_sg - 1), nks, n_sg);
+  load_wscales(sa_n, as, min(sg + 1, n_sg - 1));
+  load_w(f[(4 * GI + RING - 1) % RING], aq, min(k0 + RING - 1, last));
+  __builtin_amdgcn_sched_barrier(0);
+  mma_step<0>(f[(4 * GI) % RING], chunk, sa, sb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(f[(4 * GI + RING) % RING], aq, min(k0 + RING, last));
+  __builtin_amdgcn_sched_barrier(0);
+  if (k0 + 1 < nks) mma_step<1>(f[(4 * GI + 1) % RING], chunk, sa, sb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(f[(4 * GI + RING + 1) % RING], aq, min(k0 + RING + 1, last));
+  __builtin_amdgcn_sched_barrier(0);
+  if (k0 + 2 < nks) mma_step<2>(f[(4 * GI + 2) % RING], chunk, sa, sb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(f[(4 * GI + RING + 2) % RING], aq, min(k0 + RING + 2, last));
+  __builtin_amdgcn_sched_barrier(0);
+  if (k0 + 3 < nks) mma_step<3>(f[(4 * GI + 3) % RING], chunk, sa, sb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  stage.store(lds + ((sg + 1) & 1) * kChunkBytes);
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < NA; ++a) sa[a] = sa_n[a];
+}
+
+// K loop.  Weights: a register ring of RING k-step fragments (RING-1 steps
+// in flight ahead of the one being multiplied; weight scales one group of 4
+// k-steps ahead).  Activations: chunk sg+1 is fetched into registers at the
+// start of group sg and written to the other LDS buffer at its end, then one
+// workgroup barrier per group (it waits on LDS traffic only, not on the weight
+// loads in flight).  Loads are unconditional (clamped indices) and the
+// sched_barrier(0) points keep their issue order, so each wait on the
+// in-order vector-memory counter covers only what is about to be used.
+// RING = 8 needs the group count to be even.
+template <int RING, int NA, int THREADS>
+__device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[NA], const uint8_t* brow_q,
+                                         const uint8_t* brow_s, int nks, v4f (&acc)[NA], uint8_t* lds) {
+  static_assert(RING == 4 || RING == 8, "ring of 1 or 2 groups");
   const int n_sg = (nks + 3) / 4, last = nks - 1;
   ChunkStage<THREADS> stage;
-  WFrag<NA> f0, f1, f2, f3;
-  uint32_t sa[NA], sa_n[NA], sb[2];
+  WFrag<NA> f[RING];
+  uint32_t sa[NA], sa_n[NA];
   stage.load(brow_q, brow_s, 0, nks, n_sg);
   load_wscales(sa, as, 0);
-  load_w(f0, aq, 0);
-  load_w(f1, aq, min(1, last));
-  load_w(f2, aq, min(2, last));
+#pragma unroll
+  for (int i = 0; i < RING - 1; ++i) load_w(f[i], aq, min(i, last));
   stage.store(lds);
   __syncthreads();
-  for (int sg = 0; sg < n_sg; ++sg) {
-    const int k0 = 4 * sg;
-    const uint8_t* chunk = lds + (sg & 1) * kChunkBytes;
-    sb[0] = *(const uint32_t*)(chunk + kChunkData + lane * 4);
-    sb[1] = *(const uint32_t*)(chunk + kChunkData + 256 + lane * 4);
-    stage.load(brow_q, brow_s, min(sg + 1, n_sg - 1), nks, n_sg);
-    load_wscales(sa_n, as, min(sg + 1, n_sg - 1));
-    load_w(f3, aq, min(k0 + 3, last));
-    __builtin_amdgcn_sched_barrier(0);
-    mma_step<0>(f0, chunk, sa, sb, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(f0, aq, min(k0 + 4, last));
-    __builtin_amdgcn_sched_barrier(0);
-    if (k0 + 1 < nks) mma_step<1>(f1, chunk, sa, sb, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(f1, aq, min(k0 + 5, last));
-    __builtin_amdgcn_sched_barrier(0);
-    if (k0 + 2 < nks) mma_step<2>(f2, chunk, sa, sb, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(f2, aq, min(k0 + 6, last));
-    __builtin_amdgcn_sched_barrier(0);
-    if (k0 + 3 < nks) mma_step<3>(f3, chunk, sa, sb, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    stage.store(lds + ((sg + 1) & 1) * kChunkBytes);
-    __syncthreads();
-#pragma unroll
-    for (int a = 0; a < NA; ++a) sa[a] = sa_n[a];
+  for (int sg = 0; sg < n_sg; sg += RING / 4) {
+    k_group<0>(f, stage, sa, sa_n, aq, as, brow_q, brow_s, sg, nks, n_sg, acc, lds);
+    if (RING == 8) k_group<1>(f, stage, sa, sa_n, aq, as, brow_q, brow_s, sg + 1, nks, n_sg, acc, lds);
   }
 }
 
 // ---------------------------------------------------------------------------
 // gate/up: h = silu(min(gate, L)) * clamp(up, -L, L), written as the two-term
 // FP8 split that the down GEMM consumes (same layout as the x split, K = I).
+// Each of the 4 waves takes TPM 16-row tiles of the gate matrix and the same
+// rows of the up matrix: 16*TPM features per wave, 64*TPM per work unit.
 
+template <int TPM>
 __global__ void __launch_bounds__(256) gateup_kernel(ExpertArgs a) {
+  constexpr int NA = 2 * TPM, kFeatWave = 16 * TPM, kFeatUnit = 4 * kFeatWave;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunkBytes];
-  const int n_fb = a.R / kFeatPerWG;
+  const int n_fb = a.R / kFeatUnit;
   int unit;
   if (!xcd_unit(*a.n_groups * n_fb, &unit)) return;
   const Group g = a.groups[unit / n_fb];
   const int fb = unit % n_fb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int K = a.K, R = a.R, nks = K / 128, n_sg = (nks + 3) / 4;
-  const int f0 = fb * kFeatPerWG + wave * kFeatPerWave, rt0 = f0 / 16;
+  const int f0 = fb * kFeatUnit + wave * kFeatWave, rt0 = f0 / 16;
   const bool shared = g.e == a.E;
   const size_t mq = packed_q_bytes(R, K), ms = packed_s_bytes(R, K);
   const uint8_t* gq = shared ? a.sq0 : a.q0 + (size_t)g.e * mq;
@@ -184,121 +220,137 @@ __global__ void __launch_bounds__(256) gateup_kernel(ExpertArgs a) {
   const uint8_t* uq = shared ? a.sq1 : a.q1 + (size_t)g.e * mq;
   const uint8_t* us = shared ? a.ss1 : a.s1 + (size_t)g.e * ms;
   const size_t tq = (size_t)nks * 1024, ts = (size_t)n_sg * 256;  // one 16-row tile
-  const uint8_t* aq[4] = {gq + rt0 * tq + lane * 16, gq + (rt0 + 1) * tq + lane * 16, uq + rt0 * tq + lane * 16,
-                          uq + (rt0 + 1) * tq + lane * 16};
-  const uint8_t* as[4] = {gs + rt0 * ts + lane * 4, gs + (rt0 + 1) * ts + lane * 4, us + rt0 * ts + lane * 4,
-                          us + (rt0 + 1) * ts + lane * 4};
+  gptr aq[NA], as[NA];
+#pragma unroll
+  for (int i = 0; i < TPM; ++i) {
+    aq[i] = uniform_gptr(gq + (rt0 + i) * tq);
+    aq[TPM + i] = uniform_gptr(uq + (rt0 + i) * tq);
+    as[i] = uniform_gptr(gs + (rt0 + i) * ts);
+    as[TPM + i] = uniform_gptr(us + (rt0 + i) * ts);
+  }
   // the token row this thread stages (column tid % 16); padding columns reuse the group's first row
   const int tcol = tid & 15;
   const int p_ld = g.p0 + (tcol < g.cnt ? tcol : 0);
   const int row = shared ? p_ld - a.P : a.perm[p_ld] / a.k;
   const uint8_t* brow_q = a.aq + (size_t)row * split_q_row_bytes(K);
   const uint8_t* brow_s = a.as + (size_t)row * split_s_row_bytes(K);
-  v4f acc[4];
+  v4f acc[NA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  mainloop<4, 256>(aq, as, brow_q, brow_s, nks, acc, lds);
+  for (int i = 0; i < NA; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  if (kRing == 8 && (nks % 8) == 0)
+    mainloop<8, NA, 256>(aq, as, brow_q, brow_s, nks, acc, lds);
+  else
+    mainloop<4, NA, 256>(aq, as, brow_q, brow_s, nks, acc, lds);
 
   const int n_sg_h = (R / 128 + 3) / 4;
-  const int blk_h = f0 / 32;
   const float L = a.limit;
-  float h[8];
+  // each pair of tiles (32 features) is one 32-block of h: 4 lanes (grp 0..3) x 8 values per token
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int b = 0; b < TPM / 2; ++b) {
+    const int blk_h = f0 / 32 + b;
+    float h[8];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      float gv = acc[tt][ii], uv = acc[2 + tt][ii];
-      if (L > 0.f) {
-        gv = fminf(gv, L);
-        uv = fminf(fmaxf(uv, -L), L);
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        float gv = acc[2 * b + tt][ii], uv = acc[TPM + 2 * b + tt][ii];
+        if (L > 0.f) {
+          gv = fminf(gv, L);
+          uv = fminf(fmaxf(uv, -L), L);
+        }
+        h[tt * 4 + ii] = gv / (1.f + __expf(-gv)) * uv;
       }
-      h[tt * 4 + ii] = gv / (1.f + __expf(-gv)) * uv;
-    }
-  // 32-feature block of one token = 4 lanes (grp 0..3) x 8 values
-  float amax = 0.f;
+    float amax = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[j]));
-  amax = shfl_xor_max<16>(amax);
-  amax = shfl_xor_max<32>(amax);
-  const int e1 = split_exponent(amax);
-  const float inv1 = ldexpf(1.f, -e1), sc1 = ldexpf(1.f, e1);
-  uint32_t w1[2], w2[2];
-  float res[8];
-  float amax2 = 0.f;
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    w1[tt] = pack4_fp8(h[4 * tt] * inv1, h[4 * tt + 1] * inv1, h[4 * tt + 2] * inv1, h[4 * tt + 3] * inv1);
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      res[4 * tt + ii] = h[4 * tt + ii] - fp8_byte_to_f32(w1[tt], ii) * sc1;
-      amax2 = fmaxf(amax2, fabsf(res[4 * tt + ii]));
-    }
-  }
-  amax2 = shfl_xor_max<16>(amax2);
-  amax2 = shfl_xor_max<32>(amax2);
-  const int e2 = split_exponent(amax2);
-  const float inv2 = ldexpf(1.f, -e2);
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-    w2[tt] = pack4_fp8(res[4 * tt] * inv2, res[4 * tt + 1] * inv2, res[4 * tt + 2] * inv2, res[4 * tt + 3] * inv2);
-  if (col < g.cnt) {
-    const size_t p = (size_t)g.p0 + col;
-    // feature 16tt + 4grp + ii of block blk_h = 4ks + bb: group 2*(bb%2) + tt, byte 16*(bb/2) + 4grp + ii
-    const int bb = blk_h & 3;
-    uint8_t* dst = a.hq + p * split_q_row_bytes(R) + (size_t)(blk_h >> 2) * 256 + 16 * (bb >> 1) + 4 * grp;
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[j]));
+    amax = shfl_xor_max<16>(amax);
+    amax = shfl_xor_max<32>(amax);
+    const int e1 = split_exponent(amax);
+    const float inv1 = ldexpf(1.f, -e1), sc1 = ldexpf(1.f, e1);
+    uint32_t w1[2], w2[2];
+    float res[8];
+    float amax2 = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      uint8_t* gdst = dst + (2 * (bb & 1) + tt) * 64;
-      *(uint32_t*)(gdst) = w1[tt];
-      *(uint32_t*)(gdst + 32) = w2[tt];
+      w1[tt] = pack4_fp8(h[4 * tt] * inv1, h[4 * tt + 1] * inv1, h[4 * tt + 2] * inv1, h[4 * tt + 3] * inv1);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        res[4 * tt + ii] = h[4 * tt + ii] - fp8_byte_to_f32(w1[tt], ii) * sc1;
+        amax2 = fmaxf(amax2, fabsf(res[4 * tt + ii]));
+      }
     }
-    if (grp == 0) {
-      uint8_t* srow = a.hs + p * split_s_row_bytes(R);
-      srow[split_scale_offset_h(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
-      srow[split_scale_offset_h(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
+    amax2 = shfl_xor_max<16>(amax2);
+    amax2 = shfl_xor_max<32>(amax2);
+    const int e2 = split_exponent(amax2);
+    const float inv2 = ldexpf(1.f, -e2);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+      w2[tt] = pack4_fp8(res[4 * tt] * inv2, res[4 * tt + 1] * inv2, res[4 * tt + 2] * inv2, res[4 * tt + 3] * inv2);
+    if (col < g.cnt) {
+      const size_t p = (size_t)g.p0 + col;
+      // feature 16tt + 4grp + ii of block blk_h = 4ks + bb: group 2*(bb%2) + tt, byte 16*(bb/2) + 4grp + ii
+      const int bb = blk_h & 3;
+      uint8_t* dst = a.hq + p * split_q_row_bytes(R) + (size_t)(blk_h >> 2) * 256 + 16 * (bb >> 1) + 4 * grp;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        uint8_t* gdst = dst + (2 * (bb & 1) + tt) * 64;
+        *(uint32_t*)(gdst) = w1[tt];
+        *(uint32_t*)(gdst + 32) = w2[tt];
+      }
+      if (grp == 0) {
+        uint8_t* srow = a.hs + p * split_s_row_bytes(R);
+        srow[split_scale_offset_h(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
+        srow[split_scale_offset_h(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // down: y[p][f] = sum_n W_down[e][f][n] h[p][n], fp32 rows in expert-major
-// pair order (routed) followed by the shared expert's rows.
+// pair order (routed) followed by the shared expert's rows.  Each of the 4
+// waves takes NA 16-row tiles: 16*NA features per wave, 64*NA per unit.
 
-__global__ void __launch_bounds__(kDownThreads) down_kernel(ExpertArgs a) {
+template <int NA>
+__global__ void __launch_bounds__(256) down_kernel(ExpertArgs a) {
+  constexpr int kFeatWave = 16 * NA, kFeatUnit = 4 * kFeatWave;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunkBytes];
-  const int n_fb = a.R / kFeatPerWG;
+  const int n_fb = a.R / kFeatUnit;
   int unit;
   if (!xcd_unit(*a.n_groups * n_fb, &unit)) return;
   const Group g = a.groups[unit / n_fb];
   const int fb = unit % n_fb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int K = a.K, R = a.R, nks = K / 128, n_sg = (nks + 3) / 4;
-  const int f0 = fb * kFeatPerWG + wave * kDownFeatPerWave, rt0 = f0 / 16;
+  const int f0 = fb * kFeatUnit + wave * kFeatWave, rt0 = f0 / 16;
   const bool shared = g.e == a.E;
   const size_t mq = packed_q_bytes(R, K), ms = packed_s_bytes(R, K);
   const uint8_t* dq = shared ? a.sq0 : a.q0 + (size_t)g.e * mq;
   const uint8_t* ds = shared ? a.ss0 : a.s0 + (size_t)g.e * ms;
   const size_t tq = (size_t)nks * 1024, ts = (size_t)n_sg * 256;
-  const uint8_t* aq[4];
-  const uint8_t* as[4];
+  gptr aq[NA], as[NA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    aq[i] = dq + (rt0 + i) * tq + lane * 16;
-    as[i] = ds + (rt0 + i) * ts + lane * 4;
+  for (int i = 0; i < NA; ++i) {
+    aq[i] = uniform_gptr(dq + (rt0 + i) * tq);
+    as[i] = uniform_gptr(ds + (rt0 + i) * ts);
   }
   const int tcol = tid & 15;
   const size_t p_ld = (size_t)g.p0 + (tcol < g.cnt ? tcol : 0);
   const uint8_t* brow_q = a.aq + p_ld * split_q_row_bytes(K);
   const uint8_t* brow_s = a.as + p_ld * split_s_row_bytes(K);
-  v4f acc[4];
+  v4f acc[NA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  mainloop<4, kDownThreads>(aq, as, brow_q, brow_s, nks, acc, lds);
+  for (int i = 0; i < NA; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  if (kRing == 8 && (nks % 8) == 0)
+    mainloop<8, NA, 256>(aq, as, brow_q, brow_s, nks, acc, lds);
+  else
+    mainloop<4, NA, 256>(aq, as, brow_q, brow_s, nks, acc, lds);
   if (col < g.cnt) {
     float* dst = a.y + ((size_t)g.p0 + col) * R + f0 + 4 * grp;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) *(v4f*)(dst + 16 * tt) = acc[tt];
+    for (int tt = 0; tt < NA; ++tt) *(v4f*)(dst + 16 * tt) = acc[tt];
   }
 }
 
@@ -307,13 +359,24 @@ static unsigned unit_grid(int max_groups, int n_fb) {
   return (unsigned)(kXcds * ((units + kXcds - 1) / kXcds));
 }
 
+// The widest work unit that divides the output width: wider units stage each
+// activation chunk for more weight bytes (less activation traffic per weight byte).
 hipError_t launch_gateup(const ExpertArgs& a, int max_groups, hipStream_t stream) {
-  hipLaunchKernelGGL(gateup_kernel, dim3(unit_grid(max_groups, a.R / kFeatPerWG)), dim3(256), 0, stream, a);
+  if (a.R % 256 == 0)
+    hipLaunchKernelGGL(gateup_kernel<4>, dim3(unit_grid(max_groups, a.R / 256)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(gateup_kernel<2>, dim3(unit_grid(max_groups, a.R / 128)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down(const ExpertArgs& a, int max_groups, hipStream_t stream) {
-  hipLaunchKernelGGL(down_kernel, dim3(unit_grid(max_groups, a.R / kFeatPerWG)), dim3(kDownThreads), 0, stream, a);
+  if (a.R % kDownUnitMax == 0)
+    hipLaunchKernelGGL(down_kernel<kDownUnitMax / 64>, dim3(unit_grid(max_groups, a.R / kDownUnitMax)), dim3(256), 0,
+                       stream, a);
+  else if (a.R % 256 == 0)
+    hipLaunchKernelGGL(down_kernel<4>, dim3(unit_grid(max_groups, a.R / 256)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(down_kernel<2>, dim3(unit_grid(max_groups, a.R / 128)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -20,12 +20,19 @@ def make_config(shape: MoEShape, has_shared: bool = True, route_scale=None, swig
                           float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit))
 
 
-def pack_mxfp4(q: torch.Tensor, s: torch.Tensor, rows: int, K: int, stream=None):
-    """Natural-layout device tensors q [n][rows][K/2], s [n][rows][K/32] -> packed (q, s) device tensors."""
+def pack_mxfp4(q: torch.Tensor, s: torch.Tensor, rows: int, K: int, stream=None, out=None):
+    """Natural-layout device tensors q [n][rows][K/2], s [n][rows][K/32] -> packed (q, s) device tensors.
+
+    out: optional (q_out, s_out) uint8 device tensors of the packed sizes to pack into.
+    """
     n = q.shape[0]
     qb, sb = capi.moe_packed_mxfp4_bytes(rows, K)
-    q_out = torch.empty(n * qb, dtype=torch.uint8, device=q.device)
-    s_out = torch.empty(n * sb, dtype=torch.uint8, device=q.device)
+    if out is None:
+        q_out = torch.empty(n * qb, dtype=torch.uint8, device=q.device)
+        s_out = torch.empty(n * sb, dtype=torch.uint8, device=q.device)
+    else:
+        q_out, s_out = out
+        assert q_out.numel() == n * qb and s_out.numel() == n * sb
     st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
     rc = capi.moe_pack_mxfp4(q.data_ptr(), s.data_ptr(), n, rows, K, q_out.data_ptr(), s_out.data_ptr(), st)
     if rc != capi.MOE_OK:
@@ -33,18 +40,39 @@ def pack_mxfp4(q: torch.Tensor, s: torch.Tensor, rows: int, K: int, stream=None)
     return q_out, s_out
 
 
+_ALIGN = 2 << 20  # each packed region starts on a 2 MiB boundary inside one allocation
+
+
 class PackedExperts:
-    """Routed experts 0..E-1 and the shared expert (index E), packed on the device."""
+    """Routed experts 0..E-1 and the shared expert (index E), packed on the device.
+
+    All packed matrices live in one device allocation, each region 2 MiB
+    aligned, so the weight stream has the same placement from run to run.
+    """
 
     def __init__(self, experts: dict, shape: MoEShape, device, has_shared: bool = True):
         E, d, I = shape.n_experts, shape.d_model, shape.d_ff
+        mats = (("gate", I, d), ("up", I, d), ("down", d, I))
+        regions, total = {}, 0
+        for name, rows, K in mats:
+            qb, sb = capi.moe_packed_mxfp4_bytes(rows, K)
+            for key, count in ((name, E), ("sh_" + name, 1 if has_shared else 0)):
+                if count == 0:
+                    continue
+                for part, nbytes in (("q", count * qb), ("s", count * sb)):
+                    regions[(key, part)] = (total, nbytes)
+                    total += (nbytes + _ALIGN - 1) // _ALIGN * _ALIGN
+        self.buffer = torch.empty(total + _ALIGN, dtype=torch.uint8, device=device)
+        base = (-self.buffer.data_ptr()) % _ALIGN
+        view = lambda key, part: self.buffer[base + regions[(key, part)][0]:][:regions[(key, part)][1]]
         self.t = {}
-        for name, rows, K in (("gate", I, d), ("up", I, d), ("down", d, I)):
+        for name, rows, K in mats:
             q = torch.from_numpy(np.ascontiguousarray(experts[name + "_q"])).to(device)
             s = torch.from_numpy(np.ascontiguousarray(experts[name + "_s"])).to(device)
-            self.t[name] = pack_mxfp4(q[:E], s[:E], rows, K)
+            self.t[name] = pack_mxfp4(q[:E], s[:E], rows, K, out=(view(name, "q"), view(name, "s")))
             if has_shared:
-                self.t["sh_" + name] = pack_mxfp4(q[E:E + 1], s[E:E + 1], rows, K)
+                self.t["sh_" + name] = pack_mxfp4(q[E:E + 1], s[E:E + 1], rows, K,
+                                                  out=(view("sh_" + name, "q"), view("sh_" + name, "s")))
             del q, s
         torch.cuda.synchronize(device)
         self.has_shared = has_shared
