@@ -121,13 +121,14 @@ typedef struct moe_args {
   size_t workspace_bytes;
   /* Optional stage timing (NULL to skip): MOE_N_STAGE_EVENTS hipEvent_t handles
    * created by the caller.  Event i is recorded on `stream` just before stage i
-   * and the last one after the final stage; the stages are
-   * 0 activation split, 1 router logits, 2 top-k/hash selection, 3 routing
-   * bookkeeping, 4 gate/up GEMM, 5 down GEMM, 6 combine. */
+   * and the last one after the final stage; a NULL entry is not recorded
+   * (each recorded event costs a few microseconds of stream time).  The
+   * stages are 0 router logits + activation split, 1 top-k/hash selection +
+   * routing bookkeeping, 2 gate/up GEMM, 3 down GEMM, 4 combine. */
   void* const* stage_events;
 } moe_args_t;
 
-#define MOE_N_STAGES 7
+#define MOE_N_STAGES 5
 #define MOE_N_STAGE_EVENTS (MOE_N_STAGES + 1)
 
 /* Library version (MOE_MXFP4_VERSION). */

@@ -35,9 +35,9 @@ class MoeArgs(ctypes.Structure):
                 ("workspace", c_vp), ("workspace_bytes", c_size), ("stage_events", c_vp)]
 
 
-MOE_N_STAGES = 7
+MOE_N_STAGES = 5
 MOE_N_STAGE_EVENTS = MOE_N_STAGES + 1
-STAGE_NAMES = ("split", "router_logits", "select", "route", "gateup", "down", "combine")
+STAGE_NAMES = ("router", "select_route", "gateup", "down", "combine")
 
 
 _lib = None

@@ -398,24 +398,38 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     gw[j] = (j < k) ? gates[(size_t)r * k + j] : 0.f;
   }
   const float* ysh = has_shared ? y + ((size_t)P + r) * d : nullptr;
-  for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4) {
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
+  // kU chunks of 4 features per thread: all of their loads are issued first
+  constexpr int kU = 4;
+  const int step = blockDim.x * 4;
+  for (int c0 = threadIdx.x * 4; c0 < d; c0 += kU * step) {
+    v4f v[kU][kMaxK + 1];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < k) {
-        const v4f v = *(const v4f*)(src[j] + c);
+    for (int u = 0; u < kU; ++u) {
+      const int c = min(c0 + u * step, d - 4);  // past the end: re-read the last chunk (not stored)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(gw[j], v[i], acc[i]);
-      }
+      for (int j = 0; j < kMaxK; ++j)
+        if (j < k) v[u][j] = *(const v4f*)(src[j] + c);
+      v[u][kMaxK] = ysh ? *(const v4f*)(ysh + c) : v4f{0.f, 0.f, 0.f, 0.f};
     }
-    v4f sh = {0.f, 0.f, 0.f, 0.f};
-    if (ysh) sh = *(const v4f*)(ysh + c);
-    uint2 packed;
-    packed.x = (uint32_t)f32_to_bf16_rne(fmaf(route_scale, acc[0], sh[0])) |
-               ((uint32_t)f32_to_bf16_rne(fmaf(route_scale, acc[1], sh[1])) << 16);
-    packed.y = (uint32_t)f32_to_bf16_rne(fmaf(route_scale, acc[2], sh[2])) |
-               ((uint32_t)f32_to_bf16_rne(fmaf(route_scale, acc[3], sh[3])) << 16);
-    *(uint2*)(out + (size_t)r * d + c) = packed;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + u * step;
+      if (c >= d) break;
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j)
+        if (j < k) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = fmaf(gw[j], v[u][j][i], acc[i]);
+        }
+      const v4f sh = v[u][kMaxK];
+      uint2 packed;
+      packed.x = (uint32_t)f32_to_bf16_rne(fmaf(route_scale, acc[0], sh[0])) |
+                 ((uint32_t)f32_to_bf16_rne(fmaf(route_scale, acc[1], sh[1])) << 16);
+      packed.y = (uint32_t)f32_to_bf16_rne(fmaf(route_scale, acc[2], sh[2])) |
+                 ((uint32_t)f32_to_bf16_rne(fmaf(route_scale, acc[3], sh[3])) << 16);
+      *(uint2*)(out + (size_t)r * d + c) = packed;
+    }
   }
 }
 

@@ -25,17 +25,20 @@ __host__ __device__ inline size_t split_s_row_bytes(int K) {
 hipError_t launch_pack_mxfp4(const uint8_t* q, const uint8_t* s, int n_mat, int rows, int K, uint8_t* q_out,
                              uint8_t* s_out, hipStream_t stream);
 
-hipError_t launch_split_bf16(const uint16_t* x, int n_rows, int K, uint8_t* xq, uint8_t* xs, hipStream_t stream);
+hipError_t launch_prologue(const uint16_t* x, const float* w, const float* bias, int n_rows, int d, int E, float* z,
+                           uint8_t* xq, uint8_t* xs, int32_t* done, hipStream_t stream);
 
-hipError_t launch_router_logits(const uint16_t* x, const float* w, const float* bias, int n_rows, int d, int E,
-                                float* z, hipStream_t stream);
+hipError_t launch_select_route(const float* z, int n_rows, int E, int k, int routing, const int32_t* token_ids,
+                               const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, int has_shared,
+                               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, Group* groups,
+                               int32_t* n_groups, int32_t* hist, int32_t* done, hipStream_t stream);
 
-hipError_t launch_select(const float* z, int n_rows, int E, int k, int routing, const int32_t* token_ids,
-                         const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, hipStream_t stream);
-
-hipError_t launch_route(const int32_t* idx, int n_rows, int k, int E, int has_shared, int32_t* counts,
-                        int32_t* offsets, int32_t* perm, int32_t* inv, Group* groups, int32_t* n_groups,
-                        hipStream_t stream);
+// Selection workgroups (16 rows each) and the size of their per-expert
+// histogram rows (E rounded up to 4 int32).
+inline int route_workgroups(int n_rows) { return (n_rows + 15) / 16; }
+inline size_t route_hist_bytes(int n_rows, int E) {
+  return (size_t)route_workgroups(n_rows) * (size_t)((E + 3) & ~3) * 4;
+}
 
 struct ExpertArgs {
   // weights of the routed experts (E matrices) and of the shared expert
@@ -60,7 +63,7 @@ hipError_t launch_down(const ExpertArgs& a, int max_groups, hipStream_t stream);
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* gates, int n_rows, int d, int k,
                           int P, int has_shared, float route_scale, uint16_t* out, hipStream_t stream);
 
-// Worst-case number of work groups for n_rows rows: sum_e ceil(c_e/32) <= ceil(P/32) + E, plus the shared rows.
+// Worst-case number of work groups for n_rows rows: sum_e ceil(c_e/16) <= ceil(P/16) + E, plus the shared rows.
 inline int max_work_groups(int n_rows, int k, int E, int has_shared) {
   const long P = (long)n_rows * k;
   return (int)((P + kGroupRows - 1) / kGroupRows + E + (has_shared ? (n_rows + kGroupRows - 1) / kGroupRows : 0));

@@ -12,7 +12,7 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, xq, xs, hq, hs, y, total;
+  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, hist, done, xq, xs, hq, hs, y, total;
   int max_groups;
 };
 
@@ -37,6 +37,8 @@ Layout make_layout(const moe_config_t& c, int n) {
   L.inv = take(P * 4);
   L.groups = take((size_t)L.max_groups * sizeof(Group));
   L.n_groups = take(4);
+  L.hist = take(route_hist_bytes(n, c.n_experts));
+  L.done = take(4);
   L.xq = take(N * split_q_row_bytes(c.d_model));
   L.xs = take(N * split_s_row_bytes(c.d_model));
   L.hq = take(Ptot * split_q_row_bytes(c.d_ff));
@@ -171,23 +173,20 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   float* y = (float*)(ws + L.y);
   const int P = N * k;
 
+  int32_t* hist = (int32_t*)(ws + L.hist);
+  int32_t* done = (int32_t*)(ws + L.done);
   hipError_t err;
   auto mark = [&](int i) -> bool {
-    return !a.stage_events || hipEventRecord((hipEvent_t)a.stage_events[i], stream) == hipSuccess;
+    return !a.stage_events || !a.stage_events[i] ||
+           hipEventRecord((hipEvent_t)a.stage_events[i], stream) == hipSuccess;
   };
   if (!mark(0)) return MOE_ERR_HIP;
-  if ((err = launch_split_bf16((const uint16_t*)a.x, N, d, xq, xs, stream)) != hipSuccess) return MOE_ERR_HIP;
+  if ((err = launch_prologue((const uint16_t*)a.x, a.router_w, a.router_bias, N, d, E, z, xq, xs, done, stream)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
-  if ((err = launch_router_logits((const uint16_t*)a.x, a.router_w, a.router_bias, N, d, E, z, stream)) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
-  if (!mark(2)) return MOE_ERR_HIP;
-  if ((err = launch_select(z, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, stream)) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
-  if (!mark(3)) return MOE_ERR_HIP;
-  if ((err = launch_route(idx, N, k, E, c.has_shared, counts, offsets, perm, inv, groups, n_groups, stream)) !=
-      hipSuccess)
+  if ((err = launch_select_route(z, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, c.has_shared,
+                                 counts, offsets, perm, inv, groups, n_groups, hist, done, stream)) != hipSuccess)
     return MOE_ERR_HIP;
 
   ExpertArgs ga;
@@ -213,7 +212,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   ga.limit = c.swiglu_limit;
   ga.hq = hq;
   ga.hs = hs;
-  if (!mark(4)) return MOE_ERR_HIP;
+  if (!mark(2)) return MOE_ERR_HIP;
   if ((err = launch_gateup(ga, L.max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
 
   ExpertArgs da = ga;
@@ -229,14 +228,14 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   da.R = d;
   da.hq = da.hs = nullptr;
   da.y = y;
-  if (!mark(5)) return MOE_ERR_HIP;
+  if (!mark(3)) return MOE_ERR_HIP;
   if ((err = launch_down(da, L.max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
-  if (!mark(6)) return MOE_ERR_HIP;
+  if (!mark(4)) return MOE_ERR_HIP;
 
   if ((err = launch_combine(y, inv, gates, N, d, k, P, c.has_shared, c.route_scale, (uint16_t*)a.out, stream)) !=
       hipSuccess)
     return MOE_ERR_HIP;
-  if (!mark(7)) return MOE_ERR_HIP;
+  if (!mark(5)) return MOE_ERR_HIP;
   return MOE_OK;
 }
 
