@@ -6,9 +6,9 @@
 // q2*2^e2), so every product is weight * (q1 + q2) accumulated in fp32.
 //
 // One workgroup = one work unit = (group of <= 16 rows of one expert = one
-// MFMA column tile, a block of output features).  4 waves per workgroup, each
-// with several 16-row weight tiles; the block is the widest of 512/256/128
-// features that divides the output width.
+// MFMA column tile, a block of output features).  4 or 8 waves per workgroup,
+// each with several 16-row weight tiles; the block is the widest that divides
+// the output width.
 // Weight fragments go straight from HBM into a 4-deep register ring per wave:
 // the packed layout makes each wave's 16-byte-per-lane load one contiguous
 // kilobyte, and every weight byte is used by exactly one wave.  The
@@ -196,12 +196,13 @@ __device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[
 // ---------------------------------------------------------------------------
 // gate/up: h = silu(min(gate, L)) * clamp(up, -L, L), written as the two-term
 // FP8 split that the down GEMM consumes (same layout as the x split, K = I).
-// Each of the 4 waves takes TPM 16-row tiles of the gate matrix and the same
-// rows of the up matrix: 16*TPM features per wave, 64*TPM per work unit.
+// Each of the WAVES waves takes TPM 16-row tiles of the gate matrix and the
+// same rows of the up matrix: 16*TPM features per wave, 16*TPM*WAVES per work
+// unit.
 
-template <int TPM>
-__global__ void __launch_bounds__(256) gateup_kernel(ExpertArgs a) {
-  constexpr int NA = 2 * TPM, kFeatWave = 16 * TPM, kFeatUnit = 4 * kFeatWave;
+template <int TPM, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
+  constexpr int NA = 2 * TPM, kFeatWave = 16 * TPM, kFeatUnit = WAVES * kFeatWave, kThreads = 64 * WAVES;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunkBytes];
   const int n_fb = a.R / kFeatUnit;
   int unit;
@@ -238,9 +239,9 @@ __global__ void __launch_bounds__(256) gateup_kernel(ExpertArgs a) {
 #pragma unroll
   for (int i = 0; i < NA; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   if (kRing == 8 && (nks % 8) == 0)
-    mainloop<8, NA, 256>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<8, NA, kThreads>(aq, as, brow_q, brow_s, nks, acc, lds);
   else
-    mainloop<4, NA, 256>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<4, NA, kThreads>(aq, as, brow_q, brow_s, nks, acc, lds);
 
   const int n_sg_h = (R / 128 + 3) / 4;
   const float L = a.limit;
@@ -308,12 +309,13 @@ __global__ void __launch_bounds__(256) gateup_kernel(ExpertArgs a) {
 
 // ---------------------------------------------------------------------------
 // down: y[p][f] = sum_n W_down[e][f][n] h[p][n], fp32 rows in expert-major
-// pair order (routed) followed by the shared expert's rows.  Each of the 4
-// waves takes NA 16-row tiles: 16*NA features per wave, 64*NA per unit.
+// pair order (routed) followed by the shared expert's rows.  Each of the
+// WAVES waves takes NA 16-row tiles: 16*NA features per wave, 16*NA*WAVES per
+// unit.
 
-template <int NA>
-__global__ void __launch_bounds__(256) down_kernel(ExpertArgs a) {
-  constexpr int kFeatWave = 16 * NA, kFeatUnit = 4 * kFeatWave;
+template <int NA, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
+  constexpr int kFeatWave = 16 * NA, kFeatUnit = WAVES * kFeatWave, kThreads = 64 * WAVES;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunkBytes];
   const int n_fb = a.R / kFeatUnit;
   int unit;
@@ -344,9 +346,9 @@ __global__ void __launch_bounds__(256) down_kernel(ExpertArgs a) {
 #pragma unroll
   for (int i = 0; i < NA; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   if (kRing == 8 && (nks % 8) == 0)
-    mainloop<8, NA, 256>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<8, NA, kThreads>(aq, as, brow_q, brow_s, nks, acc, lds);
   else
-    mainloop<4, NA, 256>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<4, NA, kThreads>(aq, as, brow_q, brow_s, nks, acc, lds);
   if (col < g.cnt) {
     float* dst = a.y + ((size_t)g.p0 + col) * R + f0 + 4 * grp;
 #pragma unroll
@@ -360,23 +362,41 @@ static unsigned unit_grid(int max_groups, int n_fb) {
 }
 
 // The widest work unit that divides the output width: wider units stage each
-// activation chunk for more weight bytes (less activation traffic per weight byte).
+// activation chunk for more weight bytes (less activation traffic per weight
+// byte).  For gate/up, 8-wave units halve that traffic again once the batch
+// has enough pairs (kWideUnitPairs) to give every CU several of them.
+constexpr int kWideUnitPairs = 1024;
+
+template <int TPM, int WAVES>
+static void gateup_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
+  hipLaunchKernelGGL((gateup_kernel<TPM, WAVES>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
+                     dim3(64 * WAVES), 0, stream, a);
+}
+
+template <int NA, int WAVES>
+static void down_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
+  hipLaunchKernelGGL((down_kernel<NA, WAVES>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
+                     dim3(64 * WAVES), 0, stream, a);
+}
+
 hipError_t launch_gateup(const ExpertArgs& a, int max_groups, hipStream_t stream) {
-  if (a.R % 256 == 0)
-    hipLaunchKernelGGL(gateup_kernel<4>, dim3(unit_grid(max_groups, a.R / 256)), dim3(256), 0, stream, a);
+  if (a.P >= kWideUnitPairs && a.R % 512 == 0)
+    gateup_launch<4, 8>(a, max_groups, stream);
+  else if (a.R % 256 == 0)
+    gateup_launch<4, 4>(a, max_groups, stream);
   else
-    hipLaunchKernelGGL(gateup_kernel<2>, dim3(unit_grid(max_groups, a.R / 128)), dim3(256), 0, stream, a);
+    gateup_launch<2, 4>(a, max_groups, stream);
   return hipGetLastError();
 }
 
+// (8-wave down units measured slower: the down GEMM keeps 4-wave units.)
 hipError_t launch_down(const ExpertArgs& a, int max_groups, hipStream_t stream) {
   if (a.R % kDownUnitMax == 0)
-    hipLaunchKernelGGL(down_kernel<kDownUnitMax / 64>, dim3(unit_grid(max_groups, a.R / kDownUnitMax)), dim3(256), 0,
-                       stream, a);
+    down_launch<kDownUnitMax / 64, 4>(a, max_groups, stream);
   else if (a.R % 256 == 0)
-    hipLaunchKernelGGL(down_kernel<4>, dim3(unit_grid(max_groups, a.R / 256)), dim3(256), 0, stream, a);
+    down_launch<4, 4>(a, max_groups, stream);
   else
-    hipLaunchKernelGGL(down_kernel<2>, dim3(unit_grid(max_groups, a.R / 128)), dim3(256), 0, stream, a);
+    down_launch<2, 4>(a, max_groups, stream);
   return hipGetLastError();
 }
 

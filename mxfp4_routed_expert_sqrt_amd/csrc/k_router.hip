@@ -1,6 +1,7 @@
 // Router and routing bookkeeping, in two launches:
-//  1. prologue: fp32 router logits (MFMA) and, in the same grid, the two-term
-//     FP8 split of x for the expert GEMMs;
+//  1. prologue: router logits (bf16 MFMA on an exact three-term split of the
+//     fp32 weights) and, in the same grid, the two-term FP8 split of x for the
+//     expert GEMMs;
 //  2. select+route: sqrt-softplus scores with a wave-level top-k per row, and
 //     the expert-major bookkeeping (histogram, scan, stable permute, work
 //     list), which the last workgroup to finish its rows performs.
@@ -10,71 +11,140 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// z[r][e] = sum_i x[r][i] * W[e][i] + bias[e], fp32 accumulation on
-// v_mfma_f32_16x16x4_f32 (bf16 x is exact in fp32).  A workgroup computes one
-// 16-row x 16-expert tile; its 4 waves take one quarter of K each and the
-// partial tiles are added in wave order through LDS.  Each lane loads 8
-// consecutive K values of its row and of its expert per 32-wide k-chunk (lane
-// group g supplies k = k0 + 8g + i to MFMA i, for A and B alike), and 4 chunks
-// are loaded before any is multiplied.
-__device__ __forceinline__ void logits_tile(const uint16_t* __restrict__ x, const float* __restrict__ w,
-                                            const float* __restrict__ bias, int n_rows, int d, int E,
-                                            float* __restrict__ z, int r0, int e0, float (*part)[16][17]) {
+// Router logits z[r][e] = sum_i x[r][i] * W[e][i] on bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation) without loss of precision:
+// each fp32 weight is cut into three bf16 terms by truncation,
+//   hi = w with the low 16 bits cleared, mid = (w - hi) likewise, lo = w - hi - mid,
+// where both differences are exact and lo has at most 8 significant bits, so
+// hi + mid + lo = w exactly; bf16 x times a bf16 term is exact in fp32.  The
+// three products are accumulated like the fp32 dot product, in a different
+// order.
+//
+// A workgroup computes a 64-row x 64-expert tile over one of S contiguous
+// K-ranges (split-K when the row count gives too few tiles).  K advances in
+// 64-wide chunks staged through LDS: the workgroup reads the chunk's x rows
+// (bf16) and W rows (fp32) with row-contiguous 16-byte loads into registers
+// one chunk ahead, and stores them to one of two LDS buffers whose rows are
+// padded by 16 bytes so that the 16 rows of an MFMA fragment fall in distinct
+// banks.  Wave w takes experts e0+16w..e0+16w+15 as the B operand (it alone
+// splits those weights) against four 16-row blocks of x as A operands; lane
+// group g supplies k = kk+8g..kk+8g+7 of each 32-wide k-step for A and B
+// alike.  The partial sums go to z_part[s][r][e]; the selection adds the S
+// partials in s order and the bias.
+constexpr int kLgRows = 64, kLgExperts = 64, kLgChunk = 64;
+constexpr int kLgXStride = kLgChunk * 2 + 16;  // bytes per x row in LDS
+constexpr int kLgWStride = kLgChunk * 4 + 16;  // bytes per W row in LDS
+constexpr int kLgBufBytes = kLgRows * kLgXStride + kLgExperts * kLgWStride;
+
+__host__ __device__ inline int logits_row_tiles(int n_rows) { return (n_rows + kLgRows - 1) / kLgRows; }
+
+struct LgRegs {
+  u32x4 x[2];  // pieces t and t+256 of the x chunk: row p/8, 16-byte column p%8
+  u32x4 w[4];  // pieces t+256i of the W chunk: expert p/16, column p%16
+};
+
+__device__ __forceinline__ void lg_fetch(LgRegs& g, const uint16_t* __restrict__ x, const float* __restrict__ w,
+                                         int n_rows, int d, int E, int r0, int e0, int k0) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = t + 256 * i, row = min(r0 + (p >> 3), n_rows - 1);
+    g.x[i] = *(const u32x4*)(x + (size_t)row * d + k0 + 8 * (p & 7));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = t + 256 * i, ex = min(e0 + (p >> 4), E - 1);
+    g.w[i] = *(const u32x4*)(w + (size_t)ex * d + k0 + 4 * (p & 15));
+  }
+}
+
+__device__ __forceinline__ void lg_stash(const LgRegs& g, uint8_t* buf) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = t + 256 * i;
+    *(u32x4*)(buf + (p >> 3) * kLgXStride + 16 * (p & 7)) = g.x[i];
+  }
+  uint8_t* wb = buf + kLgRows * kLgXStride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = t + 256 * i;
+    *(u32x4*)(wb + (p >> 4) * kLgWStride + 16 * (p & 15)) = g.w[i];
+  }
+}
+
+// One 32-wide k-step (kk within the chunk) of the wave's 64x16 tile from LDS.
+__device__ __forceinline__ void lg_step(const uint8_t* buf, int kk, v4f* acc) {
+  typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int ra = min(r0 + col, n_rows - 1);  // A operand row of this lane (clamped; result discarded)
-  const int eb = min(e0 + col, E - 1);       // B operand expert of this lane
-  const int kq = d / 4, kbeg = wave * kq;    // kq is a multiple of 32
-  const uint16_t* xp = x + (size_t)ra * d + kbeg + 8 * grp;
-  const float* wp = w + (size_t)eb * d + kbeg + 8 * grp;
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int kUnroll = 4;
-  int kk = 0;
-  for (; kk + 32 * kUnroll <= kq; kk += 32 * kUnroll) {
-    u32x4 xa[kUnroll];
-    float4 wa[kUnroll], wb[kUnroll];
+  const float* wr = (const float*)(buf + kLgRows * kLgXStride + (16 * wave + col) * kLgWStride) + kk + 8 * grp;
+  const float4 b0 = *(const float4*)wr, b1 = *(const float4*)(wr + 4);
+  const float wv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  uint32_t hi[8], mid[8], lo[8];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      xa[u] = *(const u32x4*)(xp + kk + 32 * u);
-      wa[u] = *(const float4*)(wp + kk + 32 * u);
-      wb[u] = *(const float4*)(wp + kk + 32 * u + 4);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // all 4 chunks in flight before the first multiply
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float wv[8] = {wa[u].x, wa[u].y, wa[u].z, wa[u].w, wb[u].x, wb[u].y, wb[u].z, wb[u].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t pair = xa[u][i >> 1];
-        const float xv = __uint_as_float((i & 1) ? (pair & 0xffff0000u) : (pair << 16));
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, wv[i], acc, 0, 0, 0);
-      }
-    }
+  for (int i = 0; i < 8; ++i) {
+    hi[i] = __float_as_uint(wv[i]) & 0xffff0000u;
+    const float r1 = wv[i] - __uint_as_float(hi[i]);
+    mid[i] = __float_as_uint(r1) & 0xffff0000u;
+    lo[i] = __float_as_uint(r1 - __uint_as_float(mid[i]));
   }
-  for (; kk < kq; kk += 32) {
-    const u32x4 xa = *(const u32x4*)(xp + kk);
-    const float4 wa = *(const float4*)(wp + kk), wb = *(const float4*)(wp + kk + 4);
-    const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+  u32x4 th, tm, tl;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t pair = xa[i >> 1];
-      const float xv = __uint_as_float((i & 1) ? (pair & 0xffff0000u) : (pair << 16));
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, wv[i], acc, 0, 0, 0);
-    }
+  for (int j = 0; j < 4; ++j) {  // upper halves of elements 2j (low) and 2j+1 (high)
+    th[j] = __builtin_amdgcn_perm(hi[2 * j + 1], hi[2 * j], 0x07060302u);
+    tm[j] = __builtin_amdgcn_perm(mid[2 * j + 1], mid[2 * j], 0x07060302u);
+    tl[j] = __builtin_amdgcn_perm(lo[2 * j + 1], lo[2 * j], 0x07060302u);
   }
-  // lane holds D[row 4*grp + i][expert col]
+  const v8bf bh = __builtin_bit_cast(v8bf, th), bm = __builtin_bit_cast(v8bf, tm), bl = __builtin_bit_cast(v8bf, tl);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) part[wave][4 * grp + i][col] = acc[i];
+  for (int rb = 0; rb < 4; ++rb) {
+    const v8bf av = *(const v8bf*)(buf + (16 * rb + col) * kLgXStride + 2 * (kk + 8 * grp));
+    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[rb], 0, 0, 0);
+    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bm, acc[rb], 0, 0, 0);
+    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[rb], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void logits_tile(const uint16_t* __restrict__ x, const float* __restrict__ w, int n_rows,
+                                            int d, int E, int S, float* __restrict__ z_part, int tile,
+                                            uint8_t* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int n_rt = logits_row_tiles(n_rows), n_et = (E + kLgExperts - 1) / kLgExperts;
+  const int rt = tile % n_rt, et = (tile / n_rt) % n_et, sp = tile / (n_rt * n_et);
+  const int r0 = rt * kLgRows, e0 = et * kLgExperts;
+  const int nch = d / kLgChunk, c_beg = sp * nch / S, c_end = (sp + 1) * nch / S;
+  v4f acc[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) acc[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+  LgRegs g;
+  lg_fetch(g, x, w, n_rows, d, E, r0, e0, c_beg * kLgChunk);
+  lg_stash(g, lds);
+  if (c_beg + 1 < c_end) lg_fetch(g, x, w, n_rows, d, E, r0, e0, (c_beg + 1) * kLgChunk);
   __syncthreads();
-  const int t = threadIdx.x, rr = t >> 4, ee = t & 15;
-  const int r = r0 + rr, e = e0 + ee;
-  if (r < n_rows && e < E) {
-    float v = part[0][rr][ee];
-    v += part[1][rr][ee];
-    v += part[2][rr][ee];
-    v += part[3][rr][ee];
-    if (bias) v += bias[e];
-    z[(size_t)r * E + e] = v;
+  for (int c = c_beg; c < c_end; ++c) {
+    uint8_t* cur = lds + ((c - c_beg) & 1) * kLgBufBytes;
+    uint8_t* nxt = lds + ((c - c_beg + 1) & 1) * kLgBufBytes;
+    lg_step(cur, 0, acc);
+    lg_step(cur, 32, acc);
+    if (c + 1 < c_end) {
+      lg_stash(g, nxt);  // chunk c+1, loaded during chunk c
+      if (c + 2 < c_end) lg_fetch(g, x, w, n_rows, d, E, r0, e0, (c + 2) * kLgChunk);
+    }
+    __syncthreads();
+  }
+  // lane holds D[row 4*grp + i][expert col] of each row block
+  const int e = e0 + 16 * wave + col;
+  if (e < E) {
+    float* zp = z_part + (size_t)sp * logits_partial_stride(n_rows, E) + e;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 16 * rb + 4 * grp + i;
+        if (r < n_rows) zp[(size_t)r * E] = acc[rb][i];
+      }
   }
 }
 
@@ -82,27 +152,27 @@ __device__ __forceinline__ void logits_tile(const uint16_t* __restrict__ x, cons
 // 32-value block per thread).  Workgroup 0 also clears the completion counter
 // of the select+route launch that follows on the stream.
 __global__ void __launch_bounds__(256) prologue_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
-                                                        const float* __restrict__ bias, int n_rows, int d, int E,
-                                                        float* __restrict__ z, uint8_t* __restrict__ xq,
+                                                        int n_rows, int d, int E, int S, int n_tiles,
+                                                        float* __restrict__ z_part, uint8_t* __restrict__ xq,
                                                         uint8_t* __restrict__ xs, int32_t* __restrict__ done) {
-  __shared__ float part[4][16][17];
-  const int n_rt = (n_rows + 15) / 16, n_tiles = n_rt * ((E + 15) / 16);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kLgBufBytes];
   const int b = blockIdx.x;
   if (b == 0 && threadIdx.x == 0) *done = 0;
   if (b < n_tiles) {
-    logits_tile(x, w, bias, n_rows, d, E, z, (b % n_rt) * 16, (b / n_rt) * 16, part);
+    logits_tile(x, w, n_rows, d, E, S, z_part, b, lds);
   } else {
     const size_t t = (size_t)(b - n_tiles) * blockDim.x + threadIdx.x;
     if (t < (size_t)n_rows * (d / 32)) split_bf16_block(x, d, xq, xs, t);
   }
 }
 
-hipError_t launch_prologue(const uint16_t* x, const float* w, const float* bias, int n_rows, int d, int E, float* z,
+hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d, int E, float* z_part,
                            uint8_t* xq, uint8_t* xs, int32_t* done, hipStream_t stream) {
-  const int n_tiles = ((n_rows + 15) / 16) * ((E + 15) / 16);
+  const int S = logits_splits(n_rows, E, d);
+  const int n_tiles = logits_row_tiles(n_rows) * ((E + kLgExperts - 1) / kLgExperts) * S;
   const size_t n_split = ((size_t)n_rows * (d / 32) + 255) / 256;
-  hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)(n_tiles + n_split)), dim3(256), 0, stream, x, w, bias, n_rows,
-                     d, E, z, xq, xs, done);
+  hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)(n_tiles + n_split)), dim3(256), 0, stream, x, w, n_rows, d, E,
+                     S, n_tiles, z_part, xq, xs, done);
   return hipGetLastError();
 }
 
@@ -161,20 +231,23 @@ __device__ __forceinline__ void wave_best(float& bv, int& be) {
   be = re;
 }
 
-__device__ __forceinline__ void select_row(const float* __restrict__ z, int r, int E, int k, int routing,
-                                           const int32_t* __restrict__ token_ids,
+// NC = score slots per lane the code is unrolled for (expert c*64 + lane in
+// slot c); E <= 64*NC.  Instantiated for 1, 2, 4, 8 and 16 slots so that the
+// selection loops run over no more slots than E needs.
+template <int NC>
+__device__ __forceinline__ void select_row(const float* zr /* LDS: the row's logits */, int r, int E, int k,
+                                           int routing, const int32_t* __restrict__ token_ids,
                                            const int32_t* __restrict__ tid2eid, int64_t vocab,
                                            int32_t* __restrict__ idx, float* __restrict__ gates,
                                            int32_t* sel_lds) {
   const int lane = threadIdx.x & 63;
-  const float* zr = z + (size_t)r * E;
-  const int nc = (E + 63) / 64;  // score slots per lane in use
+  const int nc = (E + 63) / 64;  // score slots per lane in use (<= NC)
   int sel[kMaxTopK];
   float sv[kMaxTopK];
   if (routing == 0) {
-    float s[kMaxExpertsPerLane];
+    float s[NC];
 #pragma unroll
-    for (int c = 0; c < kMaxExpertsPerLane; ++c) {
+    for (int c = 0; c < NC; ++c) {
       const int e = c * 64 + lane;
       s[c] = -INFINITY;
       if (c < nc && e < E) s[c] = router_score(zr[e]);
@@ -189,7 +262,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ z, int r, i
         float bv = -INFINITY;
         int be = kNoExpert;
 #pragma unroll
-        for (int c = 0; c < kMaxExpertsPerLane; ++c) {
+        for (int c = 0; c < NC; ++c) {
           const int e = c * 64 + lane;
           if (c < nc && e < E && !((taken >> c) & 1u) && better(s[c], e, bv, be)) {
             bv = s[c];
@@ -326,11 +399,12 @@ __device__ __forceinline__ void write_groups(const int32_t* s_cnt, const int32_t
 // on a device-scope counter (cleared by the prologue launch); the workgroup
 // that finishes last sees every workgroup's results and runs step 2.
 __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
-    const float* __restrict__ z, int n_rows, int E, int k, int routing, const int32_t* __restrict__ token_ids,
+    const float* __restrict__ z, int n_split, const float* __restrict__ bias, int n_rows, int E, int k, int routing, const int32_t* __restrict__ token_ids,
     const int32_t* __restrict__ tid2eid, int64_t vocab, int32_t* __restrict__ idx, float* __restrict__ gates,
     int has_shared, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, Group* __restrict__ groups, int32_t* __restrict__ n_groups, int32_t* hist,
     int32_t* done, int scatter_here) {
+  extern __shared__ float s_z[];  // [16][E] logits of the workgroup's rows
   __shared__ int32_t s_sel[kRouteWaves * kMaxTopK];
   __shared__ int32_t s_a[kMaxExperts];      // step 1: histogram; step 2: counts
   __shared__ int32_t s_off[kMaxExperts];    // step 2: offsets
@@ -342,10 +416,55 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
   const int Ep = (E + 3) & ~3;
   const int P = n_rows * k;
 
+  // logits of the workgroup's rows into LDS: the split-K partials (stride
+  // n_rows*E) added in split order, then the bias
+  {
+    // the block's logits are contiguous in each partial and start on a 16-byte
+    // boundary (16*b*E floats; the partial stride is padded to 4 floats)
+    const int r0 = b * kRouteWaves, cnt = min(kRouteWaves, n_rows - r0) * E;
+    const float* zb = z + (size_t)r0 * E;
+    const size_t zstride = logits_partial_stride(n_rows, E);
+    for (int i = 4 * tid; i < cnt; i += 4 * kRouteThreads) {
+      if (i + 4 <= cnt) {
+        float4 v = *(const float4*)(zb + i);
+#pragma unroll 8
+        for (int sp = 1; sp < n_split; ++sp) {
+          const float4 u = *(const float4*)(zb + sp * zstride + i);
+          v.x += u.x;
+          v.y += u.y;
+          v.z += u.z;
+          v.w += u.w;
+        }
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_z[i + j] = bias ? vv[j] + bias[(i + j) % E] : vv[j];
+      } else {
+        for (int j = i; j < cnt; ++j) {
+          float v = zb[j];
+          for (int sp = 1; sp < n_split; ++sp) v += zb[sp * zstride + j];
+          s_z[j] = bias ? v + bias[j % E] : v;
+        }
+      }
+    }
+  }
   // step 1
   for (int e = tid; e < Ep; e += kRouteThreads) s_a[e] = 0;
+  __syncthreads();
   const int r = b * kRouteWaves + wave;
-  if (r < n_rows) select_row(z, r, E, k, routing, token_ids, tid2eid, vocab, idx, gates, s_sel + wave * k);
+  if (r < n_rows) {
+    const float* zr = s_z + wave * E;
+    int32_t* sl = s_sel + wave * k;
+    if (E <= 64)
+      select_row<1>(zr, r, E, k, routing, token_ids, tid2eid, vocab, idx, gates, sl);
+    else if (E <= 128)
+      select_row<2>(zr, r, E, k, routing, token_ids, tid2eid, vocab, idx, gates, sl);
+    else if (E <= 256)
+      select_row<4>(zr, r, E, k, routing, token_ids, tid2eid, vocab, idx, gates, sl);
+    else if (E <= 512)
+      select_row<8>(zr, r, E, k, routing, token_ids, tid2eid, vocab, idx, gates, sl);
+    else
+      select_row<kMaxExpertsPerLane>(zr, r, E, k, routing, token_ids, tid2eid, vocab, idx, gates, sl);
+  }
   __syncthreads();
   const int q0 = b * kRouteWaves * k;
   const int nq = min(kRouteWaves, n_rows - b * kRouteWaves) * k;
@@ -486,15 +605,23 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
 // thread); above it the scatter is its own launch.
 constexpr int kScatterInBlockMax = 8 * kRouteThreads;
 
-hipError_t launch_select_route(const float* z, int n_rows, int E, int k, int routing, const int32_t* token_ids,
+hipError_t launch_select_route(const float* z, const float* bias, int d, int n_rows, int E, int k, int routing, const int32_t* token_ids,
                                const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, int has_shared,
                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, Group* groups,
                                int32_t* n_groups, int32_t* hist, int32_t* done, hipStream_t stream) {
   if (E > kMaxExperts || k > kMaxTopK) return hipErrorInvalidValue;
+  static bool attr_set = false;  // one-time raise of the dynamic LDS limit (64 KB at E = 1024)
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute((const void*)select_route_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)(sizeof(float) * kRouteWaves * kMaxExperts));
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
   const int P = n_rows * k;
   const int here = P <= kScatterInBlockMax;
-  hipLaunchKernelGGL(select_route_kernel, dim3((unsigned)route_workgroups(n_rows)), dim3(kRouteThreads), 0, stream,
-                     z, n_rows, E, k, routing, token_ids, tid2eid, vocab, idx, gates, has_shared, counts, offsets,
+  const size_t lds = sizeof(float) * kRouteWaves * E;
+  hipLaunchKernelGGL(select_route_kernel, dim3((unsigned)route_workgroups(n_rows)), dim3(kRouteThreads), lds, stream,
+                     z, logits_splits(n_rows, E, d), bias, n_rows, E, k, routing, token_ids, tid2eid, vocab, idx, gates, has_shared, counts, offsets,
                      perm, inv, groups, n_groups, hist, done, here);
   if (!here) {
     hipError_t err = hipGetLastError();

@@ -25,10 +25,24 @@ __host__ __device__ inline size_t split_s_row_bytes(int K) {
 hipError_t launch_pack_mxfp4(const uint8_t* q, const uint8_t* s, int n_mat, int rows, int K, uint8_t* q_out,
                              uint8_t* s_out, hipStream_t stream);
 
-hipError_t launch_prologue(const uint16_t* x, const float* w, const float* bias, int n_rows, int d, int E, float* z,
-                           uint8_t* xq, uint8_t* xs, int32_t* done, hipStream_t stream);
+hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d, int E, float* z_part, uint8_t* xq,
+                           uint8_t* xs, int32_t* done, hipStream_t stream);
 
-hipError_t launch_select_route(const float* z, int n_rows, int E, int k, int routing, const int32_t* token_ids,
+// Split-K factor of the router logits: enough 64x64 tiles for >= 256
+// workgroups, at most 16 partials and at least two 64-wide K chunks each.
+__host__ __device__ inline int logits_splits(int n_rows, int E, int d) {
+  const int tiles = ((n_rows + 63) / 64) * ((E + 63) / 64);
+  int S = (256 + tiles - 1) / tiles;
+  S = S < 16 ? S : 16;
+  S = S < d / 128 ? S : d / 128;
+  return S > 1 ? S : 1;
+}
+// Floats between consecutive logits partials (n_rows*E rounded up to 4).
+__host__ __device__ inline size_t logits_partial_stride(int n_rows, int E) {
+  return ((size_t)n_rows * E + 3) & ~(size_t)3;
+}
+
+hipError_t launch_select_route(const float* z, const float* bias, int d, int n_rows, int E, int k, int routing, const int32_t* token_ids,
                                const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, int has_shared,
                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, Group* groups,
                                int32_t* n_groups, int32_t* hist, int32_t* done, hipStream_t stream);

@@ -28,7 +28,7 @@ Layout make_layout(const moe_config_t& c, int n) {
     off = align256(off + bytes);
     return at;
   };
-  L.z = take(N * E * 4);
+  L.z = take((size_t)logits_splits(n, c.n_experts, c.d_model) * logits_partial_stride(n, c.n_experts) * 4);
   L.idx = take(P * 4);
   L.gates = take(P * 4);
   L.counts = take(E * 4);
@@ -181,11 +181,10 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
            hipEventRecord((hipEvent_t)a.stage_events[i], stream) == hipSuccess;
   };
   if (!mark(0)) return MOE_ERR_HIP;
-  if ((err = launch_prologue((const uint16_t*)a.x, a.router_w, a.router_bias, N, d, E, z, xq, xs, done, stream)) !=
-      hipSuccess)
+  if ((err = launch_prologue((const uint16_t*)a.x, a.router_w, N, d, E, z, xq, xs, done, stream)) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
-  if ((err = launch_select_route(z, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, c.has_shared,
+  if ((err = launch_select_route(z, a.router_bias, d, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, c.has_shared,
                                  counts, offsets, perm, inv, groups, n_groups, hist, done, stream)) != hipSuccess)
     return MOE_ERR_HIP;
 

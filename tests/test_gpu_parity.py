@@ -141,6 +141,9 @@ EDGE = {
     "k1": MoEShape("edge_k1", 40, 256, 16, 1, 128, "topk", "tiny"),
     "e20_k8": MoEShape("edge_e20_k8", 70, 384, 20, 8, 256, "topk", "edge20"),
     "hash_small": MoEShape("edge_hash", 50, 256, 16, 2, 128, "hash", "tiny", vocab=97),
+    # more than 256 experts: 6 and 16 score slots per lane in the selection
+    "e384_k6": MoEShape("edge_e384_k6", 96, 256, 384, 6, 128, "topk", "edge384"),
+    "e1000_k4": MoEShape("edge_e1000_k4", 64, 128, 1000, 4, 128, "topk", "edge1000"),
 }
 
 
