@@ -181,7 +181,7 @@ hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d,
 // softplus(z) = max(z,0) + log1p(exp(-|z|)).  Top-k mode takes the k largest
 // scores (equal scores: lower expert id first) by k rounds of a wave argmax;
 // hash mode takes tid2eid[token_ids[r]].  Selected ids are written ascending
-// with gates = s / sum(s) (summed in ascending id order).
+// with gates = s / sum(s).
 
 __device__ __forceinline__ float router_score(float zv) {
   return sqrtf(fmaxf(zv, 0.f) + log1pf(expf(-fabsf(zv))));
@@ -189,51 +189,52 @@ __device__ __forceinline__ float router_score(float zv) {
 
 constexpr int kMaxExpertsPerLane = 16;  // E <= 1024
 constexpr int kMaxTopK = 8;
-constexpr int kNoExpert = 0x7fffffff;
 
-// (value, id) order used by the selection: larger value first, then lower id;
-// an empty candidate (id kNoExpert) loses to any real one.
-__device__ __forceinline__ bool better(float v, int e, float bv, int be) {
-  return e != kNoExpert && (be == kNoExpert || v > bv || (v == bv && e < be));
+// Selection keys: score bits in the high word (scores are >= +0, so their
+// bit patterns order like the values; a NaN score sorts above every number)
+// and the complemented expert id in the low word, so that of two equal scores
+// the lower id has the larger key.  Every real candidate has a key > 0; a
+// taken or absent candidate is 0.
+__device__ __forceinline__ uint64_t sel_key(float score, int e) {
+  return ((uint64_t)(__float_as_uint(score) & 0x7fffffffu) << 32) | (uint32_t)~e;  // -0 as +0
 }
 
-// One DPP step of the (value, id) max-reduction inside each row of 16 lanes.
-template <int kCtrl>
-__device__ __forceinline__ void dpp_best(float& bv, int& be) {
-  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), kCtrl, 0xF, 0xF, false));
-  const int oe = __builtin_amdgcn_update_dpp(kNoExpert, be, kCtrl, 0xF, 0xF, false);
-  if (better(ov, oe, bv, be)) {
-    bv = ov;
-    be = oe;
-  }
+// max(v, v from the lane named by the DPP control); rows outside kRowMask keep v.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, kCtrl, kRowMask, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, kCtrl, kRowMask, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
 }
 
-// Best (value, id) over the wave, returned uniform in every lane: DPP
-// exchanges within rows of 16 lanes (xor 1, xor 2, rotate 4, rotate 8), then
-// the four row results are read out and compared in scalar registers.
-__device__ __forceinline__ void wave_best(float& bv, int& be) {
-  dpp_best<0xB1>(bv, be);   // quad_perm [1,0,3,2]
-  dpp_best<0x4E>(bv, be);   // quad_perm [2,3,0,1]
-  dpp_best<0x124>(bv, be);  // row_ror:4
-  dpp_best<0x128>(bv, be);  // row_ror:8
-  float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
-  int re = __builtin_amdgcn_readlane(be, 0);
-#pragma unroll
-  for (int row = 1; row < 4; ++row) {
-    const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * row));
-    const int oe = __builtin_amdgcn_readlane(be, 16 * row);
-    if (better(ov, oe, rv, re)) {
-      rv = ov;
-      re = oe;
-    }
-  }
-  bv = rv;
-  be = re;
+// Largest key of the wave, uniform: DPP within rows of 16 lanes (xor 1,
+// xor 2, rotate 4, rotate 8), then row 0 -> 1 and 2 -> 3 (row_bcast:15) and
+// rows 0-1 -> 2-3 (row_bcast:31), so lane 63 ends with the maximum.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  v = dpp_max<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max<0x124, 0xF>(v);  // row_ror:4
+  v = dpp_max<0x128, 0xF>(v);  // row_ror:8
+  v = dpp_max<0x142, 0xA>(v);  // row_bcast:15
+  v = dpp_max<0x143, 0xC>(v);  // row_bcast:31
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // NC = score slots per lane the code is unrolled for (expert c*64 + lane in
 // slot c); E <= 64*NC.  Instantiated for 1, 2, 4, 8 and 16 slots so that the
-// selection loops run over no more slots than E needs.
+// selection runs over no more slots than E needs.
+//
+// Top-k mode: k rounds of (lane-local max key, wave max key); the winner's key
+// is zeroed, so the k winners are distinct and come out by descending score
+// (equal scores: lower id first).  Hash mode: the ids tid2eid[token_ids[r]].
+// Lane j < k then takes the j-th selected id; its output slot is its rank in
+// (id, j) order, so the ids are written ascending (a repeated hash id keeps
+// table order), and gate = score / (sum of the k scores, added in selection
+// order).
 template <int NC>
 __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's logits */, int r, int E, int k,
                                            int routing, const int32_t* __restrict__ token_ids,
@@ -241,44 +242,32 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
                                            int32_t* __restrict__ idx, float* __restrict__ gates,
                                            int32_t* sel_lds) {
   const int lane = threadIdx.x & 63;
-  const int nc = (E + 63) / 64;  // score slots per lane in use (<= NC)
   int sel[kMaxTopK];
   float sv[kMaxTopK];
   if (routing == 0) {
-    float s[NC];
+    uint64_t key[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = c * 64 + lane;
-      s[c] = -INFINITY;
-      if (c < nc && e < E) s[c] = router_score(zr[e]);
+      key[c] = e < E ? sel_key(router_score(zr[e]), e) : 0ull;
     }
-    uint32_t taken = 0;  // bit c: expert c*64 + lane already selected
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j < k) {
-        // lane-local best among untaken experts; the first candidate is always
-        // accepted, so some untaken id wins even if scores are NaN and the
-        // selection stays a set of k distinct valid ids
-        float bv = -INFINITY;
-        int be = kNoExpert;
+        uint64_t m = key[0];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int e = c * 64 + lane;
-          if (c < nc && e < E && !((taken >> c) & 1u) && better(s[c], e, bv, be)) {
-            bv = s[c];
-            be = e;
-          }
-        }
-        wave_best(bv, be);
-        sel[j] = be;
-        sv[j] = bv;
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        for (int c = 1; c < NC; ++c) m = key[c] > m ? key[c] : m;
+        m = wave_max_key(m);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) key[c] = key[c] == m ? 0ull : key[c];
+        sel[j] = (int)~(uint32_t)m;
+        sv[j] = __uint_as_float((uint32_t)(m >> 32));
       }
     }
   } else {
-    // Hash mode.  Table entries must be valid (distinct ids in [0, E)); an
-    // invalid token id or expert id is clamped into range so that a bad table
-    // gives an unspecified routing but never an out-of-bounds access.
+    // Table entries must be valid (ids in [0, E)); an out-of-range token id
+    // or expert id is clamped into range so that a bad table gives an
+    // unspecified routing but never an out-of-bounds access.
     const int64_t t = min(max((int64_t)token_ids[r], (int64_t)0), vocab - 1);
     const int32_t* row = tid2eid + t * k;
 #pragma unroll
@@ -289,30 +278,27 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
       }
     }
   }
-  // ascending expert id (k <= 8: compare-exchange passes on wave-uniform values)
-#pragma unroll
-  for (int pass = 0; pass < kMaxTopK; ++pass)
-#pragma unroll
-    for (int b = 1; b < kMaxTopK; ++b)
-      if (b < k && sel[b - 1] > sel[b]) {
-        const int te = sel[b];
-        sel[b] = sel[b - 1];
-        sel[b - 1] = te;
-        const float tv = sv[b];
-        sv[b] = sv[b - 1];
-        sv[b - 1] = tv;
-      }
   float sum = 0.f;
+  int my_id = 0;
+  float my_sv = 0.f;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j)
-    if (j < k) sum += sv[j];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j)
-    if (j < k && lane == j) {
-      idx[(size_t)r * k + j] = sel[j];
-      gates[(size_t)r * k + j] = sv[j] / sum;
-      sel_lds[j] = sel[j];
+    if (j < k) {
+      sum += sv[j];
+      if (lane == j) {
+        my_id = sel[j];
+        my_sv = sv[j];
+      }
     }
+  int rank = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxTopK; ++i)
+    if (i < k) rank += (sel[i] < my_id || (sel[i] == my_id && i < lane)) ? 1 : 0;
+  if (lane < k) {
+    idx[(size_t)r * k + rank] = my_id;
+    gates[(size_t)r * k + rank] = my_sv / sum;
+    sel_lds[rank] = my_id;
+  }
 }
 
 // ---------------------------------------------------------------------------
