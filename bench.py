@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 EXPERT_BYTES_NOTE = "gate+up MXFP4 bytes of every touched expert (incl. shared) + x and h at 2 B/value"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_verify512_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_verify512_traffic.txt")
 
 
 def parse():
@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+                    help="also run one elementwise kernel over 1 GiB (reads 1 GiB, writes 1 GiB: the reference "
+                         "for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -84,9 +85,9 @@ def recorded_traffic(workload):
     vals = {}
     with open(TRAFFIC_FILE) as f:
         for line in f:
-            if line.startswith("- ") and ":" in line:
-                k, v = line[2:].split(":", 1)
-                vals[k.strip()] = v.strip().strip("`")
+            parts = line.split()
+            if len(parts) == 2 and not line.startswith("#"):
+                vals[parts[0]] = parts[1]
     if vals.get("kernel_source_digest") != kernel_source_digest():
         return None
     try:
@@ -199,9 +200,12 @@ def main():
             hip.destroy(e)
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # one elementwise kernel that reads 1 GiB and writes 1 GiB (a device copy may go to a DMA engine,
+        # whose traffic the per-kernel counters do not see)
+        src = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.cuda.synchronize()
+        torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
