@@ -32,6 +32,33 @@ __device__ __forceinline__ bool xcd_unit(int n_units, int* unit) {
   return true;
 }
 
+// Like xcd_unit, in half units: each XCD's contiguous range of units is taken
+// whole, except its last `tail_units`, which are taken one half at a time
+// (two workgroups each), so the XCD's final round of work is half as long.
+// Sets *half_idx = 2*unit + half (half = 0 for a whole unit) and *is_half.
+__device__ __forceinline__ bool xcd_unit_split(int n_units, int tail_units, int* half_idx, bool* is_half) {
+  const int bid = blockIdx.x;
+  const int xcd = bid % kXcds, slot = bid / kXcds;
+  const int H = 2 * n_units;
+  int per = (H + kXcds - 1) / kXcds;
+  per += per & 1;  // whole units never straddle two XCDs
+  const int h0 = xcd * per;
+  const int hx = min(per, max(0, H - h0));
+  const int tail = min(hx, 2 * tail_units);
+  const int n_whole = (hx - tail) / 2;
+  if (slot < n_whole) {
+    *half_idx = h0 + 2 * slot;
+    *is_half = false;
+    return true;
+  }
+  if (slot < n_whole + tail) {
+    *half_idx = h0 + 2 * n_whole + (slot - n_whole);
+    *is_half = true;
+    return true;
+  }
+  return false;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

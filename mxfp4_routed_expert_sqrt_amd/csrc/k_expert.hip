@@ -200,20 +200,16 @@ __device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[
 // same rows of the up matrix: 16*TPM features per wave, 16*TPM*WAVES per work
 // unit.
 
+// One work unit: features [fu0, fu0 + WAVES*16*TPM) of gate and up for the
+// rows of group g.
 template <int TPM, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
-  constexpr int NA = 2 * TPM, kFeatWave = 16 * TPM, kFeatUnit = WAVES * kFeatWave, kThreads = 64 * WAVES;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunkBytes];
-  const int n_fb = a.R / kFeatUnit;
-  int unit;
-  if (!xcd_unit(*a.n_groups * n_fb, &unit)) return;
-  const Group g = a.groups[unit / n_fb];
-  const int fb = unit % n_fb;
+__device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
+  constexpr int NA = 2 * TPM, kFeatWave = 16 * TPM, kThreads = 64 * WAVES;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int K = a.K, R = a.R, nks = K / 128, n_sg = (nks + 3) / 4;
-  const int f0 = fb * kFeatUnit + wave * kFeatWave, rt0 = f0 / 16;
+  const int f0 = fu0 + wave * kFeatWave, rt0 = f0 / 16;
   const bool shared = g.e == a.E;
   const size_t mq = packed_q_bytes(R, K), ms = packed_s_bytes(R, K);
   const uint8_t* gq = shared ? a.sq0 : a.q0 + (size_t)g.e * mq;
@@ -307,6 +303,26 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
   }
 }
 
+template <int TPM, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
+  constexpr int kFeatUnit = WAVES * 16 * TPM;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunkBytes];
+  const int n_fb = a.R / kFeatUnit;
+  int half_idx;
+  bool is_half;
+  if (!xcd_unit_split(*a.n_groups * n_fb, TPM >= 4 ? a.tail_units : 0, &half_idx, &is_half)) return;
+  const int unit = half_idx >> 1;
+  const Group g = a.groups[unit / n_fb];
+  const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
+  if constexpr (TPM >= 4) {
+    if (is_half) {
+      gateup_unit<TPM / 2, WAVES>(a, g, fu0, lds);
+      return;
+    }
+  }
+  gateup_unit<TPM, WAVES>(a, g, fu0, lds);
+}
+
 // ---------------------------------------------------------------------------
 // down: y[p][f] = sum_n W_down[e][f][n] h[p][n], fp32 rows in expert-major
 // pair order (routed) followed by the shared expert's rows.  Each of the
@@ -314,19 +330,13 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
 // unit.
 
 template <int NA, int WAVES>
-__global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
-  constexpr int kFeatWave = 16 * NA, kFeatUnit = WAVES * kFeatWave, kThreads = 64 * WAVES;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunkBytes];
-  const int n_fb = a.R / kFeatUnit;
-  int unit;
-  if (!xcd_unit(*a.n_groups * n_fb, &unit)) return;
-  const Group g = a.groups[unit / n_fb];
-  const int fb = unit % n_fb;
+__device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
+  constexpr int kFeatWave = 16 * NA, kThreads = 64 * WAVES;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int K = a.K, R = a.R, nks = K / 128, n_sg = (nks + 3) / 4;
-  const int f0 = fb * kFeatUnit + wave * kFeatWave, rt0 = f0 / 16;
+  const int f0 = fu0 + wave * kFeatWave, rt0 = f0 / 16;
   const bool shared = g.e == a.E;
   const size_t mq = packed_q_bytes(R, K), ms = packed_s_bytes(R, K);
   const uint8_t* dq = shared ? a.sq0 : a.q0 + (size_t)g.e * mq;
@@ -356,9 +366,32 @@ __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   }
 }
 
+template <int NA, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
+  constexpr int kFeatUnit = WAVES * 16 * NA;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunkBytes];
+  const int n_fb = a.R / kFeatUnit;
+  int half_idx;
+  bool is_half;
+  if (!xcd_unit_split(*a.n_groups * n_fb, NA >= 2 ? a.tail_units : 0, &half_idx, &is_half)) return;
+  const int unit = half_idx >> 1;
+  const Group g = a.groups[unit / n_fb];
+  const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
+  if constexpr (NA >= 2) {
+    if (is_half) {
+      down_unit<NA / 2, WAVES>(a, g, fu0, lds);
+      return;
+    }
+  }
+  down_unit<NA, WAVES>(a, g, fu0, lds);
+}
+
+// Enough workgroups for every unit to be taken in halves (see xcd_unit_split).
 static unsigned unit_grid(int max_groups, int n_fb) {
-  const size_t units = (size_t)max_groups * n_fb;
-  return (unsigned)(kXcds * ((units + kXcds - 1) / kXcds));
+  const size_t halves = 2 * (size_t)max_groups * n_fb;
+  size_t per = (halves + kXcds - 1) / kXcds;
+  per += per & 1;
+  return (unsigned)(kXcds * per);
 }
 
 // The widest work unit that divides the output width: wider units stage each
@@ -379,7 +412,15 @@ static void down_launch(const ExpertArgs& a, int max_groups, hipStream_t stream)
                      dim3(64 * WAVES), 0, stream, a);
 }
 
-hipError_t launch_gateup(const ExpertArgs& a, int max_groups, hipStream_t stream) {
+// Small batches (fewer than kWideUnitPairs routed pairs, e.g. 8 rows: about
+// one round of units) take the last kSmallTailUnits units of each XCD range in
+// halves, which puts twice as many CUs to work; on larger batches halves
+// measured slightly slower (more activation staging per weight byte).
+constexpr int kSmallTailUnits = 64;
+
+hipError_t launch_gateup(const ExpertArgs& a0, int max_groups, hipStream_t stream) {
+  ExpertArgs a = a0;
+  a.tail_units = a.P < kWideUnitPairs ? kSmallTailUnits : 0;
   if (a.P >= kWideUnitPairs && a.R % 512 == 0)
     gateup_launch<4, 8>(a, max_groups, stream);
   else if (a.R % 256 == 0)
@@ -390,7 +431,9 @@ hipError_t launch_gateup(const ExpertArgs& a, int max_groups, hipStream_t stream
 }
 
 // (8-wave down units measured slower: the down GEMM keeps 4-wave units.)
-hipError_t launch_down(const ExpertArgs& a, int max_groups, hipStream_t stream) {
+hipError_t launch_down(const ExpertArgs& a0, int max_groups, hipStream_t stream) {
+  ExpertArgs a = a0;
+  a.tail_units = a.P < kWideUnitPairs ? kSmallTailUnits : 0;
   if (a.R % kDownUnitMax == 0)
     down_launch<kDownUnitMax / 64, 4>(a, max_groups, stream);
   else if (a.R % 256 == 0)

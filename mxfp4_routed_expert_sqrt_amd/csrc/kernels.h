@@ -69,6 +69,7 @@ struct ExpertArgs {
   uint8_t* hq;                           // gate/up output: split h bytes
   uint8_t* hs;                           // gate/up output: split h scales
   float* y;                              // down output [pairs][R]
+  int tail_units;                        // units per XCD processed as two halves at the end
 };
 
 hipError_t launch_gateup(const ExpertArgs& a, int max_groups, hipStream_t stream);
