@@ -11,6 +11,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kGroupRows = 16;   // token rows of one grouped-GEMM work unit (one MFMA column tile)
+constexpr int kTallGroupRows = 64;  // token rows of a tall work unit (4 column tiles)
 constexpr int kXcds = 8;         // gfx950: workgroups are dealt round-robin to 8 XCDs
 
 // One work unit of the grouped GEMMs: rows [p0, p0 + cnt) of expert e.

@@ -48,34 +48,46 @@ constexpr int kRing = 4;           // weight ring slots per wave (4 or 8)
 constexpr int kDownUnitMax = 512;  // widest down work unit (features)
 constexpr int kChunkBytes = kChunkData + 512;
 
-// This thread's share of one chunk (global -> registers -> LDS).  Piece
-// p = tid + THREADS*m (16 bytes) of the chunk is (j, t, h, g, col) =
-// (p>>8, p>>7 & 1, p>>6 & 1, p>>4 & 3, p & 15); col = tid % 16 for every m,
-// so each thread reads one token row.
-template <int THREADS>
+// This thread's share of one chunk of NB column tiles (global -> registers ->
+// LDS).  Tile t of a chunk buffer sits at t * kChunkBytes.  Piece
+// p = tid + THREADS*m (16 bytes) of the chunk belongs to tile p >> 10, and
+// inside it is (j, t, h, g, col) = (p>>8 & 3, p>>7 & 1, p>>6 & 1, p>>4 & 3,
+// p & 15); col = tid % 16 for every m, so each thread reads one token row per
+// tile.  THREADS divides 1024, so the tile of piece m is (THREADS*m) >> 10.
+// Thread tid < 128*NB also carries one scale dword of tile tid >> 7.
+template <int THREADS, int NB>
 struct ChunkStage {
-  static constexpr int kPieces = 1024 / THREADS;
+  static_assert(1024 % THREADS == 0 && THREADS >= 128 * NB, "chunk staging shape");
+  static constexpr int kPieces = 1024 * NB / THREADS;
   u32x4 q[kPieces];
   uint32_t s;
 
-  __device__ __forceinline__ void load(const uint8_t* brow_q, const uint8_t* brow_s, int sg, int nks, int n_sg) {
+  // brow_q[t]: this thread's token row of tile t; brow_s: the scale row of tile tid >> 7
+  __device__ __forceinline__ void load(const uint8_t* const (&brow_q)[NB], const uint8_t* brow_s, int sg, int nks,
+                                       int n_sg) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < kPieces; ++m) {
-      const int p = tid + THREADS * m;
+      const int tile = (THREADS * m) >> 10;
+      const int p = (tid + THREADS * m) & 1023;
       const int j = p >> 8, t = (p >> 7) & 1, h = (p >> 6) & 1, g = (p >> 4) & 3;
       const int ks = min(4 * sg + j, nks - 1);  // past the end: any valid step (never multiplied)
-      q[m] = *(const u32x4*)(brow_q + (size_t)ks * 256 + g * 64 + t * 32 + h * 16);
+      q[m] = *(const u32x4*)(brow_q[tile] + (size_t)ks * 256 + g * 64 + t * 32 + h * 16);
     }
-    const int t = (tid >> 6) & 1, g = (tid >> 4) & 3;
-    s = *(const uint32_t*)(brow_s + (size_t)(t * n_sg + sg) * 16 + g * 4);
+    if (tid < 128 * NB) {
+      const int t = (tid >> 6) & 1, g = (tid >> 4) & 3;
+      s = *(const uint32_t*)(brow_s + (size_t)(t * n_sg + sg) * 16 + g * 4);
+    }
   }
 
-  __device__ __forceinline__ void store(uint8_t* chunk) const {
+  __device__ __forceinline__ void store(uint8_t* buf) const {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int m = 0; m < kPieces; ++m) *(u32x4*)(chunk + (tid + THREADS * m) * 16) = q[m];
-    if (tid < 128) *(uint32_t*)(chunk + kChunkData + tid * 4) = s;
+    for (int m = 0; m < kPieces; ++m) {
+      const int tile = (THREADS * m) >> 10;
+      *(u32x4*)(buf + tile * kChunkBytes + ((tid + THREADS * m) & 1023) * 16) = q[m];
+    }
+    if (tid < 128 * NB) *(uint32_t*)(buf + (tid >> 7) * kChunkBytes + kChunkData + (tid & 127) * 4) = s;
   }
 };
 
@@ -109,18 +121,35 @@ __device__ __forceinline__ void load_wscales(uint32_t (&sa)[NA], const gptr (&ws
   for (int a = 0; a < NA; ++a) sa[a] = *(const __attribute__((address_space(1))) uint32_t*)(ws[a] + off);
 }
 
-// k-step J of the current chunk: B from LDS, weights from a ring slot.
-template <int J, int NA>
+// k-step J of the current chunk: B (NB column tiles) from LDS, weights from a
+// ring slot; every weight fragment meets every column tile.  The 2*NB B
+// fragments (tile tt, term t at i = 2tt + t) are double-buffered: fragment
+// i+1 is read from LDS before fragment i's MFMAs are issued, so the LDS
+// latency is covered by MFMA work.
+template <int J>
+__device__ __forceinline__ v8i read_b(const uint8_t* chunk, int i) {
+  const int lane = threadIdx.x & 63, tt = i >> 1, t = i & 1;
+  const uint8_t* c = chunk + tt * kChunkBytes + (J * 2 + t) * 2048 + lane * 16;
+  const u32x4 lo = *(const u32x4*)c;
+  const u32x4 hi = *(const u32x4*)(c + 1024);
+  return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+template <int J, int NA, int NB>
 __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chunk, const uint32_t (&sa)[NA],
-                                         const uint32_t (&sb)[2], v4f (&acc)[NA]) {
-  const int lane = threadIdx.x & 63;
+                                         const uint32_t (&sb)[NB][2], v4f (&acc)[NA][NB]) {
+  constexpr int NF = 2 * NB;
+  v8i b0 = read_b<J>(chunk, 0), b1;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const u32x4 lo = *(const u32x4*)(chunk + ((J * 2 + t) * 2 + 0) * 1024 + lane * 16);
-    const u32x4 hi = *(const u32x4*)(chunk + ((J * 2 + t) * 2 + 1) * 1024 + lane * 16);
-    const v8i b = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  for (int i = 0; i < NF; ++i) {
+    v8i& cur = (i & 1) ? b1 : b0;
+    v8i& nxt = (i & 1) ? b0 : b1;
+    if (i + 1 < NF) nxt = read_b<J>(chunk, i + 1);
+    if (NF > 2) __builtin_amdgcn_sched_barrier(0);  // keep the read ahead of these MFMAs
 #pragma unroll
-    for (int a = 0; a < NA; ++a) acc[a] = mfma_fp4_fp8<J>(f.A[a], b, acc[a], sa[a], sb[t]);
+    for (int a = 0; a < NA; ++a)
+      acc[a][i >> 1] = mfma_fp4_fp8<J>(f.A[a], cur, acc[a][i >> 1], sa[a], sb[i >> 1][i & 1]);
+    if (NF > 2) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -129,17 +158,20 @@ __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chun
 // fragments of ks+1 .. ks+RING-1 are in flight.  GI = position of this group
 // inside a ring cycle (RING/4 groups per cycle), so every slot index and scale
 // byte is a compile-time constant.
-template <int GI, int RING, int NA, int THREADS>
-__device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS>& stage, uint32_t (&sa)[NA],
+template <int GI, int RING, int NA, int THREADS, int NB>
+__device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB>& stage, uint32_t (&sa)[NA],
                                         uint32_t (&sa_n)[NA], const gptr (&aq)[NA], const gptr (&as)[NA],
-                                        const uint8_t* brow_q,
-                                        const uint8_t* brow_s, int sg, int nks, int n_sg, v4f (&acc)[NA],
-                                        uint8_t* lds) {
+                                        const uint8_t* const (&brow_q)[NB], const uint8_t* brow_s, int sg, int nks,
+                                        int n_sg, v4f (&acc)[NA][NB], uint8_t* lds) {
+  constexpr int kBuf = NB * kChunkBytes;
   const int lane = threadIdx.x & 63, last = nks - 1, k0 = 4 * sg;
-  const uint8_t* chunk = lds + (sg & 1) * kChunkBytes;
-  uint32_t sb[2];
-  sb[0] = *(const uint32_t*)(chunk + kChunkData + lane * 4);
-  sb[1] = *(const uint32_t*)(chunk + kChunkData + 256 + lane * 4);
+  const uint8_t* chunk = lds + (sg & 1) * kBuf;
+  uint32_t sb[NB][2];
+#pragma unroll
+  for (int tt = 0; tt < NB; ++tt) {
+    sb[tt][0] = *(const uint32_t*)(chunk + tt * kChunkBytes + kChunkData + lane * 4);
+    sb[tt][1] = *(const uint32_t*)(chunk + tt * kChunkBytes + kChunkData + 256 + lane * 4);
+  }
   stage.load(brow_q, brow_s, min(sg + 1, n_sg - 1), nks, n_sg);
   load_wscales(sa_n, as, min(sg + 1, n_sg - 1));
   load_w(f[(4 * GI + RING - 1) % RING], aq, min(k0 + RING - 1, last));
@@ -158,7 +190,7 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
   __builtin_amdgcn_sched_barrier(0);
   if (k0 + 3 < nks) mma_step<3>(f[(4 * GI + 3) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
-  stage.store(lds + ((sg + 1) & 1) * kChunkBytes);
+  stage.store(lds + ((sg + 1) & 1) * kBuf);
   __syncthreads();
 #pragma unroll
   for (int a = 0; a < NA; ++a) sa[a] = sa_n[a];
@@ -173,12 +205,12 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
 // sched_barrier(0) points keep their issue order, so each wait on the
 // in-order vector-memory counter covers only what is about to be used.
 // RING = 8 needs the group count to be even.
-template <int RING, int NA, int THREADS>
-__device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[NA], const uint8_t* brow_q,
-                                         const uint8_t* brow_s, int nks, v4f (&acc)[NA], uint8_t* lds) {
+template <int RING, int NA, int THREADS, int NB>
+__device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[NA], const uint8_t* const (&brow_q)[NB],
+                                         const uint8_t* brow_s, int nks, v4f (&acc)[NA][NB], uint8_t* lds) {
   static_assert(RING == 4 || RING == 8, "ring of 1 or 2 groups");
   const int n_sg = (nks + 3) / 4, last = nks - 1;
-  ChunkStage<THREADS> stage;
+  ChunkStage<THREADS, NB> stage;
   WFrag<NA> f[RING];
   uint32_t sa[NA], sa_n[NA];
   stage.load(brow_q, brow_s, 0, nks, n_sg);
@@ -193,6 +225,27 @@ __device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[
   }
 }
 
+// Token rows staged by this thread: tile tt holds rows p0+16tt .. of the
+// group (column tid % 16); padding columns reuse the group's first row.  The
+// scale row is that of tile tid >> 7 (threads beyond 128*NB load no scales).
+// pair_rows: the activation rows are in pair order (h for down); otherwise
+// they are token rows of x reached through perm (the shared expert's rows
+// follow the routed pairs in natural order).
+template <int NB>
+__device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Group g, int K, bool shared, bool pair_rows,
+                                           const uint8_t* (&brow_q)[NB], const uint8_t*& brow_s) {
+  const int tid = threadIdx.x, tcol = tid & 15;
+  auto row_of = [&](int tt) -> size_t {
+    const int c = 16 * tt + tcol;
+    const int p = g.p0 + (c < g.cnt ? c : 0);
+    if (pair_rows) return (size_t)p;
+    return (size_t)(shared ? p - a.P : a.perm[p] / a.k);
+  };
+#pragma unroll
+  for (int tt = 0; tt < NB; ++tt) brow_q[tt] = a.aq + row_of(tt) * split_q_row_bytes(K);
+  brow_s = a.as + row_of(min(tid >> 7, NB - 1)) * split_s_row_bytes(K);
+}
+
 // ---------------------------------------------------------------------------
 // gate/up: h = silu(min(gate, L)) * clamp(up, -L, L), written as the two-term
 // FP8 split that the down GEMM consumes (same layout as the x split, K = I).
@@ -202,7 +255,7 @@ __device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[
 
 // One work unit: features [fu0, fu0 + WAVES*16*TPM) of gate and up for the
 // rows of group g.
-template <int TPM, int WAVES>
+template <int TPM, int WAVES, int NB>
 __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
   constexpr int NA = 2 * TPM, kFeatWave = 16 * TPM, kThreads = 64 * WAVES;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -225,23 +278,24 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
     as[i] = uniform_gptr(gs + (rt0 + i) * ts);
     as[TPM + i] = uniform_gptr(us + (rt0 + i) * ts);
   }
-  // the token row this thread stages (column tid % 16); padding columns reuse the group's first row
-  const int tcol = tid & 15;
-  const int p_ld = g.p0 + (tcol < g.cnt ? tcol : 0);
-  const int row = shared ? p_ld - a.P : a.perm[p_ld] / a.k;
-  const uint8_t* brow_q = a.aq + (size_t)row * split_q_row_bytes(K);
-  const uint8_t* brow_s = a.as + (size_t)row * split_s_row_bytes(K);
-  v4f acc[NA];
+  const uint8_t* brow_q[NB];
+  const uint8_t* brow_s;
+  stage_rows<NB>(a, g, K, shared, false, brow_q, brow_s);
+  v4f acc[NA][NB];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
   if (kRing == 8 && (nks % 8) == 0)
-    mainloop<8, NA, kThreads>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<8, NA, kThreads, NB>(aq, as, brow_q, brow_s, nks, acc, lds);
   else
-    mainloop<4, NA, kThreads>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<4, NA, kThreads, NB>(aq, as, brow_q, brow_s, nks, acc, lds);
 
   const int n_sg_h = (R / 128 + 3) / 4;
   const float L = a.limit;
   // each pair of tiles (32 features) is one 32-block of h: 4 lanes (grp 0..3) x 8 values per token
+#pragma unroll
+  for (int c = 0; c < NB; ++c)
 #pragma unroll
   for (int b = 0; b < TPM / 2; ++b) {
     const int blk_h = f0 / 32 + b;
@@ -250,7 +304,7 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        float gv = acc[2 * b + tt][ii], uv = acc[TPM + 2 * b + tt][ii];
+        float gv = acc[2 * b + tt][c][ii], uv = acc[TPM + 2 * b + tt][c][ii];
         if (L > 0.f) {
           gv = fminf(gv, L);
           uv = fminf(fmaxf(uv, -L), L);
@@ -283,8 +337,8 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
       w2[tt] = pack4_fp8(res[4 * tt] * inv2, res[4 * tt + 1] * inv2, res[4 * tt + 2] * inv2, res[4 * tt + 3] * inv2);
-    if (col < g.cnt) {
-      const size_t p = (size_t)g.p0 + col;
+    if (16 * c + col < g.cnt) {
+      const size_t p = (size_t)g.p0 + 16 * c + col;
       // feature 16tt + 4grp + ii of block blk_h = 4ks + bb: group 2*(bb%2) + tt, byte 16*(bb/2) + 4grp + ii
       const int bb = blk_h & 3;
       uint8_t* dst = a.hq + p * split_q_row_bytes(R) + (size_t)(blk_h >> 2) * 256 + 16 * (bb >> 1) + 4 * grp;
@@ -303,10 +357,10 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
   }
 }
 
-template <int TPM, int WAVES>
+template <int TPM, int WAVES, int NB>
 __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * TPM;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunkBytes];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
   const int n_fb = a.R / kFeatUnit;
   int half_idx;
   bool is_half;
@@ -316,11 +370,11 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
   const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
   if constexpr (TPM >= 4) {
     if (is_half) {
-      gateup_unit<TPM / 2, WAVES>(a, g, fu0, lds);
+      gateup_unit<TPM / 2, WAVES, NB>(a, g, fu0, lds);
       return;
     }
   }
-  gateup_unit<TPM, WAVES>(a, g, fu0, lds);
+  gateup_unit<TPM, WAVES, NB>(a, g, fu0, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -329,7 +383,7 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
 // WAVES waves takes NA 16-row tiles: 16*NA features per wave, 16*NA*WAVES per
 // unit.
 
-template <int NA, int WAVES>
+template <int NA, int WAVES, int NB>
 __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
   constexpr int kFeatWave = 16 * NA, kThreads = 64 * WAVES;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -348,28 +402,31 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
     aq[i] = uniform_gptr(dq + (rt0 + i) * tq);
     as[i] = uniform_gptr(ds + (rt0 + i) * ts);
   }
-  const int tcol = tid & 15;
-  const size_t p_ld = (size_t)g.p0 + (tcol < g.cnt ? tcol : 0);
-  const uint8_t* brow_q = a.aq + p_ld * split_q_row_bytes(K);
-  const uint8_t* brow_s = a.as + p_ld * split_s_row_bytes(K);
-  v4f acc[NA];
+  const uint8_t* brow_q[NB];
+  const uint8_t* brow_s;
+  stage_rows<NB>(a, g, K, shared, true, brow_q, brow_s);
+  v4f acc[NA][NB];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
   if (kRing == 8 && (nks % 8) == 0)
-    mainloop<8, NA, kThreads>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<8, NA, kThreads, NB>(aq, as, brow_q, brow_s, nks, acc, lds);
   else
-    mainloop<4, NA, kThreads>(aq, as, brow_q, brow_s, nks, acc, lds);
-  if (col < g.cnt) {
-    float* dst = a.y + ((size_t)g.p0 + col) * R + f0 + 4 * grp;
+    mainloop<4, NA, kThreads, NB>(aq, as, brow_q, brow_s, nks, acc, lds);
 #pragma unroll
-    for (int tt = 0; tt < NA; ++tt) *(v4f*)(dst + 16 * tt) = acc[tt];
-  }
+  for (int c = 0; c < NB; ++c)
+    if (16 * c + col < g.cnt) {
+      float* dst = a.y + ((size_t)g.p0 + 16 * c + col) * R + f0 + 4 * grp;
+#pragma unroll
+      for (int tt = 0; tt < NA; ++tt) *(v4f*)(dst + 16 * tt) = acc[tt][c];
+    }
 }
 
-template <int NA, int WAVES>
+template <int NA, int WAVES, int NB>
 __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * NA;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kChunkBytes];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
   const int n_fb = a.R / kFeatUnit;
   int half_idx;
   bool is_half;
@@ -379,11 +436,11 @@ __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
   if constexpr (NA >= 2) {
     if (is_half) {
-      down_unit<NA / 2, WAVES>(a, g, fu0, lds);
+      down_unit<NA / 2, WAVES, NB>(a, g, fu0, lds);
       return;
     }
   }
-  down_unit<NA, WAVES>(a, g, fu0, lds);
+  down_unit<NA, WAVES, NB>(a, g, fu0, lds);
 }
 
 // Enough workgroups for every unit to be taken in halves (see xcd_unit_split).
@@ -400,16 +457,36 @@ static unsigned unit_grid(int max_groups, int n_fb) {
 // has enough pairs (kWideUnitPairs) to give every CU several of them.
 constexpr int kWideUnitPairs = 1024;
 
-template <int TPM, int WAVES>
-static void gateup_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
-  hipLaunchKernelGGL((gateup_kernel<TPM, WAVES>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
-                     dim3(64 * WAVES), 0, stream, a);
+// Dynamic LDS of one kernel instantiation: two chunk buffers of NB column
+// tiles; above 64 KB the limit is raised once per instantiation.
+template <typename Kern>
+static hipError_t lds_limit(Kern* kernel, size_t bytes, bool& done) {
+  if (done || bytes <= 65536) return hipSuccess;
+  hipError_t err = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (err == hipSuccess) done = true;
+  return err;
 }
 
-template <int NA, int WAVES>
-static void down_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
-  hipLaunchKernelGGL((down_kernel<NA, WAVES>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
-                     dim3(64 * WAVES), 0, stream, a);
+template <int TPM, int WAVES, int NB>
+static hipError_t gateup_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
+  static bool attr = false;
+  const size_t lds = 2 * NB * (size_t)kChunkBytes;
+  hipError_t err = lds_limit(gateup_kernel<TPM, WAVES, NB>, lds, attr);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((gateup_kernel<TPM, WAVES, NB>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
+                     dim3(64 * WAVES), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int NA, int WAVES, int NB>
+static hipError_t down_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
+  static bool attr = false;
+  const size_t lds = 2 * NB * (size_t)kChunkBytes;
+  hipError_t err = lds_limit(down_kernel<NA, WAVES, NB>, lds, attr);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((down_kernel<NA, WAVES, NB>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
+                     dim3(64 * WAVES), lds, stream, a);
+  return hipGetLastError();
 }
 
 // Small batches (fewer than kWideUnitPairs routed pairs, e.g. 8 rows: about
@@ -418,29 +495,40 @@ static void down_launch(const ExpertArgs& a, int max_groups, hipStream_t stream)
 // measured slightly slower (more activation staging per weight byte).
 constexpr int kSmallTailUnits = 64;
 
-hipError_t launch_gateup(const ExpertArgs& a0, int max_groups, hipStream_t stream) {
+// Batches with at least kTallRowsPerExpert routed rows per expert on average
+// (prefill-like) use units of up to 64 rows (4 column tiles) from the 64-row
+// work list: each weight fragment then feeds 4x as many MFMAs.
+constexpr int kTallRowsPerExpert = 32;
+
+static bool tall_batch(const ExpertArgs& a) { return a.P >= kTallRowsPerExpert * a.E; }
+
+hipError_t launch_gateup(const ExpertArgs& a0, int max_groups, int max_tall_groups, hipStream_t stream) {
   ExpertArgs a = a0;
   a.tail_units = a.P < kWideUnitPairs ? kSmallTailUnits : 0;
-  if (a.P >= kWideUnitPairs && a.R % 512 == 0)
-    gateup_launch<4, 8>(a, max_groups, stream);
-  else if (a.R % 256 == 0)
-    gateup_launch<4, 4>(a, max_groups, stream);
-  else
-    gateup_launch<2, 4>(a, max_groups, stream);
-  return hipGetLastError();
+  if (tall_batch(a) && a.R % 256 == 0) {
+    a.groups = a.tall_groups;
+    a.n_groups = a.n_tall_groups;
+    a.tail_units = 0;
+    return gateup_launch<2, 8, 4>(a, max_tall_groups, stream);
+  }
+  if (a.P >= kWideUnitPairs && a.R % 512 == 0) return gateup_launch<4, 8, 1>(a, max_groups, stream);
+  if (a.R % 256 == 0) return gateup_launch<4, 4, 1>(a, max_groups, stream);
+  return gateup_launch<2, 4, 1>(a, max_groups, stream);
 }
 
-// (8-wave down units measured slower: the down GEMM keeps 4-wave units.)
-hipError_t launch_down(const ExpertArgs& a0, int max_groups, hipStream_t stream) {
+// (8-wave down units measured slower with 16-row units: those keep 4 waves.)
+hipError_t launch_down(const ExpertArgs& a0, int max_groups, int max_tall_groups, hipStream_t stream) {
   ExpertArgs a = a0;
   a.tail_units = a.P < kWideUnitPairs ? kSmallTailUnits : 0;
-  if (a.R % kDownUnitMax == 0)
-    down_launch<kDownUnitMax / 64, 4>(a, max_groups, stream);
-  else if (a.R % 256 == 0)
-    down_launch<4, 4>(a, max_groups, stream);
-  else
-    down_launch<2, 4>(a, max_groups, stream);
-  return hipGetLastError();
+  if (tall_batch(a) && a.R % 512 == 0) {
+    a.groups = a.tall_groups;
+    a.n_groups = a.n_tall_groups;
+    a.tail_units = 0;
+    return down_launch<4, 8, 4>(a, max_tall_groups, stream);
+  }
+  if (a.R % kDownUnitMax == 0) return down_launch<kDownUnitMax / 64, 4, 1>(a, max_groups, stream);
+  if (a.R % 256 == 0) return down_launch<4, 4, 1>(a, max_groups, stream);
+  return down_launch<2, 4, 1>(a, max_groups, stream);
 }
 
 // ---------------------------------------------------------------------------

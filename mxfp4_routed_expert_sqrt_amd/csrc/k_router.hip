@@ -336,13 +336,16 @@ __device__ __forceinline__ int wave_match_rank(int e, bool act, int lane, bool* 
   return __popcll(peers & lt_mask);
 }
 
-// Work list and offsets[E] once counts and offsets (in LDS) are final.
+// Work list of groups of <= ROWS rows (ceil(count/ROWS) per expert in expert
+// order, then the shared expert's rows) once counts and offsets (in LDS) are
+// final.
+template <int ROWS>
 __device__ __forceinline__ void write_groups(const int32_t* s_cnt, const int32_t* s_off, int n_rows, int P, int E,
                                              int has_shared, Group* __restrict__ groups,
                                              int32_t* __restrict__ n_groups, int32_t* wave_tot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = (tid < E) ? s_cnt[tid] : 0;
-  const int ng = (c + kGroupRows - 1) / kGroupRows;
+  const int ng = (c + ROWS - 1) / ROWS;
   int incl = ng;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -362,18 +365,18 @@ __device__ __forceinline__ void write_groups(const int32_t* s_cnt, const int32_t
     for (int g = 0; g < ng; ++g) {
       Group gr;
       gr.e = tid;
-      gr.p0 = p0 + g * kGroupRows;
-      gr.cnt = min(kGroupRows, c - g * kGroupRows);
+      gr.p0 = p0 + g * ROWS;
+      gr.cnt = min(ROWS, c - g * ROWS);
       gr.pad = 0;
       groups[g0 + g] = gr;
     }
   }
-  const int nsh = has_shared ? (n_rows + kGroupRows - 1) / kGroupRows : 0;
+  const int nsh = has_shared ? (n_rows + ROWS - 1) / ROWS : 0;
   for (int g = tid; g < nsh; g += kRouteThreads) {
     Group gr;
     gr.e = E;
-    gr.p0 = P + g * kGroupRows;
-    gr.cnt = min(kGroupRows, n_rows - g * kGroupRows);
+    gr.p0 = P + g * ROWS;
+    gr.cnt = min(ROWS, n_rows - g * ROWS);
     gr.pad = 0;
     groups[total + g] = gr;
   }
@@ -388,8 +391,9 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
     const float* __restrict__ z, int n_split, const float* __restrict__ bias, int n_rows, int E, int k, int routing, const int32_t* __restrict__ token_ids,
     const int32_t* __restrict__ tid2eid, int64_t vocab, int32_t* __restrict__ idx, float* __restrict__ gates,
     int has_shared, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, Group* __restrict__ groups, int32_t* __restrict__ n_groups, int32_t* hist,
-    int32_t* done, int scatter_here) {
+    int32_t* __restrict__ inv, Group* __restrict__ groups, int32_t* __restrict__ n_groups,
+    Group* __restrict__ tall_groups, int32_t* __restrict__ n_tall_groups, int32_t* hist, int32_t* done,
+    int scatter_here) {
   extern __shared__ float s_z[];  // [16][E] logits of the workgroup's rows
   __shared__ int32_t s_sel[kRouteWaves * kMaxTopK];
   __shared__ int32_t s_a[kMaxExperts];      // step 1: histogram; step 2: counts
@@ -568,7 +572,9 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
     }
   }
   __syncthreads();  // wave_tot reuse
-  write_groups(s_a, s_off, n_rows, P, E, has_shared, groups, n_groups, wave_tot);
+  write_groups<kGroupRows>(s_a, s_off, n_rows, P, E, has_shared, groups, n_groups, wave_tot);
+  __syncthreads();
+  write_groups<kTallGroupRows>(s_a, s_off, n_rows, P, E, has_shared, tall_groups, n_tall_groups, wave_tot);
 }
 
 // Scatter of perm/inv, one pair per thread (bases and offsets come from the
@@ -594,7 +600,8 @@ constexpr int kScatterInBlockMax = 8 * kRouteThreads;
 hipError_t launch_select_route(const float* z, const float* bias, int d, int n_rows, int E, int k, int routing, const int32_t* token_ids,
                                const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, int has_shared,
                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, Group* groups,
-                               int32_t* n_groups, int32_t* hist, int32_t* done, hipStream_t stream) {
+                               int32_t* n_groups, Group* tall_groups, int32_t* n_tall_groups, int32_t* hist,
+                               int32_t* done, hipStream_t stream) {
   if (E > kMaxExperts || k > kMaxTopK) return hipErrorInvalidValue;
   static bool attr_set = false;  // one-time raise of the dynamic LDS limit (64 KB at E = 1024)
   if (!attr_set) {
@@ -608,7 +615,7 @@ hipError_t launch_select_route(const float* z, const float* bias, int d, int n_r
   const size_t lds = sizeof(float) * kRouteWaves * E;
   hipLaunchKernelGGL(select_route_kernel, dim3((unsigned)route_workgroups(n_rows)), dim3(kRouteThreads), lds, stream,
                      z, logits_splits(n_rows, E, d), bias, n_rows, E, k, routing, token_ids, tid2eid, vocab, idx, gates, has_shared, counts, offsets,
-                     perm, inv, groups, n_groups, hist, done, here);
+                     perm, inv, groups, n_groups, tall_groups, n_tall_groups, hist, done, here);
   if (!here) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

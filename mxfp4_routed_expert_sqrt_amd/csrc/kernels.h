@@ -45,7 +45,8 @@ __host__ __device__ inline size_t logits_partial_stride(int n_rows, int E) {
 hipError_t launch_select_route(const float* z, const float* bias, int d, int n_rows, int E, int k, int routing, const int32_t* token_ids,
                                const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, int has_shared,
                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, Group* groups,
-                               int32_t* n_groups, int32_t* hist, int32_t* done, hipStream_t stream);
+                               int32_t* n_groups, Group* tall_groups, int32_t* n_tall_groups, int32_t* hist,
+                               int32_t* done, hipStream_t stream);
 
 // Selection workgroups (16 rows each) and the size of their per-expert
 // histogram rows (E rounded up to 4 int32).
@@ -61,8 +62,10 @@ struct ExpertArgs {
   const uint8_t* aq;                     // activation split bytes (x for gate/up, h for down)
   const uint8_t* as;                     // activation split scales
   const int32_t* perm;                   // expert-major pair -> r*k + j
-  const Group* groups;
+  const Group* groups;                   // work list of <= 16-row groups
   const int32_t* n_groups;
+  const Group* tall_groups;              // work list of <= 64-row groups
+  const int32_t* n_tall_groups;
   int K, R;                              // contraction length, rows of each weight matrix
   int E, k, P;                           // experts, top-k, routed pairs (N*k)
   float limit;                           // swiglu limit (<= 0: none)
@@ -72,16 +75,17 @@ struct ExpertArgs {
   int tail_units;                        // units per XCD processed as two halves at the end
 };
 
-hipError_t launch_gateup(const ExpertArgs& a, int max_groups, hipStream_t stream);
-hipError_t launch_down(const ExpertArgs& a, int max_groups, hipStream_t stream);
+hipError_t launch_gateup(const ExpertArgs& a, int max_groups, int max_tall_groups, hipStream_t stream);
+hipError_t launch_down(const ExpertArgs& a, int max_groups, int max_tall_groups, hipStream_t stream);
 
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* gates, int n_rows, int d, int k,
                           int P, int has_shared, float route_scale, uint16_t* out, hipStream_t stream);
 
-// Worst-case number of work groups for n_rows rows: sum_e ceil(c_e/16) <= ceil(P/16) + E, plus the shared rows.
-inline int max_work_groups(int n_rows, int k, int E, int has_shared) {
+// Worst-case number of work groups of <= rows rows each for n_rows rows:
+// sum_e ceil(c_e/rows) <= ceil(P/rows) + E, plus the shared rows.
+inline int max_work_groups(int n_rows, int k, int E, int has_shared, int rows = kGroupRows) {
   const long P = (long)n_rows * k;
-  return (int)((P + kGroupRows - 1) / kGroupRows + E + (has_shared ? (n_rows + kGroupRows - 1) / kGroupRows : 0));
+  return (int)((P + rows - 1) / rows + E + (has_shared ? (n_rows + rows - 1) / rows : 0));
 }
 
 }  // namespace moe

@@ -12,8 +12,8 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, hist, done, xq, xs, hq, hs, y, total;
-  int max_groups;
+  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, tall_groups, n_tall_groups, hist, done, xq, xs, hq, hs, y, total;
+  int max_groups, max_tall_groups;
 };
 
 // Workspace carve-up; every region starts on a 256-byte boundary.
@@ -22,6 +22,7 @@ Layout make_layout(const moe_config_t& c, int n) {
   const size_t N = (size_t)n, E = (size_t)c.n_experts, k = (size_t)c.top_k;
   const size_t P = N * k, Ptot = P + (c.has_shared ? N : 0);
   L.max_groups = max_work_groups(n, c.top_k, c.n_experts, c.has_shared);
+  L.max_tall_groups = max_work_groups(n, c.top_k, c.n_experts, c.has_shared, kTallGroupRows);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -37,6 +38,8 @@ Layout make_layout(const moe_config_t& c, int n) {
   L.inv = take(P * 4);
   L.groups = take((size_t)L.max_groups * sizeof(Group));
   L.n_groups = take(4);
+  L.tall_groups = take((size_t)L.max_tall_groups * sizeof(Group));
+  L.n_tall_groups = take(4);
   L.hist = take(route_hist_bytes(n, c.n_experts));
   L.done = take(4);
   L.xq = take(N * split_q_row_bytes(c.d_model));
@@ -169,6 +172,8 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   int32_t* inv = a.inv ? a.inv : (int32_t*)(ws + L.inv);
   Group* groups = (Group*)(ws + L.groups);
   int32_t* n_groups = (int32_t*)(ws + L.n_groups);
+  Group* tall_groups = (Group*)(ws + L.tall_groups);
+  int32_t* n_tall_groups = (int32_t*)(ws + L.n_tall_groups);
   uint8_t *xq = ws + L.xq, *xs = ws + L.xs, *hq = ws + L.hq, *hs = ws + L.hs;
   float* y = (float*)(ws + L.y);
   const int P = N * k;
@@ -185,7 +190,8 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
   if ((err = launch_select_route(z, a.router_bias, d, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, c.has_shared,
-                                 counts, offsets, perm, inv, groups, n_groups, hist, done, stream)) != hipSuccess)
+                                 counts, offsets, perm, inv, groups, n_groups, tall_groups, n_tall_groups, hist, done,
+                                 stream)) != hipSuccess)
     return MOE_ERR_HIP;
 
   ExpertArgs ga;
@@ -203,6 +209,8 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   ga.perm = perm;
   ga.groups = groups;
   ga.n_groups = n_groups;
+  ga.tall_groups = tall_groups;
+  ga.n_tall_groups = n_tall_groups;
   ga.K = d;
   ga.R = I;
   ga.E = E;
@@ -212,7 +220,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   ga.hq = hq;
   ga.hs = hs;
   if (!mark(2)) return MOE_ERR_HIP;
-  if ((err = launch_gateup(ga, L.max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
+  if ((err = launch_gateup(ga, L.max_groups, L.max_tall_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
 
   ExpertArgs da = ga;
   da.q0 = (const uint8_t*)a.w.down_q;
@@ -228,7 +236,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   da.hq = da.hs = nullptr;
   da.y = y;
   if (!mark(3)) return MOE_ERR_HIP;
-  if ((err = launch_down(da, L.max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
+  if ((err = launch_down(da, L.max_groups, L.max_tall_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
   if (!mark(4)) return MOE_ERR_HIP;
 
   if ((err = launch_combine(y, inv, gates, N, d, k, P, c.has_shared, c.route_scale, (uint16_t*)a.out, stream)) !=

@@ -144,6 +144,8 @@ EDGE = {
     # more than 256 experts: 6 and 16 score slots per lane in the selection
     "e384_k6": MoEShape("edge_e384_k6", 96, 256, 384, 6, 128, "topk", "edge384"),
     "e1000_k4": MoEShape("edge_e1000_k4", 64, 128, 1000, 4, 128, "topk", "edge1000"),
+    # >= 32 routed rows per expert: the 64-row work units (4 column tiles) of both GEMMs, ragged groups
+    "tall": MoEShape("edge_tall", 611, 512, 8, 4, 256, "topk", "edge_tall"),
 }
 
 
