@@ -54,17 +54,20 @@ constexpr int kChunkBytes = kChunkData + 512;
 // inside it is (j, t, h, g, col) = (p>>8 & 3, p>>7 & 1, p>>6 & 1, p>>4 & 3,
 // p & 15); col = tid % 16 for every m, so each thread reads one token row per
 // tile.  THREADS divides 1024, so the tile of piece m is (THREADS*m) >> 10.
-// Thread tid < 128*NB also carries one scale dword of tile tid >> 7.
+// The chunk's 128*NB scale dwords are carried as dword tid + THREADS*i
+// (tile (tid + THREADS*i) >> 7).
 template <int THREADS, int NB>
 struct ChunkStage {
-  static_assert(1024 % THREADS == 0 && THREADS >= 128 * NB, "chunk staging shape");
+  static_assert(1024 % THREADS == 0, "chunk staging shape");
   static constexpr int kPieces = 1024 * NB / THREADS;
+  static constexpr int kScales = (128 * NB + THREADS - 1) / THREADS;
   u32x4 q[kPieces];
-  uint32_t s;
+  uint32_t s[kScales];
 
-  // brow_q[t]: this thread's token row of tile t; brow_s: the scale row of tile tid >> 7
-  __device__ __forceinline__ void load(const uint8_t* const (&brow_q)[NB], const uint8_t* brow_s, int sg, int nks,
-                                       int n_sg) {
+  // brow_q[t]: this thread's token row of tile t; brow_s[i]: the scale row of
+  // the tile of scale dword tid + THREADS*i
+  __device__ __forceinline__ void load(const uint8_t* const (&brow_q)[NB], const uint8_t* const (&brow_s)[kScales],
+                                       int sg, int nks, int n_sg) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < kPieces; ++m) {
@@ -74,9 +77,13 @@ struct ChunkStage {
       const int ks = min(4 * sg + j, nks - 1);  // past the end: any valid step (never multiplied)
       q[m] = *(const u32x4*)(brow_q[tile] + (size_t)ks * 256 + g * 64 + t * 32 + h * 16);
     }
-    if (tid < 128 * NB) {
-      const int t = (tid >> 6) & 1, g = (tid >> 4) & 3;
-      s = *(const uint32_t*)(brow_s + (size_t)(t * n_sg + sg) * 16 + g * 4);
+#pragma unroll
+    for (int i = 0; i < kScales; ++i) {
+      const int u = tid + THREADS * i;
+      if (u < 128 * NB) {
+        const int t = (u >> 6) & 1, g = (u >> 4) & 3;
+        s[i] = *(const uint32_t*)(brow_s[i] + (size_t)(t * n_sg + sg) * 16 + g * 4);
+      }
     }
   }
 
@@ -87,7 +94,11 @@ struct ChunkStage {
       const int tile = (THREADS * m) >> 10;
       *(u32x4*)(buf + tile * kChunkBytes + ((tid + THREADS * m) & 1023) * 16) = q[m];
     }
-    if (tid < 128 * NB) *(uint32_t*)(buf + (tid >> 7) * kChunkBytes + kChunkData + (tid & 127) * 4) = s;
+#pragma unroll
+    for (int i = 0; i < kScales; ++i) {
+      const int u = tid + THREADS * i;
+      if (u < 128 * NB) *(uint32_t*)(buf + (u >> 7) * kChunkBytes + kChunkData + (u & 127) * 4) = s[i];
+    }
   }
 };
 
@@ -161,8 +172,9 @@ __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chun
 template <int GI, int RING, int NA, int THREADS, int NB>
 __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB>& stage, uint32_t (&sa)[NA],
                                         uint32_t (&sa_n)[NA], const gptr (&aq)[NA], const gptr (&as)[NA],
-                                        const uint8_t* const (&brow_q)[NB], const uint8_t* brow_s, int sg, int nks,
-                                        int n_sg, v4f (&acc)[NA][NB], uint8_t* lds) {
+                                        const uint8_t* const (&brow_q)[NB],
+                                        const uint8_t* const (&brow_s)[ChunkStage<THREADS, NB>::kScales], int sg,
+                                        int nks, int n_sg, v4f (&acc)[NA][NB], uint8_t* lds) {
   constexpr int kBuf = NB * kChunkBytes;
   const int lane = threadIdx.x & 63, last = nks - 1, k0 = 4 * sg;
   const uint8_t* chunk = lds + (sg & 1) * kBuf;
@@ -207,7 +219,8 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
 // RING = 8 needs the group count to be even.
 template <int RING, int NA, int THREADS, int NB>
 __device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[NA], const uint8_t* const (&brow_q)[NB],
-                                         const uint8_t* brow_s, int nks, v4f (&acc)[NA][NB], uint8_t* lds) {
+                                         const uint8_t* const (&brow_s)[ChunkStage<THREADS, NB>::kScales], int nks,
+                                         v4f (&acc)[NA][NB], uint8_t* lds) {
   static_assert(RING == 4 || RING == 8, "ring of 1 or 2 groups");
   const int n_sg = (nks + 3) / 4, last = nks - 1;
   ChunkStage<THREADS, NB> stage;
@@ -231,9 +244,10 @@ __device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[
 // pair_rows: the activation rows are in pair order (h for down); otherwise
 // they are token rows of x reached through perm (the shared expert's rows
 // follow the routed pairs in natural order).
-template <int NB>
+template <int THREADS, int NB>
 __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Group g, int K, bool shared, bool pair_rows,
-                                           const uint8_t* (&brow_q)[NB], const uint8_t*& brow_s) {
+                                           const uint8_t* (&brow_q)[NB],
+                                           const uint8_t* (&brow_s)[ChunkStage<THREADS, NB>::kScales]) {
   const int tid = threadIdx.x, tcol = tid & 15;
   auto row_of = [&](int tt) -> size_t {
     const int c = 16 * tt + tcol;
@@ -243,7 +257,9 @@ __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Group g, i
   };
 #pragma unroll
   for (int tt = 0; tt < NB; ++tt) brow_q[tt] = a.aq + row_of(tt) * split_q_row_bytes(K);
-  brow_s = a.as + row_of(min(tid >> 7, NB - 1)) * split_s_row_bytes(K);
+#pragma unroll
+  for (int i = 0; i < ChunkStage<THREADS, NB>::kScales; ++i)
+    brow_s[i] = a.as + row_of(min((tid + THREADS * i) >> 7, NB - 1)) * split_s_row_bytes(K);
 }
 
 // ---------------------------------------------------------------------------
@@ -255,7 +271,7 @@ __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Group g, i
 
 // One work unit: features [fu0, fu0 + WAVES*16*TPM) of gate and up for the
 // rows of group g.
-template <int TPM, int WAVES, int NB>
+template <int TPM, int WAVES, int NB, int RING>
 __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
   constexpr int NA = 2 * TPM, kFeatWave = 16 * TPM, kThreads = 64 * WAVES;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -279,14 +295,14 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
     as[TPM + i] = uniform_gptr(us + (rt0 + i) * ts);
   }
   const uint8_t* brow_q[NB];
-  const uint8_t* brow_s;
-  stage_rows<NB>(a, g, K, shared, false, brow_q, brow_s);
+  const uint8_t* brow_s[ChunkStage<kThreads, NB>::kScales];
+  stage_rows<kThreads, NB>(a, g, K, shared, false, brow_q, brow_s);
   v4f acc[NA][NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i)
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
-  if (kRing == 8 && (nks % 8) == 0)
+  if (RING == 8 && (nks % 8) == 0)
     mainloop<8, NA, kThreads, NB>(aq, as, brow_q, brow_s, nks, acc, lds);
   else
     mainloop<4, NA, kThreads, NB>(aq, as, brow_q, brow_s, nks, acc, lds);
@@ -357,7 +373,7 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
   }
 }
 
-template <int TPM, int WAVES, int NB>
+template <int TPM, int WAVES, int NB, int RING>
 __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * TPM;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
@@ -370,11 +386,11 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
   const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
   if constexpr (TPM >= 4) {
     if (is_half) {
-      gateup_unit<TPM / 2, WAVES, NB>(a, g, fu0, lds);
+      gateup_unit<TPM / 2, WAVES, NB, RING>(a, g, fu0, lds);
       return;
     }
   }
-  gateup_unit<TPM, WAVES, NB>(a, g, fu0, lds);
+  gateup_unit<TPM, WAVES, NB, RING>(a, g, fu0, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -383,7 +399,7 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
 // WAVES waves takes NA 16-row tiles: 16*NA features per wave, 16*NA*WAVES per
 // unit.
 
-template <int NA, int WAVES, int NB>
+template <int NA, int WAVES, int NB, int RING>
 __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
   constexpr int kFeatWave = 16 * NA, kThreads = 64 * WAVES;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -403,14 +419,14 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
     as[i] = uniform_gptr(ds + (rt0 + i) * ts);
   }
   const uint8_t* brow_q[NB];
-  const uint8_t* brow_s;
-  stage_rows<NB>(a, g, K, shared, true, brow_q, brow_s);
+  const uint8_t* brow_s[ChunkStage<kThreads, NB>::kScales];
+  stage_rows<kThreads, NB>(a, g, K, shared, true, brow_q, brow_s);
   v4f acc[NA][NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i)
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
-  if (kRing == 8 && (nks % 8) == 0)
+  if (RING == 8 && (nks % 8) == 0)
     mainloop<8, NA, kThreads, NB>(aq, as, brow_q, brow_s, nks, acc, lds);
   else
     mainloop<4, NA, kThreads, NB>(aq, as, brow_q, brow_s, nks, acc, lds);
@@ -423,7 +439,7 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
     }
 }
 
-template <int NA, int WAVES, int NB>
+template <int NA, int WAVES, int NB, int RING>
 __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * NA;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
@@ -436,11 +452,11 @@ __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
   if constexpr (NA >= 2) {
     if (is_half) {
-      down_unit<NA / 2, WAVES, NB>(a, g, fu0, lds);
+      down_unit<NA / 2, WAVES, NB, RING>(a, g, fu0, lds);
       return;
     }
   }
-  down_unit<NA, WAVES, NB>(a, g, fu0, lds);
+  down_unit<NA, WAVES, NB, RING>(a, g, fu0, lds);
 }
 
 // Enough workgroups for every unit to be taken in halves (see xcd_unit_split).
@@ -467,24 +483,24 @@ static hipError_t lds_limit(Kern* kernel, size_t bytes, bool& done) {
   return err;
 }
 
-template <int TPM, int WAVES, int NB>
+template <int TPM, int WAVES, int NB, int RING = kRing>
 static hipError_t gateup_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
   static bool attr = false;
   const size_t lds = 2 * NB * (size_t)kChunkBytes;
-  hipError_t err = lds_limit(gateup_kernel<TPM, WAVES, NB>, lds, attr);
+  hipError_t err = lds_limit(gateup_kernel<TPM, WAVES, NB, RING>, lds, attr);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((gateup_kernel<TPM, WAVES, NB>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
+  hipLaunchKernelGGL((gateup_kernel<TPM, WAVES, NB, RING>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
                      dim3(64 * WAVES), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int NA, int WAVES, int NB>
+template <int NA, int WAVES, int NB, int RING = kRing>
 static hipError_t down_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
   static bool attr = false;
   const size_t lds = 2 * NB * (size_t)kChunkBytes;
-  hipError_t err = lds_limit(down_kernel<NA, WAVES, NB>, lds, attr);
+  hipError_t err = lds_limit(down_kernel<NA, WAVES, NB, RING>, lds, attr);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((down_kernel<NA, WAVES, NB>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
+  hipLaunchKernelGGL((down_kernel<NA, WAVES, NB, RING>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
                      dim3(64 * WAVES), lds, stream, a);
   return hipGetLastError();
 }
