@@ -118,11 +118,15 @@ __device__ __forceinline__ gptr uniform_gptr(const uint8_t* p) {
   return (gptr)(((uint64_t)hi << 32) | lo);
 }
 
-template <int NA>
+// Weight fragment of k-step ks of each tile.  NT: non-temporal loads.
+template <bool NT, int NA>
 __device__ __forceinline__ void load_w(WFrag<NA>& f, const gptr (&wq)[NA], int ks) {
   const uint32_t off = (threadIdx.x & 63) * 16 + (uint32_t)ks * 1024;
 #pragma unroll
-  for (int a = 0; a < NA; ++a) f.A[a] = *(const __attribute__((address_space(1))) u32x4*)(wq[a] + off);
+  for (int a = 0; a < NA; ++a) {
+    const __attribute__((address_space(1))) u32x4* p = (const __attribute__((address_space(1))) u32x4*)(wq[a] + off);
+    f.A[a] = NT ? __builtin_nontemporal_load(p) : *p;
+  }
 }
 
 template <int NA>
@@ -169,7 +173,7 @@ __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chun
 // fragments of ks+1 .. ks+RING-1 are in flight.  GI = position of this group
 // inside a ring cycle (RING/4 groups per cycle), so every slot index and scale
 // byte is a compile-time constant.
-template <int GI, int RING, int NA, int THREADS, int NB>
+template <int GI, int RING, int NA, int THREADS, int NB, bool NT>
 __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB>& stage, uint32_t (&sa)[NA],
                                         uint32_t (&sa_n)[NA], const gptr (&aq)[NA], const gptr (&as)[NA],
                                         const uint8_t* const (&brow_q)[NB],
@@ -186,19 +190,19 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
   }
   stage.load(brow_q, brow_s, min(sg + 1, n_sg - 1), nks, n_sg);
   load_wscales(sa_n, as, min(sg + 1, n_sg - 1));
-  load_w(f[(4 * GI + RING - 1) % RING], aq, min(k0 + RING - 1, last));
+  load_w<NT>(f[(4 * GI + RING - 1) % RING], aq, min(k0 + RING - 1, last));
   __builtin_amdgcn_sched_barrier(0);
   mma_step<0>(f[(4 * GI) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
-  load_w(f[(4 * GI + RING) % RING], aq, min(k0 + RING, last));
+  load_w<NT>(f[(4 * GI + RING) % RING], aq, min(k0 + RING, last));
   __builtin_amdgcn_sched_barrier(0);
   if (k0 + 1 < nks) mma_step<1>(f[(4 * GI + 1) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
-  load_w(f[(4 * GI + RING + 1) % RING], aq, min(k0 + RING + 1, last));
+  load_w<NT>(f[(4 * GI + RING + 1) % RING], aq, min(k0 + RING + 1, last));
   __builtin_amdgcn_sched_barrier(0);
   if (k0 + 2 < nks) mma_step<2>(f[(4 * GI + 2) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
-  load_w(f[(4 * GI + RING + 2) % RING], aq, min(k0 + RING + 2, last));
+  load_w<NT>(f[(4 * GI + RING + 2) % RING], aq, min(k0 + RING + 2, last));
   __builtin_amdgcn_sched_barrier(0);
   if (k0 + 3 < nks) mma_step<3>(f[(4 * GI + 3) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
@@ -217,7 +221,7 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
 // sched_barrier(0) points keep their issue order, so each wait on the
 // in-order vector-memory counter covers only what is about to be used.
 // RING = 8 needs the group count to be even.
-template <int RING, int NA, int THREADS, int NB>
+template <int RING, int NA, int THREADS, int NB, bool NT>
 __device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[NA], const uint8_t* const (&brow_q)[NB],
                                          const uint8_t* const (&brow_s)[ChunkStage<THREADS, NB>::kScales], int nks,
                                          v4f (&acc)[NA][NB], uint8_t* lds) {
@@ -229,12 +233,13 @@ __device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[
   stage.load(brow_q, brow_s, 0, nks, n_sg);
   load_wscales(sa, as, 0);
 #pragma unroll
-  for (int i = 0; i < RING - 1; ++i) load_w(f[i], aq, min(i, last));
+  for (int i = 0; i < RING - 1; ++i) load_w<NT>(f[i], aq, min(i, last));
   stage.store(lds);
   __syncthreads();
   for (int sg = 0; sg < n_sg; sg += RING / 4) {
-    k_group<0>(f, stage, sa, sa_n, aq, as, brow_q, brow_s, sg, nks, n_sg, acc, lds);
-    if (RING == 8) k_group<1>(f, stage, sa, sa_n, aq, as, brow_q, brow_s, sg + 1, nks, n_sg, acc, lds);
+    k_group<0, RING, NA, THREADS, NB, NT>(f, stage, sa, sa_n, aq, as, brow_q, brow_s, sg, nks, n_sg, acc, lds);
+    if (RING == 8)
+      k_group<1, RING, NA, THREADS, NB, NT>(f, stage, sa, sa_n, aq, as, brow_q, brow_s, sg + 1, nks, n_sg, acc, lds);
   }
 }
 
@@ -271,7 +276,7 @@ __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Group g, i
 
 // One work unit: features [fu0, fu0 + WAVES*16*TPM) of gate and up for the
 // rows of group g.
-template <int TPM, int WAVES, int NB, int RING>
+template <int TPM, int WAVES, int NB, int RING, bool NT>
 __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
   constexpr int NA = 2 * TPM, kFeatWave = 16 * TPM, kThreads = 64 * WAVES;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -303,9 +308,9 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
   if (RING == 8 && (nks % 8) == 0)
-    mainloop<8, NA, kThreads, NB>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<8, NA, kThreads, NB, NT>(aq, as, brow_q, brow_s, nks, acc, lds);
   else
-    mainloop<4, NA, kThreads, NB>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<4, NA, kThreads, NB, NT>(aq, as, brow_q, brow_s, nks, acc, lds);
 
   const int n_sg_h = (R / 128 + 3) / 4;
   const float L = a.limit;
@@ -373,7 +378,7 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
   }
 }
 
-template <int TPM, int WAVES, int NB, int RING>
+template <int TPM, int WAVES, int NB, int RING, bool NT>
 __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * TPM;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
@@ -386,11 +391,11 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
   const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
   if constexpr (TPM >= 4) {
     if (is_half) {
-      gateup_unit<TPM / 2, WAVES, NB, RING>(a, g, fu0, lds);
+      gateup_unit<TPM / 2, WAVES, NB, RING, NT>(a, g, fu0, lds);
       return;
     }
   }
-  gateup_unit<TPM, WAVES, NB, RING>(a, g, fu0, lds);
+  gateup_unit<TPM, WAVES, NB, RING, NT>(a, g, fu0, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -399,7 +404,7 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
 // WAVES waves takes NA 16-row tiles: 16*NA features per wave, 16*NA*WAVES per
 // unit.
 
-template <int NA, int WAVES, int NB, int RING>
+template <int NA, int WAVES, int NB, int RING, bool NT>
 __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
   constexpr int kFeatWave = 16 * NA, kThreads = 64 * WAVES;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -427,9 +432,9 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
   if (RING == 8 && (nks % 8) == 0)
-    mainloop<8, NA, kThreads, NB>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<8, NA, kThreads, NB, NT>(aq, as, brow_q, brow_s, nks, acc, lds);
   else
-    mainloop<4, NA, kThreads, NB>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<4, NA, kThreads, NB, NT>(aq, as, brow_q, brow_s, nks, acc, lds);
 #pragma unroll
   for (int c = 0; c < NB; ++c)
     if (16 * c + col < g.cnt) {
@@ -439,7 +444,7 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
     }
 }
 
-template <int NA, int WAVES, int NB, int RING>
+template <int NA, int WAVES, int NB, int RING, bool NT>
 __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * NA;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
@@ -452,11 +457,11 @@ __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
   if constexpr (NA >= 2) {
     if (is_half) {
-      down_unit<NA / 2, WAVES, NB, RING>(a, g, fu0, lds);
+      down_unit<NA / 2, WAVES, NB, RING, NT>(a, g, fu0, lds);
       return;
     }
   }
-  down_unit<NA, WAVES, NB, RING>(a, g, fu0, lds);
+  down_unit<NA, WAVES, NB, RING, NT>(a, g, fu0, lds);
 }
 
 // Enough workgroups for every unit to be taken in halves (see xcd_unit_split).
@@ -483,24 +488,24 @@ static hipError_t lds_limit(Kern* kernel, size_t bytes, bool& done) {
   return err;
 }
 
-template <int TPM, int WAVES, int NB, int RING = kRing>
+template <int TPM, int WAVES, int NB, bool NT = false, int RING = kRing>
 static hipError_t gateup_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
   static bool attr = false;
   const size_t lds = 2 * NB * (size_t)kChunkBytes;
-  hipError_t err = lds_limit(gateup_kernel<TPM, WAVES, NB, RING>, lds, attr);
+  hipError_t err = lds_limit(gateup_kernel<TPM, WAVES, NB, RING, NT>, lds, attr);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((gateup_kernel<TPM, WAVES, NB, RING>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
+  hipLaunchKernelGGL((gateup_kernel<TPM, WAVES, NB, RING, NT>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
                      dim3(64 * WAVES), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int NA, int WAVES, int NB, int RING = kRing>
+template <int NA, int WAVES, int NB, bool NT = false, int RING = kRing>
 static hipError_t down_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
   static bool attr = false;
   const size_t lds = 2 * NB * (size_t)kChunkBytes;
-  hipError_t err = lds_limit(down_kernel<NA, WAVES, NB, RING>, lds, attr);
+  hipError_t err = lds_limit(down_kernel<NA, WAVES, NB, RING, NT>, lds, attr);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((down_kernel<NA, WAVES, NB, RING>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
+  hipLaunchKernelGGL((down_kernel<NA, WAVES, NB, RING, NT>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
                      dim3(64 * WAVES), lds, stream, a);
   return hipGetLastError();
 }
@@ -528,6 +533,10 @@ hipError_t launch_gateup(const ExpertArgs& a0, int max_groups, int max_tall_grou
     return gateup_launch<2, 8, 4>(a, max_tall_groups, stream);
   }
   if (a.P >= kWideUnitPairs && a.R % 512 == 0) return gateup_launch<4, 8, 1>(a, max_groups, stream);
+  if (a.P < kWideUnitPairs) {  // small batch: every weight byte is read once, non-temporal loads
+    if (a.R % 256 == 0) return gateup_launch<4, 4, 1, true>(a, max_groups, stream);
+    return gateup_launch<2, 4, 1, true>(a, max_groups, stream);
+  }
   if (a.R % 256 == 0) return gateup_launch<4, 4, 1>(a, max_groups, stream);
   return gateup_launch<2, 4, 1>(a, max_groups, stream);
 }
@@ -541,6 +550,11 @@ hipError_t launch_down(const ExpertArgs& a0, int max_groups, int max_tall_groups
     a.n_groups = a.n_tall_groups;
     a.tail_units = 0;
     return down_launch<4, 8, 4>(a, max_tall_groups, stream);
+  }
+  if (a.P < kWideUnitPairs) {  // small batch: every weight byte is read once, non-temporal loads
+    if (a.R % kDownUnitMax == 0) return down_launch<kDownUnitMax / 64, 4, 1, true>(a, max_groups, stream);
+    if (a.R % 256 == 0) return down_launch<4, 4, 1, true>(a, max_groups, stream);
+    return down_launch<2, 4, 1, true>(a, max_groups, stream);
   }
   if (a.R % kDownUnitMax == 0) return down_launch<kDownUnitMax / 64, 4, 1>(a, max_groups, stream);
   if (a.R % 256 == 0) return down_launch<4, 4, 1>(a, max_groups, stream);
