@@ -138,12 +138,13 @@ __device__ __forceinline__ void load_wscales(uint32_t (&sa)[NA], const gptr (&ws
 
 // k-step J of the current chunk: B (NB column tiles) from LDS, weights from a
 // ring slot; every weight fragment meets every column tile.  The 2*NB B
-// fragments (tile tt, term t at i = 2tt + t) are double-buffered: fragment
-// i+1 is read from LDS before fragment i's MFMAs are issued, so the LDS
-// latency is covered by MFMA work.
-template <int J>
+// fragments are taken term-major (i = t*NB + tt), so the two terms of one
+// accumulator are NA*NB MFMAs apart, and double-buffered: fragment i+1 is read
+// from LDS before fragment i's MFMAs are issued, so the LDS latency is
+// covered by MFMA work.
+template <int J, int NB>
 __device__ __forceinline__ v8i read_b(const uint8_t* chunk, int i) {
-  const int lane = threadIdx.x & 63, tt = i >> 1, t = i & 1;
+  const int lane = threadIdx.x & 63, tt = i % NB, t = i / NB;
   const uint8_t* c = chunk + tt * kChunkBytes + (J * 2 + t) * 2048 + lane * 16;
   const u32x4 lo = *(const u32x4*)c;
   const u32x4 hi = *(const u32x4*)(c + 1024);
@@ -154,16 +155,16 @@ template <int J, int NA, int NB>
 __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chunk, const uint32_t (&sa)[NA],
                                          const uint32_t (&sb)[NB][2], v4f (&acc)[NA][NB]) {
   constexpr int NF = 2 * NB;
-  v8i b0 = read_b<J>(chunk, 0), b1;
+  v8i b0 = read_b<J, NB>(chunk, 0), b1;
 #pragma unroll
   for (int i = 0; i < NF; ++i) {
     v8i& cur = (i & 1) ? b1 : b0;
     v8i& nxt = (i & 1) ? b0 : b1;
-    if (i + 1 < NF) nxt = read_b<J>(chunk, i + 1);
+    const int tt = i % NB, t = i / NB;
+    if (i + 1 < NF) nxt = read_b<J, NB>(chunk, i + 1);
     if (NF > 2) __builtin_amdgcn_sched_barrier(0);  // keep the read ahead of these MFMAs
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
-      acc[a][i >> 1] = mfma_fp4_fp8<J>(f.A[a], cur, acc[a][i >> 1], sa[a], sb[i >> 1][i & 1]);
+    for (int a = 0; a < NA; ++a) acc[a][tt] = mfma_fp4_fp8<J>(f.A[a], cur, acc[a][tt], sa[a], sb[tt][t]);
     if (NF > 2) __builtin_amdgcn_sched_barrier(0);
   }
 }
