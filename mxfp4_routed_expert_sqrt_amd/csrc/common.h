@@ -20,22 +20,10 @@ struct Group {
 };
 
 // Maps this workgroup to a work unit so that each XCD receives a contiguous
-// range of units (units of one group share activations in that XCD's L2).
+// range of units (units of one group share activations in that XCD's L2),
+// counted in half units: each XCD's range is taken whole, except its last
+// `tail_units`, which are taken one half at a time (two workgroups each).
 // Returns false for workgroups beyond the device-side unit count.
-__device__ __forceinline__ bool xcd_unit(int n_units, int* unit) {
-  const int bid = blockIdx.x;
-  const int xcd = bid % kXcds, slot = bid / kXcds;
-  const int per = (n_units + kXcds - 1) / kXcds;
-  if (slot >= per) return false;
-  const int u = xcd * per + slot;
-  if (u >= n_units) return false;
-  *unit = u;
-  return true;
-}
-
-// Like xcd_unit, in half units: each XCD's contiguous range of units is taken
-// whole, except its last `tail_units`, which are taken one half at a time
-// (two workgroups each), so the XCD's final round of work is half as long.
 // Sets *half_idx = 2*unit + half (half = 0 for a whole unit) and *is_half.
 __device__ __forceinline__ bool xcd_unit_split(int n_units, int tail_units, int* half_idx, bool* is_half) {
   const int bid = blockIdx.x;

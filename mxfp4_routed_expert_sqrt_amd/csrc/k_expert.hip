@@ -480,20 +480,12 @@ static unsigned unit_grid(int max_groups, int n_fb) {
 constexpr int kWideUnitPairs = 1024;
 
 // Dynamic LDS of one kernel instantiation: two chunk buffers of NB column
-// tiles; above 64 KB the limit is raised once per instantiation.
-template <typename Kern>
-static hipError_t lds_limit(Kern* kernel, size_t bytes, bool& done) {
-  if (done || bytes <= 65536) return hipSuccess;
-  hipError_t err = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (err == hipSuccess) done = true;
-  return err;
-}
-
+// tiles (above 64 KB the per-device limit is raised on first use).
 template <int TPM, int WAVES, int NB, bool NT = false, int RING = kRing>
 static hipError_t gateup_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
-  static bool attr = false;
+  static std::atomic<uint64_t> attr{0};
   const size_t lds = 2 * NB * (size_t)kChunkBytes;
-  hipError_t err = lds_limit(gateup_kernel<TPM, WAVES, NB, RING, NT>, lds, attr);
+  hipError_t err = ensure_dynamic_lds(gateup_kernel<TPM, WAVES, NB, RING, NT>, lds, attr);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((gateup_kernel<TPM, WAVES, NB, RING, NT>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
                      dim3(64 * WAVES), lds, stream, a);
@@ -502,9 +494,9 @@ static hipError_t gateup_launch(const ExpertArgs& a, int max_groups, hipStream_t
 
 template <int NA, int WAVES, int NB, bool NT = false, int RING = kRing>
 static hipError_t down_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
-  static bool attr = false;
+  static std::atomic<uint64_t> attr{0};
   const size_t lds = 2 * NB * (size_t)kChunkBytes;
-  hipError_t err = lds_limit(down_kernel<NA, WAVES, NB, RING, NT>, lds, attr);
+  hipError_t err = ensure_dynamic_lds(down_kernel<NA, WAVES, NB, RING, NT>, lds, attr);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((down_kernel<NA, WAVES, NB, RING, NT>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
                      dim3(64 * WAVES), lds, stream, a);

@@ -603,12 +603,10 @@ hipError_t launch_select_route(const float* z, const float* bias, int d, int n_r
                                int32_t* n_groups, Group* tall_groups, int32_t* n_tall_groups, int32_t* hist,
                                int32_t* done, hipStream_t stream) {
   if (E > kMaxExperts || k > kMaxTopK) return hipErrorInvalidValue;
-  static bool attr_set = false;  // one-time raise of the dynamic LDS limit (64 KB at E = 1024)
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void*)select_route_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)(sizeof(float) * kRouteWaves * kMaxExperts));
+  static std::atomic<uint64_t> attr{0};  // dynamic LDS up to 64 KB (E = 1024) plus the static part
+  {
+    hipError_t err = ensure_dynamic_lds(select_route_kernel, sizeof(float) * kRouteWaves * kMaxExperts, attr);
     if (err != hipSuccess) return err;
-    attr_set = true;
   }
   const int P = n_rows * k;
   const int here = P <= kScatterInBlockMax;

@@ -1,6 +1,7 @@
 // Launch wrappers of the gfx950 kernels (host side).  All launches are
 // asynchronous on `stream`; shapes are validated by the caller.
 #pragma once
+#include <atomic>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -8,6 +9,22 @@
 #include "common.h"
 
 namespace moe {
+
+// Sets a kernel's dynamic LDS limit to `bytes` once per device (the limit is
+// a per-device function attribute; `done` holds one bit per device id < 64,
+// higher ids set it on every call).  Concurrent first calls both set it, which
+// is harmless.
+template <typename Kern>
+inline hipError_t ensure_dynamic_lds(Kern* kernel, size_t bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
+  if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+  err = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (err == hipSuccess) done.fetch_or(bit, std::memory_order_relaxed);
+  return err;
+}
 
 // Packed-layout sizes of one MXFP4 matrix [rows][K] (rows % 16 == 0, K % 128 == 0).
 __host__ __device__ inline size_t packed_q_bytes(int rows, int K) { return (size_t)rows * (size_t)(K / 2); }

@@ -1,0 +1,115 @@
+"""Run-to-run and workspace robustness of the HIP path, through the C ABI.
+
+The layer keeps no state between calls: every workspace region it reads is
+written earlier in the same call.  These tests poison the workspace, reuse it
+across calls of different sizes and record stage events with some entries
+left NULL, and require bitwise-identical outputs and routing.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from mxfp4_routed_expert_sqrt_amd import capi  # noqa: E402
+from mxfp4_routed_expert_sqrt_amd.configs import SHAPES, MoEShape  # noqa: E402
+from mxfp4_routed_expert_sqrt_amd.layer import MoELayer, PackedExperts  # noqa: E402
+from tests.inputs import workload  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TALL = MoEShape("edge_tall", 611, 512, 8, 4, 256, "topk", "edge_tall")
+
+
+def _layer(wl):
+    sh = wl["shape"]
+    dev = torch.device("cuda")
+    packed = PackedExperts(wl["experts"], sh, dev, True)
+    return MoELayer(sh, wl["router_w"], packed, dev, router_bias=wl["bias"])
+
+
+def _inputs(wl, rows=None):
+    sh = wl["shape"]
+    x = wl["x"] if rows is None else wl["x"][:rows]
+    xt = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    tok = tab = None
+    if sh.routing == "hash":
+        ids = wl["token_ids"] if rows is None else wl["token_ids"][:rows]
+        tok = torch.from_numpy(np.ascontiguousarray(ids)).cuda()
+        tab = torch.from_numpy(wl["tid2eid"]).cuda()
+    return xt, tok, tab
+
+
+def _run(layer, x, tok, tab, ws):
+    out, routing = layer.forward(x, tok, tab, workspace=ws, with_routing=True)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy() for k, v in routing.items()}
+    res["out"] = out.view(torch.int16).cpu().numpy()
+    return res
+
+
+def _same(a, b, label):
+    for key in a:
+        assert np.array_equal(a[key], b[key]), f"{label}: {key} differs"
+
+
+@pytest.mark.parametrize("shape", [TALL, SHAPES["hash2048"]], ids=["tall", "hash2048-scatter"])
+def test_poisoned_workspace_repeatable(shape):
+    # tall: the 64-row work units; hash2048: 12288 pairs, so the separate scatter launch
+    wl = workload(shape)
+    layer = _layer(wl)
+    x, tok, tab = _inputs(wl)
+    print(f"poisoned workspace {shape.name} N={shape.n_rows}", flush=True)
+    ws = torch.full((layer.workspace_bytes(shape.n_rows),), 0xAB, dtype=torch.uint8, device="cuda")
+    first = _run(layer, x, tok, tab, ws)
+    ws.fill_(0x5C)
+    second = _run(layer, x, tok, tab, ws)
+    third = _run(layer, x, tok, tab, layer.new_workspace(shape.n_rows))
+    _same(first, second, shape.name)
+    _same(first, third, shape.name)
+
+
+def test_workspace_reused_for_a_smaller_batch():
+    wl = workload(TALL)
+    layer = _layer(wl)
+    big = layer.new_workspace(TALL.n_rows)
+    x, tok, tab = _inputs(wl)
+    _run(layer, x, tok, tab, big)  # leaves the big call's data in the workspace
+    xs, toks, tabs = _inputs(wl, rows=100)
+    print("workspace reuse: 611 rows, then 100 rows", flush=True)
+    reused = _run(layer, xs, toks, tabs, big)
+    fresh = _run(layer, xs, toks, tabs, layer.new_workspace(100))
+    _same(reused, fresh, "reuse")
+
+
+def test_stage_events_with_null_entries():
+    wl = workload("tiny")
+    layer = _layer(wl)
+    x, tok, tab = _inputs(wl)
+    want = _run(layer, x, tok, tab, layer.new_workspace(x.shape[0]))
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(2):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    arr = (ctypes.c_void_p * capi.MOE_N_STAGE_EVENTS)(*([None] * capi.MOE_N_STAGE_EVENTS))
+    g = capi.STAGE_NAMES.index("gateup")
+    arr[g], arr[g + 1] = evs
+    out = torch.empty_like(x)
+    ws = layer.new_workspace(x.shape[0])
+    call = layer.args(x, out, ws, tok, tab)
+    call.stage_events = ctypes.cast(arr, ctypes.c_void_p)
+    print("stage events: only the two around gate/up", flush=True)
+    assert capi.moe_layer_forward(layer.cfg, call, torch.cuda.current_stream().cuda_stream) == capi.MOE_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy(), want["out"])
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[0]), ctypes.c_void_p(evs[1])) == 0
+    assert ms.value > 0.0
+    for e in evs:
+        hip.hipEventDestroy(ctypes.c_void_p(e))
