@@ -2,8 +2,9 @@
 
 The layer keeps no state between calls: every workspace region it reads is
 written earlier in the same call.  These tests poison the workspace, reuse it
-across calls of different sizes and record stage events with some entries
-left NULL, and require bitwise-identical outputs and routing.
+across calls of different sizes, record stage events with some entries left
+NULL and replay a captured HIP graph of one call, and require
+bitwise-identical outputs and routing.
 """
 import ctypes
 
@@ -113,3 +114,31 @@ def test_stage_events_with_null_entries():
     assert ms.value > 0.0
     for e in evs:
         hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+@pytest.mark.parametrize("name", ["decode8", "verify512"])
+def test_graph_capture_replays_match_eager(name):
+    # The forward enqueues kernels only (no memsets, no host synchronisation), so
+    # one call can be captured in a HIP graph; every replay must equal the eager result.
+    wl = workload(name)
+    layer = _layer(wl)
+    x, tok, tab = _inputs(wl)
+    ws = layer.new_workspace(x.shape[0])
+    out = torch.empty_like(x)
+    eager = layer.forward(x, tok, tab, out=torch.empty_like(x), workspace=layer.new_workspace(x.shape[0]))
+    torch.cuda.synchronize()
+    want = eager.view(torch.int16).cpu().numpy()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):  # first call outside capture (one-time attribute setup)
+        layer.forward(x, tok, tab, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    print(f"graph capture {name}", flush=True)
+    with torch.cuda.graph(g, stream=side):
+        layer.forward(x, tok, tab, out=out, workspace=ws)
+    for i in range(4):
+        out.zero_()
+        layer.forward(x, tok, tab, out=torch.empty_like(x), workspace=layer.new_workspace(x.shape[0]))  # eager work in between
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.view(torch.int16).cpu().numpy(), want), f"replay {i} differs"
