@@ -441,7 +441,7 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
     if (16 * c + col < g.cnt) {
       float* dst = a.y + ((size_t)g.p0 + 16 * c + col) * R + f0 + 4 * grp;
 #pragma unroll
-      for (int tt = 0; tt < NA; ++tt) *(v4f*)(dst + 16 * tt) = acc[tt][c];
+      for (int tt = 0; tt < NA; ++tt) __builtin_nontemporal_store(acc[tt][c], (v4f*)(dst + 16 * tt));
     }
 }
 
@@ -556,7 +556,9 @@ hipError_t launch_down(const ExpertArgs& a0, int max_groups, int max_tall_groups
 
 // ---------------------------------------------------------------------------
 // out[r] = y_shared[r] + route_scale * sum_j g[r][j] * y[inv[r][j]], fp32 in
-// ascending slot order, rounded once to bf16 (nearest even).
+// ascending slot order, rounded once to bf16 (nearest even).  y is written
+// once by the down GEMM and read once here: both sides use non-temporal
+// accesses.
 
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ inv,
                                                        const float* __restrict__ gates, int d, int k, int P,
@@ -582,8 +584,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
       const int c = min(c0 + u * step, d - 4);  // past the end: re-read the last chunk (not stored)
 #pragma unroll
       for (int j = 0; j < kMaxK; ++j)
-        if (j < k) v[u][j] = *(const v4f*)(src[j] + c);
-      v[u][kMaxK] = ysh ? *(const v4f*)(ysh + c) : v4f{0.f, 0.f, 0.f, 0.f};
+        if (j < k) v[u][j] = __builtin_nontemporal_load((const v4f*)(src[j] + c));
+      v[u][kMaxK] = ysh ? __builtin_nontemporal_load((const v4f*)(ysh + c)) : v4f{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
