@@ -86,6 +86,46 @@ __device__ __forceinline__ float fp8_byte_to_f32(uint32_t word, int byte) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// FP6 E2M3: sign, 2 exponent bits (bias 1), 3 mantissa bits; subnormals m/8,
+// normals 2^(e-1) * (1 + m/8), largest 7.5.  The scaled MFMA's 6-bit operand
+// holds K values 32*(l/16)..+31 of lane l as a little-endian bitstream over
+// the lane's first 6 dwords, value i at bits 6i..6i+5 (measured on gfx950;
+// the probe test pins it).
+
+// Shared exponent of a block whose largest magnitude is amax, so that
+// amax / 2^e <= 7.5 (inside E2M3, no saturation); clamped to the E8M0 range.
+__device__ __forceinline__ int fp6_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int ex;
+  frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex): amax / 2^(ex-3) in [4, 8)
+  int e = ex - 3;
+  if (amax > ldexpf(7.5f, e)) ++e;
+  e = e < -127 ? -127 : e;
+  e = e > 127 ? 127 : e;
+  return e;
+}
+
+// E2M3 code of f (|f| <= 7.5), rounded to nearest (ties to even mantissa).
+__device__ __forceinline__ uint32_t e2m3_code(float f) {
+  const float a = fabsf(f);
+  int code;
+  if (a < 1.f) {
+    code = (int)__builtin_rintf(a * 8.f);  // subnormal m/8; m = 8 is the code of 1.0
+  } else {
+    const int E = a >= 4.f ? 2 : (a >= 2.f ? 1 : 0);
+    code = ((E + 1) << 3) + (int)__builtin_rintf((a * ldexpf(1.f, -E) - 1.f) * 8.f);
+  }
+  code = code > 31 ? 31 : code;
+  return (uint32_t)code | (f < 0.f ? 0x20u : 0u);
+}
+
+__device__ __forceinline__ float e2m3_value(uint32_t code) {
+  const int e = (code >> 3) & 3, m = code & 7;
+  const float mag = e == 0 ? (float)m * 0.125f : ldexpf(1.f + (float)m * 0.125f, e - 1);
+  return (code & 0x20u) ? -mag : mag;
+}
+
 template <int kOff>
 __device__ __forceinline__ float shfl_xor_max(float v) {
   return fmaxf(v, __shfl_xor(v, kOff, kWave));

@@ -31,11 +31,11 @@ __device__ __forceinline__ size_t split_scale_offset_h(int term, int blk, int n_
   return (size_t)(((term * n_sg + (ks >> 2)) * 4 + (blk & 3)) * 4 + (ks & 3));
 }
 
-template <int J>
+template <int J, bool FP6 = false>
 __device__ __forceinline__ v4f mfma_fp4_fp8(const u32x4& a, const v8i& b, const v4f& c, uint32_t sa, uint32_t sb) {
   const v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b, c, 4 /* A: E2M1 */, 0 /* B: E4M3 */, J, (int)sa, J,
-                                                          (int)sb);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b, c, 4 /* A: E2M1 */, FP6 ? 2 /* B: E2M3 */ : 0 /* E4M3 */,
+                                                          J, (int)sa, J, (int)sb);
 }
 
 // ---------------------------------------------------------------------------
@@ -56,12 +56,18 @@ constexpr int kChunkBytes = kChunkData + 512;
 // tile.  THREADS divides 1024, so the tile of piece m is (THREADS*m) >> 10.
 // The chunk's 128*NB scale dwords are carried as dword tid + THREADS*i
 // (tile (tid + THREADS*i) >> 7).
-template <int THREADS, int NB>
+//
+// FP6 chunks (two E2M3 terms): per tile and (k-step j, term t) 1536 bytes, a
+// 16-byte plane [lane][dwords 0-3] at (2j+t)*1536 and an 8-byte plane
+// [lane][dwords 4-5] at (2j+t)*1536 + 1024; piece p (of 512 per tile and
+// plane) is (j, t, g, col) = (p>>7, p>>6 & 1, p>>4 & 3, p & 15).
+template <int THREADS, int NB, bool FP6 = false>
 struct ChunkStage {
-  static_assert(1024 % THREADS == 0, "chunk staging shape");
-  static constexpr int kPieces = 1024 * NB / THREADS;
+  static_assert(1024 % THREADS == 0 && (!FP6 || 512 % THREADS == 0), "chunk staging shape");
+  static constexpr int kPieces = FP6 ? 512 * NB / THREADS : 1024 * NB / THREADS;
   static constexpr int kScales = (128 * NB + THREADS - 1) / THREADS;
   u32x4 q[kPieces];
+  uint2 q8[FP6 ? kPieces : 1];
   uint32_t s[kScales];
 
   // brow_q[t]: this thread's token row of tile t; brow_s[i]: the scale row of
@@ -69,13 +75,26 @@ struct ChunkStage {
   __device__ __forceinline__ void load(const uint8_t* const (&brow_q)[NB], const uint8_t* const (&brow_s)[kScales],
                                        int sg, int nks, int n_sg) {
     const int tid = threadIdx.x;
+    if constexpr (FP6) {
 #pragma unroll
-    for (int m = 0; m < kPieces; ++m) {
-      const int tile = (THREADS * m) >> 10;
-      const int p = (tid + THREADS * m) & 1023;
-      const int j = p >> 8, t = (p >> 7) & 1, h = (p >> 6) & 1, g = (p >> 4) & 3;
-      const int ks = min(4 * sg + j, nks - 1);  // past the end: any valid step (never multiplied)
-      q[m] = *(const u32x4*)(brow_q[tile] + (size_t)ks * 256 + g * 64 + t * 32 + h * 16);
+      for (int m = 0; m < kPieces; ++m) {
+        const int tile = (THREADS * m) >> 9;
+        const int p = (tid + THREADS * m) & 511;
+        const int j = p >> 7, t = (p >> 6) & 1, g = (p >> 4) & 3;
+        const int ks = min(4 * sg + j, nks - 1);
+        const uint8_t* src = brow_q[tile] + (size_t)ks * 192 + t * 96;
+        q[m] = *(const u32x4*)(src + g * 16);
+        q8[m] = *(const uint2*)(src + 64 + g * 8);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < kPieces; ++m) {
+        const int tile = (THREADS * m) >> 10;
+        const int p = (tid + THREADS * m) & 1023;
+        const int j = p >> 8, t = (p >> 7) & 1, h = (p >> 6) & 1, g = (p >> 4) & 3;
+        const int ks = min(4 * sg + j, nks - 1);  // past the end: any valid step (never multiplied)
+        q[m] = *(const u32x4*)(brow_q[tile] + (size_t)ks * 256 + g * 64 + t * 32 + h * 16);
+      }
     }
 #pragma unroll
     for (int i = 0; i < kScales; ++i) {
@@ -89,10 +108,21 @@ struct ChunkStage {
 
   __device__ __forceinline__ void store(uint8_t* buf) const {
     const int tid = threadIdx.x;
+    if constexpr (FP6) {
 #pragma unroll
-    for (int m = 0; m < kPieces; ++m) {
-      const int tile = (THREADS * m) >> 10;
-      *(u32x4*)(buf + tile * kChunkBytes + ((tid + THREADS * m) & 1023) * 16) = q[m];
+      for (int m = 0; m < kPieces; ++m) {
+        const int tile = (THREADS * m) >> 9;
+        const int p = (tid + THREADS * m) & 511;
+        uint8_t* dst = buf + tile * kChunkBytes + (p >> 6) * 1536;
+        *(u32x4*)(dst + (p & 63) * 16) = q[m];
+        *(uint2*)(dst + 1024 + (p & 63) * 8) = q8[m];
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < kPieces; ++m) {
+        const int tile = (THREADS * m) >> 10;
+        *(u32x4*)(buf + tile * kChunkBytes + ((tid + THREADS * m) & 1023) * 16) = q[m];
+      }
     }
 #pragma unroll
     for (int i = 0; i < kScales; ++i) {
@@ -142,29 +172,36 @@ __device__ __forceinline__ void load_wscales(uint32_t (&sa)[NA], const gptr (&ws
 // accumulator are NA*NB MFMAs apart, and double-buffered: fragment i+1 is read
 // from LDS before fragment i's MFMAs are issued, so the LDS latency is
 // covered by MFMA work.
-template <int J, int NB>
+template <int J, int NB, bool FP6>
 __device__ __forceinline__ v8i read_b(const uint8_t* chunk, int i) {
   const int lane = threadIdx.x & 63, tt = i % NB, t = i / NB;
-  const uint8_t* c = chunk + tt * kChunkBytes + (J * 2 + t) * 2048 + lane * 16;
-  const u32x4 lo = *(const u32x4*)c;
-  const u32x4 hi = *(const u32x4*)(c + 1024);
-  return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  if constexpr (FP6) {
+    const uint8_t* c = chunk + tt * kChunkBytes + (J * 2 + t) * 1536;
+    const u32x4 lo = *(const u32x4*)(c + lane * 16);
+    const uint2 hi = *(const uint2*)(c + 1024 + lane * 8);
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi.x, (int)hi.y, 0, 0};
+  } else {
+    const uint8_t* c = chunk + tt * kChunkBytes + (J * 2 + t) * 2048 + lane * 16;
+    const u32x4 lo = *(const u32x4*)c;
+    const u32x4 hi = *(const u32x4*)(c + 1024);
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
 }
 
-template <int J, int NA, int NB>
+template <int J, int NA, int NB, bool FP6>
 __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chunk, const uint32_t (&sa)[NA],
                                          const uint32_t (&sb)[NB][2], v4f (&acc)[NA][NB]) {
   constexpr int NF = 2 * NB;
-  v8i b0 = read_b<J, NB>(chunk, 0), b1;
+  v8i b0 = read_b<J, NB, FP6>(chunk, 0), b1;
 #pragma unroll
   for (int i = 0; i < NF; ++i) {
     v8i& cur = (i & 1) ? b1 : b0;
     v8i& nxt = (i & 1) ? b0 : b1;
     const int tt = i % NB, t = i / NB;
-    if (i + 1 < NF) nxt = read_b<J, NB>(chunk, i + 1);
+    if (i + 1 < NF) nxt = read_b<J, NB, FP6>(chunk, i + 1);
     if (NF > 2) __builtin_amdgcn_sched_barrier(0);  // keep the read ahead of these MFMAs
 #pragma unroll
-    for (int a = 0; a < NA; ++a) acc[a][tt] = mfma_fp4_fp8<J>(f.A[a], cur, acc[a][tt], sa[a], sb[tt][t]);
+    for (int a = 0; a < NA; ++a) acc[a][tt] = mfma_fp4_fp8<J, FP6>(f.A[a], cur, acc[a][tt], sa[a], sb[tt][t]);
     if (NF > 2) __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -175,7 +212,8 @@ __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chun
 // inside a ring cycle (RING/4 groups per cycle), so every slot index and scale
 // byte is a compile-time constant.
 template <int GI, int RING, int NA, int THREADS, int NB, bool NT>
-__device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB>& stage, uint32_t (&sa)[NA],
+__device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB, (NB > 1)>& stage,
+                                        uint32_t (&sa)[NA],
                                         uint32_t (&sa_n)[NA], const gptr (&aq)[NA], const gptr (&as)[NA],
                                         const uint8_t* const (&brow_q)[NB],
                                         const uint8_t* const (&brow_s)[ChunkStage<THREADS, NB>::kScales], int sg,
@@ -193,19 +231,19 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
   load_wscales(sa_n, as, min(sg + 1, n_sg - 1));
   load_w<NT>(f[(4 * GI + RING - 1) % RING], aq, min(k0 + RING - 1, last));
   __builtin_amdgcn_sched_barrier(0);
-  mma_step<0>(f[(4 * GI) % RING], chunk, sa, sb, acc);
+  mma_step<0, NA, NB, (NB > 1)>(f[(4 * GI) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
   load_w<NT>(f[(4 * GI + RING) % RING], aq, min(k0 + RING, last));
   __builtin_amdgcn_sched_barrier(0);
-  if (k0 + 1 < nks) mma_step<1>(f[(4 * GI + 1) % RING], chunk, sa, sb, acc);
+  if (k0 + 1 < nks) mma_step<1, NA, NB, (NB > 1)>(f[(4 * GI + 1) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
   load_w<NT>(f[(4 * GI + RING + 1) % RING], aq, min(k0 + RING + 1, last));
   __builtin_amdgcn_sched_barrier(0);
-  if (k0 + 2 < nks) mma_step<2>(f[(4 * GI + 2) % RING], chunk, sa, sb, acc);
+  if (k0 + 2 < nks) mma_step<2, NA, NB, (NB > 1)>(f[(4 * GI + 2) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
   load_w<NT>(f[(4 * GI + RING + 2) % RING], aq, min(k0 + RING + 2, last));
   __builtin_amdgcn_sched_barrier(0);
-  if (k0 + 3 < nks) mma_step<3>(f[(4 * GI + 3) % RING], chunk, sa, sb, acc);
+  if (k0 + 3 < nks) mma_step<3, NA, NB, (NB > 1)>(f[(4 * GI + 3) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
   stage.store(lds + ((sg + 1) & 1) * kBuf);
   __syncthreads();
@@ -228,7 +266,7 @@ __device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[
                                          v4f (&acc)[NA][NB], uint8_t* lds) {
   static_assert(RING == 4 || RING == 8, "ring of 1 or 2 groups");
   const int n_sg = (nks + 3) / 4, last = nks - 1;
-  ChunkStage<THREADS, NB> stage;
+  ChunkStage<THREADS, NB, (NB > 1)> stage;
   WFrag<NA> f[RING];
   uint32_t sa[NA], sa_n[NA];
   stage.load(brow_q, brow_s, 0, nks, n_sg);
@@ -274,6 +312,72 @@ __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Group g, i
 // Each of the WAVES waves takes TPM 16-row tiles of the gate matrix and the
 // same rows of the up matrix: 16*TPM features per wave, 16*TPM*WAVES per work
 // unit.
+
+// The 24-bit run of four E2M3 codes of v[0..3] * inv (value i at bits 6i).
+__device__ __forceinline__ uint32_t e2m3_run4(const float* v, float inv) {
+  return e2m3_code(v[0] * inv) | (e2m3_code(v[1] * inv) << 6) | (e2m3_code(v[2] * inv) << 12) |
+         (e2m3_code(v[3] * inv) << 18);
+}
+
+// Tall units write h as the two-term FP6 split (the x split's FP6 layout, K =
+// I).  Lane (col, grp) holds values 4grp..4grp+3 and 16+4grp..+3 of block
+// blk_h of token column col: 24-bit runs at bits 24grp and 96+24grp of the
+// block's 192-bit operand.  The four lanes of a column exchange their runs;
+// lane grp then stores term grp/2, plane grp%2 (dwords 0-3 or 4-5).
+__device__ __forceinline__ void write_h_fp6(const ExpertArgs& a, const Group g, int c, int col, int grp, int blk_h,
+                                            int n_sg_h, const float (&h)[8], float amax) {
+  const int e1 = fp6_exponent(amax);
+  const float inv1 = ldexpf(1.f, -e1), sc1 = ldexpf(1.f, e1);
+  uint32_t run[2][2];  // [term][half]
+  float res[8];
+  float amax2 = 0.f;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    run[0][hh] = e2m3_run4(h + 4 * hh, inv1);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      res[4 * hh + ii] = h[4 * hh + ii] - e2m3_value((run[0][hh] >> (6 * ii)) & 63u) * sc1;
+      amax2 = fmaxf(amax2, fabsf(res[4 * hh + ii]));
+    }
+  }
+  amax2 = shfl_xor_max<16>(amax2);
+  amax2 = shfl_xor_max<32>(amax2);
+  const int e2 = fp6_exponent(amax2);
+  const float inv2 = ldexpf(1.f, -e2);
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) run[1][hh] = e2m3_run4(res + 4 * hh, inv2);
+  // r[t][hh][q]: run of lane col + 16q
+  uint32_t r[2][2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[t][hh][q] = (uint32_t)__shfl((int)run[t][hh], col + 16 * q, 64);
+  if (16 * c + col < g.cnt) {
+    const int t = grp >> 1;
+    uint32_t D[6];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint32_t* q = t ? r[1][hh] : r[0][hh];
+      D[3 * hh] = q[0] | (q[1] << 24);
+      D[3 * hh + 1] = (q[1] >> 8) | (q[2] << 16);
+      D[3 * hh + 2] = (q[2] >> 16) | (q[3] << 8);
+    }
+    const size_t p = (size_t)g.p0 + 16 * c + col;
+    uint8_t* dst = a.hq + p * split_q_row_bytes(a.R) + (size_t)(blk_h >> 2) * kFp6StepBytes + t * kFp6TermBytes;
+    const int bb = blk_h & 3;
+    if (grp & 1)
+      *(uint2*)(dst + 64 + 8 * bb) = uint2{D[4], D[5]};
+    else
+      *(u32x4*)(dst + 16 * bb) = u32x4{D[0], D[1], D[2], D[3]};
+    if (grp == 0) {
+      uint8_t* srow = a.hs + p * split_s_row_bytes(a.R);
+      srow[split_scale_offset_h(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
+      srow[split_scale_offset_h(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
+    }
+  }
+}
 
 // One work unit: features [fu0, fu0 + WAVES*16*TPM) of gate and up for the
 // rows of group g.
@@ -338,6 +442,10 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[j]));
     amax = shfl_xor_max<16>(amax);
     amax = shfl_xor_max<32>(amax);
+    if constexpr (NB > 1) {
+      write_h_fp6(a, g, c, col, grp, blk_h, n_sg_h, h, amax);
+      continue;
+    }
     const int e1 = split_exponent(amax);
     const float inv1 = ldexpf(1.f, -e1), sc1 = ldexpf(1.f, e1);
     uint32_t w1[2], w2[2];
@@ -509,17 +617,15 @@ static hipError_t down_launch(const ExpertArgs& a, int max_groups, hipStream_t s
 // measured slightly slower (more activation staging per weight byte).
 constexpr int kSmallTailUnits = 64;
 
-// Batches with at least kTallRowsPerExpert routed rows per expert on average
-// (prefill-like) use units of up to 64 rows (4 column tiles) from the 64-row
-// work list: each weight fragment then feeds 4x as many MFMAs.
-constexpr int kTallRowsPerExpert = 32;
-
-static bool tall_batch(const ExpertArgs& a) { return a.P >= kTallRowsPerExpert * a.E; }
+// Tall batches (a.tall, see use_tall_units: prefill-like, many routed rows
+// per expert) use units of up to 64 rows (4 column tiles) from the 64-row work
+// list: each weight fragment then feeds 4x as many MFMAs.  Their activations
+// (x and h) are the two-term FP6 split, whose MFMA runs at twice the FP8 rate.
 
 hipError_t launch_gateup(const ExpertArgs& a0, int max_groups, int max_tall_groups, hipStream_t stream) {
   ExpertArgs a = a0;
   a.tail_units = a.P < kWideUnitPairs ? kSmallTailUnits : 0;
-  if (tall_batch(a) && a.R % 256 == 0) {
+  if (a.tall) {
     a.groups = a.tall_groups;
     a.n_groups = a.n_tall_groups;
     a.tail_units = 0;
@@ -538,7 +644,7 @@ hipError_t launch_gateup(const ExpertArgs& a0, int max_groups, int max_tall_grou
 hipError_t launch_down(const ExpertArgs& a0, int max_groups, int max_tall_groups, hipStream_t stream) {
   ExpertArgs a = a0;
   a.tail_units = a.P < kWideUnitPairs ? kSmallTailUnits : 0;
-  if (tall_batch(a) && a.R % 512 == 0) {
+  if (a.tall) {
     a.groups = a.tall_groups;
     a.n_groups = a.n_tall_groups;
     a.tail_units = 0;

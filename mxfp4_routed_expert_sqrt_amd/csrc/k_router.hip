@@ -149,12 +149,12 @@ __device__ __forceinline__ void logits_tile(const uint16_t* __restrict__ x, cons
 }
 
 // Workgroups [0, n_tiles) compute logits tiles; the rest split x (one
-// 32-value block per thread).  Workgroup 0 also clears the completion counter
+// 32-value block per thread; FP6 for batches of tall work units, else FP8).  Workgroup 0 also clears the completion counter
 // of the select+route launch that follows on the stream.
 __global__ void __launch_bounds__(256) prologue_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
                                                         int n_rows, int d, int E, int S, int n_tiles,
                                                         float* __restrict__ z_part, uint8_t* __restrict__ xq,
-                                                        uint8_t* __restrict__ xs, int32_t* __restrict__ done) {
+                                                        uint8_t* __restrict__ xs, int32_t* __restrict__ done, int fp6) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kLgBufBytes];
   const int b = blockIdx.x;
   if (b == 0 && threadIdx.x == 0) *done = 0;
@@ -162,17 +162,17 @@ __global__ void __launch_bounds__(256) prologue_kernel(const uint16_t* __restric
     logits_tile(x, w, n_rows, d, E, S, z_part, b, lds);
   } else {
     const size_t t = (size_t)(b - n_tiles) * blockDim.x + threadIdx.x;
-    if (t < (size_t)n_rows * (d / 32)) split_bf16_block(x, d, xq, xs, t);
+    if (t < (size_t)n_rows * (d / 32)) split_bf16_block(x, d, xq, xs, t, fp6 != 0);
   }
 }
 
 hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d, int E, float* z_part,
-                           uint8_t* xq, uint8_t* xs, int32_t* done, hipStream_t stream) {
+                           uint8_t* xq, uint8_t* xs, int32_t* done, bool fp6, hipStream_t stream) {
   const int S = logits_splits(n_rows, E, d);
   const int n_tiles = logits_row_tiles(n_rows) * ((E + kLgExperts - 1) / kLgExperts) * S;
   const size_t n_split = ((size_t)n_rows * (d / 32) + 255) / 256;
   hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)(n_tiles + n_split)), dim3(256), 0, stream, x, w, n_rows, d, E,
-                     S, n_tiles, z_part, xq, xs, done);
+                     S, n_tiles, z_part, xq, xs, done, fp6 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -34,6 +34,8 @@ __host__ __device__ inline size_t packed_s_bytes(int rows, int K) {
 }
 // Two-term FP8 split of activation rows of length K.
 __host__ __device__ inline size_t split_q_row_bytes(int K) { return (size_t)K * 2; }
+// FP6 split rows (tall units) use 192 bytes per 128-wide k-step of the same row, 96 per term.
+constexpr int kFp6StepBytes = 192, kFp6TermBytes = 96;
 __host__ __device__ inline size_t split_s_row_bytes(int K) {
   const int nks = K / 128, n_sg = (nks + 3) / 4;
   return (size_t)2 * n_sg * 16;
@@ -43,7 +45,15 @@ hipError_t launch_pack_mxfp4(const uint8_t* q, const uint8_t* s, int n_mat, int 
                              uint8_t* s_out, hipStream_t stream);
 
 hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d, int E, float* z_part, uint8_t* xq,
-                           uint8_t* xs, int32_t* done, hipStream_t stream);
+                           uint8_t* xs, int32_t* done, bool fp6, hipStream_t stream);
+
+// Batches with at least 32 routed rows per expert on average (prefill-like)
+// run the expert GEMMs as tall work units (up to 64 rows of one expert) on
+// activations split into two FP6 terms; both GEMMs need their tall widths
+// (gate/up I % 256, down d % 512).
+inline bool use_tall_units(int n_pairs, int E, int d, int I) {
+  return n_pairs >= 32 * E && I % 256 == 0 && d % 512 == 0;
+}
 
 // Split-K factor of the router logits: enough 64x64 tiles for >= 256
 // workgroups, at most 16 partials and at least two 64-wide K chunks each.
@@ -90,6 +100,7 @@ struct ExpertArgs {
   uint8_t* hs;                           // gate/up output: split h scales
   float* y;                              // down output [pairs][R]
   int tail_units;                        // units per XCD processed as two halves at the end
+  int tall;                              // tall work units on FP6 activations (use_tall_units)
 };
 
 hipError_t launch_gateup(const ExpertArgs& a, int max_groups, int max_tall_groups, hipStream_t stream);

@@ -186,7 +186,9 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
            hipEventRecord((hipEvent_t)a.stage_events[i], stream) == hipSuccess;
   };
   if (!mark(0)) return MOE_ERR_HIP;
-  if ((err = launch_prologue((const uint16_t*)a.x, a.router_w, N, d, E, z, xq, xs, done, stream)) != hipSuccess)
+  const bool tall = use_tall_units(P, E, d, I);
+  if ((err = launch_prologue((const uint16_t*)a.x, a.router_w, N, d, E, z, xq, xs, done, tall, stream)) !=
+      hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
   if ((err = launch_select_route(z, a.router_bias, d, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, c.has_shared,
@@ -211,6 +213,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   ga.n_groups = n_groups;
   ga.tall_groups = tall_groups;
   ga.n_tall_groups = n_tall_groups;
+  ga.tall = tall ? 1 : 0;
   ga.K = d;
   ga.R = I;
   ga.E = E;

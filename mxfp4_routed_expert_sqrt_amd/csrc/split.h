@@ -1,5 +1,5 @@
-// Two-term FP8 split of bf16 activation rows (device code shared by the
-// kernels that produce the split).
+// Two-term FP8 and FP6 splits of activation rows (device code shared by the
+// kernels that produce the splits).
 #pragma once
 #include "kernels.h"
 
@@ -53,9 +53,62 @@ __device__ __forceinline__ size_t split_scale_offset(int term, int blk, int n_sg
   return (size_t)(((term * n_sg + (ks >> 2)) * 4 + (blk & 3)) * 4 + (ks & 3));
 }
 
-// Split of one 32-value block t = row * (K/32) + block of x (t < n_rows * K/32).
+// ---------------------------------------------------------------------------
+// Two-term FP6 (E2M3) split, used for batches of tall work units: v ~= q1 *
+// 2^e1 + q2 * 2^e2 with q1, q2 E2M3 (the same scheme as the FP8 split; the
+// second term leaves a residual of about 2^-10 of the block maximum).
+//
+// Row layout: k-step ks occupies 192 bytes at ks*192 (inside a row of the FP8
+// split's length), term t at t*96 as two planes of the lane groups' 6-dword
+// operands: dwords 0-3 of group g at g*16, dwords 4-5 at 64 + g*8.  Group g
+// = the 32-block 4ks+g.  Scales as for the FP8 split.
+
+// E2M3 codes of v[i] * inv for 32 values, packed as the operand bitstream
+// (6 dwords, value i at bits 6i..6i+5).
+__device__ __forceinline__ void pack_fp6_block(const float* v, float inv, uint32_t* q /*6 dwords*/) {
+#pragma unroll
+  for (int w = 0; w < 6; ++w) q[w] = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t c = e2m3_code(v[i] * inv);
+    const int bit = 6 * i, w = bit >> 5, sh = bit & 31;
+    q[w] |= c << sh;
+    if (sh > 26) q[w + 1] |= c >> (32 - sh);
+  }
+}
+
+__device__ __forceinline__ float fp6_code_at(const uint32_t* q, int i) {
+  const int bit = 6 * i, w = bit >> 5, sh = bit & 31;
+  uint32_t c = q[w] >> sh;
+  if (sh > 26) c |= q[w + 1] << (32 - sh);
+  return e2m3_value(c & 63u);
+}
+
+__device__ __forceinline__ void split_block32_fp6(const float* v, uint32_t* q /*12 dwords*/, int* e1_out,
+                                                  int* e2_out) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e1 = fp6_exponent(amax);
+  pack_fp6_block(v, ldexpf(1.f, -e1), q);
+  const float sc1 = ldexpf(1.f, e1);
+  float r[32];
+  float amax2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    r[i] = v[i] - fp6_code_at(q, i) * sc1;
+    amax2 = fmaxf(amax2, fabsf(r[i]));
+  }
+  const int e2 = fp6_exponent(amax2);
+  pack_fp6_block(r, ldexpf(1.f, -e2), q + 6);
+  *e1_out = e1;
+  *e2_out = e2;
+}
+
+// Split of one 32-value block t = row * (K/32) + block of x (t < n_rows * K/32),
+// FP6 when fp6 is set, else FP8.
 __device__ __forceinline__ void split_bf16_block(const uint16_t* __restrict__ x, int K, uint8_t* __restrict__ xq,
-                                                 uint8_t* __restrict__ xs, size_t t) {
+                                                 uint8_t* __restrict__ xs, size_t t, bool fp6) {
   const int nkb = K / 32, n_sg = (K / 128 + 3) / 4;
   const size_t row = t / nkb;
   const int blk = (int)(t % nkb);
@@ -69,6 +122,23 @@ __device__ __forceinline__ void split_bf16_block(const uint16_t* __restrict__ x,
       v[c * 8 + 2 * h] = __uint_as_float(w[h] << 16);
       v[c * 8 + 2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
     }
+  }
+  if (fp6) {
+    uint32_t q[12];
+    int e1, e2;
+    split_block32_fp6(v, q, &e1, &e2);
+    uint8_t* step = xq + row * split_q_row_bytes(K) + (size_t)(blk >> 2) * kFp6StepBytes;
+    const int g = blk & 3;
+#pragma unroll
+    for (int term = 0; term < 2; ++term) {
+      const uint32_t* w = q + 6 * term;
+      *(u32x4*)(step + term * kFp6TermBytes + g * 16) = u32x4{w[0], w[1], w[2], w[3]};
+      *(uint2*)(step + term * kFp6TermBytes + 64 + g * 8) = uint2{w[4], w[5]};
+    }
+    uint8_t* srow = xs + row * split_s_row_bytes(K);
+    srow[split_scale_offset(0, blk, n_sg)] = (uint8_t)(e1 + 127);
+    srow[split_scale_offset(1, blk, n_sg)] = (uint8_t)(e2 + 127);
+    return;
   }
   uint32_t q[16];
   int e1, e2;

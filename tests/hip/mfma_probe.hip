@@ -1,6 +1,6 @@
 // Single-wave probes of the gfx950 instructions the expert kernels rely on:
-// the scaled FP4 x FP8 MFMA (operand lane layout, scale byte selection, result
-// layout) and the FP8 (E4M3) conversions.  Test-only; every access is within
+// the scaled FP4 x FP8 (and FP4 x FP6) MFMA (operand lane layout, scale byte
+// selection, result layout) and the FP8 (E4M3) conversions.  Test-only; every access is within
 // the 64-lane buffers the host passes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,7 +30,7 @@ __global__ void probe_fp8_kernel(const float* in, uint32_t* packed, float* back,
 
 // a, b: 64 lanes x 32 bytes; sa, sb: 64 dwords; d: 64 x 4 floats.
 // variant 0: A E2M1, B E4M3, scale bytes 0/0; 1: same with scale bytes 2 (A) / 1 (B);
-// variant 2: A E2M1, B E2M1, scale bytes 0/0.
+// variant 2: A E2M1, B E2M1, scale bytes 0/0; 3: A E2M1, B E2M3 (FP6), scale bytes 0/0.
 extern "C" int probe_mfma(const void* a, const void* b, const void* sa, const void* sb, void* d, int variant) {
   const u32x4* A = (const u32x4*)a;
   const u32x4* B = (const u32x4*)b;
@@ -43,6 +43,8 @@ extern "C" int probe_mfma(const void* a, const void* b, const void* sa, const vo
     hipLaunchKernelGGL((probe_mfma_kernel<2, 1, 4, 0>), dim3(1), dim3(64), 0, 0, A, B, SA, SB, D);
   else if (variant == 2)
     hipLaunchKernelGGL((probe_mfma_kernel<0, 0, 4, 4>), dim3(1), dim3(64), 0, 0, A, B, SA, SB, D);
+  else if (variant == 3)
+    hipLaunchKernelGGL((probe_mfma_kernel<0, 0, 4, 2>), dim3(1), dim3(64), 0, 0, A, B, SA, SB, D);
   else
     return -1;
   if (hipGetLastError() != hipSuccess) return -4;

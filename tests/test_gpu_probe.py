@@ -5,6 +5,9 @@
     32*(l/16) .. +31 as nibbles, low nibble first;
   * an 8-bit (E4M3) operand: lane l holds row/column l%16, K values
     16*(l/16) .. +15 in bytes 0..15 and 64 + 16*(l/16) .. +15 in bytes 16..31;
+  * a 6-bit (E2M3) operand: lane l holds row/column l%16, K values
+    32*(l/16) .. +31, value i in bits 6i .. 6i+5 of the little-endian bit
+    string of dwords 0..5 (dwords 6 and 7 unused);
   * the E8M0 scale of row/column n and 32-block b (K 32b .. 32b+31) is the
     selected byte of the scale register of lane n + 16*b, for either format;
   * the fp32 result has D[4*(l/16)+i][l%16] in element i of lane l;
@@ -88,6 +91,22 @@ def _dense_fp8(b_bytes, scales):
     return M * _block_scales(scales)
 
 
+def e2m3(codes):
+    codes = codes.astype(np.int64)
+    sign = np.where(codes & 0x20, -1.0, 1.0)
+    E, M = (codes >> 3) & 3, codes & 7
+    return sign * np.where(E == 0, M / 8.0, np.ldexp(1.0 + M / 8.0, E - 1))
+
+
+def _dense_fp6(b_bytes, scales):
+    M = np.zeros((16, 128))
+    for l in range(64):
+        bits = int.from_bytes(b_bytes[l, :24].tobytes(), "little")
+        codes = np.array([(bits >> (6 * i)) & 63 for i in range(32)])
+        M[l % 16, 32 * (l // 16):32 * (l // 16) + 32] = e2m3(codes)
+    return M * _block_scales(scales)
+
+
 def _block_scales(scales):
     """Scale of (row n, block b) comes from lane n + 16 b."""
     S = np.zeros((16, 128))
@@ -101,13 +120,13 @@ def _lane_layout(D):
     return np.array([[D[4 * (l // 16) + i, l % 16] for i in range(4)] for l in range(64)])
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
 def test_scaled_mfma_layout(variant):
     print(f"probe_mfma variant {variant}", flush=True)
     rng = np.random.default_rng(10 + variant)
     a = rng.integers(0, 256, (64, 32), dtype=np.uint8)
     b = rng.integers(0, 256, (64, 32), dtype=np.uint8)
-    if variant != 2:
+    if variant in (0, 1):
         b[(b & 0x7F) == 0x7F] = 0x3C  # no NaN encodings
     sa_w = rng.integers(0, 2 ** 32, 64, dtype=np.uint64).astype(np.uint32)
     sb_w = rng.integers(0, 2 ** 32, 64, dtype=np.uint64).astype(np.uint32)
@@ -117,7 +136,7 @@ def test_scaled_mfma_layout(variant):
     sa_w = (sa_w & ~np.uint32(0xFF << (8 * ja))) | (sa.astype(np.uint32) << np.uint32(8 * ja))
     sb_w = (sb_w & ~np.uint32(0xFF << (8 * jb))) | (sb.astype(np.uint32) << np.uint32(8 * jb))
     A = _dense_fp4(a, sa)
-    B = _dense_fp4(b, sb) if variant == 2 else _dense_fp8(b, sb)
+    B = {2: _dense_fp4, 3: _dense_fp6}.get(variant, _dense_fp8)(b, sb)
     exp = _lane_layout(A @ B.T)
     max_prod = _lane_layout(np.abs(A[:, None, :] * B[None, :, :]).max(-1))
     dev = torch.device("cuda")
