@@ -122,7 +122,8 @@ typedef struct moe_args {
   /* Optional stage timing (NULL to skip): MOE_N_STAGE_EVENTS hipEvent_t handles
    * created by the caller.  Event i is recorded on `stream` just before stage i
    * and the last one after the final stage; a NULL entry is not recorded
-   * (each recorded event costs a few microseconds of stream time).  The
+   * (each recorded event costs several microseconds of stream time, about 9 us
+   * measured on MI355X between two kernels).  The
    * stages are 0 router logits + activation split, 1 top-k/hash selection +
    * routing bookkeeping, 2 gate/up GEMM, 3 down GEMM, 4 combine. */
   void* const* stage_events;

@@ -10,8 +10,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kGroupRows = 16;   // token rows of one grouped-GEMM work unit (one MFMA column tile)
-constexpr int kTallGroupRows = 64;  // token rows of a tall work unit (4 column tiles)
+constexpr int kGroupRows = 16;       // token rows of a narrow work unit (one MFMA column tile)
+constexpr int kMediumGroupRows = 32;  // token rows of a medium work unit (2 column tiles)
+constexpr int kTallGroupRows = 64;    // token rows of a tall work unit (4 column tiles)
 constexpr int kXcds = 8;         // gfx950: workgroups are dealt round-robin to 8 XCDs
 
 // One work unit of the grouped GEMMs: rows [p0, p0 + cnt) of expert e.

@@ -211,8 +211,8 @@ __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chun
 // fragments of ks+1 .. ks+RING-1 are in flight.  GI = position of this group
 // inside a ring cycle (RING/4 groups per cycle), so every slot index and scale
 // byte is a compile-time constant.
-template <int GI, int RING, int NA, int THREADS, int NB, bool NT>
-__device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB, (NB > 1)>& stage,
+template <int GI, int RING, int NA, int THREADS, int NB, bool NT, bool FP6>
+__device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB, FP6>& stage,
                                         uint32_t (&sa)[NA],
                                         uint32_t (&sa_n)[NA], const gptr (&aq)[NA], const gptr (&as)[NA],
                                         const uint8_t* const (&brow_q)[NB],
@@ -231,19 +231,19 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
   load_wscales(sa_n, as, min(sg + 1, n_sg - 1));
   load_w<NT>(f[(4 * GI + RING - 1) % RING], aq, min(k0 + RING - 1, last));
   __builtin_amdgcn_sched_barrier(0);
-  mma_step<0, NA, NB, (NB > 1)>(f[(4 * GI) % RING], chunk, sa, sb, acc);
+  mma_step<0, NA, NB, FP6>(f[(4 * GI) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
   load_w<NT>(f[(4 * GI + RING) % RING], aq, min(k0 + RING, last));
   __builtin_amdgcn_sched_barrier(0);
-  if (k0 + 1 < nks) mma_step<1, NA, NB, (NB > 1)>(f[(4 * GI + 1) % RING], chunk, sa, sb, acc);
+  if (k0 + 1 < nks) mma_step<1, NA, NB, FP6>(f[(4 * GI + 1) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
   load_w<NT>(f[(4 * GI + RING + 1) % RING], aq, min(k0 + RING + 1, last));
   __builtin_amdgcn_sched_barrier(0);
-  if (k0 + 2 < nks) mma_step<2, NA, NB, (NB > 1)>(f[(4 * GI + 2) % RING], chunk, sa, sb, acc);
+  if (k0 + 2 < nks) mma_step<2, NA, NB, FP6>(f[(4 * GI + 2) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
   load_w<NT>(f[(4 * GI + RING + 2) % RING], aq, min(k0 + RING + 2, last));
   __builtin_amdgcn_sched_barrier(0);
-  if (k0 + 3 < nks) mma_step<3, NA, NB, (NB > 1)>(f[(4 * GI + 3) % RING], chunk, sa, sb, acc);
+  if (k0 + 3 < nks) mma_step<3, NA, NB, FP6>(f[(4 * GI + 3) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
   stage.store(lds + ((sg + 1) & 1) * kBuf);
   __syncthreads();
@@ -260,13 +260,13 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
 // sched_barrier(0) points keep their issue order, so each wait on the
 // in-order vector-memory counter covers only what is about to be used.
 // RING = 8 needs the group count to be even.
-template <int RING, int NA, int THREADS, int NB, bool NT>
+template <int RING, int NA, int THREADS, int NB, bool NT, bool FP6>
 __device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[NA], const uint8_t* const (&brow_q)[NB],
                                          const uint8_t* const (&brow_s)[ChunkStage<THREADS, NB>::kScales], int nks,
                                          v4f (&acc)[NA][NB], uint8_t* lds) {
   static_assert(RING == 4 || RING == 8, "ring of 1 or 2 groups");
   const int n_sg = (nks + 3) / 4, last = nks - 1;
-  ChunkStage<THREADS, NB, (NB > 1)> stage;
+  ChunkStage<THREADS, NB, FP6> stage;
   WFrag<NA> f[RING];
   uint32_t sa[NA], sa_n[NA];
   stage.load(brow_q, brow_s, 0, nks, n_sg);
@@ -276,9 +276,9 @@ __device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[
   stage.store(lds);
   __syncthreads();
   for (int sg = 0; sg < n_sg; sg += RING / 4) {
-    k_group<0, RING, NA, THREADS, NB, NT>(f, stage, sa, sa_n, aq, as, brow_q, brow_s, sg, nks, n_sg, acc, lds);
+    k_group<0, RING, NA, THREADS, NB, NT, FP6>(f, stage, sa, sa_n, aq, as, brow_q, brow_s, sg, nks, n_sg, acc, lds);
     if (RING == 8)
-      k_group<1, RING, NA, THREADS, NB, NT>(f, stage, sa, sa_n, aq, as, brow_q, brow_s, sg + 1, nks, n_sg, acc, lds);
+      k_group<1, RING, NA, THREADS, NB, NT, FP6>(f, stage, sa, sa_n, aq, as, brow_q, brow_s, sg + 1, nks, n_sg, acc, lds);
   }
 }
 
@@ -381,7 +381,7 @@ __device__ __forceinline__ void write_h_fp6(const ExpertArgs& a, const Group g, 
 
 // One work unit: features [fu0, fu0 + WAVES*16*TPM) of gate and up for the
 // rows of group g.
-template <int TPM, int WAVES, int NB, int RING, bool NT>
+template <int TPM, int WAVES, int NB, int RING, bool NT, bool FP6>
 __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
   constexpr int NA = 2 * TPM, kFeatWave = 16 * TPM, kThreads = 64 * WAVES;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -413,9 +413,9 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
   if (RING == 8 && (nks % 8) == 0)
-    mainloop<8, NA, kThreads, NB, NT>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<8, NA, kThreads, NB, NT, FP6>(aq, as, brow_q, brow_s, nks, acc, lds);
   else
-    mainloop<4, NA, kThreads, NB, NT>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<4, NA, kThreads, NB, NT, FP6>(aq, as, brow_q, brow_s, nks, acc, lds);
 
   const int n_sg_h = (R / 128 + 3) / 4;
   const float L = a.limit;
@@ -442,7 +442,7 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[j]));
     amax = shfl_xor_max<16>(amax);
     amax = shfl_xor_max<32>(amax);
-    if constexpr (NB > 1) {
+    if constexpr (FP6) {
       write_h_fp6(a, g, c, col, grp, blk_h, n_sg_h, h, amax);
       continue;
     }
@@ -487,7 +487,7 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
   }
 }
 
-template <int TPM, int WAVES, int NB, int RING, bool NT>
+template <int TPM, int WAVES, int NB, int RING, bool NT, bool FP6>
 __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * TPM;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
@@ -500,11 +500,11 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
   const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
   if constexpr (TPM >= 4) {
     if (is_half) {
-      gateup_unit<TPM / 2, WAVES, NB, RING, NT>(a, g, fu0, lds);
+      gateup_unit<TPM / 2, WAVES, NB, RING, NT, FP6>(a, g, fu0, lds);
       return;
     }
   }
-  gateup_unit<TPM, WAVES, NB, RING, NT>(a, g, fu0, lds);
+  gateup_unit<TPM, WAVES, NB, RING, NT, FP6>(a, g, fu0, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -513,7 +513,7 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
 // WAVES waves takes NA 16-row tiles: 16*NA features per wave, 16*NA*WAVES per
 // unit.
 
-template <int NA, int WAVES, int NB, int RING, bool NT>
+template <int NA, int WAVES, int NB, int RING, bool NT, bool FP6>
 __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
   constexpr int kFeatWave = 16 * NA, kThreads = 64 * WAVES;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -541,9 +541,9 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
   if (RING == 8 && (nks % 8) == 0)
-    mainloop<8, NA, kThreads, NB, NT>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<8, NA, kThreads, NB, NT, FP6>(aq, as, brow_q, brow_s, nks, acc, lds);
   else
-    mainloop<4, NA, kThreads, NB, NT>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<4, NA, kThreads, NB, NT, FP6>(aq, as, brow_q, brow_s, nks, acc, lds);
 #pragma unroll
   for (int c = 0; c < NB; ++c)
     if (16 * c + col < g.cnt) {
@@ -553,7 +553,7 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
     }
 }
 
-template <int NA, int WAVES, int NB, int RING, bool NT>
+template <int NA, int WAVES, int NB, int RING, bool NT, bool FP6>
 __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * NA;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
@@ -566,11 +566,11 @@ __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
   if constexpr (NA >= 2) {
     if (is_half) {
-      down_unit<NA / 2, WAVES, NB, RING, NT>(a, g, fu0, lds);
+      down_unit<NA / 2, WAVES, NB, RING, NT, FP6>(a, g, fu0, lds);
       return;
     }
   }
-  down_unit<NA, WAVES, NB, RING, NT>(a, g, fu0, lds);
+  down_unit<NA, WAVES, NB, RING, NT, FP6>(a, g, fu0, lds);
 }
 
 // Enough workgroups for every unit to be taken in halves (see xcd_unit_split).
@@ -581,32 +581,30 @@ static unsigned unit_grid(int max_groups, int n_fb) {
   return (unsigned)(kXcds * per);
 }
 
-// The widest work unit that divides the output width: wider units stage each
-// activation chunk for more weight bytes (less activation traffic per weight
-// byte).  For gate/up, 8-wave units halve that traffic again once the batch
-// has enough pairs (kWideUnitPairs) to give every CU several of them.
-constexpr int kWideUnitPairs = 1024;
+// Narrow (16-row) units: the widest unit that divides the output width;
+// wider units stage each activation chunk for more weight bytes (less
+// activation traffic per weight byte).
 
 // Dynamic LDS of one kernel instantiation: two chunk buffers of NB column
 // tiles (above 64 KB the per-device limit is raised on first use).
-template <int TPM, int WAVES, int NB, bool NT = false, int RING = kRing>
+template <int TPM, int WAVES, int NB, bool NT = false, bool FP6 = false, int RING = kRing>
 static hipError_t gateup_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
   static std::atomic<uint64_t> attr{0};
   const size_t lds = 2 * NB * (size_t)kChunkBytes;
-  hipError_t err = ensure_dynamic_lds(gateup_kernel<TPM, WAVES, NB, RING, NT>, lds, attr);
+  hipError_t err = ensure_dynamic_lds(gateup_kernel<TPM, WAVES, NB, RING, NT, FP6>, lds, attr);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((gateup_kernel<TPM, WAVES, NB, RING, NT>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
+  hipLaunchKernelGGL((gateup_kernel<TPM, WAVES, NB, RING, NT, FP6>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
                      dim3(64 * WAVES), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int NA, int WAVES, int NB, bool NT = false, int RING = kRing>
+template <int NA, int WAVES, int NB, bool NT = false, bool FP6 = false, int RING = kRing>
 static hipError_t down_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
   static std::atomic<uint64_t> attr{0};
   const size_t lds = 2 * NB * (size_t)kChunkBytes;
-  hipError_t err = ensure_dynamic_lds(down_kernel<NA, WAVES, NB, RING, NT>, lds, attr);
+  hipError_t err = ensure_dynamic_lds(down_kernel<NA, WAVES, NB, RING, NT, FP6>, lds, attr);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((down_kernel<NA, WAVES, NB, RING, NT>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
+  hipLaunchKernelGGL((down_kernel<NA, WAVES, NB, RING, NT, FP6>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
                      dim3(64 * WAVES), lds, stream, a);
   return hipGetLastError();
 }
@@ -617,40 +615,39 @@ static hipError_t down_launch(const ExpertArgs& a, int max_groups, hipStream_t s
 // measured slightly slower (more activation staging per weight byte).
 constexpr int kSmallTailUnits = 64;
 
-// Tall batches (a.tall, see use_tall_units: prefill-like, many routed rows
-// per expert) use units of up to 64 rows (4 column tiles) from the 64-row work
-// list: each weight fragment then feeds 4x as many MFMAs.  Their activations
-// (x and h) are the two-term FP6 split, whose MFMA runs at twice the FP8 rate.
-
-hipError_t launch_gateup(const ExpertArgs& a0, int max_groups, int max_tall_groups, hipStream_t stream) {
+// Work units by the rows of the work list (unit_rows):
+//  - 64 (tall, prefill-like): 4 column tiles per unit, so each weight fragment
+//    feeds 4x as many MFMAs, on the two-term FP6 activation split (twice the
+//    FP8 MFMA rate);
+//  - 32 (medium, e.g. 512-row verify batches): 2 column tiles; nearly every
+//    expert is one group, so its weights are read once and stream with
+//    non-temporal loads;
+//  - 16 (small batches): one column tile, non-temporal weight loads and tail
+//    halves; 16-row lists of larger batches (widths the wider units do not
+//    divide) use the widest unit that fits.
+hipError_t launch_gateup(const ExpertArgs& a0, int max_groups, hipStream_t stream) {
   ExpertArgs a = a0;
-  a.tail_units = a.P < kWideUnitPairs ? kSmallTailUnits : 0;
-  if (a.tall) {
-    a.groups = a.tall_groups;
-    a.n_groups = a.n_tall_groups;
-    a.tail_units = 0;
-    return gateup_launch<2, 8, 4>(a, max_tall_groups, stream);
-  }
-  if (a.P >= kWideUnitPairs && a.R % 512 == 0) return gateup_launch<4, 8, 1>(a, max_groups, stream);
-  if (a.P < kWideUnitPairs) {  // small batch: every weight byte is read once, non-temporal loads
+  a.tail_units = 0;
+  if (a.rows == kTallGroupRows) return gateup_launch<2, 8, 4, false, true>(a, max_groups, stream);
+  if (a.rows == kMediumGroupRows) return gateup_launch<2, 8, 2, true>(a, max_groups, stream);
+  if (a.P < kWideUnitPairs) {
+    a.tail_units = kSmallTailUnits;
     if (a.R % 256 == 0) return gateup_launch<4, 4, 1, true>(a, max_groups, stream);
     return gateup_launch<2, 4, 1, true>(a, max_groups, stream);
   }
+  if (a.R % 512 == 0) return gateup_launch<4, 8, 1>(a, max_groups, stream);
   if (a.R % 256 == 0) return gateup_launch<4, 4, 1>(a, max_groups, stream);
   return gateup_launch<2, 4, 1>(a, max_groups, stream);
 }
 
 // (8-wave down units measured slower with 16-row units: those keep 4 waves.)
-hipError_t launch_down(const ExpertArgs& a0, int max_groups, int max_tall_groups, hipStream_t stream) {
+hipError_t launch_down(const ExpertArgs& a0, int max_groups, hipStream_t stream) {
   ExpertArgs a = a0;
-  a.tail_units = a.P < kWideUnitPairs ? kSmallTailUnits : 0;
-  if (a.tall) {
-    a.groups = a.tall_groups;
-    a.n_groups = a.n_tall_groups;
-    a.tail_units = 0;
-    return down_launch<4, 8, 4>(a, max_tall_groups, stream);
-  }
-  if (a.P < kWideUnitPairs) {  // small batch: every weight byte is read once, non-temporal loads
+  a.tail_units = 0;
+  if (a.rows == kTallGroupRows) return down_launch<4, 8, 4, false, true>(a, max_groups, stream);
+  if (a.rows == kMediumGroupRows) return down_launch<4, 8, 2, true>(a, max_groups, stream);
+  if (a.P < kWideUnitPairs) {
+    a.tail_units = kSmallTailUnits;
     if (a.R % kDownUnitMax == 0) return down_launch<kDownUnitMax / 64, 4, 1, true>(a, max_groups, stream);
     if (a.R % 256 == 0) return down_launch<4, 4, 1, true>(a, max_groups, stream);
     return down_launch<2, 4, 1, true>(a, max_groups, stream);

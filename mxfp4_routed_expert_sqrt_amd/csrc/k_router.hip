@@ -316,7 +316,7 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
 //     over segments of rows, a scan over the segments, then a second pass
 //     that overwrites each row with its exclusive base.  The counts, their
 //     exclusive scan (offsets), the scatter of perm/inv and the work list of
-//     the grouped GEMMs (groups of <= 16 rows of one expert, then the shared
+//     the grouped GEMMs (groups of <= 16, 32 or 64 rows of one expert, then the shared
 //     expert's rows) follow.
 // Histogram rows are E rounded up to a multiple of 4 ints wide, so both scan
 // passes move 16-byte columns.
@@ -336,16 +336,15 @@ __device__ __forceinline__ int wave_match_rank(int e, bool act, int lane, bool* 
   return __popcll(peers & lt_mask);
 }
 
-// Work list of groups of <= ROWS rows (ceil(count/ROWS) per expert in expert
+// Work list of groups of <= rows rows (ceil(count/rows) per expert in expert
 // order, then the shared expert's rows) once counts and offsets (in LDS) are
 // final.
-template <int ROWS>
-__device__ __forceinline__ void write_groups(const int32_t* s_cnt, const int32_t* s_off, int n_rows, int P, int E,
+__device__ __forceinline__ void write_groups(int rows, const int32_t* s_cnt, const int32_t* s_off, int n_rows, int P, int E,
                                              int has_shared, Group* __restrict__ groups,
                                              int32_t* __restrict__ n_groups, int32_t* wave_tot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = (tid < E) ? s_cnt[tid] : 0;
-  const int ng = (c + ROWS - 1) / ROWS;
+  const int ng = (c + rows - 1) / rows;
   int incl = ng;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -365,18 +364,18 @@ __device__ __forceinline__ void write_groups(const int32_t* s_cnt, const int32_t
     for (int g = 0; g < ng; ++g) {
       Group gr;
       gr.e = tid;
-      gr.p0 = p0 + g * ROWS;
-      gr.cnt = min(ROWS, c - g * ROWS);
+      gr.p0 = p0 + g * rows;
+      gr.cnt = min(rows, c - g * rows);
       gr.pad = 0;
       groups[g0 + g] = gr;
     }
   }
-  const int nsh = has_shared ? (n_rows + ROWS - 1) / ROWS : 0;
+  const int nsh = has_shared ? (n_rows + rows - 1) / rows : 0;
   for (int g = tid; g < nsh; g += kRouteThreads) {
     Group gr;
     gr.e = E;
-    gr.p0 = P + g * ROWS;
-    gr.cnt = min(ROWS, n_rows - g * ROWS);
+    gr.p0 = P + g * rows;
+    gr.cnt = min(rows, n_rows - g * rows);
     gr.pad = 0;
     groups[total + g] = gr;
   }
@@ -391,9 +390,8 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
     const float* __restrict__ z, int n_split, const float* __restrict__ bias, int n_rows, int E, int k, int routing, const int32_t* __restrict__ token_ids,
     const int32_t* __restrict__ tid2eid, int64_t vocab, int32_t* __restrict__ idx, float* __restrict__ gates,
     int has_shared, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv, Group* __restrict__ groups, int32_t* __restrict__ n_groups,
-    Group* __restrict__ tall_groups, int32_t* __restrict__ n_tall_groups, int32_t* hist, int32_t* done,
-    int scatter_here) {
+    int32_t* __restrict__ inv, int group_rows, Group* __restrict__ groups, int32_t* __restrict__ n_groups,
+    int32_t* hist, int32_t* done, int scatter_here) {
   extern __shared__ float s_z[];  // [16][E] logits of the workgroup's rows
   __shared__ int32_t s_sel[kRouteWaves * kMaxTopK];
   __shared__ int32_t s_a[kMaxExperts];      // step 1: histogram; step 2: counts
@@ -572,9 +570,7 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
     }
   }
   __syncthreads();  // wave_tot reuse
-  write_groups<kGroupRows>(s_a, s_off, n_rows, P, E, has_shared, groups, n_groups, wave_tot);
-  __syncthreads();
-  write_groups<kTallGroupRows>(s_a, s_off, n_rows, P, E, has_shared, tall_groups, n_tall_groups, wave_tot);
+  write_groups(group_rows, s_a, s_off, n_rows, P, E, has_shared, groups, n_groups, wave_tot);
 }
 
 // Scatter of perm/inv, one pair per thread (bases and offsets come from the
@@ -599,9 +595,8 @@ constexpr int kScatterInBlockMax = 8 * kRouteThreads;
 
 hipError_t launch_select_route(const float* z, const float* bias, int d, int n_rows, int E, int k, int routing, const int32_t* token_ids,
                                const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, int has_shared,
-                               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, Group* groups,
-                               int32_t* n_groups, Group* tall_groups, int32_t* n_tall_groups, int32_t* hist,
-                               int32_t* done, hipStream_t stream) {
+                               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, int group_rows,
+                               Group* groups, int32_t* n_groups, int32_t* hist, int32_t* done, hipStream_t stream) {
   if (E > kMaxExperts || k > kMaxTopK) return hipErrorInvalidValue;
   static std::atomic<uint64_t> attr{0};  // dynamic LDS up to 64 KB (E = 1024) plus the static part
   {
@@ -613,7 +608,7 @@ hipError_t launch_select_route(const float* z, const float* bias, int d, int n_r
   const size_t lds = sizeof(float) * kRouteWaves * E;
   hipLaunchKernelGGL(select_route_kernel, dim3((unsigned)route_workgroups(n_rows)), dim3(kRouteThreads), lds, stream,
                      z, logits_splits(n_rows, E, d), bias, n_rows, E, k, routing, token_ids, tid2eid, vocab, idx, gates, has_shared, counts, offsets,
-                     perm, inv, groups, n_groups, tall_groups, n_tall_groups, hist, done, here);
+                     perm, inv, group_rows, groups, n_groups, hist, done, here);
   if (!here) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

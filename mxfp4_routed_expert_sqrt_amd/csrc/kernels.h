@@ -47,12 +47,21 @@ hipError_t launch_pack_mxfp4(const uint8_t* q, const uint8_t* s, int n_mat, int 
 hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d, int E, float* z_part, uint8_t* xq,
                            uint8_t* xs, int32_t* done, bool fp6, hipStream_t stream);
 
-// Batches with at least 32 routed rows per expert on average (prefill-like)
-// run the expert GEMMs as tall work units (up to 64 rows of one expert) on
-// activations split into two FP6 terms; both GEMMs need their tall widths
-// (gate/up I % 256, down d % 512).
-inline bool use_tall_units(int n_pairs, int E, int d, int I) {
-  return n_pairs >= 32 * E && I % 256 == 0 && d % 512 == 0;
+// Rows of one work group (and work unit) of the expert GEMMs for a batch of
+// n_pairs routed pairs:
+//  - 64 (tall units, activations split into two FP6 terms) once the batch has
+//    at least 32 routed rows per expert on average (prefill-like);
+//  - 32 (medium units, FP8 terms) from kWideUnitPairs pairs on: nearly every
+//    expert then fits one group, so its weights are read once;
+//  - 16 otherwise (small batches, or widths the wider units do not divide).
+// The wider units need gate/up I % 256 and down d % 512.
+constexpr int kWideUnitPairs = 1024;
+
+inline int unit_rows(int n_pairs, int E, int d, int I) {
+  if (I % 256 != 0 || d % 512 != 0) return kGroupRows;
+  if (n_pairs >= 32 * E) return kTallGroupRows;
+  if (n_pairs >= kWideUnitPairs) return kMediumGroupRows;
+  return kGroupRows;
 }
 
 // Split-K factor of the router logits: enough 64x64 tiles for >= 256
@@ -71,9 +80,8 @@ __host__ __device__ inline size_t logits_partial_stride(int n_rows, int E) {
 
 hipError_t launch_select_route(const float* z, const float* bias, int d, int n_rows, int E, int k, int routing, const int32_t* token_ids,
                                const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, int has_shared,
-                               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, Group* groups,
-                               int32_t* n_groups, Group* tall_groups, int32_t* n_tall_groups, int32_t* hist,
-                               int32_t* done, hipStream_t stream);
+                               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, int group_rows,
+                               Group* groups, int32_t* n_groups, int32_t* hist, int32_t* done, hipStream_t stream);
 
 // Selection workgroups (16 rows each) and the size of their per-expert
 // histogram rows (E rounded up to 4 int32).
@@ -89,10 +97,8 @@ struct ExpertArgs {
   const uint8_t* aq;                     // activation split bytes (x for gate/up, h for down)
   const uint8_t* as;                     // activation split scales
   const int32_t* perm;                   // expert-major pair -> r*k + j
-  const Group* groups;                   // work list of <= 16-row groups
+  const Group* groups;                   // work list of <= rows-row groups
   const int32_t* n_groups;
-  const Group* tall_groups;              // work list of <= 64-row groups
-  const int32_t* n_tall_groups;
   int K, R;                              // contraction length, rows of each weight matrix
   int E, k, P;                           // experts, top-k, routed pairs (N*k)
   float limit;                           // swiglu limit (<= 0: none)
@@ -100,11 +106,12 @@ struct ExpertArgs {
   uint8_t* hs;                           // gate/up output: split h scales
   float* y;                              // down output [pairs][R]
   int tail_units;                        // units per XCD processed as two halves at the end
-  int tall;                              // tall work units on FP6 activations (use_tall_units)
+  int rows;                              // rows of the work list's groups (unit_rows); 64: FP6 activations
 };
 
-hipError_t launch_gateup(const ExpertArgs& a, int max_groups, int max_tall_groups, hipStream_t stream);
-hipError_t launch_down(const ExpertArgs& a, int max_groups, int max_tall_groups, hipStream_t stream);
+// max_groups: capacity of the work list (max_work_groups for a.rows)
+hipError_t launch_gateup(const ExpertArgs& a, int max_groups, hipStream_t stream);
+hipError_t launch_down(const ExpertArgs& a, int max_groups, hipStream_t stream);
 
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* gates, int n_rows, int d, int k,
                           int P, int has_shared, float route_scale, uint16_t* out, hipStream_t stream);

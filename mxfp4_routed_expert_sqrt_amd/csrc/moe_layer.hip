@@ -12,8 +12,8 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, tall_groups, n_tall_groups, hist, done, xq, xs, hq, hs, y, total;
-  int max_groups, max_tall_groups;
+  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, hist, done, xq, xs, hq, hs, y, total;
+  int max_groups;  // capacity of the work list: groups of kGroupRows rows, the most there can be
 };
 
 // Workspace carve-up; every region starts on a 256-byte boundary.
@@ -21,8 +21,7 @@ Layout make_layout(const moe_config_t& c, int n) {
   Layout L;
   const size_t N = (size_t)n, E = (size_t)c.n_experts, k = (size_t)c.top_k;
   const size_t P = N * k, Ptot = P + (c.has_shared ? N : 0);
-  L.max_groups = max_work_groups(n, c.top_k, c.n_experts, c.has_shared);
-  L.max_tall_groups = max_work_groups(n, c.top_k, c.n_experts, c.has_shared, kTallGroupRows);
+  L.max_groups = max_work_groups(n, c.top_k, c.n_experts, c.has_shared, kGroupRows);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -38,8 +37,6 @@ Layout make_layout(const moe_config_t& c, int n) {
   L.inv = take(P * 4);
   L.groups = take((size_t)L.max_groups * sizeof(Group));
   L.n_groups = take(4);
-  L.tall_groups = take((size_t)L.max_tall_groups * sizeof(Group));
-  L.n_tall_groups = take(4);
   L.hist = take(route_hist_bytes(n, c.n_experts));
   L.done = take(4);
   L.xq = take(N * split_q_row_bytes(c.d_model));
@@ -172,8 +169,6 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   int32_t* inv = a.inv ? a.inv : (int32_t*)(ws + L.inv);
   Group* groups = (Group*)(ws + L.groups);
   int32_t* n_groups = (int32_t*)(ws + L.n_groups);
-  Group* tall_groups = (Group*)(ws + L.tall_groups);
-  int32_t* n_tall_groups = (int32_t*)(ws + L.n_tall_groups);
   uint8_t *xq = ws + L.xq, *xs = ws + L.xs, *hq = ws + L.hq, *hs = ws + L.hs;
   float* y = (float*)(ws + L.y);
   const int P = N * k;
@@ -186,14 +181,15 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
            hipEventRecord((hipEvent_t)a.stage_events[i], stream) == hipSuccess;
   };
   if (!mark(0)) return MOE_ERR_HIP;
-  const bool tall = use_tall_units(P, E, d, I);
-  if ((err = launch_prologue((const uint16_t*)a.x, a.router_w, N, d, E, z, xq, xs, done, tall, stream)) !=
+  const int rows = unit_rows(P, E, d, I);
+  const int max_groups = max_work_groups(N, k, E, c.has_shared, rows);
+  if ((err = launch_prologue((const uint16_t*)a.x, a.router_w, N, d, E, z, xq, xs, done, rows == kTallGroupRows,
+                             stream)) !=
       hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
   if ((err = launch_select_route(z, a.router_bias, d, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, c.has_shared,
-                                 counts, offsets, perm, inv, groups, n_groups, tall_groups, n_tall_groups, hist, done,
-                                 stream)) != hipSuccess)
+                                 counts, offsets, perm, inv, rows, groups, n_groups, hist, done, stream)) != hipSuccess)
     return MOE_ERR_HIP;
 
   ExpertArgs ga;
@@ -211,9 +207,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   ga.perm = perm;
   ga.groups = groups;
   ga.n_groups = n_groups;
-  ga.tall_groups = tall_groups;
-  ga.n_tall_groups = n_tall_groups;
-  ga.tall = tall ? 1 : 0;
+  ga.rows = rows;
   ga.K = d;
   ga.R = I;
   ga.E = E;
@@ -223,7 +217,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   ga.hq = hq;
   ga.hs = hs;
   if (!mark(2)) return MOE_ERR_HIP;
-  if ((err = launch_gateup(ga, L.max_groups, L.max_tall_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
+  if ((err = launch_gateup(ga, max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
 
   ExpertArgs da = ga;
   da.q0 = (const uint8_t*)a.w.down_q;
@@ -239,7 +233,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   da.hq = da.hs = nullptr;
   da.y = y;
   if (!mark(3)) return MOE_ERR_HIP;
-  if ((err = launch_down(da, L.max_groups, L.max_tall_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
+  if ((err = launch_down(da, max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
   if (!mark(4)) return MOE_ERR_HIP;
 
   if ((err = launch_combine(y, inv, gates, N, d, k, P, c.has_shared, c.route_scale, (uint16_t*)a.out, stream)) !=

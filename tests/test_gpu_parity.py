@@ -146,6 +146,9 @@ EDGE = {
     "e1000_k4": MoEShape("edge_e1000_k4", 64, 128, 1000, 4, 128, "topk", "edge1000"),
     # >= 32 routed rows per expert: the 64-row work units (4 column tiles) of both GEMMs, ragged groups
     "tall": MoEShape("edge_tall", 611, 512, 8, 4, 256, "topk", "edge_tall"),
+    # >= 1024 routed pairs but < 32 per expert: the 32-row work units (2 column tiles); the Zipf
+    # bias gives the hottest experts several groups and leaves others with a few rows
+    "medium": MoEShape("edge_medium", 300, 512, 64, 4, 256, "topk", "edge_medium", bias="zipf"),
 }
 
 

@@ -21,6 +21,7 @@ from tests.inputs import workload  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 TALL = MoEShape("edge_tall", 611, 512, 8, 4, 256, "topk", "edge_tall")
+MEDIUM = MoEShape("edge_medium", 300, 512, 64, 4, 256, "topk", "edge_medium", bias="zipf")
 
 
 def _layer(wl):
@@ -55,9 +56,9 @@ def _same(a, b, label):
         assert np.array_equal(a[key], b[key]), f"{label}: {key} differs"
 
 
-@pytest.mark.parametrize("shape", [TALL, SHAPES["hash2048"]], ids=["tall", "hash2048-scatter"])
+@pytest.mark.parametrize("shape", [TALL, MEDIUM, SHAPES["hash2048"]], ids=["tall", "medium", "hash2048-scatter"])
 def test_poisoned_workspace_repeatable(shape):
-    # tall: the 64-row work units; hash2048: 12288 pairs, so the separate scatter launch
+    # tall, medium: the 64- and 32-row work units; hash2048: 12288 pairs, so the separate scatter launch
     wl = workload(shape)
     layer = _layer(wl)
     x, tok, tab = _inputs(wl)
