@@ -181,7 +181,8 @@ hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d,
 // softplus(z) = max(z,0) + log1p(exp(-|z|)).  Top-k mode takes the k largest
 // scores (equal scores: lower expert id first) by k rounds of a wave argmax;
 // hash mode takes tid2eid[token_ids[r]].  Selected ids are written ascending
-// with gates = s / sum(s).
+// with gates = s / sum(s).  s increases strictly with z, so the argmax runs
+// on the logits and only the k selected scores are computed.
 
 __device__ __forceinline__ float router_score(float zv) {
   return sqrtf(fmaxf(zv, 0.f) + log1pf(expf(-fabsf(zv))));
@@ -190,37 +191,51 @@ __device__ __forceinline__ float router_score(float zv) {
 constexpr int kMaxExpertsPerLane = 16;  // E <= 1024
 constexpr int kMaxTopK = 8;
 
-// Selection keys: score bits in the high word (scores are >= +0, so their
-// bit patterns order like the values; a NaN score sorts above every number)
-// and the complemented expert id in the low word, so that of two equal scores
-// the lower id has the larger key.  Every real candidate has a key > 0; a
-// taken or absent candidate is 0.
-__device__ __forceinline__ uint64_t sel_key(float score, int e) {
-  return ((uint64_t)(__float_as_uint(score) & 0x7fffffffu) << 32) | (uint32_t)~e;  // -0 as +0
+// Order-preserving code of a logit: larger z, larger code; -0 as +0 (equal
+// scores); NaN (a NaN score) above every number.  Never 0.
+__device__ __forceinline__ uint32_t logit_code(float z) {
+  if (z != z) return 0xFFFFFFFFu;
+  uint32_t u = __float_as_uint(z);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// max(v, v from the lane named by the DPP control); rows outside kRowMask keep v.
+__device__ __forceinline__ float logit_of_code(uint32_t c) {
+  return __uint_as_float((c & 0x80000000u) ? (c & 0x7fffffffu) : ~c);
+}
+
+// Selection keys: the logit code in the high word and the complemented expert
+// id in the low word, so that of two equal logits the lower id has the larger
+// key.  Every real candidate has a key > 0; a taken or absent candidate is 0.
+__device__ __forceinline__ uint64_t sel_key(float z, int e) {
+  return ((uint64_t)logit_code(z) << 32) | (uint32_t)~e;
+}
+
+// Largest value of the wave, uniform: max with the value of another lane by
+// DPP within rows of 16 lanes (xor 1, xor 2, rotate 4, rotate 8), then row 0
+// -> 1 and 2 -> 3 (row_bcast:15) and rows 0-1 -> 2-3 (row_bcast:31), so lane
+// 63 ends with the maximum.
 template <int kCtrl, int kRowMask>
-__device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, kCtrl, kRowMask, 0xF, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, kCtrl, kRowMask, 0xF, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtrl, kRowMask, 0xF, false);
   return o > v ? o : v;
 }
 
-// Largest key of the wave, uniform: DPP within rows of 16 lanes (xor 1,
-// xor 2, rotate 4, rotate 8), then row 0 -> 1 and 2 -> 3 (row_bcast:15) and
-// rows 0-1 -> 2-3 (row_bcast:31), so lane 63 ends with the maximum.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = dpp_max<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
   v = dpp_max<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
   v = dpp_max<0x124, 0xF>(v);  // row_ror:4
   v = dpp_max<0x128, 0xF>(v);  // row_ror:8
   v = dpp_max<0x142, 0xA>(v);  // row_bcast:15
   v = dpp_max<0x143, 0xC>(v);  // row_bcast:31
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Largest 64-bit key of the wave: the largest high word, then the largest
+// low word among the lanes holding it.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
   return ((uint64_t)hi << 32) | lo;
 }
 
@@ -243,13 +258,13 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
                                            int32_t* sel_lds) {
   const int lane = threadIdx.x & 63;
   int sel[kMaxTopK];
-  float sv[kMaxTopK];
+  float zsel[kMaxTopK];
   if (routing == 0) {
     uint64_t key[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = c * 64 + lane;
-      key[c] = e < E ? sel_key(router_score(zr[e]), e) : 0ull;
+      key[c] = e < E ? sel_key(zr[e], e) : 0ull;
     }
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
@@ -261,7 +276,7 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
 #pragma unroll
         for (int c = 0; c < NC; ++c) key[c] = key[c] == m ? 0ull : key[c];
         sel[j] = (int)~(uint32_t)m;
-        sv[j] = __uint_as_float((uint32_t)(m >> 32));
+        zsel[j] = logit_of_code((uint32_t)(m >> 32));
       }
     }
   } else {
@@ -274,22 +289,24 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j < k) {
         sel[j] = min(max(row[j], 0), E - 1);
-        sv[j] = router_score(zr[sel[j]]);
+        zsel[j] = zr[sel[j]];
       }
     }
   }
-  float sum = 0.f;
+  // lane j < k scores the j-th selection; the sum runs in selection order
   int my_id = 0;
-  float my_sv = 0.f;
+  float my_z = 0.f;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j)
-    if (j < k) {
-      sum += sv[j];
-      if (lane == j) {
-        my_id = sel[j];
-        my_sv = sv[j];
-      }
+    if (j < k && lane == j) {
+      my_id = sel[j];
+      my_z = zsel[j];
     }
+  const float my_sv = router_score(my_z);
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k) sum += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_sv), j));
   int rank = 0;
 #pragma unroll
   for (int i = 0; i < kMaxTopK; ++i)
