@@ -45,10 +45,15 @@ SHAPES = {
     "zipf2048": MoEShape("zipf2048", 2048, 4096, 256, 6, 2048, "topk", "v4layer", bias="zipf"),
     # hash-routed: experts from a seeded [129280][6] table, uniform token ids
     "hash2048": MoEShape("hash2048", 2048, 4096, 256, 6, 2048, "hash", "v4layer"),
+    # DSpark drafter MoE slab: 64 requests x one 7-row draft query block
+    "draft448": MoEShape("draft448", 448, 4096, 256, 6, 2048, "topk", "v4layer"),
+    # the same slab at ds4's draft block size of 5 rows per request
+    "draft320": MoEShape("draft320", 320, 4096, 256, 6, 2048, "topk", "v4layer"),
 }
 
 # Stable numeric tags for the seeded streams of each workload and weight family.
-CFG_TAG = {"tiny": 0, "verify512": 1, "decode8": 2, "prefill8192": 3, "zipf2048": 4, "hash2048": 5}
+CFG_TAG = {"tiny": 0, "verify512": 1, "decode8": 2, "prefill8192": 3, "zipf2048": 4, "hash2048": 5,
+           "draft448": 6, "draft320": 7}
 SET_TAG = {"tiny": 100, "v4layer": 101}
 
 # Parameters of the synthetic distributions (standard deviations).

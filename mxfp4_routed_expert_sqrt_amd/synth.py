@@ -15,6 +15,8 @@ Recipe (seed 0 unless stated):
   uniform over the vocabulary.
 - Zipf load: per-row selection probability q_e = min(1, c * rank_e^-1.2) with
   sum q = k; ranks map to a seeded permutation of the experts.
+- with the input RMSNorm: x rows scaled by 2^u, u uniform in {-3, ..., 3}
+  (exact in bf16); norm weight 1 + N(0, 0.1) and residual N(0, 1), both bf16.
 """
 import ctypes
 import os
@@ -187,23 +189,60 @@ def zipf_targets(shape: MoEShape, s: float = 1.2, seed: int = 0) -> np.ndarray:
     return q
 
 
-def resample_rows(shape: MoEShape, accept_rows, seed: int = 0, max_tries: int = 1000, threads=None):
+def resample_rows(shape: MoEShape, accept_rows, seed: int = 0, max_tries: int = 1000, threads=None,
+                  with_index: bool = False):
     """Draw x and redraw every row that the filter rejects.
 
-    `accept_rows(x_rows) -> bool[len(x_rows)]` is called on the rows drawn in
-    each round (all rows first, then only the redrawn ones).  A rejected row r
-    moves to its next attempt (a fresh stream of the same seed), so the
-    accepted x is a function of the seed and the filter only.
-    Returns (x, attempts).
+    `accept_rows(x_rows) -> bool[len(x_rows)]` (with_index: `accept_rows(x_rows,
+    row_indices)`) is called on the rows drawn in each round (all rows first,
+    then only the redrawn ones).  A rejected row r moves to its next attempt (a
+    fresh stream of the same seed), so the accepted x is a function of the seed
+    and the filter only.  Returns (x, attempts).
     """
     attempts = np.zeros(shape.n_rows, dtype=np.int32)
     x = gen_x(shape, seed, attempts, threads)
     todo = np.arange(shape.n_rows)
     for _ in range(max_tries):
-        ok = np.asarray(accept_rows(x[todo]), dtype=bool)
+        ok = np.asarray(accept_rows(x[todo], todo) if with_index else accept_rows(x[todo]), dtype=bool)
         todo = todo[~ok]
         if todo.size == 0:
             return x, attempts
         attempts[todo] += 1
         x = gen_x(shape, seed, attempts, threads)
     raise RuntimeError(f"{shape.name}: rows still rejected after {max_tries} redraws")
+
+
+# Streams of the input-RMSNorm extras (numpy generators keyed by seed, workload and tensor).
+_TAG_ROW_EXP, _TAG_NORM_W, _TAG_RESIDUAL = 11, 12, 13
+
+
+def _rng(shape: MoEShape, seed: int, tag: int):
+    return np.random.default_rng(np.random.SeedSequence([seed, _cfg_tag(shape), tag]))
+
+
+def bf16_bits(v) -> np.ndarray:
+    """fp64/fp32 values -> bf16 bit patterns (via fp32, round to nearest even; finite inputs)."""
+    u = np.ascontiguousarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def gen_row_exponents(shape: MoEShape, seed: int = 0) -> np.ndarray:
+    """Per-row power-of-two scale exponents in [-3, 3] for the input-RMSNorm workloads."""
+    return _rng(shape, seed, _TAG_ROW_EXP).integers(-3, 4, shape.n_rows).astype(np.int32)
+
+
+def scale_rows_bf16(x_bits: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    """bf16 rows times 2^exps[r] (exact while in range)."""
+    f = (x_bits.astype(np.uint32) << 16).view(np.float32) * np.ldexp(np.float32(1), exps)[:, None].astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def gen_norm_weight(shape: MoEShape, seed: int = 0) -> np.ndarray:
+    """RMSNorm weight [d] as bf16 bits: 1 + N(0, 0.1)."""
+    return bf16_bits(1.0 + 0.1 * _rng(shape, seed, _TAG_NORM_W).standard_normal(shape.d_model))
+
+
+def gen_residual(shape: MoEShape, seed: int = 0) -> np.ndarray:
+    """Residual rows [N][d] as bf16 bits: N(0, 1)."""
+    return bf16_bits(_rng(shape, seed, _TAG_RESIDUAL).standard_normal((shape.n_rows, shape.d_model)))

@@ -28,7 +28,7 @@ def build() -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int), ("d", ctypes.c_int), ("E", ctypes.c_int), ("k", ctypes.c_int),
                 ("I", ctypes.c_int), ("routing", ctypes.c_int), ("route_scale", ctypes.c_double),
-                ("swiglu_limit", ctypes.c_double)]
+                ("swiglu_limit", ctypes.c_double), ("norm_eps", ctypes.c_float)]
 
 
 class _Inputs(ctypes.Structure):
@@ -36,7 +36,7 @@ class _Inputs(ctypes.Structure):
                 ("token_ids", ctypes.c_void_p), ("tid2eid", ctypes.c_void_p), ("vocab", ctypes.c_long)] + \
                [(n, ctypes.c_void_p) for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s",
                                               "sh_gate_q", "sh_gate_s", "sh_up_q", "sh_up_s", "sh_down_q",
-                                              "sh_down_s")]
+                                              "sh_down_s", "norm_w", "residual")]
 
 
 def _load():
@@ -49,6 +49,8 @@ def _load():
         lib.orc_e2m1.argtypes, lib.orc_e2m1.restype = [i32], dbl
         lib.orc_e8m0.argtypes, lib.orc_e8m0.restype = [i32], dbl
         lib.orc_bf16.argtypes, lib.orc_bf16.restype = [ctypes.c_uint16], dbl
+        lib.orc_f32_to_bf16.argtypes, lib.orc_f32_to_bf16.restype = [ctypes.c_float], ctypes.c_uint16
+        lib.orc_rmsnorm_bf16.argtypes = [vp, i32, i32, vp, ctypes.c_float, vp]
         lib.orc_decode_mxfp4_row.argtypes = [vp, vp, i32, vp]
         lib.orc_router_logits.argtypes = [vp, i32, i32, vp, i32, vp, vp, i32]
         lib.orc_softplus.argtypes, lib.orc_softplus.restype = [dbl], dbl
@@ -157,9 +159,24 @@ def bookkeeping(idx: np.ndarray, n_experts: int):
     return counts, offsets, perm, inv
 
 
+def rmsnorm_bf16(x_bf16: np.ndarray, g_bf16: np.ndarray, eps: float) -> np.ndarray:
+    """bf16 [N][d] -> bf16 [N][d]: RMSNorm in fp32, one rounding (orc_rmsnorm_bf16)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    g = np.ascontiguousarray(g_bf16, dtype=np.uint16)
+    N, d = x.shape
+    assert g.shape == (d,)
+    out = np.empty_like(x)
+    _load().orc_rmsnorm_bf16(_p(x), N, d, _p(g), float(eps), _p(out))
+    return out
+
+
 def forward(shape, x, router_w, experts, router_bias=None, token_ids=None, tid2eid=None, rows=None,
-            route_scale=None, swiglu_limit=None, with_shared=True, threads=None) -> dict:
+            route_scale=None, swiglu_limit=None, with_shared=True, threads=None, norm_w=None, norm_eps=1e-6,
+            residual=None) -> dict:
     """The whole layer in fp64.
+
+    norm_w: optional bf16 [d] RMSNorm weight; the layer then runs on rmsnorm_bf16(x, norm_w, norm_eps).
+    residual: optional bf16 [N][d] added to the output.
 
     experts: dict of natural-layout MXFP4 arrays gate_q/gate_s/up_q/up_s [E+1][I][...] and
     down_q/down_s [E+1][d][...]; index E is the shared expert (ignored if with_shared=False).
@@ -171,7 +188,7 @@ def forward(shape, x, router_w, experts, router_bias=None, token_ids=None, tid2e
     assert x.shape == (N, d)
     cfg = _Cfg(N, d, E, k, I, 0 if shape.routing == "topk" else 1,
                float(shape.route_scale if route_scale is None else route_scale),
-               float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit))
+               float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit), float(norm_eps))
     keep = []
 
     def P(a, dtype=None):
@@ -188,7 +205,8 @@ def forward(shape, x, router_w, experts, router_bias=None, token_ids=None, tid2e
                   P(w["down_q"][:E]), P(w["down_s"][:E]),
                   P(w["gate_q"][E]) if with_shared else None, P(w["gate_s"][E]) if with_shared else None,
                   P(w["up_q"][E]) if with_shared else None, P(w["up_s"][E]) if with_shared else None,
-                  P(w["down_q"][E]) if with_shared else None, P(w["down_s"][E]) if with_shared else None)
+                  P(w["down_q"][E]) if with_shared else None, P(w["down_s"][E]) if with_shared else None,
+                  P(norm_w, np.uint16), P(residual, np.uint16))
     rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
     n_out = N if rows_arr is None else rows_arr.shape[0]
     out = np.empty((n_out, d), dtype=np.float64)

@@ -56,6 +56,40 @@ double orc_bf16(uint16_t b) {
   return (double)f;
 }
 
+/* fp32 -> bf16 bit pattern, round to nearest even (NaN stays a quiet NaN). */
+uint16_t orc_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* RMSNorm in front of the layer (the FFN input norm, ffn_norm in the ds4
+ * issue's loader spec; RMSNorm kernels in the FaStar README, Features; "hc_pre
+ * -> rmsnorm" in the pypto DSpark point pipeline).  The pages fix neither the
+ * precision nor eps; the layer's activations are bf16, so the normalised row is
+ * computed in fp32, the precision of the kernel that takes the same rounding
+ * decision, and rounded once to bf16:
+ *   ms = (sum_i x_i^2) / d  (fp32, i ascending),  r = 1 / sqrt(ms + eps),
+ *   xn_i = bf16((x_i * r) * g_i). */
+void orc_rmsnorm_bf16(const uint16_t* x, int N, int d, const uint16_t* g, float eps, uint16_t* xn) {
+  for (long r = 0; r < N; ++r) {
+    const uint16_t* xr = x + (size_t)r * d;
+    float ss = 0.0f;
+    for (int i = 0; i < d; ++i) {
+      const float v = (float)orc_bf16(xr[i]);
+      ss = ss + v * v;
+    }
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int i = 0; i < d; ++i) {
+      const float v = (float)orc_bf16(xr[i]);
+      const float t = v * inv;
+      xn[(size_t)r * d + i] = orc_f32_to_bf16(t * (float)orc_bf16(g[i]));
+    }
+  }
+}
+
 /* One row of an MXFP4 matrix: K values, element t in byte t/2 (low nibble when
  * t is even), scale byte t/32. */
 void orc_decode_mxfp4_row(const uint8_t* q, const uint8_t* s, int K, double* out) {
@@ -312,6 +346,7 @@ typedef struct {
   int routing;          /* 0 = sqrt-softplus top-k, 1 = hash */
   double route_scale;   /* multiplies the routed sum only */
   double swiglu_limit;  /* <= 0 disables the clamp */
+  float norm_eps;       /* RMSNorm eps (used when norm_w != NULL) */
 } orc_cfg;
 
 typedef struct {
@@ -325,10 +360,14 @@ typedef struct {
   const uint8_t *gate_q, *gate_s, *up_q, *up_s, *down_q, *down_s;
   /* shared expert, same layout with one matrix; gate_q == NULL means no shared expert */
   const uint8_t *sh_gate_q, *sh_gate_s, *sh_up_q, *sh_up_s, *sh_down_q, *sh_down_s;
+  const uint16_t* norm_w;   /* bf16 [d]: the layer runs on RMSNorm(x) (orc_rmsnorm_bf16); NULL: on x */
+  const uint16_t* residual; /* bf16 [N][d] added to the output, or NULL */
 } orc_inputs;
 
 /*
- * The whole layer.  rows (may be NULL = all N rows, in order) lists the rows
+ * The whole layer: out[r] = residual[r] + MoE(x'[r]) with x' = RMSNorm(x) when
+ * norm_w is given, else x; the residual term only when residual is given.
+ * rows (may be NULL = all N rows, in order) lists the rows
  * whose outputs are computed; routing and bookkeeping always cover all N rows.
  * out: [n_out][d] fp64 for the listed rows.  z, idx, gates, margin, counts,
  * offsets, perm, inv: optional (NULL to skip) full-size outputs.
@@ -339,13 +378,20 @@ int orc_forward(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows, i
                 int32_t* offsets, int32_t* perm, int32_t* inv, int nthreads) {
   const int N = cfg->N, d = cfg->d, E = cfg->E, k = cfg->k, I = cfg->I;
   if (N == 0) return 0;
+  uint16_t* xn = NULL;
+  const uint16_t* x = in->x;
+  if (in->norm_w) {
+    xn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)N * d);
+    orc_rmsnorm_bf16(in->x, N, d, in->norm_w, cfg->norm_eps, xn);
+    x = xn;
+  }
   double* z = (double*)malloc(sizeof(double) * (size_t)N * E);
   int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)N * k);
   double* gates = (double*)malloc(sizeof(double) * (size_t)N * k);
-  orc_router_logits(in->x, N, d, in->router_w, E, in->router_bias, z, nthreads);
+  orc_router_logits(x, N, d, in->router_w, E, in->router_bias, z, nthreads);
   int rc = orc_route(z, N, E, k, cfg->routing, in->token_ids, in->tid2eid, in->vocab, idx, gates, margin_out);
   if (rc != 0) {
-    free(z); free(idx); free(gates);
+    free(z); free(idx); free(gates); free(xn);
     return rc;
   }
   if (counts || offsets || perm || inv) {
@@ -392,7 +438,7 @@ int orc_forward(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows, i
     double* xd = (double*)malloc(sizeof(double) * (size_t)n_out * d);
     for (int o = 0; o < n_out; ++o) {
       int r = rows ? rows[o] : o;
-      for (int i = 0; i < d; ++i) xd[(size_t)o * d + i] = orc_bf16(in->x[(size_t)r * d + i]);
+      for (int i = 0; i < d; ++i) xd[(size_t)o * d + i] = orc_bf16(x[(size_t)r * d + i]);
     }
     double* h = (double*)malloc(sizeof(double) * (size_t)n_pairs * I);
     double* y = (double*)malloc(sizeof(double) * (size_t)n_pairs * d);
@@ -402,7 +448,7 @@ int orc_forward(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows, i
                   E, pair_row, exp_start, xd, h, y};
     orc_parallel(ffn_gateup_item, &fc, (long)(E + 1) * I, nthreads);
     orc_parallel(ffn_down_item, &fc, (long)(E + 1) * d, nthreads);
-    /* out = y_shared + route_scale * sum_j g_j y_j, slots in ascending order */
+    /* out = y_shared + route_scale * sum_j g_j y_j (+ residual), slots in ascending order */
     for (int o = 0; o < n_out; ++o) {
       int r = rows ? rows[o] : o;
       for (int m = 0; m < d; ++m) {
@@ -410,11 +456,12 @@ int orc_forward(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows, i
         for (int j = 0; j < k; ++j)
           acc += gates[(size_t)r * k + j] * y[(size_t)pair_of[(size_t)o * slots + j] * d + m];
         double sh = has_shared ? y[(size_t)pair_of[(size_t)o * slots + k] * d + m] : 0.0;
-        out[(size_t)o * d + m] = sh + cfg->route_scale * acc;
+        double res = in->residual ? orc_bf16(in->residual[(size_t)r * d + m]) : 0.0;
+        out[(size_t)o * d + m] = res + (sh + cfg->route_scale * acc);
       }
     }
     free(exp_start); free(pair_row); free(pair_of); free(fill); free(xd); free(h); free(y);
   }
-  free(z); free(idx); free(gates);
+  free(z); free(idx); free(gates); free(xn);
   return 0;
 }

@@ -73,6 +73,35 @@ def workload(name, seed: int = 0, x_scale: float = 1.0):
                 experts=experts, attempts=attempts)
 
 
+NORM_EPS = 1e-6
+
+
+@functools.lru_cache(maxsize=None)
+def norm_workload(name, seed: int = 0):
+    """The workload with the input RMSNorm and a residual: x rows drawn as usual, scaled by
+    2^u per row (u in [-3, 3]), with the margin filter applied to RMSNorm(x); plus norm_w,
+    norm_eps and residual."""
+    base = workload(name, seed)
+    shape = base["shape"]
+    exps = synth.gen_row_exponents(shape, seed)
+    g = synth.gen_norm_weight(shape, seed)
+
+    def accept(rows, idx):
+        xn = oracle.rmsnorm_bf16(synth.scale_rows_bf16(rows, exps[idx]), g, NORM_EPS)
+        z = oracle.router_logits(xn, base["router_w"], base["bias"])
+        _, _, margin = oracle.route(z, shape.top_k)
+        return margin >= MIN_MARGIN
+
+    if shape.routing == "hash":
+        x, attempts = synth.gen_x(shape, seed), np.zeros(shape.n_rows, dtype=np.int32)
+    else:
+        x, attempts = synth.resample_rows(shape, accept, seed, with_index=True)
+    wl = dict(base)
+    wl.update(x=synth.scale_rows_bf16(x, exps), attempts=attempts, norm_w=g, norm_eps=NORM_EPS,
+              residual=synth.gen_residual(shape, seed))
+    return wl
+
+
 def _scale_bf16(x_bits, factor):
     """Multiply bf16 bit patterns by a power of two (exact while in range)."""
     f = (x_bits.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
@@ -80,5 +109,9 @@ def _scale_bf16(x_bits, factor):
 
 
 def oracle_forward(wl, rows=None, **kw):
+    if "norm_w" in wl:
+        kw.setdefault("norm_w", wl["norm_w"])
+        kw.setdefault("norm_eps", wl["norm_eps"])
+        kw.setdefault("residual", wl["residual"])
     return oracle.forward(wl["shape"], wl["x"], wl["router_w"], wl["experts"], router_bias=wl["bias"],
                           token_ids=wl["token_ids"], tid2eid=wl["tid2eid"], rows=rows, **kw)

@@ -118,7 +118,7 @@ def test_decode8_full_parity():
 # ---------------------------------------------------------------- full size
 
 @pytest.mark.parametrize("name,n_sample", [("verify512", 48), ("prefill8192", 24), ("zipf2048", 24),
-                                           ("hash2048", 24)])
+                                           ("hash2048", 24), ("draft448", 24), ("draft320", 24)])
 def test_full_size_parity(name, n_sample):
     wl = workload(name)
     gpu, *_ = run_gpu(wl)

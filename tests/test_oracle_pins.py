@@ -365,3 +365,74 @@ def test_byte_model_matches_pages():
     total_gib = g["layers"]["value"] * sh.n_experts * per_expert / 2 ** 30
     assert abs(total_gib - g["routed_expert_gib_printed"]["value"]) < 0.5
     assert abs(sh.n_experts * 3 * d * I / 1e9 - g["params_per_layer_billion_printed"]["value"]) < 0.01
+
+
+# ------------------------------------------------- input RMSNorm and residual
+
+def _bf16_f32(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def test_rmsnorm_matches_torch_rms_norm():
+    # A library routine of the same definition (fp32, its own reduction order): the bf16
+    # results agree except where the two fp32 values straddle a bf16 rounding boundary.
+    torch = pytest.importorskip("torch")
+    sh = MoEShape("n", 64, 256, 16, 2, 128, "topk", "tiny")
+    rng = np.random.default_rng(21)
+    x = synth.scale_rows_bf16(synth.bf16_bits(rng.standard_normal((64, 256))), rng.integers(-3, 4, 64))
+    g = synth.bf16_bits(1.0 + 0.1 * rng.standard_normal(256))
+    ours = oracle.rmsnorm_bf16(x, g, 1e-6)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(_bf16_f32(x)), (256,), torch.from_numpy(_bf16_f32(g)),
+                                       eps=1e-6)
+    ref_bits = synth.bf16_bits(ref.numpy())
+    diff = np.abs(ours.astype(np.int32) - ref_bits.astype(np.int32))
+    assert diff.max() <= 1 and (diff > 0).mean() < 1e-2
+    assert sh.d_model == 256
+
+
+def test_rmsnorm_closed_forms():
+    d = 128
+    g1 = synth.bf16_bits(np.ones(d))
+    # constant rows +-2^k with eps 0: x / sqrt(mean x^2) = +-1 exactly
+    for c in (0.25, 1.0, -8.0):
+        x = synth.bf16_bits(np.full((1, d), c))
+        assert np.all(_bf16_f32(oracle.rmsnorm_bf16(x, g1, 0.0)) == np.sign(c))
+    # power-of-two scaling of a row changes no bit (eps 0: every fp32 step scales exactly)
+    rng = np.random.default_rng(5)
+    x = synth.bf16_bits(rng.standard_normal((4, d)))
+    g = synth.bf16_bits(1.0 + 0.1 * rng.standard_normal(d))
+    a = oracle.rmsnorm_bf16(x, g, 0.0)
+    b = oracle.rmsnorm_bf16(synth.scale_rows_bf16(x, np.array([5, -7, 1, 3])), g, 0.0)
+    assert np.array_equal(a, b)
+    # the weight multiplies elementwise: a weight of 2 doubles every element exactly
+    g2 = synth.bf16_bits(np.full(d, 2.0))
+    assert np.array_equal(_bf16_f32(oracle.rmsnorm_bf16(x, g2, 0.0)), 2 * _bf16_f32(oracle.rmsnorm_bf16(x, g1, 0.0)))
+    # eps dominates a zero row: the output is exactly zero
+    assert np.all(_bf16_f32(oracle.rmsnorm_bf16(np.zeros((1, d), np.uint16), g, 1e-6)) == 0)
+
+
+def test_norm_forward_is_forward_on_normalised_rows_plus_residual():
+    from tests.inputs import norm_workload
+    wl = norm_workload("tiny")
+    sh = wl["shape"]
+    a = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], norm_w=wl["norm_w"], norm_eps=wl["norm_eps"],
+                       residual=wl["residual"])
+    xn = oracle.rmsnorm_bf16(wl["x"], wl["norm_w"], wl["norm_eps"])
+    b = oracle.forward(sh, xn, wl["router_w"], wl["experts"])
+    for key in ("idx", "gates", "perm", "inv", "offsets"):
+        assert np.array_equal(a[key], b[key])
+    res = _bf16_f32(wl["residual"]).astype(np.float64)
+    assert np.allclose(a["out"] - b["out"], res, rtol=0, atol=1e-12)
+    # a zero norm weight zeroes the FFN input, so only the residual is left
+    z = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], norm_w=np.zeros(sh.d_model, np.uint16),
+                       norm_eps=wl["norm_eps"], residual=wl["residual"])
+    assert np.array_equal(z["out"], res)
+
+
+def test_norm_workload_margins():
+    from tests.inputs import norm_workload
+    wl = norm_workload("tiny")
+    xn = oracle.rmsnorm_bf16(wl["x"], wl["norm_w"], wl["norm_eps"])
+    _, _, margin = oracle.route(oracle.router_logits(xn, wl["router_w"]), wl["shape"].top_k)
+    assert margin.min() >= 1e-3
+    assert len(set(synth.gen_row_exponents(wl["shape"]).tolist())) > 3
