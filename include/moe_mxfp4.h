@@ -9,6 +9,8 @@
  *   g[r][j]  = s[r][sel_j] / sum_j' s[r][sel_j']                gates, sum 1
  *   FFN_e(v) = W_down[e] (silu(min(W_gate[e] v, L)) * clamp(W_up[e] v, -L, L))
  *   out[r]   = FFN_shared(x[r]) + route_scale * sum_j g[r][j] FFN_{sel_j}(x[r])
+ * Optionally the layer first normalises its input, x <- RMSNorm(x) (norm_w),
+ * and adds a residual row to its output (residual); see moe_args_t.
  * Sources (pages on DeepSeek V4 Flash):
  *   - top-6 of 256 routed experts plus one shared expert, sqrt-softplus routing
  *     with hash layers: TensorSharp "DeepSeek V4 Flash (deepseek4)", intro and
@@ -48,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_MXFP4_VERSION 1
+#define MOE_MXFP4_VERSION 2
 
 enum {
   MOE_OK = 0,
@@ -74,6 +76,7 @@ typedef struct moe_config {
   int32_t has_shared;   /* 1: one shared expert on every row; 0: none */
   float route_scale;    /* multiplies the routed sum only (1.0 = plain sum) */
   float swiglu_limit;   /* L; <= 0 disables the clamp */
+  float norm_eps;       /* eps of the input RMSNorm (used when moe_args_t.norm_w != NULL); >= 0 */
 } moe_config_t;
 
 /*
@@ -127,9 +130,20 @@ typedef struct moe_args {
    * stages are 0 router logits + activation split, 1 top-k/hash selection +
    * routing bookkeeping, 2 gate/up GEMM, 3 down GEMM, 4 combine. */
   void* const* stage_events;
+  /* Input RMSNorm (the FFN input norm: ffn_norm in the ds4 issue's loader
+   * spec; the rmsnorm step of the pypto DSpark pipeline).  norm_w: bf16 [d],
+   * 16-byte aligned, or NULL (x is used as given).  The layer then runs on
+   *   x'[r][i] = bf16((x[r][i] * rs[r]) * norm_w[i]),  rs[r] = 1/sqrt(sum_i x[r][i]^2 / d + norm_eps),
+   * computed in fp32 and rounded once to nearest even, as an unfused bf16
+   * pipeline would store it (the pages fix neither precision nor eps). */
+  const void* norm_w;
+  /* Residual: bf16 [N][d], 16-byte aligned, or NULL.  out[r] = bf16(residual[r]
+   * + layer output), added in fp32 before the one rounding.  It may be `out`
+   * itself (in-place update) or x, but not overlap `out` partially. */
+  const void* residual;
 } moe_args_t;
 
-#define MOE_N_STAGES 5
+#define MOE_N_STAGES 5  /* the input RMSNorm, when asked for, belongs to stage 0 */
 #define MOE_N_STAGE_EVENTS (MOE_N_STAGES + 1)
 
 /* Library version (MOE_MXFP4_VERSION). */

@@ -20,7 +20,7 @@ c_i32, c_i64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_flo
 
 class MoeConfig(ctypes.Structure):
     _fields_ = [("d_model", c_i32), ("d_ff", c_i32), ("n_experts", c_i32), ("top_k", c_i32), ("routing", c_i32),
-                ("has_shared", c_i32), ("route_scale", c_f32), ("swiglu_limit", c_f32)]
+                ("has_shared", c_i32), ("route_scale", c_f32), ("swiglu_limit", c_f32), ("norm_eps", c_f32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -32,7 +32,8 @@ class MoeArgs(ctypes.Structure):
     _fields_ = [("n_rows", c_i32), ("x", c_vp), ("router_w", c_vp), ("router_bias", c_vp), ("token_ids", c_vp),
                 ("tid2eid", c_vp), ("vocab", c_i64), ("w", MoeWeights), ("out", c_vp), ("topk_idx", c_vp),
                 ("topk_w", c_vp), ("counts", c_vp), ("offsets", c_vp), ("perm", c_vp), ("inv", c_vp),
-                ("workspace", c_vp), ("workspace_bytes", c_size), ("stage_events", c_vp)]
+                ("workspace", c_vp), ("workspace_bytes", c_size), ("stage_events", c_vp), ("norm_w", c_vp),
+                ("residual", c_vp)]
 
 
 MOE_N_STAGES = 5

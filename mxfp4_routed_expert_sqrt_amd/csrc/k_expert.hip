@@ -658,15 +658,15 @@ hipError_t launch_down(const ExpertArgs& a0, int max_groups, hipStream_t stream)
 }
 
 // ---------------------------------------------------------------------------
-// out[r] = y_shared[r] + route_scale * sum_j g[r][j] * y[inv[r][j]], fp32 in
-// ascending slot order, rounded once to bf16 (nearest even).  y is written
+// out[r] = y_shared[r] + route_scale * sum_j g[r][j] * y[inv[r][j]] (+ residual[r]),
+// fp32 in ascending slot order, rounded once to bf16 (nearest even).  y is written
 // once by the down GEMM and read once here: both sides use non-temporal
 // accesses.
 
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ inv,
                                                        const float* __restrict__ gates, int d, int k, int P,
-                                                       int has_shared, float route_scale,
-                                                       uint16_t* __restrict__ out) {
+                                                       int has_shared, float route_scale, const uint16_t* residual,
+                                                       uint16_t* out) {
   constexpr int kMaxK = 8;
   const int r = blockIdx.x;
   const float* src[kMaxK];
@@ -702,20 +702,29 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
           for (int i = 0; i < 4; ++i) acc[i] = fmaf(gw[j], v[u][j][i], acc[i]);
         }
       const v4f sh = v[u][kMaxK];
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = fmaf(route_scale, acc[i], sh[i]);
+      if (residual) {  // read before the store: residual may be out itself
+        const uint2 rb = *(const uint2*)(residual + (size_t)r * d + c);
+        o[0] += __uint_as_float(rb.x << 16);
+        o[1] += __uint_as_float(rb.x & 0xffff0000u);
+        o[2] += __uint_as_float(rb.y << 16);
+        o[3] += __uint_as_float(rb.y & 0xffff0000u);
+      }
       uint2 packed;
-      packed.x = (uint32_t)f32_to_bf16_rne(fmaf(route_scale, acc[0], sh[0])) |
-                 ((uint32_t)f32_to_bf16_rne(fmaf(route_scale, acc[1], sh[1])) << 16);
-      packed.y = (uint32_t)f32_to_bf16_rne(fmaf(route_scale, acc[2], sh[2])) |
-                 ((uint32_t)f32_to_bf16_rne(fmaf(route_scale, acc[3], sh[3])) << 16);
+      packed.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+      packed.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
       *(uint2*)(out + (size_t)r * d + c) = packed;
     }
   }
 }
 
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* gates, int n_rows, int d, int k, int P,
-                          int has_shared, float route_scale, uint16_t* out, hipStream_t stream) {
+                          int has_shared, float route_scale, const uint16_t* residual, uint16_t* out,
+                          hipStream_t stream) {
   hipLaunchKernelGGL(combine_kernel, dim3(n_rows), dim3(256), 0, stream, y, inv, gates, d, k, P, has_shared,
-                     route_scale, out);
+                     route_scale, residual, out);
   return hipGetLastError();
 }
 

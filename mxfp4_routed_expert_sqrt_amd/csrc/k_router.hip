@@ -166,6 +166,51 @@ __global__ void __launch_bounds__(256) prologue_kernel(const uint16_t* __restric
   }
 }
 
+// Input RMSNorm (the FFN input norm), one 256-thread workgroup per row.  The
+// fp32 sum of squares runs in a fixed order: each thread its 8-value chunks
+// in order, a butterfly inside each wave, then the four wave sums in order;
+// rs = 1/sqrt(ss/d + eps) and xn = bf16((x * rs) * g), rounded to nearest even.
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ g,
+                                                       int d, float eps, uint16_t* __restrict__ xn) {
+  __shared__ float wave_sum[4];
+  const int tid = threadIdx.x;
+  const size_t row = (size_t)blockIdx.x * d;
+  float ss = 0.f;
+  for (int c = tid * 8; c < d; c += 256 * 8) {
+    const u32x4 v = *(const u32x4*)(x + row + c);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float lo = __uint_as_float(v[h] << 16), hi = __uint_as_float(v[h] & 0xffff0000u);
+      ss += lo * lo;
+      ss += hi * hi;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m, 64);
+  if ((tid & 63) == 0) wave_sum[tid >> 6] = ss;
+  __syncthreads();
+  const float total = ((wave_sum[0] + wave_sum[1]) + wave_sum[2]) + wave_sum[3];
+  const float rs = 1.0f / sqrtf(total / (float)d + eps);
+  for (int c = tid * 8; c < d; c += 256 * 8) {
+    const u32x4 v = *(const u32x4*)(x + row + c);
+    const u32x4 w = *(const u32x4*)(g + c);
+    u32x4 o;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float lo = (__uint_as_float(v[h] << 16) * rs) * __uint_as_float(w[h] << 16);
+      const float hi = (__uint_as_float(v[h] & 0xffff0000u) * rs) * __uint_as_float(w[h] & 0xffff0000u);
+      o[h] = (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+    }
+    *(u32x4*)(xn + row + c) = o;
+  }
+}
+
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* g, int n_rows, int d, float eps, uint16_t* xn,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)n_rows), dim3(256), 0, stream, x, g, d, eps, xn);
+  return hipGetLastError();
+}
+
 hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d, int E, float* z_part,
                            uint8_t* xq, uint8_t* xs, int32_t* done, bool fp6, hipStream_t stream) {
   const int S = logits_splits(n_rows, E, d);

@@ -47,6 +47,10 @@ hipError_t launch_pack_mxfp4(const uint8_t* q, const uint8_t* s, int n_mat, int 
 hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d, int E, float* z_part, uint8_t* xq,
                            uint8_t* xs, int32_t* done, bool fp6, hipStream_t stream);
 
+// xn[r] = bf16((x[r][i] * rs[r]) * g[i]), rs[r] = 1/sqrt(mean_i x[r][i]^2 + eps), fp32 (d % 128 == 0).
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* g, int n_rows, int d, float eps, uint16_t* xn,
+                          hipStream_t stream);
+
 // Rows of one work group (and work unit) of the expert GEMMs for a batch of
 // n_pairs routed pairs:
 //  - 64 (tall units, activations split into two FP6 terms) once the batch has
@@ -113,8 +117,10 @@ struct ExpertArgs {
 hipError_t launch_gateup(const ExpertArgs& a, int max_groups, hipStream_t stream);
 hipError_t launch_down(const ExpertArgs& a, int max_groups, hipStream_t stream);
 
+// residual: bf16 [N][d] added before the rounding, or NULL (may equal out)
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* gates, int n_rows, int d, int k,
-                          int P, int has_shared, float route_scale, uint16_t* out, hipStream_t stream);
+                          int P, int has_shared, float route_scale, const uint16_t* residual, uint16_t* out,
+                          hipStream_t stream);
 
 // Worst-case number of work groups of <= rows rows each for n_rows rows:
 // sum_e ceil(c_e/rows) <= ceil(P/rows) + E, plus the shared rows.

@@ -12,7 +12,7 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, hist, done, xq, xs, hq, hs, y, total;
+  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, hist, done, xn, xq, xs, hq, hs, y, total;
   int max_groups;  // capacity of the work list: groups of kGroupRows rows, the most there can be
 };
 
@@ -39,6 +39,7 @@ Layout make_layout(const moe_config_t& c, int n) {
   L.n_groups = take(4);
   L.hist = take(route_hist_bytes(n, c.n_experts));
   L.done = take(4);
+  L.xn = take(N * (size_t)c.d_model * 2);  // the normalised input (when norm_w is given)
   L.xq = take(N * split_q_row_bytes(c.d_model));
   L.xs = take(N * split_s_row_bytes(c.d_model));
   L.hq = take(Ptot * split_q_row_bytes(c.d_ff));
@@ -64,6 +65,7 @@ int check_config(const moe_config_t* c) {
   if (c->n_experts < 1 || c->n_experts > 1024) return MOE_ERR_UNSUPPORTED;
   if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts) return MOE_ERR_UNSUPPORTED;
   if (!(c->route_scale == c->route_scale) || !(c->swiglu_limit == c->swiglu_limit)) return MOE_ERR_INVALID;
+  if (!(c->norm_eps >= 0.f) || c->norm_eps == INFINITY) return MOE_ERR_INVALID;
   return MOE_OK;
 }
 
@@ -153,6 +155,9 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
     if (p && !aligned(p, 4)) return MOE_ERR_INVALID;
   const size_t out_bytes = (size_t)N * d * 2;
   if (overlap(a.out, out_bytes, a.x, out_bytes)) return MOE_ERR_INVALID;
+  if (a.norm_w && !aligned(a.norm_w, 16)) return MOE_ERR_INVALID;
+  if (a.residual && (!aligned(a.residual, 16) || (a.residual != a.out && overlap(a.residual, out_bytes, a.out, out_bytes))))
+    return MOE_ERR_INVALID;
   const Layout L = make_layout(c, N);
   if (!a.workspace || a.workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned(a.workspace, 256)) return MOE_ERR_INVALID;
@@ -183,8 +188,14 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   if (!mark(0)) return MOE_ERR_HIP;
   const int rows = unit_rows(P, E, d, I);
   const int max_groups = max_work_groups(N, k, E, c.has_shared, rows);
-  if ((err = launch_prologue((const uint16_t*)a.x, a.router_w, N, d, E, z, xq, xs, done, rows == kTallGroupRows,
-                             stream)) !=
+  const uint16_t* x = (const uint16_t*)a.x;
+  if (a.norm_w) {
+    uint16_t* xn = (uint16_t*)(ws + L.xn);
+    if ((err = launch_rmsnorm(x, (const uint16_t*)a.norm_w, N, d, c.norm_eps, xn, stream)) != hipSuccess)
+      return MOE_ERR_HIP;
+    x = xn;
+  }
+  if ((err = launch_prologue(x, a.router_w, N, d, E, z, xq, xs, done, rows == kTallGroupRows, stream)) !=
       hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
@@ -236,8 +247,8 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   if ((err = launch_down(da, max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
   if (!mark(4)) return MOE_ERR_HIP;
 
-  if ((err = launch_combine(y, inv, gates, N, d, k, P, c.has_shared, c.route_scale, (uint16_t*)a.out, stream)) !=
-      hipSuccess)
+  if ((err = launch_combine(y, inv, gates, N, d, k, P, c.has_shared, c.route_scale, (const uint16_t*)a.residual,
+                            (uint16_t*)a.out, stream)) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(5)) return MOE_ERR_HIP;
   return MOE_OK;

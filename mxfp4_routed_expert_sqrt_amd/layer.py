@@ -12,12 +12,13 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def make_config(shape: MoEShape, has_shared: bool = True, route_scale=None, swiglu_limit=None) -> capi.MoeConfig:
+def make_config(shape: MoEShape, has_shared: bool = True, route_scale=None, swiglu_limit=None,
+                norm_eps: float = 1e-6) -> capi.MoeConfig:
     return capi.MoeConfig(shape.d_model, shape.d_ff, shape.n_experts, shape.top_k,
                           capi.MOE_ROUTING_TOPK if shape.routing == "topk" else capi.MOE_ROUTING_HASH,
                           1 if has_shared else 0,
                           float(shape.route_scale if route_scale is None else route_scale),
-                          float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit))
+                          float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit), float(norm_eps))
 
 
 def pack_mxfp4(q: torch.Tensor, s: torch.Tensor, rows: int, K: int, stream=None, out=None):
@@ -87,11 +88,14 @@ class PackedExperts:
 
 class MoELayer:
     def __init__(self, shape: MoEShape, router_w, experts, device="cuda", router_bias=None,
-                 has_shared: bool = True, route_scale=None, swiglu_limit=None):
-        """experts: natural-layout arrays (dict, packed here) or an already packed PackedExperts."""
+                 has_shared: bool = True, route_scale=None, swiglu_limit=None, norm_w=None, norm_eps: float = 1e-6):
+        """experts: natural-layout arrays (dict, packed here) or an already packed PackedExperts.
+        norm_w: optional bf16 bit patterns [d] of the input RMSNorm weight (the layer then normalises x)."""
         self.shape = shape
         self.device = torch.device(device)
-        self.cfg = make_config(shape, has_shared, route_scale, swiglu_limit)
+        self.cfg = make_config(shape, has_shared, route_scale, swiglu_limit, norm_eps)
+        self.norm_w = None if norm_w is None else \
+            torch.from_numpy(np.ascontiguousarray(norm_w, dtype=np.uint16).view(np.int16)).to(self.device)
         self.router_w = torch.as_tensor(np.ascontiguousarray(router_w, dtype=np.float32)).to(self.device)
         self.router_bias = None if router_bias is None else \
             torch.as_tensor(np.ascontiguousarray(router_bias, dtype=np.float32)).to(self.device)
@@ -109,18 +113,19 @@ class MoELayer:
     def new_workspace(self, n_rows: int) -> torch.Tensor:
         return torch.empty(max(self.workspace_bytes(n_rows), 256), dtype=torch.uint8, device=self.device)
 
-    def args(self, x, out, workspace, token_ids=None, tid2eid=None, routing=None) -> capi.MoeArgs:
+    def args(self, x, out, workspace, token_ids=None, tid2eid=None, routing=None, residual=None) -> capi.MoeArgs:
         N = x.shape[0]
         r = routing or {}
         return capi.MoeArgs(N, _ptr(x), _ptr(self.router_w), _ptr(self.router_bias), _ptr(token_ids), _ptr(tid2eid),
                             0 if tid2eid is None else tid2eid.shape[0], self.experts.weights(self.has_shared), _ptr(out),
                             _ptr(r.get("topk_idx")), _ptr(r.get("topk_w")), _ptr(r.get("counts")),
                             _ptr(r.get("offsets")), _ptr(r.get("perm")), _ptr(r.get("inv")), _ptr(workspace),
-                            0 if workspace is None else workspace.numel())
+                            0 if workspace is None else workspace.numel(), None, _ptr(self.norm_w), _ptr(residual))
 
     def forward(self, x: torch.Tensor, token_ids=None, tid2eid=None, out=None, workspace=None, with_routing=False,
-                stream=None):
-        """x: bf16 [N][d] on the device.  Returns out (bf16 [N][d]) or (out, routing dict)."""
+                stream=None, residual=None):
+        """x: bf16 [N][d] on the device; residual: optional bf16 [N][d] added to the output.
+        Returns out (bf16 [N][d]) or (out, routing dict)."""
         N, k, E = x.shape[0], self.shape.top_k, self.shape.n_experts
         if out is None:
             out = torch.empty_like(x)
@@ -136,7 +141,7 @@ class MoELayer:
                            perm=torch.empty(N * k, dtype=torch.int32, device=dev),
                            inv=torch.empty(N * k, dtype=torch.int32, device=dev))
         st = torch.cuda.current_stream(self.device).cuda_stream if stream is None else stream
-        rc = capi.moe_layer_forward(self.cfg, self.args(x, out, workspace, token_ids, tid2eid, routing), st)
+        rc = capi.moe_layer_forward(self.cfg, self.args(x, out, workspace, token_ids, tid2eid, routing, residual), st)
         if rc != capi.MOE_OK:
             raise capi.MoeError(rc)
         return (out, routing) if with_routing else out

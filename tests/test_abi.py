@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert capi.moe_version() == 1
+    assert capi.moe_version() == 2
     for st in (0, -1, -2, -3, -4):
         assert capi.moe_status_string(st) != "unknown status"
     assert capi.moe_status_string(7) == "unknown status"
@@ -57,9 +57,9 @@ def test_workspace_size_arithmetic():
     b = capi.moe_workspace_size(cfg, 512)
     N, k, E, d, I = 512, 6, 256, 4096, 2048
     Ptot = N * k + N
-    # the big regions: fp32 y, split h, split x, router logits (1 to 16 split-K partials)
-    assert b >= Ptot * d * 4 + Ptot * I * 2 + N * d * 2 + N * E * 4
-    assert b < (Ptot * d * 4 + Ptot * I * 2 + N * d * 2 + 16 * N * E * 4) * 1.05
+    # the big regions: fp32 y, split h, split x, the normalised input, router logits (1 to 16 split-K partials)
+    assert b >= Ptot * d * 4 + Ptot * I * 2 + N * d * 2 + N * d * 2 + N * E * 4
+    assert b < (Ptot * d * 4 + Ptot * I * 2 + N * d * 2 + N * d * 2 + 16 * N * E * 4) * 1.05
     assert capi.moe_workspace_size(cfg, 0) == 0
     assert capi.moe_workspace_size(cfg, 1024) > b
 
@@ -69,6 +69,8 @@ def test_workspace_size_arithmetic():
     ("n_experts", 0, capi.MOE_ERR_UNSUPPORTED), ("n_experts", 1025, capi.MOE_ERR_UNSUPPORTED),
     ("top_k", 0, capi.MOE_ERR_UNSUPPORTED), ("top_k", 9, capi.MOE_ERR_UNSUPPORTED),
     ("routing", 2, capi.MOE_ERR_INVALID), ("has_shared", 3, capi.MOE_ERR_INVALID),
+    ("norm_eps", -1e-6, capi.MOE_ERR_INVALID), ("norm_eps", float("inf"), capi.MOE_ERR_INVALID),
+    ("norm_eps", float("nan"), capi.MOE_ERR_INVALID),
 ])
 def test_bad_config_rejected(field, value, status):
     cfg = make_config(SHAPES["tiny"])
@@ -109,6 +111,9 @@ def test_invalid_arguments_return_before_any_hip_call():
     a = _valid_args(cfg, N); a.perm = 0x90000002; cases.append((a, capi.MOE_ERR_INVALID))
     a = _valid_args(cfg, N); a.n_rows = -1; cases.append((a, capi.MOE_ERR_INVALID))
     a = _valid_args(cfg, N); a.n_rows = capi.MOE_MAX_ROWS + 1; cases.append((a, capi.MOE_ERR_UNSUPPORTED))
+    a = _valid_args(cfg, N); a.norm_w = 0xA0000008; cases.append((a, capi.MOE_ERR_INVALID))   # misaligned
+    a = _valid_args(cfg, N); a.residual = 0xB0000004; cases.append((a, capi.MOE_ERR_INVALID))  # misaligned
+    a = _valid_args(cfg, N); a.residual = a.out + 512; cases.append((a, capi.MOE_ERR_INVALID))  # partial overlap
     for a, st in cases:
         assert capi.moe_layer_forward(cfg, a, None) == st
     hcfg = make_config(SHAPES["hash2048"])

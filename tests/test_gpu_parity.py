@@ -13,13 +13,19 @@ torch = pytest.importorskip("torch")
 
 from mxfp4_routed_expert_sqrt_amd.configs import SHAPES, MoEShape  # noqa: E402
 from mxfp4_routed_expert_sqrt_amd.layer import MoELayer, PackedExperts  # noqa: E402
-from tests.inputs import oracle_forward, workload  # noqa: E402
+from tests.inputs import norm_workload, oracle_forward, workload  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
 MAX_ERR = 2e-2
 MEAN_REL = 5e-3
 GATE_RTOL = 1e-5
+# With the input RMSNorm the two sides round the normalised row to bf16 from fp32 sums of
+# squares taken in different orders (the oracle in index order, the kernel as a tree).  Where
+# the fp32 values fall within an ulp of a bf16 rounding boundary (about one element in 1e3) the
+# roundings differ by one bf16 ulp; that moves a logit by ~1e-4 and a gate by up to ~3e-4
+# relative.  The routing stays bit-exact (the inputs keep a 1e-3 score margin).
+GATE_RTOL_NORM = 1e-3
 
 _PACKED = {}
 
@@ -52,28 +58,35 @@ def packed_for(wl, has_shared=True):
 def run_gpu(wl, has_shared=True, **cfg_kw):
     sh = wl["shape"]
     dev = torch.device("cuda")
+    if "norm_w" in wl:
+        cfg_kw = dict(cfg_kw, norm_w=wl["norm_w"], norm_eps=wl["norm_eps"])
     layer = MoELayer(sh, wl["router_w"], packed_for(wl, has_shared), dev, router_bias=wl["bias"],
                      has_shared=has_shared, **cfg_kw)
     x = torch.from_numpy(wl["x"].view(np.int16)).to(dev).view(torch.bfloat16)
-    tok = tab = None
+    tok = tab = resid = None
     if sh.routing == "hash":
         tok = torch.from_numpy(wl["token_ids"]).to(dev)
         tab = torch.from_numpy(wl["tid2eid"]).to(dev)
-    print(f"gpu forward {sh.name} N={sh.n_rows} shared={has_shared} {cfg_kw}", flush=True)
-    out, routing = layer.forward(x, tok, tab, with_routing=True)
+    if "residual" in wl:
+        resid = torch.from_numpy(wl["residual"].view(np.int16)).to(dev).view(torch.bfloat16)
+    print(f"gpu forward {sh.name} N={sh.n_rows} shared={has_shared} norm={'norm_w' in wl} "
+          f"{ {k: v for k, v in cfg_kw.items() if k != 'norm_w'} }", flush=True)
+    out, routing = layer.forward(x, tok, tab, with_routing=True, residual=resid)
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in routing.items()}
     res["out"] = out.view(torch.int16).cpu().numpy().view(np.uint16)
     return res, layer, x, tok, tab
 
 
-def check_routing(gpu, ref, label=""):
+def check_routing(gpu, ref, label="", gate_rtol=GATE_RTOL):
     assert np.array_equal(gpu["topk_idx"], ref["idx"]), f"{label}: expert ids differ"
     assert np.array_equal(gpu["counts"], ref["counts"]), f"{label}: counts differ"
     assert np.array_equal(gpu["offsets"], ref["offsets"]), f"{label}: offsets differ"
     assert np.array_equal(gpu["perm"], ref["perm"]), f"{label}: perm differs"
     assert np.array_equal(gpu["inv"], ref["inv"]), f"{label}: inv differs"
-    np.testing.assert_allclose(gpu["topk_w"], ref["gates"], rtol=GATE_RTOL, atol=0)
+    rel = np.abs(gpu["topk_w"] - ref["gates"]) / np.abs(ref["gates"])
+    print(f"{label}: gates max rel diff {rel.max():.2e}", flush=True)
+    np.testing.assert_allclose(gpu["topk_w"], ref["gates"], rtol=gate_rtol, atol=0)
 
 
 def sample_rows(n, count, seed=0):
@@ -131,6 +144,19 @@ def test_full_size_parity(name, n_sample):
         load = gpu["counts"] / wl["shape"].n_rows
         print(f"zipf2048 hottest expert load {load.max():.3f} of rows, {load.max() / wl['shape'].top_k:.3f} of "
               f"assignments", flush=True)
+
+
+# ------------------------------------------------ input RMSNorm and residual
+
+@pytest.mark.parametrize("name,n_sample", [("tiny", 0), ("verify512", 32), ("prefill8192", 16), ("hash2048", 16)])
+def test_input_norm_and_residual(name, n_sample):
+    # rows scaled by 2^-3 .. 2^3 before the norm; the residual is added before the output rounding
+    wl = norm_workload(name)
+    gpu, *_ = run_gpu(wl)
+    rows = None if n_sample == 0 else sample_rows(wl["shape"].n_rows, n_sample)
+    ref = oracle_forward(wl, rows=rows)
+    check_routing(gpu, ref, name + "+norm", gate_rtol=GATE_RTOL_NORM)
+    check_out(gpu["out"] if rows is None else gpu["out"][rows], ref["out"], name + "+norm")
 
 
 # ---------------------------------------------------------------- edge cases

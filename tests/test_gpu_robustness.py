@@ -85,6 +85,26 @@ def test_workspace_reused_for_a_smaller_batch():
     _same(reused, fresh, "reuse")
 
 
+def test_residual_in_place_matches_separate_buffers():
+    from tests.inputs import norm_workload
+    wl = norm_workload("tiny")
+    sh = wl["shape"]
+    dev = torch.device("cuda")
+    layer = MoELayer(sh, wl["router_w"], PackedExperts(wl["experts"], sh, dev, True), dev, norm_w=wl["norm_w"],
+                     norm_eps=wl["norm_eps"])
+    x, _, _ = _inputs(wl)
+    resid = torch.from_numpy(wl["residual"].view(np.int16)).to(dev).view(torch.bfloat16)
+    print("residual: separate buffer, then in place", flush=True)
+    sep = layer.forward(x, residual=resid)
+    inplace = resid.clone()
+    layer.forward(x, out=inplace, residual=inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(sep.view(torch.int16), inplace.view(torch.int16))
+    plain = layer.forward(x)  # no residual: out differs from sep by the residual only
+    torch.cuda.synchronize()
+    assert not torch.equal(sep, plain)
+
+
 def test_stage_events_with_null_entries():
     wl = workload("tiny")
     layer = _layer(wl)
