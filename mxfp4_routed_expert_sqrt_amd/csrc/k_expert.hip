@@ -3,12 +3,12 @@
 // A operand = the expert's MXFP4 weight rows (E2M1, with their E8M0 scales
 // fed to the MFMA directly, so there is no dequantisation step); B operand =
 // activations as two FP8 (E4M3) terms with per-32 E8M0 scales (x ~= q1*2^e1 +
-// q2*2^e2), so every product is weight * (q1 + q2) accumulated in fp32.
+// q2*2^e2), or two FP6 (E2M3) terms on tall work units, so every product is
+// weight * (q1 + q2) accumulated in fp32.
 //
-// One workgroup = one work unit = (group of <= 16 rows of one expert = one
-// MFMA column tile, a block of output features).  4 or 8 waves per workgroup,
-// each with several 16-row weight tiles; the block is the widest that divides
-// the output width.
+// One workgroup = one work unit = (group of <= 16, 32 or 64 rows of one expert
+// = NB MFMA column tiles, a block of output features).  4 or 8 waves per
+// workgroup, each with several 16-row weight tiles.
 // Weight fragments go straight from HBM into a 4-deep register ring per wave:
 // the packed layout makes each wave's 16-byte-per-lane load one contiguous
 // kilobyte, and every weight byte is used by exactly one wave.  The
@@ -19,7 +19,9 @@
 // Lane layout of the 16x16x128 scaled MFMA (measured on gfx950; the probe test
 // pins it): lane l supplies row/column l%16; a 4-bit operand holds K values
 // 32*(l/16)..+31 (low nibble first), an 8-bit operand holds K values
-// 16*(l/16)..+15 and 64+16*(l/16)..+15; the E8M0 scale of 32-block b of
+// 16*(l/16)..+15 and 64+16*(l/16)..+15, a 6-bit operand holds K values
+// 32*(l/16)..+31 as a 192-bit little-endian string (value i at bits 6i, dwords
+// 0-5 of the 8-dword operand); the E8M0 scale of 32-block b of
 // row/column n is byte `opsel` of lane n+16b's scale register; the fp32 result
 // has D[4*(l/16) + i][l%16] in element i of lane l.
 #include "kernels.h"
@@ -308,7 +310,8 @@ __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Group g, i
 
 // ---------------------------------------------------------------------------
 // gate/up: h = silu(min(gate, L)) * clamp(up, -L, L), written as the two-term
-// FP8 split that the down GEMM consumes (same layout as the x split, K = I).
+// split that the down GEMM consumes (FP8, or FP6 on tall units; the layout of
+// the x split with K = I).
 // Each of the WAVES waves takes TPM 16-row tiles of the gate matrix and the
 // same rows of the up matrix: 16*TPM features per wave, 16*TPM*WAVES per work
 // unit.
