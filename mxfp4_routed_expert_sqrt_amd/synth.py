@@ -17,6 +17,7 @@ Recipe (seed 0 unless stated):
   sum q = k; ranks map to a seeded permutation of the experts.
 - with the input RMSNorm: x rows scaled by 2^u, u uniform in {-3, ..., 3}
   (exact in bf16); norm weight 1 + N(0, 0.1) and residual N(0, 1), both bf16.
+- selection-only router bias: N(0, 0.05) fp32 per expert.
 """
 import ctypes
 import os
@@ -212,8 +213,9 @@ def resample_rows(shape: MoEShape, accept_rows, seed: int = 0, max_tries: int = 
     raise RuntimeError(f"{shape.name}: rows still rejected after {max_tries} redraws")
 
 
-# Streams of the input-RMSNorm extras (numpy generators keyed by seed, workload and tensor).
-_TAG_ROW_EXP, _TAG_NORM_W, _TAG_RESIDUAL = 11, 12, 13
+# Streams of the input-RMSNorm extras and the selection-only bias (numpy generators keyed by
+# seed, workload and tensor).
+_TAG_ROW_EXP, _TAG_NORM_W, _TAG_RESIDUAL, _TAG_SEL_BIAS = 11, 12, 13, 14
 
 
 def _rng(shape: MoEShape, seed: int, tag: int):
@@ -246,3 +248,8 @@ def gen_norm_weight(shape: MoEShape, seed: int = 0) -> np.ndarray:
 def gen_residual(shape: MoEShape, seed: int = 0) -> np.ndarray:
     """Residual rows [N][d] as bf16 bits: N(0, 1)."""
     return bf16_bits(_rng(shape, seed, _TAG_RESIDUAL).standard_normal((shape.n_rows, shape.d_model)))
+
+
+def gen_selection_bias(shape: MoEShape, seed: int = 0) -> np.ndarray:
+    """Router bias [E] fp32, N(0, 0.05), for the selection-only bias reading."""
+    return (0.05 * _rng(shape, seed, _TAG_SEL_BIAS).standard_normal(shape.n_experts)).astype(np.float32)

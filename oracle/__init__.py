@@ -28,7 +28,7 @@ def build() -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int), ("d", ctypes.c_int), ("E", ctypes.c_int), ("k", ctypes.c_int),
                 ("I", ctypes.c_int), ("routing", ctypes.c_int), ("route_scale", ctypes.c_double),
-                ("swiglu_limit", ctypes.c_double), ("norm_eps", ctypes.c_float)]
+                ("swiglu_limit", ctypes.c_double), ("norm_eps", ctypes.c_float), ("bias_mode", ctypes.c_int)]
 
 
 class _Inputs(ctypes.Structure):
@@ -56,7 +56,7 @@ def _load():
         lib.orc_softplus.argtypes, lib.orc_softplus.restype = [dbl], dbl
         lib.orc_score.argtypes, lib.orc_score.restype = [dbl], dbl
         lib.orc_topk.argtypes, lib.orc_topk.restype = [vp, i32, i32, vp], dbl
-        lib.orc_route.argtypes = [vp, i32, i32, i32, i32, vp, vp, ctypes.c_long, vp, vp, vp]
+        lib.orc_route.argtypes = [vp, i32, i32, i32, i32, vp, vp, ctypes.c_long, vp, vp, vp, vp]
         lib.orc_route.restype = i32
         lib.orc_bookkeeping.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
         lib.orc_forward.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_Inputs), vp, i32, vp, vp, vp, vp, vp,
@@ -130,8 +130,9 @@ def topk(s: np.ndarray, k: int):
     return idx, gap
 
 
-def route(z: np.ndarray, k: int, routing: str = "topk", token_ids=None, tid2eid=None):
-    """(idx [N][k] ascending, gates [N][k], margin [N]) from logits z [N][E]."""
+def route(z: np.ndarray, k: int, routing: str = "topk", token_ids=None, tid2eid=None, sel_bias=None):
+    """(idx [N][k] ascending, gates [N][k], margin [N]) from logits z [N][E].
+    sel_bias: optional [E] added to the scores for the selection only."""
     z = np.ascontiguousarray(z, dtype=np.float64)
     N, E = z.shape
     idx = np.empty((N, k), dtype=np.int32)
@@ -141,7 +142,8 @@ def route(z: np.ndarray, k: int, routing: str = "topk", token_ids=None, tid2eid=
     tok = None if token_ids is None else np.ascontiguousarray(token_ids, dtype=np.int32)
     tab = None if tid2eid is None else np.ascontiguousarray(tid2eid, dtype=np.int32)
     vocab = 0 if tab is None else tab.shape[0]
-    rc = _load().orc_route(_p(z), N, E, k, mode, _p(tok), _p(tab), vocab, _p(idx), _p(gates), _p(margin))
+    sb = None if sel_bias is None else np.ascontiguousarray(sel_bias, dtype=np.float32)
+    rc = _load().orc_route(_p(z), N, E, k, mode, _p(tok), _p(tab), vocab, _p(sb), _p(idx), _p(gates), _p(margin))
     if rc != 0:
         raise ValueError("invalid hash-routing table entry")
     return idx, gates, margin
@@ -172,8 +174,11 @@ def rmsnorm_bf16(x_bf16: np.ndarray, g_bf16: np.ndarray, eps: float) -> np.ndarr
 
 def forward(shape, x, router_w, experts, router_bias=None, token_ids=None, tid2eid=None, rows=None,
             route_scale=None, swiglu_limit=None, with_shared=True, threads=None, norm_w=None, norm_eps=1e-6,
-            residual=None) -> dict:
+            residual=None, bias_mode=0) -> dict:
     """The whole layer in fp64.
+
+    bias_mode: 0 = router_bias added to the logits (selection and gates); 1 = added to the
+    scores for the selection only (gates from the unbiased scores).
 
     norm_w: optional bf16 [d] RMSNorm weight; the layer then runs on rmsnorm_bf16(x, norm_w, norm_eps).
     residual: optional bf16 [N][d] added to the output.
@@ -188,7 +193,7 @@ def forward(shape, x, router_w, experts, router_bias=None, token_ids=None, tid2e
     assert x.shape == (N, d)
     cfg = _Cfg(N, d, E, k, I, 0 if shape.routing == "topk" else 1,
                float(shape.route_scale if route_scale is None else route_scale),
-               float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit), float(norm_eps))
+               float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit), float(norm_eps), int(bias_mode))
     keep = []
 
     def P(a, dtype=None):

@@ -196,20 +196,26 @@ double orc_topk(const double* s, int E, int k, int* idx) {
 }
 
 /* Routing of N rows from logits z [N][E].
- * routing 0: the k highest scores.  routing 1 (hash): the k experts listed in
+ * routing 0: the k highest scores, or with sel_bias (the selection-only bias
+ * reading of the router bias, gate.bias in the ds4 loader spec) the k highest
+ * s + sel_bias.  routing 1 (hash): the k experts listed in
  * tid2eid[token_ids[r]] (distinct, in range; returns -1 otherwise).
- * idx [N][k] ascending expert id; gates [N][k] = s at idx, normalised to sum 1;
- * margin [N] (may be NULL): top-k score gap (routing 0) or +inf (routing 1). */
+ * idx [N][k] ascending expert id; gates [N][k] = s at idx (never biased),
+ * normalised to sum 1; margin [N] (may be NULL): gap between the k-th and the
+ * (k+1)-th selection value (routing 0) or +inf (routing 1). */
 int orc_route(const double* z, int N, int E, int k, int routing, const int32_t* token_ids,
-              const int32_t* tid2eid, long vocab, int32_t* idx, double* gates, double* margin) {
+              const int32_t* tid2eid, long vocab, const float* sel_bias, int32_t* idx, double* gates,
+              double* margin) {
   double* s = (double*)malloc(sizeof(double) * (size_t)E);
+  double* t = (double*)malloc(sizeof(double) * (size_t)E);
   int sel[1024];
   int rc = 0;
   for (int r = 0; r < N && rc == 0; ++r) {
     for (int e = 0; e < E; ++e) s[e] = orc_score(z[(size_t)r * E + e]);
     double m = INFINITY;
     if (routing == 0) {
-      m = orc_topk(s, E, k, sel);
+      for (int e = 0; e < E; ++e) t[e] = sel_bias ? s[e] + (double)sel_bias[e] : s[e];
+      m = orc_topk(t, E, k, sel);
     } else {
       long t = token_ids[r];
       if (t < 0 || t >= vocab) { rc = -1; break; }
@@ -236,6 +242,7 @@ int orc_route(const double* z, int N, int E, int k, int routing, const int32_t* 
     if (margin) margin[r] = m;
   }
   free(s);
+  free(t);
   return rc;
 }
 
@@ -347,6 +354,7 @@ typedef struct {
   double route_scale;   /* multiplies the routed sum only */
   double swiglu_limit;  /* <= 0 disables the clamp */
   float norm_eps;       /* RMSNorm eps (used when norm_w != NULL) */
+  int bias_mode;        /* router_bias: 0 added to the logits; 1 added to the scores for the selection only */
 } orc_cfg;
 
 typedef struct {
@@ -388,8 +396,10 @@ int orc_forward(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows, i
   double* z = (double*)malloc(sizeof(double) * (size_t)N * E);
   int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)N * k);
   double* gates = (double*)malloc(sizeof(double) * (size_t)N * k);
-  orc_router_logits(x, N, d, in->router_w, E, in->router_bias, z, nthreads);
-  int rc = orc_route(z, N, E, k, cfg->routing, in->token_ids, in->tid2eid, in->vocab, idx, gates, margin_out);
+  const int sel_only = cfg->bias_mode == 1;
+  orc_router_logits(x, N, d, in->router_w, E, sel_only ? NULL : in->router_bias, z, nthreads);
+  int rc = orc_route(z, N, E, k, cfg->routing, in->token_ids, in->tid2eid, in->vocab,
+                     sel_only ? in->router_bias : NULL, idx, gates, margin_out);
   if (rc != 0) {
     free(z); free(idx); free(gates); free(xn);
     return rc;

@@ -102,6 +102,26 @@ def norm_workload(name, seed: int = 0):
     return wl
 
 
+@functools.lru_cache(maxsize=None)
+def selection_bias_workload(name, seed: int = 0):
+    """The workload with a router bias read as a selection-only bias (bias_mode 1): a seeded
+    N(0, 0.05) fp32 bias added to the scores for choosing the experts; the margin filter runs on
+    score + bias."""
+    base = workload(name, seed)
+    shape = base["shape"]
+    bias = synth.gen_selection_bias(shape, seed)
+
+    def accept(rows):
+        z = oracle.router_logits(rows, base["router_w"])
+        _, _, margin = oracle.route(z, shape.top_k, sel_bias=bias)
+        return margin >= MIN_MARGIN
+
+    x, attempts = synth.resample_rows(shape, accept, seed)
+    wl = dict(base)
+    wl.update(x=x, attempts=attempts, bias=bias, bias_mode=1)
+    return wl
+
+
 def _scale_bf16(x_bits, factor):
     """Multiply bf16 bit patterns by a power of two (exact while in range)."""
     f = (x_bits.astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
@@ -109,6 +129,8 @@ def _scale_bf16(x_bits, factor):
 
 
 def oracle_forward(wl, rows=None, **kw):
+    if "bias_mode" in wl:
+        kw.setdefault("bias_mode", wl["bias_mode"])
     if "norm_w" in wl:
         kw.setdefault("norm_w", wl["norm_w"])
         kw.setdefault("norm_eps", wl["norm_eps"])

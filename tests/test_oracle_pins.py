@@ -436,3 +436,44 @@ def test_norm_workload_margins():
     _, _, margin = oracle.route(oracle.router_logits(xn, wl["router_w"]), wl["shape"].top_k)
     assert margin.min() >= 1e-3
     assert len(set(synth.gen_row_exponents(wl["shape"]).tolist())) > 3
+
+
+# --------------------------------------------------- selection-only router bias
+
+def test_selection_only_bias_brute_force():
+    # bias_mode 1: the k largest s + b choose the experts; the gates are the chosen unbiased
+    # scores normalised (numpy: logits by matmul, s = sqrt(log(1 + e^z)), stable argsort)
+    wl = workload("tiny")
+    sh = wl["shape"]
+    b = np.random.default_rng(8).normal(0, 0.05, sh.n_experts).astype(np.float32)
+    r = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], router_bias=b, bias_mode=1)
+    x = _bf16_f32(wl["x"]).astype(np.float64)
+    z = x @ wl["router_w"].astype(np.float64).T
+    s = np.sqrt(np.logaddexp(0.0, z))
+    t = s + b.astype(np.float64)[None, :]
+    for row in range(sh.n_rows):
+        want = np.sort(np.argsort(-t[row], kind="stable")[:sh.top_k])
+        assert np.array_equal(r["idx"][row], want)
+        g = s[row, want] / s[row, want].sum()
+        assert np.allclose(r["gates"][row], g, rtol=1e-12, atol=0)
+    assert np.allclose(r["z"], z, rtol=1e-12, atol=1e-12)  # the logits carry no bias in this mode
+
+
+def test_selection_only_bias_zero_and_forcing():
+    wl = workload("tiny")
+    sh = wl["shape"]
+    plain = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"])
+    zero = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], router_bias=np.zeros(sh.n_experts, np.float32),
+                          bias_mode=1)
+    for key in ("out", "idx", "gates", "perm"):
+        assert np.array_equal(plain[key], zero[key])
+    # a large bias on expert 5 puts it in every row; its gate stays its unbiased score's share
+    b = np.zeros(sh.n_experts, np.float32)
+    b[5] = 100.0
+    forced = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], router_bias=b, bias_mode=1)
+    assert np.all((forced["idx"] == 5).any(axis=1))
+    s = np.sqrt(np.logaddexp(0.0, forced["z"]))
+    col = np.argmax(forced["idx"] == 5, axis=1)
+    g5 = forced["gates"][np.arange(sh.n_rows), col]
+    assert np.allclose(g5, s[:, 5] / np.take_along_axis(s, forced["idx"], 1).sum(1), rtol=1e-12)
+    assert g5.max() < 0.9  # not dominated by the bias
