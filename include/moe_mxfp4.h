@@ -28,7 +28,8 @@
  * The pages do not fix gate normalisation, the placement of the swiglu clamp
  * or the bias semantics; this library normalises the selected scores to sum
  * 1, clamps the gate from above and the up projection on both sides at L, and
- * adds the bias to the logit before the score.
+ * adds the bias to the logit before the score (or, with bias_mode
+ * MOE_BIAS_SELECT, to the score for the selection only).
  *
  * Conventions for every entry point:
  *   - Return 0 (MOE_OK) or a negative MOE_ERR_* code.  Argument validation is
@@ -61,6 +62,7 @@ enum {
 };
 
 enum { MOE_ROUTING_TOPK = 0, MOE_ROUTING_HASH = 1 };
+enum { MOE_BIAS_LOGIT = 0, MOE_BIAS_SELECT = 1 };
 
 /* Supported shapes: d_model and d_ff multiples of 128 (>= 128, <= 65536),
  * 1 <= n_experts <= 1024, 1 <= top_k <= min(8, n_experts),
@@ -77,6 +79,10 @@ typedef struct moe_config {
   float route_scale;    /* multiplies the routed sum only (1.0 = plain sum) */
   float swiglu_limit;   /* L; <= 0 disables the clamp */
   float norm_eps;       /* eps of the input RMSNorm (used when moe_args_t.norm_w != NULL); >= 0 */
+  int32_t bias_mode;    /* router_bias: 0 (MOE_BIAS_LOGIT) added to the logits, so it shifts both the
+                           selection and the gates; 1 (MOE_BIAS_SELECT) added to the scores for the
+                           top-k selection only, the gates use the unbiased scores.  The pages name the
+                           bias (gate.bias, ds4 issue "Loader spec") but not its use. */
 } moe_config_t;
 
 /*

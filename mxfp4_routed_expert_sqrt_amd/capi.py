@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mxfp4.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_ROUTING_TOPK, MOE_ROUTING_HASH = 0, 1
+MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_MAX_ROWS = 1 << 20
 
 c_i32, c_i64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -20,7 +21,8 @@ c_i32, c_i64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_flo
 
 class MoeConfig(ctypes.Structure):
     _fields_ = [("d_model", c_i32), ("d_ff", c_i32), ("n_experts", c_i32), ("top_k", c_i32), ("routing", c_i32),
-                ("has_shared", c_i32), ("route_scale", c_f32), ("swiglu_limit", c_f32), ("norm_eps", c_f32)]
+                ("has_shared", c_i32), ("route_scale", c_f32), ("swiglu_limit", c_f32), ("norm_eps", c_f32),
+                ("bias_mode", c_i32)]
 
 
 class MoeWeights(ctypes.Structure):

@@ -297,7 +297,8 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
 // order).
 template <int NC>
 __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's logits */, int r, int E, int k,
-                                           int routing, const int32_t* __restrict__ token_ids,
+                                           int routing, const float* __restrict__ sel_bias,
+                                           const int32_t* __restrict__ token_ids,
                                            const int32_t* __restrict__ tid2eid, int64_t vocab,
                                            int32_t* __restrict__ idx, float* __restrict__ gates,
                                            int32_t* sel_lds) {
@@ -305,11 +306,13 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
   int sel[kMaxTopK];
   float zsel[kMaxTopK];
   if (routing == 0) {
+    // keys: the logit (it orders like the score), or with a selection-only
+    // bias the biased score itself
     uint64_t key[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = c * 64 + lane;
-      key[c] = e < E ? sel_key(zr[e], e) : 0ull;
+      key[c] = e >= E ? 0ull : sel_bias ? sel_key(router_score(zr[e]) + sel_bias[e], e) : sel_key(zr[e], e);
     }
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
@@ -321,7 +324,7 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
 #pragma unroll
         for (int c = 0; c < NC; ++c) key[c] = key[c] == m ? 0ull : key[c];
         sel[j] = (int)~(uint32_t)m;
-        zsel[j] = logit_of_code((uint32_t)(m >> 32));
+        zsel[j] = sel_bias ? zr[sel[j]] : logit_of_code((uint32_t)(m >> 32));
       }
     }
   } else {
@@ -449,7 +452,7 @@ __device__ __forceinline__ void write_groups(int rows, const int32_t* s_cnt, con
 // on a device-scope counter (cleared by the prologue launch); the workgroup
 // that finishes last sees every workgroup's results and runs step 2.
 __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
-    const float* __restrict__ z, int n_split, const float* __restrict__ bias, int n_rows, int E, int k, int routing, const int32_t* __restrict__ token_ids,
+    const float* __restrict__ z, int n_split, const float* __restrict__ bias, int bias_mode, int n_rows, int E, int k, int routing, const int32_t* __restrict__ token_ids,
     const int32_t* __restrict__ tid2eid, int64_t vocab, int32_t* __restrict__ idx, float* __restrict__ gates,
     int has_shared, int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ inv, int group_rows, Group* __restrict__ groups, int32_t* __restrict__ n_groups,
@@ -465,9 +468,12 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
   const int b = blockIdx.x, nb = gridDim.x;
   const int Ep = (E + 3) & ~3;
   const int P = n_rows * k;
+  const float* lbias = bias_mode == 0 ? bias : nullptr;
+  const float* sbias = bias_mode == 1 ? bias : nullptr;
 
   // logits of the workgroup's rows into LDS: the split-K partials (stride
-  // n_rows*E) added in split order, then the bias
+  // n_rows*E) added in split order, then the bias when it is a logit bias
+  // (bias_mode 0; a selection-only bias enters the selection keys instead)
   {
     // the block's logits are contiguous in each partial and start on a 16-byte
     // boundary (16*b*E floats; the partial stride is padded to 4 floats)
@@ -487,12 +493,12 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
         }
         const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s_z[i + j] = bias ? vv[j] + bias[(i + j) % E] : vv[j];
+        for (int j = 0; j < 4; ++j) s_z[i + j] = lbias ? vv[j] + lbias[(i + j) % E] : vv[j];
       } else {
         for (int j = i; j < cnt; ++j) {
           float v = zb[j];
           for (int sp = 1; sp < n_split; ++sp) v += zb[sp * zstride + j];
-          s_z[j] = bias ? v + bias[j % E] : v;
+          s_z[j] = lbias ? v + lbias[j % E] : v;
         }
       }
     }
@@ -505,15 +511,15 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
     const float* zr = s_z + wave * E;
     int32_t* sl = s_sel + wave * k;
     if (E <= 64)
-      select_row<1>(zr, r, E, k, routing, token_ids, tid2eid, vocab, idx, gates, sl);
+      select_row<1>(zr, r, E, k, routing, sbias, token_ids, tid2eid, vocab, idx, gates, sl);
     else if (E <= 128)
-      select_row<2>(zr, r, E, k, routing, token_ids, tid2eid, vocab, idx, gates, sl);
+      select_row<2>(zr, r, E, k, routing, sbias, token_ids, tid2eid, vocab, idx, gates, sl);
     else if (E <= 256)
-      select_row<4>(zr, r, E, k, routing, token_ids, tid2eid, vocab, idx, gates, sl);
+      select_row<4>(zr, r, E, k, routing, sbias, token_ids, tid2eid, vocab, idx, gates, sl);
     else if (E <= 512)
-      select_row<8>(zr, r, E, k, routing, token_ids, tid2eid, vocab, idx, gates, sl);
+      select_row<8>(zr, r, E, k, routing, sbias, token_ids, tid2eid, vocab, idx, gates, sl);
     else
-      select_row<kMaxExpertsPerLane>(zr, r, E, k, routing, token_ids, tid2eid, vocab, idx, gates, sl);
+      select_row<kMaxExpertsPerLane>(zr, r, E, k, routing, sbias, token_ids, tid2eid, vocab, idx, gates, sl);
   }
   __syncthreads();
   const int q0 = b * kRouteWaves * k;
@@ -655,7 +661,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
 // thread); above it the scatter is its own launch.
 constexpr int kScatterInBlockMax = 8 * kRouteThreads;
 
-hipError_t launch_select_route(const float* z, const float* bias, int d, int n_rows, int E, int k, int routing, const int32_t* token_ids,
+hipError_t launch_select_route(const float* z, const float* bias, int bias_mode, int d, int n_rows, int E, int k, int routing, const int32_t* token_ids,
                                const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, int has_shared,
                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, int group_rows,
                                Group* groups, int32_t* n_groups, int32_t* hist, int32_t* done, hipStream_t stream) {
@@ -669,7 +675,7 @@ hipError_t launch_select_route(const float* z, const float* bias, int d, int n_r
   const int here = P <= kScatterInBlockMax;
   const size_t lds = sizeof(float) * kRouteWaves * E;
   hipLaunchKernelGGL(select_route_kernel, dim3((unsigned)route_workgroups(n_rows)), dim3(kRouteThreads), lds, stream,
-                     z, logits_splits(n_rows, E, d), bias, n_rows, E, k, routing, token_ids, tid2eid, vocab, idx, gates, has_shared, counts, offsets,
+                     z, logits_splits(n_rows, E, d), bias, bias_mode, n_rows, E, k, routing, token_ids, tid2eid, vocab, idx, gates, has_shared, counts, offsets,
                      perm, inv, group_rows, groups, n_groups, hist, done, here);
   if (!here) {
     hipError_t err = hipGetLastError();

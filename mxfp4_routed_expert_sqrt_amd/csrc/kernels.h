@@ -82,7 +82,8 @@ __host__ __device__ inline size_t logits_partial_stride(int n_rows, int E) {
   return ((size_t)n_rows * E + 3) & ~(size_t)3;
 }
 
-hipError_t launch_select_route(const float* z, const float* bias, int d, int n_rows, int E, int k, int routing, const int32_t* token_ids,
+// bias_mode 0: bias added to the logits; 1: added to the scores for the selection only
+hipError_t launch_select_route(const float* z, const float* bias, int bias_mode, int d, int n_rows, int E, int k, int routing, const int32_t* token_ids,
                                const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, int has_shared,
                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, int group_rows,
                                Group* groups, int32_t* n_groups, int32_t* hist, int32_t* done, hipStream_t stream);

@@ -66,6 +66,7 @@ int check_config(const moe_config_t* c) {
   if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts) return MOE_ERR_UNSUPPORTED;
   if (!(c->route_scale == c->route_scale) || !(c->swiglu_limit == c->swiglu_limit)) return MOE_ERR_INVALID;
   if (!(c->norm_eps >= 0.f) || c->norm_eps == INFINITY) return MOE_ERR_INVALID;
+  if (c->bias_mode != 0 && c->bias_mode != 1) return MOE_ERR_INVALID;
   return MOE_OK;
 }
 
@@ -199,7 +200,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
       hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
-  if ((err = launch_select_route(z, a.router_bias, d, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, c.has_shared,
+  if ((err = launch_select_route(z, a.router_bias, c.bias_mode, d, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, c.has_shared,
                                  counts, offsets, perm, inv, rows, groups, n_groups, hist, done, stream)) != hipSuccess)
     return MOE_ERR_HIP;
 

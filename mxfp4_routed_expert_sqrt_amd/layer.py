@@ -13,12 +13,13 @@ def _ptr(t):
 
 
 def make_config(shape: MoEShape, has_shared: bool = True, route_scale=None, swiglu_limit=None,
-                norm_eps: float = 1e-6) -> capi.MoeConfig:
+                norm_eps: float = 1e-6, bias_mode: int = capi.MOE_BIAS_LOGIT) -> capi.MoeConfig:
     return capi.MoeConfig(shape.d_model, shape.d_ff, shape.n_experts, shape.top_k,
                           capi.MOE_ROUTING_TOPK if shape.routing == "topk" else capi.MOE_ROUTING_HASH,
                           1 if has_shared else 0,
                           float(shape.route_scale if route_scale is None else route_scale),
-                          float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit), float(norm_eps))
+                          float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit), float(norm_eps),
+                          int(bias_mode))
 
 
 def pack_mxfp4(q: torch.Tensor, s: torch.Tensor, rows: int, K: int, stream=None, out=None):
@@ -88,12 +89,13 @@ class PackedExperts:
 
 class MoELayer:
     def __init__(self, shape: MoEShape, router_w, experts, device="cuda", router_bias=None,
-                 has_shared: bool = True, route_scale=None, swiglu_limit=None, norm_w=None, norm_eps: float = 1e-6):
+                 has_shared: bool = True, route_scale=None, swiglu_limit=None, norm_w=None, norm_eps: float = 1e-6,
+                 bias_mode: int = capi.MOE_BIAS_LOGIT):
         """experts: natural-layout arrays (dict, packed here) or an already packed PackedExperts.
         norm_w: optional bf16 bit patterns [d] of the input RMSNorm weight (the layer then normalises x)."""
         self.shape = shape
         self.device = torch.device(device)
-        self.cfg = make_config(shape, has_shared, route_scale, swiglu_limit, norm_eps)
+        self.cfg = make_config(shape, has_shared, route_scale, swiglu_limit, norm_eps, bias_mode)
         self.norm_w = None if norm_w is None else \
             torch.from_numpy(np.ascontiguousarray(norm_w, dtype=np.uint16).view(np.int16)).to(self.device)
         self.router_w = torch.as_tensor(np.ascontiguousarray(router_w, dtype=np.float32)).to(self.device)

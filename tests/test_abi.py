@@ -70,7 +70,8 @@ def test_workspace_size_arithmetic():
     ("top_k", 0, capi.MOE_ERR_UNSUPPORTED), ("top_k", 9, capi.MOE_ERR_UNSUPPORTED),
     ("routing", 2, capi.MOE_ERR_INVALID), ("has_shared", 3, capi.MOE_ERR_INVALID),
     ("norm_eps", -1e-6, capi.MOE_ERR_INVALID), ("norm_eps", float("inf"), capi.MOE_ERR_INVALID),
-    ("norm_eps", float("nan"), capi.MOE_ERR_INVALID),
+    ("norm_eps", float("nan"), capi.MOE_ERR_INVALID), ("bias_mode", 2, capi.MOE_ERR_INVALID),
+    ("bias_mode", -1, capi.MOE_ERR_INVALID),
 ])
 def test_bad_config_rejected(field, value, status):
     cfg = make_config(SHAPES["tiny"])

@@ -13,7 +13,7 @@ torch = pytest.importorskip("torch")
 
 from mxfp4_routed_expert_sqrt_amd.configs import SHAPES, MoEShape  # noqa: E402
 from mxfp4_routed_expert_sqrt_amd.layer import MoELayer, PackedExperts  # noqa: E402
-from tests.inputs import norm_workload, oracle_forward, workload  # noqa: E402
+from tests.inputs import norm_workload, oracle_forward, selection_bias_workload, workload  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -60,6 +60,8 @@ def run_gpu(wl, has_shared=True, **cfg_kw):
     dev = torch.device("cuda")
     if "norm_w" in wl:
         cfg_kw = dict(cfg_kw, norm_w=wl["norm_w"], norm_eps=wl["norm_eps"])
+    if "bias_mode" in wl:
+        cfg_kw = dict(cfg_kw, bias_mode=wl["bias_mode"])
     layer = MoELayer(sh, wl["router_w"], packed_for(wl, has_shared), dev, router_bias=wl["bias"],
                      has_shared=has_shared, **cfg_kw)
     x = torch.from_numpy(wl["x"].view(np.int16)).to(dev).view(torch.bfloat16)
@@ -157,6 +159,20 @@ def test_input_norm_and_residual(name, n_sample):
     ref = oracle_forward(wl, rows=rows)
     check_routing(gpu, ref, name + "+norm", gate_rtol=GATE_RTOL_NORM)
     check_out(gpu["out"] if rows is None else gpu["out"][rows], ref["out"], name + "+norm")
+
+
+# ------------------------------------------------------ selection-only bias
+
+@pytest.mark.parametrize("name,n_sample", [("tiny", 0), ("verify512", 32), ("prefill8192", 16), ("e384", 0)])
+def test_selection_only_router_bias(name, n_sample):
+    # the bias shifts which experts are chosen (k largest score + bias) but not the gates
+    shape = EDGE["e384_k6"] if name == "e384" else name
+    wl = selection_bias_workload(shape)
+    gpu, *_ = run_gpu(wl)
+    rows = None if n_sample == 0 else sample_rows(wl["shape"].n_rows, n_sample)
+    ref = oracle_forward(wl, rows=rows)
+    check_routing(gpu, ref, wl["shape"].name + "+selbias")
+    check_out(gpu["out"] if rows is None else gpu["out"][rows], ref["out"], wl["shape"].name + "+selbias")
 
 
 # ---------------------------------------------------------------- edge cases
