@@ -126,7 +126,8 @@ typedef struct moe_args {
   int32_t* offsets;
   int32_t* perm;
   int32_t* inv;
-  void* workspace;            /* device scratch, 256-byte aligned, >= moe_workspace_size() */
+  void* workspace;            /* device scratch, 256-byte aligned, >= moe_workspace_size(); must not
+                                 overlap out, x, router_w, router_bias, norm_w or residual */
   size_t workspace_bytes;
   /* Optional stage timing (NULL to skip): MOE_N_STAGE_EVENTS hipEvent_t handles
    * created by the caller.  Event i is recorded on `stream` just before stage i

@@ -163,6 +163,13 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   if (!a.workspace || a.workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned(a.workspace, 256)) return MOE_ERR_INVALID;
   if (overlap(a.out, out_bytes, a.workspace, L.total)) return MOE_ERR_INVALID;
+  // inputs read after the workspace is first written must not lie inside it
+  if (overlap(a.x, out_bytes, a.workspace, L.total) ||
+      overlap(a.router_w, (size_t)E * d * 4, a.workspace, L.total) ||
+      (a.router_bias && overlap(a.router_bias, (size_t)E * 4, a.workspace, L.total)) ||
+      (a.norm_w && overlap(a.norm_w, (size_t)d * 2, a.workspace, L.total)) ||
+      (a.residual && overlap(a.residual, out_bytes, a.workspace, L.total)))
+    return MOE_ERR_INVALID;
 
   hipStream_t stream = (hipStream_t)stream_;
   uint8_t* ws = (uint8_t*)a.workspace;

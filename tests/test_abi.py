@@ -115,6 +115,9 @@ def test_invalid_arguments_return_before_any_hip_call():
     a = _valid_args(cfg, N); a.norm_w = 0xA0000008; cases.append((a, capi.MOE_ERR_INVALID))   # misaligned
     a = _valid_args(cfg, N); a.residual = 0xB0000004; cases.append((a, capi.MOE_ERR_INVALID))  # misaligned
     a = _valid_args(cfg, N); a.residual = a.out + 512; cases.append((a, capi.MOE_ERR_INVALID))  # partial overlap
+    a = _valid_args(cfg, N); a.x = a.workspace + 256; cases.append((a, capi.MOE_ERR_INVALID))     # x in workspace
+    a = _valid_args(cfg, N); a.router_w = a.workspace; cases.append((a, capi.MOE_ERR_INVALID))
+    a = _valid_args(cfg, N); a.residual = a.workspace + 4096; cases.append((a, capi.MOE_ERR_INVALID))
     for a, st in cases:
         assert capi.moe_layer_forward(cfg, a, None) == st
     hcfg = make_config(SHAPES["hash2048"])
@@ -141,3 +144,43 @@ def test_pack_rejects_bad_arguments():
     assert capi.moe_pack_mxfp4(0x1008, 0x2000, 1, 16, 128, 0x3000, 0x4000, None) == capi.MOE_ERR_INVALID
     assert capi.moe_pack_mxfp4(0x1000, 0x2000, 1, 16, 128, 0x1200, 0x4000, None) == capi.MOE_ERR_INVALID  # overlap
     assert L is not None
+
+
+def test_binding_structs_match_the_c_header(tmp_path):
+    # offsets and sizes of every field of the three ABI structs, as the C compiler lays them out
+    # from include/moe_mxfp4.h, against the ctypes mirrors; and the header's constants
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no host C compiler")
+    structs = {"moe_config_t": capi.MoeConfig, "moe_weights_t": capi.MoeWeights, "moe_args_t": capi.MoeArgs}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "moe_mxfp4.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    consts = ["MOE_OK", "MOE_ERR_INVALID", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
+              "MOE_ROUTING_TOPK", "MOE_ROUTING_HASH", "MOE_BIAS_LOGIT", "MOE_BIAS_SELECT", "MOE_MAX_ROWS",
+              "MOE_N_STAGES", "MOE_N_STAGE_EVENTS", "MOE_MXFP4_VERSION"]
+    for c in consts:
+        lines.append(f'  printf("const {c} %ld\\n", (long)({c}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-std=c99", "-I", inc, "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    seen = 0
+    for line in filter(None, out):
+        kind, name, value = line.split()
+        value = int(value)
+        if kind == "const":
+            want = getattr(capi, name) if name != "MOE_MXFP4_VERSION" else capi.moe_version()
+            assert value == want, name
+        elif name == "sizeof":
+            assert value == ctypes.sizeof(structs[kind]), kind
+        else:
+            assert value == getattr(structs[kind], name).offset, f"{kind}.{name}"
+        seen += 1
+    assert seen == len(consts) + sum(len(c._fields_) + 1 for c in structs.values())
