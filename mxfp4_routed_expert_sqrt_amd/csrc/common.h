@@ -107,24 +107,22 @@ __device__ __forceinline__ int fp6_exponent(float amax) {
   return e;
 }
 
-// E2M3 code of f (|f| <= 7.5), rounded to nearest (ties to even mantissa).
-__device__ __forceinline__ uint32_t e2m3_code(float f) {
+// E2M3 code of f, rounded to nearest (ties to even mantissa), and the value
+// it encodes.  With E = [|f| >= 2] + [|f| >= 4] (the binade; 0 also for the
+// subnormal range, whose step 1/8 equals binade 0's) the code is
+// 8E + rint(|f| * 2^(3-E)): |f| * 2^(3-E) is exact, so this is the textbook
+// piecewise rounding without branches; a carry out of the mantissa lands on
+// the next binade's code.  Saturates at 7.5 (code 31); the callers scale f
+// into [-7.5, 7.5].
+__device__ __forceinline__ uint32_t e2m3_round(float f, float* value) {
   const float a = fabsf(f);
-  int code;
-  if (a < 1.f) {
-    code = (int)__builtin_rintf(a * 8.f);  // subnormal m/8; m = 8 is the code of 1.0
-  } else {
-    const int E = a >= 4.f ? 2 : (a >= 2.f ? 1 : 0);
-    code = ((E + 1) << 3) + (int)__builtin_rintf((a * ldexpf(1.f, -E) - 1.f) * 8.f);
-  }
+  const bool c2 = a >= 2.f, c4 = a >= 4.f;
+  const float q = __builtin_rintf(a * (c4 ? 2.f : (c2 ? 4.f : 8.f)));
+  int code = (int)q + (c4 ? 16 : (c2 ? 8 : 0));
   code = code > 31 ? 31 : code;
+  const float mag = fminf(q * (c4 ? 0.5f : (c2 ? 0.25f : 0.125f)), 7.5f);
+  *value = f < 0.f ? -mag : mag;
   return (uint32_t)code | (f < 0.f ? 0x20u : 0u);
-}
-
-__device__ __forceinline__ float e2m3_value(uint32_t code) {
-  const int e = (code >> 3) & 3, m = code & 7;
-  const float mag = e == 0 ? (float)m * 0.125f : ldexpf(1.f + (float)m * 0.125f, e - 1);
-  return (code & 0x20u) ? -mag : mag;
 }
 
 template <int kOff>

@@ -316,10 +316,13 @@ __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Group g, i
 // same rows of the up matrix: 16*TPM features per wave, 16*TPM*WAVES per work
 // unit.
 
-// The 24-bit run of four E2M3 codes of v[0..3] * inv (value i at bits 6i).
-__device__ __forceinline__ uint32_t e2m3_run4(const float* v, float inv) {
-  return e2m3_code(v[0] * inv) | (e2m3_code(v[1] * inv) << 6) | (e2m3_code(v[2] * inv) << 12) |
-         (e2m3_code(v[3] * inv) << 18);
+// The 24-bit run of four E2M3 codes of v[0..3] * inv (value i at bits 6i);
+// rv[i] = the value of code i (unscaled).
+__device__ __forceinline__ uint32_t e2m3_run4(const float* v, float inv, float* rv) {
+  uint32_t run = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) run |= e2m3_round(v[i] * inv, &rv[i]) << (6 * i);
+  return run;
 }
 
 // Tall units write h as the two-term FP6 split (the x split's FP6 layout, K =
@@ -336,10 +339,10 @@ __device__ __forceinline__ void write_h_fp6(const ExpertArgs& a, const Group g, 
   float amax2 = 0.f;
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
-    run[0][hh] = e2m3_run4(h + 4 * hh, inv1);
+    run[0][hh] = e2m3_run4(h + 4 * hh, inv1, res + 4 * hh);
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      res[4 * hh + ii] = h[4 * hh + ii] - e2m3_value((run[0][hh] >> (6 * ii)) & 63u) * sc1;
+      res[4 * hh + ii] = h[4 * hh + ii] - res[4 * hh + ii] * sc1;
       amax2 = fmaxf(amax2, fabsf(res[4 * hh + ii]));
     }
   }
@@ -347,8 +350,9 @@ __device__ __forceinline__ void write_h_fp6(const ExpertArgs& a, const Group g, 
   amax2 = shfl_xor_max<32>(amax2);
   const int e2 = fp6_exponent(amax2);
   const float inv2 = ldexpf(1.f, -e2);
+  float unused[8];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) run[1][hh] = e2m3_run4(res + 4 * hh, inv2);
+  for (int hh = 0; hh < 2; ++hh) run[1][hh] = e2m3_run4(res + 4 * hh, inv2, unused + 4 * hh);
   // r[t][hh][q]: run of lane col + 16q
   uint32_t r[2][2][4];
 #pragma unroll
@@ -438,7 +442,7 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
           gv = fminf(gv, L);
           uv = fminf(fmaxf(uv, -L), L);
         }
-        h[tt * 4 + ii] = gv / (1.f + __expf(-gv)) * uv;
+        h[tt * 4 + ii] = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;  // silu with a 1-ulp reciprocal
       }
     float amax = 0.f;
 #pragma unroll

@@ -64,24 +64,17 @@ __device__ __forceinline__ size_t split_scale_offset(int term, int blk, int n_sg
 // = the 32-block 4ks+g.  Scales as for the FP8 split.
 
 // E2M3 codes of v[i] * inv for 32 values, packed as the operand bitstream
-// (6 dwords, value i at bits 6i..6i+5).
-__device__ __forceinline__ void pack_fp6_block(const float* v, float inv, uint32_t* q /*6 dwords*/) {
+// (6 dwords, value i at bits 6i..6i+5); rv[i] = the value of code i (unscaled).
+__device__ __forceinline__ void pack_fp6_block(const float* v, float inv, uint32_t* q /*6 dwords*/, float* rv) {
 #pragma unroll
   for (int w = 0; w < 6; ++w) q[w] = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const uint32_t c = e2m3_code(v[i] * inv);
+    const uint32_t c = e2m3_round(v[i] * inv, &rv[i]);
     const int bit = 6 * i, w = bit >> 5, sh = bit & 31;
     q[w] |= c << sh;
     if (sh > 26) q[w + 1] |= c >> (32 - sh);
   }
-}
-
-__device__ __forceinline__ float fp6_code_at(const uint32_t* q, int i) {
-  const int bit = 6 * i, w = bit >> 5, sh = bit & 31;
-  uint32_t c = q[w] >> sh;
-  if (sh > 26) c |= q[w + 1] << (32 - sh);
-  return e2m3_value(c & 63u);
 }
 
 __device__ __forceinline__ void split_block32_fp6(const float* v, uint32_t* q /*12 dwords*/, int* e1_out,
@@ -90,17 +83,18 @@ __device__ __forceinline__ void split_block32_fp6(const float* v, uint32_t* q /*
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
   const int e1 = fp6_exponent(amax);
-  pack_fp6_block(v, ldexpf(1.f, -e1), q);
-  const float sc1 = ldexpf(1.f, e1);
   float r[32];
+  pack_fp6_block(v, ldexpf(1.f, -e1), q, r);
+  const float sc1 = ldexpf(1.f, e1);
   float amax2 = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    r[i] = v[i] - fp6_code_at(q, i) * sc1;
+    r[i] = v[i] - r[i] * sc1;
     amax2 = fmaxf(amax2, fabsf(r[i]));
   }
   const int e2 = fp6_exponent(amax2);
-  pack_fp6_block(r, ldexpf(1.f, -e2), q + 6);
+  float unused[32];
+  pack_fp6_block(r, ldexpf(1.f, -e2), q + 6, unused);
   *e1_out = e1;
   *e2_out = e2;
 }
