@@ -28,10 +28,6 @@
 
 namespace moe {
 
-__device__ __forceinline__ size_t split_scale_offset_h(int term, int blk, int n_sg) {
-  const int ks = blk >> 2;
-  return (size_t)(((term * n_sg + (ks >> 2)) * 4 + (blk & 3)) * 4 + (ks & 3));
-}
 
 template <int J, bool FP6 = false>
 __device__ __forceinline__ v4f mfma_fp4_fp8(const u32x4& a, const v8i& b, const v4f& c, uint32_t sa, uint32_t sb) {
@@ -380,8 +376,8 @@ __device__ __forceinline__ void write_h_fp6(const ExpertArgs& a, const Group g, 
       *(u32x4*)(dst + 16 * bb) = u32x4{D[0], D[1], D[2], D[3]};
     if (grp == 0) {
       uint8_t* srow = a.hs + p * split_s_row_bytes(a.R);
-      srow[split_scale_offset_h(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
-      srow[split_scale_offset_h(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
+      srow[split_scale_offset(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
+      srow[split_scale_offset(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
     }
   }
 }
@@ -487,8 +483,8 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
       }
       if (grp == 0) {
         uint8_t* srow = a.hs + p * split_s_row_bytes(R);
-        srow[split_scale_offset_h(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
-        srow[split_scale_offset_h(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
+        srow[split_scale_offset(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
+        srow[split_scale_offset(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
       }
     }
   }

@@ -34,6 +34,14 @@ __host__ __device__ inline size_t packed_s_bytes(int rows, int K) {
 }
 // Two-term FP8 split of activation rows of length K.
 __host__ __device__ inline size_t split_q_row_bytes(int K) { return (size_t)K * 2; }
+// Byte of the scale of 32-block blk, term `term`, in an activation split's
+// scale row ([term][n_sg][4][4]: lane group g of a k-step reads the scales of
+// its block for 4 consecutive k-steps as one dword).
+__host__ __device__ inline size_t split_scale_offset(int term, int blk, int n_sg) {
+  const int ks = blk >> 2;
+  return (size_t)(((term * n_sg + (ks >> 2)) * 4 + (blk & 3)) * 4 + (ks & 3));
+}
+
 // FP6 split rows (tall units) use 192 bytes per 128-wide k-step of the same row, 96 per term.
 constexpr int kFp6StepBytes = 192, kFp6TermBytes = 96;
 __host__ __device__ inline size_t split_s_row_bytes(int K) {

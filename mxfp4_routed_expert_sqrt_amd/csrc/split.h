@@ -48,10 +48,6 @@ __device__ __forceinline__ void split_block32(const float* v, uint32_t* q /*16 d
   *e2_out = e2;
 }
 
-__device__ __forceinline__ size_t split_scale_offset(int term, int blk, int n_sg) {
-  const int ks = blk >> 2;
-  return (size_t)(((term * n_sg + (ks >> 2)) * 4 + (blk & 3)) * 4 + (ks & 3));
-}
 
 // ---------------------------------------------------------------------------
 // Two-term FP6 (E2M3) split, used for batches of tall work units: v ~= q1 *
