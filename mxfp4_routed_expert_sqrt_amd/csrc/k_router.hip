@@ -224,10 +224,10 @@ hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d,
 // ---------------------------------------------------------------------------
 // Scores and selection, one wave per row.  s = sqrt(softplus(z)) with
 // softplus(z) = max(z,0) + log1p(exp(-|z|)).  Top-k mode takes the k largest
-// scores (equal scores: lower expert id first) by k rounds of a wave argmax;
-// hash mode takes tid2eid[token_ids[r]].  Selected ids are written ascending
-// with gates = s / sum(s).  s increases strictly with z, so the argmax runs
-// on the logits and only the k selected scores are computed.
+// scores (equal scores: lower expert id first) by a threshold search; hash
+// mode takes tid2eid[token_ids[r]].  Selected ids are written ascending with
+// gates = s / sum(s).  s increases strictly with z, so the selection runs on
+// the logits and only the k selected scores are computed.
 
 __device__ __forceinline__ float router_score(float zv) {
   return sqrtf(fmaxf(zv, 0.f) + log1pf(expf(-fabsf(zv))));
@@ -245,56 +245,24 @@ __device__ __forceinline__ uint32_t logit_code(float z) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float logit_of_code(uint32_t c) {
-  return __uint_as_float((c & 0x80000000u) ? (c & 0x7fffffffu) : ~c);
-}
-
-// Selection keys: the logit code in the high word and the complemented expert
-// id in the low word, so that of two equal logits the lower id has the larger
-// key.  Every real candidate has a key > 0; a taken or absent candidate is 0.
-__device__ __forceinline__ uint64_t sel_key(float z, int e) {
-  return ((uint64_t)logit_code(z) << 32) | (uint32_t)~e;
-}
-
-// Largest value of the wave, uniform: max with the value of another lane by
-// DPP within rows of 16 lanes (xor 1, xor 2, rotate 4, rotate 8), then row 0
-// -> 1 and 2 -> 3 (row_bcast:15) and rows 0-1 -> 2-3 (row_bcast:31), so lane
-// 63 ends with the maximum.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
-  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtrl, kRowMask, 0xF, false);
-  return o > v ? o : v;
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = dpp_max<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-  v = dpp_max<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-  v = dpp_max<0x124, 0xF>(v);  // row_ror:4
-  v = dpp_max<0x128, 0xF>(v);  // row_ror:8
-  v = dpp_max<0x142, 0xA>(v);  // row_bcast:15
-  v = dpp_max<0x143, 0xC>(v);  // row_bcast:31
-  return __builtin_amdgcn_readlane(v, 63);
-}
-
-// Largest 64-bit key of the wave: the largest high word, then the largest
-// low word among the lanes holding it.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
-  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
-  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // NC = score slots per lane the code is unrolled for (expert c*64 + lane in
 // slot c); E <= 64*NC.  Instantiated for 1, 2, 4, 8 and 16 slots so that the
 // selection runs over no more slots than E needs.
 //
-// Top-k mode: k rounds of (lane-local max key, wave max key); the winner's key
-// is zeroed, so the k winners are distinct and come out by descending score
-// (equal scores: lower id first).  Hash mode: the ids tid2eid[token_ids[r]].
-// Lane j < k then takes the j-th selected id; its output slot is its rank in
-// (id, j) order, so the ids are written ascending (a repeated hash id keeps
-// table order), and gate = score / (sum of the k scores, added in selection
-// order).
+// Top-k mode, with every candidate reduced to one 32-bit order-preserving code
+// (of the logit, or with a selection-only bias of the biased score; absent
+// experts are 0, below every real code):
+//  - threshold T = the k-th largest code, as the largest T with at least k
+//    codes >= T, found bit by bit from the top (32 steps, each a compare per
+//    slot and a popcount of the ballots: no cross-lane shuffles);
+//  - the selection is every code > T plus, of the codes equal to T, the
+//    lowest ids (so equal values favour the lower id) up to k in all;
+//  - the selected lanes write their ids, ascending (slot-major, then lane),
+//    to the wave's k LDS slots.
+// Hash mode: the ids tid2eid[token_ids[r]], placed by their rank in (id, table
+// position) order, so a repeated id keeps table order.
+// Lane j < k then holds the j-th smallest selected id, scores it, and the gate
+// is score / (sum of the k scores, added in ascending id order).
 template <int NC>
 __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's logits */, int r, int E, int k,
                                            int routing, const float* __restrict__ sel_bias,
@@ -303,29 +271,47 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
                                            int32_t* __restrict__ idx, float* __restrict__ gates,
                                            int32_t* sel_lds) {
   const int lane = threadIdx.x & 63;
-  int sel[kMaxTopK];
-  float zsel[kMaxTopK];
   if (routing == 0) {
-    // keys: the logit (it orders like the score), or with a selection-only
-    // bias the biased score itself
-    uint64_t key[NC];
+    uint32_t code[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = c * 64 + lane;
-      key[c] = e >= E ? 0ull : sel_bias ? sel_key(router_score(zr[e]) + sel_bias[e], e) : sel_key(zr[e], e);
+      code[c] = e >= E ? 0u : logit_code(sel_bias ? router_score(zr[e]) + sel_bias[e] : zr[e]);
+    }
+    uint32_t T = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) cnt += __popcll(__ballot(code[c] >= cand));
+      T = cnt >= k ? cand : T;
+    }
+    uint64_t take[NC];
+    int need = k;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      take[c] = __ballot(code[c] > T);
+      need -= __popcll(take[c]);
     }
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < k) {
-        uint64_t m = key[0];
-#pragma unroll
-        for (int c = 1; c < NC; ++c) m = key[c] > m ? key[c] : m;
-        m = wave_max_key(m);
-#pragma unroll
-        for (int c = 0; c < NC; ++c) key[c] = key[c] == m ? 0ull : key[c];
-        sel[j] = (int)~(uint32_t)m;
-        zsel[j] = sel_bias ? zr[sel[j]] : logit_of_code((uint32_t)(m >> 32));
+    for (int c = 0; c < NC; ++c) {
+      uint64_t m = __ballot(code[c] == T);
+      while (need > 0 && m != 0ull) {
+        const uint64_t low = m & (~m + 1ull);
+        take[c] |= low;
+        m ^= low;
+        --need;
       }
+    }
+    int base = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if ((take[c] >> lane) & 1ull) {
+        const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(take[c] >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)take[c], 0u));
+        sel_lds[base + below] = c * 64 + lane;
+      }
+      base += __popcll(take[c]);
     }
   } else {
     // Table entries must be valid (ids in [0, E)); an out-of-range token id
@@ -333,36 +319,30 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
     // unspecified routing but never an out-of-bounds access.
     const int64_t t = min(max((int64_t)token_ids[r], (int64_t)0), vocab - 1);
     const int32_t* row = tid2eid + t * k;
+    int sel[kMaxTopK];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j < k) {
-        sel[j] = min(max(row[j], 0), E - 1);
-        zsel[j] = zr[sel[j]];
-      }
-    }
+    for (int j = 0; j < kMaxTopK; ++j) sel[j] = j < k ? min(max(row[j], 0), E - 1) : 0;
+    int my = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) my = (j < k && lane == j) ? sel[j] : my;
+    int rank = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxTopK; ++i)
+      if (i < k) rank += (sel[i] < my || (sel[i] == my && i < lane)) ? 1 : 0;
+    if (lane < k) sel_lds[rank] = my;
   }
-  // lane j < k scores the j-th selection; the sum runs in selection order
-  int my_id = 0;
-  float my_z = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j)
-    if (j < k && lane == j) {
-      my_id = sel[j];
-      my_z = zsel[j];
-    }
-  const float my_sv = router_score(my_z);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int my_id = lane < k ? sel_lds[lane] : 0;
+  const float my_sv = router_score(lane < k ? zr[my_id] : 0.f);
   float sum = 0.f;
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j)
     if (j < k) sum += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(my_sv), j));
-  int rank = 0;
-#pragma unroll
-  for (int i = 0; i < kMaxTopK; ++i)
-    if (i < k) rank += (sel[i] < my_id || (sel[i] == my_id && i < lane)) ? 1 : 0;
   if (lane < k) {
-    idx[(size_t)r * k + rank] = my_id;
-    gates[(size_t)r * k + rank] = my_sv / sum;
-    sel_lds[rank] = my_id;
+    idx[(size_t)r * k + lane] = my_id;
+    gates[(size_t)r * k + lane] = my_sv / sum;
   }
 }
 
@@ -381,8 +361,8 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
 //     over segments of rows, a scan over the segments, then a second pass
 //     that overwrites each row with its exclusive base.  The counts, their
 //     exclusive scan (offsets), the scatter of perm/inv and the work list of
-//     the grouped GEMMs (groups of <= 16, 32 or 64 rows of one expert, then the shared
-//     expert's rows) follow.
+//     the grouped GEMMs (groups of <= 16, 32 or 64 rows of one expert, and
+//     the shared expert's rows) follow.
 // Histogram rows are E rounded up to a multiple of 4 ints wide, so both scan
 // passes move 16-byte columns.
 constexpr int kRouteThreads = 1024;
@@ -402,11 +382,19 @@ __device__ __forceinline__ int wave_match_rank(int e, bool act, int lane, bool* 
 }
 
 // Work list of groups of <= rows rows (ceil(count/rows) per expert in expert
-// order, then the shared expert's rows) once counts and offsets (in LDS) are
-// final.
+// order, and the shared expert's rows) once counts and offsets (in LDS) are
+// final.  The expert kernels hand each XCD a contiguous range of the list and
+// each XCD runs its range in order.  With 32-row groups (about one group per
+// routed expert) the shared expert's groups, whose units carry the most rows
+// and run longest, go first: last, they made the XCD holding them finish its
+// range well after the others.  The 16- and 64-row lists keep them last: on
+// 64-row lists shared-first measured slower (2048 hash-routed rows: the down
+// launch 24 us longer).
 __device__ __forceinline__ void write_groups(int rows, const int32_t* s_cnt, const int32_t* s_off, int n_rows, int P, int E,
                                              int has_shared, Group* __restrict__ groups,
                                              int32_t* __restrict__ n_groups, int32_t* wave_tot) {
+  const int nsh = has_shared ? (n_rows + rows - 1) / rows : 0;
+  const bool shared_first = rows == kMediumGroupRows;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = (tid < E) ? s_cnt[tid] : 0;
   const int ng = (c + rows - 1) / rows;
@@ -423,8 +411,9 @@ __device__ __forceinline__ void write_groups(int rows, const int32_t* s_cnt, con
     if (w < wave) wbase += wave_tot[w];
     total += wave_tot[w];
   }
+  const int routed0 = shared_first ? nsh : 0, shared0 = shared_first ? 0 : total;
   if (tid < E) {
-    const int g0 = wbase + incl - ng;
+    const int g0 = routed0 + wbase + incl - ng;
     const int p0 = s_off[tid];
     for (int g = 0; g < ng; ++g) {
       Group gr;
@@ -435,14 +424,13 @@ __device__ __forceinline__ void write_groups(int rows, const int32_t* s_cnt, con
       groups[g0 + g] = gr;
     }
   }
-  const int nsh = has_shared ? (n_rows + rows - 1) / rows : 0;
   for (int g = tid; g < nsh; g += kRouteThreads) {
     Group gr;
     gr.e = E;
     gr.p0 = P + g * rows;
     gr.cnt = min(rows, n_rows - g * rows);
     gr.pad = 0;
-    groups[total + g] = gr;
+    groups[shared0 + g] = gr;
   }
   if (tid == 0) *n_groups = total + nsh;
 }
