@@ -49,6 +49,46 @@ __device__ __forceinline__ bool xcd_unit_split(int n_units, int tail_units, int*
   return false;
 }
 
+// Units per XCD range that are dealt dynamically by xcd_unit_claim.
+constexpr int kPoolUnits = 16;
+
+// Dealing with a shared tail: XCD x's range (as in xcd_unit_split, whole
+// units) is taken statically in slot order except for its last kPoolUnits
+// units.  Those tails of all eight ranges form one pool, ordered tail unit 0
+// of XCD 0..7, then tail unit 1, ...; a workgroup past its XCD's static part
+// claims the next pool entry with an atomic on *ctr (zeroed before the
+// launch), so XCDs that run faster take over the end of slower ones' ranges.
+// The claim loop ends once the counter passes the pool size.  Returns the
+// half index (2 * unit) or -1 when nothing is left; s_claim is a
+// workgroup-shared int.  Every thread of the workgroup must call it.
+__device__ __forceinline__ int xcd_unit_claim(int n_units, int32_t* ctr, int* s_claim) {
+  const int bid = blockIdx.x, xcd = bid % kXcds, slot = bid / kXcds;
+  const int H = 2 * n_units;
+  int per = (H + kXcds - 1) / kXcds;
+  per += per & 1;
+  const int nx = min(per, max(0, H - xcd * per)) / 2;
+  const int tx = min(kPoolUnits, nx);
+  if (slot < nx - tx) return xcd * per + 2 * slot;
+  if (threadIdx.x == 0) {
+    int got = -1;
+    constexpr int kPool = kXcds * kPoolUnits;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < kPool) {
+      const int u = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (u >= kPool) break;
+      const int x = u % kXcds, t = u / kXcds;
+      const int n = min(per, max(0, H - x * per)) / 2;
+      const int tn = min(kPoolUnits, n);
+      if (t < tn) {
+        got = x * per + 2 * (n - tn + t);
+        break;
+      }
+    }
+    *s_claim = got;
+  }
+  __syncthreads();
+  return *s_claim;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

@@ -490,14 +490,22 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
   }
 }
 
-template <int TPM, int WAVES, int NB, int RING, bool NT, bool FP6>
+// POOL: units dealt by xcd_unit_claim (static ranges with a shared tail),
+// else by xcd_unit_split (static ranges, optional tail halves).
+template <int TPM, int WAVES, int NB, int RING, bool NT, bool FP6, bool POOL>
 __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * TPM;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
   const int n_fb = a.R / kFeatUnit;
   int half_idx;
-  bool is_half;
-  if (!xcd_unit_split(*a.n_groups * n_fb, TPM >= 4 ? a.tail_units : 0, &half_idx, &is_half)) return;
+  bool is_half = false;
+  if constexpr (POOL) {
+    __shared__ int s_claim;
+    half_idx = xcd_unit_claim(*a.n_groups * n_fb, a.pool, &s_claim);
+    if (half_idx < 0) return;
+  } else if (!xcd_unit_split(*a.n_groups * n_fb, TPM >= 4 ? a.tail_units : 0, &half_idx, &is_half)) {
+    return;
+  }
   const int unit = half_idx >> 1;
   const Group g = a.groups[unit / n_fb];
   const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
@@ -556,14 +564,20 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
     }
 }
 
-template <int NA, int WAVES, int NB, int RING, bool NT, bool FP6>
+template <int NA, int WAVES, int NB, int RING, bool NT, bool FP6, bool POOL>
 __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * NA;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
   const int n_fb = a.R / kFeatUnit;
   int half_idx;
-  bool is_half;
-  if (!xcd_unit_split(*a.n_groups * n_fb, NA >= 2 ? a.tail_units : 0, &half_idx, &is_half)) return;
+  bool is_half = false;
+  if constexpr (POOL) {
+    __shared__ int s_claim;
+    half_idx = xcd_unit_claim(*a.n_groups * n_fb, a.pool, &s_claim);
+    if (half_idx < 0) return;
+  } else if (!xcd_unit_split(*a.n_groups * n_fb, NA >= 2 ? a.tail_units : 0, &half_idx, &is_half)) {
+    return;
+  }
   const int unit = half_idx >> 1;
   const Group g = a.groups[unit / n_fb];
   const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
@@ -590,24 +604,24 @@ static unsigned unit_grid(int max_groups, int n_fb) {
 
 // Dynamic LDS of one kernel instantiation: two chunk buffers of NB column
 // tiles (above 64 KB the per-device limit is raised on first use).
-template <int TPM, int WAVES, int NB, bool NT = false, bool FP6 = false, int RING = kRing>
+template <int TPM, int WAVES, int NB, bool NT = false, bool FP6 = false, bool POOL = false, int RING = kRing>
 static hipError_t gateup_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
   static std::atomic<uint64_t> attr{0};
   const size_t lds = 2 * NB * (size_t)kChunkBytes;
-  hipError_t err = ensure_dynamic_lds(gateup_kernel<TPM, WAVES, NB, RING, NT, FP6>, lds, attr);
+  hipError_t err = ensure_dynamic_lds(gateup_kernel<TPM, WAVES, NB, RING, NT, FP6, POOL>, lds, attr);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((gateup_kernel<TPM, WAVES, NB, RING, NT, FP6>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
+  hipLaunchKernelGGL((gateup_kernel<TPM, WAVES, NB, RING, NT, FP6, POOL>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
                      dim3(64 * WAVES), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int NA, int WAVES, int NB, bool NT = false, bool FP6 = false, int RING = kRing>
+template <int NA, int WAVES, int NB, bool NT = false, bool FP6 = false, bool POOL = false, int RING = kRing>
 static hipError_t down_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
   static std::atomic<uint64_t> attr{0};
   const size_t lds = 2 * NB * (size_t)kChunkBytes;
-  hipError_t err = ensure_dynamic_lds(down_kernel<NA, WAVES, NB, RING, NT, FP6>, lds, attr);
+  hipError_t err = ensure_dynamic_lds(down_kernel<NA, WAVES, NB, RING, NT, FP6, POOL>, lds, attr);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((down_kernel<NA, WAVES, NB, RING, NT, FP6>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
+  hipLaunchKernelGGL((down_kernel<NA, WAVES, NB, RING, NT, FP6, POOL>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
                      dim3(64 * WAVES), lds, stream, a);
   return hipGetLastError();
 }
@@ -631,8 +645,8 @@ constexpr int kSmallTailUnits = 64;
 hipError_t launch_gateup(const ExpertArgs& a0, int max_groups, hipStream_t stream) {
   ExpertArgs a = a0;
   a.tail_units = 0;
-  if (a.rows == kTallGroupRows) return gateup_launch<2, 8, 4, false, true>(a, max_groups, stream);
-  if (a.rows == kMediumGroupRows) return gateup_launch<2, 8, 2, true>(a, max_groups, stream);
+  if (a.rows == kTallGroupRows) return gateup_launch<2, 8, 4, false, true, true>(a, max_groups, stream);
+  if (a.rows == kMediumGroupRows) return gateup_launch<2, 8, 2, true, false, true>(a, max_groups, stream);
   if (a.P < kWideUnitPairs) {
     a.tail_units = kSmallTailUnits;
     if (a.R % 256 == 0) return gateup_launch<4, 4, 1, true>(a, max_groups, stream);
@@ -647,8 +661,8 @@ hipError_t launch_gateup(const ExpertArgs& a0, int max_groups, hipStream_t strea
 hipError_t launch_down(const ExpertArgs& a0, int max_groups, hipStream_t stream) {
   ExpertArgs a = a0;
   a.tail_units = 0;
-  if (a.rows == kTallGroupRows) return down_launch<4, 8, 4, false, true>(a, max_groups, stream);
-  if (a.rows == kMediumGroupRows) return down_launch<4, 8, 2, true>(a, max_groups, stream);
+  if (a.rows == kTallGroupRows) return down_launch<4, 8, 4, false, true, true>(a, max_groups, stream);
+  if (a.rows == kMediumGroupRows) return down_launch<4, 8, 2, true, false, true>(a, max_groups, stream);
   if (a.P < kWideUnitPairs) {
     a.tail_units = kSmallTailUnits;
     if (a.R % kDownUnitMax == 0) return down_launch<kDownUnitMax / 64, 4, 1, true>(a, max_groups, stream);

@@ -149,15 +149,17 @@ __device__ __forceinline__ void logits_tile(const uint16_t* __restrict__ x, cons
 }
 
 // Workgroups [0, n_tiles) compute logits tiles; the rest split x (one
-// 32-value block per thread; FP6 for batches of tall work units, else FP8).  Workgroup 0 also clears the completion counter
-// of the select+route launch that follows on the stream.
+// 32-value block per thread; FP6 for batches of tall work units, else FP8).
+// Workgroup 0 also clears the three counters of the launches that follow on
+// the stream: the selection's completion count and the unit claim counters of
+// gate/up and down.
 __global__ void __launch_bounds__(256) prologue_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
                                                         int n_rows, int d, int E, int S, int n_tiles,
                                                         float* __restrict__ z_part, uint8_t* __restrict__ xq,
                                                         uint8_t* __restrict__ xs, int32_t* __restrict__ done, int fp6) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kLgBufBytes];
   const int b = blockIdx.x;
-  if (b == 0 && threadIdx.x == 0) *done = 0;
+  if (b == 0 && threadIdx.x < 3) done[threadIdx.x] = 0;
   if (b < n_tiles) {
     logits_tile(x, w, n_rows, d, E, S, z_part, b, lds);
   } else {

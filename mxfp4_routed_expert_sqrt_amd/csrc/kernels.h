@@ -119,6 +119,7 @@ struct ExpertArgs {
   uint8_t* hs;                           // gate/up output: split h scales
   float* y;                              // down output [pairs][R]
   int tail_units;                        // units per XCD processed as two halves at the end
+  int32_t* pool;                         // claim counter of xcd_unit_claim (medium and tall units)
   int rows;                              // rows of the work list's groups (unit_rows); 64: FP6 activations
 };
 

@@ -38,7 +38,7 @@ Layout make_layout(const moe_config_t& c, int n) {
   L.groups = take((size_t)L.max_groups * sizeof(Group));
   L.n_groups = take(4);
   L.hist = take(route_hist_bytes(n, c.n_experts));
-  L.done = take(4);
+  L.done = take(12);  // selection completion count, gate/up and down claim counters
   L.xn = take(N * (size_t)c.d_model * 2);  // the normalised input (when norm_w is given)
   L.xq = take(N * split_q_row_bytes(c.d_model));
   L.xs = take(N * split_s_row_bytes(c.d_model));
@@ -235,6 +235,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   ga.limit = c.swiglu_limit;
   ga.hq = hq;
   ga.hs = hs;
+  ga.pool = done + 1;
   if (!mark(2)) return MOE_ERR_HIP;
   if ((err = launch_gateup(ga, max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
 
@@ -246,6 +247,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   da.ss0 = (const uint8_t*)a.w.sh_down_s;
   da.sq1 = da.ss1 = nullptr;
   da.aq = hq;
+  da.pool = done + 2;
   da.as = hs;
   da.K = I;
   da.R = d;
