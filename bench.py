@@ -27,6 +27,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 EXPERT_BYTES_NOTE = "gate+up MXFP4 bytes of every touched expert (incl. shared) + x and h at 2 B/value"
+EXPERT_BYTES_NOTE_BF16 = ("gate+up MXFP4 bytes of every touched routed expert + the bf16 shared gate/up matrices "
+                          "+ x and h at 2 B/value (two kernels: routed grouped GEMM and bf16 shared GEMM)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_verify512_traffic.txt")
 
 
@@ -39,6 +41,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shared-bf16", action="store_true",
+                    help="the shared expert in bf16 (its own bf16-MFMA GEMMs) instead of MXFP4")
     ap.add_argument("--with-norm", action="store_true",
                     help="run the layer with its input RMSNorm and a residual add (seeded bf16 weight and residual)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -155,7 +159,8 @@ def main():
     if args.with_norm:
         norm_w = synth.gen_norm_weight(shape, args.seed)
         resid = torch.from_numpy(synth.gen_residual(shape, args.seed).view(np.int16)).to(dev).view(torch.bfloat16)
-    layer = MoELayer(shape, w_np, experts, dev, norm_w=norm_w)
+    shared_bf16 = synth.gen_shared_bf16(shape, args.seed) if args.shared_bf16 else None
+    layer = MoELayer(shape, w_np, experts, dev, norm_w=norm_w, shared_bf16=shared_bf16)
     x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
     tok = None if tok_np is None else torch.from_numpy(tok_np).to(dev)
     tab = None if tab_np is None else torch.from_numpy(tab_np).to(dev)
@@ -169,8 +174,14 @@ def main():
     touched = int((counts > 0).sum()) + 1  # + shared expert
     N, d, I, E = shape.n_rows, shape.d_model, shape.d_ff, shape.n_experts
     per_expert = 3 * (I * d // 2 + I * d // 32)
-    layer_bytes = touched * per_expert + E * d * 4 + 2 * N * d * 2
-    gateup_bytes = touched * 2 * (I * d // 2 + I * d // 32) + N * d * 2 + (N * shape.top_k + N) * I * 2
+    if args.shared_bf16:  # the grouped kernels then carry the routed experts only
+        layer_bytes = (touched - 1) * per_expert + 3 * I * d * 2 + E * d * 4 + 2 * N * d * 2
+        # the gate/up stage then times two kernels: the routed grouped GEMM and the bf16 shared GEMM
+        gateup_bytes = ((touched - 1) * 2 * (I * d // 2 + I * d // 32) + N * d * 2 + N * shape.top_k * I * 2
+                        + 2 * I * d * 2 + N * I * 2)
+    else:
+        layer_bytes = touched * per_expert + E * d * 4 + 2 * N * d * 2
+        gateup_bytes = touched * 2 * (I * d // 2 + I * d // 32) + N * d * 2 + (N * shape.top_k + N) * I * 2
 
     hip = Hip()
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -233,7 +244,7 @@ def main():
     stages_us = {n: round(float(np.mean(stage_ms[:, s])) * 1e3, 2) for s, n in enumerate(capi.STAGE_NAMES)}
     t_gateup = float(np.mean(gateup_ms)) * 1e-3
     achieved = gateup_bytes / t_gateup / 1e9
-    traffic = recorded_traffic(shape.name)
+    traffic = None if args.shared_bf16 else recorded_traffic(shape.name)
     result = {
         "metric": "MoE-layer token rows/s at 512-row verify" if shape.name == "verify512"
         else f"MoE-layer token rows/s ({shape.name})",
@@ -252,12 +263,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{shape.name}: {N} token rows, d={d}, {E} routed experts top-{shape.top_k} + 1 "
                                f"shared, I={I}, MXFP4 experts ({shape.routing} routing)"
-                               + (", input RMSNorm + residual add" if args.with_norm else ""),
+                               + (", input RMSNorm + residual add" if args.with_norm else "")
+                               + (", bf16 shared expert" if args.shared_bf16 else ""),
                    "global_batch": N, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gateup_kernel", "algorithmic_bytes": gateup_bytes,
-                     "bytes_definition": EXPERT_BYTES_NOTE, "kernel_us": t_gateup * 1e6,
+                     "kernel": "gateup_kernel" + (" + shared_bf16_kernel<2>" if args.shared_bf16 else ""),
+                     "algorithmic_bytes": gateup_bytes,
+                     "bytes_definition": EXPERT_BYTES_NOTE_BF16 if args.shared_bf16 else EXPERT_BYTES_NOTE,
+                     "kernel_us": t_gateup * 1e6,
                      "kernel_timing": f"HIP events around the gate/up kernel in {len(sampled)} of the {K} timed steps"},
         "layer": {"algorithmic_bytes": layer_bytes, "hbm_frac": layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                   "touched_experts": touched, "stages_us": stages_us,

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_MXFP4_VERSION 2
+#define MOE_MXFP4_VERSION 3
 
 enum {
   MOE_OK = 0,
@@ -63,6 +63,7 @@ enum {
 
 enum { MOE_ROUTING_TOPK = 0, MOE_ROUTING_HASH = 1 };
 enum { MOE_BIAS_LOGIT = 0, MOE_BIAS_SELECT = 1 };
+enum { MOE_SHARED_MXFP4 = 0, MOE_SHARED_BF16 = 1 };
 
 /* Supported shapes: d_model and d_ff multiples of 128 (>= 128, <= 65536),
  * 1 <= n_experts <= 1024, 1 <= top_k <= min(8, n_experts),
@@ -83,6 +84,11 @@ typedef struct moe_config {
                            selection and the gates; 1 (MOE_BIAS_SELECT) added to the scores for the
                            top-k selection only, the gates use the unbiased scores.  The pages name the
                            bias (gate.bias, ds4 issue "Loader spec") but not its use. */
+  int32_t shared_format; /* weights of the shared expert: MOE_SHARED_MXFP4 (packed like the routed
+                           experts, sh_*_q/s) or MOE_SHARED_BF16 (plain bf16 matrices, sh_*_w).  The
+                           model card ("Preprocessing"; "Model Architecture and Objective") keeps the
+                           expert blocks in MXFP4 and the shared tensors in Q8_0/BF16 without saying on
+                           which side the per-layer shared expert falls; both are supported. */
 } moe_config_t;
 
 /*
@@ -91,8 +97,12 @@ typedef struct moe_config {
  * values along K.  Each group of n_mat matrices is stored back to back.
  *   gate, up : routed, n_mat = E, each [I][d]   (w1 and w3 of each expert)
  *   down     : routed, n_mat = E, each [d][I]   (w2)
- *   sh_*     : the shared expert, n_mat = 1 (ignored when has_shared == 0)
+ *   sh_*_q/s : the shared expert, n_mat = 1 (used when has_shared == 1 and
+ *              shared_format == MOE_SHARED_MXFP4)
  * q pointers 16-byte aligned, s pointers 4-byte aligned.
+ * sh_*_w: the shared expert in bf16, row-major with K contiguous (used when
+ * has_shared == 1 and shared_format == MOE_SHARED_BF16, else ignored):
+ *   sh_gate_w, sh_up_w [I][d];  sh_down_w [d][I];  16-byte aligned.
  */
 typedef struct moe_weights {
   const void *gate_q, *gate_s;
@@ -101,6 +111,7 @@ typedef struct moe_weights {
   const void *sh_gate_q, *sh_gate_s;
   const void *sh_up_q, *sh_up_s;
   const void *sh_down_q, *sh_down_s;
+  const void *sh_gate_w, *sh_up_w, *sh_down_w;
 } moe_weights_t;
 
 typedef struct moe_args {
@@ -127,7 +138,8 @@ typedef struct moe_args {
   int32_t* perm;
   int32_t* inv;
   void* workspace;            /* device scratch, 256-byte aligned, >= moe_workspace_size(); must not
-                                 overlap out, x, router_w, router_bias, norm_w or residual */
+                                 overlap out, x, router_w, router_bias, norm_w, residual or the bf16
+                                 shared-expert weights */
   size_t workspace_bytes;
   /* Optional stage timing (NULL to skip): MOE_N_STAGE_EVENTS hipEvent_t handles
    * created by the caller.  Event i is recorded on `stream` just before stage i
@@ -135,7 +147,8 @@ typedef struct moe_args {
    * (each recorded event costs several microseconds of stream time, about 9 us
    * measured on MI355X between two kernels).  The
    * stages are 0 router logits + activation split, 1 top-k/hash selection +
-   * routing bookkeeping, 2 gate/up GEMM, 3 down GEMM, 4 combine. */
+   * routing bookkeeping, 2 gate/up GEMM, 3 down GEMM, 4 combine (a bf16 shared
+   * expert's GEMMs run in stages 2 and 3). */
   void* const* stage_events;
   /* Input RMSNorm (the FFN input norm: ffn_norm in the ds4 issue's loader
    * spec; the rmsnorm step of the pypto DSpark pipeline).  norm_w: bf16 [d],

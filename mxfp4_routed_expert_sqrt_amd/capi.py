@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mxfp4.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_ROUTING_TOPK, MOE_ROUTING_HASH = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
+MOE_SHARED_MXFP4, MOE_SHARED_BF16 = 0, 1
 MOE_MAX_ROWS = 1 << 20
 
 c_i32, c_i64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -22,12 +23,13 @@ c_i32, c_i64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_flo
 class MoeConfig(ctypes.Structure):
     _fields_ = [("d_model", c_i32), ("d_ff", c_i32), ("n_experts", c_i32), ("top_k", c_i32), ("routing", c_i32),
                 ("has_shared", c_i32), ("route_scale", c_f32), ("swiglu_limit", c_f32), ("norm_eps", c_f32),
-                ("bias_mode", c_i32)]
+                ("bias_mode", c_i32), ("shared_format", c_i32)]
 
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, c_vp) for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s", "sh_gate_q", "sh_gate_s",
-                                    "sh_up_q", "sh_up_s", "sh_down_q", "sh_down_s")]
+                                    "sh_up_q", "sh_up_s", "sh_down_q", "sh_down_s", "sh_gate_w", "sh_up_w",
+                                    "sh_down_w")]
 
 
 class MoeArgs(ctypes.Structure):

@@ -12,16 +12,21 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, hist, done, xn, xq, xs, hq, hs, y, total;
+  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, hist, done, xn, xq, xs, hq, hs, hsh, y, total;
   int max_groups;  // capacity of the work list: groups of kGroupRows rows, the most there can be
 };
+
+// The shared expert runs inside the grouped GEMMs (as work-list groups) when
+// it is MXFP4; a bf16 shared expert has GEMMs of its own.
+bool shared_in_list(const moe_config_t& c) { return c.has_shared && c.shared_format == MOE_SHARED_MXFP4; }
+bool shared_bf16(const moe_config_t& c) { return c.has_shared && c.shared_format == MOE_SHARED_BF16; }
 
 // Workspace carve-up; every region starts on a 256-byte boundary.
 Layout make_layout(const moe_config_t& c, int n) {
   Layout L;
   const size_t N = (size_t)n, E = (size_t)c.n_experts, k = (size_t)c.top_k;
-  const size_t P = N * k, Ptot = P + (c.has_shared ? N : 0);
-  L.max_groups = max_work_groups(n, c.top_k, c.n_experts, c.has_shared, kGroupRows);
+  const size_t P = N * k, Ptot = P + (c.has_shared ? N : 0), Phq = P + (shared_in_list(c) ? N : 0);
+  L.max_groups = max_work_groups(n, c.top_k, c.n_experts, shared_in_list(c), kGroupRows);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -42,8 +47,9 @@ Layout make_layout(const moe_config_t& c, int n) {
   L.xn = take(N * (size_t)c.d_model * 2);  // the normalised input (when norm_w is given)
   L.xq = take(N * split_q_row_bytes(c.d_model));
   L.xs = take(N * split_s_row_bytes(c.d_model));
-  L.hq = take(Ptot * split_q_row_bytes(c.d_ff));
-  L.hs = take(Ptot * split_s_row_bytes(c.d_ff));
+  L.hq = take(Phq * split_q_row_bytes(c.d_ff));
+  L.hs = take(Phq * split_s_row_bytes(c.d_ff));
+  L.hsh = take(shared_bf16(c) ? N * (size_t)c.d_ff * 2 : 0);  // bf16 h of a bf16 shared expert
   L.y = take(Ptot * (size_t)c.d_model * 4);
   L.total = off;
   return L;
@@ -67,6 +73,7 @@ int check_config(const moe_config_t* c) {
   if (!(c->route_scale == c->route_scale) || !(c->swiglu_limit == c->swiglu_limit)) return MOE_ERR_INVALID;
   if (!(c->norm_eps >= 0.f) || c->norm_eps == INFINITY) return MOE_ERR_INVALID;
   if (c->bias_mode != 0 && c->bias_mode != 1) return MOE_ERR_INVALID;
+  if (c->shared_format != MOE_SHARED_MXFP4 && c->shared_format != MOE_SHARED_BF16) return MOE_ERR_INVALID;
   return MOE_OK;
 }
 
@@ -144,9 +151,16 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   if ((rc = check_mat(a.w.gate_q, a.w.gate_s)) || (rc = check_mat(a.w.up_q, a.w.up_s)) ||
       (rc = check_mat(a.w.down_q, a.w.down_s)))
     return rc;
-  if (c.has_shared && ((rc = check_mat(a.w.sh_gate_q, a.w.sh_gate_s)) || (rc = check_mat(a.w.sh_up_q, a.w.sh_up_s)) ||
-                       (rc = check_mat(a.w.sh_down_q, a.w.sh_down_s))))
+  if (shared_in_list(c) && ((rc = check_mat(a.w.sh_gate_q, a.w.sh_gate_s)) ||
+                             (rc = check_mat(a.w.sh_up_q, a.w.sh_up_s)) ||
+                             (rc = check_mat(a.w.sh_down_q, a.w.sh_down_s))))
     return rc;
+  const size_t sh_w_bytes = (size_t)I * d * 2;  // each bf16 shared matrix
+  if (shared_bf16(c)) {
+    const void* shw[] = {a.w.sh_gate_w, a.w.sh_up_w, a.w.sh_down_w};
+    for (const void* p : shw)
+      if (!p || !aligned(p, 16)) return MOE_ERR_INVALID;
+  }
   if (c.routing == MOE_ROUTING_HASH) {
     if (!a.token_ids || !a.tid2eid || a.vocab < 1 || !aligned(a.token_ids, 4) || !aligned(a.tid2eid, 4))
       return MOE_ERR_INVALID;
@@ -169,6 +183,10 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
       (a.router_bias && overlap(a.router_bias, (size_t)E * 4, a.workspace, L.total)) ||
       (a.norm_w && overlap(a.norm_w, (size_t)d * 2, a.workspace, L.total)) ||
       (a.residual && overlap(a.residual, out_bytes, a.workspace, L.total)))
+    return MOE_ERR_INVALID;
+  if (shared_bf16(c) && (overlap(a.w.sh_gate_w, sh_w_bytes, a.workspace, L.total) ||
+                         overlap(a.w.sh_up_w, sh_w_bytes, a.workspace, L.total) ||
+                         overlap(a.w.sh_down_w, sh_w_bytes, a.workspace, L.total)))
     return MOE_ERR_INVALID;
 
   hipStream_t stream = (hipStream_t)stream_;
@@ -195,7 +213,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   };
   if (!mark(0)) return MOE_ERR_HIP;
   const int rows = unit_rows(P, E, d, I);
-  const int max_groups = max_work_groups(N, k, E, c.has_shared, rows);
+  const int max_groups = max_work_groups(N, k, E, shared_in_list(c), rows);
   const uint16_t* x = (const uint16_t*)a.x;
   if (a.norm_w) {
     uint16_t* xn = (uint16_t*)(ws + L.xn);
@@ -207,7 +225,7 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
       hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
-  if ((err = launch_select_route(z, a.router_bias, c.bias_mode, d, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, c.has_shared,
+  if ((err = launch_select_route(z, a.router_bias, c.bias_mode, d, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx, gates, shared_in_list(c),
                                  counts, offsets, perm, inv, rows, groups, n_groups, hist, done, stream)) != hipSuccess)
     return MOE_ERR_HIP;
 
@@ -238,6 +256,11 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   ga.pool = done + 1;
   if (!mark(2)) return MOE_ERR_HIP;
   if ((err = launch_gateup(ga, max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
+  uint16_t* hsh = (uint16_t*)(ws + L.hsh);
+  if (shared_bf16(c) &&
+      (err = launch_shared_bf16_gateup(x, N, d, I, (const uint16_t*)a.w.sh_gate_w, (const uint16_t*)a.w.sh_up_w,
+                                       c.swiglu_limit, hsh, stream)) != hipSuccess)
+    return MOE_ERR_HIP;
 
   ExpertArgs da = ga;
   da.q0 = (const uint8_t*)a.w.down_q;
@@ -255,6 +278,10 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   da.y = y;
   if (!mark(3)) return MOE_ERR_HIP;
   if ((err = launch_down(da, max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
+  if (shared_bf16(c) &&
+      (err = launch_shared_bf16_down(hsh, N, d, I, (const uint16_t*)a.w.sh_down_w, y + (size_t)P * d, stream)) !=
+          hipSuccess)
+    return MOE_ERR_HIP;
   if (!mark(4)) return MOE_ERR_HIP;
 
   if ((err = launch_combine(y, inv, gates, N, d, k, P, c.has_shared, c.route_scale, (const uint16_t*)a.residual,

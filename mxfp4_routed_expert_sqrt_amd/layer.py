@@ -13,13 +13,14 @@ def _ptr(t):
 
 
 def make_config(shape: MoEShape, has_shared: bool = True, route_scale=None, swiglu_limit=None,
-                norm_eps: float = 1e-6, bias_mode: int = capi.MOE_BIAS_LOGIT) -> capi.MoeConfig:
+                norm_eps: float = 1e-6, bias_mode: int = capi.MOE_BIAS_LOGIT,
+                shared_format: int = capi.MOE_SHARED_MXFP4) -> capi.MoeConfig:
     return capi.MoeConfig(shape.d_model, shape.d_ff, shape.n_experts, shape.top_k,
                           capi.MOE_ROUTING_TOPK if shape.routing == "topk" else capi.MOE_ROUTING_HASH,
                           1 if has_shared else 0,
                           float(shape.route_scale if route_scale is None else route_scale),
                           float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit), float(norm_eps),
-                          int(bias_mode))
+                          int(bias_mode), int(shared_format))
 
 
 def pack_mxfp4(q: torch.Tensor, s: torch.Tensor, rows: int, K: int, stream=None, out=None):
@@ -79,34 +80,48 @@ class PackedExperts:
         torch.cuda.synchronize(device)
         self.has_shared = has_shared
 
-    def weights(self, with_shared: bool = True) -> capi.MoeWeights:
+    def weights(self, with_shared: bool = True, shared_bf16=None) -> capi.MoeWeights:
+        """shared_bf16: optional dict of bf16 device tensors gate/up [I][d], down [d][I] (the shared expert
+        in bf16; the packed MXFP4 shared expert is then not passed)."""
         t = self.t
-        sh = (lambda n, i: _ptr(t["sh_" + n][i])) if (self.has_shared and with_shared) else (lambda n, i: None)
+        mx = self.has_shared and with_shared and shared_bf16 is None
+        sh = (lambda n, i: _ptr(t["sh_" + n][i])) if mx else (lambda n, i: None)
+        b = shared_bf16 or {}
         return capi.MoeWeights(_ptr(t["gate"][0]), _ptr(t["gate"][1]), _ptr(t["up"][0]), _ptr(t["up"][1]),
                                _ptr(t["down"][0]), _ptr(t["down"][1]), sh("gate", 0), sh("gate", 1), sh("up", 0),
-                               sh("up", 1), sh("down", 0), sh("down", 1))
+                               sh("up", 1), sh("down", 0), sh("down", 1), _ptr(b.get("gate")), _ptr(b.get("up")),
+                               _ptr(b.get("down")))
 
 
 class MoELayer:
     def __init__(self, shape: MoEShape, router_w, experts, device="cuda", router_bias=None,
                  has_shared: bool = True, route_scale=None, swiglu_limit=None, norm_w=None, norm_eps: float = 1e-6,
-                 bias_mode: int = capi.MOE_BIAS_LOGIT):
+                 bias_mode: int = capi.MOE_BIAS_LOGIT, shared_bf16=None):
         """experts: natural-layout arrays (dict, packed here) or an already packed PackedExperts.
-        norm_w: optional bf16 bit patterns [d] of the input RMSNorm weight (the layer then normalises x)."""
+        norm_w: optional bf16 bit patterns [d] of the input RMSNorm weight (the layer then normalises x).
+        shared_bf16: optional dict of bf16 bit patterns gate/up [I][d], down [d][I]: the shared expert in
+        bf16 (MOE_SHARED_BF16) instead of the MXFP4 shared expert at index E of experts."""
         self.shape = shape
         self.device = torch.device(device)
-        self.cfg = make_config(shape, has_shared, route_scale, swiglu_limit, norm_eps, bias_mode)
+        fmt = capi.MOE_SHARED_MXFP4 if shared_bf16 is None else capi.MOE_SHARED_BF16
+        if shared_bf16 is not None:
+            has_shared = True
+        self.cfg = make_config(shape, has_shared, route_scale, swiglu_limit, norm_eps, bias_mode, fmt)
+        self.shared_bf16 = None if shared_bf16 is None else {
+            n: torch.from_numpy(np.ascontiguousarray(shared_bf16[n], dtype=np.uint16).view(np.int16)).to(self.device)
+            for n in ("gate", "up", "down")}
         self.norm_w = None if norm_w is None else \
             torch.from_numpy(np.ascontiguousarray(norm_w, dtype=np.uint16).view(np.int16)).to(self.device)
         self.router_w = torch.as_tensor(np.ascontiguousarray(router_w, dtype=np.float32)).to(self.device)
         self.router_bias = None if router_bias is None else \
             torch.as_tensor(np.ascontiguousarray(router_bias, dtype=np.float32)).to(self.device)
+        mx_shared = has_shared and shared_bf16 is None
         if isinstance(experts, PackedExperts):
-            if has_shared and not experts.has_shared:
+            if mx_shared and not experts.has_shared:
                 raise ValueError("packed experts carry no shared expert")
             self.experts = experts
         else:
-            self.experts = PackedExperts(experts, shape, self.device, has_shared)
+            self.experts = PackedExperts(experts, shape, self.device, mx_shared)
         self.has_shared = has_shared
 
     def workspace_bytes(self, n_rows: int) -> int:
@@ -119,7 +134,8 @@ class MoELayer:
         N = x.shape[0]
         r = routing or {}
         return capi.MoeArgs(N, _ptr(x), _ptr(self.router_w), _ptr(self.router_bias), _ptr(token_ids), _ptr(tid2eid),
-                            0 if tid2eid is None else tid2eid.shape[0], self.experts.weights(self.has_shared), _ptr(out),
+                            0 if tid2eid is None else tid2eid.shape[0],
+                            self.experts.weights(self.has_shared, self.shared_bf16), _ptr(out),
                             _ptr(r.get("topk_idx")), _ptr(r.get("topk_w")), _ptr(r.get("counts")),
                             _ptr(r.get("offsets")), _ptr(r.get("perm")), _ptr(r.get("inv")), _ptr(workspace),
                             0 if workspace is None else workspace.numel(), None, _ptr(self.norm_w), _ptr(residual))

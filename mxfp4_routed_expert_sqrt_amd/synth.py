@@ -215,7 +215,7 @@ def resample_rows(shape: MoEShape, accept_rows, seed: int = 0, max_tries: int = 
 
 # Streams of the input-RMSNorm extras and the selection-only bias (numpy generators keyed by
 # seed, workload and tensor).
-_TAG_ROW_EXP, _TAG_NORM_W, _TAG_RESIDUAL, _TAG_SEL_BIAS = 11, 12, 13, 14
+_TAG_ROW_EXP, _TAG_NORM_W, _TAG_RESIDUAL, _TAG_SEL_BIAS, _TAG_SHARED_BF16 = 11, 12, 13, 14, 15
 
 
 def _rng(shape: MoEShape, seed: int, tag: int):
@@ -253,3 +253,13 @@ def gen_residual(shape: MoEShape, seed: int = 0) -> np.ndarray:
 def gen_selection_bias(shape: MoEShape, seed: int = 0) -> np.ndarray:
     """Router bias [E] fp32, N(0, 0.05), for the selection-only bias reading."""
     return (0.05 * _rng(shape, seed, _TAG_SEL_BIAS).standard_normal(shape.n_experts)).astype(np.float32)
+
+
+def gen_shared_bf16(shape: MoEShape, seed: int = 0) -> dict:
+    """A shared expert with bf16 weights, bf16 bit patterns: gate/up [I][d] ~ N(0, 1/sqrt(d)),
+    down [d][I] ~ N(0, 1/sqrt(I)) (the routed experts' distributions before quantisation)."""
+    g = _rng(shape, seed, _TAG_SHARED_BF16)
+    d, I = shape.d_model, shape.d_ff
+    return dict(gate=bf16_bits(expert_std(d) * g.standard_normal((I, d))),
+                up=bf16_bits(expert_std(d) * g.standard_normal((I, d))),
+                down=bf16_bits(expert_std(I) * g.standard_normal((d, I))))

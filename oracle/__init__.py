@@ -36,7 +36,8 @@ class _Inputs(ctypes.Structure):
                 ("token_ids", ctypes.c_void_p), ("tid2eid", ctypes.c_void_p), ("vocab", ctypes.c_long)] + \
                [(n, ctypes.c_void_p) for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s",
                                               "sh_gate_q", "sh_gate_s", "sh_up_q", "sh_up_s", "sh_down_q",
-                                              "sh_down_s", "norm_w", "residual")]
+                                              "sh_down_s", "norm_w", "residual", "sh_gate_w", "sh_up_w",
+                                              "sh_down_w")]
 
 
 def _load():
@@ -174,7 +175,7 @@ def rmsnorm_bf16(x_bf16: np.ndarray, g_bf16: np.ndarray, eps: float) -> np.ndarr
 
 def forward(shape, x, router_w, experts, router_bias=None, token_ids=None, tid2eid=None, rows=None,
             route_scale=None, swiglu_limit=None, with_shared=True, threads=None, norm_w=None, norm_eps=1e-6,
-            residual=None, bias_mode=0) -> dict:
+            residual=None, bias_mode=0, shared_bf16=None) -> dict:
     """The whole layer in fp64.
 
     bias_mode: 0 = router_bias added to the logits (selection and gates); 1 = added to the
@@ -182,6 +183,8 @@ def forward(shape, x, router_w, experts, router_bias=None, token_ids=None, tid2e
 
     norm_w: optional bf16 [d] RMSNorm weight; the layer then runs on rmsnorm_bf16(x, norm_w, norm_eps).
     residual: optional bf16 [N][d] added to the output.
+    shared_bf16: optional dict of bf16 bit patterns gate/up [I][d], down [d][I]: the shared expert in
+    bf16 (the MXFP4 shared expert at index E is then not used).
 
     experts: dict of natural-layout MXFP4 arrays gate_q/gate_s/up_q/up_s [E+1][I][...] and
     down_q/down_s [E+1][d][...]; index E is the shared expert (ignored if with_shared=False).
@@ -204,14 +207,17 @@ def forward(shape, x, router_w, experts, router_bias=None, token_ids=None, tid2e
         return a.ctypes.data
 
     w = experts
+    mx_sh = with_shared and shared_bf16 is None
+    b = shared_bf16 or {}
     ins = _Inputs(P(x), P(router_w, np.float32), P(router_bias, np.float32), P(token_ids, np.int32),
                   P(tid2eid, np.int32), 0 if tid2eid is None else int(np.asarray(tid2eid).shape[0]),
                   P(w["gate_q"][:E]), P(w["gate_s"][:E]), P(w["up_q"][:E]), P(w["up_s"][:E]),
                   P(w["down_q"][:E]), P(w["down_s"][:E]),
-                  P(w["gate_q"][E]) if with_shared else None, P(w["gate_s"][E]) if with_shared else None,
-                  P(w["up_q"][E]) if with_shared else None, P(w["up_s"][E]) if with_shared else None,
-                  P(w["down_q"][E]) if with_shared else None, P(w["down_s"][E]) if with_shared else None,
-                  P(norm_w, np.uint16), P(residual, np.uint16))
+                  P(w["gate_q"][E]) if mx_sh else None, P(w["gate_s"][E]) if mx_sh else None,
+                  P(w["up_q"][E]) if mx_sh else None, P(w["up_s"][E]) if mx_sh else None,
+                  P(w["down_q"][E]) if mx_sh else None, P(w["down_s"][E]) if mx_sh else None,
+                  P(norm_w, np.uint16), P(residual, np.uint16), P(b.get("gate"), np.uint16),
+                  P(b.get("up"), np.uint16), P(b.get("down"), np.uint16))
     rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
     n_out = N if rows_arr is None else rows_arr.shape[0]
     out = np.empty((n_out, d), dtype=np.float64)

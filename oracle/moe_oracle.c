@@ -25,6 +25,9 @@
  *   weighted sum of the routed experts plus the shared expert (TensorSharp
  *   "Fitting the model": weighted-sum epilogue; pypto "MoE and output stages":
  *   shared and routed FFN paths).
+ * - the shared expert optionally in bf16 instead of MXFP4 (model card,
+ *   Preprocessing and "Model Architecture and Objective": shared tensors in
+ *   Q8_0/BF16, expert blocks in MXFP4).
  */
 #include <math.h>
 #include <pthread.h>
@@ -279,7 +282,8 @@ typedef struct {
   double limit;
   /* per expert e in [0, E]: gate/up [I][d], down [d][I]; E = shared */
   const uint8_t *gq, *gs, *uq, *us, *dq, *ds;       /* routed, [E][...] */
-  const uint8_t *sgq, *sgs, *suq, *sus, *sdq, *sds; /* shared */
+  const uint8_t *sgq, *sgs, *suq, *sus, *sdq, *sds; /* shared, MXFP4 */
+  const uint16_t *sgw, *suw, *sdw;                  /* shared, bf16 (used when sgw != NULL) */
   int E;
   /* work list: pairs grouped by expert */
   const int* pair_row;   /* [n_pairs] index into xd */
@@ -305,6 +309,19 @@ static orc_mat mat_of(const ffn_ctx* c, int e, int which) {
   return m;
 }
 
+/* Row `row` of matrix `which` (0 gate, 1 up: K = d; 2 down: K = I) of expert e
+ * in fp64: the shared expert (e == E) from its bf16 weights when given, else
+ * from MXFP4. */
+static void weight_row(const ffn_ctx* c, int e, int which, int row, int K, double* out) {
+  if (e == c->E && c->sgw) {
+    const uint16_t* w = which == 0 ? c->sgw : which == 1 ? c->suw : c->sdw;
+    for (int i = 0; i < K; ++i) out[i] = orc_bf16(w[(size_t)row * K + i]);
+    return;
+  }
+  orc_mat m = mat_of(c, e, which);
+  orc_decode_mxfp4_row(m.q + (size_t)row * (K / 2), m.s + (size_t)row * (K / 32), K, out);
+}
+
 /* Item = (expert e, intermediate unit n): h[p][n] for every pair p of e. */
 static void ffn_gateup_item(void* p, long item) {
   ffn_ctx* c = (ffn_ctx*)p;
@@ -313,9 +330,8 @@ static void ffn_gateup_item(void* p, long item) {
   if (p0 == p1) return; /* an expert with no rows reads no weights */
   double* wg = (double*)malloc(sizeof(double) * (size_t)c->d * 2);
   double* wu = wg + c->d;
-  orc_mat g = mat_of(c, e, 0), u = mat_of(c, e, 1);
-  orc_decode_mxfp4_row(g.q + (size_t)n * (c->d / 2), g.s + (size_t)n * (c->d / 32), c->d, wg);
-  orc_decode_mxfp4_row(u.q + (size_t)n * (c->d / 2), u.s + (size_t)n * (c->d / 32), c->d, wu);
+  weight_row(c, e, 0, n, c->d, wg);
+  weight_row(c, e, 1, n, c->d, wu);
   for (int pp = p0; pp < p1; ++pp) {
     const double* xr = c->xd + (size_t)c->pair_row[pp] * c->d;
     double a = 0.0, b = 0.0;
@@ -337,8 +353,7 @@ static void ffn_down_item(void* p, long item) {
   int p0 = c->exp_start[e], p1 = c->exp_start[e + 1];
   if (p0 == p1) return;
   double* wd = (double*)malloc(sizeof(double) * (size_t)c->I);
-  orc_mat dm = mat_of(c, e, 2);
-  orc_decode_mxfp4_row(dm.q + (size_t)m * (c->I / 2), dm.s + (size_t)m * (c->I / 32), c->I, wd);
+  weight_row(c, e, 2, m, c->I, wd);
   for (int pp = p0; pp < p1; ++pp) {
     const double* hr = c->h + (size_t)pp * c->I;
     double acc = 0.0;
@@ -370,6 +385,11 @@ typedef struct {
   const uint8_t *sh_gate_q, *sh_gate_s, *sh_up_q, *sh_up_s, *sh_down_q, *sh_down_s;
   const uint16_t* norm_w;   /* bf16 [d]: the layer runs on RMSNorm(x) (orc_rmsnorm_bf16); NULL: on x */
   const uint16_t* residual; /* bf16 [N][d] added to the output, or NULL */
+  /* shared expert with bf16 weights (gate/up [I][d], down [d][I]) instead of
+   * MXFP4, or NULL.  The model card ("Preprocessing"; "Model Architecture and
+   * Objective") stores expert blocks in MXFP4 and shared tensors in Q8_0/BF16
+   * without placing the shared expert; both readings are covered. */
+  const uint16_t *sh_gate_w, *sh_up_w, *sh_down_w;
 } orc_inputs;
 
 /*
@@ -421,7 +441,7 @@ int orc_forward(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows, i
   if (gates_out) memcpy(gates_out, gates, sizeof(double) * (size_t)N * k);
 
   if (out && n_out > 0) {
-    const int has_shared = in->sh_gate_q != NULL;
+    const int has_shared = in->sh_gate_q != NULL || in->sh_gate_w != NULL;
     const int slots = k + has_shared;
     /* pairs of the listed rows, grouped by expert (E = shared), row order inside */
     const long n_pairs = (long)n_out * slots;
@@ -455,6 +475,7 @@ int orc_forward(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows, i
     ffn_ctx fc = {d, I, cfg->swiglu_limit,
                   in->gate_q, in->gate_s, in->up_q, in->up_s, in->down_q, in->down_s,
                   in->sh_gate_q, in->sh_gate_s, in->sh_up_q, in->sh_up_s, in->sh_down_q, in->sh_down_s,
+                  in->sh_gate_w, in->sh_up_w, in->sh_down_w,
                   E, pair_row, exp_start, xd, h, y};
     orc_parallel(ffn_gateup_item, &fc, (long)(E + 1) * I, nthreads);
     orc_parallel(ffn_down_item, &fc, (long)(E + 1) * d, nthreads);

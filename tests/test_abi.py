@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert capi.moe_version() == 2
+    assert capi.moe_version() == 3
     for st in (0, -1, -2, -3, -4):
         assert capi.moe_status_string(st) != "unknown status"
     assert capi.moe_status_string(7) == "unknown status"
@@ -71,7 +71,8 @@ def test_workspace_size_arithmetic():
     ("routing", 2, capi.MOE_ERR_INVALID), ("has_shared", 3, capi.MOE_ERR_INVALID),
     ("norm_eps", -1e-6, capi.MOE_ERR_INVALID), ("norm_eps", float("inf"), capi.MOE_ERR_INVALID),
     ("norm_eps", float("nan"), capi.MOE_ERR_INVALID), ("bias_mode", 2, capi.MOE_ERR_INVALID),
-    ("bias_mode", -1, capi.MOE_ERR_INVALID),
+    ("bias_mode", -1, capi.MOE_ERR_INVALID), ("shared_format", 2, capi.MOE_ERR_INVALID),
+    ("shared_format", -1, capi.MOE_ERR_INVALID),
 ])
 def test_bad_config_rejected(field, value, status):
     cfg = make_config(SHAPES["tiny"])
@@ -123,6 +124,15 @@ def test_invalid_arguments_return_before_any_hip_call():
     hcfg = make_config(SHAPES["hash2048"])
     a = _valid_args(hcfg, 8)
     assert capi.moe_layer_forward(hcfg, a, None) == capi.MOE_ERR_INVALID  # hash mode without a table
+    bcfg = make_config(SHAPES["tiny"], shared_format=capi.MOE_SHARED_BF16)
+    for field, value in (("sh_up_w", None), ("sh_down_w", 0x4C000008), ("sh_gate_w", None)):
+        a = _valid_args(bcfg, N); setattr(a.w, field, value)
+        assert capi.moe_layer_forward(bcfg, a, None) == capi.MOE_ERR_INVALID, field
+    a = _valid_args(bcfg, N); a.w.sh_gate_w = a.workspace + 512
+    assert capi.moe_layer_forward(bcfg, a, None) == capi.MOE_ERR_INVALID  # bf16 shared weights in the workspace
+    a = _valid_args(bcfg, N); a.w.sh_gate_q = None; a.w.sh_down_s = None
+    a.workspace_bytes = 0
+    assert capi.moe_layer_forward(bcfg, a, None) == capi.MOE_ERR_WORKSPACE  # MXFP4 shared pointers not needed
     nosh = make_config(SHAPES["tiny"], has_shared=False)
     a = _valid_args(nosh, N); a.w.sh_gate_q = None
     a.workspace_bytes = 0
@@ -160,7 +170,8 @@ def test_binding_structs_match_the_c_header(tmp_path):
         for fname, _ in cls._fields_:
             lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
     consts = ["MOE_OK", "MOE_ERR_INVALID", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
-              "MOE_ROUTING_TOPK", "MOE_ROUTING_HASH", "MOE_BIAS_LOGIT", "MOE_BIAS_SELECT", "MOE_MAX_ROWS",
+              "MOE_ROUTING_TOPK", "MOE_ROUTING_HASH", "MOE_BIAS_LOGIT", "MOE_BIAS_SELECT", "MOE_SHARED_MXFP4",
+              "MOE_SHARED_BF16", "MOE_MAX_ROWS",
               "MOE_N_STAGES", "MOE_N_STAGE_EVENTS", "MOE_MXFP4_VERSION"]
     for c in consts:
         lines.append(f'  printf("const {c} %ld\\n", (long)({c}));')

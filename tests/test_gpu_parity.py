@@ -11,6 +11,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
+from mxfp4_routed_expert_sqrt_amd import synth  # noqa: E402
 from mxfp4_routed_expert_sqrt_amd.configs import SHAPES, MoEShape  # noqa: E402
 from mxfp4_routed_expert_sqrt_amd.layer import MoELayer, PackedExperts  # noqa: E402
 from tests.inputs import norm_workload, oracle_forward, selection_bias_workload, workload  # noqa: E402
@@ -72,7 +73,8 @@ def run_gpu(wl, has_shared=True, **cfg_kw):
     if "residual" in wl:
         resid = torch.from_numpy(wl["residual"].view(np.int16)).to(dev).view(torch.bfloat16)
     print(f"gpu forward {sh.name} N={sh.n_rows} shared={has_shared} norm={'norm_w' in wl} "
-          f"{ {k: v for k, v in cfg_kw.items() if k != 'norm_w'} }", flush=True)
+          f"{ {k: v for k, v in cfg_kw.items() if k not in ('norm_w', 'shared_bf16')} }"
+          f"{' bf16 shared' if 'shared_bf16' in cfg_kw else ''}", flush=True)
     out, routing = layer.forward(x, tok, tab, with_routing=True, residual=resid)
     torch.cuda.synchronize()
     res = {k: v.cpu().numpy() for k, v in routing.items()}
@@ -201,6 +203,33 @@ def test_edge_shapes(case):
     ref = oracle_forward(wl)
     check_routing(gpu, ref, case)
     check_out(gpu["out"], ref["out"], case)
+
+
+# ------------------------------------------------------- bf16 shared expert
+
+@pytest.mark.parametrize("name,n_sample", [("tiny", 0), ("ragged37", 0), ("decode8", 0), ("verify512", 32),
+                                           ("prefill8192", 16), ("tall", 0)])
+def test_shared_expert_bf16(name, n_sample):
+    # the shared expert with bf16 weights: its own bf16-MFMA GEMMs over all rows (ragged row tiles at 37
+    # and 611 rows), the routed experts unchanged; the work list then holds routed groups only
+    shape = EDGE[name] if name in EDGE else name
+    wl = workload(shape)
+    b = synth.gen_shared_bf16(wl["shape"])
+    gpu, *_ = run_gpu(wl, shared_bf16=b)
+    rows = None if n_sample == 0 else sample_rows(wl["shape"].n_rows, n_sample)
+    ref = oracle_forward(wl, rows=rows, shared_bf16=b)
+    check_routing(gpu, ref, wl["shape"].name + "+bf16shared")
+    check_out(gpu["out"] if rows is None else gpu["out"][rows], ref["out"], wl["shape"].name + "+bf16shared")
+
+
+def test_shared_expert_bf16_with_norm_and_clamp():
+    # the bf16 shared GEMM runs on the normalised rows; a small swiglu limit makes its clamp bind
+    wl = norm_workload("tiny")
+    b = synth.gen_shared_bf16(wl["shape"])
+    gpu, *_ = run_gpu(wl, shared_bf16=b, swiglu_limit=0.05)
+    ref = oracle_forward(wl, shared_bf16=b, swiglu_limit=0.05)
+    check_routing(gpu, ref, "tiny+norm+bf16shared+clamp", gate_rtol=GATE_RTOL_NORM)
+    check_out(gpu["out"], ref["out"], "tiny+norm+bf16shared+clamp")
 
 
 def test_no_shared_expert_bias_and_route_scale():

@@ -477,3 +477,48 @@ def test_selection_only_bias_zero_and_forcing():
     g5 = forced["gates"][np.arange(sh.n_rows), col]
     assert np.allclose(g5, s[:, 5] / np.take_along_axis(s, forced["idx"], 1).sum(1), rtol=1e-12)
     assert g5.max() < 0.9  # not dominated by the bias
+
+
+# ------------------------------------------------------- bf16 shared expert
+
+def _bf16_exact_bits(v):
+    """fp64 values that bf16 holds exactly -> bit patterns (asserts the exactness)."""
+    v = np.asarray(v, dtype=np.float64)
+    f = v.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), v)
+    u = f.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0)
+    return (u >> 16).astype(np.uint16)
+
+
+def test_bf16_shared_expert_holding_the_mxfp4_values_changes_no_bit():
+    # MXFP4 values have at most two significant bits and a power-of-two scale, so a bf16 copy of the
+    # shared expert (decoded here independently of the oracle) holds them exactly: the layer is the same
+    wl = workload("tiny")
+    sh, ex = wl["shape"], wl["experts"]
+    E = sh.n_experts
+    b = {n: _bf16_exact_bits(_numpy_decode(ex[n + "_q"][E], ex[n + "_s"][E])) for n in ("gate", "up", "down")}
+    r_mx = oracle.forward(sh, wl["x"], wl["router_w"], ex)
+    r_bf = oracle.forward(sh, wl["x"], wl["router_w"], ex, shared_bf16=b)
+    assert np.array_equal(r_mx["idx"], r_bf["idx"])
+    assert np.array_equal(r_mx["out"], r_bf["out"])
+
+
+@pytest.mark.parametrize("limit", [10.0, 0.05])
+def test_bf16_shared_expert_matches_dense_numpy(limit):
+    # the layer minus the layer without a shared expert is the shared FFN; here computed densely from
+    # the bf16 weights (gate/up [I][d], down [d][I]); at limit 0.05 the clamp binds on most units
+    wl = workload("tiny")
+    sh = wl["shape"]
+    b = synth.gen_shared_bf16(sh)
+    r = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], shared_bf16=b, swiglu_limit=limit)
+    r0 = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], with_shared=False, swiglu_limit=limit)
+    f = lambda bits: (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    x = f(wl["x"])
+    a, c = x @ f(b["gate"]).T, x @ f(b["up"]).T
+    if limit == 0.05:
+        assert np.mean(np.abs(a) > limit) > 0.5
+    a, c = np.minimum(a, limit), np.clip(c, -limit, limit)
+    y = (a / (1.0 + np.exp(-a)) * c) @ f(b["down"]).T
+    assert np.array_equal(r["idx"], r0["idx"])
+    assert np.allclose(r["out"] - r0["out"], y, rtol=1e-9, atol=1e-12 * np.abs(y).max())
