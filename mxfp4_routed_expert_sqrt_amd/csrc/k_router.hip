@@ -364,7 +364,8 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
 //     that overwrites each row with its exclusive base.  The counts, their
 //     exclusive scan (offsets), the scatter of perm/inv and the work list of
 //     the grouped GEMMs (groups of <= 16, 32 or 64 rows of one expert, and
-//     the shared expert's rows) follow.
+//     the shared expert's rows) follow.  A launch of one workgroup (<= 16
+//     rows) takes its own histogram row as the counts, with zero bases.
 // Histogram rows are E rounded up to a multiple of 4 ints wide, so both scan
 // passes move 16-byte columns.
 constexpr int kRouteThreads = 1024;
@@ -531,70 +532,80 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
     }
   }
   __syncthreads();
-  for (int e = tid; e < Ep; e += kRouteThreads) hist[(size_t)b * Ep + e] = s_a[e];
+  // One workgroup (at most 16 rows) holds every pair: its own histogram row is
+  // the counts and every base is 0, so it goes straight to the offsets with no
+  // histogram round trip and no device-scope handshake.
+  const bool single = nb == 1;
+  if (single) {
+    for (int e = tid; e < E; e += kRouteThreads) counts[e] = s_a[e];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // idx and the ranks in inv, read back in 2e
+    __syncthreads();
+  } else {
+    for (int e = tid; e < Ep; e += kRouteThreads) hist[(size_t)b * Ep + e] = s_a[e];
 
-  // Every wave waits until its own stores are acknowledged by the L2; after the
-  // barrier, thread 0's device-scope release (part of the acq_rel atomic)
-  // writes the L2 back once for the whole workgroup.  One release per
-  // workgroup instead of one per wave: each costs an L2 write-back.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = prev == nb - 1;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see the other workgroups' results
+    // Every wave waits until its own stores are acknowledged by the L2; after the
+    // barrier, thread 0's device-scope release (part of the acq_rel atomic)
+    // writes the L2 back once for the whole workgroup.  One release per
+    // workgroup instead of one per wave: each costs an L2 write-back.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      const int prev = __hip_atomic_fetch_add(done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      is_last = prev == nb - 1;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see the other workgroups' results
 
-  // step 2a: per (column of 4 experts, segment of histogram rows) sums
-  const int C = Ep / 4;
-  const int S = max(1, min(kRouteThreads / C, nb));  // segments
-  const int L = (nb + S - 1) / S;                     // rows per segment
-  const int4* h4 = (const int4*)hist;
-  if (tid < C * S) {
-    const int c = tid % C, sg = tid / C;
-    const int b0 = min(sg * L, nb), b1 = min(b0 + L, nb);
-    int4 acc = {0, 0, 0, 0};
+    // step 2a: per (column of 4 experts, segment of histogram rows) sums
+    const int C = Ep / 4;
+    const int S = max(1, min(kRouteThreads / C, nb));  // segments
+    const int L = (nb + S - 1) / S;                     // rows per segment
+    const int4* h4 = (const int4*)hist;
+    if (tid < C * S) {
+      const int c = tid % C, sg = tid / C;
+      const int b0 = min(sg * L, nb), b1 = min(b0 + L, nb);
+      int4 acc = {0, 0, 0, 0};
 #pragma unroll 8
-    for (int bb = b0; bb < b1; ++bb) {
-      const int4 v = h4[(size_t)bb * C + c];
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+      for (int bb = b0; bb < b1; ++bb) {
+        const int4 v = h4[(size_t)bb * C + c];
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+      *(int4*)(s_seg + sg * Ep + 4 * c) = acc;
     }
-    *(int4*)(s_seg + sg * Ep + 4 * c) = acc;
-  }
-  __syncthreads();
-  // 2b: per expert, exclusive scan over the segments; counts
-  for (int e = tid; e < E; e += kRouteThreads) {
-    int run = 0;
-    for (int sg = 0; sg < S; ++sg) {
-      const int v = s_seg[sg * Ep + e];
-      s_seg[sg * Ep + e] = run;
-      run += v;
+    __syncthreads();
+    // 2b: per expert, exclusive scan over the segments; counts
+    for (int e = tid; e < E; e += kRouteThreads) {
+      int run = 0;
+      for (int sg = 0; sg < S; ++sg) {
+        const int v = s_seg[sg * Ep + e];
+        s_seg[sg * Ep + e] = run;
+        run += v;
+      }
+      s_a[e] = run;
+      counts[e] = run;
     }
-    s_a[e] = run;
-    counts[e] = run;
-  }
-  __syncthreads();
-  // 2c: each histogram row becomes its exclusive base
-  if (tid < C * S) {
-    const int c = tid % C, sg = tid / C;
-    const int b0 = min(sg * L, nb), b1 = min(b0 + L, nb);
-    int4 run = *(const int4*)(s_seg + sg * Ep + 4 * c);
-    int4* w4 = (int4*)hist;
+    __syncthreads();
+    // 2c: each histogram row becomes its exclusive base
+    if (tid < C * S) {
+      const int c = tid % C, sg = tid / C;
+      const int b0 = min(sg * L, nb), b1 = min(b0 + L, nb);
+      int4 run = *(const int4*)(s_seg + sg * Ep + 4 * c);
+      int4* w4 = (int4*)hist;
 #pragma unroll 8
-    for (int bb = b0; bb < b1; ++bb) {
-      const int4 v = w4[(size_t)bb * C + c];
-      w4[(size_t)bb * C + c] = run;
-      run.x += v.x;
-      run.y += v.y;
-      run.z += v.z;
-      run.w += v.w;
+      for (int bb = b0; bb < b1; ++bb) {
+        const int4 v = w4[(size_t)bb * C + c];
+        w4[(size_t)bb * C + c] = run;
+        run.x += v.x;
+        run.y += v.y;
+        run.z += v.z;
+        run.w += v.w;
+      }
     }
-  }
+  }  // multi-workgroup step 2a-2c
   // 2d: offsets = exclusive scan of the counts over experts (E <= 1024: one per thread)
   {
     const int v = (tid < E) ? s_a[tid] : 0;
@@ -621,7 +632,7 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
 #pragma unroll 4
   for (int q = tid; q < (scatter_here ? P : 0); q += kRouteThreads) {
     const int e = idx[q];
-    const int p = s_off[e] + hist[(size_t)(q / per_b) * Ep + e] + inv[q];
+    const int p = s_off[e] + (single ? 0 : hist[(size_t)(q / per_b) * Ep + e]) + inv[q];
     if ((unsigned)p < (unsigned)P) {  // always true for ranks from step 1; guards the scatter
       perm[p] = q;
       inv[q] = p;
