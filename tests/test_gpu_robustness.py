@@ -137,29 +137,42 @@ def test_stage_events_with_null_entries():
         hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-@pytest.mark.parametrize("name", ["decode8", "verify512"])
-def test_graph_capture_replays_match_eager(name):
+@pytest.mark.parametrize("name,bf16_shared", [("decode8", False), ("verify512", False), ("verify512", True)],
+                         ids=["decode8", "verify512", "verify512-bf16shared"])
+def test_graph_capture_replays_match_eager(name, bf16_shared):
     # The forward enqueues kernels only (no memsets, no host synchronisation), so
-    # one call can be captured in a HIP graph; every replay must equal the eager result.
-    wl = workload(name)
-    layer = _layer(wl)
-    x, tok, tab = _inputs(wl)
+    # one call can be captured in a HIP graph.  Replays alternate two different
+    # batches copied into the captured input buffer, with eager calls in between:
+    # each must equal the eager result of its batch (no state carried over).
+    from mxfp4_routed_expert_sqrt_amd import synth
+    wls = [workload(name, seed) for seed in (0, 1)]
+    sh = wls[0]["shape"]
+    dev = torch.device("cuda")
+    shared_bf16 = synth.gen_shared_bf16(sh) if bf16_shared else None
+    layer = MoELayer(sh, wls[0]["router_w"], PackedExperts(wls[0]["experts"], sh, dev, True), dev,
+                     router_bias=wls[0]["bias"], shared_bf16=shared_bf16)
+    xs = [_inputs(w)[0] for w in wls]
+    want = []
+    for xb in xs:
+        eager = layer.forward(xb, out=torch.empty_like(xb), workspace=layer.new_workspace(xb.shape[0]))
+        torch.cuda.synchronize()
+        want.append(eager.view(torch.int16).cpu().numpy())
+    assert not np.array_equal(want[0], want[1])
+    x = xs[0].clone()
     ws = layer.new_workspace(x.shape[0])
     out = torch.empty_like(x)
-    eager = layer.forward(x, tok, tab, out=torch.empty_like(x), workspace=layer.new_workspace(x.shape[0]))
-    torch.cuda.synchronize()
-    want = eager.view(torch.int16).cpu().numpy()
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):  # first call outside capture (one-time attribute setup)
-        layer.forward(x, tok, tab, out=out, workspace=ws)
+        layer.forward(x, out=out, workspace=ws)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    print(f"graph capture {name}", flush=True)
+    print(f"graph capture {name} bf16_shared={bf16_shared}", flush=True)
     with torch.cuda.graph(g, stream=side):
-        layer.forward(x, tok, tab, out=out, workspace=ws)
+        layer.forward(x, out=out, workspace=ws)
     for i in range(4):
         out.zero_()
-        layer.forward(x, tok, tab, out=torch.empty_like(x), workspace=layer.new_workspace(x.shape[0]))  # eager work in between
+        x.copy_(xs[i % 2])
+        layer.forward(xs[1 - i % 2], out=torch.empty_like(x), workspace=layer.new_workspace(x.shape[0]))  # eager work
         g.replay()
         torch.cuda.synchronize()
-        assert np.array_equal(out.view(torch.int16).cpu().numpy(), want), f"replay {i} differs"
+        assert np.array_equal(out.view(torch.int16).cpu().numpy(), want[i % 2]), f"replay {i} differs"
