@@ -28,7 +28,6 @@
 
 namespace moe {
 
-
 template <int J, bool FP6 = false>
 __device__ __forceinline__ v4f mfma_fp4_fp8(const u32x4& a, const v8i& b, const v4f& c, uint32_t sa, uint32_t sb) {
   const v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};

@@ -109,6 +109,24 @@ def test_tiny_full_parity():
     check_out(gpu["out"], ref["out"], "tiny")
 
 
+def test_exact_logit_ties_go_to_the_lower_expert_id():
+    # router rows duplicated in pairs (expert 2j+1 = expert 2j) give every logit twice, bit for bit on
+    # both sides; with k = 3 the third selection of every row falls in a tied pair, which the
+    # selection must resolve to the lower id, as the oracle does
+    sh = MoEShape("edge_ties", 64, 256, 16, 3, 128, "topk", "tiny")
+    wl = dict(workload(sh))
+    w = np.array(wl["router_w"], dtype=np.float32)
+    w[1::2] = w[0::2]
+    wl["router_w"] = w
+    gpu, *_ = run_gpu(wl)
+    ref = oracle_forward(wl)
+    for row in ref["idx"]:  # ids ascending: one complete pair, and the lower (even) id of the tied pair
+        pairs, n = np.unique(row // 2, return_counts=True)
+        assert sorted(n) == [1, 2] and row[row // 2 == pairs[n == 1][0]][0] % 2 == 0, row
+    check_routing(gpu, ref, "ties")
+    check_out(gpu["out"], ref["out"], "ties")
+
+
 def test_tiny_bitwise_deterministic_across_runs_and_streams():
     wl = workload("tiny")
     gpu, layer, x, tok, tab = run_gpu(wl)
