@@ -153,7 +153,10 @@ __device__ __forceinline__ void logits_tile(const uint16_t* __restrict__ x, cons
 // Workgroup 0 also clears the three counters of the launches that follow on
 // the stream: the selection's completion count and the unit claim counters of
 // gate/up and down.
-__global__ void __launch_bounds__(256) prologue_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
+// The bound of two workgroups per CU (at most 256 registers per lane) keeps
+// the MFMA accumulators in VGPRs; with the whole register file the compiler
+// placed them in AGPRs and copied them on every chunk.
+__global__ void __launch_bounds__(256, 2) prologue_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
                                                         int n_rows, int d, int E, int S, int n_tiles,
                                                         float* __restrict__ z_part, uint8_t* __restrict__ xq,
                                                         uint8_t* __restrict__ xs, int32_t* __restrict__ done, int fp6) {

@@ -84,8 +84,11 @@ __device__ __forceinline__ void sb_step(const uint8_t* buf, int kk, v4f (*acc)[4
 
 // NW = 2: gate/up tile, writes bf16 h [N][n_feat]; NW = 1: down tile, writes
 // fp32 y rows y_row0 + r of width n_feat.
+// The bound of two workgroups per CU (at most 256 registers per lane) keeps
+// the MFMA accumulators in VGPRs; with the whole register file the compiler
+// placed them in AGPRs and copied them on every chunk.
 template <int NW>
-__global__ void __launch_bounds__(256) shared_bf16_kernel(const uint16_t* __restrict__ a, int n_rows, int K,
+__global__ void __launch_bounds__(256, 2) shared_bf16_kernel(const uint16_t* __restrict__ a, int n_rows, int K,
                                                           const uint16_t* __restrict__ w0,
                                                           const uint16_t* __restrict__ w1, int n_feat, float limit,
                                                           uint16_t* __restrict__ h, float* __restrict__ y) {
