@@ -3,16 +3,28 @@
 expert, MXFP4 SwiGLU experts) on one MI355X, through the C ABI.
 
 One step = one moe_layer_forward over one batch of token rows with every input
-already resident in HBM: activation split, router logits, top-k selection,
-routing bookkeeping, gate/up GEMM, down GEMM, combine.  Default workload: the
+already resident in HBM: router logits and activation split, top-k selection,
+routing bookkeeping, gate/up GEMM, down GEMM, combine.  Headline workload: the
 512-row DSpark verify step (64 requests x 8 rows), d=4096, I=2048.
 
-Prints one JSON line (rank 0).  Besides the contract fields it carries
-- roofline: the gate/up GEMM (the dominant kernel) against HBM bandwidth, its
-  duration measured with HIP events recorded on the launch stream around that
-  kernel in every timed step;
-- cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
-  workload on this host (routing of all rows, outputs of the first rows).
+Protocol per workload: a pre-heat of layer calls for a fixed wall time (the
+GPU's clocks settle), the W warm-up steps, then exactly K timed steps between
+device synchronisations with no event recorded inside them (two HIP events on
+the launch stream bracket the whole window as a cross-check).  Kernel
+durations come from a separate loop of K steps after the timed window, with a
+HIP event before every stage on the launch stream (each record adds stream
+time between kernels, which is why they stay out of the timed steps).
+
+Prints one JSON line.  Besides the contract fields it carries
+- roofline: the dominant kernel (gate/up) against HBM bandwidth, its algorithmic
+  bytes (gate+up MXFP4 bytes of every touched expert + x) over its duration;
+  layer_frac: the whole layer's algorithmic bytes (touched experts' weights,
+  router weight, x, out) over ms_per_step;
+- workloads: the same measurement on the other layer configurations (8-row
+  decode with four weight copies rotated, 8192-row prefill with its FP4-MFMA
+  fraction, Zipf-skewed and hash-routed 2048-row batches);
+- cpu_baseline: the fp64 CPU oracle on a bounded sample of the headline
+  workload on this host (all host cores, and one core on 8 rows).
 """
 import argparse
 import ctypes
@@ -26,10 +38,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-EXPERT_BYTES_NOTE = "gate+up MXFP4 bytes of every touched expert (incl. shared) + x and h at 2 B/value"
-EXPERT_BYTES_NOTE_BF16 = ("gate+up MXFP4 bytes of every touched routed expert + the bf16 shared gate/up matrices "
-                          "+ x and h at 2 B/value (two kernels: routed grouped GEMM and bf16 shared GEMM)")
+FP4_PEAK_TFLOPS = 10100.0  # dense MXFP4 MFMA, MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_verify512_traffic.txt")
+EXTRA_WORKLOADS = ("decode8", "prefill8192", "zipf2048", "hash2048")
+DECODE_WEIGHT_COPIES = 4  # 8-row batches touch ~0.6 GB of weights: rotate copies past the 256 MB MALL
 
 
 def parse():
@@ -37,7 +49,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="verify512")
+    ap.add_argument("--preheat-s", type=float, default=1.0,
+                    help="wall time of untimed layer calls before the warm-up steps of each workload")
+    ap.add_argument("--workload", default="verify512", help="the headline workload")
+    ap.add_argument("--only", action="store_true", help="measure the headline workload only")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -64,6 +79,7 @@ class Hip:
     def __init__(self):
         self.lib = ctypes.CDLL("libamdhip64.so")
         self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
@@ -72,6 +88,10 @@ class Hip:
         if self.lib.hipEventCreateWithFlags(ctypes.byref(ev), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
             raise RuntimeError("hipEventCreateWithFlags failed")
         return ev.value
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -109,7 +129,133 @@ def recorded_traffic(workload):
         return None
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---------------------------------------------------------------- byte model
+
+def mxfp4_matrix_bytes(rows, K):
+    return rows * K // 2 + rows * K // 32  # E2M1 nibbles + one E8M0 byte per 32 values
+
+
+def algorithmic(shape, touched_routed, shared_bf16=False, has_bias=False):
+    """Algorithmic HBM bytes and FP4-equivalent flops of the layer and its two GEMMs.
+
+    Bytes: weights of every touched expert (an expert with no rows reads none) + router weight + x + out
+    (+ bias, token ids and the rows' table entries in hash mode).  Intermediates (logits, h, y, index
+    arrays) are implementation traffic, not algorithmic bytes.  Flops: 2 per multiply-add of the FP4
+    weights (6*d*I per (row, expert): gate, up, down), whatever the activation format.
+    """
+    N, d, I, E, k = shape.n_rows, shape.d_model, shape.d_ff, shape.n_experts, shape.top_k
+    m = mxfp4_matrix_bytes(I, d)  # gate, up [I][d] and down [d][I] have the same size
+    sh_mat = I * d * 2 if shared_bf16 else m
+    x_bytes = out_bytes = N * d * 2
+    extra = (E * 4 if has_bias else 0) + ((N * 4 + N * k * 4) if shape.routing == "hash" else 0)
+    pairs = N * (k + 1)
+    return {
+        "layer_bytes": touched_routed * 3 * m + 3 * sh_mat + E * d * 4 + x_bytes + out_bytes + extra,
+        "gateup_bytes": touched_routed * 2 * m + 2 * sh_mat + x_bytes,
+        "down_bytes": touched_routed * m + sh_mat,
+        "layer_flops": 6 * d * I * pairs,
+        "gateup_flops": 4 * d * I * pairs,
+        "down_flops": 2 * d * I * pairs,
+    }
+
+
+# ---------------------------------------------------------------- measurement
+
+class Runner:
+    """Runs one workload's layer calls on the current stream and times them."""
+
+    def __init__(self, hip, layer, calls, stream):
+        from mxfp4_routed_expert_sqrt_amd import capi
+        self.capi, self.hip, self.layer, self.calls, self.stream = capi, hip, layer, calls, stream
+        self.i = 0
+
+    def step(self, events=None):
+        call = self.calls[self.i % len(self.calls)]
+        self.i += 1
+        call.stage_events = events
+        rc = self.capi.moe_layer_forward(self.layer.cfg, call, self.stream)
+        call.stage_events = None
+        if rc != self.capi.MOE_OK:
+            raise self.capi.MoeError(rc)
+
+    def run(self, K, W, preheat_s):
+        import numpy as np
+        import torch
+        capi, hip = self.capi, self.hip
+        # pre-heat for a fixed wall time, synchronising every 16 calls
+        t0, n_pre = time.perf_counter(), 0
+        while time.perf_counter() - t0 < preheat_s:
+            for _ in range(16):
+                self.step()
+            n_pre += 16
+            torch.cuda.synchronize()
+        preheat = time.perf_counter() - t0
+        for _ in range(W):
+            self.step()
+        torch.cuda.synchronize()
+        ev0, ev1 = hip.event(), hip.event()
+        t0 = time.perf_counter()
+        hip.record(ev0, self.stream)
+        for _ in range(K):
+            self.step()
+        hip.record(ev1, self.stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        gpu_ms = hip.elapsed_ms(ev0, ev1)
+        # kernel durations: a separate loop of K steps with an event before every stage
+        evs = [[hip.event() for _ in range(capi.MOE_N_STAGE_EVENTS)] for _ in range(K)]
+        arrays = [(ctypes.c_void_p * capi.MOE_N_STAGE_EVENTS)(*e) for e in evs]
+        for i in range(K):
+            self.step(ctypes.cast(arrays[i], ctypes.c_void_p))
+        torch.cuda.synchronize()
+        stage_ms = np.array([[hip.elapsed_ms(e[s], e[s + 1]) for s in range(capi.MOE_N_STAGES)] for e in evs])
+        for e in evs + [[ev0, ev1]]:
+            for x in e:
+                hip.destroy(x)
+        return {"preheat_s": preheat, "preheat_calls": n_pre, "ms_per_step": elapsed * 1e3 / K,
+                "gpu_ms_per_step": gpu_ms / K,
+                "stages_us": {n: float(np.mean(stage_ms[:, s])) * 1e3 for s, n in enumerate(capi.STAGE_NAMES)}}
+
+
+def summarise(shape, timing, touched_routed, shared_bf16=False, has_bias=False):
+    a = algorithmic(shape, touched_routed, shared_bf16, has_bias)
+    t = timing["ms_per_step"] * 1e-3
+    gu, dn = timing["stages_us"]["gateup"] * 1e-6, timing["stages_us"]["down"] * 1e-6
+    r = lambda v: round(v, 4)
+    return {
+        "rows": shape.n_rows,
+        "rows_per_s": shape.n_rows / t,
+        "us_per_step": timing["ms_per_step"] * 1e3,
+        "gpu_event_us_per_step": timing["gpu_ms_per_step"] * 1e3,
+        "touched_experts": touched_routed + 1,
+        "layer": {"algorithmic_bytes": a["layer_bytes"], "hbm_frac": r(a["layer_bytes"] / t / 1e9 / HBM_PEAK_GBS),
+                  "fp4_flops": a["layer_flops"], "fp4_frac": r(a["layer_flops"] / t / 1e12 / FP4_PEAK_TFLOPS)},
+        "gateup": {"us": timing["stages_us"]["gateup"], "algorithmic_bytes": a["gateup_bytes"],
+                   "hbm_frac": r(a["gateup_bytes"] / gu / 1e9 / HBM_PEAK_GBS),
+                   "fp4_frac": r(a["gateup_flops"] / gu / 1e12 / FP4_PEAK_TFLOPS)},
+        "down": {"us": timing["stages_us"]["down"], "algorithmic_bytes": a["down_bytes"],
+                 "hbm_frac": r(a["down_bytes"] / dn / 1e9 / HBM_PEAK_GBS),
+                 "fp4_frac": r(a["down_flops"] / dn / 1e12 / FP4_PEAK_TFLOPS)},
+        "stages_us": {k: round(v, 2) for k, v in timing["stages_us"].items()},
+        "preheat_s": round(timing["preheat_s"], 3),
+        "preheat_calls": timing["preheat_calls"],
+    }
+
+
 def cpu_baseline(shape, x, router_w, experts, rows, bias=None, token_ids=None, tid2eid=None):
+    import numpy as np
+
     import oracle
     from mxfp4_routed_expert_sqrt_amd.synth import usable_cpus
     threads = usable_cpus()
@@ -117,14 +263,103 @@ def cpu_baseline(shape, x, router_w, experts, rows, bias=None, token_ids=None, t
     # repeated until at least 10 s of CPU work (at most 3 passes) so that the rate is not a single short run
     passes, t0 = 0, time.perf_counter()
     while passes < 3 and (passes == 0 or time.perf_counter() - t0 < 10.0):
-        oracle.forward(shape, x, router_w, experts, router_bias=bias, token_ids=token_ids, tid2eid=tid2eid,
-                       rows=sample, threads=threads)
+        ref = oracle.forward(shape, x, router_w, experts, router_bias=bias, token_ids=token_ids, tid2eid=tid2eid,
+                             rows=sample, threads=threads)
         passes += 1
     dt = time.perf_counter() - t0
+    # one core on 8 rows (the 8-row decode batch's size; every expert those rows touch decoded once)
+    one = list(range(min(8, shape.n_rows)))
+    t1 = time.perf_counter()
+    oracle.forward(shape, x, router_w, experts, router_bias=bias, token_ids=token_ids, tid2eid=tid2eid, rows=one,
+                   threads=1)
+    dt1 = time.perf_counter() - t1
+    # the oracle's rounding floor: what one bf16 rounding of its own output costs against the bar
+    out = ref["out"]
+    u = out.astype(np.float32).view(np.uint32)  # fp32 then bf16, each to nearest even, as the combine rounds
+    rounded = (((u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16) << 16).view(np.float32)
+    err = np.abs(rounded.astype(np.float64) - out)
     return {"value": passes * len(sample) / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"fp64 oracle on rows 0..{len(sample) - 1} of the {shape.n_rows}-row {shape.name} batch "
                       f"(routing of all {shape.n_rows} rows, every touched expert decoded once), same inputs, "
-                      f"{passes} pass(es); {dt:.1f} s wall"}
+                      f"{passes} pass(es); {dt:.1f} s wall",
+            "one_core": {"rows": len(one), "seconds": dt1, "rows_per_s": len(one) / dt1},
+            "rounding_floor": {"max_err_over_rms": float(err.max() / np.sqrt(np.mean(out ** 2))),
+                               "mean_rel": float(err.sum() / np.abs(out).sum())}}
+
+
+# ---------------------------------------------------------------- workloads
+
+def calibrate_zipf_bias(shape, layer, x, steps=120, damping=0.25, seed=0):
+    """Logit bias that steers the per-row selection probability of expert e towards the Zipf(1.2) target
+    q_e: b_e += 0.25 * (ln q_e - ln max(q_hat_e, 1/(2N))), q_hat from the layer's own counts, 120 steps,
+    then frozen (the recipe of the parity tests, with the layer's routing in place of the oracle's)."""
+    import numpy as np
+    import torch
+
+    from mxfp4_routed_expert_sqrt_amd import synth
+    q = synth.zipf_targets(shape, seed=seed)
+    floor = 1.0 / (2 * shape.n_rows)
+    b = np.zeros(shape.n_experts, dtype=np.float32)
+    for _ in range(steps):
+        layer.router_bias.copy_(torch.from_numpy(b))
+        _, routing = layer.forward(x, with_routing=True)
+        q_hat = routing["counts"].cpu().numpy() / shape.n_rows
+        b = (b.astype(np.float64) + damping * (np.log(q) - np.log(np.maximum(q_hat, floor)))).astype(np.float32)
+    layer.router_bias.copy_(torch.from_numpy(b))
+    torch.cuda.synchronize()
+    return b
+
+
+def measure_workload(name, ctx, args, hip):
+    import numpy as np
+    import torch
+
+    from mxfp4_routed_expert_sqrt_amd import synth
+    from mxfp4_routed_expert_sqrt_amd.configs import SHAPES
+    from mxfp4_routed_expert_sqrt_amd.layer import MoELayer
+
+    shape = SHAPES[name]
+    dev = ctx["dev"]
+    x_np = synth.gen_x(shape, args.seed)
+    x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    tok = tab = None
+    if shape.routing == "hash":
+        tok = torch.from_numpy(synth.gen_token_ids(shape, args.seed)).to(dev)
+        tab = torch.from_numpy(synth.gen_tid2eid(shape, args.seed)).to(dev)
+    bias = np.zeros(shape.n_experts, dtype=np.float32) if shape.bias == "zipf" else None
+    layer = MoELayer(shape, ctx["router_w"], ctx["packed"], dev, router_bias=bias)
+    note = None
+    if shape.bias == "zipf":
+        calibrate_zipf_bias(shape, layer, x, seed=args.seed)
+    _, routing = layer.forward(x, tok, tab, with_routing=True)
+    torch.cuda.synchronize()
+    counts = routing["counts"].cpu().numpy()
+    touched = int((counts > 0).sum())
+    copies = [ctx["packed"]]
+    if name == "decode8":
+        while len(ctx["copies"]) < DECODE_WEIGHT_COPIES - 1:
+            ctx["copies"].append(ctx["packed"].copy())
+        copies += ctx["copies"]
+        torch.cuda.synchronize()
+        note = f"{len(copies)} device copies of the packed weights, used in turn"
+    out = torch.empty_like(x)
+    ws = layer.new_workspace(shape.n_rows)
+    calls = []
+    for c in copies:
+        layer.experts = c
+        calls.append(layer.args(x, out, ws, tok, tab))
+    layer.experts = ctx["packed"]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    timing = Runner(hip, layer, calls, stream).run(args.steps, args.warmup, args.preheat_s)
+    res = summarise(shape, timing, touched, has_bias=bias is not None)
+    if note:
+        res["weights"] = note
+    if shape.bias == "zipf":
+        load = counts / shape.n_rows
+        res["hottest_expert_share_of_assignments"] = round(float(load.max() / shape.top_k), 4)
+    del ws, out
+    return res
 
 
 def main():
@@ -138,13 +373,13 @@ def main():
     import numpy as np
     import torch
 
-    from mxfp4_routed_expert_sqrt_amd import capi, synth
+    from mxfp4_routed_expert_sqrt_amd import synth
     from mxfp4_routed_expert_sqrt_amd.configs import SHAPES
-    from mxfp4_routed_expert_sqrt_amd.layer import MoELayer
+    from mxfp4_routed_expert_sqrt_amd.layer import MoELayer, PackedExperts
 
     shape = SHAPES[args.workload]
     if shape.bias != "none":
-        raise SystemExit(f"{shape.name} needs a calibrated router bias; benchmark a top-k or hash workload")
+        raise SystemExit(f"{shape.name} needs a calibrated router bias: it runs in the workloads block")
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
     x_np = synth.gen_x(shape, args.seed)
@@ -160,7 +395,8 @@ def main():
         norm_w = synth.gen_norm_weight(shape, args.seed)
         resid = torch.from_numpy(synth.gen_residual(shape, args.seed).view(np.int16)).to(dev).view(torch.bfloat16)
     shared_bf16 = synth.gen_shared_bf16(shape, args.seed) if args.shared_bf16 else None
-    layer = MoELayer(shape, w_np, experts, dev, norm_w=norm_w, shared_bf16=shared_bf16)
+    packed = PackedExperts(experts, shape, dev, True)
+    layer = MoELayer(shape, w_np, packed, dev, norm_w=norm_w, shared_bf16=shared_bf16)
     x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
     tok = None if tok_np is None else torch.from_numpy(tok_np).to(dev)
     tab = None if tab_np is None else torch.from_numpy(tab_np).to(dev)
@@ -170,65 +406,15 @@ def main():
     # routing of this batch (untimed): touched experts for the byte count
     _, routing = layer.forward(x, tok, tab, with_routing=True, residual=resid)
     torch.cuda.synchronize()
-    counts = routing["counts"].cpu().numpy()
-    touched = int((counts > 0).sum()) + 1  # + shared expert
-    N, d, I, E = shape.n_rows, shape.d_model, shape.d_ff, shape.n_experts
-    per_expert = 3 * (I * d // 2 + I * d // 32)
-    if args.shared_bf16:  # the grouped kernels then carry the routed experts only
-        layer_bytes = (touched - 1) * per_expert + 3 * I * d * 2 + E * d * 4 + 2 * N * d * 2
-        # the gate/up stage then times two kernels: the routed grouped GEMM and the bf16 shared GEMM
-        gateup_bytes = ((touched - 1) * 2 * (I * d // 2 + I * d // 32) + N * d * 2 + N * shape.top_k * I * 2
-                        + 2 * I * d * 2 + N * I * 2)
-    else:
-        layer_bytes = touched * per_expert + E * d * 4 + 2 * N * d * 2
-        gateup_bytes = touched * 2 * (I * d // 2 + I * d // 32) + N * d * 2 + (N * shape.top_k + N) * I * 2
+    touched = int((routing["counts"].cpu().numpy() > 0).sum())
 
     hip = Hip()
     stream = torch.cuda.current_stream(dev).cuda_stream
     K, W = args.steps, args.warmup
-    call = layer.args(x, out, ws, tok, tab, residual=resid)
-    G = capi.STAGE_NAMES.index("gateup")
-
-    def step(ev=None):
-        call.stage_events = ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None
-        rc = capi.moe_layer_forward(layer.cfg, call, stream)
-        if rc != capi.MOE_OK:
-            raise capi.MoeError(rc)
-
-    def event_array(evs):
-        return (ctypes.c_void_p * capi.MOE_N_STAGE_EVENTS)(*evs)
-
-    # timed steps: the only events recorded are the two around the gate/up
-    # kernel, in every EV_STRIDE-th step (each event record costs ~9 us of
-    # stream time, so events in every step would slow the measured step)
-    ev_stride = max(1, K // 8)
-    sampled = list(range(0, K, ev_stride))
-    gu_events = [(hip.event(), hip.event()) for _ in sampled]
-    gu_arrays = {i: event_array([a if s == G else b if s == G + 1 else None for s in range(capi.MOE_N_STAGE_EVENTS)])
-                 for i, (a, b) in zip(sampled, gu_events)}
-    for _ in range(W):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(gu_arrays.get(i))
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    gateup_ms = np.array([hip.elapsed_ms(a, b) for a, b in gu_events])
-
-    # per-stage breakdown (untimed steps with every stage event recorded)
-    KB = min(K, 20)
-    events = [[hip.event() for _ in range(capi.MOE_N_STAGE_EVENTS)] for _ in range(KB)]
-    ev_arrays = [event_array(evs) for evs in events]
-    for i in range(KB):
-        step(ev_arrays[i])
-    torch.cuda.synchronize()
-    stage_ms = np.array([[hip.elapsed_ms(events[i][s], events[i][s + 1]) for s in range(capi.MOE_N_STAGES)]
-                         for i in range(KB)])
-    gpu_ms = np.array([hip.elapsed_ms(events[i][0], events[i][-1]) for i in range(KB)])
-    for evs in events + [list(p) for p in gu_events]:
-        for e in evs:
-            hip.destroy(e)
+    print(f"[bench] {shape.name}: pre-heat {args.preheat_s:.1f}s, {W} warm-up, {K} timed steps", file=sys.stderr,
+          flush=True)
+    timing = Runner(hip, layer, [layer.args(x, out, ws, tok, tab, residual=resid)], stream).run(K, W, args.preheat_s)
+    head = summarise(shape, timing, touched, shared_bf16=args.shared_bf16)
 
     if args.copy_calibration:
         # one elementwise kernel that reads 1 GiB and writes 1 GiB (a device copy may go to a DMA engine,
@@ -240,11 +426,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ms_per_step = elapsed * 1e3 / K
-    stages_us = {n: round(float(np.mean(stage_ms[:, s])) * 1e3, 2) for s, n in enumerate(capi.STAGE_NAMES)}
-    t_gateup = float(np.mean(gateup_ms)) * 1e-3
-    achieved = gateup_bytes / t_gateup / 1e9
-    traffic = None if args.shared_bf16 else recorded_traffic(shape.name)
+    N, d, I, E = shape.n_rows, shape.d_model, shape.d_ff, shape.n_experts
+    ms_per_step = timing["ms_per_step"]
+    gu = head["gateup"]
+    achieved = gu["algorithmic_bytes"] / (gu["us"] * 1e-6) / 1e9
+    traffic = None if (args.shared_bf16 or args.with_norm) else recorded_traffic(shape.name)
     result = {
         "metric": "MoE-layer token rows/s at 512-row verify" if shape.name == "verify512"
         else f"MoE-layer token rows/s ({shape.name})",
@@ -253,6 +439,8 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
+        "preheat_s": round(timing["preheat_s"], 3),
+        "preheat_calls": timing["preheat_calls"],
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -269,15 +457,26 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gateup_kernel" + (" + shared_bf16_kernel<2>" if args.shared_bf16 else ""),
-                     "algorithmic_bytes": gateup_bytes,
-                     "bytes_definition": EXPERT_BYTES_NOTE_BF16 if args.shared_bf16 else EXPERT_BYTES_NOTE,
-                     "kernel_us": t_gateup * 1e6,
-                     "kernel_timing": f"HIP events around the gate/up kernel in {len(sampled)} of the {K} timed steps"},
-        "layer": {"algorithmic_bytes": layer_bytes, "hbm_frac": layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                  "touched_experts": touched, "stages_us": stages_us,
-                  "stages_note": "separate untimed steps with an event before every stage (each event adds a few us)",
-                  "gpu_us_per_step_with_stage_events": float(np.mean(gpu_ms)) * 1e3},
+                     "algorithmic_bytes": gu["algorithmic_bytes"],
+                     "bytes_definition": "gate+up MXFP4 bytes (nibbles + E8M0 scales) of every touched expert, "
+                                         "incl. the shared one, + x (bf16)",
+                     "kernel_us": gu["us"],
+                     "kernel_timing": f"HIP events before every stage in a separate loop of {K} steps after the "
+                                      "timed window, on the launch stream",
+                     "layer_frac": head["layer"]["hbm_frac"],
+                     "layer_bytes_definition": "MXFP4 weights of every touched expert + router weight fp32 + x + "
+                                               "out (bf16), over ms_per_step"},
+        "layer": head,
     }
+    if not args.only:
+        ctx = {"dev": dev, "router_w": w_np, "packed": packed, "copies": []}
+        result["workloads"] = {}
+        for name in EXTRA_WORKLOADS:
+            if name == shape.name:
+                continue
+            print(f"[bench] workload {name}", file=sys.stderr, flush=True)
+            result["workloads"][name] = measure_workload(name, ctx, args, hip)
+        del ctx
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(shape, x_np, w_np, experts, args.cpu_sample_rows,

@@ -40,6 +40,12 @@
  *     stream).  No allocation, no host<->device copy, no host synchronisation.
  *   - Results are bitwise reproducible for identical inputs and sizes.
  *   - Concurrent calls are safe when their workspaces and outputs differ.
+ *   - Buffers the layer writes (out, the workspace, the optional routing
+ *     outputs) must not overlap any other buffer of the call: inputs, packed
+ *     weights (each weight set over its full packed size), hash-mode token
+ *     ids and the whole tid2eid table, or each other.  The one exception is a
+ *     residual that is `out` itself.  Inputs may overlap each other.  A call
+ *     that breaks this returns MOE_ERR_INVALID and enqueues nothing.
  */
 #ifndef MOE_MXFP4_H
 #define MOE_MXFP4_H
@@ -125,7 +131,7 @@ typedef struct moe_args {
                                  out-of-bounds access (token and expert ids are clamped) */
   int64_t vocab;              /* hash mode: rows of tid2eid */
   moe_weights_t w;            /* packed expert weights */
-  void* out;                  /* bf16 [N][d], 16-byte aligned; must not overlap x */
+  void* out;                  /* bf16 [N][d], 16-byte aligned; must not overlap x or any other buffer */
   /* Optional outputs (NULL to skip), for inspection of the routing:
    *   topk_idx [N][k] int32 ascending expert ids;  topk_w [N][k] fp32 gates;
    *   counts [E] rows per expert; offsets [E+1] exclusive prefix sum of counts;
@@ -138,8 +144,7 @@ typedef struct moe_args {
   int32_t* perm;
   int32_t* inv;
   void* workspace;            /* device scratch, 256-byte aligned, >= moe_workspace_size(); must not
-                                 overlap out, x, router_w, router_bias, norm_w, residual or the bf16
-                                 shared-expert weights */
+                                 overlap any other buffer of the call */
   size_t workspace_bytes;
   /* Optional stage timing (NULL to skip): MOE_N_STAGE_EVENTS hipEvent_t handles
    * created by the caller.  Event i is recorded on `stream` just before stage i

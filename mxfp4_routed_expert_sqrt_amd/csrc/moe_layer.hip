@@ -83,68 +83,72 @@ int check_mat(const void* q, const void* s) {
   return MOE_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int moe_version(void) { return MOE_MXFP4_VERSION; }
-
-const char* moe_status_string(int status) {
-  switch (status) {
-    case MOE_OK: return "ok";
-    case MOE_ERR_INVALID: return "invalid argument";
-    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
-    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
-    case MOE_ERR_HIP: return "HIP launch failed";
-    default: return "unknown status";
+// Every buffer the layer writes (out, the workspace, the optional routing
+// outputs) must be disjoint from every other buffer of the call, read or
+// written; the one exception is a residual that is `out` itself.  Sizes of
+// the read buffers are those the layer reads: each packed weight set in full,
+// the token ids and the whole tid2eid table in hash mode.
+bool buffers_disjoint(const moe_config_t& c, const moe_args_t& a, const void* ws, size_t ws_bytes) {
+  struct Region {
+    const void* p;
+    size_t n;
+    bool written;
+  };
+  const size_t N = (size_t)a.n_rows, d = (size_t)c.d_model, I = (size_t)c.d_ff, E = (size_t)c.n_experts,
+               k = (size_t)c.top_k;
+  const size_t gq = packed_q_bytes(c.d_ff, c.d_model), gs = packed_s_bytes(c.d_ff, c.d_model);
+  const size_t dq = packed_q_bytes(c.d_model, c.d_ff), ds = packed_s_bytes(c.d_model, c.d_ff);
+  Region r[32];
+  int n = 0;
+  auto add = [&](const void* p, size_t bytes, bool written) {
+    if (p && bytes) r[n++] = Region{p, bytes, written};
+  };
+  add(a.out, N * d * 2, true);
+  add(ws, ws_bytes, true);
+  add(a.topk_idx, N * k * 4, true);
+  add(a.topk_w, N * k * 4, true);
+  add(a.counts, E * 4, true);
+  add(a.offsets, (E + 1) * 4, true);
+  add(a.perm, N * k * 4, true);
+  add(a.inv, N * k * 4, true);
+  add(a.x, N * d * 2, false);
+  add(a.router_w, E * d * 4, false);
+  add(a.router_bias, E * 4, false);
+  add(a.norm_w, a.norm_w ? d * 2 : 0, false);
+  if (a.residual != a.out) add(a.residual, N * d * 2, false);
+  add(a.w.gate_q, E * gq, false);
+  add(a.w.gate_s, E * gs, false);
+  add(a.w.up_q, E * gq, false);
+  add(a.w.up_s, E * gs, false);
+  add(a.w.down_q, E * dq, false);
+  add(a.w.down_s, E * ds, false);
+  if (shared_in_list(c)) {
+    add(a.w.sh_gate_q, gq, false);
+    add(a.w.sh_gate_s, gs, false);
+    add(a.w.sh_up_q, gq, false);
+    add(a.w.sh_up_s, gs, false);
+    add(a.w.sh_down_q, dq, false);
+    add(a.w.sh_down_s, ds, false);
   }
+  if (shared_bf16(c)) {
+    add(a.w.sh_gate_w, I * d * 2, false);
+    add(a.w.sh_up_w, I * d * 2, false);
+    add(a.w.sh_down_w, I * d * 2, false);
+  }
+  if (c.routing == MOE_ROUTING_HASH) {
+    add(a.token_ids, N * 4, false);
+    add(a.tid2eid, (size_t)a.vocab * k * 4, false);
+  }
+  for (int i = 0; i < n; ++i)
+    for (int j = i + 1; j < n; ++j)
+      if ((r[i].written || r[j].written) && overlap(r[i].p, r[i].n, r[j].p, r[j].n)) return false;
+  return true;
 }
 
-int moe_packed_mxfp4_bytes(int32_t rows, int32_t K, size_t* q_bytes, size_t* s_bytes) {
-  if (!q_bytes || !s_bytes) return MOE_ERR_INVALID;
-  if (rows < 16 || rows % 16 || K < 128 || K % 128) return MOE_ERR_UNSUPPORTED;
-  *q_bytes = packed_q_bytes(rows, K);
-  *s_bytes = packed_s_bytes(rows, K);
-  return MOE_OK;
-}
-
-int moe_pack_mxfp4(const void* q, const void* s, int32_t n_mat, int32_t rows, int32_t K, void* q_out, void* s_out,
-                   void* stream) {
-  if (n_mat < 0) return MOE_ERR_INVALID;
-  if (rows < 16 || rows % 16 || K < 128 || K % 128 || rows > 65536 || K > 65536) return MOE_ERR_UNSUPPORTED;
-  if (n_mat == 0) return MOE_OK;
-  if (!q || !s || !q_out || !s_out) return MOE_ERR_INVALID;
-  if (!aligned(q, 16) || !aligned(q_out, 16) || !aligned(s_out, 4)) return MOE_ERR_INVALID;
-  const size_t nq = (size_t)n_mat * packed_q_bytes(rows, K);
-  const size_t ns_in = (size_t)n_mat * rows * (K / 32), ns_out = (size_t)n_mat * packed_s_bytes(rows, K);
-  if (overlap(q, nq, q_out, nq) || overlap(s, ns_in, s_out, ns_out) || overlap(q, nq, s_out, ns_out) ||
-      overlap(s, ns_in, q_out, nq))
-    return MOE_ERR_INVALID;
-  hipError_t err = launch_pack_mxfp4((const uint8_t*)q, (const uint8_t*)s, n_mat, rows, K, (uint8_t*)q_out,
-                                     (uint8_t*)s_out, (hipStream_t)stream);
-  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
-}
-
-int moe_workspace_size(const moe_config_t* cfg, int32_t n_rows, size_t* bytes) {
-  int rc = check_config(cfg);
-  if (rc) return rc;
-  if (!bytes || n_rows < 0) return MOE_ERR_INVALID;
-  if (n_rows > MOE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
-  *bytes = n_rows == 0 ? 0 : make_layout(*cfg, n_rows).total;
-  return MOE_OK;
-}
-
-int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* stream_) {
-  int rc = check_config(cfg);
-  if (rc) return rc;
-  if (!args) return MOE_ERR_INVALID;
-  const moe_config_t& c = *cfg;
-  const moe_args_t& a = *args;
-  const int N = a.n_rows;
-  if (N < 0) return MOE_ERR_INVALID;
-  if (N > MOE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
-  if (N == 0) return MOE_OK;
-  const int d = c.d_model, I = c.d_ff, E = c.n_experts, k = c.top_k;
+// Every argument check of the layer call except those on the workspace
+// (host-only; nothing is enqueued).  n_rows > 0.
+int check_args(const moe_config_t& c, const moe_args_t& a) {
+  int rc;
   if (!a.x || !a.router_w || !a.out) return MOE_ERR_INVALID;
   if (!aligned(a.x, 16) || !aligned(a.router_w, 16) || !aligned(a.out, 16)) return MOE_ERR_INVALID;
   if (a.router_bias && !aligned(a.router_bias, 4)) return MOE_ERR_INVALID;
@@ -155,7 +159,6 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
                              (rc = check_mat(a.w.sh_up_q, a.w.sh_up_s)) ||
                              (rc = check_mat(a.w.sh_down_q, a.w.sh_down_s))))
     return rc;
-  const size_t sh_w_bytes = (size_t)I * d * 2;  // each bf16 shared matrix
   if (shared_bf16(c)) {
     const void* shw[] = {a.w.sh_gate_w, a.w.sh_up_w, a.w.sh_down_w};
     for (const void* p : shw)
@@ -168,29 +171,15 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   const void* opt[] = {a.topk_idx, a.topk_w, a.counts, a.offsets, a.perm, a.inv};
   for (const void* p : opt)
     if (p && !aligned(p, 4)) return MOE_ERR_INVALID;
-  const size_t out_bytes = (size_t)N * d * 2;
-  if (overlap(a.out, out_bytes, a.x, out_bytes)) return MOE_ERR_INVALID;
   if (a.norm_w && !aligned(a.norm_w, 16)) return MOE_ERR_INVALID;
-  if (a.residual && (!aligned(a.residual, 16) || (a.residual != a.out && overlap(a.residual, out_bytes, a.out, out_bytes))))
-    return MOE_ERR_INVALID;
-  const Layout L = make_layout(c, N);
-  if (!a.workspace || a.workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
-  if (!aligned(a.workspace, 256)) return MOE_ERR_INVALID;
-  if (overlap(a.out, out_bytes, a.workspace, L.total)) return MOE_ERR_INVALID;
-  // inputs read after the workspace is first written must not lie inside it
-  if (overlap(a.x, out_bytes, a.workspace, L.total) ||
-      overlap(a.router_w, (size_t)E * d * 4, a.workspace, L.total) ||
-      (a.router_bias && overlap(a.router_bias, (size_t)E * 4, a.workspace, L.total)) ||
-      (a.norm_w && overlap(a.norm_w, (size_t)d * 2, a.workspace, L.total)) ||
-      (a.residual && overlap(a.residual, out_bytes, a.workspace, L.total)))
-    return MOE_ERR_INVALID;
-  if (shared_bf16(c) && (overlap(a.w.sh_gate_w, sh_w_bytes, a.workspace, L.total) ||
-                         overlap(a.w.sh_up_w, sh_w_bytes, a.workspace, L.total) ||
-                         overlap(a.w.sh_down_w, sh_w_bytes, a.workspace, L.total)))
-    return MOE_ERR_INVALID;
+  if (a.residual && !aligned(a.residual, 16)) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
 
-  hipStream_t stream = (hipStream_t)stream_;
-  uint8_t* ws = (uint8_t*)a.workspace;
+// The launch sequence of one layer call on workspace ws (laid out as L).
+int run_layer(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const Layout& L, hipStream_t stream) {
+  const int N = a.n_rows;
+  const int d = c.d_model, I = c.d_ff, E = c.n_experts, k = c.top_k;
   float* z = (float*)(ws + L.z);
   int32_t* idx = a.topk_idx ? a.topk_idx : (int32_t*)(ws + L.idx);
   float* gates = a.topk_w ? a.topk_w : (float*)(ws + L.gates);
@@ -289,6 +278,75 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
     return MOE_ERR_HIP;
   if (!mark(5)) return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return MOE_MXFP4_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_packed_mxfp4_bytes(int32_t rows, int32_t K, size_t* q_bytes, size_t* s_bytes) {
+  if (!q_bytes || !s_bytes) return MOE_ERR_INVALID;
+  if (rows < 16 || rows % 16 || K < 128 || K % 128) return MOE_ERR_UNSUPPORTED;
+  *q_bytes = packed_q_bytes(rows, K);
+  *s_bytes = packed_s_bytes(rows, K);
+  return MOE_OK;
+}
+
+int moe_pack_mxfp4(const void* q, const void* s, int32_t n_mat, int32_t rows, int32_t K, void* q_out, void* s_out,
+                   void* stream) {
+  if (n_mat < 0) return MOE_ERR_INVALID;
+  if (rows < 16 || rows % 16 || K < 128 || K % 128 || rows > 65536 || K > 65536) return MOE_ERR_UNSUPPORTED;
+  if (n_mat == 0) return MOE_OK;
+  if (!q || !s || !q_out || !s_out) return MOE_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(q_out, 16) || !aligned(s_out, 4)) return MOE_ERR_INVALID;
+  const size_t nq = (size_t)n_mat * packed_q_bytes(rows, K);
+  const size_t ns_in = (size_t)n_mat * rows * (K / 32), ns_out = (size_t)n_mat * packed_s_bytes(rows, K);
+  if (overlap(q, nq, q_out, nq) || overlap(s, ns_in, s_out, ns_out) || overlap(q, nq, s_out, ns_out) ||
+      overlap(s, ns_in, q_out, nq))
+    return MOE_ERR_INVALID;
+  hipError_t err = launch_pack_mxfp4((const uint8_t*)q, (const uint8_t*)s, n_mat, rows, K, (uint8_t*)q_out,
+                                     (uint8_t*)s_out, (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_workspace_size(const moe_config_t* cfg, int32_t n_rows, size_t* bytes) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!bytes || n_rows < 0) return MOE_ERR_INVALID;
+  if (n_rows > MOE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
+  *bytes = n_rows == 0 ? 0 : make_layout(*cfg, n_rows).total;
+  return MOE_OK;
+}
+
+int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!args) return MOE_ERR_INVALID;
+  const moe_config_t& c = *cfg;
+  const moe_args_t& a = *args;
+  if (a.n_rows < 0) return MOE_ERR_INVALID;
+  if (a.n_rows > MOE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
+  if (a.n_rows == 0) return MOE_OK;
+  if ((rc = check_args(c, a))) return rc;
+  const Layout L = make_layout(c, a.n_rows);
+  if (!a.workspace || a.workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(a.workspace, 256)) return MOE_ERR_INVALID;
+  if (!buffers_disjoint(c, a, a.workspace, L.total)) return MOE_ERR_INVALID;
+  return run_layer(c, a, (uint8_t*)a.workspace, L, (hipStream_t)stream);
 }
 
 }  // extern "C"

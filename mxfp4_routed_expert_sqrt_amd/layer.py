@@ -65,20 +65,32 @@ class PackedExperts:
                 for part, nbytes in (("q", count * qb), ("s", count * sb)):
                     regions[(key, part)] = (total, nbytes)
                     total += (nbytes + _ALIGN - 1) // _ALIGN * _ALIGN
-        self.buffer = torch.empty(total + _ALIGN, dtype=torch.uint8, device=device)
-        base = (-self.buffer.data_ptr()) % _ALIGN
-        view = lambda key, part: self.buffer[base + regions[(key, part)][0]:][:regions[(key, part)][1]]
-        self.t = {}
+        self._regions, self._total = regions, total
+        self._alloc(device)
         for name, rows, K in mats:
             q = torch.from_numpy(np.ascontiguousarray(experts[name + "_q"])).to(device)
             s = torch.from_numpy(np.ascontiguousarray(experts[name + "_s"])).to(device)
-            self.t[name] = pack_mxfp4(q[:E], s[:E], rows, K, out=(view(name, "q"), view(name, "s")))
+            self.t[name] = pack_mxfp4(q[:E], s[:E], rows, K, out=self.t[name])
             if has_shared:
-                self.t["sh_" + name] = pack_mxfp4(q[E:E + 1], s[E:E + 1], rows, K,
-                                                  out=(view("sh_" + name, "q"), view("sh_" + name, "s")))
+                self.t["sh_" + name] = pack_mxfp4(q[E:E + 1], s[E:E + 1], rows, K, out=self.t["sh_" + name])
             del q, s
         torch.cuda.synchronize(device)
         self.has_shared = has_shared
+
+    def _alloc(self, device):
+        """One allocation with every region on a 2 MiB boundary; self.t = (q, s) views per matrix set."""
+        self.buffer = torch.empty(self._total + _ALIGN, dtype=torch.uint8, device=device)
+        self._base = (-self.buffer.data_ptr()) % _ALIGN
+        view = lambda key, part: self.buffer[self._base + self._regions[(key, part)][0]:][:self._regions[(key, part)][1]]
+        self.t = {key: (view(key, "q"), view(key, "s")) for key, part in self._regions if part == "q"}
+
+    def copy(self) -> "PackedExperts":
+        """A second device copy of the same packed weights (its own allocation, same 2 MiB placement)."""
+        c = object.__new__(PackedExperts)
+        c._regions, c._total, c.has_shared = self._regions, self._total, self.has_shared
+        c._alloc(self.buffer.device)
+        c.buffer[c._base:c._base + self._total].copy_(self.buffer[self._base:self._base + self._total])
+        return c
 
     def weights(self, with_shared: bool = True, shared_bf16=None) -> capi.MoeWeights:
         """shared_bf16: optional dict of bf16 device tensors gate/up [I][d], down [d][I] (the shared expert

@@ -75,9 +75,18 @@ def _p(a):
 
 
 def _threads(n):
+    """n, or the CPUs this process may use: its affinity mask capped by a cgroup v2 CPU quota."""
     if n:
         return int(n)
-    return len(os.sched_getaffinity(0))
+    cpus = len(os.sched_getaffinity(0))
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            cpus = min(cpus, int(quota) // int(period))
+    except (OSError, ValueError):
+        pass
+    return max(1, cpus)
 
 
 def e2m1(code: int) -> float:

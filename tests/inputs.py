@@ -5,8 +5,10 @@ making the routing decisions:
 - rows whose top-k score margin (k-th minus (k+1)-th largest sqrt-softplus
   score, fp64, after any bias) is below 1e-3 are redrawn, so that the choice of
   experts cannot depend on rounding (all top-k workloads);
-- the Zipf workload's logit bias is calibrated by 30 fixed-point steps
-  b_e += ln q_e - ln max(q_hat_e, 1/(2N)) on the workload's x, then frozen.
+- the Zipf workload's logit bias is calibrated by 120 damped fixed-point steps
+  b_e += 0.25 * (ln q_e - ln max(q_hat_e, 1/(2N))) on the workload's x, then
+  frozen (undamped steps oscillate: the square root of the softplus compresses
+  the score gaps of strongly biased experts).
 """
 import functools
 import time
@@ -20,7 +22,10 @@ from mxfp4_routed_expert_sqrt_amd.configs import SHAPES
 MIN_MARGIN = 1e-3
 
 
-def calibrate_zipf_bias(shape, x, w, steps=30, seed=0):
+ZIPF_STEPS, ZIPF_DAMPING = 120, 0.25
+
+
+def calibrate_zipf_bias(shape, x, w, steps=ZIPF_STEPS, seed=0):
     q = synth.zipf_targets(shape, seed=seed)
     z0 = oracle.router_logits(x, w)
     b = np.zeros(shape.n_experts, dtype=np.float32)
@@ -28,7 +33,7 @@ def calibrate_zipf_bias(shape, x, w, steps=30, seed=0):
     for _ in range(steps):
         idx, _, _ = oracle.route(z0 + b.astype(np.float64)[None, :], shape.top_k)
         q_hat = np.bincount(idx.ravel(), minlength=shape.n_experts) / shape.n_rows
-        b = (b.astype(np.float64) + np.log(q) - np.log(np.maximum(q_hat, floor))).astype(np.float32)
+        b = (b.astype(np.float64) + ZIPF_DAMPING * (np.log(q) - np.log(np.maximum(q_hat, floor)))).astype(np.float32)
     return b, q
 
 

@@ -9,7 +9,7 @@ import re
 import pytest
 
 from mxfp4_routed_expert_sqrt_amd import capi
-from mxfp4_routed_expert_sqrt_amd.configs import SHAPES
+from mxfp4_routed_expert_sqrt_amd.configs import SHAPES, MoEShape
 from mxfp4_routed_expert_sqrt_amd.layer import make_config
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -137,6 +137,40 @@ def test_invalid_arguments_return_before_any_hip_call():
     a = _valid_args(nosh, N); a.w.sh_gate_q = None
     a.workspace_bytes = 0
     assert capi.moe_layer_forward(nosh, a, None) == capi.MOE_ERR_WORKSPACE  # shared pointers not needed
+
+
+def test_every_written_buffer_is_disjoint_from_the_others():
+    # out, the workspace and the optional routing outputs are written; none may overlap any buffer of
+    # the call (weights, hash tables, routing outputs included), or the call is rejected before any
+    # HIP call.  Reads may overlap each other.
+    cfg = make_config(SHAPES["tiny"])
+    N, E, k = 32, 16, 2
+    cases = []
+    a = _valid_args(cfg, N); a.w.gate_q = a.workspace + 256; cases.append(("weights in workspace", a))
+    a = _valid_args(cfg, N); a.w.down_s = a.out + 64; cases.append(("scales under out", a))
+    a = _valid_args(cfg, N); a.w.sh_up_q = a.workspace + 4096; cases.append(("shared weights in workspace", a))
+    a = _valid_args(cfg, N); a.topk_idx = a.out; cases.append(("topk_idx on out", a))
+    a = _valid_args(cfg, N); a.perm = a.x + 16; cases.append(("perm on x", a))
+    a = _valid_args(cfg, N); a.counts = 0x90000000; a.offsets = 0x90000000 + 4 * (E - 1)
+    cases.append(("counts and offsets overlap", a))
+    a = _valid_args(cfg, N); a.inv = a.workspace + 1024; cases.append(("inv in workspace", a))
+    a = _valid_args(cfg, N); a.topk_w = a.w.up_s; cases.append(("gates on weight scales", a))
+    for label, a in cases:
+        assert capi.moe_layer_forward(cfg, a, None) == capi.MOE_ERR_INVALID, label
+    # hash mode: the token ids and the whole table are read
+    hsh = MoEShape("edge_hash", 50, 256, 16, 2, 128, "hash", "tiny", vocab=97)
+    hcfg = make_config(hsh)
+    a = _valid_args(hcfg, 50); a.token_ids, a.tid2eid, a.vocab = 0xC0000000, 0xD0000000, 97
+    a.workspace_bytes -= 1
+    assert capi.moe_layer_forward(hcfg, a, None) == capi.MOE_ERR_WORKSPACE  # valid up to the workspace size
+    a.workspace_bytes += 1
+    a.tid2eid = a.workspace + a.workspace_bytes - 8  # the table's first row is inside, the rest beyond
+    assert capi.moe_layer_forward(hcfg, a, None) == capi.MOE_ERR_INVALID
+    a.tid2eid, a.token_ids = 0xD0000000, a.out + 50 * 256 * 2 - 4  # the ids' first entry is out's last 4 bytes
+    assert capi.moe_layer_forward(hcfg, a, None) == capi.MOE_ERR_INVALID
+    # reads overlapping each other are allowed: residual == x, gate and up scales shared
+    a = _valid_args(cfg, N); a.residual = a.x; a.w.up_s = a.w.gate_s; a.workspace_bytes -= 1
+    assert capi.moe_layer_forward(cfg, a, None) == capi.MOE_ERR_WORKSPACE
 
 
 def test_zero_rows_is_a_no_op():

@@ -22,6 +22,8 @@ pytestmark = pytest.mark.gpu
 
 TALL = MoEShape("edge_tall", 611, 512, 8, 4, 256, "topk", "edge_tall")
 MEDIUM = MoEShape("edge_medium", 300, 512, 64, 4, 256, "topk", "edge_medium", bias="zipf")
+# 1200 routed pairs at widths the wider units do not divide: the 16-row units of larger batches
+WIDE16 = MoEShape("edge_w16_d768_i512", 300, 768, 64, 4, 512, "topk", "edge_w16b")
 
 
 def _layer(wl):
@@ -56,9 +58,11 @@ def _same(a, b, label):
         assert np.array_equal(a[key], b[key]), f"{label}: {key} differs"
 
 
-@pytest.mark.parametrize("shape", [TALL, MEDIUM, SHAPES["hash2048"]], ids=["tall", "medium", "hash2048-scatter"])
+@pytest.mark.parametrize("shape", [TALL, MEDIUM, WIDE16, SHAPES["hash2048"]],
+                         ids=["tall", "medium", "wide16", "hash2048-scatter"])
 def test_poisoned_workspace_repeatable(shape):
-    # tall, medium: the 64- and 32-row work units; hash2048: 12288 pairs, so the separate scatter launch
+    # tall, medium: the 64- and 32-row work units; wide16: 16-row units of a batch of >= 1024 pairs;
+    # hash2048: 12288 pairs, so the separate scatter launch
     wl = workload(shape)
     layer = _layer(wl)
     x, tok, tab = _inputs(wl)

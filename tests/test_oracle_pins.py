@@ -239,6 +239,62 @@ def test_layer_matches_dense_numpy_with_bias_and_scale():
     assert np.allclose(r["out"], ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
 
 
+def _numpy_byte_table():
+    """Both E2M1 values of every byte (low nibble first), from the closed form in _numpy_decode."""
+    b = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 16, axis=1)  # one 32-value block per byte
+    return _numpy_decode(b, np.full((256, 1), 127, dtype=np.uint8))[:, :2]
+
+
+def _numpy_decode_fast(q, s, table):
+    """_numpy_decode through a 256-entry byte table (the same closed form, fast enough for V4 matrices)."""
+    R = q.shape[0]
+    return table[q].reshape(R, -1) * np.repeat(np.ldexp(1.0, s.astype(np.int64) - 127), 32, axis=-1)
+
+
+@pytest.mark.slow
+def test_layer_matches_dense_numpy_at_v4_scale():
+    # The oracle at the V4 layer's own sizes (d 4096, 256 experts top-6 + shared, I 2048; 512-row
+    # verify batch): 16 rows spread over the batch, first and last included, against the dense numpy
+    # fp64 formulation restricted to those rows (every expert they touch, masked by the routing),
+    # and the whole batch's bookkeeping against numpy's stable argsort.  Sizes where index arithmetic
+    # could overflow or an (expert, feature) work split could go wrong only show up here.
+    wl = workload("verify512")
+    sh, ex = wl["shape"], wl["experts"]
+    E, k, d = sh.n_experts, sh.top_k, sh.d_model
+    rows = np.unique(np.linspace(0, sh.n_rows - 1, 16).astype(np.int32))
+    r = oracle.forward(sh, wl["x"], wl["router_w"], ex, rows=rows)
+
+    x = (wl["x"][rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    s = np.sqrt(np.logaddexp(0.0, x @ wl["router_w"].astype(np.float64).T))
+    top = np.sort(np.argsort(-s, axis=1, kind="stable")[:, :k], axis=1)
+    sel = np.take_along_axis(s, top, 1)
+    g = sel / sel.sum(1, keepdims=True)
+    assert np.array_equal(r["idx"][rows], top)
+    assert np.allclose(r["gates"][rows], g, rtol=1e-13)
+
+    mask = np.zeros((len(rows), E))
+    np.put_along_axis(mask, top, g, 1)
+    table = _numpy_byte_table()
+    out = np.zeros((len(rows), d))
+    for e in sorted(set(top.ravel().tolist())) + [E]:
+        Wg = _numpy_decode_fast(ex["gate_q"][e], ex["gate_s"][e], table)
+        Wu = _numpy_decode_fast(ex["up_q"][e], ex["up_s"][e], table)
+        Wd = _numpy_decode_fast(ex["down_q"][e], ex["down_s"][e], table)
+        a = np.minimum(x @ Wg.T, sh.swiglu_limit)
+        b = np.clip(x @ Wu.T, -sh.swiglu_limit, sh.swiglu_limit)
+        y = (a / (1 + np.exp(-a)) * b) @ Wd.T
+        out += y if e == E else mask[:, e:e + 1] * y
+    assert np.allclose(r["out"], out, rtol=1e-11, atol=1e-12 * np.abs(out).max())
+
+    idx = r["idx"].ravel()
+    perm = np.argsort(idx, kind="stable")  # expert-major; pairs r*k+j ascending inside an expert
+    counts = np.bincount(idx, minlength=E)
+    _, off, p, inv = oracle.bookkeeping(r["idx"], E)
+    assert np.array_equal(p, perm) and np.array_equal(off, np.concatenate([[0], np.cumsum(counts)]))
+    assert np.array_equal(inv[perm], np.arange(sh.n_rows * k))
+    assert np.array_equal(r["perm"], perm) and np.array_equal(r["counts"], counts)
+
+
 def _single_entry_experts(sh, entries):
     """Weights that are zero except listed (matrix, expert, row, col) = 1.0 entries."""
     E, d, I = sh.n_experts, sh.d_model, sh.d_ff
@@ -341,6 +397,23 @@ def test_constant_hash_table_routes_every_row_alike():
     r = oracle.forward(sh, wl["x"], wl["router_w"], wl["experts"], token_ids=tok, tid2eid=table)
     assert np.all(r["idx"] == [3, 9])
     assert r["counts"][3] == 32 and r["counts"][9] == 32 and r["counts"].sum() == 64
+
+
+def test_zipf_calibration_reaches_the_skew_targets():
+    # the calibrated bias steers the per-row selection probability towards q_e = min(1, c * rank^-1.2),
+    # sum q = 6: the hottest expert on (nearly) every row, i.e. (nearly) 1/6 of all assignments, the cap
+    # that 6 distinct experts per row allow
+    from tests.inputs import calibrate_zipf_bias
+    sh = SHAPES["zipf2048"]
+    x, w = synth.gen_x(sh), synth.gen_router(sh)
+    b, q = calibrate_zipf_bias(sh, x, w)
+    assert np.isclose(q.sum(), sh.top_k) and q.max() == 1.0
+    idx, _, _ = oracle.route(oracle.router_logits(x, w, b), sh.top_k)
+    q_hat = np.bincount(idx.ravel(), minlength=sh.n_experts) / sh.n_rows
+    assert q_hat[np.argmax(q)] >= 0.95
+    assert np.abs(q_hat - q).sum() < 0.2
+    order = np.argsort(-q)  # the load falls with the target rank
+    assert np.all(np.diff(q_hat[order[:8]]) <= 0.02)
 
 
 def test_tiny_workload_margins():
