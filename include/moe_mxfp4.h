@@ -64,7 +64,8 @@ enum {
   MOE_ERR_INVALID = -1,     /* null/misaligned pointer, bad enum, aliasing output */
   MOE_ERR_UNSUPPORTED = -2, /* shape outside the supported range */
   MOE_ERR_WORKSPACE = -3,   /* workspace missing or too small */
-  MOE_ERR_HIP = -4          /* a HIP launch failed */
+  MOE_ERR_HIP = -4,         /* a HIP launch failed */
+  MOE_ERR_SCRATCH = -5      /* moe_layer_forward_noalloc: the call needs more scratch than the library holds */
 };
 
 enum { MOE_ROUTING_TOPK = 0, MOE_ROUTING_HASH = 1 };
@@ -206,6 +207,29 @@ int moe_workspace_size(const moe_config_t* cfg, int32_t n_rows, size_t* bytes);
 
 /* The whole layer (router, routing bookkeeping, expert FFNs, combine) on `stream`. */
 int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* stream);
+
+/*
+ * moe_layer_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The layer runs on a static device array
+ * of the library, MOE_NOALLOC_SCRATCH_BYTES per GPU, held from the library's
+ * load until the process ends; this call allocates nothing and frees nothing.
+ *   - args->workspace must be NULL and args->workspace_bytes 0 (else
+ *     MOE_ERR_INVALID); every other argument as for moe_layer_forward.
+ *   - A call is accepted when moe_workspace_size(cfg, n_rows) <=
+ *     MOE_NOALLOC_SCRATCH_BYTES (at d 4096, I 2048, 256 experts top-6 + 1
+ *     MXFP4 shared expert: up to 598 rows); a larger one returns
+ *     MOE_ERR_SCRATCH and enqueues nothing.
+ *   - Every call on one GPU uses that GPU's one scratch array: calls that can
+ *     overlap in time on one GPU (different streams without ordering, or
+ *     several host threads) race and give undefined results.  Order them on
+ *     one stream or with events.  The array keeps the last call's contents;
+ *     each call re-initialises what it reads.
+ *   - The first call on each device looks up that device's copy of the array
+ *     (hipGetSymbolAddress, no allocation); a failure returns MOE_ERR_HIP.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (96u << 20)
+int moe_layer_forward_noalloc(const moe_config_t* cfg, const moe_args_t* args, void* stream);
 
 #ifdef __cplusplus
 }

@@ -12,6 +12,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mxfp4.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_SCRATCH = -5
+MOE_NOALLOC_SCRATCH_BYTES = 96 << 20
 MOE_ROUTING_TOPK, MOE_ROUTING_HASH = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_SHARED_MXFP4, MOE_SHARED_BF16 = 0, 1
@@ -65,12 +67,14 @@ def lib():
         L.moe_workspace_size.restype = ctypes.c_int
         L.moe_layer_forward.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeArgs), c_vp]
         L.moe_layer_forward.restype = ctypes.c_int
+        L.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeArgs), c_vp]
+        L.moe_layer_forward_noalloc.restype = ctypes.c_int
         _lib = L
     return _lib
 
 
 EXPORTED = ("moe_version", "moe_status_string", "moe_packed_mxfp4_bytes", "moe_pack_mxfp4", "moe_workspace_size",
-            "moe_layer_forward")
+            "moe_layer_forward", "moe_layer_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -111,3 +115,7 @@ def moe_workspace_size(cfg: MoeConfig, n_rows: int) -> int:
 
 def moe_layer_forward(cfg: MoeConfig, args: MoeArgs, stream) -> int:
     return lib().moe_layer_forward(ctypes.byref(cfg), ctypes.byref(args), stream)
+
+
+def moe_layer_forward_noalloc(cfg: MoeConfig, args: MoeArgs, stream) -> int:
+    return lib().moe_layer_forward_noalloc(ctypes.byref(cfg), ctypes.byref(args), stream)

@@ -2,12 +2,39 @@
 // the launch sequence on the caller's stream.
 #include <string.h>
 
+#include <atomic>
+
 #include "kernels.h"
 #include "moe_mxfp4.h"
 
 using namespace moe;
 
+// Device scratch of moe_layer_forward_noalloc: one copy per GPU, held from the
+// library's load until the process ends.  In host code `scratch` names a
+// host-side stand-in, never a device address: host code uses only the
+// per-device pointer that hipGetSymbolAddress returns (scratch_on_device).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+// The current device's copy of `scratch`, looked up once per device (with
+// that device current) and kept.  Returns a MOE_* status.
+int scratch_on_device(uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // concurrent first calls on one device look the address up twice and store the same value
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = (uint8_t*)p;
+  return MOE_OK;
+}
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -294,6 +321,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH: return "call needs more than the library's static scratch (MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -347,6 +375,26 @@ int moe_layer_forward(const moe_config_t* cfg, const moe_args_t* args, void* str
   if (!aligned(a.workspace, 256)) return MOE_ERR_INVALID;
   if (!buffers_disjoint(c, a, a.workspace, L.total)) return MOE_ERR_INVALID;
   return run_layer(c, a, (uint8_t*)a.workspace, L, (hipStream_t)stream);
+}
+
+int moe_layer_forward_noalloc(const moe_config_t* cfg, const moe_args_t* args, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!args) return MOE_ERR_INVALID;
+  const moe_config_t& c = *cfg;
+  const moe_args_t& a = *args;
+  if (a.n_rows < 0) return MOE_ERR_INVALID;
+  if (a.n_rows > MOE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
+  if (a.workspace || a.workspace_bytes) return MOE_ERR_INVALID;  // the library's scratch replaces it
+  if (a.n_rows == 0) return MOE_OK;
+  if ((rc = check_args(c, a))) return rc;
+  const Layout L = make_layout(c, a.n_rows);
+  if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  // the scratch is a separate allocation of the library, so only the caller's buffers can overlap
+  if (!buffers_disjoint(c, a, nullptr, 0)) return MOE_ERR_INVALID;
+  uint8_t* ws = nullptr;
+  if ((rc = scratch_on_device(&ws))) return rc;
+  return run_layer(c, a, ws, L, (hipStream_t)stream);
 }
 
 }  // extern "C"

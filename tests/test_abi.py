@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     assert capi.moe_version() == 3
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert capi.moe_status_string(st) != "unknown status"
     assert capi.moe_status_string(7) == "unknown status"
 
@@ -205,7 +205,7 @@ def test_binding_structs_match_the_c_header(tmp_path):
             lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
     consts = ["MOE_OK", "MOE_ERR_INVALID", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
               "MOE_ROUTING_TOPK", "MOE_ROUTING_HASH", "MOE_BIAS_LOGIT", "MOE_BIAS_SELECT", "MOE_SHARED_MXFP4",
-              "MOE_SHARED_BF16", "MOE_MAX_ROWS",
+              "MOE_SHARED_BF16", "MOE_MAX_ROWS", "MOE_ERR_SCRATCH", "MOE_NOALLOC_SCRATCH_BYTES",
               "MOE_N_STAGES", "MOE_N_STAGE_EVENTS", "MOE_MXFP4_VERSION"]
     for c in consts:
         lines.append(f'  printf("const {c} %ld\\n", (long)({c}));')
