@@ -15,9 +15,10 @@ constexpr int kMediumGroupRows = 32;  // token rows of a medium work unit (2 col
 constexpr int kTallGroupRows = 64;    // token rows of a tall work unit (4 column tiles)
 constexpr int kXcds = 8;         // gfx950: workgroups are dealt round-robin to 8 XCDs
 
-// One work unit of the grouped GEMMs: rows [p0, p0 + cnt) of expert e.
+// One work group of the grouped GEMMs: rows [p0, p0 + cnt) of expert e; the
+// expert's groups are entries [first, first + ng) of the work list.
 struct Group {
-  int32_t e, p0, cnt, pad;
+  int32_t e, p0, cnt, first, ng, pad0, pad1, pad2;
 };
 
 // Maps this workgroup to a work unit so that each XCD receives a contiguous

@@ -489,6 +489,27 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
   }
 }
 
+// Work group and feature block of unit `unit`.  Units run through the work
+// list expert by expert.  Group-major (FBMAJOR false): the n_fb feature blocks
+// of one group are consecutive, so they share that group's activations in L2.
+// Feature-block-major (the tall units): within an expert, the expert's ng
+// groups of one feature block are consecutive, so they share that block's
+// weights in L2 while they run side by side on one XCD (at 8192 rows this
+// took the gate/up weight fetch from 6.31 to 3.68 GB per launch and down from
+// 2.41 to 1.69 GB).
+template <bool FBMAJOR>
+__device__ __forceinline__ Group unit_group(const Group* groups, int unit, int n_fb, int* fb) {
+  const Group g = groups[unit / n_fb];
+  if constexpr (!FBMAJOR) {
+    *fb = unit % n_fb;
+    return g;
+  } else {
+    const int l = unit - g.first * n_fb;
+    *fb = l / g.ng;
+    return groups[g.first + l % g.ng];
+  }
+}
+
 // POOL: units dealt by xcd_unit_claim (static ranges with a shared tail),
 // else by xcd_unit_split (static ranges, optional tail halves).
 template <int TPM, int WAVES, int NB, int RING, bool NT, bool FP6, bool POOL>
@@ -505,9 +526,9 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
   } else if (!xcd_unit_split(*a.n_groups * n_fb, TPM >= 4 ? a.tail_units : 0, &half_idx, &is_half)) {
     return;
   }
-  const int unit = half_idx >> 1;
-  const Group g = a.groups[unit / n_fb];
-  const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
+  int fb;
+  const Group g = unit_group<FP6>(a.groups, half_idx >> 1, n_fb, &fb);
+  const int fu0 = fb * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
   if constexpr (TPM >= 4) {
     if (is_half) {
       gateup_unit<TPM / 2, WAVES, NB, RING, NT, FP6>(a, g, fu0, lds);
@@ -577,9 +598,9 @@ __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   } else if (!xcd_unit_split(*a.n_groups * n_fb, NA >= 2 ? a.tail_units : 0, &half_idx, &is_half)) {
     return;
   }
-  const int unit = half_idx >> 1;
-  const Group g = a.groups[unit / n_fb];
-  const int fu0 = (unit % n_fb) * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
+  int fb;
+  const Group g = unit_group<FP6>(a.groups, half_idx >> 1, n_fb, &fb);
+  const int fu0 = fb * kFeatUnit + (half_idx & 1) * (kFeatUnit / 2);
   if constexpr (NA >= 2) {
     if (is_half) {
       down_unit<NA / 2, WAVES, NB, RING, NT, FP6>(a, g, fu0, lds);

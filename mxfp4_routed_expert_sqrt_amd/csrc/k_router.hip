@@ -426,7 +426,9 @@ __device__ __forceinline__ void write_groups(int rows, const int32_t* s_cnt, con
       gr.e = tid;
       gr.p0 = p0 + g * rows;
       gr.cnt = min(rows, c - g * rows);
-      gr.pad = 0;
+      gr.first = g0;
+      gr.ng = ng;
+      gr.pad0 = gr.pad1 = gr.pad2 = 0;
       groups[g0 + g] = gr;
     }
   }
@@ -435,7 +437,9 @@ __device__ __forceinline__ void write_groups(int rows, const int32_t* s_cnt, con
     gr.e = E;
     gr.p0 = P + g * rows;
     gr.cnt = min(rows, n_rows - g * rows);
-    gr.pad = 0;
+    gr.first = shared0;
+    gr.ng = nsh;
+    gr.pad0 = gr.pad1 = gr.pad2 = 0;
     groups[shared0 + g] = gr;
   }
   if (tid == 0) *n_groups = total + nsh;
