@@ -14,6 +14,8 @@
  * the bytes do not depend on the thread count.  Normals come from the
  * Marsaglia-Bray polar method (1964) on consecutive uniform pairs.
  *
+ * Q2_K encoding: the GGUF Q2_K super-block layout (see encode_q2k_block).
+ *
  * MXFP4 encoding (OCP Microscaling Formats v1.0, section 6.3 conversion):
  * per 32-element block the shared exponent is floor(log2(amax)) - 2 (2 is the
  * largest E2M1 exponent), stored as E8M0 = exponent + 127; every element is
@@ -237,6 +239,124 @@ void synth_encode_mxfp4(const float* v, long rows, long K, uint8_t* q, uint8_t* 
   for (long r = 0; r < rows; ++r)
     for (long b = 0; b < K / 32; ++b)
       encode_block32(v + r * K + 32 * b, q + r * (K / 2) + 16 * b, s + r * (K / 32) + b);
+}
+
+/* ---- Q2_K encoding -------------------------------------------------------------------- */
+
+/* fp32 -> IEEE half bits, round to nearest even (overflow to infinity,
+ * gradual underflow to subnormals). */
+static uint16_t f32_to_f16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const int32_t ex = (int32_t)((u >> 23) & 0xFF) - 127;
+  uint32_t man = u & 0x7FFFFFu;
+  if (ex == 128) return (uint16_t)(sign | 0x7C00u | (man ? 0x200u : 0u));
+  if (ex > 15) return (uint16_t)(sign | 0x7C00u);
+  if (ex >= -14) { /* normal half: 10 mantissa bits kept of 23 */
+    uint32_t h = ((uint32_t)(ex + 15) << 10) | (man >> 13);
+    const uint32_t rest = man & 0x1FFFu;
+    if (rest > 0x1000u || (rest == 0x1000u && (h & 1u))) ++h; /* may carry into the exponent: still exact RNE */
+    return (uint16_t)(sign | h);
+  }
+  if (ex < -25) return (uint16_t)sign;
+  /* subnormal half: value = m * 2^-24 with m = (1.man) * 2^(ex + 24) */
+  man |= 0x800000u;
+  const int shift = -ex - 1; /* 14 .. 24: bits dropped from the 24-bit significand to units of 2^-24 */
+  uint32_t h = man >> shift;
+  const uint32_t rest = man & ((1u << shift) - 1u), half = 1u << (shift - 1);
+  if (rest > half || (rest == half && (h & 1u))) ++h;
+  return (uint16_t)(sign | h);
+}
+
+static double f16_bits_to_double(uint16_t h) {
+  const int ex = (h >> 10) & 0x1F, man = h & 0x3FF;
+  double v = ex == 0 ? ldexp((double)man, -24) : ldexp((double)(man | 0x400), ex - 25);
+  return (h & 0x8000) ? -v : v;
+}
+
+/* One Q2_K super-block: 256 values into 84 bytes, the GGUF Q2_K block layout:
+ * bytes 0-15 one byte per 16-value sub-block (low nibble its scale, high
+ * nibble its min), bytes 16-79 the 2-bit quants (value t of the block in
+ * byte 16 + 32*(t/128) + (t%32), bits 2*((t%128)/32)), then d and dmin as
+ * half floats.  Value t decodes to d*scale*q - dmin*min of its sub-block t/16.
+ * Quantiser (for synthetic inputs only): per sub-block the range [lo, hi]
+ * with lo = min(0, smallest value) is cut in 3 steps, s = (hi - lo)/3 and
+ * m = -lo; d = max s / 15 and dmin = max m / 15 (rounded to half), the 4-bit
+ * scale and min round s/d and m/dmin, and each q rounds (v + dmin*min) /
+ * (d*scale) into 0..3. */
+static void encode_q2k_block(const float* v, uint8_t* blk) {
+  double s[16], m[16], smax = 0.0, mmax = 0.0;
+  for (int sb = 0; sb < 16; ++sb) {
+    double lo = 0.0, hi = -INFINITY;
+    for (int i = 0; i < 16; ++i) {
+      const double x = v[16 * sb + i];
+      if (x < lo) lo = x;
+      if (x > hi) hi = x;
+    }
+    if (hi < lo) hi = lo;
+    s[sb] = (hi - lo) / 3.0;
+    m[sb] = -lo;
+    if (s[sb] > smax) smax = s[sb];
+    if (m[sb] > mmax) mmax = m[sb];
+  }
+  const uint16_t dh = f32_to_f16_rne((float)(smax / 15.0)), mh = f32_to_f16_rne((float)(mmax / 15.0));
+  const double d = f16_bits_to_double(dh), dmin = f16_bits_to_double(mh);
+  memset(blk, 0, 84);
+  for (int sb = 0; sb < 16; ++sb) {
+    int sc = d > 0.0 ? (int)lrint(s[sb] / d) : 0, mn = dmin > 0.0 ? (int)lrint(m[sb] / dmin) : 0;
+    sc = sc < 0 ? 0 : (sc > 15 ? 15 : sc);
+    mn = mn < 0 ? 0 : (mn > 15 ? 15 : mn);
+    blk[sb] = (uint8_t)(sc | (mn << 4));
+    const double step = d * sc, off = dmin * mn;
+    for (int i = 0; i < 16; ++i) {
+      const int t = 16 * sb + i;
+      int q = step > 0.0 ? (int)lrint(((double)v[t] + off) / step) : 0;
+      q = q < 0 ? 0 : (q > 3 ? 3 : q);
+      blk[16 + 32 * (t / 128) + (t % 32)] |= (uint8_t)(q << (2 * ((t % 128) / 32)));
+    }
+  }
+  blk[80] = (uint8_t)(dh & 0xFF);
+  blk[81] = (uint8_t)(dh >> 8);
+  blk[82] = (uint8_t)(mh & 0xFF);
+  blk[83] = (uint8_t)(mh >> 8);
+}
+
+typedef struct {
+  uint64_t seed, set_tag, mat_tag;
+  long first_mat, rows, K;
+  double std;
+  uint8_t* out;
+} q2k_ctx;
+
+static void q2k_row(void* p, long flat) {
+  q2k_ctx* c = (q2k_ctx*)p;
+  long m = flat / c->rows, n = flat % c->rows;
+  uint64_t key = stream_key(c->seed, c->set_tag, c->mat_tag, (uint64_t)(c->first_mat + m), (uint64_t)n);
+  double* buf = (double*)malloc(sizeof(double) * (size_t)(c->K + 1));
+  float* f = (float*)malloc(sizeof(float) * (size_t)c->K);
+  fill_normal(key, c->std, c->K, buf);
+  for (long i = 0; i < c->K; ++i) f[i] = (float)buf[i];
+  uint8_t* row = c->out + (size_t)flat * (size_t)(c->K / 256) * 84;
+  for (long b = 0; b < c->K / 256; ++b) encode_q2k_block(f + 256 * b, row + 84 * b);
+  free(f);
+  free(buf);
+}
+
+/* n_mat matrices [rows][K] with entries ~N(0, std), encoded to Q2_K blocks:
+ * out [n_mat][rows][K/256][84].  K must be a multiple of 256. */
+int synth_q2k(uint64_t seed, uint64_t set_tag, uint64_t mat_tag, long first_mat, long n_mat, long rows, long K,
+              double std, uint8_t* out, int nthreads) {
+  if (K % 256 != 0 || rows <= 0 || n_mat < 0) return -1;
+  q2k_ctx c = {seed, set_tag, mat_tag, first_mat, rows, K, std, out};
+  parallel_rows(q2k_row, &c, n_mat * rows, nthreads);
+  return 0;
+}
+
+/* Encode caller-given fp32 rows [rows][K] to Q2_K blocks (hand-built test weights). */
+void synth_encode_q2k(const float* v, long rows, long K, uint8_t* out) {
+  for (long r = 0; r < rows; ++r)
+    for (long b = 0; b < K / 256; ++b) encode_q2k_block(v + r * K + 256 * b, out + (r * (K / 256) + b) * 84);
 }
 
 /* ---- hash routing tables ------------------------------------------------------------ */

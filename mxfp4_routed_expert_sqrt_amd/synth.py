@@ -66,6 +66,9 @@ def _load():
         lib.synth_router_f32.argtypes = [u64, u64, i64, i64, dbl, vp, i32]
         lib.synth_mxfp4.argtypes = [u64, u64, u64, i64, i64, i64, i64, dbl, vp, vp, i32]
         lib.synth_mxfp4.restype = i32
+        lib.synth_q2k.argtypes = [u64, u64, u64, i64, i64, i64, i64, dbl, vp, i32]
+        lib.synth_q2k.restype = i32
+        lib.synth_encode_q2k.argtypes = [vp, i64, i64, vp]
         lib.synth_encode_mxfp4.argtypes = [vp, i64, i64, vp, vp]
         lib.synth_tid2eid.argtypes = [u64, u64, i64, i32, i32, vp, i32]
         lib.synth_tid2eid.restype = i32
@@ -130,6 +133,47 @@ def gen_experts(shape: MoEShape, seed: int = 0, threads=None) -> dict:
     w["down_q"], w["down_s"] = gen_mxfp4(st, MAT_DOWN, 0, E + 1, d, I, expert_std(I), seed, threads)
     _EXPERT_CACHE[key] = w
     return w
+
+
+Q2K_BLOCK_BYTES = 84  # bytes per 256-value Q2_K super-block
+MAT_Q2K = 16            # stream families of Q2_K matrices: MAT_Q2K + MAT_GATE/UP/DOWN
+
+
+def gen_q2k(set_tag: int, mat_tag: int, first: int, count: int, rows: int, K: int, std: float, seed: int = 0,
+            threads=None) -> np.ndarray:
+    out = np.empty((count, rows, K // 256 * Q2K_BLOCK_BYTES), dtype=np.uint8)
+    rc = _load().synth_q2k(seed, set_tag, mat_tag, first, count, rows, K, std, _ptr(out), threads or usable_cpus())
+    if rc != 0:
+        raise ValueError("synth_q2k: bad shape")
+    return out
+
+
+_Q2K_CACHE = {}
+
+
+def gen_experts_q2k(shape: MoEShape, seed: int = 0, threads=None) -> dict:
+    """Routed experts 0..E-1 as Q2_K super-blocks: gate/up [E][I][d/256*84], down [E][d][I/256*84] (uint8);
+    entries ~N(0, 1/sqrt(fan_in)) before quantisation, like the MXFP4 experts.  Cached per process."""
+    key = (shape.weight_set, shape.n_experts, shape.d_model, shape.d_ff, seed)
+    if key in _Q2K_CACHE:
+        return _Q2K_CACHE[key]
+    st = _set_tag(shape)
+    E, d, I = shape.n_experts, shape.d_model, shape.d_ff
+    w = {"gate": gen_q2k(st, MAT_Q2K + MAT_GATE, 0, E, I, d, expert_std(d), seed, threads),
+         "up": gen_q2k(st, MAT_Q2K + MAT_UP, 0, E, I, d, expert_std(d), seed, threads),
+         "down": gen_q2k(st, MAT_Q2K + MAT_DOWN, 0, E, d, I, expert_std(I), seed, threads)}
+    _Q2K_CACHE[key] = w
+    return w
+
+
+def encode_q2k(v: np.ndarray) -> np.ndarray:
+    """Encode fp32 rows [R][K] (K % 256 == 0) to Q2_K super-blocks [R][K/256*84]."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    R, K = v.shape
+    assert K % 256 == 0
+    out = np.empty((R, K // 256 * Q2K_BLOCK_BYTES), dtype=np.uint8)
+    _load().synth_encode_q2k(_ptr(v), R, K, _ptr(out))
+    return out
 
 
 def encode_mxfp4(v: np.ndarray):

@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg use it to check and time the HIP implementation; the product
 path never imports it.  It shares no code with the HIP implementation: inputs
 arrive as plain arrays (bf16 bit patterns, fp32, MXFP4 bytes in the natural
-[rows][K/2] + [rows][K/32] layout) and results come back in fp64.
+[rows][K/2] + [rows][K/32] layout, or Q2_K super-blocks [rows][K/256*84])
+and results come back in fp64.
 """
 import ctypes
 import os
@@ -28,7 +29,8 @@ def build() -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int), ("d", ctypes.c_int), ("E", ctypes.c_int), ("k", ctypes.c_int),
                 ("I", ctypes.c_int), ("routing", ctypes.c_int), ("route_scale", ctypes.c_double),
-                ("swiglu_limit", ctypes.c_double), ("norm_eps", ctypes.c_float), ("bias_mode", ctypes.c_int)]
+                ("swiglu_limit", ctypes.c_double), ("norm_eps", ctypes.c_float), ("bias_mode", ctypes.c_int),
+                ("expert_format", ctypes.c_int)]
 
 
 class _Inputs(ctypes.Structure):
@@ -53,6 +55,8 @@ def _load():
         lib.orc_f32_to_bf16.argtypes, lib.orc_f32_to_bf16.restype = [ctypes.c_float], ctypes.c_uint16
         lib.orc_rmsnorm_bf16.argtypes = [vp, i32, i32, vp, ctypes.c_float, vp]
         lib.orc_decode_mxfp4_row.argtypes = [vp, vp, i32, vp]
+        lib.orc_decode_q2k_row.argtypes = [vp, i32, vp]
+        lib.orc_half.argtypes, lib.orc_half.restype = [ctypes.c_uint16], dbl
         lib.orc_router_logits.argtypes = [vp, i32, i32, vp, i32, vp, vp, i32]
         lib.orc_softplus.argtypes, lib.orc_softplus.restype = [dbl], dbl
         lib.orc_score.argtypes, lib.orc_score.restype = [dbl], dbl
@@ -110,6 +114,22 @@ def decode_mxfp4(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     lib = _load()
     for r in range(R):
         lib.orc_decode_mxfp4_row(_p(q[r]), _p(s[r]), K, _p(out[r]))
+    return out
+
+
+def half(bits: int) -> float:
+    return _load().orc_half(int(bits))
+
+
+def decode_q2k(blocks: np.ndarray, K: int) -> np.ndarray:
+    """Decode a Q2_K matrix [R][K/256*84] (GGUF Q2_K super-blocks) to fp64 [R][K], one row at a time."""
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    R = blocks.shape[0]
+    assert blocks.shape[1] == K // 256 * 84
+    out = np.empty((R, K), dtype=np.float64)
+    lib = _load()
+    for r in range(R):
+        lib.orc_decode_q2k_row(_p(blocks[r]), K, _p(out[r]))
     return out
 
 
@@ -184,7 +204,7 @@ def rmsnorm_bf16(x_bf16: np.ndarray, g_bf16: np.ndarray, eps: float) -> np.ndarr
 
 def forward(shape, x, router_w, experts, router_bias=None, token_ids=None, tid2eid=None, rows=None,
             route_scale=None, swiglu_limit=None, with_shared=True, threads=None, norm_w=None, norm_eps=1e-6,
-            residual=None, bias_mode=0, shared_bf16=None) -> dict:
+            residual=None, bias_mode=0, shared_bf16=None, experts_q2k=None) -> dict:
     """The whole layer in fp64.
 
     bias_mode: 0 = router_bias added to the logits (selection and gates); 1 = added to the
@@ -194,6 +214,9 @@ def forward(shape, x, router_w, experts, router_bias=None, token_ids=None, tid2e
     residual: optional bf16 [N][d] added to the output.
     shared_bf16: optional dict of bf16 bit patterns gate/up [I][d], down [d][I]: the shared expert in
     bf16 (the MXFP4 shared expert at index E is then not used).
+    experts_q2k: optional dict of Q2_K blocks gate/up [E][I][d/256*84], down [E][d][I/256*84]: the routed
+    experts in Q2_K instead of the MXFP4 experts (whose shared expert, index E, still applies unless
+    shared_bf16 is given or with_shared is False).
 
     experts: dict of natural-layout MXFP4 arrays gate_q/gate_s/up_q/up_s [E+1][I][...] and
     down_q/down_s [E+1][d][...]; index E is the shared expert (ignored if with_shared=False).
@@ -205,7 +228,8 @@ def forward(shape, x, router_w, experts, router_bias=None, token_ids=None, tid2e
     assert x.shape == (N, d)
     cfg = _Cfg(N, d, E, k, I, 0 if shape.routing == "topk" else 1,
                float(shape.route_scale if route_scale is None else route_scale),
-               float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit), float(norm_eps), int(bias_mode))
+               float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit), float(norm_eps), int(bias_mode),
+               0 if experts_q2k is None else 1)
     keep = []
 
     def P(a, dtype=None):
@@ -218,10 +242,16 @@ def forward(shape, x, router_w, experts, router_bias=None, token_ids=None, tid2e
     w = experts
     mx_sh = with_shared and shared_bf16 is None
     b = shared_bf16 or {}
+    if experts_q2k is not None:
+        assert d % 256 == 0 and I % 256 == 0, "Q2_K experts need d and I multiples of 256"
+        qk = experts_q2k
+        routed = (P(qk["gate"][:E]), None, P(qk["up"][:E]), None, P(qk["down"][:E]), None)
+    else:
+        routed = (P(w["gate_q"][:E]), P(w["gate_s"][:E]), P(w["up_q"][:E]), P(w["up_s"][:E]),
+                  P(w["down_q"][:E]), P(w["down_s"][:E]))
     ins = _Inputs(P(x), P(router_w, np.float32), P(router_bias, np.float32), P(token_ids, np.int32),
                   P(tid2eid, np.int32), 0 if tid2eid is None else int(np.asarray(tid2eid).shape[0]),
-                  P(w["gate_q"][:E]), P(w["gate_s"][:E]), P(w["up_q"][:E]), P(w["up_s"][:E]),
-                  P(w["down_q"][:E]), P(w["down_s"][:E]),
+                  *routed,
                   P(w["gate_q"][E]) if mx_sh else None, P(w["gate_s"][E]) if mx_sh else None,
                   P(w["up_q"][E]) if mx_sh else None, P(w["up_s"][E]) if mx_sh else None,
                   P(w["down_q"][E]) if mx_sh else None, P(w["down_s"][E]) if mx_sh else None,

@@ -28,6 +28,12 @@
  * - the shared expert optionally in bf16 instead of MXFP4 (model card,
  *   Preprocessing and "Model Architecture and Objective": shared tensors in
  *   Q8_0/BF16, expert blocks in MXFP4).
+ * - the routed experts optionally as Q2_K blocks (TensorSharp "Getting a
+ *   drafter": --expert-type q2_k for the drafter's routed experts; the
+ *   layout is GGUF's Q2_K, see orc_decode_q2k_row).  The pages do not define
+ *   the format, so its byte-level reading is parity unpinned against a GGUF
+ *   implementation: the pins check the decode against the format's published
+ *   description (positions, scales, mins, fp16 factors), not against a file.
  */
 #include <math.h>
 #include <pthread.h>
@@ -103,6 +109,43 @@ void orc_decode_mxfp4_row(const uint8_t* q, const uint8_t* s, int K, double* out
       int code = (t & 1) ? (byte >> 4) : (byte & 15);
       out[t] = orc_e2m1(code) * scale;
     }
+  }
+}
+
+/* IEEE half-precision bits -> value (sign, 5 exponent bits with bias 15, 10
+ * fraction bits; exponent 0 = subnormal f * 2^-24; exponent 31 = inf / NaN). */
+double orc_half(uint16_t h) {
+  const int sign = h >> 15, ex = (h >> 10) & 31, f = h & 1023;
+  double mag;
+  if (ex == 0) mag = ldexp((double)f, -24);
+  else if (ex == 31) mag = f ? NAN : INFINITY;
+  else mag = ldexp(1.0 + f / 1024.0, ex - 15);
+  return sign ? -mag : mag;
+}
+
+/* One row of a Q2_K matrix (the GGUF Q2_K format; the pages name the format,
+ * TensorSharp "Getting a drafter", --expert-type q2_k, without defining it):
+ * K values in K/256 super-blocks of 84 bytes.  A super-block holds 16
+ * sub-blocks of 16 consecutive values; byte n (0..15) carries sub-block n's
+ * 4-bit scale (low nibble) and 4-bit min (high nibble); bytes 16..79 carry the
+ * 2-bit quants, four to a byte: the block's two halves of 128 values use 32
+ * bytes each, and inside a half, byte i (0..31) holds in bits 2j..2j+1 the
+ * quant of value 32j + i; bytes 80..81 and 82..83 are the half-precision
+ * factors d and dmin.  A value decodes to d * scale * q - dmin * min. */
+void orc_decode_q2k_row(const uint8_t* row, int K, double* out) {
+  for (int b = 0; b < K / 256; ++b) {
+    const uint8_t* blk = row + (size_t)b * 84;
+    const double d = orc_half((uint16_t)(blk[80] | (blk[81] << 8)));
+    const double dmin = orc_half((uint16_t)(blk[82] | (blk[83] << 8)));
+    double* o = out + 256 * b;
+    for (int half = 0; half < 2; ++half)
+      for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < 32; ++i) {
+          const int t = 128 * half + 32 * j + i;
+          const int q = (blk[16 + 32 * half + i] >> (2 * j)) & 3;
+          const int sb = blk[t / 16];
+          o[t] = d * (double)(sb & 15) * q - dmin * (double)(sb >> 4);
+        }
   }
 }
 
@@ -279,6 +322,7 @@ typedef struct {
 
 typedef struct {
   int d, I;
+  int q2k;  /* routed experts in Q2_K blocks (gq/uq/dq), else MXFP4 */
   double limit;
   /* per expert e in [0, E]: gate/up [I][d], down [d][I]; E = shared */
   const uint8_t *gq, *gs, *uq, *us, *dq, *ds;       /* routed, [E][...] */
@@ -313,6 +357,12 @@ static orc_mat mat_of(const ffn_ctx* c, int e, int which) {
  * in fp64: the shared expert (e == E) from its bf16 weights when given, else
  * from MXFP4. */
 static void weight_row(const ffn_ctx* c, int e, int which, int row, int K, double* out) {
+  if (e < c->E && c->q2k) {
+    const uint8_t* base = which == 0 ? c->gq : which == 1 ? c->uq : c->dq;
+    const size_t rows = which == 2 ? (size_t)c->d : (size_t)c->I, row_bytes = (size_t)(K / 256) * 84;
+    orc_decode_q2k_row(base + ((size_t)e * rows + row) * row_bytes, K, out);
+    return;
+  }
   if (e == c->E && c->sgw) {
     const uint16_t* w = which == 0 ? c->sgw : which == 1 ? c->suw : c->sdw;
     for (int i = 0; i < K; ++i) out[i] = orc_bf16(w[(size_t)row * K + i]);
@@ -370,6 +420,7 @@ typedef struct {
   double swiglu_limit;  /* <= 0 disables the clamp */
   float norm_eps;       /* RMSNorm eps (used when norm_w != NULL) */
   int bias_mode;        /* router_bias: 0 added to the logits; 1 added to the scores for the selection only */
+  int expert_format;    /* routed experts: 0 MXFP4 (gate_q/gate_s ...), 1 Q2_K blocks (gate_q, up_q, down_q) */
 } orc_cfg;
 
 typedef struct {
@@ -379,7 +430,8 @@ typedef struct {
   const int32_t* token_ids; /* [N] (hash) */
   const int32_t* tid2eid;   /* [vocab][k] (hash) */
   long vocab;
-  /* routed experts, natural layout: gate/up q [E][I][d/2] s [E][I][d/32], down q [E][d][I/2] s [E][d][I/32] */
+  /* routed experts, natural layout: gate/up q [E][I][d/2] s [E][I][d/32], down q [E][d][I/2] s [E][d][I/32];
+   * with expert_format 1, gate_q/up_q [E][I][d/256 * 84] and down_q [E][d][I/256 * 84] Q2_K blocks */
   const uint8_t *gate_q, *gate_s, *up_q, *up_s, *down_q, *down_s;
   /* shared expert, same layout with one matrix; gate_q == NULL means no shared expert */
   const uint8_t *sh_gate_q, *sh_gate_s, *sh_up_q, *sh_up_s, *sh_down_q, *sh_down_s;
@@ -472,7 +524,7 @@ int orc_forward(const orc_cfg* cfg, const orc_inputs* in, const int32_t* rows, i
     }
     double* h = (double*)malloc(sizeof(double) * (size_t)n_pairs * I);
     double* y = (double*)malloc(sizeof(double) * (size_t)n_pairs * d);
-    ffn_ctx fc = {d, I, cfg->swiglu_limit,
+    ffn_ctx fc = {d, I, cfg->expert_format == 1, cfg->swiglu_limit,
                   in->gate_q, in->gate_s, in->up_q, in->up_s, in->down_q, in->down_s,
                   in->sh_gate_q, in->sh_gate_s, in->sh_up_q, in->sh_up_s, in->sh_down_q, in->sh_down_s,
                   in->sh_gate_w, in->sh_up_w, in->sh_down_w,
