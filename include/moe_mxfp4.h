@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOE_MXFP4_VERSION 3
+#define MOE_MXFP4_VERSION 4
 
 enum {
   MOE_OK = 0,
@@ -71,6 +71,7 @@ enum {
 enum { MOE_ROUTING_TOPK = 0, MOE_ROUTING_HASH = 1 };
 enum { MOE_BIAS_LOGIT = 0, MOE_BIAS_SELECT = 1 };
 enum { MOE_SHARED_MXFP4 = 0, MOE_SHARED_BF16 = 1 };
+enum { MOE_EXPERTS_MXFP4 = 0, MOE_EXPERTS_Q2K = 1 };
 
 /* Supported shapes: d_model and d_ff multiples of 128 (>= 128, <= 65536),
  * 1 <= n_experts <= 1024, 1 <= top_k <= min(8, n_experts),
@@ -96,10 +97,17 @@ typedef struct moe_config {
                            model card ("Preprocessing"; "Model Architecture and Objective") keeps the
                            expert blocks in MXFP4 and the shared tensors in Q8_0/BF16 without saying on
                            which side the per-layer shared expert falls; both are supported. */
+  int32_t expert_format; /* weights of the routed experts: MOE_EXPERTS_MXFP4 (packed MXFP4, w.*_q and
+                           w.*_s) or MOE_EXPERTS_Q2K (packed Q2_K, w.gate_q/up_q/down_q only; see
+                           moe_pack_q2k).  Q2_K needs d and I multiples of 256 and a shared expert, if
+                           any, in bf16 (MOE_SHARED_BF16); otherwise MOE_ERR_UNSUPPORTED.  TensorSharp
+                           "Getting a drafter" names q2_k as the drafter's routed-expert type. */
 } moe_config_t;
 
 /*
- * MXFP4 matrices in the library's packed layout (see moe_pack_mxfp4).  A
+ * Routed experts in the library's packed layout: MXFP4 (moe_pack_mxfp4) or,
+ * with expert_format MOE_EXPERTS_Q2K, Q2_K (moe_pack_q2k, *_q pointers only,
+ * 16-byte aligned, the *_s pointers ignored).  An MXFP4 matrix: a
  * matrix [rows][K] of E2M1 values with one E8M0 scale per 32 consecutive
  * values along K.  Each group of n_mat matrices is stored back to back.
  *   gate, up : routed, n_mat = E, each [I][d]   (w1 and w3 of each expert)
@@ -201,6 +209,33 @@ int moe_packed_mxfp4_bytes(int32_t rows, int32_t K, size_t* q_bytes, size_t* s_b
  */
 int moe_pack_mxfp4(const void* q, const void* s, int32_t n_mat, int32_t rows, int32_t K, void* q_out,
                    void* s_out, void* stream);
+
+/*
+ * Q2_K matrices (MOE_EXPERTS_Q2K): GGUF's Q2_K super-blocks, 256 values of a
+ * row in 84 bytes (the pages name the type, not its layout): bytes 0..15 one
+ * byte per 16-value sub-block (scale in the low nibble, min in the high
+ * nibble), bytes 16..79 the 2-bit quants (the block's two 128-value halves 32
+ * bytes each; value 32j + i of a half in bits 2j..2j+1 of the half's byte i),
+ * bytes 80..83 fp16 d then fp16 dmin; a value is d * scale * q - dmin * min.
+ *
+ * Bytes of one Q2_K matrix [rows][K], natural or packed (the same size):
+ * rows * (K/256) * 84; rows % 16 == 0, K % 256 == 0.
+ */
+int moe_q2k_bytes(int32_t rows, int32_t K, size_t* bytes);
+
+/*
+ * Re-lay n_mat Q2_K matrices from the natural layout [n_mat][rows][K/256][84]
+ * (row-major super-blocks) to the packed layout the layer reads (same values,
+ * one-time weight preparation).  Packed, per matrix: the 16-row tile rt and
+ * super-block b at byte (rt*(K/256) + b)*1344, holding
+ *   [0, 1024)    lane l (0..63): quant bytes 8g..8g+7 of both halves (natural
+ *                bytes 16+8g..+7 then 48+8g..+7) of row 16*rt + l%16, g = l/16;
+ *   [1024, 1280) the 16 scale/min bytes of each of the 16 rows;
+ *   [1280, 1344) d and dmin (4 bytes) of each of the 16 rows.
+ * q 4-byte aligned, q_out 16-byte aligned, not overlapping.  Asynchronous on
+ * `stream`.
+ */
+int moe_pack_q2k(const void* q, int32_t n_mat, int32_t rows, int32_t K, void* q_out, void* stream);
 
 /* Device workspace bytes that moe_layer_forward needs for n_rows rows. */
 int moe_workspace_size(const moe_config_t* cfg, int32_t n_rows, size_t* bytes);

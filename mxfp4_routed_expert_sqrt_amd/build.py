@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 ARCH = "gfx950"
 
-HIP_SOURCES = ["moe_layer.hip", "k_pack.hip", "k_router.hip", "k_expert.hip", "k_shared.hip"]
+HIP_SOURCES = ["moe_layer.hip", "k_pack.hip", "k_router.hip", "k_expert.hip", "k_shared.hip", "k_q2k.hip"]
 
 # Packed-FP32 instructions are kept out of generated code on purpose.
 HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared", "-Wall",

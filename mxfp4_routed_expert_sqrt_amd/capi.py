@@ -17,6 +17,8 @@ MOE_NOALLOC_SCRATCH_BYTES = 96 << 20
 MOE_ROUTING_TOPK, MOE_ROUTING_HASH = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_SHARED_MXFP4, MOE_SHARED_BF16 = 0, 1
+MOE_EXPERTS_MXFP4, MOE_EXPERTS_Q2K = 0, 1
+Q2K_BLOCK_BYTES = 84  # one 256-value Q2_K super-block
 MOE_MAX_ROWS = 1 << 20
 
 c_i32, c_i64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -25,7 +27,7 @@ c_i32, c_i64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_flo
 class MoeConfig(ctypes.Structure):
     _fields_ = [("d_model", c_i32), ("d_ff", c_i32), ("n_experts", c_i32), ("top_k", c_i32), ("routing", c_i32),
                 ("has_shared", c_i32), ("route_scale", c_f32), ("swiglu_limit", c_f32), ("norm_eps", c_f32),
-                ("bias_mode", c_i32), ("shared_format", c_i32)]
+                ("bias_mode", c_i32), ("shared_format", c_i32), ("expert_format", c_i32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -63,6 +65,10 @@ def lib():
         L.moe_packed_mxfp4_bytes.restype = ctypes.c_int
         L.moe_pack_mxfp4.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
         L.moe_pack_mxfp4.restype = ctypes.c_int
+        L.moe_q2k_bytes.argtypes = [c_i32, c_i32, ctypes.POINTER(c_size)]
+        L.moe_q2k_bytes.restype = ctypes.c_int
+        L.moe_pack_q2k.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]
+        L.moe_pack_q2k.restype = ctypes.c_int
         L.moe_workspace_size.argtypes = [ctypes.POINTER(MoeConfig), c_i32, ctypes.POINTER(c_size)]
         L.moe_workspace_size.restype = ctypes.c_int
         L.moe_layer_forward.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeArgs), c_vp]
@@ -73,8 +79,8 @@ def lib():
     return _lib
 
 
-EXPORTED = ("moe_version", "moe_status_string", "moe_packed_mxfp4_bytes", "moe_pack_mxfp4", "moe_workspace_size",
-            "moe_layer_forward", "moe_layer_forward_noalloc")
+EXPORTED = ("moe_version", "moe_status_string", "moe_packed_mxfp4_bytes", "moe_pack_mxfp4", "moe_q2k_bytes",
+            "moe_pack_q2k", "moe_workspace_size", "moe_layer_forward", "moe_layer_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -105,6 +111,16 @@ def moe_packed_mxfp4_bytes(rows: int, K: int):
 
 def moe_pack_mxfp4(q, s, n_mat, rows, K, q_out, s_out, stream) -> int:
     return lib().moe_pack_mxfp4(q, s, n_mat, rows, K, q_out, s_out, stream)
+
+
+def moe_q2k_bytes(rows: int, K: int) -> int:
+    b = c_size()
+    _check(lib().moe_q2k_bytes(rows, K, ctypes.byref(b)))
+    return b.value
+
+
+def moe_pack_q2k(q, n_mat, rows, K, q_out, stream) -> int:
+    return lib().moe_pack_q2k(q, n_mat, rows, K, q_out, stream)
 
 
 def moe_workspace_size(cfg: MoeConfig, n_rows: int) -> int:

@@ -90,6 +90,27 @@ __device__ __forceinline__ int xcd_unit_claim(int n_units, int32_t* ctr, int* s_
   return *s_claim;
 }
 
+// Work group and feature block of unit `unit`.  Units run through the work
+// list expert by expert.  Group-major (FBMAJOR false): the n_fb feature blocks
+// of one group are consecutive, so they share that group's activations in L2.
+// Feature-block-major (the tall units): within an expert, the expert's ng
+// groups of one feature block are consecutive, so they share that block's
+// weights in L2 while they run side by side on one XCD (at 8192 rows this
+// took the gate/up weight fetch from 6.31 to 3.68 GB per launch and down from
+// 2.41 to 1.69 GB).
+template <bool FBMAJOR>
+__device__ __forceinline__ Group unit_group(const Group* groups, int unit, int n_fb, int* fb) {
+  const Group g = groups[unit / n_fb];
+  if constexpr (!FBMAJOR) {
+    *fb = unit % n_fb;
+    return g;
+  } else {
+    const int l = unit - g.first * n_fb;
+    *fb = l / g.ng;
+    return groups[g.first + l % g.ng];
+  }
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

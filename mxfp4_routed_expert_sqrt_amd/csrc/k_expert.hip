@@ -489,27 +489,6 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
   }
 }
 
-// Work group and feature block of unit `unit`.  Units run through the work
-// list expert by expert.  Group-major (FBMAJOR false): the n_fb feature blocks
-// of one group are consecutive, so they share that group's activations in L2.
-// Feature-block-major (the tall units): within an expert, the expert's ng
-// groups of one feature block are consecutive, so they share that block's
-// weights in L2 while they run side by side on one XCD (at 8192 rows this
-// took the gate/up weight fetch from 6.31 to 3.68 GB per launch and down from
-// 2.41 to 1.69 GB).
-template <bool FBMAJOR>
-__device__ __forceinline__ Group unit_group(const Group* groups, int unit, int n_fb, int* fb) {
-  const Group g = groups[unit / n_fb];
-  if constexpr (!FBMAJOR) {
-    *fb = unit % n_fb;
-    return g;
-  } else {
-    const int l = unit - g.first * n_fb;
-    *fb = l / g.ng;
-    return groups[g.first + l % g.ng];
-  }
-}
-
 // POOL: units dealt by xcd_unit_claim (static ranges with a shared tail),
 // else by xcd_unit_split (static ranges, optional tail halves).
 template <int TPM, int WAVES, int NB, int RING, bool NT, bool FP6, bool POOL>
@@ -608,14 +587,6 @@ __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
     }
   }
   down_unit<NA, WAVES, NB, RING, NT, FP6>(a, g, fu0, lds);
-}
-
-// Enough workgroups for every unit to be taken in halves (see xcd_unit_split).
-static unsigned unit_grid(int max_groups, int n_fb) {
-  const size_t halves = 2 * (size_t)max_groups * n_fb;
-  size_t per = (halves + kXcds - 1) / kXcds;
-  per += per & 1;
-  return (unsigned)(kXcds * per);
 }
 
 // Narrow (16-row) units: the widest unit that divides the output width;

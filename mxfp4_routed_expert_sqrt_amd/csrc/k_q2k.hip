@@ -1,0 +1,410 @@
+// Routed experts in Q2_K, the drafter's expert type (TensorSharp "Getting a
+// drafter", --expert-type q2_k; the block layout is GGUF's Q2_K): weight
+// packing, activation sub-block sums and the grouped gate/up and down GEMMs on
+// bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation).
+//
+// A Q2_K super-block holds 256 values of one weight row: 2-bit quants q, a
+// 4-bit scale sc and min mn per 16-value sub-block m, and fp16 factors d and
+// dmin; a value is d * sc * q - dmin * mn.  For weight row n and activation
+// row r, the dot product over super-block b is
+//     d * (T1 - 128 X) - dmin * T2,
+//     T1 = sum_t (128 + sc[t/16] q[t]) x[r][t]        8 MFMA k-steps
+//     T2 = sum_m mn[m] (xh[r][m] + xl[r][m])           1 MFMA k-step
+//     X  = sum_t x[r][t],   xh + xl = the sum of x over sub-block m (bf16 hi/lo)
+// 128 + sc * q (at most 173) is an integer, so it is exact in bf16, and it is
+// built by byte shuffles alone (a byte p under the high byte 0x43 is the bf16
+// number 128 + p); bf16 x times an integer is exact in fp32.  What rounds:
+// the fp32 sums, xh + xl (16 bits of each sub-block sum) and the fold; h is
+// rounded once to bf16 for the down GEMM.
+//
+// A workgroup = one work unit = (group of <= 16*NB rows of one expert, a
+// block of output features).  Each wave owns TPM 16-row weight tiles (of gate
+// and of up, for gate/up), their per-lane fragments loaded straight from HBM
+// into registers one super-block ahead; the activation rows, their sub-block
+// pairs and X are staged once per workgroup through LDS (double-buffered).
+// MFMA operands: A = 16 activation rows, B = 16 weight rows; lane (col, g)
+// supplies row col, K values 8g..8g+7 of each 32-wide k-step, and holds
+// D[activation row 4g+i][weight row col], so each lane's four results share
+// one weight row and its d and dmin.
+#include "kernels.h"
+
+namespace moe {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Packed tile (16 rows x one super-block): [0, 1024) quants, lane l = 16 bytes
+// of row l%16 (natural bytes 16+8g..+7 and 48+8g..+7, g = l/16); [1024, 1280)
+// the 16 scale/min bytes of each row; [1280, 1344) d and dmin of each row.
+constexpr int kQkScales = 1024, kQkFactors = 1280;
+
+// Natural [n_mat][rows][K/256][84] -> packed, one dword per thread.
+__global__ void pack_q2k_kernel(const uint8_t* __restrict__ q, size_t n_words, int K, uint8_t* __restrict__ out) {
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_words) return;
+  const int nb = K / 256;
+  const size_t tile = t / 336;
+  const int w = (int)(t % 336);
+  const size_t mat_rt = tile / nb;  // matrix * rows/16 + row tile
+  const int b = (int)(tile % nb);
+  int row, off;
+  if (w < 256) {
+    const int l = w >> 2, part = w & 3;
+    row = l & 15;
+    off = (part < 2 ? 16 : 48) + 8 * (l >> 4) + 4 * (part & 1);
+  } else if (w < 320) {
+    row = (w - 256) >> 2;
+    off = 4 * ((w - 256) & 3);
+  } else {
+    row = w - 320;
+    off = 80;
+  }
+  const uint8_t* src = q + ((mat_rt * 16 + row) * nb + b) * (size_t)kQ2kBlockBytes + off;
+  *(uint32_t*)(out + tile * kQ2kTileBytes + 4 * (size_t)w) = *(const uint32_t*)src;
+}
+
+hipError_t launch_pack_q2k(const uint8_t* q, int n_mat, int rows, int K, uint8_t* out, hipStream_t stream) {
+  const size_t n_words = (size_t)n_mat * (rows / 16) * (K / 256) * 336;
+  if (n_words == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_q2k_kernel, dim3((unsigned)((n_words + 255) / 256)), dim3(256), 0, stream, q, n_words, K,
+                     out);
+  return hipGetLastError();
+}
+
+// One thread per (row, 16-value sub-block): the fp32 sum in ascending order,
+// stored as bf16 hi (truncated) | bf16 lo (rest, nearest even) << 16; the 16
+// sub-blocks of a super-block are 16 consecutive lanes, whose butterfly sum
+// (a fixed order) is X.
+__global__ void q2k_sums_kernel(const uint16_t* __restrict__ act, size_t total, uint32_t* __restrict__ pairs,
+                                float* __restrict__ X) {
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  float s = 0.f;
+  if (t < total) {
+    const uint16_t* src = act + t * 16;
+    const u32x4 v0 = *(const u32x4*)src, v1 = *(const u32x4*)(src + 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s += __uint_as_float(v0[i] << 16);
+      s += __uint_as_float(v0[i] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s += __uint_as_float(v1[i] << 16);
+      s += __uint_as_float(v1[i] & 0xffff0000u);
+    }
+  }
+  float x = s;
+  x += __shfl_xor(x, 1, kWave);
+  x += __shfl_xor(x, 2, kWave);
+  x += __shfl_xor(x, 4, kWave);
+  x += __shfl_xor(x, 8, kWave);
+  if (t < total) {
+    const uint32_t hi = __float_as_uint(s) & 0xffff0000u;
+    pairs[t] = (hi >> 16) | ((uint32_t)f32_to_bf16_rne(s - __uint_as_float(hi)) << 16);
+    if ((t & 15) == 0) X[t >> 4] = x;
+  }
+}
+
+hipError_t launch_q2k_sums(const uint16_t* act, int rows, int K, uint32_t* pairs, float* X, hipStream_t stream) {
+  const size_t total = (size_t)rows * (K / 16);  // a multiple of 16: whole super-blocks per lane group
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(q2k_sums_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, act, total,
+                     pairs, X);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// LDS buffer of one super-block of the unit's 16*NB activation rows: the rows
+// (256 bf16 + 16 bytes of padding, so the 16 rows of a fragment read fall in
+// distinct banks), their 16 sub-block pairs (+16 bytes) and their X values.
+constexpr int kQkXStride = 528, kQkPStride = 80;
+
+template <int NB>
+struct QkBuf {
+  static constexpr int kRows = 16 * NB;
+  static constexpr int kPairs = kRows * kQkXStride;
+  static constexpr int kSums = kPairs + kRows * kQkPStride;
+  static constexpr int kBytes = kSums + kRows * 4;
+};
+
+// This thread's share of one super-block of activations (global -> registers
+// -> LDS).  Activation piece p (16 bytes) = row p/32, bytes 16*(p%32); pair
+// piece tid < 4*rows = row tid/4, pairs 4*(tid%4)..; X of row tid < rows.
+template <int THREADS, int NB>
+struct QkStage {
+  static constexpr int kRows = 16 * NB;
+  static constexpr int kPieces = kRows * 32 / THREADS;
+  static_assert(kRows * 32 % THREADS == 0 && 4 * kRows <= THREADS, "staging shape");
+  u32x4 x[kPieces];
+  u32x4 pr;
+  float xs;
+  int xrow[kPieces], prow, srow;  // activation row of each piece
+
+  __device__ __forceinline__ void load(const Q2kArgs& a, int b) {
+    const int tid = threadIdx.x, nb = a.K / 256;
+#pragma unroll
+    for (int m = 0; m < kPieces; ++m)
+      x[m] = *(const u32x4*)(a.act + (size_t)xrow[m] * a.K + 256 * b + 8 * ((tid + THREADS * m) & 31));
+    if (tid < 4 * kRows) pr = *(const u32x4*)(a.pairs + ((size_t)prow * nb + b) * 16 + 4 * (tid & 3));
+    if (tid < kRows) xs = a.X[(size_t)srow * nb + b];
+  }
+
+  __device__ __forceinline__ void store(uint8_t* buf) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < kPieces; ++m) {
+      const int p = tid + THREADS * m;
+      *(u32x4*)(buf + (p >> 5) * kQkXStride + 16 * (p & 31)) = x[m];
+    }
+    if (tid < 4 * kRows) *(u32x4*)(buf + QkBuf<NB>::kPairs + (tid >> 2) * kQkPStride + 16 * (tid & 3)) = pr;
+    if (tid < kRows) *(float*)(buf + QkBuf<NB>::kSums + 4 * tid) = xs;
+  }
+};
+
+// Per-lane fragments of NA weight tiles for one super-block.
+template <int NA>
+struct QkW {
+  u32x4 qs[NA], sc[NA];
+  uint32_t dd[NA];
+};
+
+typedef const __attribute__((address_space(1))) uint8_t* qk_gptr;
+
+__device__ __forceinline__ qk_gptr qk_uniform(const uint8_t* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (qk_gptr)(((uint64_t)hi << 32) | lo);
+}
+
+template <int NA>
+__device__ __forceinline__ void qk_load_w(QkW<NA>& f, const qk_gptr (&w)[NA], int b) {
+  typedef const __attribute__((address_space(1))) u32x4* p4;
+  typedef const __attribute__((address_space(1))) uint32_t* p1;
+  const int lane = threadIdx.x & 63, col = lane & 15;
+  const uint32_t off = (uint32_t)b * kQ2kTileBytes;
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    f.qs[i] = __builtin_nontemporal_load((p4)(w[i] + off + 16 * lane));
+    f.sc[i] = *(p4)(w[i] + off + kQkScales + 16 * col);
+    f.dd[i] = *(p1)(w[i] + off + kQkFactors + 4 * col);
+  }
+}
+
+// bf16 pairs 128 + byte: bytes 0,1 (LO) or 2,3 of p under the high byte 0x43.
+__device__ __forceinline__ uint32_t qk_pair_lo(uint32_t p) { return 0x43004300u | (p & 0xffu) | ((p & 0xff00u) << 8); }
+__device__ __forceinline__ uint32_t qk_pair_hi(uint32_t p) {
+  return 0x43004300u | ((p >> 16) & 0xffu) | ((p >> 8) & 0xff0000u);
+}
+
+// B fragment of k-step S (values 32S + 8g .. +7 of the super-block) as the
+// bf16 numbers 128 + sc*q.  Those values sit in half S/4 at bits 2*(S%4) of
+// the lane's 8 quant bytes of that half, in sub-block 2S + g/2, whose scale is
+// nibble 0 of scale byte 2S + g/2 (gsh = 8*(g/2)).
+template <int S>
+__device__ __forceinline__ v8bf qk_frag(const u32x4& qs, const u32x4& sc, uint32_t gsh) {
+  constexpr int H = S >> 2, J = S & 3;
+  const uint32_t scv = (sc[S >> 1] >> (16 * (S & 1) + gsh)) & 15u;
+  const u16x2 m = {(unsigned short)scv, (unsigned short)scv};
+  const uint32_t q0 = (qs[2 * H] >> (2 * J)) & 0x03030303u, q1 = (qs[2 * H + 1] >> (2 * J)) & 0x03030303u;
+  // sc * q per byte (at most 45, so the two bytes of a 16-bit lane never carry)
+  const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, q0) * m);
+  const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, q1) * m);
+  const u32x4 r = {qk_pair_lo(p0), qk_pair_hi(p0), qk_pair_lo(p1), qk_pair_hi(p1)};
+  return __builtin_bit_cast(v8bf, r);
+}
+
+// B fragment of the min k-step: k = 2m + t (t = 0 hi, 1 lo) holds mn[m] of
+// sub-blocks m = 4g..4g+3 (high nibbles of scale dword g), as exact bf16.
+__device__ __forceinline__ v8bf qk_min_frag(const u32x4& sc, int g) {
+  const uint32_t sg = g == 0 ? sc[0] : (g == 1 ? sc[1] : (g == 2 ? sc[2] : sc[3]));
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = __float_as_uint((float)((sg >> (8 * i + 4)) & 15u)) >> 16;
+    r[i] = b | (b << 16);
+  }
+  return __builtin_bit_cast(v8bf, r);
+}
+
+// One super-block: T1 over 8 k-steps, the fold d * (T1 - 128 X), then T2 and
+// the fold - dmin * T2, into acc[tile][row block].
+template <int NA, int NB>
+__device__ __forceinline__ void qk_superblock(const QkW<NA>& f, const uint8_t* buf, v4f (&acc)[NA][NB]) {
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+  const uint32_t gsh = 8 * (g >> 1);
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  v4f t[NA][NB];
+#define QK_STEP(S)                                                                                    \
+  {                                                                                                   \
+    v8bf bw[NA];                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < NA; ++i) bw[i] = qk_frag<S>(f.qs[i], f.sc[i], gsh);         \
+    _Pragma("unroll") for (int tt = 0; tt < NB; ++tt) {                                               \
+      const v8bf av = *(const v8bf*)(buf + (16 * tt + col) * kQkXStride + 64 * (S) + 16 * g);         \
+      _Pragma("unroll") for (int i = 0; i < NA; ++i) t[i][tt] =                                       \
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[i], (S) == 0 ? zero : t[i][tt], 0, 0, 0);    \
+    }                                                                                                 \
+  }
+  QK_STEP(0)
+  QK_STEP(1)
+  QK_STEP(2)
+  QK_STEP(3)
+  QK_STEP(4)
+  QK_STEP(5)
+  QK_STEP(6)
+  QK_STEP(7)
+#undef QK_STEP
+  v4f xv[NB];
+#pragma unroll
+  for (int tt = 0; tt < NB; ++tt) xv[tt] = *(const v4f*)(buf + QkBuf<NB>::kSums + 4 * (16 * tt + 4 * g));
+  float dmin[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const f16x2 dd = __builtin_bit_cast(f16x2, f.dd[i]);
+    const float dv = (float)dd[0];
+    dmin[i] = (float)dd[1];
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][tt][e] = fmaf(dv, fmaf(-128.f, xv[tt][e], t[i][tt][e]), acc[i][tt][e]);
+  }
+  v8bf pv[NB];
+#pragma unroll
+  for (int tt = 0; tt < NB; ++tt)
+    pv[tt] = *(const v8bf*)(buf + QkBuf<NB>::kPairs + (16 * tt + col) * kQkPStride + 16 * g);
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const v8bf bm = qk_min_frag(f.sc[i], g);
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt) {
+      const v4f t2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pv[tt], bm, zero, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][tt][e] = fmaf(-dmin[i], t2[e], acc[i][tt][e]);
+    }
+  }
+}
+
+// One work unit: output features [fu0, fu0 + WAVES*16*TPM) of group g; GU:
+// gate and up, written as h; else down, written as y.
+template <int TPM, int WAVES, int NB, bool GU>
+__device__ __forceinline__ void qk_unit(const Q2kArgs& a, const Group g, int fu0, uint8_t* lds) {
+  constexpr int NA = GU ? 2 * TPM : TPM, kThreads = 64 * WAVES, kRows = 16 * NB;
+  constexpr int kBuf = QkBuf<NB>::kBytes;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int K = a.K, R = a.R, nb = K / 256;
+  const int f0 = fu0 + wave * 16 * TPM;
+  const size_t mat = q2k_matrix_bytes(R, K), tile = (size_t)nb * kQ2kTileBytes;
+  qk_gptr w[NA];
+#pragma unroll
+  for (int i = 0; i < TPM; ++i) {
+    w[i] = qk_uniform(a.w0 + (size_t)g.e * mat + (size_t)(f0 / 16 + i) * tile);
+    if constexpr (GU) w[TPM + i] = qk_uniform(a.w1 + (size_t)g.e * mat + (size_t)(f0 / 16 + i) * tile);
+  }
+  // activation row of unit row c (padding rows repeat the group's first row)
+  auto act_row = [&](int c) -> int {
+    const int p = g.p0 + (c < g.cnt ? c : 0);
+    return GU ? a.perm[p] / a.k : p;
+  };
+  QkStage<kThreads, NB> st;
+#pragma unroll
+  for (int m = 0; m < QkStage<kThreads, NB>::kPieces; ++m) st.xrow[m] = act_row((tid + kThreads * m) >> 5);
+  st.prow = act_row(min(tid >> 2, kRows - 1));
+  st.srow = act_row(min(tid, kRows - 1));
+
+  v4f acc[NA][NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt) acc[i][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+  QkW<NA> fa, fb;
+  qk_load_w(fa, w, 0);
+  st.load(a, 0);
+  st.store(lds);
+  if (nb > 1) st.load(a, 1);
+  __syncthreads();
+  for (int b = 0; b < nb; b += 2) {
+    if (b + 1 < nb) qk_load_w(fb, w, b + 1);
+    qk_superblock(fa, lds, acc);
+    if (b + 1 < nb) {
+      st.store(lds + kBuf);
+      if (b + 2 < nb) st.load(a, b + 2);
+    }
+    __syncthreads();
+    if (b + 1 >= nb) break;
+    if (b + 2 < nb) qk_load_w(fa, w, b + 2);
+    qk_superblock(fb, lds + kBuf, acc);
+    if (b + 2 < nb) {
+      st.store(lds);
+      if (b + 3 < nb) st.load(a, b + 3);
+    }
+    __syncthreads();
+  }
+
+  const float L = a.limit;
+#pragma unroll
+  for (int i = 0; i < TPM; ++i)
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 16 * tt + 4 * grp + e;
+        if (c >= g.cnt) continue;
+        const size_t o = (size_t)(g.p0 + c) * R + f0 + 16 * i + col;
+        if constexpr (GU) {
+          float gv = acc[i][tt][e], uv = acc[TPM + i][tt][e];
+          if (L > 0.f) {
+            gv = fminf(gv, L);
+            uv = fminf(fmaxf(uv, -L), L);
+          }
+          a.h[o] = f32_to_bf16_rne(gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv);
+        } else {
+          a.y[o] = acc[i][tt][e];
+        }
+      }
+}
+
+// Units dealt by xcd_unit_claim; tall units feature-block-major (unit_group).
+template <int TPM, int WAVES, int NB, bool GU>
+__global__ void __launch_bounds__(64 * WAVES) q2k_kernel(Q2kArgs a) {
+  constexpr int kFeatUnit = WAVES * 16 * TPM;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * QkBuf<NB>::kBytes
+  const int n_fb = a.R / kFeatUnit;
+  __shared__ int s_claim;
+  const int half_idx = xcd_unit_claim(*a.n_groups * n_fb, a.pool, &s_claim);
+  if (half_idx < 0) return;
+  int fb;
+  const Group g = unit_group<NB == 4>(a.groups, half_idx >> 1, n_fb, &fb);
+  qk_unit<TPM, WAVES, NB, GU>(a, g, fb * kFeatUnit, lds);
+}
+
+template <int TPM, int WAVES, int NB, bool GU>
+static hipError_t q2k_launch(const Q2kArgs& a, int max_groups, hipStream_t stream) {
+  static std::atomic<uint64_t> attr{0};
+  constexpr int kFeatUnit = WAVES * 16 * TPM;
+  if (a.R % kFeatUnit || a.K % 256) return hipErrorInvalidValue;
+  const size_t lds = 2 * (size_t)QkBuf<NB>::kBytes;
+  hipError_t err = ensure_dynamic_lds(q2k_kernel<TPM, WAVES, NB, GU>, lds, attr);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((q2k_kernel<TPM, WAVES, NB, GU>), dim3(unit_grid(max_groups, a.R / kFeatUnit)),
+                     dim3(64 * WAVES), lds, stream, a);
+  return hipGetLastError();
+}
+
+// Units of 256 output features (8 waves x 2 tiles) on 32- and 64-row groups;
+// 16-row groups (small batches) take 128 (8 waves x 1 tile) for more units.
+hipError_t launch_q2k_gateup(const Q2kArgs& a, int max_groups, hipStream_t stream) {
+  if (a.rows == kTallGroupRows) return q2k_launch<1, 8, 4, true>(a, max_groups, stream);
+  if (a.rows == kMediumGroupRows) return q2k_launch<2, 8, 2, true>(a, max_groups, stream);
+  return q2k_launch<1, 8, 1, true>(a, max_groups, stream);
+}
+
+hipError_t launch_q2k_down(const Q2kArgs& a, int max_groups, hipStream_t stream) {
+  if (a.rows == kTallGroupRows) return q2k_launch<2, 8, 4, false>(a, max_groups, stream);
+  if (a.rows == kMediumGroupRows) return q2k_launch<2, 8, 2, false>(a, max_groups, stream);
+  return q2k_launch<1, 8, 1, false>(a, max_groups, stream);
+}
+
+}  // namespace moe

@@ -220,7 +220,7 @@ hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d,
                            uint8_t* xq, uint8_t* xs, int32_t* done, bool fp6, hipStream_t stream) {
   const int S = logits_splits(n_rows, E, d);
   const int n_tiles = logits_row_tiles(n_rows) * ((E + kLgExperts - 1) / kLgExperts) * S;
-  const size_t n_split = ((size_t)n_rows * (d / 32) + 255) / 256;
+  const size_t n_split = xq ? ((size_t)n_rows * (d / 32) + 255) / 256 : 0;  // no split asked for: logits only
   hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)(n_tiles + n_split)), dim3(256), 0, stream, x, w, n_rows, d, E,
                      S, n_tiles, z_part, xq, xs, done, fp6 ? 1 : 0);
   return hipGetLastError();

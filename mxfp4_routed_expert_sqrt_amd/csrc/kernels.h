@@ -52,6 +52,8 @@ __host__ __device__ inline size_t split_s_row_bytes(int K) {
 hipError_t launch_pack_mxfp4(const uint8_t* q, const uint8_t* s, int n_mat, int rows, int K, uint8_t* q_out,
                              uint8_t* s_out, hipStream_t stream);
 
+// Router logits partials and (xq != NULL) the two-term split of x; clears the
+// three counters at done.
 hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d, int E, float* z_part, uint8_t* xq,
                            uint8_t* xs, int32_t* done, bool fp6, hipStream_t stream);
 
@@ -123,6 +125,15 @@ struct ExpertArgs {
   int rows;                              // rows of the work list's groups (unit_rows); 64: FP6 activations
 };
 
+// Workgroups of a unit-dealt launch: enough for every unit of max_groups
+// groups x n_fb feature blocks to be taken in halves (see xcd_unit_split).
+inline unsigned unit_grid(int max_groups, int n_fb) {
+  const size_t halves = 2 * (size_t)max_groups * n_fb;
+  size_t per = (halves + kXcds - 1) / kXcds;
+  per += per & 1;
+  return (unsigned)(kXcds * per);
+}
+
 // max_groups: capacity of the work list (max_work_groups for a.rows)
 hipError_t launch_gateup(const ExpertArgs& a, int max_groups, hipStream_t stream);
 hipError_t launch_down(const ExpertArgs& a, int max_groups, hipStream_t stream);
@@ -139,6 +150,46 @@ hipError_t launch_shared_bf16_gateup(const uint16_t* x, int n_rows, int d, int I
                                      const uint16_t* wu, float limit, uint16_t* h, hipStream_t stream);
 hipError_t launch_shared_bf16_down(const uint16_t* h, int n_rows, int d, int I, const uint16_t* wd, float* y_sh,
                                    hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Routed experts in Q2_K (k_q2k.hip).  Packed matrix [R][K] (R % 16 == 0,
+// K % 256 == 0): 16-row tile rt, super-block b at byte (rt * K/256 + b) * 1344.
+constexpr int kQ2kBlockBytes = 84;   // one 256-value super-block of one row
+constexpr int kQ2kTileBytes = 1344;  // 16 rows of one super-block, packed
+__host__ __device__ inline size_t q2k_matrix_bytes(int rows, int K) {
+  return (size_t)rows * (size_t)(K / 256) * kQ2kBlockBytes;
+}
+
+hipError_t launch_pack_q2k(const uint8_t* q, int n_mat, int rows, int K, uint8_t* out, hipStream_t stream);
+
+// Per activation row of length K: pairs [rows][K/256][16] (bf16 hi | lo << 16
+// of each 16-value sub-block sum) and X [rows][K/256] (fp32 super-block sums).
+hipError_t launch_q2k_sums(const uint16_t* act, int rows, int K, uint32_t* pairs, float* X, hipStream_t stream);
+
+struct Q2kArgs {
+  const uint8_t *w0, *w1;  // packed Q2_K experts: gate and up (gate/up), or down (w0)
+  const uint16_t* act;     // bf16 activation rows [*][K]: x (reached through perm) or h (pair order)
+  const uint32_t* pairs;   // sub-block sums of the activation rows (launch_q2k_sums)
+  const float* X;
+  const int32_t* perm;
+  const Group* groups;
+  const int32_t* n_groups;
+  int K, R, k, rows;       // contraction, output width, top-k, rows of the work list's groups
+  float limit;             // swiglu limit (<= 0: none)
+  uint16_t* h;             // gate/up output: bf16 [P][R]
+  float* y;                // down output: fp32 [P][R]
+  int32_t* pool;           // claim counter (zeroed before the launch)
+};
+
+hipError_t launch_q2k_gateup(const Q2kArgs& a, int max_groups, hipStream_t stream);
+hipError_t launch_q2k_down(const Q2kArgs& a, int max_groups, hipStream_t stream);
+
+// Rows of the Q2_K work list's groups (as unit_rows; d and I multiples of 256).
+inline int q2k_unit_rows(int n_pairs, int E) {
+  if (n_pairs >= 32 * E) return kTallGroupRows;
+  if (n_pairs >= kWideUnitPairs) return kMediumGroupRows;
+  return kGroupRows;
+}
 
 // Worst-case number of work groups of <= rows rows each for n_rows rows:
 // sum_e ceil(c_e/rows) <= ceil(P/rows) + E, plus the shared rows.

@@ -39,7 +39,9 @@ int scratch_on_device(uint8_t** out) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, hist, done, xn, xq, xs, hq, hs, hsh, y, total;
+  size_t z, idx, gates, counts, offsets, perm, inv, groups, n_groups, hist, done, xn, xq, xs, hq, hs, hsh, y;
+  size_t xpair, xsum, hpair, hsum;  // Q2_K experts: sub-block sums of x and of h
+  size_t total;
   int max_groups;  // capacity of the work list: groups of kGroupRows rows, the most there can be
 };
 
@@ -47,6 +49,15 @@ struct Layout {
 // it is MXFP4; a bf16 shared expert has GEMMs of its own.
 bool shared_in_list(const moe_config_t& c) { return c.has_shared && c.shared_format == MOE_SHARED_MXFP4; }
 bool shared_bf16(const moe_config_t& c) { return c.has_shared && c.shared_format == MOE_SHARED_BF16; }
+bool q2k(const moe_config_t& c) { return c.expert_format == MOE_EXPERTS_Q2K; }
+
+// Bytes of one routed weight matrix set [E] of [rows][K]: q and s parts.
+size_t set_q_bytes(const moe_config_t& c, int rows, int K) {
+  return (size_t)c.n_experts * (q2k(c) ? q2k_matrix_bytes(rows, K) : packed_q_bytes(rows, K));
+}
+size_t set_s_bytes(const moe_config_t& c, int rows, int K) {
+  return q2k(c) ? 0 : (size_t)c.n_experts * packed_s_bytes(rows, K);
+}
 
 // Workspace carve-up; every region starts on a 256-byte boundary.
 Layout make_layout(const moe_config_t& c, int n) {
@@ -72,10 +83,15 @@ Layout make_layout(const moe_config_t& c, int n) {
   L.hist = take(route_hist_bytes(n, c.n_experts));
   L.done = take(12);  // selection completion count, gate/up and down claim counters
   L.xn = take(N * (size_t)c.d_model * 2);  // the normalised input (when norm_w is given)
-  L.xq = take(N * split_q_row_bytes(c.d_model));
-  L.xs = take(N * split_s_row_bytes(c.d_model));
-  L.hq = take(Phq * split_q_row_bytes(c.d_ff));
-  L.hs = take(Phq * split_s_row_bytes(c.d_ff));
+  const bool qk = q2k(c);
+  L.xq = take(qk ? 0 : N * split_q_row_bytes(c.d_model));
+  L.xs = take(qk ? 0 : N * split_s_row_bytes(c.d_model));
+  L.hq = take(Phq * split_q_row_bytes(c.d_ff));  // Q2_K: h in bf16, the same bytes
+  L.hs = take(qk ? 0 : Phq * split_s_row_bytes(c.d_ff));
+  L.xpair = take(qk ? N * (size_t)(c.d_model / 16) * 4 : 0);
+  L.xsum = take(qk ? N * (size_t)(c.d_model / 256) * 4 : 0);
+  L.hpair = take(qk ? P * (size_t)(c.d_ff / 16) * 4 : 0);
+  L.hsum = take(qk ? P * (size_t)(c.d_ff / 256) * 4 : 0);
   L.hsh = take(shared_bf16(c) ? N * (size_t)c.d_ff * 2 : 0);  // bf16 h of a bf16 shared expert
   L.y = take(Ptot * (size_t)c.d_model * 4);
   L.total = off;
@@ -101,6 +117,10 @@ int check_config(const moe_config_t* c) {
   if (!(c->norm_eps >= 0.f) || c->norm_eps == INFINITY) return MOE_ERR_INVALID;
   if (c->bias_mode != 0 && c->bias_mode != 1) return MOE_ERR_INVALID;
   if (c->shared_format != MOE_SHARED_MXFP4 && c->shared_format != MOE_SHARED_BF16) return MOE_ERR_INVALID;
+  if (c->expert_format != MOE_EXPERTS_MXFP4 && c->expert_format != MOE_EXPERTS_Q2K) return MOE_ERR_INVALID;
+  if (c->expert_format == MOE_EXPERTS_Q2K &&
+      (c->d_model % 256 || c->d_ff % 256 || (c->has_shared && c->shared_format != MOE_SHARED_BF16)))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -125,6 +145,8 @@ bool buffers_disjoint(const moe_config_t& c, const moe_args_t& a, const void* ws
                k = (size_t)c.top_k;
   const size_t gq = packed_q_bytes(c.d_ff, c.d_model), gs = packed_s_bytes(c.d_ff, c.d_model);
   const size_t dq = packed_q_bytes(c.d_model, c.d_ff), ds = packed_s_bytes(c.d_model, c.d_ff);
+  const size_t Egq = set_q_bytes(c, c.d_ff, c.d_model), Egs = set_s_bytes(c, c.d_ff, c.d_model);
+  const size_t Edq = set_q_bytes(c, c.d_model, c.d_ff), Eds = set_s_bytes(c, c.d_model, c.d_ff);
   Region r[32];
   int n = 0;
   auto add = [&](const void* p, size_t bytes, bool written) {
@@ -143,12 +165,12 @@ bool buffers_disjoint(const moe_config_t& c, const moe_args_t& a, const void* ws
   add(a.router_bias, E * 4, false);
   add(a.norm_w, a.norm_w ? d * 2 : 0, false);
   if (a.residual != a.out) add(a.residual, N * d * 2, false);
-  add(a.w.gate_q, E * gq, false);
-  add(a.w.gate_s, E * gs, false);
-  add(a.w.up_q, E * gq, false);
-  add(a.w.up_s, E * gs, false);
-  add(a.w.down_q, E * dq, false);
-  add(a.w.down_s, E * ds, false);
+  add(a.w.gate_q, Egq, false);
+  add(a.w.gate_s, Egs, false);
+  add(a.w.up_q, Egq, false);
+  add(a.w.up_s, Egs, false);
+  add(a.w.down_q, Edq, false);
+  add(a.w.down_s, Eds, false);
   if (shared_in_list(c)) {
     add(a.w.sh_gate_q, gq, false);
     add(a.w.sh_gate_s, gs, false);
@@ -179,9 +201,14 @@ int check_args(const moe_config_t& c, const moe_args_t& a) {
   if (!a.x || !a.router_w || !a.out) return MOE_ERR_INVALID;
   if (!aligned(a.x, 16) || !aligned(a.router_w, 16) || !aligned(a.out, 16)) return MOE_ERR_INVALID;
   if (a.router_bias && !aligned(a.router_bias, 4)) return MOE_ERR_INVALID;
-  if ((rc = check_mat(a.w.gate_q, a.w.gate_s)) || (rc = check_mat(a.w.up_q, a.w.up_s)) ||
-      (rc = check_mat(a.w.down_q, a.w.down_s)))
+  if (q2k(c)) {
+    const void* wq[] = {a.w.gate_q, a.w.up_q, a.w.down_q};
+    for (const void* p : wq)
+      if (!p || !aligned(p, 16)) return MOE_ERR_INVALID;
+  } else if ((rc = check_mat(a.w.gate_q, a.w.gate_s)) || (rc = check_mat(a.w.up_q, a.w.up_s)) ||
+             (rc = check_mat(a.w.down_q, a.w.down_s))) {
     return rc;
+  }
   if (shared_in_list(c) && ((rc = check_mat(a.w.sh_gate_q, a.w.sh_gate_s)) ||
                              (rc = check_mat(a.w.sh_up_q, a.w.sh_up_s)) ||
                              (rc = check_mat(a.w.sh_down_q, a.w.sh_down_s))))
@@ -203,8 +230,103 @@ int check_args(const moe_config_t& c, const moe_args_t& a) {
   return MOE_OK;
 }
 
+// The launch sequence with Q2_K routed experts: router logits (no activation
+// split), sub-block sums of x, selection, the Q2_K gate/up GEMM writing bf16 h
+// (and the bf16 shared expert's), sub-block sums of h, the down GEMMs and the
+// combine.
+int run_layer_q2k(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const Layout& L, hipStream_t stream) {
+  const int N = a.n_rows;
+  const int d = c.d_model, I = c.d_ff, E = c.n_experts, k = c.top_k;
+  float* z = (float*)(ws + L.z);
+  int32_t* idx = a.topk_idx ? a.topk_idx : (int32_t*)(ws + L.idx);
+  float* gates = a.topk_w ? a.topk_w : (float*)(ws + L.gates);
+  int32_t* counts = a.counts ? a.counts : (int32_t*)(ws + L.counts);
+  int32_t* offsets = a.offsets ? a.offsets : (int32_t*)(ws + L.offsets);
+  int32_t* perm = a.perm ? a.perm : (int32_t*)(ws + L.perm);
+  int32_t* inv = a.inv ? a.inv : (int32_t*)(ws + L.inv);
+  Group* groups = (Group*)(ws + L.groups);
+  int32_t* n_groups = (int32_t*)(ws + L.n_groups);
+  int32_t* hist = (int32_t*)(ws + L.hist);
+  int32_t* done = (int32_t*)(ws + L.done);
+  uint16_t* h = (uint16_t*)(ws + L.hq);
+  uint16_t* hsh = (uint16_t*)(ws + L.hsh);
+  uint32_t *xpair = (uint32_t*)(ws + L.xpair), *hpair = (uint32_t*)(ws + L.hpair);
+  float *xsum = (float*)(ws + L.xsum), *hsum = (float*)(ws + L.hsum);
+  float* y = (float*)(ws + L.y);
+  const int P = N * k;
+  auto mark = [&](int i) -> bool {
+    return !a.stage_events || !a.stage_events[i] ||
+           hipEventRecord((hipEvent_t)a.stage_events[i], stream) == hipSuccess;
+  };
+  if (!mark(0)) return MOE_ERR_HIP;
+  const int rows = q2k_unit_rows(P, E);
+  const int max_groups = max_work_groups(N, k, E, 0, rows);
+  const uint16_t* x = (const uint16_t*)a.x;
+  if (a.norm_w) {
+    uint16_t* xn = (uint16_t*)(ws + L.xn);
+    if (launch_rmsnorm(x, (const uint16_t*)a.norm_w, N, d, c.norm_eps, xn, stream) != hipSuccess) return MOE_ERR_HIP;
+    x = xn;
+  }
+  if (launch_prologue(x, a.router_w, N, d, E, z, nullptr, nullptr, done, false, stream) != hipSuccess ||
+      launch_q2k_sums(x, N, d, xpair, xsum, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (!mark(1)) return MOE_ERR_HIP;
+  if (launch_select_route(z, a.router_bias, c.bias_mode, d, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx,
+                          gates, 0, counts, offsets, perm, inv, rows, groups, n_groups, hist, done,
+                          stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  Q2kArgs ga;
+  memset(&ga, 0, sizeof(ga));
+  ga.w0 = (const uint8_t*)a.w.gate_q;
+  ga.w1 = (const uint8_t*)a.w.up_q;
+  ga.act = x;
+  ga.pairs = xpair;
+  ga.X = xsum;
+  ga.perm = perm;
+  ga.groups = groups;
+  ga.n_groups = n_groups;
+  ga.K = d;
+  ga.R = I;
+  ga.k = k;
+  ga.rows = rows;
+  ga.limit = c.swiglu_limit;
+  ga.h = h;
+  ga.pool = done + 1;
+  if (!mark(2)) return MOE_ERR_HIP;
+  if (launch_q2k_gateup(ga, max_groups, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (shared_bf16(c) &&
+      launch_shared_bf16_gateup(x, N, d, I, (const uint16_t*)a.w.sh_gate_w, (const uint16_t*)a.w.sh_up_w,
+                                c.swiglu_limit, hsh, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (!mark(3)) return MOE_ERR_HIP;
+  Q2kArgs da = ga;
+  da.w0 = (const uint8_t*)a.w.down_q;
+  da.w1 = nullptr;
+  da.act = h;
+  da.pairs = hpair;
+  da.X = hsum;
+  da.K = I;
+  da.R = d;
+  da.h = nullptr;
+  da.y = y;
+  da.pool = done + 2;
+  if (launch_q2k_sums(h, P, I, hpair, hsum, stream) != hipSuccess ||
+      launch_q2k_down(da, max_groups, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (shared_bf16(c) &&
+      launch_shared_bf16_down(hsh, N, d, I, (const uint16_t*)a.w.sh_down_w, y + (size_t)P * d, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (!mark(4)) return MOE_ERR_HIP;
+  if (launch_combine(y, inv, gates, N, d, k, P, c.has_shared, c.route_scale, (const uint16_t*)a.residual,
+                     (uint16_t*)a.out, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (!mark(5)) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 // The launch sequence of one layer call on workspace ws (laid out as L).
 int run_layer(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const Layout& L, hipStream_t stream) {
+  if (q2k(c)) return run_layer_q2k(c, a, ws, L, stream);
   const int N = a.n_rows;
   const int d = c.d_model, I = c.d_ff, E = c.n_experts, k = c.top_k;
   float* z = (float*)(ws + L.z);
@@ -349,6 +471,25 @@ int moe_pack_mxfp4(const void* q, const void* s, int32_t n_mat, int32_t rows, in
   hipError_t err = launch_pack_mxfp4((const uint8_t*)q, (const uint8_t*)s, n_mat, rows, K, (uint8_t*)q_out,
                                      (uint8_t*)s_out, (hipStream_t)stream);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_q2k_bytes(int32_t rows, int32_t K, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID;
+  if (rows < 16 || rows % 16 || K < 256 || K % 256) return MOE_ERR_UNSUPPORTED;
+  *bytes = q2k_matrix_bytes(rows, K);
+  return MOE_OK;
+}
+
+int moe_pack_q2k(const void* q, int32_t n_mat, int32_t rows, int32_t K, void* q_out, void* stream) {
+  if (n_mat < 0) return MOE_ERR_INVALID;
+  if (rows < 16 || rows % 16 || K < 256 || K % 256 || rows > 65536 || K > 65536) return MOE_ERR_UNSUPPORTED;
+  if (n_mat == 0) return MOE_OK;
+  if (!q || !q_out || !aligned(q, 4) || !aligned(q_out, 16)) return MOE_ERR_INVALID;
+  const size_t n = (size_t)n_mat * q2k_matrix_bytes(rows, K);
+  if (overlap(q, n, q_out, n)) return MOE_ERR_INVALID;
+  return launch_pack_q2k((const uint8_t*)q, n_mat, rows, K, (uint8_t*)q_out, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
 }
 
 int moe_workspace_size(const moe_config_t* cfg, int32_t n_rows, size_t* bytes) {

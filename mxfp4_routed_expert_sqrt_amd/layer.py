@@ -14,13 +14,14 @@ def _ptr(t):
 
 def make_config(shape: MoEShape, has_shared: bool = True, route_scale=None, swiglu_limit=None,
                 norm_eps: float = 1e-6, bias_mode: int = capi.MOE_BIAS_LOGIT,
-                shared_format: int = capi.MOE_SHARED_MXFP4) -> capi.MoeConfig:
+                shared_format: int = capi.MOE_SHARED_MXFP4,
+                expert_format: int = capi.MOE_EXPERTS_MXFP4) -> capi.MoeConfig:
     return capi.MoeConfig(shape.d_model, shape.d_ff, shape.n_experts, shape.top_k,
                           capi.MOE_ROUTING_TOPK if shape.routing == "topk" else capi.MOE_ROUTING_HASH,
                           1 if has_shared else 0,
                           float(shape.route_scale if route_scale is None else route_scale),
                           float(shape.swiglu_limit if swiglu_limit is None else swiglu_limit), float(norm_eps),
-                          int(bias_mode), int(shared_format))
+                          int(bias_mode), int(shared_format), int(expert_format))
 
 
 def pack_mxfp4(q: torch.Tensor, s: torch.Tensor, rows: int, K: int, stream=None, out=None):
@@ -41,6 +42,19 @@ def pack_mxfp4(q: torch.Tensor, s: torch.Tensor, rows: int, K: int, stream=None,
     if rc != capi.MOE_OK:
         raise capi.MoeError(rc)
     return q_out, s_out
+
+
+def pack_q2k(q: torch.Tensor, rows: int, K: int, stream=None, out=None) -> torch.Tensor:
+    """Natural-layout Q2_K device tensor q [n][rows][K/256*84] -> packed device tensor (same size)."""
+    n = q.shape[0]
+    nbytes = n * capi.moe_q2k_bytes(rows, K)
+    q_out = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if out is None else out
+    assert q_out.numel() == nbytes
+    st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    rc = capi.moe_pack_q2k(q.data_ptr(), n, rows, K, q_out.data_ptr(), st)
+    if rc != capi.MOE_OK:
+        raise capi.MoeError(rc)
+    return q_out
 
 
 _ALIGN = 2 << 20  # each packed region starts on a 2 MiB boundary inside one allocation
@@ -105,20 +119,55 @@ class PackedExperts:
                                _ptr(b.get("down")))
 
 
+class PackedQ2kExperts:
+    """Routed experts 0..E-1 in Q2_K, packed on the device (gate, up, down), one allocation."""
+
+    def __init__(self, experts_q2k: dict, shape: MoEShape, device):
+        E, d, I = shape.n_experts, shape.d_model, shape.d_ff
+        mats = (("gate", I, d), ("up", I, d), ("down", d, I))
+        sizes = {n: E * capi.moe_q2k_bytes(rows, K) for n, rows, K in mats}
+        offs, total = {}, 0
+        for n, _, _ in mats:
+            offs[n] = total
+            total += (sizes[n] + _ALIGN - 1) // _ALIGN * _ALIGN
+        self.buffer = torch.empty(total + _ALIGN, dtype=torch.uint8, device=device)
+        base = (-self.buffer.data_ptr()) % _ALIGN
+        self.t = {}
+        for n, rows, K in mats:
+            view = self.buffer[base + offs[n]:][:sizes[n]]
+            q = torch.from_numpy(np.ascontiguousarray(experts_q2k[n][:E])).to(device)
+            self.t[n] = pack_q2k(q, rows, K, out=view)
+            del q
+        torch.cuda.synchronize(device)
+
+    def weights(self, shared_bf16=None) -> capi.MoeWeights:
+        b = shared_bf16 or {}
+        t = self.t
+        return capi.MoeWeights(_ptr(t["gate"]), None, _ptr(t["up"]), None, _ptr(t["down"]), None,
+                               None, None, None, None, None, None,
+                               _ptr(b.get("gate")), _ptr(b.get("up")), _ptr(b.get("down")))
+
+
 class MoELayer:
     def __init__(self, shape: MoEShape, router_w, experts, device="cuda", router_bias=None,
                  has_shared: bool = True, route_scale=None, swiglu_limit=None, norm_w=None, norm_eps: float = 1e-6,
-                 bias_mode: int = capi.MOE_BIAS_LOGIT, shared_bf16=None):
+                 bias_mode: int = capi.MOE_BIAS_LOGIT, shared_bf16=None, experts_q2k=None):
         """experts: natural-layout arrays (dict, packed here) or an already packed PackedExperts.
         norm_w: optional bf16 bit patterns [d] of the input RMSNorm weight (the layer then normalises x).
         shared_bf16: optional dict of bf16 bit patterns gate/up [I][d], down [d][I]: the shared expert in
-        bf16 (MOE_SHARED_BF16) instead of the MXFP4 shared expert at index E of experts."""
+        bf16 (MOE_SHARED_BF16) instead of the MXFP4 shared expert at index E of experts.
+        experts_q2k: optional natural-layout Q2_K routed experts (dict gate/up/down, packed here) or a
+        PackedQ2kExperts (MOE_EXPERTS_Q2K); experts is then not used, and the shared expert, if any,
+        must be given in bf16."""
         self.shape = shape
         self.device = torch.device(device)
         fmt = capi.MOE_SHARED_MXFP4 if shared_bf16 is None else capi.MOE_SHARED_BF16
         if shared_bf16 is not None:
             has_shared = True
-        self.cfg = make_config(shape, has_shared, route_scale, swiglu_limit, norm_eps, bias_mode, fmt)
+        efmt = capi.MOE_EXPERTS_MXFP4 if experts_q2k is None else capi.MOE_EXPERTS_Q2K
+        if experts_q2k is not None and shared_bf16 is None and has_shared:
+            raise ValueError("Q2_K routed experts take a bf16 shared expert (shared_bf16) or none (has_shared=False)")
+        self.cfg = make_config(shape, has_shared, route_scale, swiglu_limit, norm_eps, bias_mode, fmt, efmt)
         self.shared_bf16 = None if shared_bf16 is None else {
             n: torch.from_numpy(np.ascontiguousarray(shared_bf16[n], dtype=np.uint16).view(np.int16)).to(self.device)
             for n in ("gate", "up", "down")}
@@ -128,7 +177,12 @@ class MoELayer:
         self.router_bias = None if router_bias is None else \
             torch.as_tensor(np.ascontiguousarray(router_bias, dtype=np.float32)).to(self.device)
         mx_shared = has_shared and shared_bf16 is None
-        if isinstance(experts, PackedExperts):
+        self.q2k = None
+        if experts_q2k is not None:
+            self.q2k = experts_q2k if isinstance(experts_q2k, PackedQ2kExperts) else \
+                PackedQ2kExperts(experts_q2k, shape, self.device)
+            self.experts = None
+        elif isinstance(experts, PackedExperts):
             if mx_shared and not experts.has_shared:
                 raise ValueError("packed experts carry no shared expert")
             self.experts = experts
@@ -147,6 +201,7 @@ class MoELayer:
         r = routing or {}
         return capi.MoeArgs(N, _ptr(x), _ptr(self.router_w), _ptr(self.router_bias), _ptr(token_ids), _ptr(tid2eid),
                             0 if tid2eid is None else tid2eid.shape[0],
+                            self.q2k.weights(self.shared_bf16) if self.q2k is not None else
                             self.experts.weights(self.has_shared, self.shared_bf16), _ptr(out),
                             _ptr(r.get("topk_idx")), _ptr(r.get("topk_w")), _ptr(r.get("counts")),
                             _ptr(r.get("offsets")), _ptr(r.get("perm")), _ptr(r.get("inv")), _ptr(workspace),

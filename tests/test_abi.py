@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert capi.moe_version() == 3
+    assert capi.moe_version() == 4
     for st in (0, -1, -2, -3, -4, -5):
         assert capi.moe_status_string(st) != "unknown status"
     assert capi.moe_status_string(7) == "unknown status"
@@ -72,7 +72,10 @@ def test_workspace_size_arithmetic():
     ("norm_eps", -1e-6, capi.MOE_ERR_INVALID), ("norm_eps", float("inf"), capi.MOE_ERR_INVALID),
     ("norm_eps", float("nan"), capi.MOE_ERR_INVALID), ("bias_mode", 2, capi.MOE_ERR_INVALID),
     ("bias_mode", -1, capi.MOE_ERR_INVALID), ("shared_format", 2, capi.MOE_ERR_INVALID),
-    ("shared_format", -1, capi.MOE_ERR_INVALID),
+    ("shared_format", -1, capi.MOE_ERR_INVALID), ("expert_format", 2, capi.MOE_ERR_INVALID),
+    ("expert_format", -1, capi.MOE_ERR_INVALID),
+    # Q2_K experts with the MXFP4 shared expert, or widths that are not whole super-blocks
+    ("expert_format", capi.MOE_EXPERTS_Q2K, capi.MOE_ERR_UNSUPPORTED),
 ])
 def test_bad_config_rejected(field, value, status):
     cfg = make_config(SHAPES["tiny"])
@@ -173,6 +176,55 @@ def test_every_written_buffer_is_disjoint_from_the_others():
     assert capi.moe_layer_forward(cfg, a, None) == capi.MOE_ERR_WORKSPACE
 
 
+Q2K_TINY = MoEShape("tiny_q2k", 32, 256, 16, 2, 256, "topk", "tiny_q2k")
+
+
+def test_q2k_config_and_sizes():
+    assert capi.moe_q2k_bytes(2048, 4096) == 2048 * 16 * 84
+    assert capi.moe_q2k_bytes(16, 256) == 16 * 84
+    for rows, K in ((24, 256), (16, 128), (16, 384 + 64)):
+        with pytest.raises(capi.MoeError):
+            capi.moe_q2k_bytes(rows, K)
+    ok = make_config(Q2K_TINY, shared_format=capi.MOE_SHARED_BF16, expert_format=capi.MOE_EXPERTS_Q2K)
+    assert capi.moe_workspace_size(ok, 32) > 0
+    assert capi.moe_workspace_size(make_config(Q2K_TINY, has_shared=False, expert_format=capi.MOE_EXPERTS_Q2K), 32) > 0
+    b = ctypes.c_size_t()
+    for shape, shared, fmt in ((SHAPES["tiny"], True, capi.MOE_SHARED_BF16),  # I = 128
+                               (Q2K_TINY, True, capi.MOE_SHARED_MXFP4),
+                               (MoEShape("q2k_d384", 32, 384, 16, 2, 256, "topk", "x"), False, 0)):
+        cfg = make_config(shape, has_shared=shared, shared_format=fmt, expert_format=capi.MOE_EXPERTS_Q2K)
+        assert capi.lib().moe_workspace_size(ctypes.byref(cfg), 32, ctypes.byref(b)) == capi.MOE_ERR_UNSUPPORTED
+
+
+def test_q2k_arguments_checked_before_any_hip_call():
+    cfg = make_config(Q2K_TINY, shared_format=capi.MOE_SHARED_BF16, expert_format=capi.MOE_EXPERTS_Q2K)
+    N = 32
+    # the scale pointers are not used: absent scales are fine (valid up to the workspace size)
+    a = _valid_args(cfg, N)
+    for n in ("gate_s", "up_s", "down_s", "sh_gate_q", "sh_gate_s", "sh_up_q", "sh_up_s", "sh_down_q", "sh_down_s"):
+        setattr(a.w, n, None)
+    a.workspace_bytes -= 1
+    assert capi.moe_layer_forward(cfg, a, None) == capi.MOE_ERR_WORKSPACE
+    for field, value in (("gate_q", None), ("up_q", 0x41000008), ("down_q", None)):
+        a = _valid_args(cfg, N); setattr(a.w, field, value)
+        assert capi.moe_layer_forward(cfg, a, None) == capi.MOE_ERR_INVALID, field
+    # a Q2_K weight set is E * rows * K/256 * 84 bytes: one byte short of the workspace is still an overlap
+    a = _valid_args(cfg, N)
+    a.w.down_q = a.workspace - 16 * 256 * 84 + 16
+    assert capi.moe_layer_forward(cfg, a, None) == capi.MOE_ERR_INVALID
+    a.w.down_q = a.workspace - 16 * 256 * 84
+    a.workspace_bytes -= 1
+    assert capi.moe_layer_forward(cfg, a, None) == capi.MOE_ERR_WORKSPACE
+    # the packing entry point
+    assert capi.moe_pack_q2k(None, 0, 16, 256, None, None) == capi.MOE_OK
+    assert capi.moe_pack_q2k(0x1000, 1, 16, 256, None, None) == capi.MOE_ERR_INVALID
+    assert capi.moe_pack_q2k(0x1002, 1, 16, 256, 0x9000, None) == capi.MOE_ERR_INVALID   # q not 4-aligned
+    assert capi.moe_pack_q2k(0x1000, 1, 16, 256, 0x9008, None) == capi.MOE_ERR_INVALID   # out not 16-aligned
+    assert capi.moe_pack_q2k(0x1000, 1, 16, 256, 0x1100, None) == capi.MOE_ERR_INVALID   # overlap
+    assert capi.moe_pack_q2k(0x1000, 1, 16, 200, 0x9000, None) == capi.MOE_ERR_UNSUPPORTED
+    assert capi.moe_pack_q2k(0x1000, -1, 16, 256, 0x9000, None) == capi.MOE_ERR_INVALID
+
+
 def test_zero_rows_is_a_no_op():
     cfg = make_config(SHAPES["tiny"])
     a = capi.MoeArgs()
@@ -206,7 +258,7 @@ def test_binding_structs_match_the_c_header(tmp_path):
     consts = ["MOE_OK", "MOE_ERR_INVALID", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
               "MOE_ROUTING_TOPK", "MOE_ROUTING_HASH", "MOE_BIAS_LOGIT", "MOE_BIAS_SELECT", "MOE_SHARED_MXFP4",
               "MOE_SHARED_BF16", "MOE_MAX_ROWS", "MOE_ERR_SCRATCH", "MOE_NOALLOC_SCRATCH_BYTES",
-              "MOE_N_STAGES", "MOE_N_STAGE_EVENTS", "MOE_MXFP4_VERSION"]
+              "MOE_N_STAGES", "MOE_N_STAGE_EVENTS", "MOE_MXFP4_VERSION", "MOE_EXPERTS_MXFP4", "MOE_EXPERTS_Q2K"]
     for c in consts:
         lines.append(f'  printf("const {c} %ld\\n", (long)({c}));')
     lines += ["  return 0;", "}"]

@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 
 from mxfp4_routed_expert_sqrt_amd import synth  # noqa: E402
 from mxfp4_routed_expert_sqrt_amd.configs import SHAPES, MoEShape  # noqa: E402
-from mxfp4_routed_expert_sqrt_amd.layer import MoELayer, PackedExperts  # noqa: E402
+from mxfp4_routed_expert_sqrt_amd.layer import MoELayer, PackedExperts, PackedQ2kExperts  # noqa: E402
 from tests.inputs import norm_workload, oracle_forward, selection_bias_workload, workload  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -325,6 +325,70 @@ def test_swiglu_limit_binds():
     assert np.abs(ref["out"] - ref_unclamped["out"]).max() > 0.1 * np.sqrt(np.mean(ref["out"] ** 2))
     check_routing(gpu, ref, "clamp")
     check_out(gpu["out"], ref["out"], "clamp")
+
+
+# ------------------------------------------------------- Q2_K routed experts
+
+Q2K = {
+    "tiny": MoEShape("q2k_tiny", 32, 256, 16, 2, 256, "topk", "tiny_q2k"),
+    # 16-row groups, two super-blocks along d, one along I (the odd count of the double buffer)
+    "ragged": MoEShape("q2k_ragged", 37, 512, 16, 2, 256, "topk", "q2k_a"),
+    # >= 1024 routed pairs, < 32 per expert: 32-row groups; Zipf-biased load (several groups per hot expert)
+    "medium": MoEShape("q2k_medium", 300, 512, 64, 4, 512, "topk", "q2k_b", bias="zipf"),
+    # >= 32 routed rows per expert: 64-row groups, ragged
+    "tall": MoEShape("q2k_tall", 611, 512, 8, 4, 256, "topk", "q2k_c"),
+}
+
+_PACKED_Q2K = {}
+
+
+def q2k_experts(shape):
+    key = (shape.weight_set, shape.n_experts, shape.d_model, shape.d_ff)
+    if key not in _PACKED_Q2K:
+        ex = synth.gen_experts_q2k(shape)
+        _PACKED_Q2K[key] = (ex, PackedQ2kExperts(ex, shape, torch.device("cuda")))
+    return _PACKED_Q2K[key]
+
+
+def run_q2k(wl, shared, **kw):
+    ex, packed = q2k_experts(wl["shape"])
+    b = synth.gen_shared_bf16(wl["shape"]) if shared else None
+    gpu, *_ = run_gpu(wl, has_shared=shared, shared_bf16=b, experts_q2k=packed, **kw)
+    return gpu, ex, b
+
+
+@pytest.mark.parametrize("shared", [True, False])
+@pytest.mark.parametrize("name", sorted(Q2K))
+def test_q2k_experts(name, shared):
+    # the routed experts in Q2_K (bf16 MFMA on 128 + scale*q, the min term and the +128 folded per
+    # super-block), with the bf16 shared expert or none, every row against the oracle
+    wl = workload(Q2K[name])
+    gpu, ex, b = run_q2k(wl, shared)
+    ref = oracle_forward(wl, experts_q2k=ex, shared_bf16=b, with_shared=shared)
+    label = f"{wl['shape'].name}+q2k{'+bf16shared' if shared else ''}"
+    check_routing(gpu, ref, label)
+    check_out(gpu["out"], ref["out"], label)
+
+
+def test_q2k_experts_with_norm_and_clamp():
+    # input RMSNorm and residual around the Q2_K layer; a small swiglu limit makes the clamp bind
+    wl = norm_workload(Q2K["tiny"])
+    gpu, ex, b = run_q2k(wl, True, swiglu_limit=0.05)
+    ref = oracle_forward(wl, experts_q2k=ex, shared_bf16=b, swiglu_limit=0.05)
+    check_routing(gpu, ref, "q2k+norm+clamp", gate_rtol=GATE_RTOL_NORM)
+    check_out(gpu["out"], ref["out"], "q2k+norm+clamp")
+
+
+@pytest.mark.parametrize("name,cover", [("decode8", False), ("draft448", False), ("verify512", False),
+                                        ("prefill8192", True)])
+def test_q2k_experts_full_size(name, cover):
+    # the drafter's configuration at the layer's full size: Q2_K routed experts, bf16 shared expert
+    wl = workload(name)
+    gpu, ex, b = run_q2k(wl, True)
+    rows = compared_rows(gpu, wl, cover)
+    ref = oracle_forward(wl, rows=rows, experts_q2k=ex, shared_bf16=b)
+    check_routing(gpu, ref, name + "+q2k")
+    check_out(gpu["out"] if rows is None else gpu["out"][rows], ref["out"], name + "+q2k")
 
 
 def test_zero_rows_enqueue_nothing():
