@@ -13,9 +13,12 @@
 //     X  = sum_t x[r][t],   xh + xl = the sum of x over sub-block m (bf16 hi/lo)
 // 128 + sc * q (at most 173) is an integer, so it is exact in bf16, and it is
 // built by byte shuffles alone (a byte p under the high byte 0x43 is the bf16
-// number 128 + p); bf16 x times an integer is exact in fp32.  What rounds:
-// the fp32 sums, xh + xl (16 bits of each sub-block sum) and the fold; h is
-// rounded once to bf16 for the down GEMM.
+// number 128 + p); bf16 x times an integer is exact in fp32.  The down GEMM
+// runs the same way on fp16 (1024 + sc * q: high byte 0x64) when h is kept in
+// fp16: with the swiglu clamp at 0 < L <= 255, |h| <= L^2 < 65504, and fp16
+// carries 3 more bits of h than bf16; without such a clamp h stays bf16.
+// What rounds: the fp32 sums, xh + xl (16 or 22 bits of each sub-block sum),
+// the fold, and h, once, to fp16 or bf16.
 //
 // A workgroup = one work unit = (group of <= 16*NB rows of one expert, a
 // block of output features).  Each wave owns TPM 16-row weight tiles (of gate
@@ -31,6 +34,7 @@
 namespace moe {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -73,9 +77,18 @@ hipError_t launch_pack_q2k(const uint8_t* q, int n_mat, int rows, int K, uint8_t
 }
 
 // One thread per (row, 16-value sub-block): the fp32 sum in ascending order,
-// stored as bf16 hi (truncated) | bf16 lo (rest, nearest even) << 16; the 16
+// stored as hi | lo << 16 in the activations' type: bf16 hi (truncated) and lo
+// (the rest, nearest even), or fp16 hi and lo (both nearest even); the 16
 // sub-blocks of a super-block are 16 consecutive lanes, whose butterfly sum
 // (a fixed order) is X.
+__device__ __forceinline__ float qk_lo_value(uint32_t v, bool f16) {
+  return f16 ? (float)__builtin_bit_cast(f16x2, v)[0] : __uint_as_float(v << 16);
+}
+__device__ __forceinline__ float qk_hi_value(uint32_t v, bool f16) {
+  return f16 ? (float)__builtin_bit_cast(f16x2, v)[1] : __uint_as_float(v & 0xffff0000u);
+}
+
+template <bool F16>
 __global__ void q2k_sums_kernel(const uint16_t* __restrict__ act, size_t total, uint32_t* __restrict__ pairs,
                                 float* __restrict__ X) {
   const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -85,13 +98,13 @@ __global__ void q2k_sums_kernel(const uint16_t* __restrict__ act, size_t total, 
     const u32x4 v0 = *(const u32x4*)src, v1 = *(const u32x4*)(src + 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s += __uint_as_float(v0[i] << 16);
-      s += __uint_as_float(v0[i] & 0xffff0000u);
+      s += qk_lo_value(v0[i], F16);
+      s += qk_hi_value(v0[i], F16);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s += __uint_as_float(v1[i] << 16);
-      s += __uint_as_float(v1[i] & 0xffff0000u);
+      s += qk_lo_value(v1[i], F16);
+      s += qk_hi_value(v1[i], F16);
     }
   }
   float x = s;
@@ -100,17 +113,26 @@ __global__ void q2k_sums_kernel(const uint16_t* __restrict__ act, size_t total, 
   x += __shfl_xor(x, 4, kWave);
   x += __shfl_xor(x, 8, kWave);
   if (t < total) {
-    const uint32_t hi = __float_as_uint(s) & 0xffff0000u;
-    pairs[t] = (hi >> 16) | ((uint32_t)f32_to_bf16_rne(s - __uint_as_float(hi)) << 16);
+    if constexpr (F16) {
+      const _Float16 hi = (_Float16)s, lo = (_Float16)(s - (float)hi);
+      pairs[t] = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+    } else {
+      const uint32_t hi = __float_as_uint(s) & 0xffff0000u;
+      pairs[t] = (hi >> 16) | ((uint32_t)f32_to_bf16_rne(s - __uint_as_float(hi)) << 16);
+    }
     if ((t & 15) == 0) X[t >> 4] = x;
   }
 }
 
-hipError_t launch_q2k_sums(const uint16_t* act, int rows, int K, uint32_t* pairs, float* X, hipStream_t stream) {
+hipError_t launch_q2k_sums(const uint16_t* act, int rows, int K, bool f16, uint32_t* pairs, float* X,
+                           hipStream_t stream) {
   const size_t total = (size_t)rows * (K / 16);  // a multiple of 16: whole super-blocks per lane group
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(q2k_sums_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, act, total,
-                     pairs, X);
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (f16)
+    hipLaunchKernelGGL(q2k_sums_kernel<true>, grid, dim3(256), 0, stream, act, total, pairs, X);
+  else
+    hipLaunchKernelGGL(q2k_sums_kernel<false>, grid, dim3(256), 0, stream, act, total, pairs, X);
   return hipGetLastError();
 }
 
@@ -192,18 +214,46 @@ __device__ __forceinline__ void qk_load_w(QkW<NA>& f, const qk_gptr (&w)[NA], in
   }
 }
 
-// bf16 pairs 128 + byte: bytes 0,1 (LO) or 2,3 of p under the high byte 0x43.
-__device__ __forceinline__ uint32_t qk_pair_lo(uint32_t p) { return 0x43004300u | (p & 0xffu) | ((p & 0xff00u) << 8); }
-__device__ __forceinline__ uint32_t qk_pair_hi(uint32_t p) {
-  return 0x43004300u | ((p >> 16) & 0xffu) | ((p >> 8) & 0xff0000u);
+// The MFMA input type: bf16 (magic high byte 0x43: 128 + byte) or fp16
+// (0x64: 1024 + byte).
+template <bool F16>
+struct QkType {
+  typedef v8bf vec;
+  static constexpr uint32_t kMagic = 0x43004300u;
+  static constexpr float kBase = 128.f;
+  static __device__ __forceinline__ v4f mfma(const vec& a, const vec& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t small_int_bits(uint32_t n) { return __float_as_uint((float)n) >> 16; }
+};
+template <>
+struct QkType<true> {
+  typedef v8h vec;
+  static constexpr uint32_t kMagic = 0x64006400u;
+  static constexpr float kBase = 1024.f;
+  static __device__ __forceinline__ v4f mfma(const vec& a, const vec& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t small_int_bits(uint32_t n) {
+    return __builtin_bit_cast(uint16_t, (_Float16)(float)n);
+  }
+};
+
+// Pairs base + byte: bytes 0,1 (lo) or 2,3 (hi) of p under the magic high byte.
+__device__ __forceinline__ uint32_t qk_pair_lo(uint32_t p, uint32_t magic) {
+  return magic | (p & 0xffu) | ((p & 0xff00u) << 8);
+}
+__device__ __forceinline__ uint32_t qk_pair_hi(uint32_t p, uint32_t magic) {
+  return magic | ((p >> 16) & 0xffu) | ((p >> 8) & 0xff0000u);
 }
 
 // B fragment of k-step S (values 32S + 8g .. +7 of the super-block) as the
 // bf16 numbers 128 + sc*q.  Those values sit in half S/4 at bits 2*(S%4) of
 // the lane's 8 quant bytes of that half, in sub-block 2S + g/2, whose scale is
 // nibble 0 of scale byte 2S + g/2 (gsh = 8*(g/2)).
-template <int S>
-__device__ __forceinline__ v8bf qk_frag(const u32x4& qs, const u32x4& sc, uint32_t gsh) {
+template <int S, bool F16>
+__device__ __forceinline__ typename QkType<F16>::vec qk_frag(const u32x4& qs, const u32x4& sc, uint32_t gsh) {
+  constexpr uint32_t M = QkType<F16>::kMagic;
   constexpr int H = S >> 2, J = S & 3;
   const uint32_t scv = (sc[S >> 1] >> (16 * (S & 1) + gsh)) & 15u;
   const u16x2 m = {(unsigned short)scv, (unsigned short)scv};
@@ -211,39 +261,42 @@ __device__ __forceinline__ v8bf qk_frag(const u32x4& qs, const u32x4& sc, uint32
   // sc * q per byte (at most 45, so the two bytes of a 16-bit lane never carry)
   const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, q0) * m);
   const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, q1) * m);
-  const u32x4 r = {qk_pair_lo(p0), qk_pair_hi(p0), qk_pair_lo(p1), qk_pair_hi(p1)};
-  return __builtin_bit_cast(v8bf, r);
+  const u32x4 r = {qk_pair_lo(p0, M), qk_pair_hi(p0, M), qk_pair_lo(p1, M), qk_pair_hi(p1, M)};
+  return __builtin_bit_cast(typename QkType<F16>::vec, r);
 }
 
 // B fragment of the min k-step: k = 2m + t (t = 0 hi, 1 lo) holds mn[m] of
-// sub-blocks m = 4g..4g+3 (high nibbles of scale dword g), as exact bf16.
-__device__ __forceinline__ v8bf qk_min_frag(const u32x4& sc, int g) {
+// sub-blocks m = 4g..4g+3 (high nibbles of scale dword g), exact.
+template <bool F16>
+__device__ __forceinline__ typename QkType<F16>::vec qk_min_frag(const u32x4& sc, int g) {
   const uint32_t sg = g == 0 ? sc[0] : (g == 1 ? sc[1] : (g == 2 ? sc[2] : sc[3]));
   u32x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t b = __float_as_uint((float)((sg >> (8 * i + 4)) & 15u)) >> 16;
+    const uint32_t b = QkType<F16>::small_int_bits((sg >> (8 * i + 4)) & 15u);
     r[i] = b | (b << 16);
   }
-  return __builtin_bit_cast(v8bf, r);
+  return __builtin_bit_cast(typename QkType<F16>::vec, r);
 }
 
 // One super-block: T1 over 8 k-steps, the fold d * (T1 - 128 X), then T2 and
 // the fold - dmin * T2, into acc[tile][row block].
-template <int NA, int NB>
+template <int NA, int NB, bool F16>
 __device__ __forceinline__ void qk_superblock(const QkW<NA>& f, const uint8_t* buf, v4f (&acc)[NA][NB]) {
+  typedef QkType<F16> T;
+  typedef typename T::vec vec;
   const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
   const uint32_t gsh = 8 * (g >> 1);
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   v4f t[NA][NB];
 #define QK_STEP(S)                                                                                    \
   {                                                                                                   \
-    v8bf bw[NA];                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < NA; ++i) bw[i] = qk_frag<S>(f.qs[i], f.sc[i], gsh);         \
+    vec bw[NA];                                                                                       \
+    _Pragma("unroll") for (int i = 0; i < NA; ++i) bw[i] = qk_frag<S, F16>(f.qs[i], f.sc[i], gsh);    \
     _Pragma("unroll") for (int tt = 0; tt < NB; ++tt) {                                               \
-      const v8bf av = *(const v8bf*)(buf + (16 * tt + col) * kQkXStride + 64 * (S) + 16 * g);         \
+      const vec av = *(const vec*)(buf + (16 * tt + col) * kQkXStride + 64 * (S) + 16 * g);           \
       _Pragma("unroll") for (int i = 0; i < NA; ++i) t[i][tt] =                                       \
-          __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[i], (S) == 0 ? zero : t[i][tt], 0, 0, 0);    \
+          T::mfma(av, bw[i], (S) == 0 ? zero : t[i][tt]);                                             \
     }                                                                                                 \
   }
   QK_STEP(0)
@@ -267,18 +320,18 @@ __device__ __forceinline__ void qk_superblock(const QkW<NA>& f, const uint8_t* b
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[i][tt][e] = fmaf(dv, fmaf(-128.f, xv[tt][e], t[i][tt][e]), acc[i][tt][e]);
+      for (int e = 0; e < 4; ++e) acc[i][tt][e] = fmaf(dv, fmaf(-T::kBase, xv[tt][e], t[i][tt][e]), acc[i][tt][e]);
   }
-  v8bf pv[NB];
+  vec pv[NB];
 #pragma unroll
   for (int tt = 0; tt < NB; ++tt)
-    pv[tt] = *(const v8bf*)(buf + QkBuf<NB>::kPairs + (16 * tt + col) * kQkPStride + 16 * g);
+    pv[tt] = *(const vec*)(buf + QkBuf<NB>::kPairs + (16 * tt + col) * kQkPStride + 16 * g);
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const v8bf bm = qk_min_frag(f.sc[i], g);
+    const vec bm = qk_min_frag<F16>(f.sc[i], g);
 #pragma unroll
     for (int tt = 0; tt < NB; ++tt) {
-      const v4f t2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pv[tt], bm, zero, 0, 0, 0);
+      const v4f t2 = T::mfma(pv[tt], bm, zero);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][tt][e] = fmaf(-dmin[i], t2[e], acc[i][tt][e]);
     }
@@ -286,8 +339,9 @@ __device__ __forceinline__ void qk_superblock(const QkW<NA>& f, const uint8_t* b
 }
 
 // One work unit: output features [fu0, fu0 + WAVES*16*TPM) of group g; GU:
-// gate and up, written as h; else down, written as y.
-template <int TPM, int WAVES, int NB, bool GU>
+// gate and up, written as h (fp16 when a.h_f16, else bf16); else down, on
+// fp16 (F16) or bf16 activations h, written as y.
+template <int TPM, int WAVES, int NB, bool GU, bool F16>
 __device__ __forceinline__ void qk_unit(const Q2kArgs& a, const Group g, int fu0, uint8_t* lds) {
   constexpr int NA = GU ? 2 * TPM : TPM, kThreads = 64 * WAVES, kRows = 16 * NB;
   constexpr int kBuf = QkBuf<NB>::kBytes;
@@ -327,7 +381,7 @@ __device__ __forceinline__ void qk_unit(const Q2kArgs& a, const Group g, int fu0
   __syncthreads();
   for (int b = 0; b < nb; b += 2) {
     if (b + 1 < nb) qk_load_w(fb, w, b + 1);
-    qk_superblock(fa, lds, acc);
+    qk_superblock<NA, NB, F16>(fa, lds, acc);
     if (b + 1 < nb) {
       st.store(lds + kBuf);
       if (b + 2 < nb) st.load(a, b + 2);
@@ -335,7 +389,7 @@ __device__ __forceinline__ void qk_unit(const Q2kArgs& a, const Group g, int fu0
     __syncthreads();
     if (b + 1 >= nb) break;
     if (b + 2 < nb) qk_load_w(fa, w, b + 2);
-    qk_superblock(fb, lds + kBuf, acc);
+    qk_superblock<NA, NB, F16>(fb, lds + kBuf, acc);
     if (b + 2 < nb) {
       st.store(lds);
       if (b + 3 < nb) st.load(a, b + 3);
@@ -359,7 +413,8 @@ __device__ __forceinline__ void qk_unit(const Q2kArgs& a, const Group g, int fu0
             gv = fminf(gv, L);
             uv = fminf(fmaxf(uv, -L), L);
           }
-          a.h[o] = f32_to_bf16_rne(gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv);
+          const float hv = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
+          a.h[o] = a.h_f16 ? __builtin_bit_cast(uint16_t, (_Float16)hv) : f32_to_bf16_rne(hv);
         } else {
           a.y[o] = acc[i][tt][e];
         }
@@ -367,7 +422,7 @@ __device__ __forceinline__ void qk_unit(const Q2kArgs& a, const Group g, int fu0
 }
 
 // Units dealt by xcd_unit_claim; tall units feature-block-major (unit_group).
-template <int TPM, int WAVES, int NB, bool GU>
+template <int TPM, int WAVES, int NB, bool GU, bool F16>
 __global__ void __launch_bounds__(64 * WAVES) q2k_kernel(Q2kArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * TPM;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * QkBuf<NB>::kBytes
@@ -377,24 +432,26 @@ __global__ void __launch_bounds__(64 * WAVES) q2k_kernel(Q2kArgs a) {
   if (half_idx < 0) return;
   int fb;
   const Group g = unit_group<NB == 4>(a.groups, half_idx >> 1, n_fb, &fb);
-  qk_unit<TPM, WAVES, NB, GU>(a, g, fb * kFeatUnit, lds);
+  qk_unit<TPM, WAVES, NB, GU, F16>(a, g, fb * kFeatUnit, lds);
 }
 
-template <int TPM, int WAVES, int NB, bool GU>
+template <int TPM, int WAVES, int NB, bool GU, bool F16 = false>
 static hipError_t q2k_launch(const Q2kArgs& a, int max_groups, hipStream_t stream) {
   static std::atomic<uint64_t> attr{0};
   constexpr int kFeatUnit = WAVES * 16 * TPM;
   if (a.R % kFeatUnit || a.K % 256) return hipErrorInvalidValue;
   const size_t lds = 2 * (size_t)QkBuf<NB>::kBytes;
-  hipError_t err = ensure_dynamic_lds(q2k_kernel<TPM, WAVES, NB, GU>, lds, attr);
+  hipError_t err = ensure_dynamic_lds(q2k_kernel<TPM, WAVES, NB, GU, F16>, lds, attr);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((q2k_kernel<TPM, WAVES, NB, GU>), dim3(unit_grid(max_groups, a.R / kFeatUnit)),
+  hipLaunchKernelGGL((q2k_kernel<TPM, WAVES, NB, GU, F16>), dim3(unit_grid(max_groups, a.R / kFeatUnit)),
                      dim3(64 * WAVES), lds, stream, a);
   return hipGetLastError();
 }
 
-// Units of 256 output features (8 waves x 2 tiles) on 32- and 64-row groups;
-// 16-row groups (small batches) take 128 (8 waves x 1 tile) for more units.
+// Units of 256 output features (8 waves x 2 tiles) on 32-row groups and on
+// 64-row groups of down; 64-row gate/up units and 16-row groups (small
+// batches) take 128 (8 waves x 1 tile): the former to stay within 256
+// registers, the latter for more units.
 hipError_t launch_q2k_gateup(const Q2kArgs& a, int max_groups, hipStream_t stream) {
   if (a.rows == kTallGroupRows) return q2k_launch<1, 8, 4, true>(a, max_groups, stream);
   if (a.rows == kMediumGroupRows) return q2k_launch<2, 8, 2, true>(a, max_groups, stream);
@@ -402,6 +459,11 @@ hipError_t launch_q2k_gateup(const Q2kArgs& a, int max_groups, hipStream_t strea
 }
 
 hipError_t launch_q2k_down(const Q2kArgs& a, int max_groups, hipStream_t stream) {
+  if (a.h_f16) {
+    if (a.rows == kTallGroupRows) return q2k_launch<2, 8, 4, false, true>(a, max_groups, stream);
+    if (a.rows == kMediumGroupRows) return q2k_launch<2, 8, 2, false, true>(a, max_groups, stream);
+    return q2k_launch<1, 8, 1, false, true>(a, max_groups, stream);
+  }
   if (a.rows == kTallGroupRows) return q2k_launch<2, 8, 4, false>(a, max_groups, stream);
   if (a.rows == kMediumGroupRows) return q2k_launch<2, 8, 2, false>(a, max_groups, stream);
   return q2k_launch<1, 8, 1, false>(a, max_groups, stream);

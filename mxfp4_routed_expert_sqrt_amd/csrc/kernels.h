@@ -143,9 +143,9 @@ hipError_t launch_combine(const float* y, const int32_t* inv, const float* gates
                           int P, int has_shared, float route_scale, const uint16_t* residual, uint16_t* out,
                           hipStream_t stream);
 
-// Shared expert with bf16 weights: h = silu(min(Wg x, L)) * clamp(Wu x) as bf16
-// [N][I]; y_sh [N][d] = Wd h in fp32 (the shared rows of y).  d and I
-// multiples of 64.
+// Shared expert with bf16 weights: h = silu(min(Wg x, L)) * clamp(Wu x) as two
+// bf16 planes hi, lo [2][N][I] (h = hi + lo); y_sh [N][d] = Wd h in fp32 (the
+// shared rows of y).  d and I multiples of 64.
 hipError_t launch_shared_bf16_gateup(const uint16_t* x, int n_rows, int d, int I, const uint16_t* wg,
                                      const uint16_t* wu, float limit, uint16_t* h, hipStream_t stream);
 hipError_t launch_shared_bf16_down(const uint16_t* h, int n_rows, int d, int I, const uint16_t* wd, float* y_sh,
@@ -162,9 +162,11 @@ __host__ __device__ inline size_t q2k_matrix_bytes(int rows, int K) {
 
 hipError_t launch_pack_q2k(const uint8_t* q, int n_mat, int rows, int K, uint8_t* out, hipStream_t stream);
 
-// Per activation row of length K: pairs [rows][K/256][16] (bf16 hi | lo << 16
-// of each 16-value sub-block sum) and X [rows][K/256] (fp32 super-block sums).
-hipError_t launch_q2k_sums(const uint16_t* act, int rows, int K, uint32_t* pairs, float* X, hipStream_t stream);
+// Per activation row of length K (bf16, or fp16 when f16): pairs
+// [rows][K/256][16] (hi | lo << 16 in the same type, of each 16-value
+// sub-block sum) and X [rows][K/256] (fp32 super-block sums).
+hipError_t launch_q2k_sums(const uint16_t* act, int rows, int K, bool f16, uint32_t* pairs, float* X,
+                           hipStream_t stream);
 
 struct Q2kArgs {
   const uint8_t *w0, *w1;  // packed Q2_K experts: gate and up (gate/up), or down (w0)
@@ -176,7 +178,8 @@ struct Q2kArgs {
   const int32_t* n_groups;
   int K, R, k, rows;       // contraction, output width, top-k, rows of the work list's groups
   float limit;             // swiglu limit (<= 0: none)
-  uint16_t* h;             // gate/up output: bf16 [P][R]
+  uint16_t* h;             // gate/up output: [P][R], fp16 when h_f16, else bf16
+  int h_f16;               // h in fp16 (gate/up writes it, down reads it); needs |h| < 65504
   float* y;                // down output: fp32 [P][R]
   int32_t* pool;           // claim counter (zeroed before the launch)
 };

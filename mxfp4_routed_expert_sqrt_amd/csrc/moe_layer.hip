@@ -92,7 +92,7 @@ Layout make_layout(const moe_config_t& c, int n) {
   L.xsum = take(qk ? N * (size_t)(c.d_model / 256) * 4 : 0);
   L.hpair = take(qk ? P * (size_t)(c.d_ff / 16) * 4 : 0);
   L.hsum = take(qk ? P * (size_t)(c.d_ff / 256) * 4 : 0);
-  L.hsh = take(shared_bf16(c) ? N * (size_t)c.d_ff * 2 : 0);  // bf16 h of a bf16 shared expert
+  L.hsh = take(shared_bf16(c) ? 2 * N * (size_t)c.d_ff * 2 : 0);  // two-term bf16 h of a bf16 shared expert
   L.y = take(Ptot * (size_t)c.d_model * 4);
   L.total = off;
   return L;
@@ -231,9 +231,9 @@ int check_args(const moe_config_t& c, const moe_args_t& a) {
 }
 
 // The launch sequence with Q2_K routed experts: router logits (no activation
-// split), sub-block sums of x, selection, the Q2_K gate/up GEMM writing bf16 h
-// (and the bf16 shared expert's), sub-block sums of h, the down GEMMs and the
-// combine.
+// split), sub-block sums of x, selection, the Q2_K gate/up GEMM writing h
+// (fp16 under a swiglu clamp of at most 255, else bf16) and the bf16 shared
+// expert's, sub-block sums of h, the down GEMMs and the combine.
 int run_layer_q2k(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const Layout& L, hipStream_t stream) {
   const int N = a.n_rows;
   const int d = c.d_model, I = c.d_ff, E = c.n_experts, k = c.top_k;
@@ -268,7 +268,7 @@ int run_layer_q2k(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const
     x = xn;
   }
   if (launch_prologue(x, a.router_w, N, d, E, z, nullptr, nullptr, done, false, stream) != hipSuccess ||
-      launch_q2k_sums(x, N, d, xpair, xsum, stream) != hipSuccess)
+      launch_q2k_sums(x, N, d, false, xpair, xsum, stream) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
   if (launch_select_route(z, a.router_bias, c.bias_mode, d, N, E, k, c.routing, a.token_ids, a.tid2eid, a.vocab, idx,
@@ -291,6 +291,8 @@ int run_layer_q2k(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const
   ga.rows = rows;
   ga.limit = c.swiglu_limit;
   ga.h = h;
+  // h in fp16 (3 more bits than bf16) when the swiglu clamp bounds it: |h| <= L^2 < 65504
+  ga.h_f16 = c.swiglu_limit > 0.f && c.swiglu_limit <= 255.f;
   ga.pool = done + 1;
   if (!mark(2)) return MOE_ERR_HIP;
   if (launch_q2k_gateup(ga, max_groups, stream) != hipSuccess) return MOE_ERR_HIP;
@@ -310,7 +312,7 @@ int run_layer_q2k(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const
   da.h = nullptr;
   da.y = y;
   da.pool = done + 2;
-  if (launch_q2k_sums(h, P, I, hpair, hsum, stream) != hipSuccess ||
+  if (launch_q2k_sums(h, P, I, ga.h_f16 != 0, hpair, hsum, stream) != hipSuccess ||
       launch_q2k_down(da, max_groups, stream) != hipSuccess)
     return MOE_ERR_HIP;
   if (shared_bf16(c) &&
