@@ -22,7 +22,9 @@ Prints one JSON line.  Besides the contract fields it carries
   router weight, x, out) over ms_per_step;
 - workloads: the same measurement on the other layer configurations (8-row
   decode with four weight copies rotated, 8192-row prefill with its FP4-MFMA
-  fraction, Zipf-skewed and hash-routed 2048-row batches);
+  fraction, Zipf-skewed and hash-routed 2048-row batches) and on the drafter's
+  expert format (Q2_K routed experts with a bf16 shared expert) at the
+  448-row draft slab and the 512-row verify batch;
 - cpu_baseline: the fp64 CPU oracle on a bounded sample of the headline
   workload on this host (all host cores, and one core on 8 rows).
 """
@@ -39,8 +41,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP4_PEAK_TFLOPS = 10100.0  # dense MXFP4 MFMA, MI355X
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16/fp16 MFMA, MI355X (the Q2_K GEMMs)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_verify512_traffic.txt")
-EXTRA_WORKLOADS = ("decode8", "prefill8192", "zipf2048", "hash2048")
+EXTRA_WORKLOADS = ("decode8", "prefill8192", "zipf2048", "hash2048", "q2k_draft448", "q2k_verify512")
+Q2K_PREFIX = "q2k_"  # routed experts in Q2_K, shared expert in bf16, on the named shape
 DECODE_WEIGHT_COPIES = 4  # 8-row batches touch ~0.6 GB of weights: rotate copies past the 256 MB MALL
 
 
@@ -146,7 +150,11 @@ def mxfp4_matrix_bytes(rows, K):
     return rows * K // 2 + rows * K // 32  # E2M1 nibbles + one E8M0 byte per 32 values
 
 
-def algorithmic(shape, touched_routed, shared_bf16=False, has_bias=False):
+def q2k_matrix_bytes(rows, K):
+    return rows * (K // 256) * 84  # one 84-byte super-block per 256 values
+
+
+def algorithmic(shape, touched_routed, shared_bf16=False, has_bias=False, q2k=False):
     """Algorithmic HBM bytes and FP4-equivalent flops of the layer and its two GEMMs.
 
     Bytes: weights of every touched expert (an expert with no rows reads none) + router weight + x + out
@@ -155,7 +163,7 @@ def algorithmic(shape, touched_routed, shared_bf16=False, has_bias=False):
     weights (6*d*I per (row, expert): gate, up, down), whatever the activation format.
     """
     N, d, I, E, k = shape.n_rows, shape.d_model, shape.d_ff, shape.n_experts, shape.top_k
-    m = mxfp4_matrix_bytes(I, d)  # gate, up [I][d] and down [d][I] have the same size
+    m = (q2k_matrix_bytes if q2k else mxfp4_matrix_bytes)(I, d)  # gate, up [I][d] and down [d][I]: same size
     sh_mat = I * d * 2 if shared_bf16 else m
     x_bytes = out_bytes = N * d * 2
     extra = (E * 4 if has_bias else 0) + ((N * 4 + N * k * 4) if shape.routing == "hash" else 0)
@@ -228,11 +236,14 @@ class Runner:
                 "stages_us": {n: float(np.mean(stage_ms[:, s])) * 1e3 for s, n in enumerate(capi.STAGE_NAMES)}}
 
 
-def summarise(shape, timing, touched_routed, shared_bf16=False, has_bias=False):
-    a = algorithmic(shape, touched_routed, shared_bf16, has_bias)
+def summarise(shape, timing, touched_routed, shared_bf16=False, has_bias=False, q2k=False):
+    """Rates and roofline fractions; the MFMA fraction is against the FP4 peak (MXFP4 experts) or the bf16
+    peak (Q2_K experts, whose GEMMs run on bf16/fp16 MFMA), under the key fp4_frac or bf16_frac."""
+    a = algorithmic(shape, touched_routed, shared_bf16, has_bias, q2k)
     t = timing["ms_per_step"] * 1e-3
     gu, dn = timing["stages_us"]["gateup"] * 1e-6, timing["stages_us"]["down"] * 1e-6
     r = lambda v: round(v, 4)
+    peak, fk = (BF16_PEAK_TFLOPS, "bf16_frac") if q2k else (FP4_PEAK_TFLOPS, "fp4_frac")
     return {
         "rows": shape.n_rows,
         "rows_per_s": shape.n_rows / t,
@@ -240,13 +251,13 @@ def summarise(shape, timing, touched_routed, shared_bf16=False, has_bias=False):
         "gpu_event_us_per_step": timing["gpu_ms_per_step"] * 1e3,
         "touched_experts": touched_routed + 1,
         "layer": {"algorithmic_bytes": a["layer_bytes"], "hbm_frac": r(a["layer_bytes"] / t / 1e9 / HBM_PEAK_GBS),
-                  "fp4_flops": a["layer_flops"], "fp4_frac": r(a["layer_flops"] / t / 1e12 / FP4_PEAK_TFLOPS)},
+                  "flops": a["layer_flops"], fk: r(a["layer_flops"] / t / 1e12 / peak)},
         "gateup": {"us": timing["stages_us"]["gateup"], "algorithmic_bytes": a["gateup_bytes"],
                    "hbm_frac": r(a["gateup_bytes"] / gu / 1e9 / HBM_PEAK_GBS),
-                   "fp4_frac": r(a["gateup_flops"] / gu / 1e12 / FP4_PEAK_TFLOPS)},
+                   fk: r(a["gateup_flops"] / gu / 1e12 / peak)},
         "down": {"us": timing["stages_us"]["down"], "algorithmic_bytes": a["down_bytes"],
                  "hbm_frac": r(a["down_bytes"] / dn / 1e9 / HBM_PEAK_GBS),
-                 "fp4_frac": r(a["down_flops"] / dn / 1e12 / FP4_PEAK_TFLOPS)},
+                 fk: r(a["down_flops"] / dn / 1e12 / peak)},
         "stages_us": {k: round(v, 2) for k, v in timing["stages_us"].items()},
         "preheat_s": round(timing["preheat_s"], 3),
         "preheat_calls": timing["preheat_calls"],
@@ -317,9 +328,10 @@ def measure_workload(name, ctx, args, hip):
 
     from mxfp4_routed_expert_sqrt_amd import synth
     from mxfp4_routed_expert_sqrt_amd.configs import SHAPES
-    from mxfp4_routed_expert_sqrt_amd.layer import MoELayer
+    from mxfp4_routed_expert_sqrt_amd.layer import MoELayer, PackedQ2kExperts
 
-    shape = SHAPES[name]
+    q2k = name.startswith(Q2K_PREFIX)
+    shape = SHAPES[name[len(Q2K_PREFIX):] if q2k else name]
     dev = ctx["dev"]
     x_np = synth.gen_x(shape, args.seed)
     x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -328,8 +340,18 @@ def measure_workload(name, ctx, args, hip):
         tok = torch.from_numpy(synth.gen_token_ids(shape, args.seed)).to(dev)
         tab = torch.from_numpy(synth.gen_tid2eid(shape, args.seed)).to(dev)
     bias = np.zeros(shape.n_experts, dtype=np.float32) if shape.bias == "zipf" else None
-    layer = MoELayer(shape, ctx["router_w"], ctx["packed"], dev, router_bias=bias)
     note = None
+    if q2k:
+        if "q2k" not in ctx:
+            t0 = time.perf_counter()
+            ctx["q2k"] = PackedQ2kExperts(synth.gen_experts_q2k(shape, args.seed), shape, dev)
+            ctx["shared_bf16"] = synth.gen_shared_bf16(shape, args.seed)
+            print(f"[bench] Q2_K experts ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+        layer = MoELayer(shape, ctx["router_w"], None, dev, router_bias=bias, shared_bf16=ctx["shared_bf16"],
+                         experts_q2k=ctx["q2k"])
+        note = "routed experts in Q2_K (84 bytes per 256 values), shared expert in bf16"
+    else:
+        layer = MoELayer(shape, ctx["router_w"], ctx["packed"], dev, router_bias=bias)
     if shape.bias == "zipf":
         calibrate_zipf_bias(shape, layer, x, seed=args.seed)
     _, routing = layer.forward(x, tok, tab, with_routing=True)
@@ -346,13 +368,16 @@ def measure_workload(name, ctx, args, hip):
     out = torch.empty_like(x)
     ws = layer.new_workspace(shape.n_rows)
     calls = []
-    for c in copies:
-        layer.experts = c
+    if q2k:
         calls.append(layer.args(x, out, ws, tok, tab))
-    layer.experts = ctx["packed"]
+    else:
+        for c in copies:
+            layer.experts = c
+            calls.append(layer.args(x, out, ws, tok, tab))
+        layer.experts = ctx["packed"]
     stream = torch.cuda.current_stream(dev).cuda_stream
     timing = Runner(hip, layer, calls, stream).run(args.steps, args.warmup, args.preheat_s)
-    res = summarise(shape, timing, touched, has_bias=bias is not None)
+    res = summarise(shape, timing, touched, shared_bf16=q2k, has_bias=bias is not None, q2k=q2k)
     if note:
         res["weights"] = note
     if shape.bias == "zipf":

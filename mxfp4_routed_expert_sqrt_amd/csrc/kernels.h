@@ -187,9 +187,21 @@ struct Q2kArgs {
 hipError_t launch_q2k_gateup(const Q2kArgs& a, int max_groups, hipStream_t stream);
 hipError_t launch_q2k_down(const Q2kArgs& a, int max_groups, hipStream_t stream);
 
-// Rows of the Q2_K work list's groups (as unit_rows; d and I multiples of 256).
-inline int q2k_unit_rows(int n_pairs, int E) {
+// LDS of a Q2_K work unit whose 16 activation rows of length K stay resident
+// for the whole contraction (rows + sub-block pairs + X, padded rows).
+__host__ __device__ inline size_t q2k_resident_lds_bytes(int K) {
+  return 16 * (size_t)(2 * K + 16) + 16 * (size_t)(K / 4 + 16) + (size_t)(K / 256) * 64;
+}
+constexpr size_t kQ2kResidentMaxLds = 160 * 1024 - 256;  // 160 KB of LDS less room for the static claim slot
+
+// Rows of the Q2_K work list's groups: 64 once the batch has at least 32
+// routed rows per expert on average (prefill-like); else 16, whose units keep
+// their activations resident in LDS (both GEMMs' K = d and I fit at d, I <=
+// 4096), or, where they do not fit, 32 from kWideUnitPairs pairs on.
+inline int q2k_unit_rows(int n_pairs, int E, int d, int I) {
   if (n_pairs >= 32 * E) return kTallGroupRows;
+  const int K = d > I ? d : I;
+  if (q2k_resident_lds_bytes(K) <= kQ2kResidentMaxLds) return kGroupRows;
   if (n_pairs >= kWideUnitPairs) return kMediumGroupRows;
   return kGroupRows;
 }

@@ -259,7 +259,7 @@ int run_layer_q2k(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const
            hipEventRecord((hipEvent_t)a.stage_events[i], stream) == hipSuccess;
   };
   if (!mark(0)) return MOE_ERR_HIP;
-  const int rows = q2k_unit_rows(P, E);
+  const int rows = q2k_unit_rows(P, E, d, I);
   const int max_groups = max_work_groups(N, k, E, 0, rows);
   const uint16_t* x = (const uint16_t*)a.x;
   if (a.norm_w) {

@@ -342,12 +342,18 @@ def test_swiglu_limit_binds():
 
 Q2K = {
     "tiny": MoEShape("q2k_tiny", 32, 256, 16, 2, 256, "topk", "tiny_q2k"),
-    # 16-row groups, two super-blocks along d, one along I (the odd count of the double buffer)
+    # 16-row groups (activations resident in LDS), two super-blocks along d, one along I
     "ragged": MoEShape("q2k_ragged", 37, 512, 16, 2, 256, "topk", "q2k_a"),
-    # >= 1024 routed pairs, < 32 per expert: 32-row groups; Zipf-biased load (several groups per hot expert)
+    # >= 1024 routed pairs: still 16-row groups at these widths; Zipf-biased load (several groups per
+    # hot expert)
     "medium": MoEShape("q2k_medium", 300, 512, 64, 4, 512, "topk", "q2k_b", bias="zipf"),
     # >= 32 routed rows per expert: 64-row groups, ragged
     "tall": MoEShape("q2k_tall", 611, 512, 8, 4, 256, "topk", "q2k_c"),
+    # d = 4608: a 16-row unit's activations no longer fit in LDS, so gate/up stages them per
+    # super-block (16-row groups below 1024 routed pairs, 32-row groups above); down (K = I = 256)
+    # keeps them resident
+    "wide_small": MoEShape("q2k_d4608_small", 40, 4608, 16, 2, 256, "topk", "q2k_d"),
+    "wide_medium": MoEShape("q2k_d4608_medium", 300, 4608, 64, 4, 256, "topk", "q2k_e"),
 }
 
 _PACKED_Q2K = {}
