@@ -1,18 +1,17 @@
 // The shared expert with bf16 weights (MOE_SHARED_BF16): two dense GEMMs over
 // all N token rows on bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
 //   gate/up: h[r][n] = silu(min(g, L)) * clamp(u, -L, L),  g = Wg[n] . x[r],
-//            u = Wu[n] . x[r], kept as two bf16 terms h = hi + lo (hi the
-//            nearest bf16, lo the nearest bf16 to the rest: 16 bits of h);
-//   down:    y[P + r][m] = Wd[m] . hi[r] + Wd[m] . lo[r] in fp32: the shared
-//            rows of y that the combine adds to the routed sum.
+//            u = Wu[n] . x[r], rounded once to bf16 (h [N][I]);
+//   down:    y[P + r][m] = Wd[m] . h[r] in fp32: the shared rows of y that the
+//            combine adds to the routed sum.
 // bf16 times bf16 is exact in fp32, so the only roundings are the fp32 sums
-// and the two-term h.
+// and the one of h.
 //
 // A workgroup (4 waves) computes a 64-row x 64-feature tile over the whole
 // contraction, staged in 64-wide K chunks through two LDS buffers: the token
-// rows (x, or both terms of h) and the NW weight matrices' 64 rows (gate and
-// up, or down), each row padded by 16 bytes so that the 16 rows of an MFMA
-// fragment fall in distinct banks.  Row-contiguous 16-byte loads fetch chunk c+1 into
+// rows (x or h) and the NW weight matrices' 64 rows (gate and up, or down),
+// each row padded by 16 bytes so that the 16 rows of an MFMA fragment fall in
+// distinct banks.  Row-contiguous 16-byte loads fetch chunk c+1 into
 // registers while chunk c is multiplied.  Wave w takes features 16w..16w+15
 // of each weight matrix as the B operand against four 16-row blocks of tokens
 // as A operands; lane group g supplies k = kk+8g..kk+8g+7 of each 32-wide
@@ -29,33 +28,28 @@ namespace moe {
 constexpr int kSbRows = 64, kSbFeat = 64, kSbChunk = 64;
 constexpr int kSbStride = kSbChunk * 2 + 16;  // bytes per staged row
 
-// NT token-row terms (1: x; 2: the hi and lo terms of h) and NW weight matrices.
 template <int NW>
 struct SbStage {
-  static constexpr int NT = NW == 1 ? 2 : 1;
-  static constexpr int kTokRows = NT * kSbRows;
-  static constexpr int kPieces = (kTokRows + NW * kSbFeat) * (kSbChunk / 8);  // 16-byte pieces per chunk
+  static constexpr int kPieces = (kSbRows + NW * kSbFeat) * (kSbChunk / 8);  // 16-byte pieces per chunk
   static constexpr int kPerThread = kPieces / 256;
-  static constexpr int kBufBytes = (kTokRows + NW * kSbFeat) * kSbStride;
+  static constexpr int kBufBytes = (kSbRows + NW * kSbFeat) * kSbStride;
   u32x4 v[kPerThread];
 };
 
-// Piece p of a chunk: the first 64*NT rows are token rows (term t of token row
-// i at row 64t + i; term t of a token matrix at a + t*n_rows*K), then 64 rows
-// per weight matrix; 8 pieces of 8 bf16 per row.
+// Piece p of a chunk: rows 0..63 are token rows, then 64 rows per weight
+// matrix; 8 pieces of 8 bf16 per row.
 template <int NW>
 __device__ __forceinline__ void sb_fetch(SbStage<NW>& st, const uint16_t* __restrict__ a, int n_rows, int r0,
                                          const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, int f0,
                                          int K, int k0) {
-  constexpr int kTok = SbStage<NW>::kTokRows;
 #pragma unroll
   for (int i = 0; i < SbStage<NW>::kPerThread; ++i) {
     const int p = threadIdx.x + 256 * i, row = p >> 3, col = 8 * (p & 7);
     const uint16_t* src;
-    if (row < kTok) {
-      src = a + ((size_t)(row / kSbRows) * n_rows + min(r0 + row % kSbRows, n_rows - 1)) * K;
+    if (row < kSbRows) {
+      src = a + (size_t)min(r0 + row, n_rows - 1) * K;
     } else {
-      const int wr = row - kTok;
+      const int wr = row - kSbRows;
       src = (NW == 2 && wr >= kSbFeat ? w1 : w0) + (size_t)(f0 + (wr & (kSbFeat - 1))) * K;
     }
     st.v[i] = *(const u32x4*)(src + k0 + col);
@@ -74,27 +68,22 @@ __device__ __forceinline__ void sb_stash(const SbStage<NW>& st, uint8_t* buf) {
 template <int NW>
 __device__ __forceinline__ void sb_step(const uint8_t* buf, int kk, v4f (*acc)[4]) {
   typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-  constexpr int kTok = SbStage<NW>::kTokRows;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   v8bf b[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j)
-    b[j] = *(const v8bf*)(buf + (kTok + j * kSbFeat + 16 * wave + col) * kSbStride + 2 * (kk + 8 * grp));
+    b[j] = *(const v8bf*)(buf + (kSbRows + j * kSbFeat + 16 * wave + col) * kSbStride + 2 * (kk + 8 * grp));
 #pragma unroll
-  for (int t = 0; t < SbStage<NW>::NT; ++t)
+  for (int rb = 0; rb < 4; ++rb) {
+    const v8bf av = *(const v8bf*)(buf + (16 * rb + col) * kSbStride + 2 * (kk + 8 * grp));
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const v8bf av = *(const v8bf*)(buf + (kSbRows * t + 16 * rb + col) * kSbStride + 2 * (kk + 8 * grp));
-#pragma unroll
-      for (int j = 0; j < NW; ++j)
-        acc[j][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[j], acc[j][rb], 0, 0, 0);
-    }
+    for (int j = 0; j < NW; ++j) acc[j][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[j], acc[j][rb], 0, 0, 0);
+  }
 }
 
-// NW = 2: gate/up tile, writes h as two bf16 planes hi [N][n_feat] then lo
-// [N][n_feat]; NW = 1: down tile on both planes, writes fp32 y rows r of width
-// n_feat.
+// NW = 2: gate/up tile, writes bf16 h [N][n_feat]; NW = 1: down tile, writes
+// fp32 y rows y_row0 + r of width n_feat.
 // The bound of two workgroups per CU (at most 256 registers per lane) keeps
 // the MFMA accumulators in VGPRs; with the whole register file the compiler
 // placed them in AGPRs and copied them on every chunk.
@@ -144,10 +133,7 @@ __global__ void __launch_bounds__(256, 2) shared_bf16_kernel(const uint16_t* __r
           gv = fminf(gv, limit);
           uv = fminf(fmaxf(uv, -limit), limit);
         }
-        const float hv = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;
-        const uint16_t hi = f32_to_bf16_rne(hv);
-        h[(size_t)r * n_feat + f] = hi;
-        h[((size_t)n_rows + r) * n_feat + f] = f32_to_bf16_rne(hv - bf16_to_f32(hi));
+        h[(size_t)r * n_feat + f] = f32_to_bf16_rne(gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv);
       } else {
         y[(size_t)r * n_feat + f] = acc[0][rb][i];
       }

@@ -143,9 +143,9 @@ hipError_t launch_combine(const float* y, const int32_t* inv, const float* gates
                           int P, int has_shared, float route_scale, const uint16_t* residual, uint16_t* out,
                           hipStream_t stream);
 
-// Shared expert with bf16 weights: h = silu(min(Wg x, L)) * clamp(Wu x) as two
-// bf16 planes hi, lo [2][N][I] (h = hi + lo); y_sh [N][d] = Wd h in fp32 (the
-// shared rows of y).  d and I multiples of 64.
+// Shared expert with bf16 weights: h = silu(min(Wg x, L)) * clamp(Wu x) as bf16
+// [N][I]; y_sh [N][d] = Wd h in fp32 (the shared rows of y).  d and I
+// multiples of 64.
 hipError_t launch_shared_bf16_gateup(const uint16_t* x, int n_rows, int d, int I, const uint16_t* wg,
                                      const uint16_t* wu, float limit, uint16_t* h, hipStream_t stream);
 hipError_t launch_shared_bf16_down(const uint16_t* h, int n_rows, int d, int I, const uint16_t* wd, float* y_sh,

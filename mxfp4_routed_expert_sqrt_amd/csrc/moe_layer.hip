@@ -92,7 +92,7 @@ Layout make_layout(const moe_config_t& c, int n) {
   L.xsum = take(qk ? N * (size_t)(c.d_model / 256) * 4 : 0);
   L.hpair = take(qk ? P * (size_t)(c.d_ff / 16) * 4 : 0);
   L.hsum = take(qk ? P * (size_t)(c.d_ff / 256) * 4 : 0);
-  L.hsh = take(shared_bf16(c) ? 2 * N * (size_t)c.d_ff * 2 : 0);  // two-term bf16 h of a bf16 shared expert
+  L.hsh = take(shared_bf16(c) ? N * (size_t)c.d_ff * 2 : 0);  // bf16 h of a bf16 shared expert
   L.y = take(Ptot * (size_t)c.d_model * 4);
   L.total = off;
   return L;
