@@ -514,6 +514,12 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
       return;
     }
   }
+  if constexpr (NB == 2) {
+    if (g.cnt <= 16) {  // one column tile holds the group: half the staging and MFMAs
+      gateup_unit<TPM, WAVES, 1, RING, NT, FP6>(a, g, fu0, lds);
+      return;
+    }
+  }
   gateup_unit<TPM, WAVES, NB, RING, NT, FP6>(a, g, fu0, lds);
 }
 
@@ -583,6 +589,12 @@ __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   if constexpr (NA >= 2) {
     if (is_half) {
       down_unit<NA / 2, WAVES, NB, RING, NT, FP6>(a, g, fu0, lds);
+      return;
+    }
+  }
+  if constexpr (NB == 2) {
+    if (g.cnt <= 16) {  // one column tile holds the group: half the staging and MFMAs
+      down_unit<NA, WAVES, 1, RING, NT, FP6>(a, g, fu0, lds);
       return;
     }
   }
