@@ -57,6 +57,9 @@ def parse():
                     help="wall time of untimed layer calls before the warm-up steps of each workload")
     ap.add_argument("--workload", default="verify512", help="the headline workload")
     ap.add_argument("--only", action="store_true", help="measure the headline workload only")
+    ap.add_argument("--extra", default=None,
+                    help="comma-separated workloads to measure after the headline (default: all of "
+                         + ", ".join(EXTRA_WORKLOADS) + ")")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -496,7 +499,10 @@ def main():
     if not args.only:
         ctx = {"dev": dev, "router_w": w_np, "packed": packed, "copies": []}
         result["workloads"] = {}
-        for name in EXTRA_WORKLOADS:
+        extra = EXTRA_WORKLOADS if args.extra is None else tuple(w for w in args.extra.split(",") if w)
+        for name in extra:
+            if name not in EXTRA_WORKLOADS:
+                raise SystemExit(f"unknown workload {name}; choose from {', '.join(EXTRA_WORKLOADS)}")
             if name == shape.name:
                 continue
             print(f"[bench] workload {name}", file=sys.stderr, flush=True)
