@@ -10,7 +10,11 @@ namespace moe {
 // v ~= q1 * 2^e1 + q2 * 2^e2 with q1, q2 E4M3 and e1, e2 E8M0 shared
 // exponents: q1 rounds v / 2^e1, q2 rounds the exact fp32 residual
 // (v - q1 * 2^e1) / 2^e2.  For bf16 inputs (8 significant bits) the two 4-bit
-// terms reproduce every element of normal range exactly.
+// terms reproduce exactly every element of at least 2^-12 of the block's
+// largest magnitude (the residual is a multiple of the element's bf16 ulp,
+// which the second term's grid, at most 2^-20 of the block maximum, resolves);
+// a smaller element next to a large one can miss its low bits, by at most
+// half that grid, 2^-21 of the block maximum.
 //
 // Row layout (K values), shaped for the 8-bit operand of the scaled MFMA, whose
 // lane group g (lanes 16g..16g+15) reads K values 16g..16g+15 and
