@@ -8,6 +8,7 @@ namespace moe {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kGroupRows = 16;       // token rows of a narrow work unit (one MFMA column tile)
@@ -16,9 +17,11 @@ constexpr int kTallGroupRows = 64;    // token rows of a tall work unit (4 colum
 constexpr int kXcds = 8;         // gfx950: workgroups are dealt round-robin to 8 XCDs
 
 // One work group of the grouped GEMMs: rows [p0, p0 + cnt) of expert e; the
-// expert's groups are entries [first, first + ng) of the work list.
+// expert's groups are entries [first, first + ng) of the work list and cut its
+// segment of seg_rows rows from seg_p0 into pieces of `rows`, so any one entry
+// describes all of them.
 struct Group {
-  int32_t e, p0, cnt, first, ng, pad0, pad1, pad2;
+  int32_t e, p0, cnt, first, ng, seg_rows, seg_p0, rows;
 };
 
 // Maps this workgroup to a work unit so that each XCD receives a contiguous
@@ -53,6 +56,33 @@ __device__ __forceinline__ bool xcd_unit_split(int n_units, int tail_units, int*
 // Units per XCD range that are dealt dynamically by xcd_unit_claim.
 constexpr int kPoolUnits = 16;
 
+// The pool part of xcd_unit_claim, by one thread: claims the next unit of the
+// shared pool of the eight XCD ranges' last kPoolUnits units.  Returns the
+// half index (2 * unit) or -1 when the pool is used up.
+__device__ __forceinline__ int pool_claim_one(int n_units, int32_t* ctr) {
+  const int H = 2 * n_units;
+  int per = (H + kXcds - 1) / kXcds;
+  per += per & 1;
+  constexpr int kPool = kXcds * kPoolUnits;
+  __attribute__((address_space(1))) int32_t* gctr = (__attribute__((address_space(1))) int32_t*)ctr;
+  while (__hip_atomic_load(gctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < kPool) {
+    const int u = __hip_atomic_fetch_add(gctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (u >= kPool) break;
+    const int x = u % kXcds, t = u / kXcds;
+    const int n = min(per, max(0, H - x * per)) / 2;
+    const int tn = min(kPoolUnits, n);
+    if (t < tn) return x * per + 2 * (n - tn + t);
+  }
+  return -1;
+}
+
+// pool_claim_one for the workgroup: every thread must call it.
+__device__ __forceinline__ int pool_claim(int n_units, int32_t* ctr, int* s_claim) {
+  if (threadIdx.x == 0) *s_claim = pool_claim_one(n_units, ctr);
+  __syncthreads();
+  return *s_claim;
+}
+
 // Dealing with a shared tail: XCD x's range (as in xcd_unit_split, whole
 // units) is taken statically in slot order except for its last kPoolUnits
 // units.  Those tails of all eight ranges form one pool, ordered tail unit 0
@@ -70,24 +100,7 @@ __device__ __forceinline__ int xcd_unit_claim(int n_units, int32_t* ctr, int* s_
   const int nx = min(per, max(0, H - xcd * per)) / 2;
   const int tx = min(kPoolUnits, nx);
   if (slot < nx - tx) return xcd * per + 2 * slot;
-  if (threadIdx.x == 0) {
-    int got = -1;
-    constexpr int kPool = kXcds * kPoolUnits;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < kPool) {
-      const int u = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (u >= kPool) break;
-      const int x = u % kXcds, t = u / kXcds;
-      const int n = min(per, max(0, H - x * per)) / 2;
-      const int tn = min(kPoolUnits, n);
-      if (t < tn) {
-        got = x * per + 2 * (n - tn + t);
-        break;
-      }
-    }
-    *s_claim = got;
-  }
-  __syncthreads();
-  return *s_claim;
+  return pool_claim(n_units, ctr, s_claim);
 }
 
 // Work group and feature block of unit `unit`.  Units run through the work
@@ -98,16 +111,39 @@ __device__ __forceinline__ int xcd_unit_claim(int n_units, int32_t* ctr, int* s_
 // weights in L2 while they run side by side on one XCD (at 8192 rows this
 // took the gate/up weight fetch from 6.31 to 3.68 GB per launch and down from
 // 2.41 to 1.69 GB).
+// A work-list entry, read as a global load however the pointer was obtained.
+__device__ __forceinline__ Group load_group(const Group* p) {
+  typedef const __attribute__((address_space(1))) int32_t* gw;
+  const gw w = (gw)p;
+  Group g;
+  g.e = w[0], g.p0 = w[1], g.cnt = w[2], g.first = w[3];
+  g.ng = w[4], g.seg_rows = w[5], g.seg_p0 = w[6], g.rows = w[7];
+  return g;
+}
+
+// Group j of the expert of g (the work-list entry g.first + j), from g alone.
+__device__ __forceinline__ Group group_piece(Group g, int j) {
+  g.p0 = g.seg_p0 + j * g.rows;
+  g.cnt = min(g.rows, g.seg_rows - j * g.rows);
+  return g;
+}
+
+// Feature-block-major: group and feature block of unit `unit`, given the
+// work-list entry unit / n_fb.
+__device__ __forceinline__ Group unit_group_of(const Group& g, int unit, int n_fb, int* fb) {
+  const int l = unit - g.first * n_fb, j = l % g.ng;
+  *fb = l / g.ng;
+  return group_piece(g, j);
+}
+
 template <bool FBMAJOR>
 __device__ __forceinline__ Group unit_group(const Group* groups, int unit, int n_fb, int* fb) {
-  const Group g = groups[unit / n_fb];
+  const Group g = load_group(groups + unit / n_fb);
   if constexpr (!FBMAJOR) {
     *fb = unit % n_fb;
     return g;
   } else {
-    const int l = unit - g.first * n_fb;
-    *fb = l / g.ng;
-    return groups[g.first + l % g.ng];
+    return unit_group_of(g, unit, n_fb, fb);
   }
 }
 
@@ -170,19 +206,18 @@ __device__ __forceinline__ int fp6_exponent(float amax) {
 }
 
 // E2M3 code of f, rounded to nearest (ties to even mantissa), and the value
-// it encodes.  With E = [|f| >= 2] + [|f| >= 4] (the binade; 0 also for the
+// it encodes.  With E = the binade of |f| clamped to [0, 2] (0 also for the
 // subnormal range, whose step 1/8 equals binade 0's) the code is
 // 8E + rint(|f| * 2^(3-E)): |f| * 2^(3-E) is exact, so this is the textbook
 // piecewise rounding without branches; a carry out of the mantissa lands on
-// the next binade's code.  Saturates at 7.5 (code 31); the callers scale f
-// into [-7.5, 7.5].
+// the next binade's code.  E comes from f's exponent field, and both scalings
+// are ldexp, so no compare-and-select chain is needed.  Saturates at 7.5 (code
+// 31); the callers scale f into [-7.5, 7.5].
 __device__ __forceinline__ uint32_t e2m3_round(float f, float* value) {
-  const float a = fabsf(f);
-  const bool c2 = a >= 2.f, c4 = a >= 4.f;
-  const float q = __builtin_rintf(a * (c4 ? 2.f : (c2 ? 4.f : 8.f)));
-  int code = (int)q + (c4 ? 16 : (c2 ? 8 : 0));
-  code = code > 31 ? 31 : code;
-  const float mag = fminf(q * (c4 ? 0.5f : (c2 ? 0.25f : 0.125f)), 7.5f);
+  const int E = min(max((int)__builtin_amdgcn_ubfe(__float_as_uint(f), 23, 8) - 127, 0), 2);
+  const float q = __builtin_rintf(ldexpf(fabsf(f), 3 - E));
+  const int code = min((int)q + 8 * E, 31);
+  const float mag = fminf(ldexpf(q, E - 3), 7.5f);
   *value = f < 0.f ? -mag : mag;
   return (uint32_t)code | (f < 0.f ? 0x20u : 0u);
 }

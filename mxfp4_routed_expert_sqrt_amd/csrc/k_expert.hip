@@ -35,6 +35,34 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const u32x4& a, const v8i& b, const 
                                                           J, (int)sa, J, (int)sb);
 }
 
+// v, hidden from the optimiser: the constant indices of the loads that start
+// the next unit go through it, so the address arithmetic that depends on them
+// is done where they are issued instead of being hoisted out of the loop over
+// units and held in registers for the whole kernel.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// threadIdx.x, hidden from the optimiser in the same way: the lane arithmetic
+// of the code that runs once per unit (row lookup, epilogue addresses) and of
+// the activation staging is done where it runs instead of being held in
+// registers across the K loop.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// Pointers into global memory (activation rows, and the weight tiles below):
+// loads and stores through them are global, never flat, however the pointer
+// was obtained.
+typedef const __attribute__((address_space(1))) uint8_t* gptr;
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* to_global(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 // ---------------------------------------------------------------------------
 // Activation chunk in LDS: 4 k-steps of the 16 token rows of a unit, laid out
 // for conflict-free MFMA reads as [step j][term t][half h][group g][col][16 B]
@@ -64,14 +92,14 @@ struct ChunkStage {
   static constexpr int kPieces = FP6 ? 512 * NB / THREADS : 1024 * NB / THREADS;
   static constexpr int kScales = (128 * NB + THREADS - 1) / THREADS;
   u32x4 q[kPieces];
-  uint2 q8[FP6 ? kPieces : 1];
+  u32x2 q8[FP6 ? kPieces : 1];
   uint32_t s[kScales];
 
   // brow_q[t]: this thread's token row of tile t; brow_s[i]: the scale row of
   // the tile of scale dword tid + THREADS*i
-  __device__ __forceinline__ void load(const uint8_t* const (&brow_q)[NB], const uint8_t* const (&brow_s)[kScales],
+  __device__ __forceinline__ void load(const gptr (&brow_q)[NB], const gptr (&brow_s)[kScales],
                                        int sg, int nks, int n_sg) {
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
     if constexpr (FP6) {
 #pragma unroll
       for (int m = 0; m < kPieces; ++m) {
@@ -79,9 +107,9 @@ struct ChunkStage {
         const int p = (tid + THREADS * m) & 511;
         const int j = p >> 7, t = (p >> 6) & 1, g = (p >> 4) & 3;
         const int ks = min(4 * sg + j, nks - 1);
-        const uint8_t* src = brow_q[tile] + (size_t)ks * 192 + t * 96;
-        q[m] = *(const u32x4*)(src + g * 16);
-        q8[m] = *(const uint2*)(src + 64 + g * 8);
+        const gptr src = brow_q[tile] + (size_t)ks * 192 + t * 96;
+        q[m] = *(const __attribute__((address_space(1))) u32x4*)(src + g * 16);
+        q8[m] = *(const __attribute__((address_space(1))) u32x2*)(src + 64 + g * 8);
       }
     } else {
 #pragma unroll
@@ -90,7 +118,8 @@ struct ChunkStage {
         const int p = (tid + THREADS * m) & 1023;
         const int j = p >> 8, t = (p >> 7) & 1, h = (p >> 6) & 1, g = (p >> 4) & 3;
         const int ks = min(4 * sg + j, nks - 1);  // past the end: any valid step (never multiplied)
-        q[m] = *(const u32x4*)(brow_q[tile] + (size_t)ks * 256 + g * 64 + t * 32 + h * 16);
+        q[m] = *(const __attribute__((address_space(1))) u32x4*)(brow_q[tile] + (size_t)ks * 256 + g * 64 + t * 32 +
+                                                                 h * 16);
       }
     }
 #pragma unroll
@@ -98,7 +127,7 @@ struct ChunkStage {
       const int u = tid + THREADS * i;
       if (u < 128 * NB) {
         const int t = (u >> 6) & 1, g = (u >> 4) & 3;
-        s[i] = *(const uint32_t*)(brow_s[i] + (size_t)(t * n_sg + sg) * 16 + g * 4);
+        s[i] = *(const __attribute__((address_space(1))) uint32_t*)(brow_s[i] + (size_t)(t * n_sg + sg) * 16 + g * 4);
       }
     }
   }
@@ -112,7 +141,7 @@ struct ChunkStage {
         const int p = (tid + THREADS * m) & 511;
         uint8_t* dst = buf + tile * kChunkBytes + (p >> 6) * 1536;
         *(u32x4*)(dst + (p & 63) * 16) = q[m];
-        *(uint2*)(dst + 1024 + (p & 63) * 8) = q8[m];
+        *(u32x2*)(dst + 1024 + (p & 63) * 8) = q8[m];
       }
     } else {
 #pragma unroll
@@ -136,7 +165,6 @@ struct WFrag {
 
 // Wave-uniform pointer into global memory: kept in scalar registers, so each
 // weight load is "scalar base + one shared per-lane offset".
-typedef const __attribute__((address_space(1))) uint8_t* gptr;
 
 __device__ __forceinline__ gptr uniform_gptr(const uint8_t* p) {
   const uint64_t v = (uint64_t)p;
@@ -203,79 +231,107 @@ __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chun
   }
 }
 
-// One group of 4 k-steps (chunk sg of the activations is in LDS buffer sg & 1).
-// Weights: ring slot of step ks is ks % RING; while step ks is multiplied the
-// fragments of ks+1 .. ks+RING-1 are in flight.  GI = position of this group
-// inside a ring cycle (RING/4 groups per cycle), so every slot index and scale
-// byte is a compile-time constant.
+// Weight tiles and activation rows a unit's loads come from.
+template <int NA, int NB, int NS>
+struct UnitSrc {
+  gptr aq[NA], as[NA];
+  gptr brow_q[NB];
+  gptr brow_s[NS];
+};
+
+// One group of 4 k-steps: chunk sg of the activations is in LDS at `chunk`,
+// and chunk sg+1 is written to `next_buf` at the end.  Weights: ring slot of
+// step ks is ks % RING; while step ks is multiplied the fragments of
+// ks+1 .. ks+RING-1 are in flight.  GI = position of this group inside a ring
+// cycle (RING/4 groups per cycle), so every slot index and scale byte is a
+// compile-time constant.
+// Loads past the end of the unit (the chunk after the last, weight steps
+// past the last) re-read the last chunk and step (valid addresses, never
+// multiplied).
+// The chunk loaded during the group is chunk cc of cs (in a unit's K loop:
+// chunk sg+1 of the unit, clamped).
 template <int GI, int RING, int NA, int THREADS, int NB, bool NT, bool FP6>
 __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB, FP6>& stage,
-                                        uint32_t (&sa)[NA],
-                                        uint32_t (&sa_n)[NA], const gptr (&aq)[NA], const gptr (&as)[NA],
-                                        const uint8_t* const (&brow_q)[NB],
-                                        const uint8_t* const (&brow_s)[ChunkStage<THREADS, NB>::kScales], int sg,
-                                        int nks, int n_sg, v4f (&acc)[NA][NB], uint8_t* lds) {
-  constexpr int kBuf = NB * kChunkBytes;
+                                        uint32_t (&sa)[NA], uint32_t (&sa_n)[NA],
+                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales>& cur, int sg,
+                                        int nks, int n_sg, v4f (&acc)[NA][NB], const uint8_t* chunk,
+                                        uint8_t* next_buf,
+                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales>& cs, int cc) {
   const int lane = threadIdx.x & 63, last = nks - 1, k0 = 4 * sg;
-  const uint8_t* chunk = lds + (sg & 1) * kBuf;
   uint32_t sb[NB][2];
 #pragma unroll
   for (int tt = 0; tt < NB; ++tt) {
     sb[tt][0] = *(const uint32_t*)(chunk + tt * kChunkBytes + kChunkData + lane * 4);
     sb[tt][1] = *(const uint32_t*)(chunk + tt * kChunkBytes + kChunkData + 256 + lane * 4);
   }
-  stage.load(brow_q, brow_s, min(sg + 1, n_sg - 1), nks, n_sg);
-  load_wscales(sa_n, as, min(sg + 1, n_sg - 1));
-  load_w<NT>(f[(4 * GI + RING - 1) % RING], aq, min(k0 + RING - 1, last));
+  // weight step loaded at position j of the group (RING-1+j steps ahead)
+  auto load_step = [&](WFrag<NA>& slot, int j) { load_w<NT>(slot, cur.aq, min(k0 + RING - 1 + j, last)); };
+  stage.load(cs.brow_q, cs.brow_s, cc, nks, n_sg);
+  load_wscales(sa_n, cur.as, min(sg + 1, n_sg - 1));
+  load_step(f[(4 * GI + RING - 1) % RING], 0);
   __builtin_amdgcn_sched_barrier(0);
   mma_step<0, NA, NB, FP6>(f[(4 * GI) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
-  load_w<NT>(f[(4 * GI + RING) % RING], aq, min(k0 + RING, last));
+  load_step(f[(4 * GI + RING) % RING], 1);
   __builtin_amdgcn_sched_barrier(0);
   if (k0 + 1 < nks) mma_step<1, NA, NB, FP6>(f[(4 * GI + 1) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
-  load_w<NT>(f[(4 * GI + RING + 1) % RING], aq, min(k0 + RING + 1, last));
+  load_step(f[(4 * GI + RING + 1) % RING], 2);
   __builtin_amdgcn_sched_barrier(0);
   if (k0 + 2 < nks) mma_step<2, NA, NB, FP6>(f[(4 * GI + 2) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
-  load_w<NT>(f[(4 * GI + RING + 2) % RING], aq, min(k0 + RING + 2, last));
+  load_step(f[(4 * GI + RING + 2) % RING], 3);
   __builtin_amdgcn_sched_barrier(0);
   if (k0 + 3 < nks) mma_step<3, NA, NB, FP6>(f[(4 * GI + 3) % RING], chunk, sa, sb, acc);
   __builtin_amdgcn_sched_barrier(0);
-  stage.store(lds + ((sg + 1) & 1) * kBuf);
+  stage.store(next_buf);
   __syncthreads();
 #pragma unroll
   for (int a = 0; a < NA; ++a) sa[a] = sa_n[a];
 }
 
-// K loop.  Weights: a register ring of RING k-step fragments (RING-1 steps
-// in flight ahead of the one being multiplied; weight scales one group of 4
-// k-steps ahead).  Activations: chunk sg+1 is fetched into registers at the
-// start of group sg and written to the other LDS buffer at its end, then one
-// workgroup barrier per group (it waits on LDS traffic only, not on the weight
-// loads in flight).  Loads are unconditional (clamped indices) and the
-// sched_barrier(0) points keep their issue order, so each wait on the
-// in-order vector-memory counter covers only what is about to be used.
-// RING = 8 needs the group count to be even.
+// The loads that start a unit's K loop: chunk 0 into LDS at buf, the weight
+// scales of chunk 0 and the first RING-1 weight steps.
 template <int RING, int NA, int THREADS, int NB, bool NT, bool FP6>
-__device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[NA], const uint8_t* const (&brow_q)[NB],
-                                         const uint8_t* const (&brow_s)[ChunkStage<THREADS, NB>::kScales], int nks,
+__device__ __forceinline__ void k_start(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB, FP6>& stage, uint32_t (&sa)[NA],
+                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales>& cur, int nks,
+                                        uint8_t* buf) {
+  const int n_sg = (nks + 3) / 4, last = nks - 1;
+  stage.load(cur.brow_q, cur.brow_s, 0, nks, n_sg);
+  load_wscales(sa, cur.as, 0);
+#pragma unroll
+  for (int i = 0; i < RING - 1; ++i) load_w<NT>(f[i], cur.aq, min(i, last));
+  stage.store(buf);
+  __syncthreads();
+}
+
+// K loop of one unit.  Weights: a register ring of RING k-step fragments
+// (RING-1 steps in flight ahead of the one being multiplied; weight scales
+// one group of 4 k-steps ahead).  Activations: chunk sg+1 is fetched into
+// registers at the start of group sg and written to the other LDS buffer at
+// its end, then one workgroup barrier per group (it waits on LDS traffic
+// only, not on the weight loads in flight).  Loads are unconditional (clamped
+// indices) and the sched_barrier(0) points keep their issue order, so each
+// wait on the in-order vector-memory counter covers only what is about to be
+// used.  RING = 8 needs the group count to be even.
+template <int RING, int NA, int THREADS, int NB, bool NT, bool FP6>
+__device__ __forceinline__ void mainloop(const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales>& src, int nks,
                                          v4f (&acc)[NA][NB], uint8_t* lds) {
   static_assert(RING == 4 || RING == 8, "ring of 1 or 2 groups");
-  const int n_sg = (nks + 3) / 4, last = nks - 1;
+  constexpr int kBuf = NB * kChunkBytes;
+  const int n_sg = (nks + 3) / 4;
   ChunkStage<THREADS, NB, FP6> stage;
   WFrag<NA> f[RING];
   uint32_t sa[NA], sa_n[NA];
-  stage.load(brow_q, brow_s, 0, nks, n_sg);
-  load_wscales(sa, as, 0);
-#pragma unroll
-  for (int i = 0; i < RING - 1; ++i) load_w<NT>(f[i], aq, min(i, last));
-  stage.store(lds);
-  __syncthreads();
+  k_start<RING, NA, THREADS, NB, NT, FP6>(f, stage, sa, src, nks, lds);
   for (int sg = 0; sg < n_sg; sg += RING / 4) {
-    k_group<0, RING, NA, THREADS, NB, NT, FP6>(f, stage, sa, sa_n, aq, as, brow_q, brow_s, sg, nks, n_sg, acc, lds);
+    k_group<0, RING, NA, THREADS, NB, NT, FP6>(f, stage, sa, sa_n, src, sg, nks, n_sg, acc,
+                                               lds + (sg & 1) * kBuf, lds + ((sg + 1) & 1) * kBuf, src,
+                                               min(sg + 1, n_sg - 1));
     if (RING == 8)
-      k_group<1, RING, NA, THREADS, NB, NT, FP6>(f, stage, sa, sa_n, aq, as, brow_q, brow_s, sg + 1, nks, n_sg, acc, lds);
+      k_group<1, RING, NA, THREADS, NB, NT, FP6>(f, stage, sa, sa_n, src, sg + 1, nks, n_sg, acc,
+                                                 lds + ((sg + 1) & 1) * kBuf, lds + (sg & 1) * kBuf, src,
+                                                 min(sg + 2, n_sg - 1));
   }
 }
 
@@ -285,22 +341,67 @@ __device__ __forceinline__ void mainloop(const gptr (&aq)[NA], const gptr (&as)[
 // pair_rows: the activation rows are in pair order (h for down); otherwise
 // they are token rows of x reached through perm (the shared expert's rows
 // follow the routed pairs in natural order).
-template <int THREADS, int NB>
+__device__ __forceinline__ int stage_pair(const Group& g, int tt) {
+  const int c = 16 * tt + (opaque_tid() & 15);
+  return g.p0 + (c < g.cnt ? c : 0);
+}
+
+template <int THREADS, int NB, int NA>
+__device__ __forceinline__ void row_ptrs(const ExpertArgs& a, const int (&row)[NB], int K,
+                                         UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales>& src) {
+#pragma unroll
+  for (int tt = 0; tt < NB; ++tt) src.brow_q[tt] = to_global(a.aq) + (size_t)row[tt] * split_q_row_bytes(K);
+#pragma unroll
+  for (int i = 0; i < ChunkStage<THREADS, NB>::kScales; ++i) {
+    const int t = min((opaque_tid() + THREADS * i) >> 7, NB - 1);
+    int r = row[0];
+#pragma unroll
+    for (int tt = 1; tt < NB; ++tt) r = t == tt ? row[tt] : r;
+    src.brow_s[i] = to_global(a.as) + (size_t)r * split_s_row_bytes(K);
+  }
+}
+
+template <int THREADS, int NB, int NA>
 __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Group g, int K, bool shared, bool pair_rows,
-                                           const uint8_t* (&brow_q)[NB],
-                                           const uint8_t* (&brow_s)[ChunkStage<THREADS, NB>::kScales]) {
-  const int tid = threadIdx.x, tcol = tid & 15;
-  auto row_of = [&](int tt) -> size_t {
-    const int c = 16 * tt + tcol;
-    const int p = g.p0 + (c < g.cnt ? c : 0);
-    if (pair_rows) return (size_t)p;
-    return (size_t)(shared ? p - a.P : a.perm[p] / a.k);
-  };
+                                           UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales>& src) {
+  int row[NB];
 #pragma unroll
-  for (int tt = 0; tt < NB; ++tt) brow_q[tt] = a.aq + row_of(tt) * split_q_row_bytes(K);
+  for (int tt = 0; tt < NB; ++tt) {
+    const int p = stage_pair(g, tt);
+    row[tt] = pair_rows ? p : (shared ? p - a.P : to_global(a.perm)[p] / a.k);
+  }
+  row_ptrs<THREADS, NB, NA>(a, row, K, src);
+}
+
+// Weight tile pointers of this wave: gate/up takes TPM 16-row tiles of gate
+// and the same rows of up from feature f0 (NA = 2 TPM), down NA tiles.
+template <int NA, bool GU>
+__device__ __forceinline__ void weight_ptrs(const ExpertArgs& a, const Group& g, int f0, gptr (&aq)[NA],
+                                            gptr (&as)[NA]) {
+  const int K = a.K, R = a.R, nks = K / 128, n_sg = (nks + 3) / 4, rt0 = f0 / 16;
+  const bool shared = g.e == a.E;
+  const size_t mq = packed_q_bytes(R, K), ms = packed_s_bytes(R, K);
+  const size_t tq = (size_t)nks * 1024, ts = (size_t)n_sg * 256;  // one 16-row tile
+  const uint8_t* q0 = shared ? a.sq0 : a.q0 + (size_t)g.e * mq;
+  const uint8_t* s0 = shared ? a.ss0 : a.s0 + (size_t)g.e * ms;
+  if constexpr (GU) {
+    constexpr int TPM = NA / 2;
+    const uint8_t* q1 = shared ? a.sq1 : a.q1 + (size_t)g.e * mq;
+    const uint8_t* s1 = shared ? a.ss1 : a.s1 + (size_t)g.e * ms;
 #pragma unroll
-  for (int i = 0; i < ChunkStage<THREADS, NB>::kScales; ++i)
-    brow_s[i] = a.as + row_of(min((tid + THREADS * i) >> 7, NB - 1)) * split_s_row_bytes(K);
+    for (int i = 0; i < TPM; ++i) {
+      aq[i] = uniform_gptr(q0 + (rt0 + i) * tq);
+      aq[TPM + i] = uniform_gptr(q1 + (rt0 + i) * tq);
+      as[i] = uniform_gptr(s0 + (rt0 + i) * ts);
+      as[TPM + i] = uniform_gptr(s1 + (rt0 + i) * ts);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      aq[i] = uniform_gptr(q0 + (rt0 + i) * tq);
+      as[i] = uniform_gptr(s0 + (rt0 + i) * ts);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -367,58 +468,28 @@ __device__ __forceinline__ void write_h_fp6(const ExpertArgs& a, const Group g, 
       D[3 * hh + 2] = (q[2] >> 16) | (q[3] << 8);
     }
     const size_t p = (size_t)g.p0 + 16 * c + col;
-    uint8_t* dst = a.hq + p * split_q_row_bytes(a.R) + (size_t)(blk_h >> 2) * kFp6StepBytes + t * kFp6TermBytes;
+    __attribute__((address_space(1))) uint8_t* dst =
+        to_global(a.hq) + p * split_q_row_bytes(a.R) + (size_t)(blk_h >> 2) * kFp6StepBytes + t * kFp6TermBytes;
     const int bb = blk_h & 3;
     if (grp & 1)
-      *(uint2*)(dst + 64 + 8 * bb) = uint2{D[4], D[5]};
+      *(__attribute__((address_space(1))) u32x2*)(dst + 64 + 8 * bb) = u32x2{D[4], D[5]};
     else
-      *(u32x4*)(dst + 16 * bb) = u32x4{D[0], D[1], D[2], D[3]};
+      *(__attribute__((address_space(1))) u32x4*)(dst + 16 * bb) = u32x4{D[0], D[1], D[2], D[3]};
     if (grp == 0) {
-      uint8_t* srow = a.hs + p * split_s_row_bytes(a.R);
+      __attribute__((address_space(1))) uint8_t* srow = to_global(a.hs) + p * split_s_row_bytes(a.R);
       srow[split_scale_offset(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
       srow[split_scale_offset(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
     }
   }
 }
 
-// One work unit: features [fu0, fu0 + WAVES*16*TPM) of gate and up for the
-// rows of group g.
-template <int TPM, int WAVES, int NB, int RING, bool NT, bool FP6>
-__device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
-  constexpr int NA = 2 * TPM, kFeatWave = 16 * TPM, kThreads = 64 * WAVES;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, grp = lane >> 4;
-  const int K = a.K, R = a.R, nks = K / 128, n_sg = (nks + 3) / 4;
-  const int f0 = fu0 + wave * kFeatWave, rt0 = f0 / 16;
-  const bool shared = g.e == a.E;
-  const size_t mq = packed_q_bytes(R, K), ms = packed_s_bytes(R, K);
-  const uint8_t* gq = shared ? a.sq0 : a.q0 + (size_t)g.e * mq;
-  const uint8_t* gs = shared ? a.ss0 : a.s0 + (size_t)g.e * ms;
-  const uint8_t* uq = shared ? a.sq1 : a.q1 + (size_t)g.e * mq;
-  const uint8_t* us = shared ? a.ss1 : a.s1 + (size_t)g.e * ms;
-  const size_t tq = (size_t)nks * 1024, ts = (size_t)n_sg * 256;  // one 16-row tile
-  gptr aq[NA], as[NA];
-#pragma unroll
-  for (int i = 0; i < TPM; ++i) {
-    aq[i] = uniform_gptr(gq + (rt0 + i) * tq);
-    aq[TPM + i] = uniform_gptr(uq + (rt0 + i) * tq);
-    as[i] = uniform_gptr(gs + (rt0 + i) * ts);
-    as[TPM + i] = uniform_gptr(us + (rt0 + i) * ts);
-  }
-  const uint8_t* brow_q[NB];
-  const uint8_t* brow_s[ChunkStage<kThreads, NB>::kScales];
-  stage_rows<kThreads, NB>(a, g, K, shared, false, brow_q, brow_s);
-  v4f acc[NA][NB];
-#pragma unroll
-  for (int i = 0; i < NA; ++i)
-#pragma unroll
-    for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
-  if (RING == 8 && (nks % 8) == 0)
-    mainloop<8, NA, kThreads, NB, NT, FP6>(aq, as, brow_q, brow_s, nks, acc, lds);
-  else
-    mainloop<4, NA, kThreads, NB, NT, FP6>(aq, as, brow_q, brow_s, nks, acc, lds);
-
+// gate/up epilogue: h of this wave's features [f0, f0 + 16 TPM) for the rows
+// of group g, from the gate (acc[0..TPM)) and up (acc[TPM..2TPM)) sums.
+template <int TPM, int NB, bool FP6>
+__device__ __forceinline__ void gateup_epilogue(const ExpertArgs& a, const Group g, int f0,
+                                                const v4f (&acc)[2 * TPM][NB]) {
+  const int lane = opaque_tid() & 63, col = lane & 15, grp = lane >> 4;
+  const int R = a.R;
   const int n_sg_h = (R / 128 + 3) / 4;
   const float L = a.limit;
   // each pair of tiles (32 features) is one 32-block of h: 4 lanes (grp 0..3) x 8 values per token
@@ -473,20 +544,44 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
       const size_t p = (size_t)g.p0 + 16 * c + col;
       // feature 16tt + 4grp + ii of block blk_h = 4ks + bb: group 2*(bb%2) + tt, byte 16*(bb/2) + 4grp + ii
       const int bb = blk_h & 3;
-      uint8_t* dst = a.hq + p * split_q_row_bytes(R) + (size_t)(blk_h >> 2) * 256 + 16 * (bb >> 1) + 4 * grp;
+      __attribute__((address_space(1))) uint8_t* dst =
+          to_global(a.hq) + p * split_q_row_bytes(R) + (size_t)(blk_h >> 2) * 256 + 16 * (bb >> 1) + 4 * grp;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        uint8_t* gdst = dst + (2 * (bb & 1) + tt) * 64;
-        *(uint32_t*)(gdst) = w1[tt];
-        *(uint32_t*)(gdst + 32) = w2[tt];
+        __attribute__((address_space(1))) uint8_t* gdst = dst + (2 * (bb & 1) + tt) * 64;
+        *(__attribute__((address_space(1))) uint32_t*)(gdst) = w1[tt];
+        *(__attribute__((address_space(1))) uint32_t*)(gdst + 32) = w2[tt];
       }
       if (grp == 0) {
-        uint8_t* srow = a.hs + p * split_s_row_bytes(R);
+        __attribute__((address_space(1))) uint8_t* srow = to_global(a.hs) + p * split_s_row_bytes(R);
         srow[split_scale_offset(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
         srow[split_scale_offset(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
       }
     }
   }
+}
+
+
+// One work unit: features [fu0, fu0 + WAVES*16*TPM) of gate and up for the
+// rows of group g.
+template <int TPM, int WAVES, int NB, int RING, bool NT, bool FP6>
+__device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
+  constexpr int NA = 2 * TPM, kThreads = 64 * WAVES;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nks = a.K / 128, f0 = fu0 + wave * 16 * TPM;
+  UnitSrc<NA, NB, ChunkStage<kThreads, NB>::kScales> src;
+  weight_ptrs<NA, true>(a, g, f0, src.aq, src.as);
+  stage_rows<kThreads, NB, NA>(a, g, a.K, g.e == a.E, false, src);
+  v4f acc[NA][NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
+  if (RING == 8 && (nks % 8) == 0)
+    mainloop<8, NA, kThreads, NB, NT, FP6>(src, nks, acc, lds);
+  else
+    mainloop<4, NA, kThreads, NB, NT, FP6>(src, nks, acc, lds);
+  gateup_epilogue<TPM, NB, FP6>(a, g, f0, acc);
 }
 
 // POOL: units dealt by xcd_unit_claim (static ranges with a shared tail),
@@ -529,44 +624,38 @@ __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
 // WAVES waves takes NA 16-row tiles: 16*NA features per wave, 16*NA*WAVES per
 // unit.
 
+// down epilogue: this wave's features [f0, f0 + 16 NA) of the y rows of group g.
+template <int NA, int NB>
+__device__ __forceinline__ void down_epilogue(const ExpertArgs& a, const Group g, int f0, const v4f (&acc)[NA][NB]) {
+  const int lane = opaque_tid() & 63, col = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < NB; ++c)
+    if (16 * c + col < g.cnt) {
+      __attribute__((address_space(1))) float* dst = to_global(a.y) + ((size_t)g.p0 + 16 * c + col) * a.R + f0 + 4 * grp;
+#pragma unroll
+      for (int tt = 0; tt < NA; ++tt)
+        __builtin_nontemporal_store(acc[tt][c], (__attribute__((address_space(1))) v4f*)(dst + 16 * tt));
+    }
+}
+
 template <int NA, int WAVES, int NB, int RING, bool NT, bool FP6>
 __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, int fu0, uint8_t* lds) {
-  constexpr int kFeatWave = 16 * NA, kThreads = 64 * WAVES;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, grp = lane >> 4;
-  const int K = a.K, R = a.R, nks = K / 128, n_sg = (nks + 3) / 4;
-  const int f0 = fu0 + wave * kFeatWave, rt0 = f0 / 16;
-  const bool shared = g.e == a.E;
-  const size_t mq = packed_q_bytes(R, K), ms = packed_s_bytes(R, K);
-  const uint8_t* dq = shared ? a.sq0 : a.q0 + (size_t)g.e * mq;
-  const uint8_t* ds = shared ? a.ss0 : a.s0 + (size_t)g.e * ms;
-  const size_t tq = (size_t)nks * 1024, ts = (size_t)n_sg * 256;
-  gptr aq[NA], as[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    aq[i] = uniform_gptr(dq + (rt0 + i) * tq);
-    as[i] = uniform_gptr(ds + (rt0 + i) * ts);
-  }
-  const uint8_t* brow_q[NB];
-  const uint8_t* brow_s[ChunkStage<kThreads, NB>::kScales];
-  stage_rows<kThreads, NB>(a, g, K, shared, true, brow_q, brow_s);
+  constexpr int kThreads = 64 * WAVES;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nks = a.K / 128, f0 = fu0 + wave * 16 * NA;
+  UnitSrc<NA, NB, ChunkStage<kThreads, NB>::kScales> src;
+  weight_ptrs<NA, false>(a, g, f0, src.aq, src.as);
+  stage_rows<kThreads, NB, NA>(a, g, a.K, g.e == a.E, true, src);
   v4f acc[NA][NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i)
 #pragma unroll
     for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
   if (RING == 8 && (nks % 8) == 0)
-    mainloop<8, NA, kThreads, NB, NT, FP6>(aq, as, brow_q, brow_s, nks, acc, lds);
+    mainloop<8, NA, kThreads, NB, NT, FP6>(src, nks, acc, lds);
   else
-    mainloop<4, NA, kThreads, NB, NT, FP6>(aq, as, brow_q, brow_s, nks, acc, lds);
-#pragma unroll
-  for (int c = 0; c < NB; ++c)
-    if (16 * c + col < g.cnt) {
-      float* dst = a.y + ((size_t)g.p0 + 16 * c + col) * R + f0 + 4 * grp;
-#pragma unroll
-      for (int tt = 0; tt < NA; ++tt) __builtin_nontemporal_store(acc[tt][c], (v4f*)(dst + 16 * tt));
-    }
+    mainloop<4, NA, kThreads, NB, NT, FP6>(src, nks, acc, lds);
+  down_epilogue<NA, NB>(a, g, f0, acc);
 }
 
 template <int NA, int WAVES, int NB, int RING, bool NT, bool FP6, bool POOL>
@@ -600,6 +689,203 @@ __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   }
   down_unit<NA, WAVES, NB, RING, NT, FP6>(a, g, fu0, lds);
 }
+
+// ---------------------------------------------------------------------------
+// Tall units in persistent workgroups (one per CU).  Each workgroup runs units
+// one after another and always holds the next one it will run, claimed a unit
+// ahead: at the start of a unit's K loop the next unit's rows (perm) are
+// fetched; the next unit's first activation chunk is loaded by this unit's
+// last group in place of its own (clamped) one (down, whose rows are pair
+// rows) or issued before this unit's epilogue (gate/up, whose rows come from
+// perm), as are the next unit's weight scales and first RING-1 weight steps,
+// so the next K loop starts with its data in place
+// (a new workgroup per unit waits for the chain work list -> perm ->
+// activations and weights instead).
+// Claims: the next unit of the workgroup's XCD range in order (an atomic on
+// the XCD's counter: consecutive units, which share weights under
+// feature-block-major order, run side by side, and faster CUs take more
+// units), past the range's static part (all but its last kPoolUnits units) a
+// unit of the shared pool of the ranges' tails.
+constexpr int kTallWorkgroups = 256;
+
+// The launch's arguments, read again from the kernel-argument segment (the
+// kernel's only argument is the ExpertArgs, at its start) through a pointer
+// the optimiser cannot see through: the loop over units then fetches each
+// field where it is used instead of holding every argument in scalar
+// registers across all units.
+__device__ __forceinline__ ExpertArgs reload_args() {
+  static_assert(sizeof(ExpertArgs) % 4 == 0, "whole dwords");
+  typedef const __attribute__((address_space(4))) uint32_t* kernarg_words;
+  kernarg_words p = (kernarg_words)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  ExpertArgs r;
+  uint32_t w[sizeof(ExpertArgs) / 4];
+#pragma unroll
+  for (size_t i = 0; i < sizeof(ExpertArgs) / 4; ++i) w[i] = p[i];
+  __builtin_memcpy(&r, w, sizeof(r));
+  return r;
+}
+
+// Word (threadIdx.x % 8) of work-list entry i, as a global load whose result
+// is read out (entry_from_words) only where it is needed.
+__device__ __forceinline__ int entry_word(const Group* groups, int i) {
+  return ((const __attribute__((address_space(1))) int32_t*)(groups + i))[opaque_tid() & 7];
+}
+
+__device__ __forceinline__ Group entry_from_words(int w) {
+  Group g;
+  g.e = __builtin_amdgcn_readlane(w, 0), g.p0 = __builtin_amdgcn_readlane(w, 1);
+  g.cnt = __builtin_amdgcn_readlane(w, 2), g.first = __builtin_amdgcn_readlane(w, 3);
+  g.ng = __builtin_amdgcn_readlane(w, 4), g.seg_rows = __builtin_amdgcn_readlane(w, 5);
+  g.seg_p0 = __builtin_amdgcn_readlane(w, 6), g.rows = __builtin_amdgcn_readlane(w, 7);
+  return g;
+}
+
+template <int NA, int WAVES, bool GU>
+__global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
+  constexpr int NB = 4, RING = 4, kThreads = 64 * WAVES, NS = ChunkStage<kThreads, NB>::kScales;
+  constexpr int kFeatWave = 16 * (GU ? NA / 2 : NA), kFeatUnit = WAVES * kFeatWave;
+  constexpr int kBuf = NB * kChunkBytes;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
+  __shared__ int s_claim[2];
+  const int n_fb = a.R / kFeatUnit, n_units = *a.n_groups * n_fb;
+  const int nks = a.K / 128, n_sg = (nks + 3) / 4;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int xcd = blockIdx.x % kXcds;
+  const int H = 2 * n_units;
+  int per = (H + kXcds - 1) / kXcds;
+  per += per & 1;
+  const int nx = min(per, max(0, H - xcd * per)) / 2;
+  const int n_static = nx - min(kPoolUnits, nx), u_base = xcd * per / 2;
+  __attribute__((address_space(1))) int32_t* xctr = to_global(a.xcd_ctr) + xcd;
+  // the unit of counter value t (thread 0 only): in order through the
+  // static part, then from the pool (-1: none left)
+  auto resolve = [&](int t, int32_t* pool) -> int {
+    if (t < n_static) return u_base + t;
+    const int h = pool_claim_one(n_units, pool);
+    return h < 0 ? -1 : h >> 1;
+  };
+  if (tid == 0) {
+    const int t0 = __hip_atomic_fetch_add(xctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int u0 = resolve(t0, a.pool);
+    int u1 = -1;
+    if (u0 >= 0) u1 = resolve(__hip_atomic_fetch_add(xctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), a.pool);
+    s_claim[0] = u0;
+    s_claim[1] = u1;
+  }
+  __syncthreads();
+  int u = s_claim[0], q = s_claim[1];
+  if (u < 0) return;
+
+  ChunkStage<kThreads, NB, true> stage;
+  WFrag<NA> f[RING];
+  uint32_t sa[NA], sa_n[NA];
+  v4f acc[NA][NB];
+  int fb;
+  Group g = unit_group<true>(a.groups, u, n_fb, &fb);
+  int f0 = fb * kFeatUnit + wave * kFeatWave;
+  UnitSrc<NA, NB, NS> cur;
+  weight_ptrs<NA, GU>(a, g, f0, cur.aq, cur.as);
+  stage_rows<kThreads, NB, NA>(a, g, a.K, g.e == a.E, !GU, cur);
+  k_start<RING, NA, kThreads, NB, false, true>(f, stage, sa, cur, nks, lds);
+  // the queued unit (a workgroup's last unit queues itself: valid addresses,
+  // never used) and its work-list entry, one dword per lane (lane i % 8 holds
+  // word i), read out at the top of the loop
+  int uq = q >= 0 ? q : u;
+  int gword = entry_word(a.groups, uq / n_fb);
+  int bp = 0;  // LDS buffer of the unit's chunk 0
+  while (true) {
+    int fbq;
+    const Group gq = unit_group_of(entry_from_words(gword), uq, n_fb, &fbq);
+    // claim the unit after the queued one; fetch the queued unit's rows
+    // (the address goes through the opaque lane index, so the compiler does not
+    // turn this one-thread atomic into a wave-wide one that waits for its
+    // result, and with it every load in flight, right here)
+    int t = 0;
+    if (tid == 0 && q >= 0)
+      t = __hip_atomic_fetch_add(xctr + min(opaque_tid(), 0), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int row[NB];
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt) {
+      const int p = stage_pair(gq, tt);
+      row[tt] = GU ? to_global(a.perm)[min(p, a.P - 1)] : p;
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+      for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
+    UnitSrc<NA, NB, NS> nxt;
+    if constexpr (GU) {
+      for (int sg = 0; sg < n_sg; ++sg)
+        k_group<0, RING, NA, kThreads, NB, false, true>(f, stage, sa, sa_n, cur, sg, nks, n_sg, acc,
+                                                        lds + (sg & 1) * kBuf, lds + ((sg + 1) & 1) * kBuf, cur,
+                                                        min(sg + 1, n_sg - 1));
+    } else {
+      // down: the queued unit's rows are pair rows, known without a load, so
+      // the last group loads and stages its first chunk (LDS buffer n_sg & 1)
+      row_ptrs<kThreads, NB, NA>(a, row, a.K, nxt);
+      for (int sg = 0; sg < n_sg; ++sg) {
+        const bool in = sg + 1 < n_sg;
+        UnitSrc<NA, NB, NS> cs;
+#pragma unroll
+        for (int tt = 0; tt < NB; ++tt) cs.brow_q[tt] = in ? cur.brow_q[tt] : nxt.brow_q[tt];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) cs.brow_s[i] = in ? cur.brow_s[i] : nxt.brow_s[i];
+        k_group<0, RING, NA, kThreads, NB, false, true>(f, stage, sa, sa_n, cur, sg, nks, n_sg, acc,
+                                                        lds + ((bp + sg) & 1) * kBuf,
+                                                        lds + ((bp + sg + 1) & 1) * kBuf, cs, in ? sg + 1 : 0);
+      }
+      bp = (bp + n_sg) & 1;
+    }
+    const ExpertArgs A = reload_args();
+    if (tid == 0) s_claim[0] = q >= 0 ? resolve(t, A.pool) : -1;
+    __syncthreads();
+    const int q2 = s_claim[0];
+    // the unit after the queued one: its work-list entry, first of the loads
+    // issued here and read out at the top of the next iteration
+    const int uq2 = q2 >= 0 ? q2 : uq;
+    gword = entry_word(A.groups, uq2 / n_fb);
+    // the queued unit's loads (gate/up: its first chunk too)
+    const int f0q = fbq * kFeatUnit + wave * kFeatWave;
+    if constexpr (GU) {
+      const bool sh = gq.e == A.E;
+#pragma unroll
+      for (int tt = 0; tt < NB; ++tt) row[tt] = sh ? stage_pair(gq, tt) - A.P : row[tt] / A.k;
+      row_ptrs<kThreads, NB, NA>(A, row, A.K, nxt);
+      stage.load(nxt.brow_q, nxt.brow_s, opaque(0), nks, n_sg);
+    }
+    weight_ptrs<NA, GU>(A, gq, f0q, nxt.aq, nxt.as);
+    load_wscales(sa, nxt.as, opaque(0));
+#pragma unroll
+    for (int i = 0; i < RING - 1; ++i) load_w<false>(f[i], nxt.aq, min(opaque(i), nks - 1));
+    if constexpr (GU)
+      gateup_epilogue<NA / 2, NB, true>(A, g, f0, acc);
+    else
+      down_epilogue<NA, NB>(A, g, f0, acc);
+    if (q < 0) break;
+    if constexpr (GU) {
+      stage.store(lds);
+      __syncthreads();
+    }
+    u = q;
+    g = gq;
+    f0 = f0q;
+    cur = nxt;
+    q = q2;
+    uq = uq2;
+  }
+}
+
+template <int NA, int WAVES, bool GU>
+static hipError_t tall_launch(const ExpertArgs& a, hipStream_t stream) {
+  static std::atomic<uint64_t> attr{0};
+  const size_t lds = 2 * 4 * (size_t)kChunkBytes;
+  hipError_t err = ensure_dynamic_lds(tall_kernel<NA, WAVES, GU>, lds, attr);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((tall_kernel<NA, WAVES, GU>), dim3(kTallWorkgroups), dim3(64 * WAVES), lds, stream, a);
+  return hipGetLastError();
+}
+
 
 // Narrow (16-row) units: the widest unit that divides the output width;
 // wider units stage each activation chunk for more weight bytes (less
@@ -648,7 +934,9 @@ constexpr int kSmallTailUnits = 64;
 hipError_t launch_gateup(const ExpertArgs& a0, int max_groups, hipStream_t stream) {
   ExpertArgs a = a0;
   a.tail_units = 0;
-  if (a.rows == kTallGroupRows) return gateup_launch<2, 8, 4, false, true, true>(a, max_groups, stream);
+  if (a.rows == kTallGroupRows) {
+    return tall_launch<4, 8, true>(a, stream);
+  }
   if (a.rows == kMediumGroupRows) return gateup_launch<2, 8, 2, true, false, true>(a, max_groups, stream);
   if (a.P < kWideUnitPairs) {
     a.tail_units = kSmallTailUnits;
@@ -664,7 +952,9 @@ hipError_t launch_gateup(const ExpertArgs& a0, int max_groups, hipStream_t strea
 hipError_t launch_down(const ExpertArgs& a0, int max_groups, hipStream_t stream) {
   ExpertArgs a = a0;
   a.tail_units = 0;
-  if (a.rows == kTallGroupRows) return down_launch<4, 8, 4, false, true, true>(a, max_groups, stream);
+  if (a.rows == kTallGroupRows) {
+    return tall_launch<4, 8, false>(a, stream);
+  }
   if (a.rows == kMediumGroupRows) return down_launch<4, 8, 2, true, false, true>(a, max_groups, stream);
   if (a.P < kWideUnitPairs) {
     a.tail_units = kSmallTailUnits;

@@ -405,9 +405,8 @@ template <int TPM, int WAVES, int NB, int RING, bool GU, bool F16>
 __device__ __forceinline__ void qk_unit(const Q2kArgs& a, const Group g, int fu0, uint8_t* lds) {
   constexpr int NA = GU ? 2 * TPM : TPM, kThreads = 64 * WAVES, kRows = 16 * NB;
   constexpr int kBuf = QkBuf<NB>::kBytes;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, grp = lane >> 4;
   const int K = a.K, R = a.R, nb = K / 256;
   const int f0 = fu0 + wave * 16 * TPM;
   const size_t mat = q2k_matrix_bytes(R, K), tile = (size_t)nb * kQ2kTileBytes;

@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(256, 2) prologue_kernel(const uint16_t* __rest
                                                         uint8_t* __restrict__ xs, int32_t* __restrict__ done, int fp6) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kLgBufBytes];
   const int b = blockIdx.x;
-  if (b == 0 && threadIdx.x < 3) done[threadIdx.x] = 0;
+  if (b == 0 && threadIdx.x < kLayerCounters) done[threadIdx.x] = 0;
   if (b < n_tiles) {
     logits_tile(x, w, n_rows, d, E, S, z_part, b, lds);
   } else {
@@ -428,7 +428,9 @@ __device__ __forceinline__ void write_groups(int rows, const int32_t* s_cnt, con
       gr.cnt = min(rows, c - g * rows);
       gr.first = g0;
       gr.ng = ng;
-      gr.pad0 = gr.pad1 = gr.pad2 = 0;
+      gr.seg_rows = c;
+      gr.seg_p0 = p0;
+      gr.rows = rows;
       groups[g0 + g] = gr;
     }
   }
@@ -439,7 +441,9 @@ __device__ __forceinline__ void write_groups(int rows, const int32_t* s_cnt, con
     gr.cnt = min(rows, n_rows - g * rows);
     gr.first = shared0;
     gr.ng = nsh;
-    gr.pad0 = gr.pad1 = gr.pad2 = 0;
+    gr.seg_rows = n_rows;
+    gr.seg_p0 = P;
+    gr.rows = rows;
     groups[shared0 + g] = gr;
   }
   if (tid == 0) *n_groups = total + nsh;

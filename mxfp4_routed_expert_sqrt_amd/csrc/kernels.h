@@ -52,8 +52,13 @@ __host__ __device__ inline size_t split_s_row_bytes(int K) {
 hipError_t launch_pack_mxfp4(const uint8_t* q, const uint8_t* s, int n_mat, int rows, int K, uint8_t* q_out,
                              uint8_t* s_out, hipStream_t stream);
 
+// Counters of one layer call, zeroed by the prologue launch: the selection's
+// completion count, the claim pools of gate/up and down, and the per-XCD
+// claim counters of the tall gate/up and down kernels.
+constexpr int kLayerCounters = 3 + 2 * kXcds;
+
 // Router logits partials and (xq != NULL) the two-term split of x; clears the
-// three counters at done.
+// kLayerCounters counters at done.
 hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d, int E, float* z_part, uint8_t* xq,
                            uint8_t* xs, int32_t* done, bool fp6, hipStream_t stream);
 
@@ -122,6 +127,7 @@ struct ExpertArgs {
   float* y;                              // down output [pairs][R]
   int tail_units;                        // units per XCD processed as two halves at the end
   int32_t* pool;                         // claim counter of xcd_unit_claim (medium and tall units)
+  int32_t* xcd_ctr;                      // tall units: per-XCD claim counters [kXcds]
   int rows;                              // rows of the work list's groups (unit_rows); 64: FP6 activations
 };
 

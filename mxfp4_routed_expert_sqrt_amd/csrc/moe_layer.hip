@@ -81,7 +81,7 @@ Layout make_layout(const moe_config_t& c, int n) {
   L.groups = take((size_t)L.max_groups * sizeof(Group));
   L.n_groups = take(4);
   L.hist = take(route_hist_bytes(n, c.n_experts));
-  L.done = take(12);  // selection completion count, gate/up and down claim counters
+  L.done = take(4 * kLayerCounters);  // selection completion count, claim counters
   L.xn = take(N * (size_t)c.d_model * 2);  // the normalised input (when norm_w is given)
   const bool qk = q2k(c);
   L.xq = take(qk ? 0 : N * split_q_row_bytes(c.d_model));
@@ -394,6 +394,7 @@ int run_layer(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const Lay
   ga.hq = hq;
   ga.hs = hs;
   ga.pool = done + 1;
+  ga.xcd_ctr = done + 3;
   if (!mark(2)) return MOE_ERR_HIP;
   if ((err = launch_gateup(ga, max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
   uint16_t* hsh = (uint16_t*)(ws + L.hsh);
@@ -411,6 +412,7 @@ int run_layer(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const Lay
   da.sq1 = da.ss1 = nullptr;
   da.aq = hq;
   da.pool = done + 2;
+  da.xcd_ctr = done + 3 + kXcds;
   da.as = hs;
   da.K = I;
   da.R = d;
