@@ -73,43 +73,78 @@ constexpr int kRing = 4;           // weight ring slots per wave (4 or 8)
 constexpr int kDownUnitMax = 512;  // widest down work unit (features)
 constexpr int kChunkBytes = kChunkData + 512;
 
+// FP6 chunks (two E2M3 terms, tall units: NB = 4 tiles, 8 waves) are kept
+// row-major: row r of the unit (tile r / 16, column r % 16) holds its 768
+// chunk bytes (4 k-steps x 2 terms x 96: operand dwords 0-3 of lane groups
+// 0..3, then dwords 4-5 of lane groups 0..3) at r * kFp6RowStride, followed
+// by the B scales of the 4 tiles at kFp6Rows (as above, 512 B a tile).  Each
+// wave stages whole rows: one 12-byte load per lane covers a row's 768
+// contiguous chunk bytes and is stored as three dwords at the same offsets,
+// so global reads touch 6 cache lines per row instead of a line per 64 bytes.
+// The 776-byte stride puts the 16 rows of an MFMA fragment 8 bytes apart
+// modulo 128, so the fragment reads, done as 8-byte pieces, are free of bank
+// conflicts.
+constexpr int kFp6RowStride = 776;
+constexpr int kFp6Rows = 64 * kFp6RowStride;
+
+// Bytes of one chunk buffer, and the offset of tile tt's B scales in it.
+template <int NB, bool FP6>
+__host__ __device__ constexpr int chunk_buf_bytes() {
+  return FP6 ? kFp6Rows + NB * 512 : NB * kChunkBytes;
+}
+template <int NB, bool FP6>
+__device__ __forceinline__ constexpr int scale_off(int tt) {
+  return FP6 ? kFp6Rows + tt * 512 : tt * kChunkBytes + kChunkData;
+}
+
+// Rows of a unit's activation chunk that this thread stages:
+//  - FP8: row[tt] = its column tid % 16 of each tile tt;
+//  - FP6: row[0] = the row 8 * wave + lane % 8 (lane i < 8 of a wave holds the
+//    row the wave's i-th load reads; the other lanes repeat them).
+// And the row of each scale dword it stages (dword tid + THREADS*i, of tile
+// (tid + THREADS*i) >> 7).
+template <int NB, bool FP6>
+__host__ __device__ constexpr int stage_rows_n() {
+  return FP6 ? 1 : NB;
+}
+
 // This thread's share of one chunk of NB column tiles (global -> registers ->
-// LDS).  Tile t of a chunk buffer sits at t * kChunkBytes.  Piece
+// LDS).  FP8: tile t of a chunk buffer sits at t * kChunkBytes.  Piece
 // p = tid + THREADS*m (16 bytes) of the chunk belongs to tile p >> 10, and
 // inside it is (j, t, h, g, col) = (p>>8 & 3, p>>7 & 1, p>>6 & 1, p>>4 & 3,
 // p & 15); col = tid % 16 for every m, so each thread reads one token row per
 // tile.  THREADS divides 1024, so the tile of piece m is (THREADS*m) >> 10.
+// FP6: the row-major layout above, 8 rows per wave.
 // The chunk's 128*NB scale dwords are carried as dword tid + THREADS*i
 // (tile (tid + THREADS*i) >> 7).
-//
-// FP6 chunks (two E2M3 terms): per tile and (k-step j, term t) 1536 bytes, a
-// 16-byte plane [lane][dwords 0-3] at (2j+t)*1536 and an 8-byte plane
-// [lane][dwords 4-5] at (2j+t)*1536 + 1024; piece p (of 512 per tile and
-// plane) is (j, t, g, col) = (p>>7, p>>6 & 1, p>>4 & 3, p & 15).
 template <int THREADS, int NB, bool FP6 = false>
 struct ChunkStage {
-  static_assert(1024 % THREADS == 0 && (!FP6 || 512 % THREADS == 0), "chunk staging shape");
-  static constexpr int kPieces = FP6 ? 512 * NB / THREADS : 1024 * NB / THREADS;
+  static_assert(1024 % THREADS == 0 && (!FP6 || (NB == 4 && THREADS == 512)), "chunk staging shape");
+  static constexpr int kPieces = FP6 ? 8 : 1024 * NB / THREADS;
   static constexpr int kScales = (128 * NB + THREADS - 1) / THREADS;
-  u32x4 q[kPieces];
-  u32x2 q8[FP6 ? kPieces : 1];
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+  u32x4 q[FP6 ? 1 : kPieces];
+  u32x3 q3[FP6 ? kPieces : 1];
   uint32_t s[kScales];
 
-  // brow_q[t]: this thread's token row of tile t; brow_s[i]: the scale row of
-  // the tile of scale dword tid + THREADS*i
-  __device__ __forceinline__ void load(const gptr (&brow_q)[NB], const gptr (&brow_s)[kScales],
+  // brow_q: the staged rows (stage_rows_n); brow_s[i]: the scale row of the
+  // tile of scale dword tid + THREADS*i
+  __device__ __forceinline__ void load(const gptr (&brow_q)[stage_rows_n<NB, FP6>()], const gptr (&brow_s)[kScales],
                                        int sg, int nks, int n_sg) {
     const int tid = opaque_tid();
     if constexpr (FP6) {
+      // lane l: 12 bytes at chunk offset 12 l = k-step l / 16, byte 12 (l % 16)
+      const int l = tid & 63;
+      const uint32_t off = (uint32_t)min(4 * sg + (l >> 4), nks - 1) * 192 + 12 * (l & 15);
+      const uint64_t rp = (uint64_t)brow_q[0];
+      const uint32_t lo = (uint32_t)rp, hi = (uint32_t)(rp >> 32);
 #pragma unroll
-      for (int m = 0; m < kPieces; ++m) {
-        const int tile = (THREADS * m) >> 9;
-        const int p = (tid + THREADS * m) & 511;
-        const int j = p >> 7, t = (p >> 6) & 1, g = (p >> 4) & 3;
-        const int ks = min(4 * sg + j, nks - 1);
-        const gptr src = brow_q[tile] + (size_t)ks * 192 + t * 96;
-        q[m] = *(const __attribute__((address_space(1))) u32x4*)(src + g * 16);
-        q8[m] = *(const __attribute__((address_space(1))) u32x2*)(src + 64 + g * 8);
+      for (int i = 0; i < kPieces; ++i) {
+        // (each half as uint32_t: a signed low word would sign-extend into the high one)
+        const uint32_t rlo = (uint32_t)__builtin_amdgcn_readlane((int)lo, i);
+        const uint32_t rhi = (uint32_t)__builtin_amdgcn_readlane((int)hi, i);
+        const gptr row = (gptr)(((uint64_t)rhi << 32) | rlo);
+        q3[i] = *(const __attribute__((address_space(1))) u32x3*)(row + off);
       }
     } else {
 #pragma unroll
@@ -135,13 +170,13 @@ struct ChunkStage {
   __device__ __forceinline__ void store(uint8_t* buf) const {
     const int tid = threadIdx.x;
     if constexpr (FP6) {
+      const int wave = tid >> 6, l = tid & 63;
 #pragma unroll
-      for (int m = 0; m < kPieces; ++m) {
-        const int tile = (THREADS * m) >> 9;
-        const int p = (tid + THREADS * m) & 511;
-        uint8_t* dst = buf + tile * kChunkBytes + (p >> 6) * 1536;
-        *(u32x4*)(dst + (p & 63) * 16) = q[m];
-        *(u32x2*)(dst + 1024 + (p & 63) * 8) = q8[m];
+      for (int i = 0; i < kPieces; ++i) {
+        uint32_t* dst = (uint32_t*)(buf + (8 * wave + i) * kFp6RowStride + 12 * l);
+        dst[0] = q3[i][0];
+        dst[1] = q3[i][1];
+        dst[2] = q3[i][2];
       }
     } else {
 #pragma unroll
@@ -153,7 +188,7 @@ struct ChunkStage {
 #pragma unroll
     for (int i = 0; i < kScales; ++i) {
       const int u = tid + THREADS * i;
-      if (u < 128 * NB) *(uint32_t*)(buf + (u >> 7) * kChunkBytes + kChunkData + (u & 127) * 4) = s[i];
+      if (u < 128 * NB) *(uint32_t*)(buf + scale_off<NB, FP6>(u >> 7) + (u & 127) * 4) = s[i];
     }
   }
 };
@@ -201,10 +236,12 @@ template <int J, int NB, bool FP6>
 __device__ __forceinline__ v8i read_b(const uint8_t* chunk, int i) {
   const int lane = threadIdx.x & 63, tt = i % NB, t = i / NB;
   if constexpr (FP6) {
-    const uint8_t* c = chunk + tt * kChunkBytes + (J * 2 + t) * 1536;
-    const u32x4 lo = *(const u32x4*)(c + lane * 16);
-    const uint2 hi = *(const uint2*)(c + 1024 + lane * 8);
-    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi.x, (int)hi.y, 0, 0};
+    const int col = lane & 15, g = lane >> 4;
+    const uint8_t* c = chunk + (16 * tt + col) * kFp6RowStride + J * 192 + t * 96;
+    const u32x2 w0 = *(const u32x2*)(c + g * 16);
+    const u32x2 w1 = *(const u32x2*)(c + g * 16 + 8);
+    const u32x2 w2 = *(const u32x2*)(c + 64 + g * 8);
+    return v8i{(int)w0[0], (int)w0[1], (int)w1[0], (int)w1[1], (int)w2[0], (int)w2[1], 0, 0};
   } else {
     const uint8_t* c = chunk + tt * kChunkBytes + (J * 2 + t) * 2048 + lane * 16;
     const u32x4 lo = *(const u32x4*)c;
@@ -231,11 +268,12 @@ __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chun
   }
 }
 
-// Weight tiles and activation rows a unit's loads come from.
-template <int NA, int NB, int NS>
+// Weight tiles and activation rows a unit's loads come from (brow_q: the
+// staged rows, brow_s: the scale rows, as ChunkStage takes them).
+template <int NA, int NB, int NS, bool FP6 = false>
 struct UnitSrc {
   gptr aq[NA], as[NA];
-  gptr brow_q[NB];
+  gptr brow_q[stage_rows_n<NB, FP6>()];
   gptr brow_s[NS];
 };
 
@@ -253,16 +291,16 @@ struct UnitSrc {
 template <int GI, int RING, int NA, int THREADS, int NB, bool NT, bool FP6>
 __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB, FP6>& stage,
                                         uint32_t (&sa)[NA], uint32_t (&sa_n)[NA],
-                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales>& cur, int sg,
+                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& cur, int sg,
                                         int nks, int n_sg, v4f (&acc)[NA][NB], const uint8_t* chunk,
                                         uint8_t* next_buf,
-                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales>& cs, int cc) {
+                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& cs, int cc) {
   const int lane = threadIdx.x & 63, last = nks - 1, k0 = 4 * sg;
   uint32_t sb[NB][2];
 #pragma unroll
   for (int tt = 0; tt < NB; ++tt) {
-    sb[tt][0] = *(const uint32_t*)(chunk + tt * kChunkBytes + kChunkData + lane * 4);
-    sb[tt][1] = *(const uint32_t*)(chunk + tt * kChunkBytes + kChunkData + 256 + lane * 4);
+    sb[tt][0] = *(const uint32_t*)(chunk + scale_off<NB, FP6>(tt) + lane * 4);
+    sb[tt][1] = *(const uint32_t*)(chunk + scale_off<NB, FP6>(tt) + 256 + lane * 4);
   }
   // weight step loaded at position j of the group (RING-1+j steps ahead)
   auto load_step = [&](WFrag<NA>& slot, int j) { load_w<NT>(slot, cur.aq, min(k0 + RING - 1 + j, last)); };
@@ -294,7 +332,7 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
 // scales of chunk 0 and the first RING-1 weight steps.
 template <int RING, int NA, int THREADS, int NB, bool NT, bool FP6>
 __device__ __forceinline__ void k_start(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB, FP6>& stage, uint32_t (&sa)[NA],
-                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales>& cur, int nks,
+                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& cur, int nks,
                                         uint8_t* buf) {
   const int n_sg = (nks + 3) / 4, last = nks - 1;
   stage.load(cur.brow_q, cur.brow_s, 0, nks, n_sg);
@@ -315,10 +353,10 @@ __device__ __forceinline__ void k_start(WFrag<NA> (&f)[RING], ChunkStage<THREADS
 // wait on the in-order vector-memory counter covers only what is about to be
 // used.  RING = 8 needs the group count to be even.
 template <int RING, int NA, int THREADS, int NB, bool NT, bool FP6>
-__device__ __forceinline__ void mainloop(const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales>& src, int nks,
+__device__ __forceinline__ void mainloop(const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& src, int nks,
                                          v4f (&acc)[NA][NB], uint8_t* lds) {
   static_assert(RING == 4 || RING == 8, "ring of 1 or 2 groups");
-  constexpr int kBuf = NB * kChunkBytes;
+  constexpr int kBuf = chunk_buf_bytes<NB, FP6>();
   const int n_sg = (nks + 3) / 4;
   ChunkStage<THREADS, NB, FP6> stage;
   WFrag<NA> f[RING];
@@ -335,42 +373,66 @@ __device__ __forceinline__ void mainloop(const UnitSrc<NA, NB, ChunkStage<THREAD
   }
 }
 
-// Token rows staged by this thread: tile tt holds rows p0+16tt .. of the
-// group (column tid % 16); padding columns reuse the group's first row.  The
-// scale row is that of tile tid >> 7 (threads beyond 128*NB load no scales).
+// Rows staged by this thread, as positions in the unit's group (padding
+// positions past its rows reuse the group's first row): slots 0 ..
+// stage_rows_n()-1 are the staged rows (FP8: column tid % 16 of tile k; FP6: row
+// 8 * wave + lane % 8), FP6 adds the row of each scale dword (FP8 takes them
+// from the staged rows).
+template <int THREADS, int NB, bool FP6>
+__host__ __device__ constexpr int row_slots() {
+  return FP6 ? 1 + (128 * NB + THREADS - 1) / THREADS : NB;
+}
+
+template <int THREADS, int NB, bool FP6>
+__device__ __forceinline__ int slot_pos(int k) {
+  const int tid = opaque_tid();
+  if constexpr (FP6) {
+    if (k == 0) return 8 * (tid >> 6) + (tid & 7);
+    return 16 * min((tid + THREADS * (k - 1)) >> 7, NB - 1) + (tid & 15);
+  } else {
+    return 16 * k + (tid & 15);
+  }
+}
+
+__device__ __forceinline__ int group_pair(const Group& g, int c) { return g.p0 + (c < g.cnt ? c : 0); }
+
+// Row pointers from the rows (token rows of x, or pair rows of h) of the slots.
+template <int THREADS, int NB, int NA, bool FP6>
+__device__ __forceinline__ void row_ptrs(const ExpertArgs& a, const int (&row)[row_slots<THREADS, NB, FP6>()], int K,
+                                         UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& src) {
+  constexpr int NS = ChunkStage<THREADS, NB>::kScales;
+  if constexpr (FP6) {
+    src.brow_q[0] = to_global(a.aq) + (size_t)row[0] * split_q_row_bytes(K);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) src.brow_s[i] = to_global(a.as) + (size_t)row[1 + i] * split_s_row_bytes(K);
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < NB; ++tt) src.brow_q[tt] = to_global(a.aq) + (size_t)row[tt] * split_q_row_bytes(K);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int t = min((opaque_tid() + THREADS * i) >> 7, NB - 1);
+      int r = row[0];
+#pragma unroll
+      for (int tt = 1; tt < NB; ++tt) r = t == tt ? row[tt] : r;
+      src.brow_s[i] = to_global(a.as) + (size_t)r * split_s_row_bytes(K);
+    }
+  }
+}
+
 // pair_rows: the activation rows are in pair order (h for down); otherwise
 // they are token rows of x reached through perm (the shared expert's rows
 // follow the routed pairs in natural order).
-__device__ __forceinline__ int stage_pair(const Group& g, int tt) {
-  const int c = 16 * tt + (opaque_tid() & 15);
-  return g.p0 + (c < g.cnt ? c : 0);
-}
-
-template <int THREADS, int NB, int NA>
-__device__ __forceinline__ void row_ptrs(const ExpertArgs& a, const int (&row)[NB], int K,
-                                         UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales>& src) {
-#pragma unroll
-  for (int tt = 0; tt < NB; ++tt) src.brow_q[tt] = to_global(a.aq) + (size_t)row[tt] * split_q_row_bytes(K);
-#pragma unroll
-  for (int i = 0; i < ChunkStage<THREADS, NB>::kScales; ++i) {
-    const int t = min((opaque_tid() + THREADS * i) >> 7, NB - 1);
-    int r = row[0];
-#pragma unroll
-    for (int tt = 1; tt < NB; ++tt) r = t == tt ? row[tt] : r;
-    src.brow_s[i] = to_global(a.as) + (size_t)r * split_s_row_bytes(K);
-  }
-}
-
-template <int THREADS, int NB, int NA>
+template <int THREADS, int NB, int NA, bool FP6>
 __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Group g, int K, bool shared, bool pair_rows,
-                                           UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales>& src) {
-  int row[NB];
+                                           UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& src) {
+  constexpr int NR = row_slots<THREADS, NB, FP6>();
+  int row[NR];
 #pragma unroll
-  for (int tt = 0; tt < NB; ++tt) {
-    const int p = stage_pair(g, tt);
-    row[tt] = pair_rows ? p : (shared ? p - a.P : to_global(a.perm)[p] / a.k);
+  for (int k = 0; k < NR; ++k) {
+    const int p = group_pair(g, slot_pos<THREADS, NB, FP6>(k));
+    row[k] = pair_rows ? p : (shared ? p - a.P : to_global(a.perm)[p] / a.k);
   }
-  row_ptrs<THREADS, NB, NA>(a, row, K, src);
+  row_ptrs<THREADS, NB, NA, FP6>(a, row, K, src);
 }
 
 // Weight tile pointers of this wave: gate/up takes TPM 16-row tiles of gate
@@ -569,9 +631,9 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
   constexpr int NA = 2 * TPM, kThreads = 64 * WAVES;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nks = a.K / 128, f0 = fu0 + wave * 16 * TPM;
-  UnitSrc<NA, NB, ChunkStage<kThreads, NB>::kScales> src;
+  UnitSrc<NA, NB, ChunkStage<kThreads, NB>::kScales, FP6> src;
   weight_ptrs<NA, true>(a, g, f0, src.aq, src.as);
-  stage_rows<kThreads, NB, NA>(a, g, a.K, g.e == a.E, false, src);
+  stage_rows<kThreads, NB, NA, FP6>(a, g, a.K, g.e == a.E, false, src);
   v4f acc[NA][NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i)
@@ -589,7 +651,7 @@ __device__ __forceinline__ void gateup_unit(const ExpertArgs& a, const Group g, 
 template <int TPM, int WAVES, int NB, int RING, bool NT, bool FP6, bool POOL>
 __global__ void __launch_bounds__(64 * WAVES) gateup_kernel(ExpertArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * TPM;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * chunk_buf_bytes<NB, FP6>()
   const int n_fb = a.R / kFeatUnit;
   int half_idx;
   bool is_half = false;
@@ -643,9 +705,9 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
   constexpr int kThreads = 64 * WAVES;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nks = a.K / 128, f0 = fu0 + wave * 16 * NA;
-  UnitSrc<NA, NB, ChunkStage<kThreads, NB>::kScales> src;
+  UnitSrc<NA, NB, ChunkStage<kThreads, NB>::kScales, FP6> src;
   weight_ptrs<NA, false>(a, g, f0, src.aq, src.as);
-  stage_rows<kThreads, NB, NA>(a, g, a.K, g.e == a.E, true, src);
+  stage_rows<kThreads, NB, NA, FP6>(a, g, a.K, g.e == a.E, true, src);
   v4f acc[NA][NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i)
@@ -661,7 +723,7 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Group g, in
 template <int NA, int WAVES, int NB, int RING, bool NT, bool FP6, bool POOL>
 __global__ void __launch_bounds__(64 * WAVES) down_kernel(ExpertArgs a) {
   constexpr int kFeatUnit = WAVES * 16 * NA;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * chunk_buf_bytes<NB, FP6>()
   const int n_fb = a.R / kFeatUnit;
   int half_idx;
   bool is_half = false;
@@ -745,8 +807,8 @@ template <int NA, int WAVES, bool GU>
 __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
   constexpr int NB = 4, RING = 4, kThreads = 64 * WAVES, NS = ChunkStage<kThreads, NB>::kScales;
   constexpr int kFeatWave = 16 * (GU ? NA / 2 : NA), kFeatUnit = WAVES * kFeatWave;
-  constexpr int kBuf = NB * kChunkBytes;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * NB * kChunkBytes
+  constexpr int kBuf = chunk_buf_bytes<NB, true>(), NR = row_slots<kThreads, NB, true>();
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * kBuf
   __shared__ int s_claim[2];
   const int n_fb = a.R / kFeatUnit, n_units = *a.n_groups * n_fb;
   const int nks = a.K / 128, n_sg = (nks + 3) / 4;
@@ -784,9 +846,9 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
   int fb;
   Group g = unit_group<true>(a.groups, u, n_fb, &fb);
   int f0 = fb * kFeatUnit + wave * kFeatWave;
-  UnitSrc<NA, NB, NS> cur;
+  UnitSrc<NA, NB, NS, true> cur;
   weight_ptrs<NA, GU>(a, g, f0, cur.aq, cur.as);
-  stage_rows<kThreads, NB, NA>(a, g, a.K, g.e == a.E, !GU, cur);
+  stage_rows<kThreads, NB, NA, true>(a, g, a.K, g.e == a.E, !GU, cur);
   k_start<RING, NA, kThreads, NB, false, true>(f, stage, sa, cur, nks, lds);
   // the queued unit (a workgroup's last unit queues itself: valid addresses,
   // never used) and its work-list entry, one dword per lane (lane i % 8 holds
@@ -804,17 +866,17 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
     int t = 0;
     if (tid == 0 && q >= 0)
       t = __hip_atomic_fetch_add(xctr + min(opaque_tid(), 0), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int row[NB];
+    int row[NR];
 #pragma unroll
-    for (int tt = 0; tt < NB; ++tt) {
-      const int p = stage_pair(gq, tt);
-      row[tt] = GU ? to_global(a.perm)[min(p, a.P - 1)] : p;
+    for (int k = 0; k < NR; ++k) {
+      const int p = group_pair(gq, slot_pos<kThreads, NB, true>(k));
+      row[k] = GU ? to_global(a.perm)[min(p, a.P - 1)] : p;
     }
 #pragma unroll
     for (int i = 0; i < NA; ++i)
 #pragma unroll
       for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
-    UnitSrc<NA, NB, NS> nxt;
+    UnitSrc<NA, NB, NS, true> nxt;
     if constexpr (GU) {
       for (int sg = 0; sg < n_sg; ++sg)
         k_group<0, RING, NA, kThreads, NB, false, true>(f, stage, sa, sa_n, cur, sg, nks, n_sg, acc,
@@ -823,12 +885,11 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
     } else {
       // down: the queued unit's rows are pair rows, known without a load, so
       // the last group loads and stages its first chunk (LDS buffer n_sg & 1)
-      row_ptrs<kThreads, NB, NA>(a, row, a.K, nxt);
+      row_ptrs<kThreads, NB, NA, true>(a, row, a.K, nxt);
       for (int sg = 0; sg < n_sg; ++sg) {
         const bool in = sg + 1 < n_sg;
-        UnitSrc<NA, NB, NS> cs;
-#pragma unroll
-        for (int tt = 0; tt < NB; ++tt) cs.brow_q[tt] = in ? cur.brow_q[tt] : nxt.brow_q[tt];
+        UnitSrc<NA, NB, NS, true> cs;
+        cs.brow_q[0] = in ? cur.brow_q[0] : nxt.brow_q[0];
 #pragma unroll
         for (int i = 0; i < NS; ++i) cs.brow_s[i] = in ? cur.brow_s[i] : nxt.brow_s[i];
         k_group<0, RING, NA, kThreads, NB, false, true>(f, stage, sa, sa_n, cur, sg, nks, n_sg, acc,
@@ -850,8 +911,8 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
     if constexpr (GU) {
       const bool sh = gq.e == A.E;
 #pragma unroll
-      for (int tt = 0; tt < NB; ++tt) row[tt] = sh ? stage_pair(gq, tt) - A.P : row[tt] / A.k;
-      row_ptrs<kThreads, NB, NA>(A, row, A.K, nxt);
+      for (int k = 0; k < NR; ++k) row[k] = sh ? group_pair(gq, slot_pos<kThreads, NB, true>(k)) - A.P : row[k] / A.k;
+      row_ptrs<kThreads, NB, NA, true>(A, row, A.K, nxt);
       stage.load(nxt.brow_q, nxt.brow_s, opaque(0), nks, n_sg);
     }
     weight_ptrs<NA, GU>(A, gq, f0q, nxt.aq, nxt.as);
@@ -879,7 +940,7 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
 template <int NA, int WAVES, bool GU>
 static hipError_t tall_launch(const ExpertArgs& a, hipStream_t stream) {
   static std::atomic<uint64_t> attr{0};
-  const size_t lds = 2 * 4 * (size_t)kChunkBytes;
+  const size_t lds = 2 * (size_t)chunk_buf_bytes<4, true>();
   hipError_t err = ensure_dynamic_lds(tall_kernel<NA, WAVES, GU>, lds, attr);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((tall_kernel<NA, WAVES, GU>), dim3(kTallWorkgroups), dim3(64 * WAVES), lds, stream, a);
@@ -896,7 +957,7 @@ static hipError_t tall_launch(const ExpertArgs& a, hipStream_t stream) {
 template <int TPM, int WAVES, int NB, bool NT = false, bool FP6 = false, bool POOL = false, int RING = kRing>
 static hipError_t gateup_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
   static std::atomic<uint64_t> attr{0};
-  const size_t lds = 2 * NB * (size_t)kChunkBytes;
+  const size_t lds = 2 * (size_t)chunk_buf_bytes<NB, FP6>();
   hipError_t err = ensure_dynamic_lds(gateup_kernel<TPM, WAVES, NB, RING, NT, FP6, POOL>, lds, attr);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((gateup_kernel<TPM, WAVES, NB, RING, NT, FP6, POOL>), dim3(unit_grid(max_groups, a.R / (16 * TPM * WAVES))),
@@ -907,7 +968,7 @@ static hipError_t gateup_launch(const ExpertArgs& a, int max_groups, hipStream_t
 template <int NA, int WAVES, int NB, bool NT = false, bool FP6 = false, bool POOL = false, int RING = kRing>
 static hipError_t down_launch(const ExpertArgs& a, int max_groups, hipStream_t stream) {
   static std::atomic<uint64_t> attr{0};
-  const size_t lds = 2 * NB * (size_t)kChunkBytes;
+  const size_t lds = 2 * (size_t)chunk_buf_bytes<NB, FP6>();
   hipError_t err = ensure_dynamic_lds(down_kernel<NA, WAVES, NB, RING, NT, FP6, POOL>, lds, attr);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((down_kernel<NA, WAVES, NB, RING, NT, FP6, POOL>), dim3(unit_grid(max_groups, a.R / (16 * NA * WAVES))),
