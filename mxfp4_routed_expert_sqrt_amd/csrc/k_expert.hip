@@ -64,98 +64,75 @@ __device__ __forceinline__ __attribute__((address_space(1))) T* to_global(T* p) 
 }
 
 // ---------------------------------------------------------------------------
-// Activation chunk in LDS: 4 k-steps of the 16 token rows of a unit, laid out
-// for conflict-free MFMA reads as [step j][term t][half h][group g][col][16 B]
-// (16 KB), followed by the B scales [term][group][col] as dwords (512 B).  The
-// half h holds the operand bytes 16h..16h+15 of lane (col, g).
-constexpr int kChunkData = 16384;
+// Activation chunk in LDS: 4 k-steps of the 16 * NB token rows of a unit,
+// row-major.  Row r of the unit (tile r / 16, column r % 16) holds its chunk
+// bytes as they lie in the split row (FP8: 4 k-steps x 256, each [lane group
+// g][term][two 16-byte runs]; FP6: 4 k-steps x 2 terms x 96, operand dwords
+// 0-3 of lane groups 0..3 then dwords 4-5) at r * kRowStride, followed by the
+// B scales of the NB tiles (per tile [term][group][col] as dwords, 512 B).
+// Each wave stages whole rows: one load per lane (16 bytes, FP6 12) covers a
+// row's chunk bytes, contiguous, and is stored at the same offsets, so a
+// load touches 8 (FP6 6) cache lines instead of one per 32-64 bytes used.
+// Strides: FP8 1040 bytes (16 mod 128), so the 8 lanes of a 16-byte fragment
+// read cycle fall in distinct banks; FP6 776 bytes (8 mod 128), whose
+// fragment reads are done as 8-byte pieces, 16 lanes a cycle.
 constexpr int kRing = 4;           // weight ring slots per wave (4 or 8)
 constexpr int kDownUnitMax = 512;  // widest down work unit (features)
-constexpr int kChunkBytes = kChunkData + 512;
 
-// FP6 chunks (two E2M3 terms, tall units: NB = 4 tiles, 8 waves) are kept
-// row-major: row r of the unit (tile r / 16, column r % 16) holds its 768
-// chunk bytes (4 k-steps x 2 terms x 96: operand dwords 0-3 of lane groups
-// 0..3, then dwords 4-5 of lane groups 0..3) at r * kFp6RowStride, followed
-// by the B scales of the 4 tiles at kFp6Rows (as above, 512 B a tile).  Each
-// wave stages whole rows: one 12-byte load per lane covers a row's 768
-// contiguous chunk bytes and is stored as three dwords at the same offsets,
-// so global reads touch 6 cache lines per row instead of a line per 64 bytes.
-// The 776-byte stride puts the 16 rows of an MFMA fragment 8 bytes apart
-// modulo 128, so the fragment reads, done as 8-byte pieces, are free of bank
-// conflicts.
-constexpr int kFp6RowStride = 776;
-constexpr int kFp6Rows = 64 * kFp6RowStride;
+template <bool FP6>
+struct RowLayout {
+  static constexpr int kStepBytes = FP6 ? 192 : 256;  // one k-step of a split row
+  static constexpr int kLoadBytes = kStepBytes / 16;  // per lane: a row chunk is 64 loads
+  static constexpr int kStride = FP6 ? 776 : 1040;
+};
 
 // Bytes of one chunk buffer, and the offset of tile tt's B scales in it.
 template <int NB, bool FP6>
 __host__ __device__ constexpr int chunk_buf_bytes() {
-  return FP6 ? kFp6Rows + NB * 512 : NB * kChunkBytes;
+  return 16 * NB * RowLayout<FP6>::kStride + NB * 512;
 }
 template <int NB, bool FP6>
 __device__ __forceinline__ constexpr int scale_off(int tt) {
-  return FP6 ? kFp6Rows + tt * 512 : tt * kChunkBytes + kChunkData;
+  return 16 * NB * RowLayout<FP6>::kStride + tt * 512;
 }
 
-// Rows of a unit's activation chunk that this thread stages:
-//  - FP8: row[tt] = its column tid % 16 of each tile tt;
-//  - FP6: row[0] = the row 8 * wave + lane % 8 (lane i < 8 of a wave holds the
-//    row the wave's i-th load reads; the other lanes repeat them).
-// And the row of each scale dword it stages (dword tid + THREADS*i, of tile
-// (tid + THREADS*i) >> 7).
-template <int NB, bool FP6>
-__host__ __device__ constexpr int stage_rows_n() {
-  return FP6 ? 1 : NB;
+// Rows a wave stages per chunk: the unit's 16 * NB rows over THREADS / 64 waves.
+template <int THREADS, int NB>
+__host__ __device__ constexpr int rows_per_wave() {
+  return 16 * NB * 64 / THREADS;
 }
 
-// This thread's share of one chunk of NB column tiles (global -> registers ->
-// LDS).  FP8: tile t of a chunk buffer sits at t * kChunkBytes.  Piece
-// p = tid + THREADS*m (16 bytes) of the chunk belongs to tile p >> 10, and
-// inside it is (j, t, h, g, col) = (p>>8 & 3, p>>7 & 1, p>>6 & 1, p>>4 & 3,
-// p & 15); col = tid % 16 for every m, so each thread reads one token row per
-// tile.  THREADS divides 1024, so the tile of piece m is (THREADS*m) >> 10.
-// FP6: the row-major layout above, 8 rows per wave.
-// The chunk's 128*NB scale dwords are carried as dword tid + THREADS*i
-// (tile (tid + THREADS*i) >> 7).
+// This thread's share of one chunk (global -> registers -> LDS).  Wave w
+// stages rows rows_per_wave * w + i; brow_q holds their pointers, lane i for
+// row i (the other lanes repeat them), read out to a wave-uniform address per
+// load.  The chunk's 128*NB scale dwords are carried as dword tid + THREADS*i
+// (tile (tid + THREADS*i) >> 7), from the scale row brow_s[i].
 template <int THREADS, int NB, bool FP6 = false>
 struct ChunkStage {
-  static_assert(1024 % THREADS == 0 && (!FP6 || (NB == 4 && THREADS == 512)), "chunk staging shape");
-  static constexpr int kPieces = FP6 ? 8 : 1024 * NB / THREADS;
+  static constexpr int kRows = rows_per_wave<THREADS, NB>();
+  static_assert(kRows >= 1 && kRows <= 16 && (kRows & (kRows - 1)) == 0, "chunk staging shape");
   static constexpr int kScales = (128 * NB + THREADS - 1) / THREADS;
+  typedef RowLayout<FP6> L;
   typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-  u32x4 q[FP6 ? 1 : kPieces];
-  u32x3 q3[FP6 ? kPieces : 1];
+  typedef typename std::conditional<FP6, u32x3, u32x4>::type Piece;
+  Piece q[kRows];
   uint32_t s[kScales];
 
-  // brow_q: the staged rows (stage_rows_n); brow_s[i]: the scale row of the
-  // tile of scale dword tid + THREADS*i
-  __device__ __forceinline__ void load(const gptr (&brow_q)[stage_rows_n<NB, FP6>()], const gptr (&brow_s)[kScales],
-                                       int sg, int nks, int n_sg) {
+  __device__ __forceinline__ void load(gptr brow_q, const gptr (&brow_s)[kScales], int sg, int nks, int n_sg) {
     const int tid = opaque_tid();
-    if constexpr (FP6) {
-      // lane l: 12 bytes at chunk offset 12 l = k-step l / 16, byte 12 (l % 16)
-      const int l = tid & 63;
-      const uint32_t off = (uint32_t)min(4 * sg + (l >> 4), nks - 1) * 192 + 12 * (l & 15);
-      const uint64_t rp = (uint64_t)brow_q[0];
-      const uint32_t lo = (uint32_t)rp, hi = (uint32_t)(rp >> 32);
+    // lane l: kLoadBytes at row chunk offset l * kLoadBytes = k-step l / 16
+    // (clamped: past the end any valid step, never multiplied), byte (l % 16) * kLoadBytes
+    const int l = tid & 63;
+    const uint32_t off = (uint32_t)min(4 * sg + (l >> 4), nks - 1) * L::kStepBytes + L::kLoadBytes * (l & 15);
+    const uint64_t rp = (uint64_t)brow_q;
+    const uint32_t lo = (uint32_t)rp, hi = (uint32_t)(rp >> 32);
 #pragma unroll
-      for (int i = 0; i < kPieces; ++i) {
-        // (each half as uint32_t: a signed low word would sign-extend into the high one)
-        const uint32_t rlo = (uint32_t)__builtin_amdgcn_readlane((int)lo, i);
-        const uint32_t rhi = (uint32_t)__builtin_amdgcn_readlane((int)hi, i);
-        const gptr row = (gptr)(((uint64_t)rhi << 32) | rlo);
-        q3[i] = *(const __attribute__((address_space(1))) u32x3*)(row + off);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < kPieces; ++m) {
-        const int tile = (THREADS * m) >> 10;
-        const int p = (tid + THREADS * m) & 1023;
-        const int j = p >> 8, t = (p >> 7) & 1, h = (p >> 6) & 1, g = (p >> 4) & 3;
-        const int ks = min(4 * sg + j, nks - 1);  // past the end: any valid step (never multiplied)
-        q[m] = *(const __attribute__((address_space(1))) u32x4*)(brow_q[tile] + (size_t)ks * 256 + g * 64 + t * 32 +
-                                                                 h * 16);
-      }
+    for (int i = 0; i < kRows; ++i) {
+      // (each half as uint32_t: a signed low word would sign-extend into the high one)
+      const uint32_t rlo = (uint32_t)__builtin_amdgcn_readlane((int)lo, i);
+      const uint32_t rhi = (uint32_t)__builtin_amdgcn_readlane((int)hi, i);
+      const gptr row = (gptr)(((uint64_t)rhi << 32) | rlo);
+      q[i] = *(const __attribute__((address_space(1))) Piece*)(row + off);
     }
 #pragma unroll
     for (int i = 0; i < kScales; ++i) {
@@ -168,21 +145,16 @@ struct ChunkStage {
   }
 
   __device__ __forceinline__ void store(uint8_t* buf) const {
-    const int tid = threadIdx.x;
-    if constexpr (FP6) {
-      const int wave = tid >> 6, l = tid & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
 #pragma unroll
-      for (int i = 0; i < kPieces; ++i) {
-        uint32_t* dst = (uint32_t*)(buf + (8 * wave + i) * kFp6RowStride + 12 * l);
-        dst[0] = q3[i][0];
-        dst[1] = q3[i][1];
-        dst[2] = q3[i][2];
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < kPieces; ++m) {
-        const int tile = (THREADS * m) >> 10;
-        *(u32x4*)(buf + tile * kChunkBytes + ((tid + THREADS * m) & 1023) * 16) = q[m];
+    for (int i = 0; i < kRows; ++i) {
+      uint8_t* dst = buf + (kRows * wave + i) * L::kStride + L::kLoadBytes * l;
+      if constexpr (FP6) {
+        ((uint32_t*)dst)[0] = q[i][0];
+        ((uint32_t*)dst)[1] = q[i][1];
+        ((uint32_t*)dst)[2] = q[i][2];
+      } else {
+        *(u32x4*)dst = q[i];
       }
     }
 #pragma unroll
@@ -234,18 +206,17 @@ __device__ __forceinline__ void load_wscales(uint32_t (&sa)[NA], const gptr (&ws
 // covered by MFMA work.
 template <int J, int NB, bool FP6>
 __device__ __forceinline__ v8i read_b(const uint8_t* chunk, int i) {
-  const int lane = threadIdx.x & 63, tt = i % NB, t = i / NB;
+  const int lane = threadIdx.x & 63, tt = i % NB, t = i / NB, col = lane & 15, g = lane >> 4;
   if constexpr (FP6) {
-    const int col = lane & 15, g = lane >> 4;
-    const uint8_t* c = chunk + (16 * tt + col) * kFp6RowStride + J * 192 + t * 96;
+    const uint8_t* c = chunk + (16 * tt + col) * RowLayout<true>::kStride + J * 192 + t * 96;
     const u32x2 w0 = *(const u32x2*)(c + g * 16);
     const u32x2 w1 = *(const u32x2*)(c + g * 16 + 8);
     const u32x2 w2 = *(const u32x2*)(c + 64 + g * 8);
     return v8i{(int)w0[0], (int)w0[1], (int)w1[0], (int)w1[1], (int)w2[0], (int)w2[1], 0, 0};
   } else {
-    const uint8_t* c = chunk + tt * kChunkBytes + (J * 2 + t) * 2048 + lane * 16;
+    const uint8_t* c = chunk + (16 * tt + col) * RowLayout<false>::kStride + J * 256 + g * 64 + t * 32;
     const u32x4 lo = *(const u32x4*)c;
-    const u32x4 hi = *(const u32x4*)(c + 1024);
+    const u32x4 hi = *(const u32x4*)(c + 16);
     return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   }
 }
@@ -273,7 +244,7 @@ __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chun
 template <int NA, int NB, int NS, bool FP6 = false>
 struct UnitSrc {
   gptr aq[NA], as[NA];
-  gptr brow_q[stage_rows_n<NB, FP6>()];
+  gptr brow_q;
   gptr brow_s[NS];
 };
 
@@ -374,49 +345,32 @@ __device__ __forceinline__ void mainloop(const UnitSrc<NA, NB, ChunkStage<THREAD
 }
 
 // Rows staged by this thread, as positions in the unit's group (padding
-// positions past its rows reuse the group's first row): slots 0 ..
-// stage_rows_n()-1 are the staged rows (FP8: column tid % 16 of tile k; FP6: row
-// 8 * wave + lane % 8), FP6 adds the row of each scale dword (FP8 takes them
-// from the staged rows).
-template <int THREADS, int NB, bool FP6>
+// positions past its rows reuse the group's first row): slot 0 is the row
+// rows_per_wave * wave + lane % rows_per_wave (lane i < rows_per_wave holds
+// the row of the wave's i-th load), slots 1.. the row of each scale dword.
+template <int THREADS, int NB>
 __host__ __device__ constexpr int row_slots() {
-  return FP6 ? 1 + (128 * NB + THREADS - 1) / THREADS : NB;
+  return 1 + (128 * NB + THREADS - 1) / THREADS;
 }
 
-template <int THREADS, int NB, bool FP6>
+template <int THREADS, int NB>
 __device__ __forceinline__ int slot_pos(int k) {
+  constexpr int R = rows_per_wave<THREADS, NB>();
   const int tid = opaque_tid();
-  if constexpr (FP6) {
-    if (k == 0) return 8 * (tid >> 6) + (tid & 7);
-    return 16 * min((tid + THREADS * (k - 1)) >> 7, NB - 1) + (tid & 15);
-  } else {
-    return 16 * k + (tid & 15);
-  }
+  if (k == 0) return R * (tid >> 6) + (tid & (R - 1));
+  return 16 * min((tid + THREADS * (k - 1)) >> 7, NB - 1) + (tid & 15);
 }
 
 __device__ __forceinline__ int group_pair(const Group& g, int c) { return g.p0 + (c < g.cnt ? c : 0); }
 
 // Row pointers from the rows (token rows of x, or pair rows of h) of the slots.
 template <int THREADS, int NB, int NA, bool FP6>
-__device__ __forceinline__ void row_ptrs(const ExpertArgs& a, const int (&row)[row_slots<THREADS, NB, FP6>()], int K,
+__device__ __forceinline__ void row_ptrs(const ExpertArgs& a, const int (&row)[row_slots<THREADS, NB>()], int K,
                                          UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& src) {
-  constexpr int NS = ChunkStage<THREADS, NB>::kScales;
-  if constexpr (FP6) {
-    src.brow_q[0] = to_global(a.aq) + (size_t)row[0] * split_q_row_bytes(K);
+  src.brow_q = to_global(a.aq) + (size_t)row[0] * split_q_row_bytes(K);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) src.brow_s[i] = to_global(a.as) + (size_t)row[1 + i] * split_s_row_bytes(K);
-  } else {
-#pragma unroll
-    for (int tt = 0; tt < NB; ++tt) src.brow_q[tt] = to_global(a.aq) + (size_t)row[tt] * split_q_row_bytes(K);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int t = min((opaque_tid() + THREADS * i) >> 7, NB - 1);
-      int r = row[0];
-#pragma unroll
-      for (int tt = 1; tt < NB; ++tt) r = t == tt ? row[tt] : r;
-      src.brow_s[i] = to_global(a.as) + (size_t)r * split_s_row_bytes(K);
-    }
-  }
+  for (int i = 0; i < ChunkStage<THREADS, NB>::kScales; ++i)
+    src.brow_s[i] = to_global(a.as) + (size_t)row[1 + i] * split_s_row_bytes(K);
 }
 
 // pair_rows: the activation rows are in pair order (h for down); otherwise
@@ -425,11 +379,11 @@ __device__ __forceinline__ void row_ptrs(const ExpertArgs& a, const int (&row)[r
 template <int THREADS, int NB, int NA, bool FP6>
 __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Group g, int K, bool shared, bool pair_rows,
                                            UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& src) {
-  constexpr int NR = row_slots<THREADS, NB, FP6>();
+  constexpr int NR = row_slots<THREADS, NB>();
   int row[NR];
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
-    const int p = group_pair(g, slot_pos<THREADS, NB, FP6>(k));
+    const int p = group_pair(g, slot_pos<THREADS, NB>(k));
     row[k] = pair_rows ? p : (shared ? p - a.P : to_global(a.perm)[p] / a.k);
   }
   row_ptrs<THREADS, NB, NA, FP6>(a, row, K, src);
@@ -807,7 +761,7 @@ template <int NA, int WAVES, bool GU>
 __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
   constexpr int NB = 4, RING = 4, kThreads = 64 * WAVES, NS = ChunkStage<kThreads, NB>::kScales;
   constexpr int kFeatWave = 16 * (GU ? NA / 2 : NA), kFeatUnit = WAVES * kFeatWave;
-  constexpr int kBuf = chunk_buf_bytes<NB, true>(), NR = row_slots<kThreads, NB, true>();
+  constexpr int kBuf = chunk_buf_bytes<NB, true>(), NR = row_slots<kThreads, NB>();
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * kBuf
   __shared__ int s_claim[2];
   const int n_fb = a.R / kFeatUnit, n_units = *a.n_groups * n_fb;
@@ -869,7 +823,7 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
     int row[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-      const int p = group_pair(gq, slot_pos<kThreads, NB, true>(k));
+      const int p = group_pair(gq, slot_pos<kThreads, NB>(k));
       row[k] = GU ? to_global(a.perm)[min(p, a.P - 1)] : p;
     }
 #pragma unroll
@@ -889,7 +843,7 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
       for (int sg = 0; sg < n_sg; ++sg) {
         const bool in = sg + 1 < n_sg;
         UnitSrc<NA, NB, NS, true> cs;
-        cs.brow_q[0] = in ? cur.brow_q[0] : nxt.brow_q[0];
+        cs.brow_q = in ? cur.brow_q : nxt.brow_q;
 #pragma unroll
         for (int i = 0; i < NS; ++i) cs.brow_s[i] = in ? cur.brow_s[i] : nxt.brow_s[i];
         k_group<0, RING, NA, kThreads, NB, false, true>(f, stage, sa, sa_n, cur, sg, nks, n_sg, acc,
@@ -911,7 +865,7 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
     if constexpr (GU) {
       const bool sh = gq.e == A.E;
 #pragma unroll
-      for (int k = 0; k < NR; ++k) row[k] = sh ? group_pair(gq, slot_pos<kThreads, NB, true>(k)) - A.P : row[k] / A.k;
+      for (int k = 0; k < NR; ++k) row[k] = sh ? group_pair(gq, slot_pos<kThreads, NB>(k)) - A.P : row[k] / A.k;
       row_ptrs<kThreads, NB, NA, true>(A, row, A.K, nxt);
       stage.load(nxt.brow_q, nxt.brow_s, opaque(0), nks, n_sg);
     }
