@@ -499,6 +499,133 @@ __device__ __forceinline__ void write_h_fp6(const ExpertArgs& a, const Group g, 
   }
 }
 
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+
+// gfx950's FP6 conversions of one 32-value block at a power-of-two scale.
+// fp6_pack32: code j = E2M3 of v_j / scale, rounded to nearest (ties to even)
+// and saturating at 7.5, exactly the rounding of e2m3_round (checked on the
+// instruction over a sweep of [-16, 16] at scales 1/2, 1 and 2); position j
+// takes ev[j / 2] for even j and od[j / 2] for odd j, value j at bits 6j of
+// the 6 result dwords (the scaled MFMA's 6-bit operand).  The result is
+// marked early-clobber: the instruction writes its destination before it has
+// read all 32 source registers, so the two must not overlap (a destination
+// placed over the last two source registers converted stale values).
+__device__ __forceinline__ u32x6 fp6_pack32(const v16f& ev, const v16f& od, float scale) {
+  u32x6 r;
+  asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(ev), "v"(od), "v"(scale));
+  return r;
+}
+
+// fp6_unpack32: the value of code j times scale, in element j (exact).
+__device__ __forceinline__ v32f fp6_unpack32(const u32x6& codes, float scale) {
+  v32f d;
+  asm("v_cvt_scalef32_pk32_f32_fp6 %0, %1, %2" : "=&v"(d) : "v"(codes), "v"(scale));
+  return d;
+}
+
+// Swaps of 32-bit values between lane groups of 16 ("rows"): after swap32,
+// rows 2-3 of x and rows 0-1 of y are exchanged; after swap16, rows 1 and 3
+// of x and rows 0 and 2 of y.
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(s[0]);
+  y = __uint_as_float(s[1]);
+}
+__device__ __forceinline__ void swap16(float& x, float& y) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(s[0]);
+  y = __uint_as_float(s[1]);
+}
+
+// Tall gate/up epilogue (4 column tiles, FP6 h): for each 32-feature block of
+// the wave, lane (col, grp) first forms h of token 16c + col for every column
+// tile c (8 values: features 4grp..4grp+3 and 16+4grp..+3 of the block).  A
+// 4 x 4 exchange over the lane rows (two rounds of permlane swaps) then gives
+// lane (col, r) the whole block of token 16r + col: slot q holds what row q
+// had for tile r.  Each lane splits its block into two E2M3 terms with the
+// hardware conversions (term 2 rounds the exact residual of term 1) and
+// stores them as its operand dwords.  The codes and scales are those of the
+// per-value software split (write_h_fp6), bit for bit, for every block whose
+// largest |h| is at least 2^-124 (smaller blocks take the smallest normal
+// scale, 2^-126, instead of 2^-127).
+template <int TPM>
+__device__ __forceinline__ void gateup_epilogue_tall(const ExpertArgs& a, const Group g, int f0,
+                                                     const v4f (&acc)[2 * TPM][4]) {
+  const int lane = opaque_tid() & 63, col = lane & 15, r = lane >> 4;
+  const int n_sg_h = (a.R / 128 + 3) / 4;
+  const float L = a.limit;
+#pragma unroll
+  for (int b = 0; b < TPM / 2; ++b) {
+    const int blk_h = f0 / 32 + b;
+    float h[4][8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          float gv = acc[2 * b + tt][c][ii], uv = acc[TPM + 2 * b + tt][c][ii];
+          if (L > 0.f) {
+            gv = fminf(gv, L);
+            uv = fminf(fmaxf(uv, -L), L);
+          }
+          h[c][tt * 4 + ii] = gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv;  // silu with a 1-ulp reciprocal
+        }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      swap32(h[0][k], h[2][k]);
+      swap32(h[1][k], h[3][k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      swap16(h[0][k], h[1][k]);
+      swap16(h[2][k], h[3][k]);
+    }
+    // h[q][k]: feature 4q + k (k < 4) or 16 + 4q + k - 4 (k >= 4) of the block
+    v16f ev, od;
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = k < 4 ? 4 * q + k : 12 + 4 * q + k;
+        if (j & 1)
+          od[j >> 1] = h[q][k];
+        else
+          ev[j >> 1] = h[q][k];
+        amax = fmaxf(amax, fabsf(h[q][k]));
+      }
+    const int e1 = max(fp6_exponent(amax), -126);
+    const float s1 = ldexpf(1.f, e1);
+    const u32x6 t1 = fp6_pack32(ev, od, s1);
+    const v32f d1 = fp6_unpack32(t1, s1);
+    float amax2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ev[i] -= d1[2 * i];
+      od[i] -= d1[2 * i + 1];
+      amax2 = fmaxf(amax2, fmaxf(fabsf(ev[i]), fabsf(od[i])));
+    }
+    const int e2 = max(fp6_exponent(amax2), -126);
+    const u32x6 t2 = fp6_pack32(ev, od, ldexpf(1.f, e2));
+    if (16 * r + col < g.cnt) {
+      const size_t p = (size_t)g.p0 + 16 * r + col;
+      __attribute__((address_space(1))) uint8_t* dst =
+          to_global(a.hq) + p * split_q_row_bytes(a.R) + (size_t)(blk_h >> 2) * kFp6StepBytes;
+      const int gb = blk_h & 3;
+      *(__attribute__((address_space(1))) u32x4*)(dst + 16 * gb) = u32x4{t1[0], t1[1], t1[2], t1[3]};
+      *(__attribute__((address_space(1))) u32x2*)(dst + 64 + 8 * gb) = u32x2{t1[4], t1[5]};
+      *(__attribute__((address_space(1))) u32x4*)(dst + kFp6TermBytes + 16 * gb) = u32x4{t2[0], t2[1], t2[2], t2[3]};
+      *(__attribute__((address_space(1))) u32x2*)(dst + kFp6TermBytes + 64 + 8 * gb) = u32x2{t2[4], t2[5]};
+      __attribute__((address_space(1))) uint8_t* srow = to_global(a.hs) + p * split_s_row_bytes(a.R);
+      srow[split_scale_offset(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
+      srow[split_scale_offset(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
+    }
+  }
+}
+
 // gate/up epilogue: h of this wave's features [f0, f0 + 16 TPM) for the rows
 // of group g, from the gate (acc[0..TPM)) and up (acc[TPM..2TPM)) sums.
 template <int TPM, int NB, bool FP6>
@@ -874,7 +1001,7 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
 #pragma unroll
     for (int i = 0; i < RING - 1; ++i) load_w<false>(f[i], nxt.aq, min(opaque(i), nks - 1));
     if constexpr (GU)
-      gateup_epilogue<NA / 2, NB, true>(A, g, f0, acc);
+      gateup_epilogue_tall<NA / 2>(A, g, f0, acc);
     else
       down_epilogue<NA, NB>(A, g, f0, acc);
     if (q < 0) break;
