@@ -205,21 +205,69 @@ __device__ __forceinline__ int fp6_exponent(float amax) {
   return e;
 }
 
-// E2M3 code of f, rounded to nearest (ties to even mantissa), and the value
-// it encodes.  With E = the binade of |f| clamped to [0, 2] (0 also for the
-// subnormal range, whose step 1/8 equals binade 0's) the code is
-// 8E + rint(|f| * 2^(3-E)): |f| * 2^(3-E) is exact, so this is the textbook
-// piecewise rounding without branches; a carry out of the mantissa lands on
-// the next binade's code.  E comes from f's exponent field, and both scalings
-// are ldexp, so no compare-and-select chain is needed.  Saturates at 7.5 (code
-// 31); the callers scale f into [-7.5, 7.5].
-__device__ __forceinline__ uint32_t e2m3_round(float f, float* value) {
-  const int E = min(max((int)__builtin_amdgcn_ubfe(__float_as_uint(f), 23, 8) - 127, 0), 2);
-  const float q = __builtin_rintf(ldexpf(fabsf(f), 3 - E));
-  const int code = min((int)q + 8 * E, 31);
-  const float mag = fminf(ldexpf(q, E - 3), 7.5f);
-  *value = f < 0.f ? -mag : mag;
-  return (uint32_t)code | (f < 0.f ? 0x20u : 0u);
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+
+// gfx950's FP6 conversions of one 32-value block at a power-of-two scale.
+// fp6_pack32: code j = E2M3 of v_j / scale, rounded to nearest with ties to
+// the even code and saturating at 7.5 (measured on the instruction over a
+// sweep of [-16, 16] at scales 1/2, 1 and 2: every code was the
+// round-to-nearest-even one); position j takes ev[j / 2] for even j and
+// od[j / 2] for odd j, value j at bits 6j of the 6 result dwords (the scaled
+// MFMA's 6-bit operand).  The result is marked early-clobber: the
+// instruction writes its destination before it has read all 32 source
+// registers, so the two must not overlap (a destination placed over the last
+// two source registers converted stale values).
+__device__ __forceinline__ u32x6 fp6_pack32(const v16f& ev, const v16f& od, float scale) {
+  u32x6 r;
+  asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(ev), "v"(od), "v"(scale));
+  return r;
+}
+
+// fp6_unpack32: the value of code j times scale, in element j (exact).
+__device__ __forceinline__ v32f fp6_unpack32(const u32x6& codes, float scale) {
+  v32f d;
+  asm("v_cvt_scalef32_pk32_f32_fp6 %0, %1, %2" : "=&v"(d) : "v"(codes), "v"(scale));
+  return d;
+}
+
+// Two-term E2M3 split of one 32-value block (values at even positions in ev,
+// odd in od): term 1 = fp6_pack32 at scale 2^e1 with the block maximum inside
+// E2M3's range, term 2 = the exact residual v - term 1, split the same way.
+// The exponents are clamped below at -126, so each scale is a normal fp32.
+// On return ev/od hold the residuals.
+__device__ __forceinline__ void split_fp6_32(v16f& ev, v16f& od, u32x6* t1, u32x6* t2, int* e1, int* e2) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(ev[i]), fabsf(od[i])));
+  *e1 = max(fp6_exponent(amax), -126);
+  const float s1 = ldexpf(1.f, *e1);
+  *t1 = fp6_pack32(ev, od, s1);
+  const v32f d1 = fp6_unpack32(*t1, s1);
+  float amax2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ev[i] -= d1[2 * i];
+    od[i] -= d1[2 * i + 1];
+    amax2 = fmaxf(amax2, fmaxf(fabsf(ev[i]), fabsf(od[i])));
+  }
+  *e2 = max(fp6_exponent(amax2), -126);
+  *t2 = fp6_pack32(ev, od, ldexpf(1.f, *e2));
+}
+
+// Swaps of 32-bit values between lane groups of 16 ("rows"), gfx950's
+// permlane swaps: after swap32, rows 2-3 of x and rows 0-1 of y are
+// exchanged; after swap16, rows 1 and 3 of x and rows 0 and 2 of y.
+__device__ __forceinline__ void swap32(float& x, float& y) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(s[0]);
+  y = __uint_as_float(s[1]);
+}
+__device__ __forceinline__ void swap16(float& x, float& y) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  x = __uint_as_float(s[0]);
+  y = __uint_as_float(s[1]);
 }
 
 template <int kOff>

@@ -428,128 +428,14 @@ __device__ __forceinline__ void weight_ptrs(const ExpertArgs& a, const Group& g,
 // same rows of the up matrix: 16*TPM features per wave, 16*TPM*WAVES per work
 // unit.
 
-// The 24-bit run of four E2M3 codes of v[0..3] * inv (value i at bits 6i);
-// rv[i] = the value of code i (unscaled).
-__device__ __forceinline__ uint32_t e2m3_run4(const float* v, float inv, float* rv) {
-  uint32_t run = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) run |= e2m3_round(v[i] * inv, &rv[i]) << (6 * i);
-  return run;
-}
-
-// Tall units write h as the two-term FP6 split (the x split's FP6 layout, K =
-// I).  Lane (col, grp) holds values 4grp..4grp+3 and 16+4grp..+3 of block
-// blk_h of token column col: 24-bit runs at bits 24grp and 96+24grp of the
-// block's 192-bit operand.  The four lanes of a column exchange their runs;
-// lane grp then stores term grp/2, plane grp%2 (dwords 0-3 or 4-5).
-__device__ __forceinline__ void write_h_fp6(const ExpertArgs& a, const Group g, int c, int col, int grp, int blk_h,
-                                            int n_sg_h, const float (&h)[8], float amax) {
-  const int e1 = fp6_exponent(amax);
-  const float inv1 = ldexpf(1.f, -e1), sc1 = ldexpf(1.f, e1);
-  uint32_t run[2][2];  // [term][half]
-  float res[8];
-  float amax2 = 0.f;
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    run[0][hh] = e2m3_run4(h + 4 * hh, inv1, res + 4 * hh);
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      res[4 * hh + ii] = h[4 * hh + ii] - res[4 * hh + ii] * sc1;
-      amax2 = fmaxf(amax2, fabsf(res[4 * hh + ii]));
-    }
-  }
-  amax2 = shfl_xor_max<16>(amax2);
-  amax2 = shfl_xor_max<32>(amax2);
-  const int e2 = fp6_exponent(amax2);
-  const float inv2 = ldexpf(1.f, -e2);
-  float unused[8];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) run[1][hh] = e2m3_run4(res + 4 * hh, inv2, unused + 4 * hh);
-  // r[t][hh][q]: run of lane col + 16q
-  uint32_t r[2][2][4];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) r[t][hh][q] = (uint32_t)__shfl((int)run[t][hh], col + 16 * q, 64);
-  if (16 * c + col < g.cnt) {
-    const int t = grp >> 1;
-    uint32_t D[6];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const uint32_t* q = t ? r[1][hh] : r[0][hh];
-      D[3 * hh] = q[0] | (q[1] << 24);
-      D[3 * hh + 1] = (q[1] >> 8) | (q[2] << 16);
-      D[3 * hh + 2] = (q[2] >> 16) | (q[3] << 8);
-    }
-    const size_t p = (size_t)g.p0 + 16 * c + col;
-    __attribute__((address_space(1))) uint8_t* dst =
-        to_global(a.hq) + p * split_q_row_bytes(a.R) + (size_t)(blk_h >> 2) * kFp6StepBytes + t * kFp6TermBytes;
-    const int bb = blk_h & 3;
-    if (grp & 1)
-      *(__attribute__((address_space(1))) u32x2*)(dst + 64 + 8 * bb) = u32x2{D[4], D[5]};
-    else
-      *(__attribute__((address_space(1))) u32x4*)(dst + 16 * bb) = u32x4{D[0], D[1], D[2], D[3]};
-    if (grp == 0) {
-      __attribute__((address_space(1))) uint8_t* srow = to_global(a.hs) + p * split_s_row_bytes(a.R);
-      srow[split_scale_offset(0, blk_h, n_sg_h)] = (uint8_t)(e1 + 127);
-      srow[split_scale_offset(1, blk_h, n_sg_h)] = (uint8_t)(e2 + 127);
-    }
-  }
-}
-
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef float v32f __attribute__((ext_vector_type(32)));
-typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
-
-// gfx950's FP6 conversions of one 32-value block at a power-of-two scale.
-// fp6_pack32: code j = E2M3 of v_j / scale, rounded to nearest (ties to even)
-// and saturating at 7.5, exactly the rounding of e2m3_round (checked on the
-// instruction over a sweep of [-16, 16] at scales 1/2, 1 and 2); position j
-// takes ev[j / 2] for even j and od[j / 2] for odd j, value j at bits 6j of
-// the 6 result dwords (the scaled MFMA's 6-bit operand).  The result is
-// marked early-clobber: the instruction writes its destination before it has
-// read all 32 source registers, so the two must not overlap (a destination
-// placed over the last two source registers converted stale values).
-__device__ __forceinline__ u32x6 fp6_pack32(const v16f& ev, const v16f& od, float scale) {
-  u32x6 r;
-  asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(ev), "v"(od), "v"(scale));
-  return r;
-}
-
-// fp6_unpack32: the value of code j times scale, in element j (exact).
-__device__ __forceinline__ v32f fp6_unpack32(const u32x6& codes, float scale) {
-  v32f d;
-  asm("v_cvt_scalef32_pk32_f32_fp6 %0, %1, %2" : "=&v"(d) : "v"(codes), "v"(scale));
-  return d;
-}
-
-// Swaps of 32-bit values between lane groups of 16 ("rows"): after swap32,
-// rows 2-3 of x and rows 0-1 of y are exchanged; after swap16, rows 1 and 3
-// of x and rows 0 and 2 of y.
-__device__ __forceinline__ void swap32(float& x, float& y) {
-  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  x = __uint_as_float(s[0]);
-  y = __uint_as_float(s[1]);
-}
-__device__ __forceinline__ void swap16(float& x, float& y) {
-  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  x = __uint_as_float(s[0]);
-  y = __uint_as_float(s[1]);
-}
-
 // Tall gate/up epilogue (4 column tiles, FP6 h): for each 32-feature block of
 // the wave, lane (col, grp) first forms h of token 16c + col for every column
 // tile c (8 values: features 4grp..4grp+3 and 16+4grp..+3 of the block).  A
 // 4 x 4 exchange over the lane rows (two rounds of permlane swaps) then gives
 // lane (col, r) the whole block of token 16r + col: slot q holds what row q
 // had for tile r.  Each lane splits its block into two E2M3 terms with the
-// hardware conversions (term 2 rounds the exact residual of term 1) and
-// stores them as its operand dwords.  The codes and scales are those of the
-// per-value software split (write_h_fp6), bit for bit, for every block whose
-// largest |h| is at least 2^-124 (smaller blocks take the smallest normal
-// scale, 2^-126, instead of 2^-127).
+// hardware conversions (split_fp6_32) and stores them as its operand dwords
+// (the x split's FP6 layout, K = I).
 template <int TPM>
 __device__ __forceinline__ void gateup_epilogue_tall(const ExpertArgs& a, const Group g, int f0,
                                                      const v4f (&acc)[2 * TPM][4]) {
@@ -585,7 +471,6 @@ __device__ __forceinline__ void gateup_epilogue_tall(const ExpertArgs& a, const 
     }
     // h[q][k]: feature 4q + k (k < 4) or 16 + 4q + k - 4 (k >= 4) of the block
     v16f ev, od;
-    float amax = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -595,21 +480,10 @@ __device__ __forceinline__ void gateup_epilogue_tall(const ExpertArgs& a, const 
           od[j >> 1] = h[q][k];
         else
           ev[j >> 1] = h[q][k];
-        amax = fmaxf(amax, fabsf(h[q][k]));
       }
-    const int e1 = max(fp6_exponent(amax), -126);
-    const float s1 = ldexpf(1.f, e1);
-    const u32x6 t1 = fp6_pack32(ev, od, s1);
-    const v32f d1 = fp6_unpack32(t1, s1);
-    float amax2 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      ev[i] -= d1[2 * i];
-      od[i] -= d1[2 * i + 1];
-      amax2 = fmaxf(amax2, fmaxf(fabsf(ev[i]), fabsf(od[i])));
-    }
-    const int e2 = max(fp6_exponent(amax2), -126);
-    const u32x6 t2 = fp6_pack32(ev, od, ldexpf(1.f, e2));
+    u32x6 t1, t2;
+    int e1, e2;
+    split_fp6_32(ev, od, &t1, &t2, &e1, &e2);
     if (16 * r + col < g.cnt) {
       const size_t p = (size_t)g.p0 + 16 * r + col;
       __attribute__((address_space(1))) uint8_t* dst =
@@ -658,10 +532,6 @@ __device__ __forceinline__ void gateup_epilogue(const ExpertArgs& a, const Group
     for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(h[j]));
     amax = shfl_xor_max<16>(amax);
     amax = shfl_xor_max<32>(amax);
-    if constexpr (FP6) {
-      write_h_fp6(a, g, c, col, grp, blk_h, n_sg_h, h, amax);
-      continue;
-    }
     const int e1 = split_exponent(amax);
     const float inv1 = ldexpf(1.f, -e1), sc1 = ldexpf(1.f, e1);
     uint32_t w1[2], w2[2];

@@ -55,49 +55,14 @@ __device__ __forceinline__ void split_block32(const float* v, uint32_t* q /*16 d
 
 // ---------------------------------------------------------------------------
 // Two-term FP6 (E2M3) split, used for batches of tall work units: v ~= q1 *
-// 2^e1 + q2 * 2^e2 with q1, q2 E2M3 (the same scheme as the FP8 split; the
-// second term leaves a residual of about 2^-10 of the block maximum).
+// 2^e1 + q2 * 2^e2 with q1, q2 E2M3 (the same scheme as the FP8 split, made
+// by the hardware conversions of split_fp6_32; the second term leaves a
+// residual of about 2^-10 of the block maximum).
 //
 // Row layout: k-step ks occupies 192 bytes at ks*192 (inside a row of the FP8
 // split's length), term t at t*96 as two planes of the lane groups' 6-dword
 // operands: dwords 0-3 of group g at g*16, dwords 4-5 at 64 + g*8.  Group g
 // = the 32-block 4ks+g.  Scales as for the FP8 split.
-
-// E2M3 codes of v[i] * inv for 32 values, packed as the operand bitstream
-// (6 dwords, value i at bits 6i..6i+5); rv[i] = the value of code i (unscaled).
-__device__ __forceinline__ void pack_fp6_block(const float* v, float inv, uint32_t* q /*6 dwords*/, float* rv) {
-#pragma unroll
-  for (int w = 0; w < 6; ++w) q[w] = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint32_t c = e2m3_round(v[i] * inv, &rv[i]);
-    const int bit = 6 * i, w = bit >> 5, sh = bit & 31;
-    q[w] |= c << sh;
-    if (sh > 26) q[w + 1] |= c >> (32 - sh);
-  }
-}
-
-__device__ __forceinline__ void split_block32_fp6(const float* v, uint32_t* q /*12 dwords*/, int* e1_out,
-                                                  int* e2_out) {
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const int e1 = fp6_exponent(amax);
-  float r[32];
-  pack_fp6_block(v, ldexpf(1.f, -e1), q, r);
-  const float sc1 = ldexpf(1.f, e1);
-  float amax2 = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    r[i] = v[i] - r[i] * sc1;
-    amax2 = fmaxf(amax2, fabsf(r[i]));
-  }
-  const int e2 = fp6_exponent(amax2);
-  float unused[32];
-  pack_fp6_block(r, ldexpf(1.f, -e2), q + 6, unused);
-  *e1_out = e1;
-  *e2_out = e2;
-}
 
 // Split of one 32-value block t = row * (K/32) + block of x (t < n_rows * K/32),
 // FP6 when fp6 is set, else FP8.
@@ -118,16 +83,21 @@ __device__ __forceinline__ void split_bf16_block(const uint16_t* __restrict__ x,
     }
   }
   if (fp6) {
-    uint32_t q[12];
+    v16f ev, od;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ev[i] = v[2 * i];
+      od[i] = v[2 * i + 1];
+    }
+    u32x6 w[2];
     int e1, e2;
-    split_block32_fp6(v, q, &e1, &e2);
+    split_fp6_32(ev, od, &w[0], &w[1], &e1, &e2);
     uint8_t* step = xq + row * split_q_row_bytes(K) + (size_t)(blk >> 2) * kFp6StepBytes;
     const int g = blk & 3;
 #pragma unroll
     for (int term = 0; term < 2; ++term) {
-      const uint32_t* w = q + 6 * term;
-      *(u32x4*)(step + term * kFp6TermBytes + g * 16) = u32x4{w[0], w[1], w[2], w[3]};
-      *(uint2*)(step + term * kFp6TermBytes + 64 + g * 8) = uint2{w[4], w[5]};
+      *(u32x4*)(step + term * kFp6TermBytes + g * 16) = u32x4{w[term][0], w[term][1], w[term][2], w[term][3]};
+      *(uint2*)(step + term * kFp6TermBytes + 64 + g * 8) = uint2{w[term][4], w[term][5]};
     }
     uint8_t* srow = xs + row * split_s_row_bytes(K);
     srow[split_scale_offset(0, blk, n_sg)] = (uint8_t)(e1 + 127);

@@ -58,3 +58,58 @@ extern "C" int probe_fp8(const void* in, void* packed, void* back, int n4) {
   if (hipGetLastError() != hipSuccess) return -4;
   return hipDeviceSynchronize() == hipSuccess ? 0 : -4;
 }
+
+// Two-term FP6 split of n blocks of 32 floats (split_fp6_32, the helper the
+// prologue and the tall gate/up epilogue use): codes [n][2][6] dwords,
+// exponents [n][2], residual after term 1 [n][32] (ev/od interleaved back).
+__global__ void probe_fp6_kernel(const float* in, uint32_t* codes, int* exps, float* res, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  v16f ev, od;
+  for (int j = 0; j < 16; ++j) {
+    ev[j] = in[32 * i + 2 * j];
+    od[j] = in[32 * i + 2 * j + 1];
+  }
+  u32x6 t1, t2;
+  int e1, e2;
+  split_fp6_32(ev, od, &t1, &t2, &e1, &e2);
+  for (int j = 0; j < 6; ++j) {
+    codes[12 * i + j] = t1[j];
+    codes[12 * i + 6 + j] = t2[j];
+  }
+  exps[2 * i] = e1;
+  exps[2 * i + 1] = e2;
+  for (int j = 0; j < 16; ++j) {
+    res[32 * i + 2 * j] = ev[j];
+    res[32 * i + 2 * j + 1] = od[j];
+  }
+}
+
+// swap32 and swap16 on one wave: in [2][64] (x then y), out [4][64]
+// (x, y after swap32; x, y after swap16, each from the inputs).
+__global__ void probe_swap_kernel(const float* in, float* out) {
+  const int l = threadIdx.x;
+  float x = in[l], y = in[64 + l];
+  swap32(x, y);
+  out[l] = x;
+  out[64 + l] = y;
+  x = in[l];
+  y = in[64 + l];
+  swap16(x, y);
+  out[128 + l] = x;
+  out[192 + l] = y;
+}
+
+extern "C" int probe_fp6(const void* in, void* codes, void* exps, void* res, int n) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(probe_fp6_kernel, dim3((n + 63) / 64), dim3(64), 0, 0, (const float*)in, (uint32_t*)codes,
+                     (int*)exps, (float*)res, n);
+  if (hipGetLastError() != hipSuccess) return -4;
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -4;
+}
+
+extern "C" int probe_swap(const void* in, void* out) {
+  hipLaunchKernelGGL(probe_swap_kernel, dim3(1), dim3(64), 0, 0, (const float*)in, (float*)out);
+  if (hipGetLastError() != hipSuccess) return -4;
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -4;
+}

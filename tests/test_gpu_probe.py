@@ -15,6 +15,12 @@
     its error stayed below 2^-11 of the largest single product of the output
     (the bound checked here is 2^-10), which a wrong layout exceeds by far.
 - v_cvt_pk_fp8_f32 rounds to the nearest E4M3 value (ties to even).
+- The two-term FP6 split of a 32-value block (v_cvt_scalef32_2xpk16_fp6_f32
+  and its unpack, as the prologue and the tall gate/up epilogue use them):
+  codes are the nearest E2M3 values of v / 2^e (ties to the even code),
+  value j at bits 6j of the operand, term 2 rounds the exact fp32 residual of
+  term 1, and the exponents put each block maximum in (3.75, 7.5].
+- permlane32/permlane16 swaps exchange the documented lane rows.
 - moe_pack_mxfp4 produces the packed layout described in the C header.
 Expected values come from independent numpy decoders written here.
 """
@@ -37,6 +43,8 @@ def _lib():
     L = ctypes.CDLL(PROBE)
     L.probe_mfma.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int]
     L.probe_fp8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int]
+    L.probe_fp6.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int]
+    L.probe_swap.argtypes = [ctypes.c_void_p] * 2
     return L
 
 
@@ -199,3 +207,90 @@ def test_pack_layout_matches_header():
                             ks = 4 * sg + j
                             want = s[m, 16 * rt + lane % 16, 4 * ks + lane // 16] if ks < nks else 127
                             assert qo is not None and so[off + j] == want
+
+
+def e2m3(codes):
+    codes = codes.astype(np.int64)
+    sign = np.where(codes & 32, -1.0, 1.0)
+    E, M = (codes >> 3) & 3, codes & 7
+    return sign * np.where(E == 0, M / 8.0, np.ldexp(1.0 + M / 8.0, E - 1))
+
+
+def e2m3_nearest(x):
+    """Nearest E2M3 code of each value (ties to the even code), saturating at 7.5."""
+    grid = e2m3(np.arange(32))  # non-negative codes 0..31, increasing
+    a = np.minimum(np.abs(x), 7.5)
+    d = np.abs(a[:, None] - grid[None, :])
+    best = d.min(1, keepdims=True)
+    cand = np.where(d == best, np.arange(32)[None, :], 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(1)
+    code = np.where(even < 99, even, cand.min(1))
+    return np.where((x < 0) & (code != 0), code | 32, code)
+
+
+def fp6_exponent(amax):
+    """Shared exponent e with amax / 2^e in (3.75, 7.5], clamped to [-126, 127] (0 for an all-zero block)."""
+    if amax <= 0:
+        return 0
+    _, ex = np.frexp(amax)
+    e = int(ex) - 3
+    if amax > np.ldexp(7.5, e):
+        e += 1
+    return min(max(e, -126), 127)
+
+
+def test_fp6_split_conversions():
+    print("probe_fp6", flush=True)
+    rng = np.random.default_rng(6)
+    grid = e2m3(np.arange(32))
+    mids = (grid[1:] + grid[:-1]) / 2  # exact ties at scale 1
+    blocks = [rng.standard_normal(32) * 2.0 ** rng.integers(-20, 20) for _ in range(200)]
+    blocks += [np.concatenate([mids, [7.5]]) * sgn for sgn in (1, -1)]  # 31 ties + the maximum: scale 2^0
+    blocks += [np.zeros(32), np.full(32, 3.0), np.linspace(-7.5, 7.5, 32) * 2.0 ** -5]
+    one_big = rng.standard_normal(32) * 2.0 ** -16
+    one_big[7] = 1.7265625
+    blocks.append(one_big)
+    x = np.stack(blocks).astype(np.float32)
+    n = x.shape[0]
+    dev = torch.device("cuda")
+    tin = torch.from_numpy(x.reshape(-1)).to(dev)
+    codes = torch.zeros(n * 12, dtype=torch.int32, device=dev)
+    exps = torch.zeros(n * 2, dtype=torch.int32, device=dev)
+    res = torch.zeros(n * 32, dtype=torch.float32, device=dev)
+    assert _lib().probe_fp6(tin.data_ptr(), codes.data_ptr(), exps.data_ptr(), res.data_ptr(), n) == 0
+    got_w = codes.cpu().numpy().view(np.uint32).reshape(n, 2, 6)
+    got_e = exps.cpu().numpy().reshape(n, 2)
+    got_r = res.cpu().numpy().reshape(n, 32)
+    for b in range(n):
+        v = x[b]
+        e1 = fp6_exponent(float(np.abs(v).max()))
+        c1 = e2m3_nearest(v.astype(np.float64) / 2.0 ** e1)
+        r = (v - (e2m3(c1) * 2.0 ** e1).astype(np.float32)).astype(np.float32)  # fp32 subtraction, as the kernel
+        e2 = fp6_exponent(float(np.abs(r).max()))
+        c2 = e2m3_nearest(r.astype(np.float64) / 2.0 ** e2)
+        assert (got_e[b, 0], got_e[b, 1]) == (e1, e2), (b, got_e[b], e1, e2)
+        assert np.array_equal(got_r[b], r), b
+        for t, c in enumerate((c1, c2)):
+            bits = sum(int(w) << (32 * i) for i, w in enumerate(got_w[b, t]))
+            fields = np.array([(bits >> (6 * j)) & 63 for j in range(32)])
+            # values compared (a value that rounds to zero may carry either sign bit)
+            assert np.array_equal(e2m3(fields), e2m3(c)), (b, t, fields, c)
+    # the ties block: every midpoint went to the even code
+    assert got_e[n - 6, 0] == 0
+
+
+def test_permlane_swaps():
+    print("probe_swap", flush=True)
+    dev = torch.device("cuda")
+    x = np.arange(64, dtype=np.float32) + 1000
+    y = np.arange(64, dtype=np.float32) + 2000
+    out = torch.zeros(256, dtype=torch.float32, device=dev)
+    assert _lib().probe_swap(torch.from_numpy(np.concatenate([x, y])).to(dev).data_ptr(), out.data_ptr()) == 0
+    o = out.cpu().numpy().reshape(4, 64)
+    x32, y32 = x.copy(), y.copy()
+    x32[32:], y32[:32] = y[:32], x[32:]
+    x16, y16 = x.copy(), y.copy()
+    for base in (0, 32):
+        x16[base + 16:base + 32], y16[base:base + 16] = y[base:base + 16], x[base + 16:base + 32]
+    assert np.array_equal(o[0], x32) and np.array_equal(o[1], y32)
+    assert np.array_equal(o[2], x16) and np.array_equal(o[3], y16)
