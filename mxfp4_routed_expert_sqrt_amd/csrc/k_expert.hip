@@ -259,13 +259,19 @@ struct UnitSrc {
 // multiplied).
 // The chunk loaded during the group is chunk cc of cs (in a unit's K loop:
 // chunk sg+1 of the unit, clamped).
+// wn (a unit's last group, when the next unit is known and nks is a multiple
+// of 4): the weight steps past the unit's end are the next unit's steps 0,
+// 1, 2, taken from wn, and the scales loaded are its first group's, so they
+// land in the ring slots and scale registers its first group reads.
 template <int GI, int RING, int NA, int THREADS, int NB, bool NT, bool FP6>
 __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB, FP6>& stage,
                                         uint32_t (&sa)[NA], uint32_t (&sa_n)[NA],
                                         const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& cur, int sg,
                                         int nks, int n_sg, v4f (&acc)[NA][NB], const uint8_t* chunk,
                                         uint8_t* next_buf,
-                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& cs, int cc) {
+                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& cs, int cc,
+                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>* wn = nullptr,
+                                        bool wpf = false) {
   const int lane = threadIdx.x & 63, last = nks - 1, k0 = 4 * sg;
   uint32_t sb[NB][2];
 #pragma unroll
@@ -274,9 +280,27 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
     sb[tt][1] = *(const uint32_t*)(chunk + scale_off<NB, FP6>(tt) + 256 + lane * 4);
   }
   // weight step loaded at position j of the group (RING-1+j steps ahead)
-  auto load_step = [&](WFrag<NA>& slot, int j) { load_w<NT>(slot, cur.aq, min(k0 + RING - 1 + j, last)); };
+  auto load_step = [&](WFrag<NA>& slot, int j) {
+    const int s = k0 + RING - 1 + j;
+    if (wn == nullptr) {
+      load_w<NT>(slot, cur.aq, min(s, last));
+    } else {
+      const bool nx = wpf && s > last;  // wave-uniform: scalar selects, no branch
+      gptr src[NA];
+#pragma unroll
+      for (int a = 0; a < NA; ++a) src[a] = nx ? wn->aq[a] : cur.aq[a];
+      load_w<NT>(slot, src, nx ? s - nks : s);
+    }
+  };
   stage.load(cs.brow_q, cs.brow_s, cc, nks, n_sg);
-  load_wscales(sa_n, cur.as, min(sg + 1, n_sg - 1));
+  if (wn == nullptr) {
+    load_wscales(sa_n, cur.as, min(sg + 1, n_sg - 1));
+  } else {
+    gptr src[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) src[a] = wpf ? wn->as[a] : cur.as[a];
+    load_wscales(sa_n, src, wpf ? 0 : min(sg + 1, n_sg - 1));
+  }
   load_step(f[(4 * GI + RING - 1) % RING], 0);
   __builtin_amdgcn_sched_barrier(0);
   mma_step<0, NA, NB, FP6>(f[(4 * GI) % RING], chunk, sa, sb, acc);
@@ -802,14 +826,12 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
   stage_rows<kThreads, NB, NA, true>(a, g, a.K, g.e == a.E, !GU, cur);
   k_start<RING, NA, kThreads, NB, false, true>(f, stage, sa, cur, nks, lds);
   // the queued unit (a workgroup's last unit queues itself: valid addresses,
-  // never used) and its work-list entry, one dword per lane (lane i % 8 holds
-  // word i), read out at the top of the loop
+  // never used): its group and feature block
   int uq = q >= 0 ? q : u;
-  int gword = entry_word(a.groups, uq / n_fb);
+  int fbq;
+  Group gq = unit_group_of(entry_from_words(entry_word(a.groups, uq / n_fb)), uq, n_fb, &fbq);
   int bp = 0;  // LDS buffer of the unit's chunk 0
   while (true) {
-    int fbq;
-    const Group gq = unit_group_of(entry_from_words(gword), uq, n_fb, &fbq);
     // claim the unit after the queued one; fetch the queued unit's rows
     // (the address goes through the opaque lane index, so the compiler does not
     // turn this one-thread atomic into a wave-wide one that waits for its
@@ -827,45 +849,42 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
     for (int i = 0; i < NA; ++i)
 #pragma unroll
       for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
+    // K loop: chunk sg of the unit is in LDS buffer (bp + sg) & 1.  The last
+    // group loads and stages the queued unit's first chunk, and, when nks is
+    // a multiple of 4, its scales and first weight steps (wpf).
     UnitSrc<NA, NB, NS, true> nxt;
-    if constexpr (GU) {
-      for (int sg = 0; sg < n_sg; ++sg)
-        k_group<0, RING, NA, kThreads, NB, false, true>(f, stage, sa, sa_n, cur, sg, nks, n_sg, acc,
-                                                        lds + (sg & 1) * kBuf, lds + ((sg + 1) & 1) * kBuf, cur,
-                                                        min(sg + 1, n_sg - 1));
-    } else {
-      // down: the queued unit's rows are pair rows, known without a load, so
-      // the last group loads and stages its first chunk (LDS buffer n_sg & 1)
-      row_ptrs<kThreads, NB, NA, true>(a, row, a.K, nxt);
-      for (int sg = 0; sg < n_sg; ++sg) {
-        const bool in = sg + 1 < n_sg;
-        UnitSrc<NA, NB, NS, true> cs;
-        cs.brow_q = in ? cur.brow_q : nxt.brow_q;
+    if constexpr (!GU) row_ptrs<kThreads, NB, NA, true>(a, row, a.K, nxt);
+    for (int sg = 0; sg + 1 < n_sg; ++sg)
+      k_group<0, RING, NA, kThreads, NB, false, true>(f, stage, sa, sa_n, cur, sg, nks, n_sg, acc,
+                                                      lds + ((bp + sg) & 1) * kBuf, lds + ((bp + sg + 1) & 1) * kBuf,
+                                                      cur, sg + 1);
+    const int f0q = fbq * kFeatUnit + wave * kFeatWave;
+    {
+      const ExpertArgs B = reload_args();
+      if constexpr (GU) {
+        // the queued unit's token rows, from the perm entries fetched at the top
+        const bool sh = gq.e == B.E;
 #pragma unroll
-        for (int i = 0; i < NS; ++i) cs.brow_s[i] = in ? cur.brow_s[i] : nxt.brow_s[i];
-        k_group<0, RING, NA, kThreads, NB, false, true>(f, stage, sa, sa_n, cur, sg, nks, n_sg, acc,
-                                                        lds + ((bp + sg) & 1) * kBuf,
-                                                        lds + ((bp + sg + 1) & 1) * kBuf, cs, in ? sg + 1 : 0);
+        for (int k = 0; k < NR; ++k) row[k] = sh ? group_pair(gq, slot_pos<kThreads, NB>(k)) - B.P : row[k] / B.k;
+        row_ptrs<kThreads, NB, NA, true>(B, row, B.K, nxt);
       }
-      bp = (bp + n_sg) & 1;
     }
+    k_group<0, RING, NA, kThreads, NB, false, true>(f, stage, sa, sa_n, cur, n_sg - 1, nks, n_sg, acc,
+                                                    lds + ((bp + n_sg - 1) & 1) * kBuf,
+                                                    lds + ((bp + n_sg) & 1) * kBuf, nxt, 0);
+    bp = (bp + n_sg) & 1;
     const ExpertArgs A = reload_args();
     if (tid == 0) s_claim[0] = q >= 0 ? resolve(t, A.pool) : -1;
     __syncthreads();
     const int q2 = s_claim[0];
-    // the unit after the queued one: its work-list entry, first of the loads
-    // issued here and read out at the top of the next iteration
+    // the unit after the queued one: its work-list entry (one dword per lane,
+    // lane i % 8 holds word i), first of the loads issued here and read out at
+    // the end of the iteration, so that its wait leaves the loads issued after
+    // it (the queued unit's weights and chunk, the epilogue's stores) in flight
     const int uq2 = q2 >= 0 ? q2 : uq;
-    gword = entry_word(A.groups, uq2 / n_fb);
-    // the queued unit's loads (gate/up: its first chunk too)
-    const int f0q = fbq * kFeatUnit + wave * kFeatWave;
-    if constexpr (GU) {
-      const bool sh = gq.e == A.E;
-#pragma unroll
-      for (int k = 0; k < NR; ++k) row[k] = sh ? group_pair(gq, slot_pos<kThreads, NB>(k)) - A.P : row[k] / A.k;
-      row_ptrs<kThreads, NB, NA, true>(A, row, A.K, nxt);
-      stage.load(nxt.brow_q, nxt.brow_s, opaque(0), nks, n_sg);
-    }
+    const int gword = entry_word(A.groups, uq2 / n_fb);
+    // the queued unit's scales and first weight steps, unless the last group
+    // loaded them
     weight_ptrs<NA, GU>(A, gq, f0q, nxt.aq, nxt.as);
     load_wscales(sa, nxt.as, opaque(0));
 #pragma unroll
@@ -875,16 +894,13 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
     else
       down_epilogue<NA, NB>(A, g, f0, acc);
     if (q < 0) break;
-    if constexpr (GU) {
-      stage.store(lds);
-      __syncthreads();
-    }
     u = q;
     g = gq;
     f0 = f0q;
     cur = nxt;
     q = q2;
     uq = uq2;
+    gq = unit_group_of(entry_from_words(gword), uq, n_fb, &fbq);
   }
 }
 
