@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOE_MXFP4_VERSION 4
+#define MOE_MXFP4_VERSION 5
 
 enum {
   MOE_OK = 0,
@@ -175,7 +175,18 @@ typedef struct moe_args {
    * + layer output), added in fp32 before the one rounding.  It may be `out`
    * itself (in-place update) or x, but not overlap `out` partially. */
   const void* residual;
+  /* Optional (ABI version 5), with shared_format MOE_SHARED_BF16: the three
+   * bf16 shared matrices also packed by moe_pack_bf16 into one buffer, back to
+   * back: gate [I][d] at byte 0, up [I][d] at I*d*2, down [d][I] at 2*I*d*2
+   * (3*I*d*2 bytes, 16-byte aligned), or NULL.  For batches of at least
+   * MOE_SHARED_STREAM_ROWS rows with d % 512 == 0 and I % 256 == 0 the layer
+   * then streams these fragments per wave instead of tiling sh_*_w through LDS
+   * (the same values in the same summation order: identical results); sh_*_w
+   * are still required. */
+  const void* sh_packed;
 } moe_args_t;
+
+#define MOE_SHARED_STREAM_ROWS 2048
 
 #define MOE_N_STAGES 5  /* the input RMSNorm, when asked for, belongs to stage 0 */
 #define MOE_N_STAGE_EVENTS (MOE_N_STAGES + 1)
@@ -236,6 +247,19 @@ int moe_q2k_bytes(int32_t rows, int32_t K, size_t* bytes);
  * `stream`.
  */
 int moe_pack_q2k(const void* q, int32_t n_mat, int32_t rows, int32_t K, void* q_out, void* stream);
+
+/*
+ * Re-lay n_mat bf16 matrices [rows][K] (row-major, K contiguous) into the
+ * fragment order of the bf16 matrix instruction (one-time weight preparation,
+ * for moe_args_t.sh_packed): per matrix, fragment (rt, ks) for rt < rows/16,
+ * ks < K/32 at byte (rt*(K/32) + ks)*1024; its lane l (0..63) holds 16 bytes =
+ * the 8 values of row 16*rt + l%16 at columns 32*ks + 8*(l/16) .. +7.  Packed
+ * size = natural size (rows*K*2 bytes per matrix).  rows % 16 == 0, K % 32 ==
+ * 0 (each 16 .. 65536), else MOE_ERR_UNSUPPORTED; w and out 16-byte aligned,
+ * not overlapping.  Asynchronous on `stream`.  The shared expert's gate and up
+ * are [I][d] (rows I, K d), its down [d][I] (rows d, K I).
+ */
+int moe_pack_bf16(const void* w, int32_t n_mat, int32_t rows, int32_t K, void* out, void* stream);
 
 /* Device workspace bytes that moe_layer_forward needs for n_rows rows. */
 int moe_workspace_size(const moe_config_t* cfg, int32_t n_rows, size_t* bytes);

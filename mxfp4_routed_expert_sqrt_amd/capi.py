@@ -20,6 +20,7 @@ MOE_SHARED_MXFP4, MOE_SHARED_BF16 = 0, 1
 MOE_EXPERTS_MXFP4, MOE_EXPERTS_Q2K = 0, 1
 Q2K_BLOCK_BYTES = 84  # one 256-value Q2_K super-block
 MOE_MAX_ROWS = 1 << 20
+MOE_SHARED_STREAM_ROWS = 2048
 
 c_i32, c_i64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -41,7 +42,7 @@ class MoeArgs(ctypes.Structure):
                 ("tid2eid", c_vp), ("vocab", c_i64), ("w", MoeWeights), ("out", c_vp), ("topk_idx", c_vp),
                 ("topk_w", c_vp), ("counts", c_vp), ("offsets", c_vp), ("perm", c_vp), ("inv", c_vp),
                 ("workspace", c_vp), ("workspace_bytes", c_size), ("stage_events", c_vp), ("norm_w", c_vp),
-                ("residual", c_vp)]
+                ("residual", c_vp), ("sh_packed", c_vp)]
 
 
 MOE_N_STAGES = 5
@@ -69,6 +70,8 @@ def lib():
         L.moe_q2k_bytes.restype = ctypes.c_int
         L.moe_pack_q2k.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]
         L.moe_pack_q2k.restype = ctypes.c_int
+        L.moe_pack_bf16.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]
+        L.moe_pack_bf16.restype = ctypes.c_int
         L.moe_workspace_size.argtypes = [ctypes.POINTER(MoeConfig), c_i32, ctypes.POINTER(c_size)]
         L.moe_workspace_size.restype = ctypes.c_int
         L.moe_layer_forward.argtypes = [ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeArgs), c_vp]
@@ -80,7 +83,7 @@ def lib():
 
 
 EXPORTED = ("moe_version", "moe_status_string", "moe_packed_mxfp4_bytes", "moe_pack_mxfp4", "moe_q2k_bytes",
-            "moe_pack_q2k", "moe_workspace_size", "moe_layer_forward", "moe_layer_forward_noalloc")
+            "moe_pack_q2k", "moe_pack_bf16", "moe_workspace_size", "moe_layer_forward", "moe_layer_forward_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -121,6 +124,10 @@ def moe_q2k_bytes(rows: int, K: int) -> int:
 
 def moe_pack_q2k(q, n_mat, rows, K, q_out, stream) -> int:
     return lib().moe_pack_q2k(q, n_mat, rows, K, q_out, stream)
+
+
+def moe_pack_bf16(w, n_mat, rows, K, out, stream) -> int:
+    return lib().moe_pack_bf16(w, n_mat, rows, K, out, stream)
 
 
 def moe_workspace_size(cfg: MoeConfig, n_rows: int) -> int:

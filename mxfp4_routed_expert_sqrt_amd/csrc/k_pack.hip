@@ -48,6 +48,35 @@ __global__ void __launch_bounds__(256) pack_s_kernel(const uint8_t* __restrict__
   }
 }
 
+// bf16 matrices into bf16-MFMA fragments (v_mfma_f32_16x16x32_bf16 A
+// operand): one thread per 16-byte lane piece; fragment (rt, ks) of a matrix
+// [rows][K] at byte (rt * K/32 + ks) * 1024, lane l = row 16 rt + l % 16,
+// values 32 ks + 8 (l / 16) .. +7.
+__global__ void __launch_bounds__(256) pack_bf16_kernel(const uint8_t* __restrict__ w, int n_mat, int rows, int K,
+                                                         uint8_t* __restrict__ out) {
+  const int nks = K / 32;
+  const size_t per_mat = (size_t)(rows / 16) * nks * 64;
+  const size_t total = per_mat * n_mat;
+  for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (size_t)gridDim.x * blockDim.x) {
+    const size_t m = t / per_mat;
+    const size_t rem = t % per_mat;
+    const int lane = (int)(rem % 64);
+    const size_t frag = rem / 64;
+    const int ks = (int)(frag % nks), rt = (int)(frag / nks);
+    const int row = rt * 16 + (lane & 15), k0 = 32 * ks + 8 * (lane >> 4);
+    const uint8_t* src = w + ((m * rows + row) * (size_t)K + k0) * 2;
+    uint8_t* dst = out + m * (size_t)rows * K * 2 + frag * 1024 + (size_t)lane * 16;
+    *(u32x4*)dst = *(const u32x4*)src;
+  }
+}
+
+hipError_t launch_pack_bf16(const uint8_t* w, int n_mat, int rows, int K, uint8_t* out, hipStream_t stream) {
+  const size_t n = (size_t)n_mat * (rows / 16) * (K / 32) * 64;
+  const int b = (int)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536);
+  if (b > 0) hipLaunchKernelGGL(pack_bf16_kernel, dim3(b), dim3(256), 0, stream, w, n_mat, rows, K, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_mxfp4(const uint8_t* q, const uint8_t* s, int n_mat, int rows, int K, uint8_t* q_out,
                              uint8_t* s_out, hipStream_t stream) {
   const size_t nq = (size_t)n_mat * (rows / 16) * (K / 128) * 64;

@@ -140,6 +140,155 @@ __global__ void __launch_bounds__(256, 2) shared_bf16_kernel(const uint16_t* __r
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same GEMMs for large batches, on weights packed into bf16-MFMA fragments
+// (launch_pack_bf16): a workgroup (8 waves) takes 64 token rows and
+// 8 * TW * 16 features of each of its NW weight matrices.  Each wave streams
+// its NW * TW weight tiles straight from global memory into an 8-deep
+// register ring (one contiguous kilobyte per tile and 32-wide k-step), as the
+// routed experts' kernels do; only the 64 token rows, which all waves share,
+// go through LDS, in chunks of 256 K values (double-buffered, one barrier per
+// chunk).  A = weights (16 features), B = tokens (16 rows), so a lane holds 4
+// consecutive features of one token and stores them together.  The k-steps are
+// accumulated in the same order as the LDS-tiled kernel's.
+// Workgroups are numbered feature block first: with 8 feature blocks each XCD
+// streams one block of the weights.
+constexpr int kSsRows = 64, kSsWaves = 8, kSsSteps = 8;  // token rows; waves; 32-wide k-steps per chunk
+constexpr int kSsRowBytes = 32 * kSsSteps * 2 + 16;       // staged token row, padded: 16 mod 128
+constexpr int kSsBuf = kSsRows * kSsRowBytes;
+
+template <int NW, int TW>
+__global__ void __launch_bounds__(64 * kSsWaves) shared_stream_kernel(const uint16_t* __restrict__ a, int n_rows,
+                                                                      int K, const uint8_t* __restrict__ w0,
+                                                                      const uint8_t* __restrict__ w1, int n_feat,
+                                                                      float limit, uint16_t* __restrict__ h,
+                                                                      float* __restrict__ y) {
+  typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+  typedef const __attribute__((address_space(1))) uint8_t* gp;
+  constexpr int NA = NW * TW, RING = kSsSteps, kFeat = kSsWaves * TW * 16, kPieces = kSsRows * 32 / (64 * kSsWaves);
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // 2 * kSsBuf
+  const int n_fb = n_feat / kFeat;
+  const int fb = blockIdx.x % n_fb, rt = blockIdx.x / n_fb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int r0 = rt * kSsRows, f0 = fb * kFeat + wave * TW * 16;
+  const int nks = K / 32, nch = K / (32 * kSsSteps);
+  // weight tile i: matrix i / TW, 16-row tile f0/16 + i % TW (nks kilobytes each)
+  gp wq[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const uint64_t v = (uint64_t)((i < TW ? w0 : w1) + (size_t)(f0 / 16 + i % TW) * nks * 1024);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    wq[i] = (gp)(((uint64_t)hi << 32) | lo);
+  }
+  auto load_step = [&](u32x4 (&dst)[NA], int ks) {  // clamped: past the end any valid step, never multiplied
+    const uint32_t off = (uint32_t)lane * 16 + (uint32_t)min(ks, nks - 1) * 1024;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) dst[i] = *(const __attribute__((address_space(1))) u32x4*)(wq[i] + off);
+  };
+  // token chunk c (K values 256c .. 256c+255 of rows r0 .. r0+63, rows past the batch repeat its last row):
+  // piece p = tid + 512 j, row p / 32, 16 bytes at (p % 32) * 16
+  u32x4 st[kPieces];
+  auto stage_load = [&](int c) {
+    c = min(c, nch - 1);
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int pc = tid + 64 * kSsWaves * j, row = min(r0 + (pc >> 5), n_rows - 1);
+      st[j] = *(const __attribute__((address_space(1))) u32x4*)((gp)a + ((size_t)row * K + 256 * (size_t)c) * 2 +
+                                                                 (pc & 31) * 16);
+    }
+  };
+  auto stage_store = [&](uint8_t* buf) {
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int pc = tid + 64 * kSsWaves * j;
+      *(u32x4*)(buf + (pc >> 5) * kSsRowBytes + (pc & 31) * 16) = st[j];
+    }
+  };
+  v4f acc[NA][4];
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) acc[i][cc] = v4f{0.f, 0.f, 0.f, 0.f};
+  u32x4 f[RING][NA];
+  stage_load(0);
+#pragma unroll
+  for (int i = 0; i < RING - 1; ++i) load_step(f[i], i);
+  stage_store(lds);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const uint8_t* cur = lds + (c & 1) * kSsBuf;
+    stage_load(c + 1);
+#pragma unroll
+    for (int j = 0; j < kSsSteps; ++j) {
+      load_step(f[(j + RING - 1) % RING], kSsSteps * c + j + RING - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      v8bf b[4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        b[cc] = *(const v8bf*)(cur + (16 * cc + col) * kSsRowBytes + (32 * j + 8 * grp) * 2);
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const v8bf av = __builtin_bit_cast(v8bf, f[j][i]);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) acc[i][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[cc], acc[i][cc], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (c + 1 < nch) stage_store(lds + ((c + 1) & 1) * kSsBuf);
+    __syncthreads();
+  }
+  // lane: features f0 + 16t + 4grp .. +3 of token r0 + 16cc + col
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const int r = r0 + 16 * cc + col;
+    if (r >= n_rows) continue;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      const int f = f0 + 16 * t + 4 * grp;
+      if constexpr (NW == 2) {
+        uint32_t hb[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          float gv = acc[t][cc][ii], uv = acc[TW + t][cc][ii];
+          if (limit > 0.f) {
+            gv = fminf(gv, limit);
+            uv = fminf(fmaxf(uv, -limit), limit);
+          }
+          hb[ii] = f32_to_bf16_rne(gv * __builtin_amdgcn_rcpf(1.f + __expf(-gv)) * uv);
+        }
+        *(uint2*)(h + (size_t)r * n_feat + f) = uint2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+      } else {
+        *(v4f*)(y + (size_t)r * n_feat + f) = acc[t][cc];
+      }
+    }
+  }
+}
+
+template <int NW, int TW>
+static hipError_t shared_stream_launch(const uint16_t* a, int n_rows, int K, const uint8_t* w0, const uint8_t* w1,
+                                       int n_feat, float limit, uint16_t* h, float* y, hipStream_t stream) {
+  static std::atomic<uint64_t> attr{0};
+  constexpr int kFeat = kSsWaves * TW * 16;
+  if (K % (32 * kSsSteps) || n_feat % kFeat) return hipErrorInvalidValue;
+  hipError_t err = ensure_dynamic_lds(shared_stream_kernel<NW, TW>, 2 * kSsBuf, attr);
+  if (err != hipSuccess) return err;
+  const unsigned grid = (unsigned)(((n_rows + kSsRows - 1) / kSsRows) * (n_feat / kFeat));
+  hipLaunchKernelGGL((shared_stream_kernel<NW, TW>), dim3(grid), dim3(64 * kSsWaves), 2 * kSsBuf, stream, a, n_rows,
+                     K, w0, w1, n_feat, limit, h, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_stream_gateup(const uint16_t* x, int n_rows, int d, int I, const uint8_t* wg_p,
+                                       const uint8_t* wu_p, float limit, uint16_t* h, hipStream_t stream) {
+  return shared_stream_launch<2, 2>(x, n_rows, d, wg_p, wu_p, I, limit, h, nullptr, stream);
+}
+
+hipError_t launch_shared_stream_down(const uint16_t* h, int n_rows, int d, int I, const uint8_t* wd_p, float* y_sh,
+                                     hipStream_t stream) {
+  return shared_stream_launch<1, 4>(h, n_rows, I, wd_p, nullptr, d, 0.f, nullptr, y_sh, stream);
+}
+
 hipError_t launch_shared_bf16_gateup(const uint16_t* x, int n_rows, int d, int I, const uint16_t* wg,
                                      const uint16_t* wu, float limit, uint16_t* h, hipStream_t stream) {
   if (d % kSbChunk || I % kSbFeat) return hipErrorInvalidValue;

@@ -157,6 +157,20 @@ hipError_t launch_shared_bf16_gateup(const uint16_t* x, int n_rows, int d, int I
 hipError_t launch_shared_bf16_down(const uint16_t* h, int n_rows, int d, int I, const uint16_t* wd, float* y_sh,
                                    hipStream_t stream);
 
+// The same two GEMMs on weights packed by launch_pack_bf16 (bf16-MFMA
+// fragments), streamed per wave instead of tiled through LDS: faster for
+// large batches.  d and I multiples of 512.
+constexpr int kSharedStreamRows = 2048;  // batches from this size take the streamed kernels
+hipError_t launch_shared_stream_gateup(const uint16_t* x, int n_rows, int d, int I, const uint8_t* wg_p,
+                                       const uint8_t* wu_p, float limit, uint16_t* h, hipStream_t stream);
+hipError_t launch_shared_stream_down(const uint16_t* h, int n_rows, int d, int I, const uint8_t* wd_p, float* y_sh,
+                                     hipStream_t stream);
+
+// bf16 matrices [rows][K] (rows % 16 == 0, K % 32 == 0) into bf16-MFMA
+// fragments: fragment (rt, ks) at byte (rt * K/32 + ks) * 1024, lane l holding
+// row 16 rt + l % 16, values 32 ks + 8 (l / 16) .. +7.
+hipError_t launch_pack_bf16(const uint8_t* w, int n_mat, int rows, int K, uint8_t* out, hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // Routed experts in Q2_K (k_q2k.hip).  Packed matrix [R][K] (R % 16 == 0,
 // K % 256 == 0): 16-row tile rt, super-block b at byte (rt * K/256 + b) * 1344.

@@ -49,6 +49,34 @@ struct Layout {
 // it is MXFP4; a bf16 shared expert has GEMMs of its own.
 bool shared_in_list(const moe_config_t& c) { return c.has_shared && c.shared_format == MOE_SHARED_MXFP4; }
 bool shared_bf16(const moe_config_t& c) { return c.has_shared && c.shared_format == MOE_SHARED_BF16; }
+
+// The bf16 shared expert streamed from its packed copy (large batches).
+bool shared_stream(const moe_config_t& c, const moe_args_t& a) {
+  return shared_bf16(c) && a.sh_packed && a.n_rows >= kSharedStreamRows && c.d_model % 512 == 0 &&
+         c.d_ff % 256 == 0;
+}
+
+// The bf16 shared expert's GEMMs: streamed from the packed copy or tiled from sh_*_w.
+hipError_t shared_gateup(const moe_config_t& c, const moe_args_t& a, const uint16_t* x, uint16_t* hsh,
+                         hipStream_t stream) {
+  const int N = a.n_rows, d = c.d_model, I = c.d_ff;
+  if (shared_stream(c, a)) {
+    const uint8_t* p = (const uint8_t*)a.sh_packed;
+    return launch_shared_stream_gateup(x, N, d, I, p, p + (size_t)I * d * 2, c.swiglu_limit, hsh, stream);
+  }
+  return launch_shared_bf16_gateup(x, N, d, I, (const uint16_t*)a.w.sh_gate_w, (const uint16_t*)a.w.sh_up_w,
+                                   c.swiglu_limit, hsh, stream);
+}
+
+hipError_t shared_down(const moe_config_t& c, const moe_args_t& a, const uint16_t* hsh, float* y_sh,
+                       hipStream_t stream) {
+  const int N = a.n_rows, d = c.d_model, I = c.d_ff;
+  if (shared_stream(c, a))
+    return launch_shared_stream_down(hsh, N, d, I, (const uint8_t*)a.sh_packed + 2 * (size_t)I * d * 2, y_sh, stream);
+  return launch_shared_bf16_down(hsh, N, d, I, (const uint16_t*)a.w.sh_down_w, y_sh, stream);
+}
+static_assert(kSharedStreamRows == MOE_SHARED_STREAM_ROWS, "the header states the threshold");
+
 bool q2k(const moe_config_t& c) { return c.expert_format == MOE_EXPERTS_Q2K; }
 
 // Bytes of one routed weight matrix set [E] of [rows][K]: q and s parts.
@@ -183,6 +211,7 @@ bool buffers_disjoint(const moe_config_t& c, const moe_args_t& a, const void* ws
     add(a.w.sh_gate_w, I * d * 2, false);
     add(a.w.sh_up_w, I * d * 2, false);
     add(a.w.sh_down_w, I * d * 2, false);
+    add(a.sh_packed, 3 * I * d * 2, false);
   }
   if (c.routing == MOE_ROUTING_HASH) {
     add(a.token_ids, N * 4, false);
@@ -217,6 +246,7 @@ int check_args(const moe_config_t& c, const moe_args_t& a) {
     const void* shw[] = {a.w.sh_gate_w, a.w.sh_up_w, a.w.sh_down_w};
     for (const void* p : shw)
       if (!p || !aligned(p, 16)) return MOE_ERR_INVALID;
+    if (a.sh_packed && !aligned(a.sh_packed, 16)) return MOE_ERR_INVALID;
   }
   if (c.routing == MOE_ROUTING_HASH) {
     if (!a.token_ids || !a.tid2eid || a.vocab < 1 || !aligned(a.token_ids, 4) || !aligned(a.tid2eid, 4))
@@ -296,10 +326,7 @@ int run_layer_q2k(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const
   ga.pool = done + 1;
   if (!mark(2)) return MOE_ERR_HIP;
   if (launch_q2k_gateup(ga, max_groups, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (shared_bf16(c) &&
-      launch_shared_bf16_gateup(x, N, d, I, (const uint16_t*)a.w.sh_gate_w, (const uint16_t*)a.w.sh_up_w,
-                                c.swiglu_limit, hsh, stream) != hipSuccess)
-    return MOE_ERR_HIP;
+  if (shared_bf16(c) && shared_gateup(c, a, x, hsh, stream) != hipSuccess) return MOE_ERR_HIP;
   if (!mark(3)) return MOE_ERR_HIP;
   Q2kArgs da = ga;
   da.w0 = (const uint8_t*)a.w.down_q;
@@ -315,9 +342,7 @@ int run_layer_q2k(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const
   if (launch_q2k_sums(h, P, I, ga.h_f16 != 0, hpair, hsum, stream) != hipSuccess ||
       launch_q2k_down(da, max_groups, stream) != hipSuccess)
     return MOE_ERR_HIP;
-  if (shared_bf16(c) &&
-      launch_shared_bf16_down(hsh, N, d, I, (const uint16_t*)a.w.sh_down_w, y + (size_t)P * d, stream) != hipSuccess)
-    return MOE_ERR_HIP;
+  if (shared_bf16(c) && shared_down(c, a, hsh, y + (size_t)P * d, stream) != hipSuccess) return MOE_ERR_HIP;
   if (!mark(4)) return MOE_ERR_HIP;
   if (launch_combine(y, inv, gates, N, d, k, P, c.has_shared, c.route_scale, (const uint16_t*)a.residual,
                      (uint16_t*)a.out, stream) != hipSuccess)
@@ -398,10 +423,7 @@ int run_layer(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const Lay
   if (!mark(2)) return MOE_ERR_HIP;
   if ((err = launch_gateup(ga, max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
   uint16_t* hsh = (uint16_t*)(ws + L.hsh);
-  if (shared_bf16(c) &&
-      (err = launch_shared_bf16_gateup(x, N, d, I, (const uint16_t*)a.w.sh_gate_w, (const uint16_t*)a.w.sh_up_w,
-                                       c.swiglu_limit, hsh, stream)) != hipSuccess)
-    return MOE_ERR_HIP;
+  if (shared_bf16(c) && (err = shared_gateup(c, a, x, hsh, stream)) != hipSuccess) return MOE_ERR_HIP;
 
   ExpertArgs da = ga;
   da.q0 = (const uint8_t*)a.w.down_q;
@@ -420,10 +442,7 @@ int run_layer(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const Lay
   da.y = y;
   if (!mark(3)) return MOE_ERR_HIP;
   if ((err = launch_down(da, max_groups, stream)) != hipSuccess) return MOE_ERR_HIP;
-  if (shared_bf16(c) &&
-      (err = launch_shared_bf16_down(hsh, N, d, I, (const uint16_t*)a.w.sh_down_w, y + (size_t)P * d, stream)) !=
-          hipSuccess)
-    return MOE_ERR_HIP;
+  if (shared_bf16(c) && (err = shared_down(c, a, hsh, y + (size_t)P * d, stream)) != hipSuccess) return MOE_ERR_HIP;
   if (!mark(4)) return MOE_ERR_HIP;
 
   if ((err = launch_combine(y, inv, gates, N, d, k, P, c.has_shared, c.route_scale, (const uint16_t*)a.residual,
@@ -474,6 +493,17 @@ int moe_pack_mxfp4(const void* q, const void* s, int32_t n_mat, int32_t rows, in
     return MOE_ERR_INVALID;
   hipError_t err = launch_pack_mxfp4((const uint8_t*)q, (const uint8_t*)s, n_mat, rows, K, (uint8_t*)q_out,
                                      (uint8_t*)s_out, (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_pack_bf16(const void* w, int32_t n_mat, int32_t rows, int32_t K, void* out, void* stream) {
+  if (n_mat < 0) return MOE_ERR_INVALID;
+  if (rows < 16 || rows % 16 || K < 32 || K % 32 || rows > 65536 || K > 65536) return MOE_ERR_UNSUPPORTED;
+  if (n_mat == 0) return MOE_OK;
+  if (!w || !out || !aligned(w, 16) || !aligned(out, 16)) return MOE_ERR_INVALID;
+  const size_t n = (size_t)n_mat * rows * K * 2;
+  if (overlap(w, n, out, n)) return MOE_ERR_INVALID;
+  hipError_t err = launch_pack_bf16((const uint8_t*)w, n_mat, rows, K, (uint8_t*)out, (hipStream_t)stream);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -60,6 +60,19 @@ def pack_q2k(q: torch.Tensor, rows: int, K: int, stream=None, out=None) -> torch
 _ALIGN = 2 << 20  # each packed region starts on a 2 MiB boundary inside one allocation
 
 
+def pack_bf16(w: torch.Tensor, rows: int, K: int, stream=None, out=None) -> torch.Tensor:
+    """bf16 bit patterns [n][rows][K] (int16/uint16 device tensor) -> the fragment order of moe_pack_bf16
+    (uint8 device tensor of the same byte size, or written into out)."""
+    n = w.numel() // (rows * K)
+    if out is None:
+        out = torch.empty(n * rows * K * 2, dtype=torch.uint8, device=w.device)
+    st = torch.cuda.current_stream(w.device).cuda_stream if stream is None else stream
+    rc = capi.moe_pack_bf16(w.data_ptr(), n, rows, K, out.data_ptr(), st)
+    if rc != capi.MOE_OK:
+        raise capi.MoeError(rc)
+    return out
+
+
 class PackedExperts:
     """Routed experts 0..E-1 and the shared expert (index E), packed on the device.
 
@@ -151,7 +164,7 @@ class PackedQ2kExperts:
 class MoELayer:
     def __init__(self, shape: MoEShape, router_w, experts, device="cuda", router_bias=None,
                  has_shared: bool = True, route_scale=None, swiglu_limit=None, norm_w=None, norm_eps: float = 1e-6,
-                 bias_mode: int = capi.MOE_BIAS_LOGIT, shared_bf16=None, experts_q2k=None):
+                 bias_mode: int = capi.MOE_BIAS_LOGIT, shared_bf16=None, experts_q2k=None, shared_stream: bool = True):
         """experts: natural-layout arrays (dict, packed here) or an already packed PackedExperts.
         norm_w: optional bf16 bit patterns [d] of the input RMSNorm weight (the layer then normalises x).
         shared_bf16: optional dict of bf16 bit patterns gate/up [I][d], down [d][I]: the shared expert in
@@ -171,6 +184,16 @@ class MoELayer:
         self.shared_bf16 = None if shared_bf16 is None else {
             n: torch.from_numpy(np.ascontiguousarray(shared_bf16[n], dtype=np.uint16).view(np.int16)).to(self.device)
             for n in ("gate", "up", "down")}
+        # the bf16 shared expert also packed into MFMA fragments (moe_args_t.sh_packed): gate, up, down back
+        # to back; the layer streams it for batches of at least MOE_SHARED_STREAM_ROWS rows.  shared_stream
+        # False keeps the LDS-tiled kernels at every size.
+        self.sh_packed = None
+        if self.shared_bf16 is not None and shared_stream:
+            d, I = shape.d_model, shape.d_ff
+            self.sh_packed = torch.empty(3 * I * d * 2, dtype=torch.uint8, device=self.device)
+            for i, (n, rows, K) in enumerate((("gate", I, d), ("up", I, d), ("down", d, I))):
+                pack_bf16(self.shared_bf16[n], rows, K, out=self.sh_packed[i * I * d * 2:(i + 1) * I * d * 2])
+            torch.cuda.synchronize(self.device)
         self.norm_w = None if norm_w is None else \
             torch.from_numpy(np.ascontiguousarray(norm_w, dtype=np.uint16).view(np.int16)).to(self.device)
         self.router_w = torch.as_tensor(np.ascontiguousarray(router_w, dtype=np.float32)).to(self.device)
@@ -205,7 +228,8 @@ class MoELayer:
                             self.experts.weights(self.has_shared, self.shared_bf16), _ptr(out),
                             _ptr(r.get("topk_idx")), _ptr(r.get("topk_w")), _ptr(r.get("counts")),
                             _ptr(r.get("offsets")), _ptr(r.get("perm")), _ptr(r.get("inv")), _ptr(workspace),
-                            0 if workspace is None else workspace.numel(), None, _ptr(self.norm_w), _ptr(residual))
+                            0 if workspace is None else workspace.numel(), None, _ptr(self.norm_w), _ptr(residual),
+                            _ptr(self.sh_packed))
 
     def forward(self, x: torch.Tensor, token_ids=None, tid2eid=None, out=None, workspace=None, with_routing=False,
                 stream=None, residual=None):

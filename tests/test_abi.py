@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert capi.moe_version() == 4
+    assert capi.moe_version() == 5
     for st in (0, -1, -2, -3, -4, -5):
         assert capi.moe_status_string(st) != "unknown status"
     assert capi.moe_status_string(7) == "unknown status"
@@ -242,6 +242,32 @@ def test_pack_rejects_bad_arguments():
     assert L is not None
 
 
+def test_bf16_pack_and_packed_shared_expert_are_checked_before_any_hip_call():
+    # moe_pack_bf16: sizes, alignment, overlap
+    assert capi.moe_pack_bf16(None, 0, 16, 32, None, None) == capi.MOE_OK
+    assert capi.moe_pack_bf16(None, 1, 16, 32, 0x2000, None) == capi.MOE_ERR_INVALID
+    assert capi.moe_pack_bf16(0x1000, 1, 24, 32, 0x9000, None) == capi.MOE_ERR_UNSUPPORTED   # rows % 16
+    assert capi.moe_pack_bf16(0x1000, 1, 16, 48, 0x9000, None) == capi.MOE_ERR_UNSUPPORTED   # K % 32
+    assert capi.moe_pack_bf16(0x1008, 1, 16, 32, 0x9000, None) == capi.MOE_ERR_INVALID       # w not 16-aligned
+    assert capi.moe_pack_bf16(0x1000, 1, 16, 32, 0x9008, None) == capi.MOE_ERR_INVALID       # out not 16-aligned
+    assert capi.moe_pack_bf16(0x1000, 1, 16, 32, 0x1000 + 16 * 32 * 2 - 16, None) == capi.MOE_ERR_INVALID  # overlap
+    assert capi.moe_pack_bf16(0x1000, -1, 16, 32, 0x9000, None) == capi.MOE_ERR_INVALID
+    # moe_args_t.sh_packed with a bf16 shared expert: 16-byte aligned, read over 3*I*d*2 bytes
+    cfg = make_config(SHAPES["tiny"], shared_format=capi.MOE_SHARED_BF16)
+    N, d, I = 32, 256, 128
+    a = _valid_args(cfg, N); a.sh_packed = 0xE0000008
+    assert capi.moe_layer_forward(cfg, a, None) == capi.MOE_ERR_INVALID
+    a = _valid_args(cfg, N); a.sh_packed = a.workspace - 3 * I * d * 2 + 16   # its last 16 bytes in the workspace
+    assert capi.moe_layer_forward(cfg, a, None) == capi.MOE_ERR_INVALID
+    a.sh_packed = a.workspace - 3 * I * d * 2
+    a.workspace_bytes -= 1
+    assert capi.moe_layer_forward(cfg, a, None) == capi.MOE_ERR_WORKSPACE     # valid up to the workspace size
+    # with the MXFP4 shared expert the field is not read
+    mcfg = make_config(SHAPES["tiny"])
+    a = _valid_args(mcfg, N); a.sh_packed = 0xE0000008; a.workspace_bytes -= 1
+    assert capi.moe_layer_forward(mcfg, a, None) == capi.MOE_ERR_WORKSPACE
+
+
 def test_binding_structs_match_the_c_header(tmp_path):
     # offsets and sizes of every field of the three ABI structs, as the C compiler lays them out
     # from include/moe_mxfp4.h, against the ctypes mirrors; and the header's constants
@@ -258,7 +284,8 @@ def test_binding_structs_match_the_c_header(tmp_path):
     consts = ["MOE_OK", "MOE_ERR_INVALID", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_ERR_HIP",
               "MOE_ROUTING_TOPK", "MOE_ROUTING_HASH", "MOE_BIAS_LOGIT", "MOE_BIAS_SELECT", "MOE_SHARED_MXFP4",
               "MOE_SHARED_BF16", "MOE_MAX_ROWS", "MOE_ERR_SCRATCH", "MOE_NOALLOC_SCRATCH_BYTES",
-              "MOE_N_STAGES", "MOE_N_STAGE_EVENTS", "MOE_MXFP4_VERSION", "MOE_EXPERTS_MXFP4", "MOE_EXPERTS_Q2K"]
+              "MOE_N_STAGES", "MOE_N_STAGE_EVENTS", "MOE_MXFP4_VERSION", "MOE_EXPERTS_MXFP4", "MOE_EXPERTS_Q2K",
+              "MOE_SHARED_STREAM_ROWS"]
     for c in consts:
         lines.append(f'  printf("const {c} %ld\\n", (long)({c}));')
     lines += ["  return 0;", "}"]

@@ -21,7 +21,8 @@
   value j at bits 6j of the operand, term 2 rounds the exact fp32 residual of
   term 1, and the exponents put each block maximum in (3.75, 7.5].
 - permlane32/permlane16 swaps exchange the documented lane rows.
-- moe_pack_mxfp4 produces the packed layout described in the C header.
+- moe_pack_mxfp4 and moe_pack_bf16 produce the packed layouts described in
+  the C header.
 Expected values come from independent numpy decoders written here.
 """
 import ctypes
@@ -294,3 +295,24 @@ def test_permlane_swaps():
         x16[base + 16:base + 32], y16[base:base + 16] = y[base:base + 16], x[base + 16:base + 32]
     assert np.array_equal(o[0], x32) and np.array_equal(o[1], y32)
     assert np.array_equal(o[2], x16) and np.array_equal(o[3], y16)
+
+
+def test_bf16_pack_layout_matches_header():
+    from mxfp4_routed_expert_sqrt_amd.layer import pack_bf16
+    print("moe_pack_bf16", flush=True)
+    rng = np.random.default_rng(7)
+    dev = torch.device("cuda")
+    for n_mat, rows, K in [(1, 16, 32), (2, 48, 96), (3, 32, 512)]:
+        w = rng.integers(-32768, 32768, (n_mat, rows, K), dtype=np.int16)
+        out = pack_bf16(torch.from_numpy(w).to(dev), rows, K).cpu().numpy()
+        torch.cuda.synchronize()
+        assert out.size == w.nbytes
+        o16 = out.view(np.int16).reshape(n_mat, -1)
+        nks = K // 32
+        for m in range(n_mat):
+            for rt in range(rows // 16):
+                for ks in range(nks):
+                    frag = o16[m, (rt * nks + ks) * 512:(rt * nks + ks + 1) * 512].reshape(64, 8)
+                    for lane in range(64):
+                        row, k0 = 16 * rt + lane % 16, 32 * ks + 8 * (lane // 16)
+                        assert np.array_equal(frag[lane], w[m, row, k0:k0 + 8]), (m, rt, ks, lane)
