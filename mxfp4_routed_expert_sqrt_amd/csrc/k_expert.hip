@@ -259,19 +259,13 @@ struct UnitSrc {
 // multiplied).
 // The chunk loaded during the group is chunk cc of cs (in a unit's K loop:
 // chunk sg+1 of the unit, clamped).
-// wn (a unit's last group, when the next unit is known and nks is a multiple
-// of 4): the weight steps past the unit's end are the next unit's steps 0,
-// 1, 2, taken from wn, and the scales loaded are its first group's, so they
-// land in the ring slots and scale registers its first group reads.
 template <int GI, int RING, int NA, int THREADS, int NB, bool NT, bool FP6>
 __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS, NB, FP6>& stage,
                                         uint32_t (&sa)[NA], uint32_t (&sa_n)[NA],
                                         const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& cur, int sg,
                                         int nks, int n_sg, v4f (&acc)[NA][NB], const uint8_t* chunk,
                                         uint8_t* next_buf,
-                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& cs, int cc,
-                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>* wn = nullptr,
-                                        bool wpf = false) {
+                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& cs, int cc) {
   const int lane = threadIdx.x & 63, last = nks - 1, k0 = 4 * sg;
   uint32_t sb[NB][2];
 #pragma unroll
@@ -280,27 +274,9 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
     sb[tt][1] = *(const uint32_t*)(chunk + scale_off<NB, FP6>(tt) + 256 + lane * 4);
   }
   // weight step loaded at position j of the group (RING-1+j steps ahead)
-  auto load_step = [&](WFrag<NA>& slot, int j) {
-    const int s = k0 + RING - 1 + j;
-    if (wn == nullptr) {
-      load_w<NT>(slot, cur.aq, min(s, last));
-    } else {
-      const bool nx = wpf && s > last;  // wave-uniform: scalar selects, no branch
-      gptr src[NA];
-#pragma unroll
-      for (int a = 0; a < NA; ++a) src[a] = nx ? wn->aq[a] : cur.aq[a];
-      load_w<NT>(slot, src, nx ? s - nks : s);
-    }
-  };
+  auto load_step = [&](WFrag<NA>& slot, int j) { load_w<NT>(slot, cur.aq, min(k0 + RING - 1 + j, last)); };
   stage.load(cs.brow_q, cs.brow_s, cc, nks, n_sg);
-  if (wn == nullptr) {
-    load_wscales(sa_n, cur.as, min(sg + 1, n_sg - 1));
-  } else {
-    gptr src[NA];
-#pragma unroll
-    for (int a = 0; a < NA; ++a) src[a] = wpf ? wn->as[a] : cur.as[a];
-    load_wscales(sa_n, src, wpf ? 0 : min(sg + 1, n_sg - 1));
-  }
+  load_wscales(sa_n, cur.as, min(sg + 1, n_sg - 1));
   load_step(f[(4 * GI + RING - 1) % RING], 0);
   __builtin_amdgcn_sched_barrier(0);
   mma_step<0, NA, NB, FP6>(f[(4 * GI) % RING], chunk, sa, sb, acc);
@@ -850,8 +826,7 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
 #pragma unroll
       for (int c = 0; c < NB; ++c) acc[i][c] = v4f{0.f, 0.f, 0.f, 0.f};
     // K loop: chunk sg of the unit is in LDS buffer (bp + sg) & 1.  The last
-    // group loads and stages the queued unit's first chunk, and, when nks is
-    // a multiple of 4, its scales and first weight steps (wpf).
+    // group loads and stages the queued unit's first chunk.
     UnitSrc<NA, NB, NS, true> nxt;
     if constexpr (!GU) row_ptrs<kThreads, NB, NA, true>(a, row, a.K, nxt);
     for (int sg = 0; sg + 1 < n_sg; ++sg)
@@ -883,8 +858,7 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
     // it (the queued unit's weights and chunk, the epilogue's stores) in flight
     const int uq2 = q2 >= 0 ? q2 : uq;
     const int gword = entry_word(A.groups, uq2 / n_fb);
-    // the queued unit's scales and first weight steps, unless the last group
-    // loaded them
+    // the queued unit's scales and first weight steps
     weight_ptrs<NA, GU>(A, gq, f0q, nxt.aq, nxt.as);
     load_wscales(sa, nxt.as, opaque(0));
 #pragma unroll
