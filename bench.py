@@ -26,7 +26,12 @@ Prints one JSON line.  Besides the contract fields it carries
   expert format (Q2_K routed experts with a bf16 shared expert) at the
   448-row draft slab and the 512-row verify batch;
 - cpu_baseline: the fp64 CPU oracle on a bounded sample of the headline
-  workload on this host (all host cores, and one core on 8 rows).
+  workload on this host (all host cores, and one core on 8 rows);
+- hbm_read_probe: the read bandwidth a plain streaming kernel reaches on this
+  GPU (2 GiB read once per launch, regular and non-temporal loads, the best of
+  four grid sizes), the practical ceiling beside the 8 TB/s data-sheet peak;
+  roofline.peak_measured and frac_of_measured set the dominant kernel against
+  it (roofline.peak stays the data-sheet figure).
 """
 import argparse
 import ctypes
@@ -46,6 +51,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_verify512_traffic.txt")
 EXTRA_WORKLOADS = ("decode8", "prefill8192", "zipf2048", "hash2048", "q2k_draft448", "q2k_verify512")
 Q2K_PREFIX = "q2k_"  # routed experts in Q2_K, shared expert in bf16, on the named shape
 DECODE_WEIGHT_COPIES = 4  # 8-row batches touch ~0.6 GB of weights: rotate copies past the 256 MB MALL
+HBM_PROBE_LIB = os.path.join(ROOT, "mxfp4_routed_expert_sqrt_amd", "libmoe_hbm.so")
+HBM_PROBE_BYTES = 2 << 30  # 8x the 256 MB memory-side cache
+HBM_PROBE_GRIDS = (2048, 4096, 8192, 16384)  # workgroups of 256 threads
 
 
 def parse():
@@ -67,6 +75,8 @@ def parse():
                     help="the shared expert in bf16 (its own bf16-MFMA GEMMs) instead of MXFP4")
     ap.add_argument("--with-norm", action="store_true",
                     help="run the layer with its input RMSNorm and a residual add (seeded bf16 weight and residual)")
+    ap.add_argument("--hbm-probe-only", action="store_true",
+                    help="run only the streaming-read probe and print its JSON (for profiling it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one elementwise kernel over 1 GiB (reads 1 GiB, writes 1 GiB: the reference "
                          "for the HBM byte counters)")
@@ -390,6 +400,46 @@ def measure_workload(name, ctx, args, hip):
     return res
 
 
+def hbm_read_peak(hip, dev, stream, reps=10, warm=3):
+    """Read bandwidth of the streaming-read probe (libmoe_hbm.so) over HBM_PROBE_BYTES, per load kind."""
+    import torch
+    if not os.path.exists(HBM_PROBE_LIB):
+        raise SystemExit(f"{HBM_PROBE_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(HBM_PROBE_LIB)
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.hbm_probe_sink_words.argtypes = [ctypes.c_int]
+    buf = torch.zeros(HBM_PROBE_BYTES, dtype=torch.uint8, device=dev)
+    out = {"bytes_per_launch": HBM_PROBE_BYTES, "launches_timed": reps, "kernel": "hbm_read_kernel",
+           "gbs_by_workgroups": {}}
+    e0, e1 = hip.event(), hip.event()
+    for nt, kind in ((0, "regular"), (1, "nontemporal")):
+        per = {}
+        for wg in HBM_PROBE_GRIDS:
+            sink = torch.empty(lib.hbm_probe_sink_words(wg), dtype=torch.int32, device=dev)
+
+            def call():
+                if lib.hbm_read_probe(buf.data_ptr(), HBM_PROBE_BYTES, nt, sink.data_ptr(), wg, stream) != 0:
+                    raise RuntimeError("hbm_read_probe failed")
+            for _ in range(warm):
+                call()
+            torch.cuda.synchronize()
+            hip.record(e0, stream)
+            for _ in range(reps):
+                call()
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            per[wg] = round(HBM_PROBE_BYTES * reps / (hip.elapsed_ms(e0, e1) * 1e-3) / 1e9, 1)
+        out["gbs_by_workgroups"][kind] = per
+        out[f"read_gbs_{kind}"] = max(per.values())
+    hip.destroy(e0)
+    hip.destroy(e1)
+    out["read_gbs"] = max(out["read_gbs_regular"], out["read_gbs_nontemporal"])
+    out["frac_of_spec"] = round(out["read_gbs"] / HBM_PEAK_GBS, 4)
+    del buf
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -404,6 +454,12 @@ def main():
     from mxfp4_routed_expert_sqrt_amd import synth
     from mxfp4_routed_expert_sqrt_amd.configs import SHAPES
     from mxfp4_routed_expert_sqrt_amd.layer import MoELayer, PackedExperts
+
+    if args.hbm_probe_only:
+        dev = torch.device("cuda:0")
+        print(json.dumps({"hbm_read_probe": hbm_read_peak(Hip(), dev, torch.cuda.current_stream(dev).cuda_stream)}),
+              flush=True)
+        return
 
     shape = SHAPES[args.workload]
     if shape.bias != "none":
@@ -454,6 +510,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    print("[bench] streaming-read probe", file=sys.stderr, flush=True)
+    probe = hbm_read_peak(hip, dev, stream)
+
     N, d, I, E = shape.n_rows, shape.d_model, shape.d_ff, shape.n_experts
     ms_per_step = timing["ms_per_step"]
     gu = head["gateup"]
@@ -484,6 +543,7 @@ def main():
                    "global_batch": N, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "peak_measured": probe["read_gbs"], "frac_of_measured": achieved / probe["read_gbs"],
                      "kernel": "gateup_kernel" + (" + shared_bf16_kernel<2>" if args.shared_bf16 else ""),
                      "algorithmic_bytes": gu["algorithmic_bytes"],
                      "bytes_definition": "gate+up MXFP4 bytes (nibbles + E8M0 scales) of every touched expert, "
@@ -495,6 +555,7 @@ def main():
                      "layer_bytes_definition": "MXFP4 weights of every touched expert + router weight fp32 + x + "
                                                "out (bf16), over ms_per_step"},
         "layer": head,
+        "hbm_read_probe": probe,
     }
     if not args.only:
         ctx = {"dev": dev, "router_w": w_np, "packed": packed, "copies": []}

@@ -2,6 +2,8 @@
 
 - libmoe_synth.so: the seeded input generator (plain C, host compiler).
 - libmoe_mxfp4.so: the HIP kernels and the C-ABI entry points, for gfx950 only.
+- libmoe_hbm.so: the streaming-read probe that bench.py runs beside the layer
+  (measurement only).
 """
 import os
 import subprocess
@@ -35,9 +37,18 @@ def build_hip(extra_flags=()) -> str:
     return out
 
 
+def build_hbm_probe() -> str:
+    out = os.path.join(HERE, "libmoe_hbm.so")
+    tmp = out + ".tmp"
+    subprocess.run(["hipcc", *HIP_FLAGS, "-o", tmp, os.path.join(CSRC, "hbm_probe.hip")], check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def build_all() -> None:
     build_synth()
     build_hip()
+    build_hbm_probe()
 
 
 if __name__ == "__main__":

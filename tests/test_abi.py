@@ -33,6 +33,27 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(capi.EXPORTED)
 
 
+def test_hbm_probe_library_exports_its_header_and_checks_arguments():
+    # include/hbm_probe.h belongs to the streaming-read probe (libmoe_hbm.so), not to the layer's library
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "hbm_probe.h")).read(), flags=re.S)
+    names = set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(hbm_\w+)\s*\(", text, flags=re.M))
+    assert names == {"hbm_read_probe", "hbm_probe_sink_words"}
+    lib = ctypes.CDLL(os.path.join(ROOT, "mxfp4_routed_expert_sqrt_amd", "libmoe_hbm.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.hbm_probe_sink_words.argtypes = [ctypes.c_int]
+    assert lib.hbm_probe_sink_words(10) == 40
+    # rejected on the host before any launch: no buffer, a size that is not whole 16-byte pieces,
+    # a misaligned start, no workgroups
+    fake = 1 << 20
+    assert lib.hbm_read_probe(None, 1024, 0, fake, 4, None) == -1
+    assert lib.hbm_read_probe(fake, 1000, 0, fake, 4, None) == -1
+    assert lib.hbm_read_probe(fake + 8, 1024, 0, fake, 4, None) == -1
+    assert lib.hbm_read_probe(fake, 1024, 0, fake, 0, None) == -1
+
+
 def test_version_and_status_strings():
     assert capi.moe_version() == 5
     for st in (0, -1, -2, -3, -4, -5):

@@ -23,6 +23,8 @@
 - permlane32/permlane16 swaps exchange the documented lane rows.
 - moe_pack_mxfp4 and moe_pack_bf16 produce the packed layouts described in
   the C header.
+- The streaming-read probe that the benchmark times (libmoe_hbm.so) reads
+  every 16-byte piece of its buffer exactly once, whatever the grid.
 Expected values come from independent numpy decoders written here.
 """
 import ctypes
@@ -316,3 +318,28 @@ def test_bf16_pack_layout_matches_header():
                     for lane in range(64):
                         row, k0 = 16 * rt + lane % 16, 32 * ks + 8 * (lane // 16)
                         assert np.array_equal(frag[lane], w[m, row, k0:k0 + 8]), (m, rt, ks, lane)
+
+
+@pytest.mark.parametrize("nbytes,workgroups", [(1 << 20, 8), ((1 << 22) + 48, 64), (4096 * 16 * 8 + 16, 4096)])
+def test_hbm_read_probe_reads_every_piece_once(nbytes, workgroups):
+    # The XOR of the per-wave folds equals the XOR of every dword of the buffer only if each
+    # 16-byte piece is read exactly once (a missed or repeated piece of random data changes it).
+    path = os.path.join(os.path.dirname(os.path.dirname(__file__)), "mxfp4_routed_expert_sqrt_amd", "libmoe_hbm.so")
+    if not os.path.exists(path):
+        pytest.fail(f"{path} not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(path)
+    L.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                 ctypes.c_void_p]
+    L.hbm_probe_sink_words.argtypes = [ctypes.c_int]
+    dev = torch.device("cuda:0")
+    words = np.random.default_rng(nbytes).integers(0, 2 ** 32, nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).to(dev)
+    want = np.bitwise_xor.reduce(words)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for nt in (0, 1):
+        sink = torch.zeros(L.hbm_probe_sink_words(workgroups), dtype=torch.int32, device=dev)
+        assert L.hbm_read_probe(buf.data_ptr(), nbytes, nt, sink.data_ptr(), workgroups, stream) == 0
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == want, (nbytes, workgroups, nt)
+
