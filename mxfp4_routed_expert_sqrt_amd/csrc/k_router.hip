@@ -372,6 +372,7 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
 // Histogram rows are E rounded up to a multiple of 4 ints wide, so both scan
 // passes move 16-byte columns.
 constexpr int kRouteThreads = 1024;
+constexpr int kMaxSplits = 16;  // the most split-K partials of the logits (logits_splits)
 constexpr int kRouteWaves = kRouteThreads / 64;  // rows selected per workgroup
 constexpr int kMaxExperts = 1024;
 
@@ -388,39 +389,24 @@ __device__ __forceinline__ int wave_match_rank(int e, bool act, int lane, bool* 
 }
 
 // Work list of groups of <= rows rows (ceil(count/rows) per expert in expert
-// order, and the shared expert's rows) once counts and offsets (in LDS) are
-// final.  The expert kernels hand each XCD a contiguous range of the list and
-// each XCD runs its range in order.  With 32-row groups (about one group per
-// routed expert) the shared expert's groups, whose units carry the most rows
-// and run longest, go first: last, they made the XCD holding them finish its
-// range well after the others.  The 16- and 64-row lists keep them last: on
-// 64-row lists shared-first measured slower (2048 hash-routed rows: the down
-// launch 24 us longer).
-__device__ __forceinline__ void write_groups(int rows, const int32_t* s_cnt, const int32_t* s_off, int n_rows, int P, int E,
-                                             int has_shared, Group* __restrict__ groups,
-                                             int32_t* __restrict__ n_groups, int32_t* wave_tot) {
+// order, and the shared expert's rows), by the thread of expert tid: c its
+// count, ng its groups, p0 its offset, g_excl the groups of the experts before
+// it, total the routed groups of all experts.  The expert kernels hand each
+// XCD a contiguous range of the list and each XCD runs its range in order.
+// With 32-row groups (about one group per routed expert) the shared expert's
+// groups, whose units carry the most rows and run longest, go first: last,
+// they made the XCD holding them finish its range well after the others.  The
+// 16- and 64-row lists keep them last: on 64-row lists shared-first measured
+// slower (2048 hash-routed rows: the down launch 24 us longer).
+__device__ __forceinline__ void write_groups(int rows, int c, int ng, int p0, int g_excl, int total, int n_rows,
+                                             int P, int E, int has_shared, Group* __restrict__ groups,
+                                             int32_t* __restrict__ n_groups) {
   const int nsh = has_shared ? (n_rows + rows - 1) / rows : 0;
   const bool shared_first = rows == kMediumGroupRows;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = (tid < E) ? s_cnt[tid] : 0;
-  const int ng = (c + rows - 1) / rows;
-  int incl = ng;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  int wbase = 0, total = 0;
-  for (int w = 0; w < kRouteWaves; ++w) {
-    if (w < wave) wbase += wave_tot[w];
-    total += wave_tot[w];
-  }
+  const int tid = threadIdx.x;
   const int routed0 = shared_first ? nsh : 0, shared0 = shared_first ? 0 : total;
   if (tid < E) {
-    const int g0 = routed0 + wbase + incl - ng;
-    const int p0 = s_off[tid];
+    const int g0 = routed0 + g_excl;
     for (int g = 0; g < ng; ++g) {
       Group gr;
       gr.e = tid;
@@ -465,6 +451,7 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
   __shared__ int32_t s_off[kMaxExperts];    // step 2: offsets
   __shared__ int32_t s_seg[4 * kMaxExperts];  // step 2: segment sums / bases, [segment][Ep]
   __shared__ int32_t wave_tot[kRouteWaves];
+  __shared__ int32_t wave_grp[kRouteWaves];
   __shared__ int32_t is_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x, nb = gridDim.x;
@@ -484,15 +471,21 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
     const size_t zstride = logits_partial_stride(n_rows, E);
     for (int i = 4 * tid; i < cnt; i += 4 * kRouteThreads) {
       if (i + 4 <= cnt) {
-        float4 v = *(const float4*)(zb + i);
-#pragma unroll 8
-        for (int sp = 1; sp < n_split; ++sp) {
-          const float4 u = *(const float4*)(zb + sp * zstride + i);
-          v.x += u.x;
-          v.y += u.y;
-          v.z += u.z;
-          v.w += u.w;
-        }
+        // every partial is loaded before the first add (one round trip), then
+        // they are added in split order
+        float4 u[kMaxSplits];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+          if (sp < n_split) u[sp] = *(const float4*)(zb + sp * zstride + i);
+        float4 v = u[0];
+#pragma unroll
+        for (int sp = 1; sp < kMaxSplits; ++sp)
+          if (sp < n_split) {
+            v.x += u[sp].x;
+            v.y += u[sp].y;
+            v.z += u[sp].z;
+            v.w += u[sp].w;
+          }
         const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) s_z[i + j] = lbias ? vv[j] + lbias[(i + j) % E] : vv[j];
@@ -617,24 +610,41 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
       }
     }
   }  // multi-workgroup step 2a-2c
-  // 2d: offsets = exclusive scan of the counts over experts (E <= 1024: one per thread)
+  // 2d: offsets = exclusive scan of the counts over experts, and the work
+  // list's group bases = exclusive scan of the groups per expert, in one pass
+  // (E <= 1024: one expert per thread); the work list is written here
   {
-    const int v = (tid < E) ? s_a[tid] : 0;
-    int incl = v;
+    const int c = (tid < E) ? s_a[tid] : 0;
+    const int ng = (c + group_rows - 1) / group_rows;
+    int ic = c, ig = ng;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
+      const int oc = __shfl_up(ic, off, 64), og = __shfl_up(ig, off, 64);
+      if (lane >= off) {
+        ic += oc;
+        ig += og;
+      }
     }
-    if (lane == 63) wave_tot[wave] = incl;
+    if (lane == 63) {
+      wave_tot[wave] = ic;
+      wave_grp[wave] = ig;
+    }
     __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wave; ++w) wbase += wave_tot[w];
+    int wb = 0, gb = 0, g_total = 0;
+    for (int w = 0; w < kRouteWaves; ++w) {
+      if (w < wave) {
+        wb += wave_tot[w];
+        gb += wave_grp[w];
+      }
+      g_total += wave_grp[w];
+    }
+    const int p0 = wb + ic - c;
     if (tid < E) {
-      s_off[tid] = wbase + incl - v;
-      offsets[tid] = wbase + incl - v;
+      s_off[tid] = p0;
+      offsets[tid] = p0;
     }
     if (tid == 0) offsets[E] = P;
+    write_groups(group_rows, c, ng, p0, gb + ig - ng, g_total, n_rows, P, E, has_shared, groups, n_groups);
   }
   __syncthreads();
   // 2e: scatter (the bases were written by this workgroup in 2c); for large
@@ -649,8 +659,6 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
       inv[q] = p;
     }
   }
-  __syncthreads();  // wave_tot reuse
-  write_groups(group_rows, s_a, s_off, n_rows, P, E, has_shared, groups, n_groups, wave_tot);
 }
 
 // Scatter of perm/inv, one pair per thread (bases and offsets come from the
@@ -677,7 +685,7 @@ hipError_t launch_select_route(const float* z, const float* bias, int bias_mode,
                                const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, int has_shared,
                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, int group_rows,
                                Group* groups, int32_t* n_groups, int32_t* hist, int32_t* done, hipStream_t stream) {
-  if (E > kMaxExperts || k > kMaxTopK) return hipErrorInvalidValue;
+  if (E > kMaxExperts || k > kMaxTopK || logits_splits(n_rows, E, d) > kMaxSplits) return hipErrorInvalidValue;
   static std::atomic<uint64_t> attr{0};  // dynamic LDS up to 64 KB (E = 1024) plus the static part
   {
     hipError_t err = ensure_dynamic_lds(select_route_kernel, sizeof(float) * kRouteWaves * kMaxExperts, attr);
