@@ -250,6 +250,23 @@ __device__ __forceinline__ uint32_t logit_code(float z) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Largest v over the wave (unsigned): an inclusive max scan inside each row
+// of 16 lanes by DPP row shifts (1, 2, 4, 8; a lane whose source lies outside
+// its row takes 0, the identity), then the four row maxima from lanes 15, 31,
+// 47 and 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  constexpr int kRowShr = 0x110;  // DPP row_shr:n is kRowShr + n
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowShr + 1, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowShr + 2, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowShr + 4, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kRowShr + 8, 0xf, 0xf, false));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  return max(max(r0, r1), max(r2, r3));
+}
+
 // NC = score slots per lane the code is unrolled for (expert c*64 + lane in
 // slot c); E <= 64*NC.  Instantiated for 1, 2, 4, 8 and 16 slots so that the
 // selection runs over no more slots than E needs.
@@ -257,11 +274,9 @@ __device__ __forceinline__ uint32_t logit_code(float z) {
 // Top-k mode, with every candidate reduced to one 32-bit order-preserving code
 // (of the logit, or with a selection-only bias of the biased score; absent
 // experts are 0, below every real code):
-//  - threshold T = the k-th largest code, as the largest T with at least k
-//    codes >= T, found bit by bit from the top (32 steps, each a compare per
-//    slot and a popcount of the ballots: no cross-lane shuffles);
-//  - the selection is every code > T plus, of the codes equal to T, the
-//    lowest ids (so equal values favour the lower id) up to k in all;
+//  - k rounds, each taking the largest remaining code (a wave max) and, of
+//    the candidates that hold it, the lowest id (so equal values favour the
+//    lower id); a taken code becomes 0;
 //  - the selected lanes write their ids, ascending (slot-major, then lane),
 //    to the wave's k LDS slots.
 // Hash mode: the ids tid2eid[token_ids[r]], placed by their rank in (id, table
@@ -283,29 +298,24 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
       const int e = c * 64 + lane;
       code[c] = e >= E ? 0u : logit_code(sel_bias ? router_score(zr[e]) + sel_bias[e] : zr[e]);
     }
-    uint32_t T = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) cnt += __popcll(__ballot(code[c] >= cand));
-      T = cnt >= k ? cand : T;
-    }
     uint64_t take[NC];
-    int need = k;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      take[c] = __ballot(code[c] > T);
-      need -= __popcll(take[c]);
-    }
+    for (int c = 0; c < NC; ++c) take[c] = 0ull;
+    for (int j = 0; j < k; ++j) {
+      uint32_t m = code[0];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      uint64_t m = __ballot(code[c] == T);
-      while (need > 0 && m != 0ull) {
-        const uint64_t low = m & (~m + 1ull);
-        take[c] |= low;
-        m ^= low;
-        --need;
+      for (int c = 1; c < NC; ++c) m = max(m, code[c]);
+      const uint32_t M = wave_max_u32(m);
+      bool found = false;  // wave-uniform
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint64_t b = __ballot(code[c] == M);
+        if (!found && b != 0ull) {
+          const uint64_t low = b & (~b + 1ull);
+          take[c] |= low;
+          if ((low >> lane) & 1ull) code[c] = 0u;
+          found = true;
+        }
       }
     }
     int base = 0;
@@ -339,7 +349,8 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int my_id = lane < k ? sel_lds[lane] : 0;
+  // (clamped: the ids index the logits here and the weights later)
+  const int my_id = lane < k ? min(max(sel_lds[lane], 0), E - 1) : 0;
   const float my_sv = router_score(lane < k ? zr[my_id] : 0.f);
   float sum = 0.f;
 #pragma unroll
