@@ -229,7 +229,7 @@ hipError_t launch_prologue(const uint16_t* x, const float* w, int n_rows, int d,
 // ---------------------------------------------------------------------------
 // Scores and selection, one wave per row.  s = sqrt(softplus(z)) with
 // softplus(z) = max(z,0) + log1p(exp(-|z|)).  Top-k mode takes the k largest
-// scores (equal scores: lower expert id first) by a threshold search; hash
+// scores (equal scores: lower expert id first) by k rounds of a wave maximum; hash
 // mode takes tid2eid[token_ids[r]].  Selected ids are written ascending with
 // gates = s / sum(s).  s increases strictly with z, so the selection runs on
 // the logits and only the k selected scores are computed.
