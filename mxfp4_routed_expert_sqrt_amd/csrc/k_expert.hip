@@ -384,7 +384,8 @@ __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Group g, i
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
     const int p = group_pair(g, slot_pos<THREADS, NB>(k));
-    row[k] = pair_rows ? p : (shared ? p - a.P : to_global(a.perm)[p] / a.k);
+    // (perm entries clamped into [0, P): a bad entry gives a wrong row, never an access out of bounds)
+    row[k] = pair_rows ? p : (shared ? p - a.P : min(max(to_global(a.perm)[p], 0), a.P - 1) / a.k);
   }
   row_ptrs<THREADS, NB, NA, FP6>(a, row, K, src);
 }
@@ -819,7 +820,7 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       const int p = group_pair(gq, slot_pos<kThreads, NB>(k));
-      row[k] = GU ? to_global(a.perm)[min(p, a.P - 1)] : p;
+      row[k] = GU ? min(max(to_global(a.perm)[min(p, a.P - 1)], 0), a.P - 1) : p;  // (clamped as in stage_rows)
     }
 #pragma unroll
     for (int i = 0; i < NA; ++i)
@@ -985,7 +986,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   float gw[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
-    src[j] = (j < k) ? y + (size_t)inv[(size_t)r * k + j] * d : y;
+    src[j] = (j < k) ? y + (size_t)min(max(inv[(size_t)r * k + j], 0), P - 1) * d : y;  // (clamped into [0, P))
     gw[j] = (j < k) ? gates[(size_t)r * k + j] : 0.f;
   }
   const float* ysh = has_shared ? y + ((size_t)P + r) * d : nullptr;

@@ -419,7 +419,7 @@ __device__ __forceinline__ void qk_unit(const Q2kArgs& a, const Group g, int fu0
   // activation row of unit row c (padding rows repeat the group's first row)
   auto act_row = [&](int c) -> int {
     const int p = g.p0 + (c < g.cnt ? c : 0);
-    return GU ? a.perm[p] / a.k : p;
+    return GU ? min(max(a.perm[p], 0), a.P - 1) / a.k : p;  // (perm entries clamped into [0, P))
   };
   QkRows<kThreads, NB> rows;
 #pragma unroll
@@ -505,7 +505,7 @@ __device__ __forceinline__ void qk_unit_resident(const Q2kArgs& a, const Group g
   // K/8 per row, then 16-byte pair pieces, K/64 per row, then X
   auto act_row = [&](int c) -> size_t {
     const int p = g.p0 + (c < g.cnt ? c : 0);
-    return (size_t)(GU ? a.perm[p] / a.k : p);
+    return (size_t)(GU ? min(max(a.perm[p], 0), a.P - 1) / a.k : p);  // (perm entries clamped into [0, P))
   };
   const int xpr = K / 8, ppr = K / 64;
   for (int q = tid; q < 16 * xpr; q += kThreads) {

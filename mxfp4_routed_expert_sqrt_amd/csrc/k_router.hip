@@ -384,6 +384,15 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
 // passes move 16-byte columns.
 constexpr int kRouteThreads = 1024;
 constexpr int kMaxSplits = 16;  // the most split-K partials of the logits (logits_splits)
+// Pairs up to which the last selection workgroup scatters by itself (a few per
+// thread); above it the scatter is its own launch.
+constexpr int kScatterPerThread = 8;
+constexpr int kScatterInBlockMax = kScatterPerThread * kRouteThreads;
+// Histogram bases the last workgroup keeps in LDS for its scatter (workgroups
+// x experts rounded to 4; 8192 ints: the 512-row verify batch at E = 256).
+constexpr int kBaseLds = 8192;
+// Histogram rows per scan thread kept in registers between the two passes.
+constexpr int kHistRegs = 4;
 constexpr int kRouteWaves = kRouteThreads / 64;  // rows selected per workgroup
 constexpr int kMaxExperts = 1024;
 
@@ -463,6 +472,7 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
   __shared__ int32_t s_seg[4 * kMaxExperts];  // step 2: segment sums / bases, [segment][Ep]
   __shared__ int32_t wave_tot[kRouteWaves];
   __shared__ int32_t wave_grp[kRouteWaves];
+  __shared__ __attribute__((aligned(16))) int32_t s_base[kBaseLds];  // step 2: bases [workgroup][Ep]
   __shared__ int32_t is_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x, nb = gridDim.x;
@@ -551,10 +561,25 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
   // the counts and every base is 0, so it goes straight to the offsets with no
   // histogram round trip and no device-scope handshake.
   const bool single = nb == 1;
+  const bool base_lds = (size_t)nb * Ep <= (size_t)kBaseLds;
+  // the pairs this thread scatters in 2e (expert, rank), loaded as soon as
+  // they are visible so that their latency overlaps the scans
+  int q_e[kScatterPerThread], q_r[kScatterPerThread];
+  auto fetch_pairs = [&]() {
+#pragma unroll
+    for (int i = 0; i < kScatterPerThread; ++i) {
+      const int q = tid + i * kRouteThreads;
+      if (scatter_here && q < P) {
+        q_e[i] = idx[q];
+        q_r[i] = inv[q];
+      }
+    }
+  };
   if (single) {
     for (int e = tid; e < E; e += kRouteThreads) counts[e] = s_a[e];
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // idx and the ranks in inv, read back in 2e
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // idx and the ranks in inv, read back below
     __syncthreads();
+    fetch_pairs();
   } else {
     for (int e = tid; e < Ep; e += kRouteThreads) hist[(size_t)b * Ep + e] = s_a[e];
 
@@ -571,24 +596,37 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
     __syncthreads();
     if (!is_last) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see the other workgroups' results
+    fetch_pairs();
 
     // step 2a: per (column of 4 experts, segment of histogram rows) sums
     const int C = Ep / 4;
     const int S = max(1, min(kRouteThreads / C, nb));  // segments
     const int L = (nb + S - 1) / S;                     // rows per segment
     const int4* h4 = (const int4*)hist;
+    int4 hr[kHistRegs];  // this thread's first histogram rows, reused in 2c
     if (tid < C * S) {
       const int c = tid % C, sg = tid / C;
       const int b0 = min(sg * L, nb), b1 = min(b0 + L, nb);
       int4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < kHistRegs; ++j)
+        if (b0 + j < b1) hr[j] = h4[(size_t)(b0 + j) * C + c];
 #pragma unroll 8
-      for (int bb = b0; bb < b1; ++bb) {
+      for (int bb = b0 + kHistRegs; bb < b1; ++bb) {
         const int4 v = h4[(size_t)bb * C + c];
         acc.x += v.x;
         acc.y += v.y;
         acc.z += v.z;
         acc.w += v.w;
       }
+#pragma unroll
+      for (int j = 0; j < kHistRegs; ++j)
+        if (b0 + j < b1) {
+          acc.x += hr[j].x;
+          acc.y += hr[j].y;
+          acc.z += hr[j].z;
+          acc.w += hr[j].w;
+        }
       *(int4*)(s_seg + sg * Ep + 4 * c) = acc;
     }
     __syncthreads();
@@ -604,20 +642,31 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
       counts[e] = run;
     }
     __syncthreads();
-    // 2c: each histogram row becomes its exclusive base
+    // 2c: each histogram row becomes its exclusive base (in LDS when the
+    // bases fit there; in global memory when the scatter reads them there: a
+    // separate scatter launch, or too many for LDS)
     if (tid < C * S) {
       const int c = tid % C, sg = tid / C;
       const int b0 = min(sg * L, nb), b1 = min(b0 + L, nb);
+      const bool to_hist = !scatter_here || !base_lds;
       int4 run = *(const int4*)(s_seg + sg * Ep + 4 * c);
       int4* w4 = (int4*)hist;
-#pragma unroll 8
-      for (int bb = b0; bb < b1; ++bb) {
-        const int4 v = w4[(size_t)bb * C + c];
-        w4[(size_t)bb * C + c] = run;
+      // (v by value: the caller may pass the very histogram entry this overwrites)
+      auto put = [&](int bb, const int4 v) {
+        if (base_lds) *(int4*)(s_base + bb * Ep + 4 * c) = run;
+        if (to_hist) w4[(size_t)bb * C + c] = run;
         run.x += v.x;
         run.y += v.y;
         run.z += v.z;
         run.w += v.w;
+      };
+#pragma unroll
+      for (int j = 0; j < kHistRegs; ++j)
+        if (b0 + j < b1) put(b0 + j, hr[j]);
+#pragma unroll 8
+      for (int bb = b0 + kHistRegs; bb < b1; ++bb) {
+        const int4 v = w4[(size_t)bb * C + c];
+        put(bb, v);
       }
     }
   }  // multi-workgroup step 2a-2c
@@ -658,16 +707,22 @@ __global__ void __launch_bounds__(kRouteThreads) select_route_kernel(
     write_groups(group_rows, c, ng, p0, gb + ig - ng, g_total, n_rows, P, E, has_shared, groups, n_groups);
   }
   __syncthreads();
-  // 2e: scatter (the bases were written by this workgroup in 2c); for large
-  // batches a separate launch spreads it over the whole chip
+  // 2e: scatter of the pairs fetched above (the bases were written by this
+  // workgroup in 2c); for large batches a separate launch spreads it over the
+  // whole chip
   const int per_b = kRouteWaves * k;
-#pragma unroll 4
-  for (int q = tid; q < (scatter_here ? P : 0); q += kRouteThreads) {
-    const int e = idx[q];
-    const int p = s_off[e] + (single ? 0 : hist[(size_t)(q / per_b) * Ep + e]) + inv[q];
-    if ((unsigned)p < (unsigned)P) {  // always true for ranks from step 1; guards the scatter
-      perm[p] = q;
-      inv[q] = p;
+#pragma unroll
+  for (int i = 0; i < kScatterPerThread; ++i) {
+    const int q = tid + i * kRouteThreads;
+    if (scatter_here && q < P) {
+      const int e = min(max(q_e[i], 0), E - 1);
+      const int bq = q / per_b;
+      const int base = single ? 0 : (base_lds ? s_base[bq * Ep + e] : hist[(size_t)bq * Ep + e]);
+      const int p = s_off[e] + base + q_r[i];
+      if ((unsigned)p < (unsigned)P) {  // always true for ranks from step 1; guards the scatter
+        perm[p] = q;
+        inv[q] = p;
+      }
     }
   }
 }
@@ -688,9 +743,6 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
   }
 }
 
-// Pairs up to which the last selection workgroup scatters by itself (a few per
-// thread); above it the scatter is its own launch.
-constexpr int kScatterInBlockMax = 8 * kRouteThreads;
 
 hipError_t launch_select_route(const float* z, const float* bias, int bias_mode, int d, int n_rows, int E, int k, int routing, const int32_t* token_ids,
                                const int32_t* tid2eid, int64_t vocab, int32_t* idx, float* gates, int has_shared,

@@ -197,6 +197,7 @@ struct Q2kArgs {
   const Group* groups;
   const int32_t* n_groups;
   int K, R, k, rows;       // contraction, output width, top-k, rows of the work list's groups
+  int P;                   // routed pairs (N * k)
   float limit;             // swiglu limit (<= 0: none)
   uint16_t* h;             // gate/up output: [P][R], fp16 when h_f16, else bf16
   int h_f16;               // h in fp16 (gate/up writes it, down reads it); needs |h| < 65504

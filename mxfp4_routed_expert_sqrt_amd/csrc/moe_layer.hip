@@ -319,6 +319,7 @@ int run_layer_q2k(const moe_config_t& c, const moe_args_t& a, uint8_t* ws, const
   ga.R = I;
   ga.k = k;
   ga.rows = rows;
+  ga.P = P;
   ga.limit = c.swiglu_limit;
   ga.h = h;
   // h in fp16 (3 more bits than bf16) when the swiglu clamp bounds it: |h| <= L^2 < 65504

@@ -277,6 +277,9 @@ EDGE = {
     "w16_d512_i384": MoEShape("edge_w16_d512_i384", 300, 512, 64, 4, 384, "topk", "edge_w16a"),
     "w16_d768_i512": MoEShape("edge_w16_d768_i512", 300, 768, 64, 4, 512, "topk", "edge_w16b"),
     "w16_d384_i256": MoEShape("edge_w16_d384_i256", 300, 384, 64, 4, 256, "topk", "edge_w16c"),
+    # more selection workgroups x experts (38 x 256) than the last selection workgroup keeps in LDS while it
+    # still scatters the 3600 pairs itself: the histogram bases go through global memory
+    "hist_global": MoEShape("edge_hist_global", 600, 256, 256, 6, 128, "topk", "edge_hist"),
 }
 
 
