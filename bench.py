@@ -75,6 +75,8 @@ def parse():
                     help="the shared expert in bf16 (its own bf16-MFMA GEMMs) instead of MXFP4")
     ap.add_argument("--with-norm", action="store_true",
                     help="run the layer with its input RMSNorm and a residual add (seeded bf16 weight and residual)")
+    ap.add_argument("--no-hbm-probe", action="store_true",
+                    help="skip the streaming-read probe (profiling runs of the layer's kernels)")
     ap.add_argument("--hbm-probe-only", action="store_true",
                     help="run only the streaming-read probe and print its JSON (for profiling it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -510,8 +512,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    print("[bench] streaming-read probe", file=sys.stderr, flush=True)
-    probe = hbm_read_peak(hip, dev, stream)
+    probe = None
+    if not args.no_hbm_probe:
+        print("[bench] streaming-read probe", file=sys.stderr, flush=True)
+        probe = hbm_read_peak(hip, dev, stream)
 
     N, d, I, E = shape.n_rows, shape.d_model, shape.d_ff, shape.n_experts
     ms_per_step = timing["ms_per_step"]
@@ -543,7 +547,8 @@ def main():
                    "global_batch": N, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "peak_measured": probe["read_gbs"], "frac_of_measured": achieved / probe["read_gbs"],
+                     "peak_measured": probe["read_gbs"] if probe else None,
+                     "frac_of_measured": achieved / probe["read_gbs"] if probe else None,
                      "kernel": "gateup_kernel" + (" + shared_bf16_kernel<2>" if args.shared_bf16 else ""),
                      "algorithmic_bytes": gu["algorithmic_bytes"],
                      "bytes_definition": "gate+up MXFP4 bytes (nibbles + E8M0 scales) of every touched expert, "

@@ -18,7 +18,7 @@
 
 #include "hbm_probe.h"
 
-namespace {
+namespace hbm_probe {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
@@ -52,7 +52,9 @@ __global__ void __launch_bounds__(kThreads) hbm_read_kernel(const u32x4* __restr
   if ((threadIdx.x & 63) == 0) sink[(size_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = acc;
 }
 
-}  // namespace
+}  // namespace hbm_probe
+
+using namespace hbm_probe;
 
 extern "C" int hbm_read_probe(const void* src, size_t bytes, int nontemporal, uint32_t* sink, int workgroups,
                               hipStream_t stream) {
