@@ -1,6 +1,6 @@
 // Streaming-read probe: the HBM read bandwidth that a plain kernel reaches on
 // this GPU, the practical ceiling beside the 8 TB/s of the data sheet against
-// which the expert GEMMs' weight streams are judged.  Measurement only: no
+// which the expert GEMMs' weight streams are measured.  Measurement only: no
 // step of the MoE layer calls it.
 //
 // Workgroup b reads its own contiguous range of the buffer (an equal share,
