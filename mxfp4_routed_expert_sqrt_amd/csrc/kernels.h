@@ -84,10 +84,13 @@ inline int unit_rows(int n_pairs, int E, int d, int I) {
 }
 
 // Split-K factor of the router logits: enough 64x64 tiles for >= 256
-// workgroups, at most 16 partials and at least two 64-wide K chunks each.
+// workgroups (>= 768, three per CU, from 64 tiles on: a tile's K loop runs at
+// the latency of its chunk steps, so large batches gain from more tiles in
+// flight per CU), at most 16 partials and at least two 64-wide K chunks each.
 __host__ __device__ inline int logits_splits(int n_rows, int E, int d) {
   const int tiles = ((n_rows + 63) / 64) * ((E + 63) / 64);
-  int S = (256 + tiles - 1) / tiles;
+  const int target = tiles >= 64 ? 768 : 256;
+  int S = (target + tiles - 1) / tiles;
   S = S < 16 ? S : 16;
   S = S < d / 128 ? S : d / 128;
   return S > 1 ? S : 1;
