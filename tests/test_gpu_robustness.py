@@ -24,6 +24,8 @@ TALL = MoEShape("edge_tall", 611, 512, 8, 4, 256, "topk", "edge_tall")
 MEDIUM = MoEShape("edge_medium", 300, 512, 64, 4, 256, "topk", "edge_medium", bias="zipf")
 # 1200 routed pairs at widths the wider units do not divide: the 16-row units of larger batches
 WIDE16 = MoEShape("edge_w16_d768_i512", 300, 768, 64, 4, 512, "topk", "edge_w16b")
+# 38 selection workgroups x 256 experts: the histogram bases go through global memory, scatter in-kernel
+HISTG = MoEShape("edge_hist_global", 600, 256, 256, 6, 128, "topk", "edge_hist")
 
 
 def _layer(wl):
@@ -58,11 +60,12 @@ def _same(a, b, label):
         assert np.array_equal(a[key], b[key]), f"{label}: {key} differs"
 
 
-@pytest.mark.parametrize("shape", [TALL, MEDIUM, WIDE16, SHAPES["hash2048"]],
-                         ids=["tall", "medium", "wide16", "hash2048-scatter"])
+@pytest.mark.parametrize("shape", [TALL, MEDIUM, WIDE16, HISTG, SHAPES["hash2048"]],
+                         ids=["tall", "medium", "wide16", "hist-global", "hash2048-scatter"])
 def test_poisoned_workspace_repeatable(shape):
     # tall, medium: the 64- and 32-row work units; wide16: 16-row units of a batch of >= 1024 pairs;
-    # hash2048: 12288 pairs, so the separate scatter launch
+    # hist-global: the selection's bases in global memory with the in-kernel scatter (medium bases
+    # stay in LDS); hash2048: 12288 pairs, so the separate scatter launch
     wl = workload(shape)
     layer = _layer(wl)
     x, tok, tab = _inputs(wl)
