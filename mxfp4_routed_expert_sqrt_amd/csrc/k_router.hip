@@ -375,11 +375,14 @@ __device__ __forceinline__ void select_row(const float* zr /* LDS: the row's log
 //     the ranks (in inv) and its per-expert histogram row.
 //  2. The last workgroup to finish scans the histogram rows per expert: sums
 //     over segments of rows, a scan over the segments, then a second pass
-//     that overwrites each row with its exclusive base.  The counts, their
-//     exclusive scan (offsets), the scatter of perm/inv and the work list of
-//     the grouped GEMMs (groups of <= 16, 32 or 64 rows of one expert, and
-//     the shared expert's rows) follow.  A launch of one workgroup (<= 16
-//     rows) takes its own histogram row as the counts, with zero bases.
+//     that turns each row into its exclusive base (kept in LDS when the bases
+//     fit there, else written over the row in global memory).  The counts,
+//     their exclusive scan (offsets) and the work list of the grouped GEMMs
+//     (groups of <= 16, 32 or 64 rows of one expert, and the shared expert's
+//     rows) follow in one pass, then the scatter of perm/inv, whose pairs
+//     each thread fetched as soon as the workgroup took over.  A launch of one
+//     workgroup (<= 16 rows) takes its own histogram row as the counts, with
+//     zero bases.
 // Histogram rows are E rounded up to a multiple of 4 ints wide, so both scan
 // passes move 16-byte columns.
 constexpr int kRouteThreads = 1024;
