@@ -61,3 +61,18 @@ def test_a_malformed_summary_gives_no_traffic(monkeypatch, tmp_path, content):
     p.write_text(content.format(d=bench.kernel_source_digest()))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
     assert bench.recorded_traffic("verify512") is None
+
+
+def test_probe_options_parse_and_the_probe_library_is_required(monkeypatch):
+    # the streaming-read probe runs by default; --no-hbm-probe leaves it out of profiling runs
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    args = bench.parse()
+    assert not args.no_hbm_probe and not args.hbm_probe_only
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--no-hbm-probe", "--only"])
+    assert bench.parse().no_hbm_probe
+    # the probe's bytes are 8x the 256 MB memory-side cache and whole 16-byte pieces
+    assert bench.HBM_PROBE_BYTES >= 8 * 256 * 2 ** 20 and bench.HBM_PROBE_BYTES % 16 == 0
+    # without its library the probe stops with a message instead of reporting a figure
+    monkeypatch.setattr(bench, "HBM_PROBE_LIB", os.path.join(ROOT, "no_such_dir", "libmoe_hbm.so"))
+    with pytest.raises(SystemExit, match="libmoe_hbm.so is missing"):
+        bench.hbm_read_peak(None, None, None)
