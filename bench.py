@@ -246,9 +246,14 @@ class Runner:
         for e in evs + [[ev0, ev1]]:
             for x in e:
                 hip.destroy(x)
+        # per-step spread: the sum of one step's stage intervals in that loop (p10, median, p90)
+        step_us = stage_ms.sum(axis=1) * 1e3
         return {"preheat_s": preheat, "preheat_calls": n_pre, "ms_per_step": elapsed * 1e3 / K,
                 "gpu_ms_per_step": gpu_ms / K,
-                "stages_us": {n: float(np.mean(stage_ms[:, s])) * 1e3 for s, n in enumerate(capi.STAGE_NAMES)}}
+                "stages_us": {n: float(np.mean(stage_ms[:, s])) * 1e3 for s, n in enumerate(capi.STAGE_NAMES)},
+                "step_us_p10_p50_p90": [float(v) for v in np.percentile(step_us, [10, 50, 90])],
+                "gateup_us_p10_p50_p90": [float(v) for v in np.percentile(stage_ms[:, capi.STAGE_NAMES.index("gateup")] * 1e3,
+                                                                         [10, 50, 90])]}
 
 
 def summarise(shape, timing, touched_routed, shared_bf16=False, has_bias=False, q2k=False):
@@ -274,6 +279,9 @@ def summarise(shape, timing, touched_routed, shared_bf16=False, has_bias=False, 
                  "hbm_frac": r(a["down_bytes"] / dn / 1e9 / HBM_PEAK_GBS),
                  fk: r(a["down_flops"] / dn / 1e12 / peak)},
         "stages_us": {k: round(v, 2) for k, v in timing["stages_us"].items()},
+        # spread over the steps of the stage-timing loop (its events add a little stream time per step)
+        "stage_loop_step_us_p10_p50_p90": [round(v, 1) for v in timing["step_us_p10_p50_p90"]],
+        "gateup_us_p10_p50_p90": [round(v, 1) for v in timing["gateup_us_p10_p50_p90"]],
         "preheat_s": round(timing["preheat_s"], 3),
         "preheat_calls": timing["preheat_calls"],
     }
