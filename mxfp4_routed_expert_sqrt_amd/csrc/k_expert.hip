@@ -221,9 +221,11 @@ __device__ __forceinline__ v8i read_b(const uint8_t* chunk, int i) {
   }
 }
 
+// nbu (wave-uniform): column tiles multiplied; the MFMAs of tiles past it
+// (padding rows of a unit whose rows fit in fewer tiles) are branched over.
 template <int J, int NA, int NB, bool FP6>
 __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chunk, const uint32_t (&sa)[NA],
-                                         const uint32_t (&sb)[NB][2], v4f (&acc)[NA][NB]) {
+                                         const uint32_t (&sb)[NB][2], v4f (&acc)[NA][NB], int nbu = NB) {
   constexpr int NF = 2 * NB;
   v8i b0 = read_b<J, NB, FP6>(chunk, 0), b1;
 #pragma unroll
@@ -233,8 +235,10 @@ __device__ __forceinline__ void mma_step(const WFrag<NA>& f, const uint8_t* chun
     const int tt = i % NB, t = i / NB;
     if (i + 1 < NF) nxt = read_b<J, NB, FP6>(chunk, i + 1);
     if (NF > 2) __builtin_amdgcn_sched_barrier(0);  // keep the read ahead of these MFMAs
+    if (tt < 2 || tt < nbu) {  // (tiles 0 and 1 always: no branch for them)
 #pragma unroll
-    for (int a = 0; a < NA; ++a) acc[a][tt] = mfma_fp4_fp8<J, FP6>(f.A[a], cur, acc[a][tt], sa[a], sb[tt][t]);
+      for (int a = 0; a < NA; ++a) acc[a][tt] = mfma_fp4_fp8<J, FP6>(f.A[a], cur, acc[a][tt], sa[a], sb[tt][t]);
+    }
     if (NF > 2) __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -265,7 +269,8 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
                                         const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& cur, int sg,
                                         int nks, int n_sg, v4f (&acc)[NA][NB], const uint8_t* chunk,
                                         uint8_t* next_buf,
-                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& cs, int cc) {
+                                        const UnitSrc<NA, NB, ChunkStage<THREADS, NB>::kScales, FP6>& cs, int cc,
+                                        int nbu = NB) {
   const int lane = threadIdx.x & 63, last = nks - 1, k0 = 4 * sg;
   uint32_t sb[NB][2];
 #pragma unroll
@@ -279,19 +284,19 @@ __device__ __forceinline__ void k_group(WFrag<NA> (&f)[RING], ChunkStage<THREADS
   load_wscales(sa_n, cur.as, min(sg + 1, n_sg - 1));
   load_step(f[(4 * GI + RING - 1) % RING], 0);
   __builtin_amdgcn_sched_barrier(0);
-  mma_step<0, NA, NB, FP6>(f[(4 * GI) % RING], chunk, sa, sb, acc);
+  mma_step<0, NA, NB, FP6>(f[(4 * GI) % RING], chunk, sa, sb, acc, nbu);
   __builtin_amdgcn_sched_barrier(0);
   load_step(f[(4 * GI + RING) % RING], 1);
   __builtin_amdgcn_sched_barrier(0);
-  if (k0 + 1 < nks) mma_step<1, NA, NB, FP6>(f[(4 * GI + 1) % RING], chunk, sa, sb, acc);
+  if (k0 + 1 < nks) mma_step<1, NA, NB, FP6>(f[(4 * GI + 1) % RING], chunk, sa, sb, acc, nbu);
   __builtin_amdgcn_sched_barrier(0);
   load_step(f[(4 * GI + RING + 1) % RING], 2);
   __builtin_amdgcn_sched_barrier(0);
-  if (k0 + 2 < nks) mma_step<2, NA, NB, FP6>(f[(4 * GI + 2) % RING], chunk, sa, sb, acc);
+  if (k0 + 2 < nks) mma_step<2, NA, NB, FP6>(f[(4 * GI + 2) % RING], chunk, sa, sb, acc, nbu);
   __builtin_amdgcn_sched_barrier(0);
   load_step(f[(4 * GI + RING + 2) % RING], 3);
   __builtin_amdgcn_sched_barrier(0);
-  if (k0 + 3 < nks) mma_step<3, NA, NB, FP6>(f[(4 * GI + 3) % RING], chunk, sa, sb, acc);
+  if (k0 + 3 < nks) mma_step<3, NA, NB, FP6>(f[(4 * GI + 3) % RING], chunk, sa, sb, acc, nbu);
   __builtin_amdgcn_sched_barrier(0);
   stage.store(next_buf);
   __syncthreads();
@@ -830,10 +835,12 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
     // group loads and stages the queued unit's first chunk.
     UnitSrc<NA, NB, NS, true> nxt;
     if constexpr (!GU) row_ptrs<kThreads, NB, NA, true>(a, row, a.K, nxt);
+    // column tiles that hold the group's rows (the others would multiply padding rows)
+    const int nbu = __builtin_amdgcn_readfirstlane((g.cnt + 15) / 16);
     for (int sg = 0; sg + 1 < n_sg; ++sg)
       k_group<0, RING, NA, kThreads, NB, false, true>(f, stage, sa, sa_n, cur, sg, nks, n_sg, acc,
                                                       lds + ((bp + sg) & 1) * kBuf, lds + ((bp + sg + 1) & 1) * kBuf,
-                                                      cur, sg + 1);
+                                                      cur, sg + 1, nbu);
     const int f0q = fbq * kFeatUnit + wave * kFeatWave;
     {
       const ExpertArgs B = reload_args();
@@ -847,7 +854,7 @@ __global__ void __launch_bounds__(64 * WAVES) tall_kernel(ExpertArgs a) {
     }
     k_group<0, RING, NA, kThreads, NB, false, true>(f, stage, sa, sa_n, cur, n_sg - 1, nks, n_sg, acc,
                                                     lds + ((bp + n_sg - 1) & 1) * kBuf,
-                                                    lds + ((bp + n_sg) & 1) * kBuf, nxt, 0);
+                                                    lds + ((bp + n_sg) & 1) * kBuf, nxt, 0, nbu);
     bp = (bp + n_sg) & 1;
     const ExpertArgs A = reload_args();
     if (tid == 0) s_claim[0] = q >= 0 ? resolve(t, A.pool) : -1;
