@@ -76,3 +76,23 @@ def test_probe_options_parse_and_the_probe_library_is_required(monkeypatch):
     monkeypatch.setattr(bench, "HBM_PROBE_LIB", os.path.join(ROOT, "no_such_dir", "libmoe_hbm.so"))
     with pytest.raises(SystemExit, match="libmoe_hbm.so is missing"):
         bench.hbm_read_peak(None, None, None)
+
+
+def test_algorithmic_bytes_and_flops_follow_the_expert_size():
+    # one MXFP4 expert (gate, up, down at d 4096, I 2048) is 3 x 4096 x 2048 values at 4 bits plus one
+    # E8M0 byte per 32 values: 13,369,344 bytes, the 13.4 MB per expert the pages give for V4 Flash
+    # (FaStar README, "Expert virtual memory"); the verify512 layer touches all 256 routed experts + shared
+    from mxfp4_routed_expert_sqrt_amd.configs import SHAPES
+    sh = SHAPES["verify512"]
+    a = bench.algorithmic(sh, 256)
+    per_expert = 3 * (4096 * 2048 // 2 + 4096 * 2048 // 32)
+    assert per_expert == 13_369_344
+    x = out = 512 * 4096 * 2
+    assert a["layer_bytes"] == 257 * per_expert + 256 * 4096 * 4 + x + out == 3_448_504_320
+    assert a["gateup_bytes"] == 257 * per_expert * 2 // 3 + x == 2_294_808_576
+    assert a["down_bytes"] == 257 * per_expert // 3
+    # FP4-equivalent flops: 2 per multiply-add, 3 matrices of d x I per (row, expert), k + 1 experts per row
+    assert a["layer_flops"] == 6 * 4096 * 2048 * 512 * 7 == 180_388_626_432
+    assert a["gateup_flops"] + a["down_flops"] == a["layer_flops"]
+    # an expert with no rows reads no weights: fewer touched experts, fewer bytes
+    assert bench.algorithmic(sh, 100)["layer_bytes"] == a["layer_bytes"] - 156 * per_expert
